@@ -1,0 +1,265 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module only draws numbers and lays out tables: weights, hidden states,
+token ids, context lengths, the random contents of the BF16 page pool and the
+block tables that map each (layer, sequence, logical page) to a physical
+page.  It holds none of the decode step's arithmetic; both the oracle and the
+HIP path receive exactly the bytes produced here.
+
+Every tensor is drawn from ``numpy.random.default_rng([seed, tensor id,
+*index])`` so that any slice (one layer, one chunk of pool pages) can be
+regenerated on its own.  FP32 normals are turned into BF16 with torch's
+round-to-nearest-even conversion.
+
+Model shapes follow the public configurations of the two model families the
+source pages run (Llama 3.2 1B in the "Inference from Scratch" engine,
+Qwen2.5-0.5B-Instruct in llmc), with random weights: no checkpoint is used.
+"""
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+PAGE_TOKENS = 16
+
+# tensor ids for the seed sequence
+_ID = {"embed": 1, "final_norm": 2, "attn_norm": 10, "w_qkv": 11, "w_o": 12,
+       "mlp_norm": 13, "w_gate_up": 14, "w_down": 15, "hidden": 20, "tokens": 21,
+       "lens": 22, "pool": 23, "perm": 24, "q": 25, "k_new": 26, "v_new": 27}
+
+LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
+
+
+@dataclass(frozen=True)
+class ModelShape:
+    name: str
+    hidden: int
+    layers: int
+    heads: int
+    kv_heads: int
+    head_dim: int
+    inter: int
+    vocab: int
+    eps: float
+    theta: float
+    max_pos: int
+
+    @property
+    def qkv_rows(self):
+        return (self.heads + 2 * self.kv_heads) * self.head_dim
+
+    def layer_param_count(self):
+        H, D = self.hidden, self.head_dim
+        return (self.qkv_rows * H + H * self.heads * D + 2 * self.inter * H
+                + H * self.inter + 2 * H)
+
+
+QWEN05 = ModelShape("qwen2.5-0.5b-shape", hidden=896, layers=24, heads=14, kv_heads=2,
+                    head_dim=64, inter=4864, vocab=151936, eps=1e-6, theta=1e6,
+                    max_pos=32768)
+LLAMA1B = ModelShape("llama-3.2-1b-shape", hidden=2048, layers=16, heads=32, kv_heads=8,
+                     head_dim=64, inter=8192, vocab=128256, eps=1e-5, theta=5e5,
+                     max_pos=131072)
+
+
+def tiny_shape(hidden=128, layers=2, heads=4, kv_heads=2, inter=256, vocab=1000,
+               head_dim=64, eps=1e-5, theta=1e4, max_pos=4096, name="tiny"):
+    return ModelShape(name, hidden, layers, heads, kv_heads, head_dim, inter, vocab,
+                      eps, theta, max_pos)
+
+
+# ----------------------------------------------------------- primitives ---
+
+def rng(seed, name, *index):
+    return np.random.default_rng([int(seed), _ID[name], *[int(i) for i in index]])
+
+
+def to_bf16_bits(x):
+    """float32 numpy -> uint16 BF16 bit patterns (torch's RNE conversion)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_normal(seed, name, shape, sigma=1.0, mean=0.0, index=()):
+    g = rng(seed, name, *index)
+    n = int(np.prod(shape))
+    x = g.standard_normal(n, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    if mean != 0.0:
+        x += np.float32(mean)
+    return to_bf16_bits(x).reshape(shape)
+
+
+# --------------------------------------------------------------- weights ---
+
+def layer_weights(shape, seed, layer, sigma=0.02, norm_sigma=0.02):
+    H, D, I = shape.hidden, shape.head_dim, shape.inter
+    return {
+        "attn_norm": bf16_normal(seed, "attn_norm", (H,), norm_sigma, 1.0, (layer,)),
+        "w_qkv": bf16_normal(seed, "w_qkv", (shape.qkv_rows, H), sigma, 0.0, (layer,)),
+        "w_o": bf16_normal(seed, "w_o", (H, shape.heads * D), sigma, 0.0, (layer,)),
+        "mlp_norm": bf16_normal(seed, "mlp_norm", (H,), norm_sigma, 1.0, (layer,)),
+        "w_gate_up": bf16_normal(seed, "w_gate_up", (2 * I, H), sigma, 0.0, (layer,)),
+        "w_down": bf16_normal(seed, "w_down", (H, I), sigma, 0.0, (layer,)),
+    }
+
+
+def model_weights(shape, seed, sigma=0.02, norm_sigma=0.02, layers=None):
+    L = shape.layers if layers is None else layers
+    return {
+        "embed": bf16_normal(seed, "embed", (shape.vocab, shape.hidden), sigma),
+        "final_norm": bf16_normal(seed, "final_norm", (shape.hidden,), norm_sigma, 1.0),
+        "layers": [layer_weights(shape, seed, l, sigma, norm_sigma) for l in range(L)],
+    }
+
+
+# ------------------------------------------------------- pool and tables ---
+
+def page_elems(shape_or_kv_heads, head_dim=64, page_tokens=PAGE_TOKENS):
+    kv = shape_or_kv_heads.kv_heads if hasattr(shape_or_kv_heads, "kv_heads") else shape_or_kv_heads
+    return 2 * kv * page_tokens * head_dim
+
+
+def random_pool(seed, num_pages, elems_per_page, chunk_pages=2048):
+    """The whole pool as N(0,1) BF16 values, drawn chunk by chunk."""
+    out = np.empty(num_pages * elems_per_page, dtype=np.uint16)
+    for c0 in range(0, num_pages, chunk_pages):
+        c1 = min(num_pages, c0 + chunk_pages)
+        g = rng(seed, "pool", c0 // chunk_pages)
+        x = g.standard_normal((c1 - c0) * elems_per_page, dtype=np.float32)
+        out[c0 * elems_per_page:c1 * elems_per_page] = to_bf16_bits(x)
+    return out
+
+
+def pages_for(n_tokens):
+    return (np.asarray(n_tokens, dtype=np.int64) + PAGE_TOKENS - 1) // PAGE_TOKENS
+
+
+def block_tables(seed, layers, n_tokens, num_pages, max_pages=None, fill=-1):
+    """int32 [layers, B, max_pages]: the (layer, seq, logical page) entries
+    that hold tokens 0..n_b-1 take physical pages from one random
+    permutation of the pool, in that order; the other entries are `fill`."""
+    n_tokens = np.asarray(n_tokens, dtype=np.int64)
+    need = pages_for(n_tokens)
+    if max_pages is None:
+        max_pages = int(max(1, need.max()))
+    total = int(need.sum()) * layers
+    if total > num_pages:
+        raise ValueError("pool of %d pages cannot hold %d pages" % (num_pages, total))
+    perm = rng(seed, "perm").permutation(num_pages).astype(np.int32)
+    bt = np.full((layers, len(n_tokens), max_pages), fill, dtype=np.int32)
+    i = 0
+    for l in range(layers):
+        for b, k in enumerate(need):
+            bt[l, b, :k] = perm[i:i + k]
+            i += k
+    return bt
+
+
+# ----------------------------------------------------------- workloads ---
+
+@dataclass
+class Workload:
+    name: str
+    shape: ModelShape
+    batch: int
+    positions: np.ndarray          # int32 [B]: absolute position of the new token
+    num_pages: int
+    block_tables: np.ndarray       # int32 [L, B, max_pages]
+    pool: np.ndarray = None        # uint16 [num_pages * page_elems]
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def max_pages(self):
+        return self.block_tables.shape[2]
+
+    @property
+    def lens(self):
+        return self.positions.astype(np.int32) + 1
+
+
+def decode_workload(name, shape, seed, positions, layers=None, num_pages=None,
+                    max_pages=None, with_pool=True):
+    """Inputs for a decode step: token p_b is new, 0..p_b-1 are cached in the
+    pool.  The pool is sized to fit unless num_pages is given."""
+    positions = np.asarray(positions, dtype=np.int32)
+    L = shape.layers if layers is None else layers
+    need = int(pages_for(positions + 1).sum()) * L
+    npages = need if num_pages is None else num_pages
+    bt = block_tables(seed, L, positions + 1, npages, max_pages)
+    pool = random_pool(seed, npages, page_elems(shape)) if with_pool else None
+    return Workload(name, shape, len(positions), positions, npages, bt, pool)
+
+
+def c1_layer(seed=1001):
+    """One Qwen2.5-0.5B-shaped layer, batch 1, 127 cached + 1 new, 64-page pool."""
+    shape = QWEN05
+    wl = decode_workload("qwen2.5-0.5b-shape layer, batch 1, 127 cached + 1 new",
+                         shape, seed, [127], layers=1, num_pages=64)
+    wl.extra["weights"] = layer_weights(shape, seed, 0)
+    wl.extra["hidden"] = rng(seed, "hidden").standard_normal((1, shape.hidden), dtype=np.float32)
+    return wl
+
+
+def c2_lens(seed=1002, batch=16, max_len=2048):
+    return rng(seed, "lens").integers(1, max_len + 1, size=batch).astype(np.int32)
+
+
+def c2_attention(seed=1002, batch=16, pool_bytes=128 << 20):
+    """Paged GQA attention alone, Llama-3.2-1B heads, lengths U[1,2048],
+    pages drawn from a 128 MiB pool with shuffled tables; Q N(0,1) BF16."""
+    shape = LLAMA1B
+    lens = c2_lens(seed, batch)
+    npages = pool_bytes // (page_elems(shape) * 2)
+    bt = block_tables(seed, 1, lens, npages, max_pages=128)[0]
+    pool = random_pool(seed, npages, page_elems(shape))
+    q = bf16_normal(seed, "q", (batch, shape.heads, shape.head_dim))
+    return {"name": "paged GQA attention, 32/8 heads, d64, batch 16, lens U[1,2048], 128 MiB pool",
+            "shape": shape, "lens": lens, "num_pages": int(npages), "block_table": bt,
+            "pool": pool, "q": q, "scale": 0.125}
+
+
+def c3_step(seed=1003, with_pool=True, layers=None):
+    shape = LLAMA1B
+    L = shape.layers if layers is None else layers
+    wl = decode_workload("llama-3.2-1b-shape 16-layer step, batch 1, context 1024",
+                         shape, seed, [1023], layers=L, with_pool=with_pool)
+    wl.extra["tokens"] = rng(seed, "tokens").integers(0, shape.vocab, size=1).astype(np.int32)
+    return wl
+
+
+def c4_positions(seed=1004, batch=64):
+    return (rng(seed, "lens").integers(64, 2049, size=batch) - 1).astype(np.int32)
+
+
+def c4_step(seed=1004, batch=64, with_pool=True, layers=None):
+    shape = LLAMA1B
+    L = shape.layers if layers is None else layers
+    wl = decode_workload("llama-3.2-1b-shape 16-layer step, batch 64, context U[64,2048]",
+                         shape, seed, c4_positions(seed, batch), layers=L, with_pool=with_pool)
+    wl.extra["tokens"] = rng(seed, "tokens").integers(0, shape.vocab, size=batch).astype(np.int32)
+    return wl
+
+
+def c5_step(seed=1005, batch=128, with_pool=True, layers=None):
+    shape = QWEN05
+    L = shape.layers if layers is None else layers
+    wl = decode_workload("qwen2.5-0.5b-shape 24-layer step, batch 128, 4096 cached + 1 new",
+                         shape, seed, np.full(batch, 4096, dtype=np.int32), layers=L,
+                         with_pool=with_pool)
+    wl.extra["tokens"] = rng(seed, "tokens").integers(0, shape.vocab, size=batch).astype(np.int32)
+    return wl
+
+
+def bench_step(seed=1002, batch=16, with_pool=True, layers=None):
+    """Llama-3.2-1B-shaped 16-layer decode step at batch 16 whose attention
+    lengths are the paged-attention workload's draw (U[1,2048])."""
+    shape = LLAMA1B
+    L = shape.layers if layers is None else layers
+    positions = c2_lens(seed, batch) - 1
+    wl = decode_workload("llama-3.2-1b-shape 16-layer decode step, batch 16, "
+                         "attention lengths U[1,2048] (the paged-attention draw)",
+                         shape, seed, positions, layers=L, with_pool=with_pool)
+    wl.extra["tokens"] = rng(seed, "tokens").integers(0, shape.vocab, size=batch).astype(np.int32)
+    return wl

@@ -1,0 +1,118 @@
+"""Float64 brute force of the decode step for tiny shapes (test helper).
+
+Written independently of the oracle's C code and in a different form: whole
+matrices, a materialised softmax over all scores, RoPE in the rotate-half
+vector form x*cos + rotate_half(x)*sin, numpy indexing of the pool viewed as
+[page][K|V][kv head][slot][d].  Only the BF16 storage of appended K/V is
+mirrored (rounded with torch's conversion), since the pool holds BF16.
+"""
+import numpy as np
+import torch
+
+
+def bf16_bits_to_f64(h):
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_round_f64(x):
+    t = torch.from_numpy(np.asarray(x, dtype=np.float64)).to(torch.float32).to(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def rmsnorm(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+
+
+def rope(u, pos, theta):
+    """u [..., heads, D] float64 rotated at position pos (rotate-half pairs)."""
+    D = u.shape[-1]
+    j = np.arange(D // 2, dtype=np.float64)
+    ang = pos * theta ** (-2.0 * j / D)
+    cos = np.concatenate([np.cos(ang), np.cos(ang)])
+    sin = np.concatenate([np.sin(ang), np.sin(ang)])
+    rot = np.concatenate([-u[..., D // 2:], u[..., :D // 2]], axis=-1)
+    return u * cos + rot * sin
+
+
+def softmax_attention(q, K, V, scale):
+    """q [hq, D]; K, V [n, hkv, D] -> [hq, D], via repeated KV and a
+    materialised softmax."""
+    hq, D = q.shape
+    hkv = K.shape[1]
+    Kr = np.repeat(K, hq // hkv, axis=1)          # [n, hq, D]
+    Vr = np.repeat(V, hq // hkv, axis=1)
+    s = np.einsum("hd,nhd->hn", q, Kr) * scale     # [hq, n]
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    return np.einsum("hn,nhd->hd", p, Vr)
+
+
+def pool_view(pool, kv_heads, head_dim, page_tokens=16):
+    return np.asarray(pool).reshape(-1, 2, kv_heads, page_tokens, head_dim)
+
+
+def gather(pool, kv_heads, head_dim, bt_row, n, page_tokens=16):
+    """K, V [n, hkv, D] float64 of tokens 0..n-1."""
+    pv = pool_view(pool, kv_heads, head_dim, page_tokens)
+    t = np.arange(n)
+    pages = np.asarray(bt_row)[t // page_tokens]
+    slots = t % page_tokens
+    K = bf16_bits_to_f64(pv[pages, 0, :, slots, :])
+    V = bf16_bits_to_f64(pv[pages, 1, :, slots, :])
+    return K, V
+
+
+def layer(shape, lw, x, K, V, pos):
+    """One layer, one sequence; K, V [pos, hkv, D] float64 cached rows.
+    Returns (x_out, k_row, v_row) with k_row/v_row BF16-rounded float64."""
+    H, hq, hkv, D, I = shape.hidden, shape.heads, shape.kv_heads, shape.head_dim, shape.inter
+    W = {k: bf16_bits_to_f64(v) for k, v in lw.items()}
+    xn = rmsnorm(x, W["attn_norm"], shape.eps)
+    qkv = W["w_qkv"] @ xn
+    q = qkv[:hq * D].reshape(hq, D)
+    k = qkv[hq * D:(hq + hkv) * D].reshape(hkv, D)
+    v = qkv[(hq + hkv) * D:].reshape(hkv, D)
+    q = rope(q, pos, shape.theta)
+    k = bf16_round_f64(rope(k, pos, shape.theta))
+    v = bf16_round_f64(v)
+    Kall = np.concatenate([K, k[None]], axis=0)
+    Vall = np.concatenate([V, v[None]], axis=0)
+    o = softmax_attention(q, Kall, Vall, 1.0 / np.sqrt(D)).reshape(-1)
+    h1 = x + W["w_o"] @ o
+    hn = rmsnorm(h1, W["mlp_norm"], shape.eps)
+    gu = W["w_gate_up"] @ hn
+    g, u = gu[:I], gu[I:]
+    a = g / (1.0 + np.exp(-g)) * u
+    return h1 + W["w_down"] @ a, k, v
+
+
+def decode_step(shape, weights, pool, bts, positions, tokens):
+    """Full step for every sequence; returns (logits [B, V], argmax [B])."""
+    E = bf16_bits_to_f64(weights["embed"])
+    fn = bf16_bits_to_f64(weights["final_norm"])
+    out_logits, out_tok = [], []
+    for b, (p, tok) in enumerate(zip(positions, tokens)):
+        x = E[int(tok)].copy()
+        for l in range(shape.layers):
+            K, V = gather(pool, shape.kv_heads, shape.head_dim, bts[l, b], int(p))
+            x, _, _ = layer(shape, weights["layers"][l], x, K, V, int(p))
+        logits = E @ rmsnorm(x, fn, shape.eps)
+        out_logits.append(logits)
+        out_tok.append(int(np.argmax(logits)))
+    return np.array(out_logits), np.array(out_tok)
+
+
+def online_softmax_attention(q, K, V, scale, block):
+    """Float64 online softmax over blocks of `block` tokens (running max,
+    rescaled sum and accumulator), for one head: q [D], K, V [n, D]."""
+    m, l, acc = -np.inf, 0.0, np.zeros(q.shape[0])
+    for t0 in range(0, K.shape[0], block):
+        s = K[t0:t0 + block] @ q * scale
+        m_new = max(m, s.max())
+        alpha = np.exp(m - m_new) if np.isfinite(m) else 0.0
+        p = np.exp(s - m_new)
+        l = l * alpha + p.sum()
+        acc = acc * alpha + p @ V[t0:t0 + block]
+        m = m_new
+    return acc / l
