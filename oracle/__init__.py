@@ -22,7 +22,8 @@ Parity pins (what each function is checked against, in tests/):
                          a dominant key gives its V, two-token closed form
                          fixes the 1/sqrt(D) scale, GQA equals MHA over
                          repeated KV, float64 online softmax equals two-pass
-  pool gather / append   numpy reshape of the pool as [page][K|V][head][slot][d]
+  pool gather / append   numpy views of each page as K [head][slot][d] and
+                         V [head][d][slot]
   layer, step            float64 brute force with a materialised softmax on
                          tiny shapes; all-zero weights leave x unchanged
   argmax                 numpy.argmax (first maximum)
@@ -171,7 +172,8 @@ def attention(q, kc, vc, kv_heads, scale):
 # ---------------------------------------------------------------- paging ---
 
 class PoolGeometry:
-    """Page geometry: T tokens per page, [K|V][kv head][slot][d] BF16 per page."""
+    """Page geometry: T tokens per page; per page the BF16 K block
+    [kv head][slot][d] followed by the V block [kv head][d][slot]."""
 
     def __init__(self, kv_heads, head_dim, page_tokens=16):
         self.kv_heads = kv_heads

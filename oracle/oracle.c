@@ -38,7 +38,8 @@
  *   - Argmax returns the lowest index among equal maxima.
  *
  * Pool page layout (the boundary's stated layout, implemented here on its
- * own): a physical page holds, as BF16, [K then V][kv head][slot 0..T-1][d].
+ * own): a physical page holds, as BF16, first the K block [kv head][slot
+ * 0..T-1][d], then the V block [kv head][d][slot 0..T-1] (V transposed).
  */
 #include <math.h>
 #include <stdint.h>
@@ -211,11 +212,18 @@ void orc_attention(const float *q, const float *kc, const float *vc, int n,
 
 /* ------------------------------------------------------------ paging --- */
 
-/* Element offset of (page, K or V, kv head g, slot, d) inside the pool. */
+/*
+ * Element offset of (page, K or V, kv head g, slot, d) inside the pool:
+ * K at [g][slot][d] from the page start, V at [g][d][slot] after the
+ * hkv * T * D elements of the K block.
+ */
 static long pool_offset(long page_elems, int hkv, int T, int D, int page,
 			int kv, int g, int slot, int d)
 {
-	return (long)page * page_elems + (((long)kv * hkv + g) * T + slot) * D + d;
+	long start = (long)page * page_elems;
+	if (kv == 0)
+		return start + ((long)g * T + slot) * D + d;
+	return start + (long)hkv * T * D + ((long)g * D + d) * T + slot;
 }
 
 /*

@@ -2,9 +2,10 @@
 
 Written independently of the oracle's C code and in a different form: whole
 matrices, a materialised softmax over all scores, RoPE in the rotate-half
-vector form x*cos + rotate_half(x)*sin, numpy indexing of the pool viewed as
-[page][K|V][kv head][slot][d].  Only the BF16 storage of appended K/V is
-mirrored (rounded with torch's conversion), since the pool holds BF16.
+vector form x*cos + rotate_half(x)*sin, numpy indexing of the pool viewed
+per page as a K block [kv head][slot][d] and a V block [kv head][d][slot].
+Only the BF16 storage of appended K/V is mirrored (rounded with torch's
+conversion), since the pool holds BF16.
 """
 import numpy as np
 import torch
@@ -49,17 +50,21 @@ def softmax_attention(q, K, V, scale):
 
 
 def pool_view(pool, kv_heads, head_dim, page_tokens=16):
-    return np.asarray(pool).reshape(-1, 2, kv_heads, page_tokens, head_dim)
+    """Views (K [page][head][slot][d], V [page][head][d][slot]) of the pool."""
+    blk = kv_heads * page_tokens * head_dim
+    pages = np.asarray(pool).reshape(-1, 2 * blk)
+    return (pages[:, :blk].reshape(-1, kv_heads, page_tokens, head_dim),
+            pages[:, blk:].reshape(-1, kv_heads, head_dim, page_tokens))
 
 
 def gather(pool, kv_heads, head_dim, bt_row, n, page_tokens=16):
     """K, V [n, hkv, D] float64 of tokens 0..n-1."""
-    pv = pool_view(pool, kv_heads, head_dim, page_tokens)
+    kv, vv = pool_view(pool, kv_heads, head_dim, page_tokens)
     t = np.arange(n)
     pages = np.asarray(bt_row)[t // page_tokens]
     slots = t % page_tokens
-    K = bf16_bits_to_f64(pv[pages, 0, :, slots, :])
-    V = bf16_bits_to_f64(pv[pages, 1, :, slots, :])
+    K = bf16_bits_to_f64(kv[pages, :, slots, :])
+    V = bf16_bits_to_f64(vv[pages, :, :, slots])
     return K, V
 
 

@@ -285,9 +285,9 @@ def test_pool_append_matches_reshaped_view(pos):
     k = synth.to_bf16_bits(g.standard_normal(8 * 64).astype(np.float32))
     v = synth.to_bf16_bits(g.standard_normal(8 * 64).astype(np.float32))
     want = pool.copy()
-    pv = brute.pool_view(want, 8, 64)
-    pv[bt[pos // 16], 0, :, pos % 16, :] = k.reshape(8, 64)
-    pv[bt[pos // 16], 1, :, pos % 16, :] = v.reshape(8, 64)
+    kv, vv = brute.pool_view(want, 8, 64)
+    kv[bt[pos // 16], :, pos % 16, :] = k.reshape(8, 64)
+    vv[bt[pos // 16], :, :, pos % 16] = v.reshape(8, 64)
     got = pool.copy()
     oracle.pool_append(got, geo, bt, pos, k, v)
     assert np.array_equal(got, want)
