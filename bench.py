@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the gfx950 paged-KV GQA path (one GPU).
+
+Workload: one batched decode step of a Llama-3.2-1B-shaped model (hidden
+2048, 32 query / 8 kv heads, head_dim 64, SwiGLU 8192, 16 layers, tied
+128256-token embedding / LM head with FP32 logits and argmax) at batch 16,
+where the 16 sequences' attention lengths are the paged-attention
+workload's draw (lengths uniform in [1, 2048], seed 1002), so that every
+layer's attention call is exactly that workload.  Each (layer, sequence)
+keeps its pages scattered in one shared BF16 pool of 16-token pages sized
+to fit.  Weights N(0, 0.02) and cached K/V N(0, 1), BF16, seeded and
+synthetic.  A "step" is one decode_step call (every row of the hot path:
+embedding, 16 x [RMSNorm, QKV, RoPE, KV append, paged attention, O-proj +
+residual, RMSNorm, SwiGLU, down + residual], final norm, LM head, argmax),
+replayed from a HIP graph; inputs are resident in HBM before timing.
+
+Reported (one JSON line): decode tokens/s for the step; the paged
+attention kernel's achieved HBM GB/s against the 8 TB/s peak (its
+algorithmic bytes per launch over its average launch time, HIP events on
+its stream); the whole step's algorithmic bytes over the step time; and
+the CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --attention-only   (the attention launches alone, plus a
+                                      copy kernel of known size: the run
+                                      that rocprofv3 counters are taken on)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + paged-attn HBM GB/s (% of peak), Llama-1B shape, batch 16"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_attention_bench_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "paged_kv_transformer_amd", "csrc", "attention.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_bytes(lens, Hq, Hkv, q_bytes, D=64):
+    """Algorithmic bytes of one paged attention call: every attended token's
+    K and V (BF16), q in, FP32 out, one block-table entry per page."""
+    lens = np.asarray(lens, dtype=np.int64)
+    B = len(lens)
+    return int((lens * Hkv * D * 2 * 2).sum() + B * Hq * D * (q_bytes + 4) + ((lens + 15) // 16).sum() * 4)
+
+
+def step_bytes(shape, lens, logits=True):
+    """Algorithmic bytes of one decode step: weights once, each layer's
+    attention (FP32 q inside the layer), the appended K/V, the hidden state
+    in and out of each layer, the embedding rows, the LM head, the logits."""
+    B, H, V = len(lens), shape.hidden, shape.vocab
+    layer = (2 * (shape.layer_param_count())
+             + attention_bytes(lens, shape.heads, shape.kv_heads, 4)
+             + B * shape.kv_heads * shape.head_dim * 2 * 2 + 2 * B * H * 4)
+    return shape.layers * layer + B * H * 2 + 2 * V * H + H * 2 + (B * V * 4 if logits else 0)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(bytes_per_launch):
+    """HBM traffic per attention launch from the committed counter summary,
+    or None if it is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attention_source_sha") != source_sha(ATTN_SOURCE):
+        return None
+    return {"fetch_bytes": t["fetch_bytes_per_launch"], "write_bytes": t["write_bytes_per_launch"],
+            "total_bytes": t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"],
+            "ratio_to_algorithmic": (t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])
+            / bytes_per_launch,
+            "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+
+
+class Setup:
+    """Device-resident inputs of the workload."""
+
+    def __init__(self, torch, pkv, synth, with_host=False):
+        t0 = time.time()
+        wl = synth.bench_step()
+        shape = wl.shape
+        self.wl, self.shape = wl, shape
+        self.weights = synth.model_weights(shape, 1002)
+        log("inputs drawn in %.1fs (pool %d pages, %.0f MiB)" % (
+            time.time() - t0, wl.num_pages, wl.pool.nbytes / 2 ** 20))
+        self.max_pos = int(wl.positions.max()) + 1
+        self.cfg = pkv.make_config(shape, max_pos=self.max_pos)
+        self.model = pkv.upload_model(self.weights, shape.theta, self.max_pos)
+        self.pool_t = pkv.to_device(wl.pool)
+        self.pool = pkv.kv_pool_create(self.pool_t, shape.kv_heads)
+        self.bts = pkv.to_device(wl.block_tables)
+        self.pos = pkv.to_device(wl.positions)
+        self.tokens = pkv.to_device(wl.extra["tokens"])
+        B = wl.batch
+        self.logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
+        self.next = torch.empty(B, dtype=torch.int32, device="cuda")
+        self.ws = pkv.alloc_workspace(pkv.workspace_bytes(self.cfg, B, wl.max_pages))
+        torch.cuda.synchronize()
+        if not with_host:
+            self.weights = None
+
+    def step(self, pkv):
+        pkv.decode_step(self.cfg, self.model, self.pool, self.bts, self.pos, self.tokens, self.logits,
+                        self.next, self.ws)
+
+
+def time_attention(torch, pkv, synth, S, rounds, warmup):
+    """Per-launch times (ms) of the paged attention kernel over the step's
+    16 layers' block tables (distinct pages per layer), HIP events on its
+    stream around each launch."""
+    wl, shape = S.wl, S.shape
+    B = wl.batch
+    q = pkv.to_device(synth.bf16_normal(1002, "q", (B, shape.heads, shape.head_dim)))
+    lens = pkv.to_device(wl.lens)
+    out = torch.empty((B, shape.heads, shape.head_dim), dtype=torch.float32, device="cuda")
+    ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(shape.heads, shape.kv_heads, B, wl.max_pages))
+    bts = [S.bts[l].contiguous() for l in range(shape.layers)]
+    stream = torch.cuda.current_stream()
+
+    def launch(l):
+        pkv.paged_gqa_decode(S.pool, q, bts[l], lens, 0.125, out, ws, stream)
+
+    for _ in range(warmup):
+        for l in range(shape.layers):
+            launch(l)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(rounds * shape.layers)]
+    i = 0
+    for _ in range(rounds):
+        for l in range(shape.layers):
+            ev[i][0].record(stream)
+            launch(l)
+            ev[i][1].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    # back-to-back launches between two events (includes the launch gaps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(rounds):
+        for l in range(shape.layers):
+            launch(l)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b = e0.elapsed_time(e1) / (rounds * shape.layers)
+    assert pkv.device_error(ws) == 0
+    return per, b2b
+
+
+def cpu_baseline(S, seqs):
+    import oracle
+    wl = S.wl
+    geo = oracle.PoolGeometry(S.shape.kv_heads, S.shape.head_dim)
+    t0 = time.perf_counter()
+    _, nxt, _, _ = oracle.decode_step_paged(S.shape, S.weights, wl.pool, geo, wl.block_tables,
+                                            wl.positions, wl.extra["tokens"], seqs=seqs)
+    dt = time.perf_counter() - t0
+    return dt, nxt
+
+
+def attention_only(torch, pkv, synth, rounds):
+    """Launch sequence for the hardware-counter runs: the attention kernel
+    over the 16 layers' tables, then a copy of known size."""
+    S = Setup(torch, pkv, synth)
+    per, _ = time_attention(torch, pkv, synth, S, rounds, 1)
+    n = 256 << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    abytes = attention_bytes(S.wl.lens, S.shape.heads, S.shape.kv_heads, 2)
+    print("attention-only: %d launches, mean %.2f us, %d algorithmic bytes per launch; "
+          "copy calibration: 3 x %d bytes read + written" % (len(per), per.mean() * 1e3, abytes, n), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--attn-rounds", type=int, default=20)
+    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch the step directly, no HIP graph")
+    ap.add_argument("--attention-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only (the path runs on a single MI355X); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_transformer_amd as pkv
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.attention_only:
+        attention_only(torch, pkv, synth, args.attn_rounds)
+        return
+
+    S = Setup(torch, pkv, synth, with_host=not args.no_cpu_baseline)
+    shape, wl = S.shape, S.wl
+    B = wl.batch
+
+    # reference tokens from one eager step
+    S.step(pkv)
+    torch.cuda.synchronize()
+    assert pkv.device_error(S.ws) == 0
+    ref_next = S.next.clone()
+
+    if args.eager:
+        run = lambda: S.step(pkv)
+    else:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                S.step(pkv)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        run = graph.replay
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    log("step: %.3f ms (events), %.3f ms (wall)" % (ms, wall * 1e3 / args.steps))
+    assert pkv.device_error(S.ws) == 0
+    assert torch.equal(S.next, ref_next), "replayed steps changed the next tokens"
+
+    # paged attention kernel: achieved HBM rate against the peak
+    per, b2b = time_attention(torch, pkv, synth, S, args.attn_rounds, 3)
+    abytes = attention_bytes(wl.lens, shape.heads, shape.kv_heads, 2)
+    attn_ms = float(per.mean())
+    achieved = abytes / (attn_ms * 1e-3) / 1e9
+    log("attention: %.2f us per launch (events), %.2f us back-to-back, %.1f MB -> %.0f GB/s" % (
+        attn_ms * 1e3, b2b * 1e3, abytes / 1e6, achieved))
+    sbytes = step_bytes(shape, wl.lens)
+    step_gbs = sbytes / (ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(B / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) BF16 weights, N(0,1) BF16 KV pool, random page tables)",
+        "config": {
+            "workload": "llama-3.2-1b-shape 16-layer decode step, batch 16, attention lengths "
+                        "U[1,2048] (seed 1002 draw), 16-token pages scattered in one shared BF16 pool",
+            "batch": B, "layers": shape.layers, "hidden": shape.hidden, "heads": shape.heads,
+            "kv_heads": shape.kv_heads, "head_dim": shape.head_dim, "intermediate": shape.inter,
+            "vocab": shape.vocab, "context_lens": [int(x) for x in wl.lens],
+            "pool_pages": int(wl.num_pages), "page_tokens": 16, "hip_graph": not args.eager,
+        },
+        "roofline": {
+            "kernel": "paged_attention_kernel (paged_gqa_decode on each layer's tables)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(abytes),
+            "algorithmic_bytes_per_launch": abytes,
+            "avg_launch_us": round(attn_ms * 1e3, 3),
+            "back_to_back_us": round(b2b * 1e3, 3),
+            "launches": int(len(per)),
+        },
+        "step_roofline": {
+            "bound": "hbm", "algorithmic_bytes": int(sbytes), "achieved": round(step_gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        seqs = list(range(min(args.cpu_seqs, B)))
+        dt, nxt = cpu_baseline(S, seqs)
+        got = S.next.cpu().numpy()
+        log("oracle: %d sequences in %.1fs; tokens %s vs GPU %s" % (len(seqs), dt, nxt[seqs].tolist(),
+                                                                      got[seqs].tolist()))
+        result["cpu_baseline"] = {
+            "value": round(len(seqs) / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "the full 16-layer step (embedding, layers, LM head, argmax) for sequences %s "
+                      "of the batch, single-threaded FP32 C oracle; %.1f s" % (seqs, dt),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

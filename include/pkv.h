@@ -1,0 +1,250 @@
+/*
+ * pkv.h — C ABI of the MI355X (gfx950) paged-KV GQA decode path.
+ *
+ * The library computes the batched decode step of a Llama/Qwen-style
+ * grouped-query-attention decoder over one shared BF16 KV page pool, as the
+ * "Inference from Scratch" engine summary describes it (wpnews page "Hours
+ * of YouTube and 85 handtyped pages of notes on LLM Inference"): a shared
+ * BF16 page pool with 16 tokens of K and V per physical page and a block
+ * table per sequence and layer; decode appends each new token at its
+ * absolute RoPE position; direct paged decode attention with FP32 online
+ * softmax that streams each sequence's pages without gathering a contiguous
+ * prefix or storing scores; batched decode packing one token per active
+ * sequence; final RMSNorm, tied embedding / LM head to FP32 logits and GPU
+ * argmax.  The configuration fields are those of llmc's binary header
+ * (README of llmc, section "binary format v2", config header).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  BF16 data are
+ *     passed as uint16_t bit patterns.  All arrays are dense row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; no call synchronises except pkv_device_error.
+ *   - The caller owns every buffer (pool, weights, tables, activations,
+ *     logits, workspace).  The library allocates and frees nothing and keeps
+ *     no pointer after a call returns.  Buffers must stay alive until the
+ *     stream has passed the enqueued work.
+ *   - Errors are negative errno values, as in llmc's kernel-style convention
+ *     (README of llmc: every operator returns a negative errno on error):
+ *       0        success
+ *       -EINVAL  NULL pointer, bad shape, inconsistent sizes, misalignment
+ *       -ENOTSUP head_dim != 64, page_tokens != 16, or a size outside what
+ *                this version supports (stated per call)
+ *       -ENOSPC  pool smaller than one page, workspace too small
+ *       -EIO     the HIP runtime rejected a launch (the error is cleared)
+ *     Argument validation is host code that runs before any HIP call.
+ *   - Errors that only the device can see (a block-table entry outside
+ *     [0, num_pages), a position or length beyond the table or the RoPE
+ *     table, a token id outside the vocabulary) set bits of a sticky word in
+ *     the workspace (PKV_DEVERR_*); the offending page, token or sequence is
+ *     skipped and the corresponding outputs are unspecified.  Read and clear
+ *     the word with pkv_device_error.
+ *   - A workspace must be zero-initialised once (pkv_workspace_init) before
+ *     its first use; the kernels leave it ready for the next call.  Calls
+ *     that share a workspace must be ordered on one stream; calls on
+ *     different streams need different workspaces.
+ *
+ * Pool layout: physical page p starts at base + p * page_bytes and holds,
+ * as BF16, the K block [num_kv_heads][16 slots][head_dim] followed by the V
+ * block [num_kv_heads][head_dim][16 slots] (V transposed, so that a page of
+ * V is already the operand layout of the matrix cores).  page_bytes =
+ * 2 * num_kv_heads * 16 * head_dim * 2 (32 KiB for 8 kv heads, 8 KiB for 2).
+ * Token t of a sequence lives in logical page t / 16, slot t % 16; the
+ * sequence's block-table row maps the logical page to a physical page.
+ * Block tables are int32 [batch][max_pages] per layer; decode_step takes
+ * them layer-major, [num_layers][batch][max_pages].  Entries past a
+ * sequence's last page are never read.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_PAGE_TOKENS 16
+#define PKV_HEAD_DIM 64
+#define PKV_MAX_BATCH_TILE 128
+
+/* Sticky device-error bits (pkv_device_error). */
+#define PKV_DEVERR_PAGE 1u      /* block-table entry outside [0, num_pages) */
+#define PKV_DEVERR_LENGTH 2u    /* length / position beyond max_pages * 16  */
+#define PKV_DEVERR_ROPE 4u      /* position >= max_position_embeddings      */
+#define PKV_DEVERR_TOKEN 8u     /* token id outside [0, vocab_size)         */
+
+/* Model configuration: the config-header fields of llmc's binary format. */
+typedef struct pkv_config {
+	int32_t hidden_size;             /* H, multiple of 64                  */
+	int32_t num_hidden_layers;       /* layers (decode_step)              */
+	int32_t num_attention_heads;     /* Hq                                 */
+	int32_t num_key_value_heads;     /* Hkv, divides Hq                    */
+	int32_t head_dim;                /* D, must be 64                      */
+	int32_t intermediate_size;       /* I, multiple of 64                  */
+	int32_t vocab_size;              /* V (decode_step)                    */
+	int32_t max_position_embeddings; /* rows of the RoPE cos/sin tables    */
+	float rope_theta;                /* RoPE base                          */
+	float rms_norm_eps;              /* RMSNorm epsilon (inside the root)  */
+} pkv_config;
+
+/* A view of a caller-allocated device buffer as a page pool (no ownership). */
+typedef struct pkv_pool {
+	void *base;           /* device, 256-byte aligned                         */
+	int64_t bytes;        /* size of the buffer                               */
+	int64_t page_bytes;   /* 2 * num_kv_heads * page_tokens * head_dim * 2    */
+	int32_t num_pages;    /* floor(bytes / page_bytes)                        */
+	int32_t page_tokens;  /* 16                                               */
+	int32_t num_kv_heads; /* Hkv                                              */
+	int32_t head_dim;     /* 64                                               */
+} pkv_pool;
+
+/*
+ * One layer's weights, BF16, row-major [out][in] (the Hugging Face
+ * orientation), no biases:
+ *   attn_norm [H], mlp_norm [H]                  RMSNorm weights
+ *   w_qkv     [(Hq + 2 Hkv) * D][H]              q rows, then k rows, then v rows
+ *   w_o       [H][Hq * D]
+ *   w_gate_up [2 I][H]                           gate rows, then up rows
+ *   w_down    [H][I]
+ */
+typedef struct pkv_layer_weights {
+	const uint16_t *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate_up, *w_down;
+} pkv_layer_weights;
+
+/*
+ * Whole-model weights.  embed [V][H] BF16 is also the LM head (tied).
+ * layers is a HOST array of num_hidden_layers entries.  rope_cos/rope_sin
+ * are device FP32 tables [max_position_embeddings][D/2] (pkv_rope_table).
+ */
+typedef struct pkv_model_weights {
+	const uint16_t *embed, *final_norm;
+	const pkv_layer_weights *layers;
+	const float *rope_cos, *rope_sin;
+} pkv_model_weights;
+
+/*
+ * kv_pool_create — describe a caller-owned device buffer as a page pool
+ * (the engine's shared BF16 page pool sized in bytes, its --kv-cache-mib
+ * option).  No device work, no allocation; `out` is a host struct.
+ * Errors: -EINVAL (NULL, misaligned base, bytes < 0, num_kv_heads < 1),
+ * -ENOTSUP (head_dim != 64 or page_tokens != 16), -ENOSPC (less than one
+ * page, or more than INT32_MAX pages).
+ */
+int kv_pool_create(void *dev_base, int64_t bytes, int32_t num_kv_heads,
+		   int32_t head_dim, int32_t page_tokens, pkv_pool *out);
+
+/*
+ * kv_append — write one new token's K and V per sequence into the pool at
+ * its absolute position (decode appends one token at its RoPE position).
+ *   block_table [batch][max_pages] int32, positions [batch] int32,
+ *   k_new, v_new [batch][Hkv][D] BF16.
+ * Sequence b writes slot positions[b] % 16 of physical page
+ * block_table[b][positions[b] / 16].  Bit-exact copy of the given values.
+ * batch == 0 is a no-op.  Errors: -EINVAL, -ENOTSUP, -EIO; device errors
+ * PKV_DEVERR_PAGE / PKV_DEVERR_LENGTH (that sequence is skipped).
+ */
+int kv_append(const pkv_pool *pool, const int32_t *block_table,
+	      int32_t max_pages, const int32_t *positions,
+	      const uint16_t *k_new, const uint16_t *v_new, int32_t batch,
+	      void *stream);
+
+/*
+ * paged_gqa_decode — direct paged decode attention with FP32 online softmax
+ * (the engine's "direct paged decode attention": each query head streams
+ * its sequence's cached pages and accumulates weighted values without
+ * gathering a contiguous prefix or storing attention scores).
+ *   q [batch][num_q_heads][D] BF16, context_lens [batch] int32 (tokens
+ *   0..n-1 are attended), out [batch][num_q_heads][D] FP32.
+ * Query head h reads kv head h / (num_q_heads / Hkv).  For every head:
+ *   out = sum_t softmax_t(scale * q.K_t) V_t  over t < n.
+ * n == 0 gives zeros.  The result does not depend on where the pages lie
+ * in the pool (work is split on logical pages).  workspace: at least
+ * pkv_attention_workspace_bytes(...) bytes, initialised once.
+ * Errors: -EINVAL (NULL, Hq % Hkv != 0, batch < 0, max_pages < 1),
+ * -ENOTSUP (Hq / Hkv > 16), -ENOSPC (workspace), -EIO; device errors
+ * PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH.
+ */
+int paged_gqa_decode(const pkv_pool *pool, const uint16_t *q,
+		     int32_t num_q_heads, const int32_t *block_table,
+		     int32_t max_pages, const int32_t *context_lens,
+		     int32_t batch, float scale, float *out, void *workspace,
+		     size_t ws_bytes, void *stream);
+
+/*
+ * decoder_layer_decode — one decoder layer for a batch of sequences, each
+ * with one new token at positions[b] (tokens 0..positions[b]-1 already in
+ * the pool).  In order (the engine's layer op list):
+ *   xn = RMSNorm(x) * attn_norm;  [q;k;v] = W_qkv xn;  RoPE on q and k at
+ *   positions[b] (pairs (j, j + D/2), angle positions[b] * theta^(-2j/D),
+ *   cos/sin read from the tables);  append BF16(k), BF16(v) at
+ *   positions[b];  o = attention over 0..positions[b];  h1 = x + W_o o;
+ *   hn = RMSNorm(h1) * mlp_norm;  a = silu(gate) * up with [gate; up] =
+ *   W_gate_up hn;  x <- h1 + W_down a.
+ *   hidden [batch][H] FP32, in/out.  block_table: this layer's
+ *   [batch][max_pages].  rope_cos/rope_sin [max_position_embeddings][D/2].
+ * Contractions accumulate in FP32 with FP32 activations (split into two
+ * BF16 halves for the matrix cores).  Errors: as paged_gqa_decode plus
+ * -ENOTSUP (H or I not a multiple of 64); device errors PKV_DEVERR_PAGE,
+ * PKV_DEVERR_LENGTH, PKV_DEVERR_ROPE.
+ */
+int decoder_layer_decode(const pkv_config *cfg, const pkv_layer_weights *w,
+			 const float *rope_cos, const float *rope_sin,
+			 const pkv_pool *pool, const int32_t *block_table,
+			 int32_t max_pages, const int32_t *positions,
+			 int32_t batch, float *hidden, void *workspace,
+			 size_t ws_bytes, void *stream);
+
+/*
+ * decode_step — the whole batched decode step: x = embed[token_ids[b]]
+ * (BF16 widened to FP32), every layer as decoder_layer_decode with
+ * block_tables[l], then the final RMSNorm, the tied LM head
+ * logits = embed . xn in FP32, and next_tokens[b] = argmax (lowest index
+ * among equal maxima).
+ *   block_tables [num_layers][batch][max_pages], positions [batch],
+ *   token_ids [batch], logits [batch][V] FP32 or NULL (not written),
+ *   next_tokens [batch] int32.
+ * Errors: as decoder_layer_decode; device error PKV_DEVERR_TOKEN too.
+ */
+int decode_step(const pkv_config *cfg, const pkv_model_weights *w,
+		const pkv_pool *pool, const int32_t *block_tables,
+		int32_t max_pages, const int32_t *positions,
+		const int32_t *token_ids, int32_t batch, float *logits,
+		int32_t *next_tokens, void *workspace, size_t ws_bytes,
+		void *stream);
+
+/* Workspace bytes decoder_layer_decode / decode_step need (0 on bad args). */
+size_t pkv_workspace_bytes(const pkv_config *cfg, int32_t batch,
+			   int32_t max_pages);
+
+/* Workspace bytes paged_gqa_decode needs (0 on bad args). */
+size_t pkv_attention_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads,
+				     int32_t head_dim, int32_t batch,
+				     int32_t max_pages);
+
+/* Zero a workspace with a fill kernel (no memset node; graph-safe). */
+int pkv_workspace_init(void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * pkv_rope_table — fill cos/sin [max_pos][D/2] FP32 on the device with
+ * cos(p * theta^(-2j/D)) and sin(...) evaluated in double and rounded to
+ * FP32 (the article's RoPE section precomputes such tables once; here in
+ * FP32 rather than FP16).  Errors: -EINVAL, -ENOTSUP (D != 64), -EIO.
+ */
+int pkv_rope_table(float theta, int32_t head_dim, int32_t max_pos,
+		   float *cos_out, float *sin_out, void *stream);
+
+/*
+ * pkv_device_error — synchronise `stream`, return the sticky device-error
+ * bits (>= 0) of the workspace and clear them; -EINVAL / -EIO on failure.
+ */
+int pkv_device_error(void *workspace, void *stream);
+
+/* Library version string (host). */
+const char *pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

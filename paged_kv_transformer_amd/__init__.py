@@ -1,0 +1,275 @@
+"""Paged-KV GQA decode on MI355X (gfx950): ctypes binding of libpkv.so.
+
+The binding only marshals arguments into the C ABI of ``include/pkv.h``:
+torch supplies device memory and the stream, every step of the computation
+runs in the library's HIP kernels.  There is no fallback: if ``libpkv.so``
+is missing the first call raises.
+
+Entry points (same names as the C ABI): ``kv_pool_create``, ``kv_append``,
+``paged_gqa_decode``, ``decoder_layer_decode``, ``decode_step``, plus
+``workspace_bytes``, ``attention_workspace_bytes``, ``workspace_init``,
+``rope_table`` and ``device_error``.
+"""
+import ctypes
+import errno
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PAGE_TOKENS = 16
+HEAD_DIM = 64
+DEVERR_PAGE, DEVERR_LENGTH, DEVERR_ROPE, DEVERR_TOKEN = 1, 2, 4, 8
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn, rc):
+        self.rc = rc
+        name = errno.errorcode.get(-rc, str(rc))
+        super().__init__("%s failed: -%s (%d)" % (fn, name, rc))
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden_size", ctypes.c_int32), ("num_hidden_layers", ctypes.c_int32),
+                ("num_attention_heads", ctypes.c_int32), ("num_key_value_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("intermediate_size", ctypes.c_int32),
+                ("vocab_size", ctypes.c_int32), ("max_position_embeddings", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rms_norm_eps", ctypes.c_float)]
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("bytes", ctypes.c_int64), ("page_bytes", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")]
+
+
+class ModelWeights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(LayerWeights)),
+                ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p)]
+
+
+LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
+
+_lib = None
+
+
+def lib():
+    """The loaded library with argument types set (raw calls return rc)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpkv.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        PP = ctypes.POINTER(Pool)
+        sigs = {
+            "kv_pool_create": (ctypes.c_int, [P, I64, I32, I32, I32, PP]),
+            "kv_append": (ctypes.c_int, [PP, P, I32, P, P, P, I32, P]),
+            "paged_gqa_decode": (ctypes.c_int, [PP, P, I32, P, I32, P, I32, F, P, P, SZ, P]),
+            "decoder_layer_decode": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(LayerWeights),
+                                                    P, P, PP, P, I32, P, I32, P, P, SZ, P]),
+            "decode_step": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights), PP, P,
+                                           I32, P, P, I32, P, P, P, SZ, P]),
+            "pkv_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32]),
+            "pkv_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+            "pkv_workspace_init": (ctypes.c_int, [P, SZ, P]),
+            "pkv_rope_table": (ctypes.c_int, [F, I32, I32, P, P, P]),
+            "pkv_device_error": (ctypes.c_int, [P, P]),
+            "pkv_version": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, rc):
+    if rc < 0:
+        raise PkvError(fn, rc)
+    return rc
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
+_BF16_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dev(t, dtypes, what):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % what)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % what)
+    if t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (what, t.dtype, dtypes))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    return t.data_ptr()
+
+
+def make_config(shape, max_pos=None, layers=None):
+    """Config from any object with the llmc header fields' meaning
+    (hidden, layers, heads, kv_heads, head_dim, inter, vocab, max_pos,
+    theta, eps)."""
+    return Config(shape.hidden, shape.layers if layers is None else layers, shape.heads,
+                  shape.kv_heads, shape.head_dim, shape.inter, shape.vocab,
+                  shape.max_pos if max_pos is None else max_pos, shape.theta, shape.eps)
+
+
+# ------------------------------------------------------------------ pool ---
+
+def kv_pool_create(pool_tensor, num_kv_heads, head_dim=HEAD_DIM, page_tokens=PAGE_TOKENS):
+    """Describe a device tensor (any dtype) as a page pool; returns a Pool."""
+    if pool_tensor.device.type != "cuda" or not pool_tensor.is_contiguous():
+        raise ValueError("pool must be a contiguous GPU tensor")
+    out = Pool()
+    nbytes = pool_tensor.numel() * pool_tensor.element_size()
+    _check("kv_pool_create", lib().kv_pool_create(pool_tensor.data_ptr(), nbytes, num_kv_heads,
+                                                  head_dim, page_tokens, ctypes.byref(out)))
+    out._tensor = pool_tensor
+    return out
+
+
+def kv_append(pool, block_table, positions, k_new, v_new, stream=None):
+    B = positions.numel()
+    bt = _dev(block_table, (torch.int32,), "block_table")
+    _check("kv_append", lib().kv_append(
+        ctypes.byref(pool), bt, block_table.shape[-1], _dev(positions, (torch.int32,), "positions"),
+        _dev(k_new, _BF16_DTYPES, "k_new"), _dev(v_new, _BF16_DTYPES, "v_new"), B, _stream(stream)))
+
+
+# ------------------------------------------------------------- workspace ---
+
+def attention_workspace_bytes(num_q_heads, num_kv_heads, batch, max_pages, head_dim=HEAD_DIM):
+    return lib().pkv_attention_workspace_bytes(num_q_heads, num_kv_heads, head_dim, batch, max_pages)
+
+
+def workspace_bytes(cfg, batch, max_pages):
+    return lib().pkv_workspace_bytes(ctypes.byref(cfg), batch, max_pages)
+
+
+def alloc_workspace(nbytes, device="cuda", stream=None):
+    """A zero-initialised workspace tensor of at least nbytes (uint8)."""
+    ws = torch.empty(max(256, (nbytes + 255) // 256 * 256), dtype=torch.uint8, device=device)
+    workspace_init(ws, stream)
+    return ws
+
+
+def workspace_init(ws, stream=None):
+    _check("pkv_workspace_init", lib().pkv_workspace_init(
+        _dev(ws, (torch.uint8,), "workspace"), ws.numel(), _stream(stream)))
+
+
+def device_error(ws, stream=None):
+    return _check("pkv_device_error", lib().pkv_device_error(
+        _dev(ws, (torch.uint8,), "workspace"), _stream(stream)))
+
+
+def rope_table(theta, max_pos, head_dim=HEAD_DIM, device="cuda", stream=None):
+    """(cos, sin) FP32 [max_pos, head_dim/2] computed by the library's kernel."""
+    c = torch.empty((max_pos, head_dim // 2), dtype=torch.float32, device=device)
+    s = torch.empty_like(c)
+    _check("pkv_rope_table", lib().pkv_rope_table(theta, head_dim, max_pos, c.data_ptr(),
+                                                  s.data_ptr(), _stream(stream)))
+    return c, s
+
+
+# ------------------------------------------------------------- attention ---
+
+def paged_gqa_decode(pool, q, block_table, context_lens, scale, out, workspace, stream=None):
+    """q [B, Hq, 64] BF16, block_table [B, max_pages] int32, context_lens [B]
+    int32, out [B, Hq, 64] FP32 (written)."""
+    B, Hq = q.shape[0], q.shape[1]
+    _check("paged_gqa_decode", lib().paged_gqa_decode(
+        ctypes.byref(pool), _dev(q, _BF16_DTYPES, "q"), Hq,
+        _dev(block_table, (torch.int32,), "block_table"), block_table.shape[-1],
+        _dev(context_lens, (torch.int32,), "context_lens"), B, scale,
+        _dev(out, (torch.float32,), "out"), _dev(workspace, (torch.uint8,), "workspace"),
+        workspace.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- layers ---
+
+class DeviceLayer:
+    """One layer's device weights and the C struct pointing at them."""
+
+    def __init__(self, tensors):
+        self.tensors = {k: tensors[k] for k in LAYER_KEYS}
+        for k, t in self.tensors.items():
+            _dev(t, _BF16_DTYPES, k)
+        self.c = LayerWeights(*[self.tensors[k].data_ptr() for k in LAYER_KEYS])
+
+
+class DeviceModel:
+    """Whole-model device weights (embed, final_norm, layers, RoPE tables)."""
+
+    def __init__(self, embed, final_norm, layers, rope_cos, rope_sin):
+        self.embed, self.final_norm = embed, final_norm
+        self.layers = [l if isinstance(l, DeviceLayer) else DeviceLayer(l) for l in layers]
+        self.rope_cos, self.rope_sin = rope_cos, rope_sin
+        self._arr = (LayerWeights * len(self.layers))(*[l.c for l in self.layers])
+        self.c = ModelWeights(_dev(embed, _BF16_DTYPES, "embed"), _dev(final_norm, _BF16_DTYPES, "final_norm"),
+                              ctypes.cast(self._arr, ctypes.POINTER(LayerWeights)),
+                              _dev(rope_cos, (torch.float32,), "rope_cos"),
+                              _dev(rope_sin, (torch.float32,), "rope_sin"))
+
+
+def decoder_layer_decode(cfg, layer, rope_cos, rope_sin, pool, block_table, positions, hidden,
+                         workspace, stream=None):
+    """hidden [B, H] FP32 is updated in place; block_table [B, max_pages]."""
+    B = positions.numel()
+    _check("decoder_layer_decode", lib().decoder_layer_decode(
+        ctypes.byref(cfg), ctypes.byref(layer.c), _dev(rope_cos, (torch.float32,), "rope_cos"),
+        _dev(rope_sin, (torch.float32,), "rope_sin"), ctypes.byref(pool),
+        _dev(block_table, (torch.int32,), "block_table"), block_table.shape[-1],
+        _dev(positions, (torch.int32,), "positions"), B, _dev(hidden, (torch.float32,), "hidden"),
+        _dev(workspace, (torch.uint8,), "workspace"), workspace.numel(), _stream(stream)))
+
+
+def decode_step(cfg, model, pool, block_tables, positions, token_ids, logits, next_tokens,
+                workspace, stream=None):
+    """block_tables [L, B, max_pages]; logits [B, V] FP32 or None."""
+    B = positions.numel()
+    _check("decode_step", lib().decode_step(
+        ctypes.byref(cfg), ctypes.byref(model.c), ctypes.byref(pool),
+        _dev(block_tables, (torch.int32,), "block_tables"), block_tables.shape[-1],
+        _dev(positions, (torch.int32,), "positions"), _dev(token_ids, (torch.int32,), "token_ids"), B,
+        None if logits is None else _dev(logits, (torch.float32,), "logits"),
+        _dev(next_tokens, (torch.int32,), "next_tokens"), _dev(workspace, (torch.uint8,), "workspace"),
+        workspace.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------- host -> device ---
+
+def to_device(a, device="cuda"):
+    """numpy array -> contiguous device tensor (uint16 BF16 bits -> int16)."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def upload_layer(lw, device="cuda"):
+    return DeviceLayer({k: to_device(lw[k], device) for k in LAYER_KEYS})
+
+
+def upload_model(weights, theta, max_pos, device="cuda"):
+    """weights: {'embed', 'final_norm', 'layers': [layer dicts]} of BF16 bits."""
+    c, s = rope_table(theta, max_pos, device=device)
+    return DeviceModel(to_device(weights["embed"], device), to_device(weights["final_norm"], device),
+                       [upload_layer(lw, device) for lw in weights["layers"]], c, s)

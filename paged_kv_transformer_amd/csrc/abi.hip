@@ -1,0 +1,387 @@
+// Host side of the C ABI declared in include/pkv.h: argument validation
+// (pure host code, run before any HIP call), workspace carving and the
+// launch sequence of each entry point.  Every step of the computation runs
+// in the kernels of attention.hip, gemm.hip and misc.hip.
+#include <errno.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pkv.h"
+#include "pkv_dev.h"
+
+using namespace pkv;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_pool(const pkv_pool* p) {
+  if (!p || !p->base) return -EINVAL;
+  if (p->head_dim != kHeadDim || p->page_tokens != kPageTokens) return -ENOTSUP;
+  if (p->num_kv_heads < 1 || p->num_pages < 1 || p->bytes < 0) return -EINVAL;
+  if (p->page_bytes != 2LL * p->num_kv_heads * kPageTokens * kHeadDim * 2) return -EINVAL;
+  if ((int64_t)p->num_pages * p->page_bytes > p->bytes) return -EINVAL;
+  if (!aligned(p->base, 256)) return -EINVAL;
+  return 0;
+}
+
+int check_heads(int32_t Hq, int32_t Hkv) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return -EINVAL;
+  if (Hq / Hkv > kMaxGroup) return -ENOTSUP;
+  return 0;
+}
+
+int check_cfg(const pkv_config* c) {
+  if (!c) return -EINVAL;
+  if (c->head_dim != kHeadDim) return -ENOTSUP;
+  int rc = check_heads(c->num_attention_heads, c->num_key_value_heads);
+  if (rc) return rc;
+  if (c->hidden_size < 1 || c->intermediate_size < 1 || c->max_position_embeddings < 1)
+    return -EINVAL;
+  if (c->hidden_size % 64 != 0 || c->intermediate_size % 64 != 0) return -ENOTSUP;
+  if (!(c->rms_norm_eps >= 0.f) || !isfinite(c->rms_norm_eps)) return -EINVAL;
+  if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return -EINVAL;
+  return 0;
+}
+
+int check_layer_weights(const pkv_layer_weights* w) {
+  if (!w || !w->attn_norm || !w->w_qkv || !w->w_o || !w->mlp_norm || !w->w_gate_up || !w->w_down)
+    return -EINVAL;
+  return 0;
+}
+
+int io(hipError_t e) {
+  if (e == hipSuccess) return 0;
+  (void)hipGetLastError();
+  return -EIO;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+// Common checks of decoder_layer_decode / decode_step.
+int check_layer_call(const pkv_config* cfg, const pkv_pool* pool, const float* rope_cos,
+                     const float* rope_sin, const int32_t* bt, int32_t max_pages,
+                     const int32_t* positions, int32_t batch, void* ws, size_t ws_bytes) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  rc = check_pool(pool);
+  if (rc) return rc;
+  if (pool->num_kv_heads != cfg->num_key_value_heads) return -EINVAL;
+  if (batch < 0 || max_pages < 1) return -EINVAL;
+  if (batch > 65535) return -ENOTSUP;
+  if (!rope_cos || !rope_sin || !bt || !positions || !ws) return -EINVAL;
+  if (!aligned(ws, 256)) return -EINVAL;
+  const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
+                               cfg->num_key_value_heads, cfg->intermediate_size,
+                               cfg->vocab_size, max_pages, true);
+  if (ws_bytes < L.total) return -ENOSPC;
+  return 0;
+}
+
+// Launch one projection over the batch in chunks of kGemmMaxCols columns;
+// `setup(a, b0)` points the per-chunk arguments at columns b0...
+template <typename F>
+int gemm_batched(int epi, int N, int batch, const GemmArgs& base, F setup, hipStream_t st) {
+  for (int b0 = 0; b0 < batch; b0 += kGemmMaxCols) {
+    const int bc = batch - b0 < kGemmMaxCols ? batch - b0 : kGemmMaxCols;
+    GemmArgs a = base;
+    a.B = bc;
+    setup(a, b0);
+    if (int rc = io(launch_gemm(epi, a, plan_gemm(epi, N, bc), st))) return rc;
+  }
+  return 0;
+}
+
+// One decoder layer over the whole batch, hidden [batch][H] in place.
+int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* rope_cos,
+              const float* rope_sin, const pkv_pool* pool, const int32_t* bt, int32_t max_pages,
+              const int32_t* pos, int32_t batch, float* hidden, void* ws, const WsLayout& L,
+              hipStream_t st) {
+  const int H = cfg->hidden_size, Hq = cfg->num_attention_heads;
+  const int Hkv = cfg->num_key_value_heads, I = cfg->intermediate_size;
+  float* q = at<float>(ws, L.q);
+  float* o = at<float>(ws, L.o);
+  float* h1 = at<float>(ws, L.h1);
+  float* act = at<float>(ws, L.act);
+  uint32_t* err = at<uint32_t>(ws, L.err);
+  int rc;
+
+  GemmArgs base{};
+  base.eps = cfg->rms_norm_eps;
+  base.err = err;
+
+  // 1. RMSNorm + QKV + RoPE + KV append
+  {
+    GemmArgs a = base;
+    a.W = w->w_qkv;
+    a.xw = w->attn_norm;
+    a.N = (Hq + 2 * Hkv) * kHeadDim;
+    a.K = H;
+    a.pool = (uint16_t*)pool->base;
+    a.page_elems = pool->page_bytes / 2;
+    a.num_pages = pool->num_pages;
+    a.bt_stride = max_pages;
+    a.rcos = rope_cos;
+    a.rsin = rope_sin;
+    a.max_pos = cfg->max_position_embeddings;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    rc = gemm_batched(EPI_QKV, a.N, batch, a, [&](GemmArgs& c, int b0) {
+      c.X = hidden + (size_t)b0 * H;
+      c.q_out = q + (size_t)b0 * Hq * kHeadDim;
+      c.bt = bt + (size_t)b0 * max_pages;
+      c.pos = pos + b0;
+    }, st);
+    if (rc) return rc;
+  }
+
+  // 2. paged attention over tokens 0..pos
+  {
+    AttnArgs a{};
+    a.q = q;
+    a.pool = (const uint16_t*)pool->base;
+    a.page_elems = pool->page_bytes / 2;
+    a.num_pages = pool->num_pages;
+    a.bt = bt;
+    a.bt_stride = max_pages;
+    a.lens = pos;
+    a.len_add = 1;
+    a.scale = 1.0f / sqrtf((float)kHeadDim);
+    a.out = o;
+    a.part = at<float>(ws, L.attn_part);
+    a.err = err;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.max_splits = attn_max_splits(max_pages);
+    if ((rc = io(launch_attention(a, batch, false, st)))) return rc;
+  }
+
+  // 3. output projection + residual: h1 = x + W_o o
+  {
+    GemmArgs a = base;
+    a.W = w->w_o;
+    a.N = H;
+    a.K = Hq * kHeadDim;
+    rc = gemm_batched(EPI_RESID, H, batch, a, [&](GemmArgs& c, int b0) {
+      c.X = o + (size_t)b0 * Hq * kHeadDim;
+      c.out = h1 + (size_t)b0 * H;
+      c.resid = hidden + (size_t)b0 * H;
+    }, st);
+    if (rc) return rc;
+  }
+
+  // 4. RMSNorm + gate/up + SwiGLU
+  {
+    GemmArgs a = base;
+    a.W = w->w_gate_up;
+    a.xw = w->mlp_norm;
+    a.N = 2 * I;
+    a.K = H;
+    a.I = I;
+    rc = gemm_batched(EPI_SWIGLU, 2 * I, batch, a, [&](GemmArgs& c, int b0) {
+      c.X = h1 + (size_t)b0 * H;
+      c.act = act + (size_t)b0 * I;
+    }, st);
+    if (rc) return rc;
+  }
+
+  // 5. down projection + residual: x = h1 + W_down a
+  {
+    GemmArgs a = base;
+    a.W = w->w_down;
+    a.N = H;
+    a.K = I;
+    rc = gemm_batched(EPI_RESID, H, batch, a, [&](GemmArgs& c, int b0) {
+      c.X = act + (size_t)b0 * I;
+      c.out = hidden + (size_t)b0 * H;
+      c.resid = h1 + (size_t)b0 * H;
+    }, st);
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+int kv_pool_create(void* dev_base, int64_t bytes, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t page_tokens, pkv_pool* out) {
+  if (!out || !dev_base || bytes < 0 || num_kv_heads < 1) return -EINVAL;
+  if (!aligned(dev_base, 256)) return -EINVAL;
+  if (head_dim != kHeadDim || page_tokens != kPageTokens) return -ENOTSUP;
+  const int64_t page_bytes = 2LL * num_kv_heads * page_tokens * head_dim * 2;
+  const int64_t pages = bytes / page_bytes;
+  if (pages < 1 || pages > INT32_MAX) return -ENOSPC;
+  out->base = dev_base;
+  out->bytes = bytes;
+  out->page_bytes = page_bytes;
+  out->num_pages = (int32_t)pages;
+  out->page_tokens = page_tokens;
+  out->num_kv_heads = num_kv_heads;
+  out->head_dim = head_dim;
+  return 0;
+}
+
+int kv_append(const pkv_pool* pool, const int32_t* block_table, int32_t max_pages,
+              const int32_t* positions, const uint16_t* k_new, const uint16_t* v_new,
+              int32_t batch, void* stream) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  if (batch < 0 || max_pages < 1) return -EINVAL;
+  if (batch == 0) return 0;
+  if (!block_table || !positions || !k_new || !v_new) return -EINVAL;
+  return io(launch_kv_append((uint16_t*)pool->base, pool->page_bytes / 2, pool->num_pages,
+                             block_table, max_pages, positions, k_new, v_new, batch,
+                             pool->num_kv_heads, (hipStream_t)stream));
+}
+
+size_t pkv_attention_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t batch, int32_t max_pages) {
+  if (check_heads(num_q_heads, num_kv_heads) || head_dim != kHeadDim || batch < 0 ||
+      max_pages < 1)
+    return 0;
+  return ws_layout(batch, 0, num_q_heads, num_kv_heads, 0, 0, max_pages, false).total;
+}
+
+size_t pkv_workspace_bytes(const pkv_config* cfg, int32_t batch, int32_t max_pages) {
+  if (check_cfg(cfg) || batch < 0 || max_pages < 1) return 0;
+  return ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads, cfg->num_key_value_heads,
+                   cfg->intermediate_size, cfg->vocab_size, max_pages, true)
+      .total;
+}
+
+int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_heads,
+                     const int32_t* block_table, int32_t max_pages, const int32_t* context_lens,
+                     int32_t batch, float scale, float* out, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  rc = check_heads(num_q_heads, pool->num_kv_heads);
+  if (rc) return rc;
+  if (batch < 0 || max_pages < 1) return -EINVAL;
+  if (batch > 65535) return -ENOTSUP;
+  if (batch == 0) return 0;
+  if (!q || !block_table || !context_lens || !out || !workspace) return -EINVAL;
+  if (!aligned(workspace, 256) || !isfinite(scale)) return -EINVAL;
+  const WsLayout L = ws_layout(batch, 0, num_q_heads, pool->num_kv_heads, 0, 0, max_pages, false);
+  if (ws_bytes < L.total) return -ENOSPC;
+  AttnArgs a{};
+  a.q = q;
+  a.pool = (const uint16_t*)pool->base;
+  a.page_elems = pool->page_bytes / 2;
+  a.num_pages = pool->num_pages;
+  a.bt = block_table;
+  a.bt_stride = max_pages;
+  a.lens = context_lens;
+  a.len_add = 0;
+  a.scale = scale;
+  a.out = out;
+  a.part = at<float>(workspace, L.attn_part);
+  a.err = at<uint32_t>(workspace, L.err);
+  a.Hq = num_q_heads;
+  a.Hkv = pool->num_kv_heads;
+  a.G = num_q_heads / pool->num_kv_heads;
+  a.max_splits = attn_max_splits(max_pages);
+  return io(launch_attention(a, batch, true, (hipStream_t)stream));
+}
+
+int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
+                         const float* rope_cos, const float* rope_sin, const pkv_pool* pool,
+                         const int32_t* block_table, int32_t max_pages, const int32_t* positions,
+                         int32_t batch, float* hidden, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  int rc = check_layer_call(cfg, pool, rope_cos, rope_sin, block_table, max_pages, positions,
+                            batch, workspace, ws_bytes);
+  if (rc) return rc;
+  rc = check_layer_weights(w);
+  if (rc) return rc;
+  if (!hidden) return -EINVAL;
+  if (batch == 0) return 0;
+  const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
+                               cfg->num_key_value_heads, cfg->intermediate_size,
+                               cfg->vocab_size, max_pages, true);
+  return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, positions, batch,
+                   hidden, workspace, L, (hipStream_t)stream);
+}
+
+int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* pool,
+                const int32_t* block_tables, int32_t max_pages, const int32_t* positions,
+                const int32_t* token_ids, int32_t batch, float* logits, int32_t* next_tokens,
+                void* workspace, size_t ws_bytes, void* stream) {
+  if (!w) return -EINVAL;
+  int rc = check_layer_call(cfg, pool, w->rope_cos, w->rope_sin, block_tables, max_pages,
+                            positions, batch, workspace, ws_bytes);
+  if (rc) return rc;
+  if (cfg->num_hidden_layers < 1 || cfg->vocab_size < 1) return -EINVAL;
+  if (!w->embed || !w->final_norm || !w->layers || !token_ids || !next_tokens) return -EINVAL;
+  for (int l = 0; l < cfg->num_hidden_layers; ++l) {
+    rc = check_layer_weights(&w->layers[l]);
+    if (rc) return rc;
+  }
+  if (batch == 0) return 0;
+  const hipStream_t st = (hipStream_t)stream;
+  const int H = cfg->hidden_size, V = cfg->vocab_size;
+  const WsLayout L = ws_layout(batch, H, cfg->num_attention_heads, cfg->num_key_value_heads,
+                               cfg->intermediate_size, V, max_pages, true);
+  float* x = at<float>(workspace, L.x);
+  uint32_t* err = at<uint32_t>(workspace, L.err);
+
+  if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, batch, err, st)))) return rc;
+  for (int l = 0; l < cfg->num_hidden_layers; ++l) {
+    rc = run_layer(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool,
+                   block_tables + (size_t)l * batch * max_pages, max_pages, positions, batch, x,
+                   workspace, L, st);
+    if (rc) return rc;
+  }
+  GemmArgs a{};
+  a.W = w->embed;
+  a.xw = w->final_norm;
+  a.N = V;
+  a.K = H;
+  a.eps = cfg->rms_norm_eps;
+  a.err = err;
+  a.amax_part = at<unsigned long long>(workspace, L.amax_part);
+  rc = gemm_batched(EPI_LOGITS, V, batch, a, [&](GemmArgs& c, int b0) {
+    c.X = x + (size_t)b0 * H;
+    c.logits = logits ? logits + (size_t)b0 * V : nullptr;
+    c.next_tok = next_tokens + b0;
+  }, st);
+  if (rc) return rc;
+  return 0;
+}
+
+int pkv_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return -EINVAL;
+  if (ws_bytes == 0) return 0;
+  return io(launch_fill_zero(workspace, ws_bytes, (hipStream_t)stream));
+}
+
+int pkv_rope_table(float theta, int32_t head_dim, int32_t max_pos, float* cos_out, float* sin_out,
+                   void* stream) {
+  if (!cos_out || !sin_out || max_pos < 1 || !(theta > 0.f) || !isfinite(theta)) return -EINVAL;
+  if (head_dim != kHeadDim) return -ENOTSUP;
+  return io(launch_rope_table((double)theta, head_dim, max_pos, cos_out, sin_out,
+                              (hipStream_t)stream));
+}
+
+int pkv_device_error(void* workspace, void* stream) {
+  if (!workspace || !aligned(workspace, 256)) return -EINVAL;
+  const hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return io(hipErrorUnknown);
+  uint32_t bits = 0;
+  if (hipMemcpy(&bits, workspace, sizeof bits, hipMemcpyDeviceToHost) != hipSuccess)
+    return io(hipErrorUnknown);
+  const uint32_t zero = 0;
+  if (hipMemcpy(workspace, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+    return io(hipErrorUnknown);
+  return (int)(bits & 0x7fffffffu);
+}
+
+}  // extern "C"

@@ -1,0 +1,284 @@
+// Direct paged GQA decode attention with FP32 online softmax, gfx950.
+//
+// The operation is the "Inference from Scratch" engine's direct paged
+// decode attention: every query head walks its sequence's pages through
+// the block table and accumulates softmax-weighted values without gathering
+// a contiguous prefix or storing scores.  Here one workgroup takes one
+// (sequence, kv head, split of 8 logical pages); its 4 waves take 2 pages
+// each.  The whole GQA group of the kv head shares every page load.
+//
+// One 16-token page is exactly one matrix-core tile:
+//   scores  S[t][g] = sum_d K[t][d] * q[g][d]      v_mfma_f32_16x16x32_bf16 x4
+//   output  O[g][d] += sum_t P[g][t] * V[t][d]     v_mfma_f32_16x16x16_bf16 x8
+// The score tile comes out of the first product in exactly the register
+// layout the second product wants for P (lane l holds tokens 4*(l/16)+r of
+// head l%16), and the page stores V as [d][slot], so a lane reads its four
+// tokens of one dimension as 8 contiguous bytes.  q and P are FP32 values
+// split into two BF16 halves (hi + lo) so that the products keep ~16
+// significant bits on both sides; the accumulation is FP32.
+//
+// Softmax: each wave takes the maximum over its pages, exponentiates, and
+// keeps (m, l, O); waves and then splits are merged with the log-sum-exp
+// rule m = max m_i, l = sum l_i e^(m_i - m), O = sum O_i e^(m_i - m), in a
+// fixed order, so the result depends only on the logical page sequence
+// (never on where pages sit in the pool).  A sequence that fits one split
+// is finished by its workgroup; otherwise every split leaves its (m, l, O)
+// record and a second, small kernel merges them: workgroups never wait on
+// one another (on this GPU a cross-workgroup handoff inside a kernel costs
+// more than the extra launch).
+#include "pkv_dev.h"
+
+namespace pkv {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Eight consecutive q values (BF16 bits or FP32) as FP32, vector loads.
+__device__ __forceinline__ void load_q8(const uint16_t* p, float (&v)[8]) {
+  const uint4 w = *(const uint4*)p;
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void load_q8(const float* p, float (&v)[8]) {
+  const float4 x0 = *(const float4*)p, x1 = *(const float4*)(p + 4);
+  v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+  v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+}
+
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Keep the first `nv` of the four BF16 values in v (the rest -> +0).
+__device__ __forceinline__ u32x2 keep_first(u32x2 v, int nv) {
+  if (nv >= 4) return v;
+  u32x2 r;
+  r.x = nv >= 2 ? v.x : (nv == 1 ? (v.x & 0xffffu) : 0u);
+  r.y = nv == 3 ? (v.y & 0xffffu) : 0u;
+  return r;
+}
+
+template <typename QT>
+__global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) {
+  constexpr int PW = kAttnPW;
+  constexpr int CP = kAttnPagesPerSplit;
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  __shared__ float sm_o[4][16][kHeadDim + 1];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int col = l & 15, grp = l >> 4;
+  const int G = a.G;
+  float* outp = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * kHeadDim;
+
+  int n = a.lens[b] + a.len_add;
+  if (n < 0 || n > a.bt_stride * kPageTokens) {
+    if (split == 0) {
+      if (tid == 0) set_error(a.err, ERR_LENGTH);
+      for (int i = tid; i < G * kHeadDim; i += 256) outp[i] = 0.f;
+    }
+    return;
+  }
+  const int npages = (n + kPageTokens - 1) / kPageTokens;
+  const int ns = npages > 0 ? (npages + CP - 1) / CP : 1;
+  if (split >= ns) return;
+  if (n == 0) {
+    for (int i = tid; i < G * kHeadDim; i += 256) outp[i] = 0.f;
+    return;
+  }
+
+  // ---- issue every load of this wave up front, unconditionally (addresses
+  // are clamped to valid memory; invalid pages are masked afterwards), so
+  // all of them are in flight together: block-table entries, then per page
+  // K (2 x 16 B) and V (4 x 8 B), then this lane's q values.
+  int page[PW];
+  int lpv[PW];
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int lp = split * CP + 4 * i + wu;  // uniform across the wave
+    page[i] = a.bt[(size_t)b * a.bt_stride + min(lp, npages - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int lp = split * CP + 4 * i + wu;
+    const bool live = lp < npages;
+    const bool ok = (unsigned)page[i] < (unsigned)a.num_pages;
+    if (live && !ok && l == 0) set_error(a.err, ERR_PAGE);
+    lpv[i] = live && ok ? lp : -1;
+    page[i] = live && ok ? page[i] : 0;
+  }
+  u32x4 kr[PW][2];
+  u32x2 vr[PW][4];
+  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
+    const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * kHeadDim + 8 * grp;
+    kr[i][0] = *(const u32x4*)kp;
+    kr[i][1] = *(const u32x4*)(kp + 32);
+    const uint16_t* vp = pg + vblk + ((int64_t)kvh * kHeadDim + col) * kPageTokens + 4 * grp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
+  }
+  // q^T operand (prescaled): lane holds head g = col, dims 8*grp + e + 32*h;
+  // lanes past the group read head 0 of the group and use zeros
+  float qv[2][8];
+  {
+    const int gq = col < G ? col : 0;
+    const QT* qp = (const QT*)a.q + ((size_t)b * a.Hq + (size_t)kvh * G + gq) * kHeadDim + 8 * grp;
+    load_q8(qp, qv[0]);
+    load_q8(qp + 32, qv[1]);
+  }
+  bf16x8 qh[2], ql[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = col < G ? qv[h][e] * a.scale : 0.f;
+      const __bf16 hi = (__bf16)v;
+      qh[h][e] = hi;
+      ql[h][e] = (__bf16)(v - (float)hi);
+    }
+
+  // ---- scores: lane holds S[t = 4*grp + r][g = col] of each page
+  f32x4 s[PW];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma_k32(kr[i][0], qh[0], acc);
+    acc = mfma_k32(kr[i][0], ql[0], acc);
+    acc = mfma_k32(kr[i][1], qh[1], acc);
+    acc = mfma_k32(kr[i][1], ql[1], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = lpv[i] * kPageTokens + 4 * grp + r;
+      const bool ok = lpv[i] >= 0 && t < n;
+      acc[r] = ok ? acc[r] : -INFINITY;
+      mx = fmaxf(mx, acc[r]);
+    }
+    s[i] = acc;
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+  // ---- P = exp(S - m) split hi/lo; row sums
+  float lsum = 0.f;
+  s16x4 ph[PW], pl[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = s[i][r] == -INFINITY ? 0.f : expf(s[i][r] - mx);
+      lsum += p;
+      const __bf16 hi = (__bf16)p;
+      ph[i][r] = __builtin_bit_cast(short, hi);
+      pl[i][r] = __builtin_bit_cast(short, (__bf16)(p - (float)hi));
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  // ---- O[g][d]: lane holds rows g = 4*grp + r, column d = col + 16*c
+  f32x4 o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    // unused slots of a partial page may hold anything (NaN included): zero them
+    const int nv = lpv[i] < 0 ? 0 : n - (lpv[i] * kPageTokens + 4 * grp);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const s16x4 vb = __builtin_bit_cast(s16x4, keep_first(vr[i][c], nv));
+      o[c] = mfma_k16(ph[i], vb, o[c]);
+      o[c] = mfma_k16(pl[i], vb, o[c]);
+    }
+  }
+
+  // ---- merge the four waves
+  if (grp == 0) {
+    sm_m[w][col] = mx;
+    sm_l[w][col] = lsum;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * grp + r;
+      if (g < G) sm_o[w][g][col + 16 * c] = o[c][r];
+    }
+  __syncthreads();
+
+  float* rec = a.part + (((size_t)b * a.Hkv + kvh) * a.max_splits + split) * kAttnRec;
+  for (int idx = tid; idx < G * kHeadDim; idx += 256) {
+    const int g = idx >> 6, d = idx & 63;
+    const float M = fmaxf(fmaxf(sm_m[0][g], sm_m[1][g]), fmaxf(sm_m[2][g], sm_m[3][g]));
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sm_m[ww][g];
+      const float e = mw == -INFINITY ? 0.f : expf(mw - M);
+      L += e * sm_l[ww][g];
+      O += e * sm_o[ww][g][d];
+    }
+    if (ns == 1) {
+      outp[idx] = L > 0.f ? O / L : 0.f;
+    } else {
+      if (d == 0) {
+        rec[g] = M;
+        rec[16 + g] = L;
+      }
+      rec[32 + idx] = O;
+    }
+  }
+}
+
+// Merge of the split records of every (sequence, kv head) that took more
+// than one split; sequences that fit one split were finished by their only
+// workgroup.  The records come from the previous kernel on the stream.
+__global__ __launch_bounds__(256) void attention_merge_kernel(const AttnArgs a) {
+  constexpr int CP = kAttnPagesPerSplit;
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int n = a.lens[b] + a.len_add;
+  if (n <= 0 || n > a.bt_stride * kPageTokens) return;
+  const int ns = ((n + kPageTokens - 1) / kPageTokens + CP - 1) / CP;
+  if (ns <= 1) return;
+  const int G = a.G;
+  float* outp = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * kHeadDim;
+  const float* rec0 = a.part + ((size_t)b * a.Hkv + kvh) * a.max_splits * kAttnRec;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
+    const int g = idx >> 6;
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, rec0[(size_t)sp * kAttnRec + g]);
+    float L = 0.f, O = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float* r = rec0 + (size_t)sp * kAttnRec;
+      const float e = r[g] == -INFINITY ? 0.f : expf(r[g] - M);
+      L += e * r[16 + g];
+      O += e * r[32 + idx];
+    }
+    outp[idx] = L > 0.f ? O / L : 0.f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int batch, bool q_is_bf16, hipStream_t st) {
+  const dim3 grid(a.max_splits, a.Hkv, batch);
+  if (q_is_bf16)
+    paged_attention_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
+  else
+    paged_attention_kernel<float><<<grid, 256, 0, st>>>(a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_splits <= 1) return e;
+  attention_merge_kernel<<<dim3(a.Hkv, batch), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

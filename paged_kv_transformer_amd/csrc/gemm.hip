@@ -1,0 +1,369 @@
+// Weight-streaming skinny GEMM for the decode projections, gfx950.
+//
+//   y[b][n] = sum_k W[n][k] * x[b][k] * xw[k]        (xw: RMSNorm weight or 1)
+//
+// W is BF16 [N][K] (the Hugging Face [out][in] orientation) and is read from
+// HBM exactly once per launch; the batch of FP32 activations is tiny and is
+// read from L2.  This is the decode step's dense contraction (the engine
+// packs one token of every active sequence into each step), so it runs on
+// the matrix cores: v_mfma_f32_16x16x32_bf16 with W rows as the A operand
+// (each lane streams 16-byte pieces of one row) and the batch as the B
+// operand.  The FP32 activations are split into two BF16 halves x = hi + lo
+// and both are multiplied (two MFMAs per weight tile), which keeps about 16
+// significant bits of every activation while the weights, the only large
+// operand, stay BF16.  Accumulation is FP32.
+//
+// A workgroup owns RG groups of 16 output rows over the whole of K; its NW
+// waves split K, run a two-stage software pipeline (the loads of the next
+// U steps are in flight while the current ones multiply), and are summed
+// in LDS in wave order.  No workgroup ever waits on another, so the
+// result is deterministic and needs no cross-workgroup synchronisation.
+// The same workgroup accumulates the sum of squares of its activations, so
+// the RMSNorm row scale 1/sqrt(mean x^2 + eps) is applied in the epilogue.
+//
+// Fused epilogues:
+//   EPI_QKV     16 rows = 8 RoPE pairs (j, j+32) of one head: RoPE on q and
+//               k heads (angle from the FP32 cos/sin tables at the
+//               sequence's position); q -> FP32 buffer, k and v -> BF16
+//               (nearest even) into the sequence's page at its position
+//               (the KV append).
+//   EPI_RESID   out = resid + y (output projection, down projection).
+//   EPI_SWIGLU  each 16-row group = 8 gate rows + the 8 matching up rows:
+//               a = silu(gate) * up.
+//   EPI_LOGITS  FP32 logits (optional store) and, per tile and sequence,
+//               the largest logit packed with its index; a small kernel
+//               then reduces the tiles to the token ids.
+#include "pkv_dev.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
+}
+
+// Order-preserving map of an FP32 value to 32 bits, paired with the
+// inverted index so that the 64-bit maximum is the largest value and, among
+// equal values, the lowest index.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n);
+}
+
+// Matrix row of MFMA row m (0..15) of row group g in tile t, or -1.
+template <int EPI, int RG>
+__device__ __forceinline__ int tile_row(const GemmArgs& a, int t, int g, int m) {
+  if (EPI == EPI_QKV) {
+    // tile t: head t/4, RoPE pairs j = 8*(t%4) + i (rows j and j + 32)
+    const int j0 = 8 * (t & 3);
+    return (t >> 2) * kHeadDim + (m < 8 ? j0 + m : 32 + j0 + (m - 8));
+  }
+  if (EPI == EPI_SWIGLU) {
+    const int i = 8 * (t * RG + g) + (m & 7);
+    return i < a.I ? (m < 8 ? i : a.I + i) : -1;
+  }
+  const int n = (t * RG + g) * 16 + m;
+  return n < a.N ? n : -1;
+}
+
+template <int CT, int RG, int NW, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
+  constexpr bool NORM = EPI != EPI_RESID;
+  constexpr int U = 2;        // 32-wide K steps per pipeline stage
+  constexpr int R = 16 * RG;  // output rows per tile
+  constexpr int NC = 16 * CT; // batch columns per launch
+  constexpr int TS = R + 1;   // tile column stride (floats)
+
+  __shared__ f32x4 red[NW][CT][RG][64];
+  __shared__ float tile[NC * TS];
+  __shared__ float ssq_w[NW][NC];
+  __shared__ float ssq_col[NC];
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int t = blockIdx.x;
+  const int steps = a.K >> 5;
+  const int spw = (steps + NW - 1) / NW;
+  const int s0 = w * spw;
+  const int s1 = min(s0 + spw, steps);
+
+  // A operand rows (row l % 16 of each group) and B operand columns
+  // (column l % 16 of each column group); K offset 8 * (l / 16) in a step.
+  // Rows past N and columns past B read row 0 / column 0 and are never stored.
+  const int koff = 8 * (l >> 4);
+  const uint16_t* wrow[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const int n = tile_row<EPI, RG>(a, t, g, l & 15);
+    wrow[g] = a.W + (size_t)(n >= 0 ? n : 0) * a.K + koff;
+  }
+  const float* xrow[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int b = 16 * c + (l & 15);
+    xrow[c] = a.X + (size_t)(b < a.B ? b : 0) * a.K + koff;
+  }
+  const uint16_t* xwp = NORM ? a.xw + koff : nullptr;
+
+  f32x4 acc[RG][CT];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[g][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float ssq[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) ssq[c] = 0.f;
+
+  struct Stage {
+    u32x4 w[U][RG];
+    float4 x[U][CT][2];
+    uint4 xw[U];
+  };
+  // Loads of steps st .. st+U-1, clamped into this wave's K range (steps
+  // past the end are loaded again and skipped by compute): no branch, so
+  // the compiler's wait counts stay exact and the prefetch is never waited
+  // on early.
+  auto load = [&](Stage& S, int st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = min(st + u, s1 - 1) * 32;
+#pragma unroll
+      for (int g = 0; g < RG; ++g) S.w[u][g] = __builtin_nontemporal_load((const u32x4*)(wrow[g] + k));
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        S.x[u][c][0] = *(const float4*)(xrow[c] + k);
+        S.x[u][c][1] = *(const float4*)(xrow[c] + k + 4);
+      }
+      if (NORM) S.xw[u] = *(const uint4*)(xwp + k);
+    }
+  };
+  auto compute = [&](const Stage& S, int st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (st + u >= s1) break;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        float v[8] = {S.x[u][c][0].x, S.x[u][c][0].y, S.x[u][c][0].z, S.x[u][c][0].w,
+                      S.x[u][c][1].x, S.x[u][c][1].y, S.x[u][c][1].z, S.x[u][c][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ssq[c] += v[e] * v[e];
+        if (NORM) {
+          v[0] *= bf16_lo(S.xw[u].x); v[1] *= bf16_hi(S.xw[u].x);
+          v[2] *= bf16_lo(S.xw[u].y); v[3] *= bf16_hi(S.xw[u].y);
+          v[4] *= bf16_lo(S.xw[u].z); v[5] *= bf16_hi(S.xw[u].z);
+          v[6] *= bf16_lo(S.xw[u].w); v[7] *= bf16_hi(S.xw[u].w);
+        }
+        float hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = (float)(__bf16)v[e];
+          lo[e] = v[e] - hi[e];
+        }
+        const u32x4 bh = {pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3]),
+                          pack_bf16(hi[4], hi[5]), pack_bf16(hi[6], hi[7])};
+        const u32x4 bl = {pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]),
+                          pack_bf16(lo[4], lo[5]), pack_bf16(lo[6], lo[7])};
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          acc[g][c] = mfma32(S.w[u][g], bh, acc[g][c]);
+          acc[g][c] = mfma32(S.w[u][g], bl, acc[g][c]);
+        }
+      }
+    }
+  };
+
+  if (s0 < s1) {
+    Stage A, B;
+    load(A, s0);
+    for (int st = s0;; st += 2 * U) {
+      load(B, st + U);
+      compute(A, st);
+      if (st + U >= s1) break;
+      load(A, st + 2 * U);
+      compute(B, st + U);
+      if (st + 2 * U >= s1) break;
+    }
+  }
+
+  // ---- sum the waves (in wave order) into tile[col * TS + row]
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    ssq[c] += __shfl_xor(ssq[c], 16);
+    ssq[c] += __shfl_xor(ssq[c], 32);
+    if (l < 16) ssq_w[w][16 * c + l] = ssq[c];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) red[w][c][g][l] = acc[g][c];
+  }
+  __syncthreads();
+  for (int i = tid; i < CT * RG * 64 * 4; i += NW * 64) {
+    const int r = i & 3, ln = (i >> 2) & 63, g = (i >> 8) % RG, c = (i >> 8) / RG;
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) v += red[ww][c][g][ln][r];
+    const int row = 16 * g + 4 * (ln >> 4) + r;
+    const int col = 16 * c + (ln & 15);
+    tile[col * TS + row] = v;
+  }
+  if (tid < NC) {
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) v += ssq_w[ww][tid];
+    ssq_col[tid] = v;
+  }
+  __syncthreads();
+
+  // ---- epilogues
+  constexpr int NT = NW * 64;
+  if (EPI == EPI_RESID) {
+    for (int i = tid; i < R * a.B; i += NT) {
+      const int c = i / R, row = i % R;
+      const int n = t * R + row;
+      if (n < a.N) {
+        const size_t o = (size_t)c * a.N + n;
+        a.out[o] = a.resid[o] + tile[c * TS + row];
+      }
+    }
+  } else if (EPI == EPI_QKV) {
+    const int hd = t >> 2, j0 = 8 * (t & 3);
+    const bool is_q = hd < a.Hq;
+    const bool is_k = !is_q && hd < a.Hq + a.Hkv;
+    for (int idx = tid; idx < 8 * a.B; idx += NT) {
+      const int c = idx >> 3, i = idx & 7, j = j0 + i;
+      const float rs = 1.0f / sqrtf(ssq_col[c] / (float)a.K + a.eps);
+      const float x0 = tile[c * TS + i] * rs;
+      const float x1 = tile[c * TS + 8 + i] * rs;
+      const int p = a.pos[c];
+      float y0 = x0, y1 = x1;
+      if (is_q || is_k) {
+        if (p < 0 || p >= a.max_pos) {
+          set_error(a.err, ERR_ROPE);
+          continue;
+        }
+        const float cs = a.rcos[(size_t)p * 32 + j];
+        const float sn = a.rsin[(size_t)p * 32 + j];
+        y0 = __fsub_rn(__fmul_rn(x0, cs), __fmul_rn(x1, sn));
+        y1 = __fadd_rn(__fmul_rn(x0, sn), __fmul_rn(x1, cs));
+      }
+      if (is_q) {
+        float* qo = a.q_out + ((size_t)c * a.Hq + hd) * kHeadDim;
+        qo[j] = y0;
+        qo[j + 32] = y1;
+      } else {
+        if (p < 0 || p / kPageTokens >= a.bt_stride) {
+          set_error(a.err, ERR_LENGTH);
+          continue;
+        }
+        const int page = a.bt[(size_t)c * a.bt_stride + p / kPageTokens];
+        if ((unsigned)page >= (unsigned)a.num_pages) {
+          set_error(a.err, ERR_PAGE);
+          continue;
+        }
+        uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
+        const int slot = p % kPageTokens;
+        if (is_k) {
+          uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * kHeadDim;
+          kp[j] = to_bf16_bits(y0);
+          kp[j + 32] = to_bf16_bits(y1);
+        } else {
+          uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * kHeadDim +
+                         (int64_t)(hd - a.Hq - a.Hkv) * kHeadDim * kPageTokens + slot;
+          vp[j * kPageTokens] = to_bf16_bits(y0);
+          vp[(j + 32) * kPageTokens] = to_bf16_bits(y1);
+        }
+      }
+    }
+  } else if (EPI == EPI_SWIGLU) {
+    for (int idx = tid; idx < 8 * RG * a.B; idx += NT) {
+      const int c = idx / (8 * RG), gi = idx % (8 * RG), g = gi >> 3, m = gi & 7;
+      const int i = 8 * (t * RG + g) + m;
+      if (i >= a.I) continue;
+      const float rs = 1.0f / sqrtf(ssq_col[c] / (float)a.K + a.eps);
+      const float gv = tile[c * TS + 16 * g + m] * rs;
+      const float uv = tile[c * TS + 16 * g + 8 + m] * rs;
+      a.act[(size_t)c * a.I + i] = gv / (1.0f + expf(-gv)) * uv;
+    }
+  } else {  // EPI_LOGITS
+    for (int i = tid; i < R * a.B; i += NT) {
+      const int c = i / R, row = i % R;
+      const int n = t * R + row;
+      if (n < a.N && a.logits) {
+        const float rs = 1.0f / sqrtf(ssq_col[c] / (float)a.K + a.eps);
+        a.logits[(size_t)c * a.N + n] = tile[c * TS + row] * rs;
+      }
+    }
+    if (tid < a.B) {
+      const int c = tid;
+      const float rs = 1.0f / sqrtf(ssq_col[c] / (float)a.K + a.eps);
+      unsigned long long best = 0ull;
+      for (int row = 0; row < R; ++row) {
+        const int n = t * R + row;
+        if (n >= a.N) break;
+        const unsigned long long key = argmax_key(tile[c * TS + row] * rs, n);
+        best = key > best ? key : best;
+      }
+      a.amax_part[(size_t)t * a.B + c] = best;
+    }
+  }
+}
+
+// Token id per sequence: the largest packed key over the LM head's tiles.
+__global__ void argmax_finalize_kernel(const unsigned long long* part, int tiles, int B,
+                                       int32_t* next_tok) {
+  __shared__ unsigned long long sm[256];
+  const int c = blockIdx.x;
+  unsigned long long best = 0ull;
+  for (int t = threadIdx.x; t < tiles; t += blockDim.x) {
+    const unsigned long long k = part[(size_t)t * B + c];
+    best = k > best ? k : best;
+  }
+  sm[threadIdx.x] = best;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s && sm[threadIdx.x + s] > sm[threadIdx.x]) sm[threadIdx.x] = sm[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) next_tok[c] = (int32_t)(0xffffffffu - (uint32_t)(sm[0] & 0xffffffffull));
+}
+
+template <int CT, int RG, int NW, int EPI>
+hipError_t go(const GemmArgs& a, int tiles, hipStream_t st) {
+  gemm_kernel<CT, RG, NW, EPI><<<tiles, NW * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_t st) {
+  hipError_t e = hipErrorInvalidValue;
+  const bool one = p.ct == 1;
+  switch (epi) {
+    case EPI_QKV:
+      e = one ? go<1, 1, 8, EPI_QKV>(a, p.tiles, st) : go<2, 1, 8, EPI_QKV>(a, p.tiles, st);
+      break;
+    case EPI_RESID:
+      e = one ? go<1, 1, 16, EPI_RESID>(a, p.tiles, st) : go<2, 1, 16, EPI_RESID>(a, p.tiles, st);
+      break;
+    case EPI_SWIGLU:
+      e = one ? go<1, 2, 4, EPI_SWIGLU>(a, p.tiles, st) : go<2, 1, 4, EPI_SWIGLU>(a, p.tiles, st);
+      break;
+    case EPI_LOGITS:
+      e = one ? go<1, 4, 4, EPI_LOGITS>(a, p.tiles, st) : go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st);
+      if (e != hipSuccess) return e;
+      argmax_finalize_kernel<<<a.B, 256, 0, st>>>(a.amax_part, p.tiles, a.B, a.next_tok);
+      e = hipGetLastError();
+      break;
+    default:
+      break;
+  }
+  return e;
+}
+
+}  // namespace pkv

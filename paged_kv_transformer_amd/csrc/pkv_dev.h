@@ -1,0 +1,173 @@
+// Internal declarations of the gfx950 paged-KV decode library: device
+// helpers, kernel argument blocks, the workspace layout and the launch plans
+// shared by the host entry points (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kPageTokens = 16;
+constexpr int kHeadDim = 64;
+constexpr int kMaxGroup = 16;      // GQA group: one 16-wide matrix-core tile
+
+enum : uint32_t { ERR_PAGE = 1u, ERR_LENGTH = 2u, ERR_ROPE = 4u, ERR_TOKEN = 8u };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------- device ---
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// FP32 -> BF16 bits, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ void set_error(uint32_t* err, uint32_t bits) {
+  __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// --------------------------------------------------------- arguments ---
+
+struct AttnArgs {
+  const void* q;           // [B][Hq][D], BF16 bits or FP32 (template)
+  const uint16_t* pool;    // page pool base
+  int64_t page_elems;      // BF16 elements per page
+  int32_t num_pages;
+  const int32_t* bt;       // [B][bt_stride]
+  int32_t bt_stride;       // max_pages
+  const int32_t* lens;     // [B]: attention length, or position (len_add = 1)
+  int32_t len_add;
+  float scale;
+  float* out;              // [B][Hq][D] FP32
+  float* part;             // split partial records [B][Hkv][max_splits][kAttnRec]
+  uint32_t* err;
+  int32_t Hq, Hkv, G;
+  int32_t max_splits;
+};
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct GemmArgs {
+  const uint16_t* W;       // [N][K] BF16 bits, row-major
+  const float* X;          // [B][K] FP32 activations
+  const uint16_t* xw;      // RMSNorm weight [K] (epilogues that normalise)
+  int32_t N, K, B;
+  float eps;
+  uint32_t* err;
+  // EPI_RESID: out[b][n] = resid[b][n] + y
+  float* out;
+  const float* resid;
+  // EPI_QKV
+  float* q_out;            // [B][Hq][D]
+  uint16_t* pool;
+  int64_t page_elems;
+  int32_t num_pages;
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* pos;
+  const float* rcos;
+  const float* rsin;
+  int32_t max_pos;
+  int32_t Hq, Hkv;
+  // EPI_SWIGLU: act[b][i], i < I
+  float* act;
+  int32_t I;
+  // EPI_LOGITS
+  float* logits;                 // [B][N] or null
+  unsigned long long* amax_part; // [tiles][B] per-tile packed maxima
+  int32_t* next_tok;             // [B]
+};
+
+// ------------------------------------------------------------ plans ---
+
+// Attention: 4 waves per workgroup, kAttnPW pages per wave per split.
+constexpr int kAttnPW = 2;
+constexpr int kAttnPagesPerSplit = 4 * kAttnPW;
+// One split's partial record: m[16], l[16], o[16][64] floats.
+constexpr int kAttnRec = 16 + 16 + 16 * kHeadDim;
+
+inline int attn_max_splits(int max_pages) {
+  return (max_pages + kAttnPagesPerSplit - 1) / kAttnPagesPerSplit;
+}
+
+// A GEMM launch: `rg` groups of 16 output rows per workgroup, `nw` waves
+// splitting K inside the workgroup, `ct` groups of 16 batch columns.
+struct GemmPlan {
+  int tiles, ct, rg, nw;
+};
+
+constexpr int kGemmMaxCols = 32;  // batch columns per launch (ct <= 2)
+
+inline int gemm_ct(int B) { return B <= 16 ? 1 : 2; }
+
+inline int gemm_rows_per_tile(int epi, int ct) {
+  if (epi == EPI_QKV || epi == EPI_RESID) return 16;
+  return ct == 1 ? (epi == EPI_LOGITS ? 64 : 32) : 16;
+}
+
+inline GemmPlan plan_gemm(int epi, int N, int B) {
+  GemmPlan p;
+  p.ct = gemm_ct(B);
+  const int R = gemm_rows_per_tile(epi, p.ct);
+  p.rg = R / 16;
+  p.nw = epi == EPI_RESID ? 16 : (epi == EPI_QKV ? 8 : 4);
+  // the gate/up tile holds R/2 gate rows and the R/2 matching up rows
+  const int rows = epi == EPI_SWIGLU ? N / 2 : N;
+  const int per = epi == EPI_SWIGLU ? R / 2 : R;
+  p.tiles = (rows + per - 1) / per;
+  return p;
+}
+
+struct WsLayout {
+  size_t err, q, o, h1, act, x;
+  size_t attn_part, amax_part;
+  size_t total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace layout.  layer == false: attention only (no activations).
+inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_pages, bool layer) {
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  w.err = take(256);
+  w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_pages) * kAttnRec);
+  if (layer) {
+    w.q = take(sizeof(float) * (size_t)B * Hq * kHeadDim);
+    w.o = take(sizeof(float) * (size_t)B * Hq * kHeadDim);
+    w.h1 = take(sizeof(float) * (size_t)B * H);
+    w.act = take(sizeof(float) * (size_t)B * I);
+    w.x = take(sizeof(float) * (size_t)B * H);
+    const int Bc = B < kGemmMaxCols ? B : kGemmMaxCols;
+    const GemmPlan lm = plan_gemm(EPI_LOGITS, V, Bc);
+    w.amax_part = take(sizeof(unsigned long long) * (size_t)lm.tiles * (Bc > 0 ? Bc : 1));
+  }
+  w.total = off;
+  return w;
+}
+
+// ---------------------------------------------------------- launchers ---
+
+// Each returns hipSuccess or the launch error.
+// The split kernel, then the merge of sequences that took several splits.
+hipError_t launch_attention(const AttnArgs& a, int batch, bool q_is_bf16, hipStream_t st);
+hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_t st);
+hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_pages,
+                            const int32_t* bt, int32_t bt_stride, const int32_t* pos,
+                            const uint16_t* k, const uint16_t* v, int batch, int Hkv,
+                            hipStream_t st);
+hipError_t launch_embed(const uint16_t* E, int V, int H, const int32_t* tok, float* x,
+                        int batch, uint32_t* err, hipStream_t st);
+hipError_t launch_rope_table(double theta, int D, int max_pos, float* c, float* s,
+                             hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace pkv

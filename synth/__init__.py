@@ -6,10 +6,14 @@ block tables that map each (layer, sequence, logical page) to a physical
 page.  It holds none of the decode step's arithmetic; both the oracle and the
 HIP path receive exactly the bytes produced here.
 
-Every tensor is drawn from ``numpy.random.default_rng([seed, tensor id,
-*index])`` so that any slice (one layer, one chunk of pool pages) can be
-regenerated on its own.  FP32 normals are turned into BF16 with torch's
-round-to-nearest-even conversion.
+Every tensor is keyed by (seed, tensor id, *index).  Normal values come from
+torch's CPU generator, one generator per chunk of 2^24 elements seeded from
+``numpy.random.SeedSequence([seed, tensor id, *index, chunk])``, so any
+tensor or chunk regenerates on its own and the result does not depend on how
+many threads draw the chunks.  FP32 normals are turned into BF16 with
+torch's round-to-nearest-even conversion.  Small integer draws (lengths,
+token ids, page permutations) use ``numpy.random.default_rng`` with the same
+key.
 
 Model shapes follow the public configurations of the two model families the
 source pages run (Llama 3.2 1B in the "Inference from Scratch" engine,
@@ -80,15 +84,43 @@ def to_bf16_bits(x):
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+_CHUNK = 1 << 24
+
+
+def torch_generator(seed, name, *index):
+    """A torch CPU generator seeded from (seed, tensor id, *index)."""
+    ss = np.random.SeedSequence([int(seed), _ID[name], *[int(i) for i in index]])
+    return torch.Generator().manual_seed(int(ss.generate_state(1, dtype=np.uint64)[0] >> 1))
+
+
+def _normal_bf16_into(out, seed, name, index, sigma, mean):
+    n = out.size
+
+    def chunk(c):
+        lo, hi = c * _CHUNK, min(n, (c + 1) * _CHUNK)
+        g = torch_generator(seed, name, *index, c)
+        x = torch.randn(hi - lo, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        if mean != 0.0:
+            x.add_(mean)
+        out[lo:hi] = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for c in range(nchunks):
+            chunk(c)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(16, nchunks)) as ex:
+            list(ex.map(chunk, range(nchunks)))
+    return out
+
+
 def bf16_normal(seed, name, shape, sigma=1.0, mean=0.0, index=()):
-    g = rng(seed, name, *index)
-    n = int(np.prod(shape))
-    x = g.standard_normal(n, dtype=np.float32)
-    if sigma != 1.0:
-        x *= np.float32(sigma)
-    if mean != 0.0:
-        x += np.float32(mean)
-    return to_bf16_bits(x).reshape(shape)
+    """N(mean, sigma^2) values rounded to BF16, as uint16 bit patterns."""
+    out = np.empty(int(np.prod(shape)), dtype=np.uint16)
+    return _normal_bf16_into(out, seed, name, tuple(index), float(sigma), float(mean)).reshape(shape)
 
 
 # --------------------------------------------------------------- weights ---
@@ -121,15 +153,9 @@ def page_elems(shape_or_kv_heads, head_dim=64, page_tokens=PAGE_TOKENS):
     return 2 * kv * page_tokens * head_dim
 
 
-def random_pool(seed, num_pages, elems_per_page, chunk_pages=2048):
-    """The whole pool as N(0,1) BF16 values, drawn chunk by chunk."""
-    out = np.empty(num_pages * elems_per_page, dtype=np.uint16)
-    for c0 in range(0, num_pages, chunk_pages):
-        c1 = min(num_pages, c0 + chunk_pages)
-        g = rng(seed, "pool", c0 // chunk_pages)
-        x = g.standard_normal((c1 - c0) * elems_per_page, dtype=np.float32)
-        out[c0 * elems_per_page:c1 * elems_per_page] = to_bf16_bits(x)
-    return out
+def random_pool(seed, num_pages, elems_per_page):
+    """The whole pool as N(0,1) BF16 values."""
+    return bf16_normal(seed, "pool", (num_pages * elems_per_page,))
 
 
 def pages_for(n_tokens):

@@ -1,0 +1,119 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI on
+seeded inputs and compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_transformer_amd as pkv
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return pkv.to_device(a)
+
+
+def host_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def attention_gpu(pool_np, kv_heads, q_bits, bt, lens, scale, ws=None):
+    """Run paged_gqa_decode; returns (out [B, Hq, 64] float32, device error bits)."""
+    B, Hq = q_bits.shape[0], q_bits.shape[1]
+    pool_t = dev(pool_np)
+    pool = pkv.kv_pool_create(pool_t, kv_heads)
+    bt = np.ascontiguousarray(bt, dtype=np.int32)
+    out = torch.full((B, Hq, 64), float("nan"), dtype=torch.float32, device="cuda")
+    if ws is None:
+        ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(Hq, kv_heads, B, bt.shape[1]))
+    pkv.paged_gqa_decode(pool, dev(q_bits), dev(bt), dev(np.asarray(lens, dtype=np.int32)),
+                         scale, out, ws)
+    err = pkv.device_error(ws)
+    return out.cpu().numpy(), err
+
+
+def attention_oracle(pool_np, kv_heads, q_bits, bt, lens, scale, seqs=None):
+    geo = oracle.PoolGeometry(kv_heads, 64)
+    return oracle.paged_attention(pool_np, geo, oracle.bf16_to_f32(q_bits), bt, lens, scale, seqs)
+
+
+def layer_gpu(shape, lw, hidden, pool_np, bt, positions, max_pos=None):
+    """decoder_layer_decode on one layer; returns (hidden_out, pool_after, err)."""
+    B = len(positions)
+    bt = np.ascontiguousarray(bt, dtype=np.int32)
+    mp = max_pos or int(max(positions)) + 1
+    cfg = pkv.make_config(shape, max_pos=mp, layers=1)
+    layer = pkv.upload_layer(lw)
+    c, s = pkv.rope_table(shape.theta, mp)
+    pool_t = dev(pool_np)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    h = torch.from_numpy(np.ascontiguousarray(hidden, dtype=np.float32)).cuda()
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bt.shape[1]))
+    pkv.decoder_layer_decode(cfg, layer, c, s, pool, dev(bt), dev(np.asarray(positions, np.int32)), h, ws)
+    err = pkv.device_error(ws)
+    return h.cpu().numpy(), host_u16(pool_t), err
+
+
+def expected_pool_after(pool_np, geo, bt, positions, k_new, v_new, seqs=None):
+    want = pool_np.copy()
+    for b in (range(len(positions)) if seqs is None else seqs):
+        oracle.pool_append(want, geo, bt[b], int(positions[b]), k_new[b], v_new[b])
+    return want
+
+
+APPEND_REL = 1e-3
+
+
+def check_pool_after(got, want, base):
+    """Bytes the step did not append must be untouched.  An appended BF16
+    value is the rounding of an FP32 contraction whose last bits differ
+    between the two paths (summation order, the two-half BF16 split of the
+    activations), so it must lie within one BF16 ulp of the oracle's value or
+    within APPEND_REL * RMS(appended values) of it: near zero an ulp is far
+    smaller than the contraction's absolute error."""
+    touched = want != base
+    assert np.array_equal(got[~touched], base[~touched]), "pool bytes outside the appended slots changed"
+    g = oracle.bf16_to_f32(got[touched]).astype(np.float64)
+    w = oracle.bf16_to_f32(want[touched]).astype(np.float64)
+    ulp = np.abs(w) * 2.0 ** -7 + 1e-38
+    rms = float(np.sqrt(np.mean(w * w))) if w.size else 0.0
+    bad = np.abs(g - w) > np.maximum(ulp, APPEND_REL * rms)
+    assert not bad.any(), "appended K/V: %d values off by up to %.3g (RMS %.3g)" % (
+        int(bad.sum()), float(np.abs(g - w).max()), rms)
+    return float(np.abs(g - w).max(initial=0.0)), rms
+
+
+def step_gpu(shape, weights, pool_np, bts, positions, tokens, want_logits=True, max_pos=None):
+    """decode_step; returns (logits or None, next_tokens, pool_after, err)."""
+    B = len(positions)
+    mp = max_pos or int(max(positions)) + 1
+    cfg = pkv.make_config(shape, max_pos=mp)
+    model = pkv.upload_model(weights, shape.theta, mp)
+    pool_t = dev(pool_np)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    bts = np.ascontiguousarray(bts, dtype=np.int32)
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bts.shape[2]))
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda") if want_logits else None
+    nxt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    pkv.decode_step(cfg, model, pool, dev(bts), dev(np.asarray(positions, np.int32)),
+                    dev(np.asarray(tokens, np.int32)), logits, nxt, ws)
+    err = pkv.device_error(ws)
+    return (None if logits is None else logits.cpu().numpy()), nxt.cpu().numpy(), host_u16(pool_t), err
+
+
+def check_argmax_rule(ref_logits, got_tokens, gap=1e-3):
+    """Identical argmax wherever the oracle's top-2 gap exceeds `gap`."""
+    checked = 0
+    for b in range(ref_logits.shape[0]):
+        top2 = np.sort(ref_logits[b])[-2:]
+        if top2[1] - top2[0] > gap:
+            assert int(got_tokens[b]) == int(np.argmax(ref_logits[b])), \
+                "sequence %d: argmax %d vs oracle %d (gap %.3g)" % (
+                    b, int(got_tokens[b]), int(np.argmax(ref_logits[b])), top2[1] - top2[0])
+            checked += 1
+    return checked

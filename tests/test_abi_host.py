@@ -1,0 +1,145 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/pkv.h declares, and rejects bad arguments with the stated
+negative errno before any HIP call."""
+import ctypes
+import errno
+import os
+import re
+
+import pytest
+
+import paged_kv_transformer_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+if not os.path.exists(pkv.LIB_PATH):
+    pytest.skip("libpkv.so is not built", allow_module_level=True)
+
+L = pkv.lib()
+FAKE = 1 << 20          # an aligned non-null address: validation never dereferences it
+EINVAL, ENOTSUP, ENOSPC = -errno.EINVAL, -errno.ENOTSUP, -errno.ENOSPC
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    for must in ("kv_pool_create", "kv_append", "paged_gqa_decode", "decoder_layer_decode",
+                 "decode_step", "pkv_workspace_bytes", "pkv_device_error"):
+        assert must in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _pool(hkv=8, pages=64):
+    p = pkv.Pool()
+    assert L.kv_pool_create(FAKE, pages * 2 * hkv * 16 * 64 * 2, hkv, 64, 16, ctypes.byref(p)) == 0
+    return p
+
+
+def test_kv_pool_create_geometry_and_errors():
+    p = pkv.Pool()
+    assert L.kv_pool_create(FAKE, 128 << 20, 8, 64, 16, ctypes.byref(p)) == 0
+    assert p.page_bytes == 32768 and p.num_pages == 4096
+    assert L.kv_pool_create(FAKE, 8 * 8192 + 100, 2, 64, 16, ctypes.byref(p)) == 0
+    assert p.page_bytes == 8192 and p.num_pages == 8
+    assert L.kv_pool_create(None, 1 << 20, 8, 64, 16, ctypes.byref(p)) == EINVAL
+    assert L.kv_pool_create(FAKE + 8, 1 << 20, 8, 64, 16, ctypes.byref(p)) == EINVAL
+    assert L.kv_pool_create(FAKE, 1 << 20, 0, 64, 16, ctypes.byref(p)) == EINVAL
+    assert L.kv_pool_create(FAKE, 1 << 20, 8, 128, 16, ctypes.byref(p)) == ENOTSUP
+    assert L.kv_pool_create(FAKE, 1 << 20, 8, 64, 256, ctypes.byref(p)) == ENOTSUP
+    assert L.kv_pool_create(FAKE, 1000, 8, 64, 16, ctypes.byref(p)) == ENOSPC
+    assert L.kv_pool_create(FAKE, 1 << 20, 8, 64, 16, None) == EINVAL
+
+
+def test_paged_gqa_decode_validation():
+    p = _pool()
+    ws_need = L.pkv_attention_workspace_bytes(32, 8, 64, 16, 128)
+    assert ws_need > 0
+    args = lambda **kw: [ctypes.byref(kw.get("pool", p)), kw.get("q", FAKE), kw.get("hq", 32),
+                         kw.get("bt", FAKE), kw.get("mp", 128), kw.get("lens", FAKE), kw.get("b", 16),
+                         kw.get("scale", 0.125), kw.get("out", FAKE), kw.get("ws", FAKE),
+                         kw.get("wsb", ws_need), None]
+    assert L.paged_gqa_decode(*args(q=None)) == EINVAL
+    assert L.paged_gqa_decode(*args(hq=30)) == EINVAL          # 30 % 8 != 0
+    assert L.paged_gqa_decode(*args(hq=8 * 17)) == ENOTSUP     # group of 17
+    assert L.paged_gqa_decode(*args(b=-1)) == EINVAL
+    assert L.paged_gqa_decode(*args(mp=0)) == EINVAL
+    assert L.paged_gqa_decode(*args(wsb=ws_need - 1)) == ENOSPC
+    assert L.paged_gqa_decode(*args(ws=FAKE + 4)) == EINVAL
+    assert L.paged_gqa_decode(*args(scale=float("nan"))) == EINVAL
+    assert L.paged_gqa_decode(*args(b=0)) == 0                 # empty batch: nothing to do
+    bad = pkv.Pool.from_buffer_copy(p)
+    bad.page_tokens = 32
+    assert L.paged_gqa_decode(*args(pool=bad)) == ENOTSUP
+
+
+def _cfg(**kw):
+    c = pkv.Config(2048, 16, 32, 8, 64, 8192, 128256, 4096, 5e5, 1e-5)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_layer_and_step_validation():
+    p = _pool()
+    lw = pkv.LayerWeights(*([FAKE] * 6))
+    cfg = _cfg()
+    need = L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 128)
+    assert need > 0
+
+    def layer(c=cfg, w=lw, pool=p, b=16, wsb=need, ws=FAKE, hidden=FAKE):
+        return L.decoder_layer_decode(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, ctypes.byref(pool),
+                                      FAKE, 128, FAKE, b, hidden, ws, wsb, None)
+
+    assert layer(c=_cfg(head_dim=128)) == ENOTSUP
+    assert layer(c=_cfg(hidden_size=2000)) == ENOTSUP
+    assert layer(c=_cfg(intermediate_size=100)) == ENOTSUP
+    assert layer(c=_cfg(num_key_value_heads=3)) == EINVAL
+    assert layer(c=_cfg(rms_norm_eps=float("nan"))) == EINVAL
+    assert layer(pool=_pool(hkv=2)) == EINVAL                  # pool heads != config heads
+    assert layer(w=pkv.LayerWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE)) == EINVAL
+    assert layer(wsb=need - 1) == ENOSPC
+    assert layer(hidden=None) == EINVAL
+    assert layer(b=-3) == EINVAL
+    assert layer(b=0) == 0
+
+    layers = (pkv.LayerWeights * 16)(*([lw] * 16))
+    mw = pkv.ModelWeights(FAKE, FAKE, ctypes.cast(layers, ctypes.POINTER(pkv.LayerWeights)), FAKE, FAKE)
+
+    def step(c=cfg, m=mw, nxt=FAKE, wsb=need, b=16):
+        return L.decode_step(ctypes.byref(c), ctypes.byref(m), ctypes.byref(p), FAKE, 128, FAKE, FAKE, b,
+                             None, nxt, FAKE, wsb, None)
+
+    assert step(nxt=None) == EINVAL
+    assert step(c=_cfg(vocab_size=0)) == EINVAL
+    assert step(wsb=need - 256) == ENOSPC
+    layers[5] = pkv.LayerWeights(FAKE, FAKE, FAKE, FAKE, None, FAKE)
+    assert step() == EINVAL
+    assert step(b=0) == EINVAL                                 # layer 5 is still incomplete
+
+
+def test_rope_table_and_workspace_validation():
+    assert L.pkv_rope_table(1e4, 128, 10, FAKE, FAKE, None) == ENOTSUP
+    assert L.pkv_rope_table(1e4, 64, 0, FAKE, FAKE, None) == EINVAL
+    assert L.pkv_rope_table(-1.0, 64, 10, FAKE, FAKE, None) == EINVAL
+    assert L.pkv_rope_table(1e4, 64, 10, None, FAKE, None) == EINVAL
+    assert L.pkv_workspace_init(None, 256, None) == EINVAL
+    assert L.pkv_workspace_init(FAKE + 1, 256, None) == EINVAL
+    assert L.pkv_device_error(None, None) == EINVAL
+    assert L.pkv_attention_workspace_bytes(32, 8, 128, 16, 128) == 0
+    assert L.pkv_workspace_bytes(None, 1, 1) == 0
+
+
+def test_workspace_sizes_grow_with_batch_and_pages():
+    cfg = _cfg()
+    a = L.pkv_workspace_bytes(ctypes.byref(cfg), 1, 64)
+    b = L.pkv_workspace_bytes(ctypes.byref(cfg), 64, 64)
+    c = L.pkv_workspace_bytes(ctypes.byref(cfg), 64, 128)
+    assert 0 < a < b < c
+    assert all(x % 256 == 0 for x in (a, b, c))

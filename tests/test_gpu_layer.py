@@ -1,0 +1,110 @@
+"""GPU parity of decoder_layer_decode and decode_step against the oracle,
+through the C ABI.  Bars: layer outputs max-abs <= 1e-2 * RMS(out); each
+appended K/V value within one BF16 ulp of the oracle's or within 1e-3 of the
+appended values' RMS, and the rest of the pool untouched; logits max-abs
+<= 1e-2 * RMS(logits); the argmax identical wherever the oracle's top-2
+logit gap exceeds 1e-3."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (check_argmax_rule, check_pool_after, expected_pool_after, layer_gpu, say,
+                      step_gpu)
+
+pytestmark = pytest.mark.gpu
+
+LAYER_TOL = 1e-2
+
+
+def _rms(a):
+    return float(np.sqrt(np.mean(np.square(a, dtype=np.float64))))
+
+
+def _check_layer(shape, lw, hidden, wl, seqs=None):
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
+    bt = wl.block_tables[0]
+    got, pool_after, err = layer_gpu(shape, lw, hidden, wl.pool, bt, wl.positions)
+    assert err == 0
+    ref, k_new, v_new = oracle.layer_decode_paged(shape, lw, hidden, wl.pool, geo, bt, wl.positions, seqs)
+    rows = list(range(len(wl.positions))) if seqs is None else list(seqs)
+    diff = np.abs(got[rows] - ref[rows]).max()
+    delta_err = diff / max(_rms(ref[rows] - hidden[rows]), 1e-30)
+    say("layer %s B=%d: max-abs %.3g, RMS(out) %.3g, error/RMS(delta) %.3g"
+        % (shape.name, len(wl.positions), diff, _rms(ref[rows]), delta_err))
+    assert diff <= LAYER_TOL * _rms(ref[rows])
+    want = expected_pool_after(wl.pool, geo, bt, wl.positions, k_new, v_new, seqs)
+    if seqs is None:
+        kv_diff, kv_rms = check_pool_after(pool_after, want, wl.pool)
+        say("  appended K/V: max-abs %.3g (RMS %.3g)" % (kv_diff, kv_rms))
+    return diff
+
+
+def test_layer_c1_qwen_shape():
+    """One Qwen2.5-0.5B-shaped layer, batch 1, 127 cached + 1 new, 64-page pool."""
+    wl = synth.c1_layer()
+    _check_layer(wl.shape, wl.extra["weights"], wl.extra["hidden"], wl)
+
+
+@pytest.mark.parametrize("batch,hkv,heads", [(1, 2, 4), (3, 2, 14), (17, 1, 16), (40, 4, 8),
+                                             (70, 2, 4), (130, 2, 4)])
+def test_layer_tiny_shapes(batch, hkv, heads):
+    shape = synth.tiny_shape(hidden=192, heads=heads, kv_heads=hkv, inter=384, name="tiny-layer")
+    seed = 100 + batch
+    g = synth.rng(seed, "lens")
+    positions = g.integers(0, 300, size=batch).astype(np.int32)
+    positions[0] = 0
+    if batch > 2:
+        positions[1] = 15
+        positions[2] = 16
+    wl = synth.decode_workload("tiny", shape, seed, positions, layers=1)
+    lw = synth.layer_weights(shape, seed, 0, sigma=0.05, norm_sigma=0.3)
+    hidden = synth.rng(seed, "hidden").standard_normal((batch, shape.hidden)).astype(np.float32)
+    _check_layer(shape, lw, hidden, wl)
+
+
+def _check_step(shape, weights, wl, tokens, seqs=None, want_logits=True):
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
+    logits, nxt, pool_after, err = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions,
+                                            tokens, want_logits)
+    assert err == 0
+    ref_logits, ref_tok, _, _ = oracle.decode_step_paged(shape, weights, wl.pool, geo, wl.block_tables,
+                                                         wl.positions, tokens, seqs)
+    rows = list(range(len(tokens))) if seqs is None else list(seqs)
+    checked = check_argmax_rule(ref_logits[rows], nxt[rows])
+    msg = "step %s B=%d rows=%s: argmax checked %d/%d" % (shape.name, len(tokens), rows, checked, len(rows))
+    if logits is not None:
+        diff = np.abs(logits[rows] - ref_logits[rows]).max()
+        msg += ", max|dlogit| %.3g (RMS %.3g)" % (diff, _rms(ref_logits[rows]))
+        assert diff <= LAYER_TOL * _rms(ref_logits[rows])
+    say(msg)
+    return nxt
+
+
+def test_step_tiny_model():
+    shape = synth.tiny_shape(hidden=128, layers=3, heads=4, kv_heads=2, inter=256, vocab=1000)
+    positions = np.array([0, 5, 16, 47, 200], dtype=np.int32)
+    weights = synth.model_weights(shape, 7, sigma=0.05, norm_sigma=0.3)
+    wl = synth.decode_workload("tiny-step", shape, 7, positions)
+    tokens = synth.rng(7, "tokens").integers(0, shape.vocab, size=5)
+    nxt = _check_step(shape, weights, wl, tokens)
+    # the same step without logits gives the same tokens
+    _, nxt2, _, _ = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions, tokens,
+                             want_logits=False)
+    assert np.array_equal(nxt, nxt2)
+
+
+def test_step_c3_llama_shape_batch1():
+    """16-layer Llama-3.2-1B-shaped step, batch 1, context 1024."""
+    wl = synth.c3_step()
+    weights = synth.model_weights(wl.shape, 1003)
+    _check_step(wl.shape, weights, wl, wl.extra["tokens"])
+
+
+def test_step_c4_llama_shape_batch64_sampled():
+    """Batch 64, context U[64,2048]; the oracle checks a sample of sequences."""
+    wl = synth.c4_step()
+    weights = synth.model_weights(wl.shape, 1004)
+    order = np.argsort(wl.positions)
+    seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    _check_step(wl.shape, weights, wl, wl.extra["tokens"], seqs=seqs)
