@@ -66,7 +66,11 @@ extern "C" {
 
 #define PKV_PAGE_TOKENS 16
 #define PKV_HEAD_DIM 64
-#define PKV_MAX_BATCH_TILE 128
+
+/* Packed weight layouts (pkv_pack_weight). */
+#define PKV_PACK_ROWS 0     /* rows in order: w_o, w_down, embed / LM head   */
+#define PKV_PACK_QKV 1      /* w_qkv: the RoPE pairs of a head grouped        */
+#define PKV_PACK_GATE_UP 2  /* w_gate_up: 8 gate rows with their 8 up rows    */
 
 /* Sticky device-error bits (pkv_device_error). */
 #define PKV_DEVERR_PAGE 1u      /* block-table entry outside [0, num_pages) */
@@ -100,20 +104,25 @@ typedef struct pkv_pool {
 } pkv_pool;
 
 /*
- * One layer's weights, BF16, row-major [out][in] (the Hugging Face
- * orientation), no biases:
+ * One layer's weights, BF16, no biases.  The norms are plain [H] vectors;
+ * the four matrices are given by their row-major [out][in] form (the
+ * Hugging Face orientation) and passed PACKED (pkv_pack_weight, once, at
+ * load time):
  *   attn_norm [H], mlp_norm [H]                  RMSNorm weights
- *   w_qkv     [(Hq + 2 Hkv) * D][H]              q rows, then k rows, then v rows
- *   w_o       [H][Hq * D]
- *   w_gate_up [2 I][H]                           gate rows, then up rows
- *   w_down    [H][I]
+ *   w_qkv     [(Hq + 2 Hkv) * D][H]              q rows, then k rows, then v rows;
+ *                                                packed PKV_PACK_QKV
+ *   w_o       [H][Hq * D]                        packed PKV_PACK_ROWS
+ *   w_gate_up [2 I][H]                           gate rows, then up rows;
+ *                                                packed PKV_PACK_GATE_UP
+ *   w_down    [H][I]                             packed PKV_PACK_ROWS
  */
 typedef struct pkv_layer_weights {
 	const uint16_t *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gate_up, *w_down;
 } pkv_layer_weights;
 
 /*
- * Whole-model weights.  embed [V][H] BF16 is also the LM head (tied).
+ * Whole-model weights.  embed [V][H] BF16, packed PKV_PACK_ROWS, is both
+ * the embedding table (rows gathered by token id) and the LM head (tied).
  * layers is a HOST array of num_hidden_layers entries.  rope_cos/rope_sin
  * are device FP32 tables [max_position_embeddings][D/2] (pkv_rope_table).
  */
@@ -141,8 +150,9 @@ int kv_pool_create(void *dev_base, int64_t bytes, int32_t num_kv_heads,
  *   k_new, v_new [batch][Hkv][D] BF16.
  * Sequence b writes slot positions[b] % 16 of physical page
  * block_table[b][positions[b] / 16].  Bit-exact copy of the given values.
- * batch == 0 is a no-op.  Errors: -EINVAL, -ENOTSUP, -EIO; device errors
- * PKV_DEVERR_PAGE / PKV_DEVERR_LENGTH (that sequence is skipped).
+ * batch == 0 is a no-op.  Errors: -EINVAL, -ENOTSUP, -EIO.  This call takes
+ * no workspace, so a sequence whose position or table entry is out of
+ * range is skipped without a device-error report.
  */
 int kv_append(const pkv_pool *pool, const int32_t *block_table,
 	      int32_t max_pages, const int32_t *positions,
@@ -212,6 +222,39 @@ int decode_step(const pkv_config *cfg, const pkv_model_weights *w,
 		const int32_t *token_ids, int32_t batch, float *logits,
 		int32_t *next_tokens, void *workspace, size_t ws_bytes,
 		void *stream);
+
+/*
+ * Packed weight layout (used by every matrix the projections stream): the
+ * matrix is cut into groups of 16 rows and its columns into 32-wide steps;
+ * block (group G, step s) is 1 KiB, and its 16-byte chunk l = 16 i + m
+ * holds the 8 values W[row(G, m)][32 s + 8 i .. 32 s + 8 i + 7].  Blocks
+ * are ordered group-major, step-minor, so a group's columns are
+ * contiguous.  row(G, m) by layout (rows past the matrix are zero):
+ *   PKV_PACK_ROWS     16 G + m
+ *   PKV_PACK_QKV      head G / 4, j = 8 (G % 4) + (m % 8): row 64 head + j
+ *                     for m < 8, row 64 head + 32 + j for m >= 8 (the RoPE
+ *                     pairs of a head sit in one group)
+ *   PKV_PACK_GATE_UP  i = 8 G + (m % 8): gate row i for m < 8, up row I + i
+ *                     for m >= 8 (I = rows / 2)
+ * Each projection then reads whole 1 KiB blocks in the matrix-core operand
+ * order, which keeps every load instruction inside one 4 KiB page.
+ */
+
+/*
+ * Bytes of a packed [rows][cols] matrix (0 if cols is not a positive
+ * multiple of 32, rows < 1, or rows does not suit the layout: a multiple of
+ * 64 for PKV_PACK_QKV, of 16 for PKV_PACK_GATE_UP).
+ */
+size_t pkv_packed_weight_bytes(int32_t rows, int32_t cols, int32_t layout);
+
+/*
+ * pkv_pack_weight — write the packed form of a row-major BF16 matrix src
+ * [rows][cols] into dst (device, pkv_packed_weight_bytes bytes, 16-byte
+ * aligned; src and dst must not overlap).  Errors: -EINVAL (NULL,
+ * misaligned, bad sizes or layout), -ENOTSUP (matrix over 2 GiB), -EIO.
+ */
+int pkv_pack_weight(const uint16_t *src, int32_t rows, int32_t cols,
+		    int32_t layout, uint16_t *dst, void *stream);
 
 /* Workspace bytes decoder_layer_decode / decode_step need (0 on bad args). */
 size_t pkv_workspace_bytes(const pkv_config *cfg, int32_t batch,

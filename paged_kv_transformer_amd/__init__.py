@@ -8,7 +8,7 @@ is missing the first call raises.
 Entry points (same names as the C ABI): ``kv_pool_create``, ``kv_append``,
 ``paged_gqa_decode``, ``decoder_layer_decode``, ``decode_step``, plus
 ``workspace_bytes``, ``attention_workspace_bytes``, ``workspace_init``,
-``rope_table`` and ``device_error``.
+``rope_table``, ``pack_weight`` and ``device_error``.
 """
 import ctypes
 import errno
@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 PAGE_TOKENS = 16
 HEAD_DIM = 64
 DEVERR_PAGE, DEVERR_LENGTH, DEVERR_ROPE, DEVERR_TOKEN = 1, 2, 4, 8
+PACK_ROWS, PACK_QKV, PACK_GATE_UP = 0, 1, 2
 
 
 class PkvError(RuntimeError):
@@ -81,6 +82,8 @@ def lib():
             "pkv_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
             "pkv_workspace_init": (ctypes.c_int, [P, SZ, P]),
             "pkv_rope_table": (ctypes.c_int, [F, I32, I32, P, P, P]),
+            "pkv_packed_weight_bytes": (SZ, [I32, I32, I32]),
+            "pkv_pack_weight": (ctypes.c_int, [P, I32, I32, I32, P, P]),
             "pkv_device_error": (ctypes.c_int, [P, P]),
             "pkv_version": (ctypes.c_char_p, []),
         }
@@ -188,6 +191,25 @@ def rope_table(theta, max_pos, head_dim=HEAD_DIM, device="cuda", stream=None):
     return c, s
 
 
+# ---------------------------------------------------------------- packing ---
+
+def packed_weight_bytes(rows, cols, layout):
+    return lib().pkv_packed_weight_bytes(rows, cols, layout)
+
+
+def pack_weight(src, layout, stream=None):
+    """Packed copy (int16 device tensor) of a row-major BF16 [rows, cols]
+    device matrix, in the projections' tiled layout."""
+    rows, cols = src.shape
+    nbytes = packed_weight_bytes(rows, cols, layout)
+    if nbytes == 0:
+        raise ValueError("cannot pack a [%d, %d] matrix with layout %d" % (rows, cols, layout))
+    dst = torch.empty(nbytes // 2, dtype=torch.int16, device=src.device)
+    _check("pkv_pack_weight", lib().pkv_pack_weight(_dev(src, _BF16_DTYPES, "src"), rows, cols, layout,
+                                                    dst.data_ptr(), _stream(stream)))
+    return dst
+
+
 # ------------------------------------------------------------- attention ---
 
 def paged_gqa_decode(pool, q, block_table, context_lens, scale, out, workspace, stream=None):
@@ -205,7 +227,8 @@ def paged_gqa_decode(pool, q, block_table, context_lens, scale, out, workspace, 
 # ---------------------------------------------------------------- layers ---
 
 class DeviceLayer:
-    """One layer's device weights and the C struct pointing at them."""
+    """One layer's device weights (matrices already packed) and the C
+    struct pointing at them."""
 
     def __init__(self, tensors):
         self.tensors = {k: tensors[k] for k in LAYER_KEYS}
@@ -215,7 +238,8 @@ class DeviceLayer:
 
 
 class DeviceModel:
-    """Whole-model device weights (embed, final_norm, layers, RoPE tables)."""
+    """Whole-model device weights (packed embedding, final_norm, layers,
+    RoPE tables)."""
 
     def __init__(self, embed, final_norm, layers, rope_cos, rope_sin):
         self.embed, self.final_norm = embed, final_norm
@@ -264,12 +288,22 @@ def to_device(a, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+_LAYER_PACK = {"w_qkv": PACK_QKV, "w_o": PACK_ROWS, "w_gate_up": PACK_GATE_UP, "w_down": PACK_ROWS}
+
+
 def upload_layer(lw, device="cuda"):
-    return DeviceLayer({k: to_device(lw[k], device) for k in LAYER_KEYS})
+    """Row-major BF16 host matrices -> device, packed by the library."""
+    t = {}
+    for k in LAYER_KEYS:
+        d = to_device(lw[k], device)
+        t[k] = pack_weight(d, _LAYER_PACK[k]) if k in _LAYER_PACK else d
+    return DeviceLayer(t)
 
 
 def upload_model(weights, theta, max_pos, device="cuda"):
-    """weights: {'embed', 'final_norm', 'layers': [layer dicts]} of BF16 bits."""
+    """weights: {'embed', 'final_norm', 'layers': [layer dicts]} of BF16 bits
+    (row-major); the matrices are packed on the device."""
     c, s = rope_table(theta, max_pos, device=device)
-    return DeviceModel(to_device(weights["embed"], device), to_device(weights["final_norm"], device),
+    embed = pack_weight(to_device(weights["embed"], device), PACK_ROWS)
+    return DeviceModel(embed, to_device(weights["final_norm"], device),
                        [upload_layer(lw, device) for lw in weights["layers"]], c, s)

@@ -95,17 +95,24 @@ int gemm_batched(int epi, int N, int batch, const GemmArgs& base, F setup, hipSt
   return 0;
 }
 
-// One decoder layer over the whole batch, hidden [batch][H] in place.
+float* packed_at(float* base, int b0, int K) { return base + packed_act_index(b0, 0, K); }
+
+// One decoder layer over the whole batch.  hidden [batch][H] (plain) is
+// updated in place and also left packed in the workspace (x_p) for the next
+// projection; hidden_packed, if given, is hidden already packed.
 int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* rope_cos,
               const float* rope_sin, const pkv_pool* pool, const int32_t* bt, int32_t max_pages,
-              const int32_t* pos, int32_t batch, float* hidden, void* ws, const WsLayout& L,
-              hipStream_t st) {
+              const int32_t* pos, int32_t batch, float* hidden, const float* hidden_packed,
+              void* ws, const WsLayout& L, hipStream_t st) {
   const int H = cfg->hidden_size, Hq = cfg->num_attention_heads;
   const int Hkv = cfg->num_key_value_heads, I = cfg->intermediate_size;
+  const int QD = Hq * kHeadDim;
   float* q = at<float>(ws, L.q);
-  float* o = at<float>(ws, L.o);
+  float* o_p = at<float>(ws, L.o_p);
   float* h1 = at<float>(ws, L.h1);
-  float* act = at<float>(ws, L.act);
+  float* h1_p = at<float>(ws, L.h1_p);
+  float* act_p = at<float>(ws, L.act_p);
+  float* x_p = at<float>(ws, L.x_p);
   uint32_t* err = at<uint32_t>(ws, L.err);
   int rc;
 
@@ -117,9 +124,11 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   {
     GemmArgs a = base;
     a.W = w->w_qkv;
+    a.w_groups = (Hq + 2 * Hkv) * 4;
     a.xw = w->attn_norm;
     a.N = (Hq + 2 * Hkv) * kHeadDim;
     a.K = H;
+    a.x_plain = hidden_packed == nullptr;
     a.pool = (uint16_t*)pool->base;
     a.page_elems = pool->page_bytes / 2;
     a.num_pages = pool->num_pages;
@@ -130,15 +139,15 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.Hq = Hq;
     a.Hkv = Hkv;
     rc = gemm_batched(EPI_QKV, a.N, batch, a, [&](GemmArgs& c, int b0) {
-      c.X = hidden + (size_t)b0 * H;
-      c.q_out = q + (size_t)b0 * Hq * kHeadDim;
+      c.X = hidden_packed ? packed_at(const_cast<float*>(hidden_packed), b0, H) : hidden + (size_t)b0 * H;
+      c.q_out = q + (size_t)b0 * QD;
       c.bt = bt + (size_t)b0 * max_pages;
       c.pos = pos + b0;
     }, st);
     if (rc) return rc;
   }
 
-  // 2. paged attention over tokens 0..pos
+  // 2. paged attention over tokens 0..pos, output packed for the O projection
   {
     AttnArgs a{};
     a.q = q;
@@ -150,7 +159,8 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.lens = pos;
     a.len_add = 1;
     a.scale = 1.0f / sqrtf((float)kHeadDim);
-    a.out = o;
+    a.out = o_p;
+    a.out_packed = 1;
     a.part = at<float>(ws, L.attn_part);
     a.err = err;
     a.Hq = Hq;
@@ -164,11 +174,13 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   {
     GemmArgs a = base;
     a.W = w->w_o;
+    a.w_groups = H / 16;
     a.N = H;
-    a.K = Hq * kHeadDim;
+    a.K = QD;
     rc = gemm_batched(EPI_RESID, H, batch, a, [&](GemmArgs& c, int b0) {
-      c.X = o + (size_t)b0 * Hq * kHeadDim;
+      c.X = packed_at(o_p, b0, QD);
       c.out = h1 + (size_t)b0 * H;
+      c.out_packed = packed_at(h1_p, b0, H);
       c.resid = hidden + (size_t)b0 * H;
     }, st);
     if (rc) return rc;
@@ -178,13 +190,14 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   {
     GemmArgs a = base;
     a.W = w->w_gate_up;
+    a.w_groups = I / 8;
     a.xw = w->mlp_norm;
     a.N = 2 * I;
     a.K = H;
     a.I = I;
     rc = gemm_batched(EPI_SWIGLU, 2 * I, batch, a, [&](GemmArgs& c, int b0) {
-      c.X = h1 + (size_t)b0 * H;
-      c.act = act + (size_t)b0 * I;
+      c.X = packed_at(h1_p, b0, H);
+      c.act = packed_at(act_p, b0, I);
     }, st);
     if (rc) return rc;
   }
@@ -193,11 +206,13 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   {
     GemmArgs a = base;
     a.W = w->w_down;
+    a.w_groups = H / 16;
     a.N = H;
     a.K = I;
     rc = gemm_batched(EPI_RESID, H, batch, a, [&](GemmArgs& c, int b0) {
-      c.X = act + (size_t)b0 * I;
+      c.X = packed_at(act_p, b0, I);
       c.out = hidden + (size_t)b0 * H;
+      c.out_packed = packed_at(x_p, b0, H);
       c.resid = h1 + (size_t)b0 * H;
     }, st);
     if (rc) return rc;
@@ -308,7 +323,7 @@ int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
                                cfg->num_key_value_heads, cfg->intermediate_size,
                                cfg->vocab_size, max_pages, true);
   return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, positions, batch,
-                   hidden, workspace, L, (hipStream_t)stream);
+                   hidden, nullptr, workspace, L, (hipStream_t)stream);
 }
 
 int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* pool,
@@ -331,17 +346,19 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
   const WsLayout L = ws_layout(batch, H, cfg->num_attention_heads, cfg->num_key_value_heads,
                                cfg->intermediate_size, V, max_pages, true);
   float* x = at<float>(workspace, L.x);
+  float* x_p = at<float>(workspace, L.x_p);
   uint32_t* err = at<uint32_t>(workspace, L.err);
 
-  if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, batch, err, st)))) return rc;
+  if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, x_p, batch, err, st)))) return rc;
   for (int l = 0; l < cfg->num_hidden_layers; ++l) {
     rc = run_layer(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool,
                    block_tables + (size_t)l * batch * max_pages, max_pages, positions, batch, x,
-                   workspace, L, st);
+                   x_p, workspace, L, st);
     if (rc) return rc;
   }
   GemmArgs a{};
   a.W = w->embed;
+  a.w_groups = (V + 15) / 16;
   a.xw = w->final_norm;
   a.N = V;
   a.K = H;
@@ -349,12 +366,27 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
   a.err = err;
   a.amax_part = at<unsigned long long>(workspace, L.amax_part);
   rc = gemm_batched(EPI_LOGITS, V, batch, a, [&](GemmArgs& c, int b0) {
-    c.X = x + (size_t)b0 * H;
+    c.X = packed_at(x_p, b0, H);
     c.logits = logits ? logits + (size_t)b0 * V : nullptr;
     c.next_tok = next_tokens + b0;
   }, st);
   if (rc) return rc;
   return 0;
+}
+
+size_t pkv_packed_weight_bytes(int32_t rows, int32_t cols, int32_t layout) {
+  if (rows < 1 || cols < 32 || cols % 32 != 0 || layout < PACK_ROWS || layout > PACK_GATE_UP) return 0;
+  if (layout == PKV_PACK_QKV && rows % kHeadDim != 0) return 0;
+  if (layout == PKV_PACK_GATE_UP && rows % 16 != 0) return 0;
+  return (size_t)packed_weight_elems(rows, cols, layout) * 2;
+}
+
+int pkv_pack_weight(const uint16_t* src, int32_t rows, int32_t cols, int32_t layout, uint16_t* dst,
+                    void* stream) {
+  if (!src || !dst || pkv_packed_weight_bytes(rows, cols, layout) == 0) return -EINVAL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return -EINVAL;
+  if ((int64_t)rows * cols * 2 > INT32_MAX) return -ENOTSUP;
+  return io(launch_pack_weight(src, rows, cols, layout, dst, (hipStream_t)stream));
 }
 
 int pkv_workspace_init(void* workspace, size_t ws_bytes, void* stream) {

@@ -54,6 +54,16 @@ __device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Output element idx = g * D + d of kv head kvh of sequence b: plain
+// [B][Hq][D], or packed as the output projection's input ([B][Hq * D]).
+__device__ __forceinline__ void store_out(const AttnArgs& a, int b, int kvh, int idx, float v) {
+  const int k = kvh * a.G * kHeadDim + idx;
+  if (a.out_packed)
+    a.out[packed_act_index(b, k, a.Hq * kHeadDim)] = v;
+  else
+    a.out[(size_t)b * a.Hq * kHeadDim + k] = v;
+}
+
 // Keep the first `nv` of the four BF16 values in v (the rest -> +0).
 __device__ __forceinline__ u32x2 keep_first(u32x2 v, int nv) {
   if (nv >= 4) return v;
@@ -75,13 +85,12 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, grp = l >> 4;
   const int G = a.G;
-  float* outp = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * kHeadDim;
 
   int n = a.lens[b] + a.len_add;
   if (n < 0 || n > a.bt_stride * kPageTokens) {
     if (split == 0) {
       if (tid == 0) set_error(a.err, ERR_LENGTH);
-      for (int i = tid; i < G * kHeadDim; i += 256) outp[i] = 0.f;
+      for (int i = tid; i < G * kHeadDim; i += 256) store_out(a, b, kvh, i, 0.f);
     }
     return;
   }
@@ -89,7 +98,7 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
   const int ns = npages > 0 ? (npages + CP - 1) / CP : 1;
   if (split >= ns) return;
   if (n == 0) {
-    for (int i = tid; i < G * kHeadDim; i += 256) outp[i] = 0.f;
+    for (int i = tid; i < G * kHeadDim; i += 256) store_out(a, b, kvh, i, 0.f);
     return;
   }
 
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
       O += e * sm_o[ww][g][d];
     }
     if (ns == 1) {
-      outp[idx] = L > 0.f ? O / L : 0.f;
+      store_out(a, b, kvh, idx, L > 0.f ? O / L : 0.f);
     } else {
       if (d == 0) {
         rec[g] = M;
@@ -244,26 +253,50 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
 // workgroup.  The records come from the previous kernel on the stream.
 __global__ __launch_bounds__(256) void attention_merge_kernel(const AttnArgs a) {
   constexpr int CP = kAttnPagesPerSplit;
+  __shared__ float sm_M[16], sm_invL[16];
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int n = a.lens[b] + a.len_add;
   if (n <= 0 || n > a.bt_stride * kPageTokens) return;
   const int ns = ((n + kPageTokens - 1) / kPageTokens + CP - 1) / CP;
   if (ns <= 1) return;
   const int G = a.G;
-  float* outp = a.out + ((size_t)b * a.Hq + (size_t)kvh * G) * kHeadDim;
+  const int tid = threadIdx.x;
   const float* rec0 = a.part + ((size_t)b * a.Hkv + kvh) * a.max_splits * kAttnRec;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
-    const int g = idx >> 6;
+  // 1. per head: M = max_s m_s and 1 / sum_s e^(m_s - M) l_s, 16 lanes per
+  //    head, each over splits j, j + 16, ... (a fixed order)
+  {
+    const int g = tid >> 4, j = tid & 15;
+    const bool on = g < G;
     float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, rec0[(size_t)sp * kAttnRec + g]);
-    float L = 0.f, O = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float* r = rec0 + (size_t)sp * kAttnRec;
-      const float e = r[g] == -INFINITY ? 0.f : expf(r[g] - M);
-      L += e * r[16 + g];
-      O += e * r[32 + idx];
+    if (on)
+      for (int sp = j; sp < ns; sp += 16) M = fmaxf(M, rec0[(size_t)sp * kAttnRec + g]);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    float L = 0.f;
+    if (on)
+      for (int sp = j; sp < ns; sp += 16) {
+        const float m = rec0[(size_t)sp * kAttnRec + g];
+        L += (m == -INFINITY ? 0.f : expf(m - M)) * rec0[(size_t)sp * kAttnRec + 16 + g];
+      }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (on && j == 0) {
+      sm_M[g] = M;
+      sm_invL[g] = L > 0.f ? 1.f / L : 0.f;
     }
-    outp[idx] = L > 0.f ? O / L : 0.f;
+  }
+  __syncthreads();
+  // 2. outputs: o = sum_s e^(m_s - M) O_s / L, loads of the splits unrolled
+  for (int idx = tid; idx < G * kHeadDim; idx += 256) {
+    const int g = idx >> 6;
+    const float M = sm_M[g];
+    float O = 0.f;
+#pragma unroll 8
+    for (int sp = 0; sp < ns; ++sp) {
+      const float m = rec0[(size_t)sp * kAttnRec + g];
+      O += (m == -INFINITY ? 0.f : expf(m - M)) * rec0[(size_t)sp * kAttnRec + 32 + idx];
+    }
+    store_out(a, b, kvh, idx, O * sm_invL[g]);
   }
 }
 

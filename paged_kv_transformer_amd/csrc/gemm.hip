@@ -2,9 +2,9 @@
 //
 //   y[b][n] = sum_k W[n][k] * x[b][k] * xw[k]        (xw: RMSNorm weight or 1)
 //
-// W is BF16 [N][K] (the Hugging Face [out][in] orientation) and is read from
-// HBM exactly once per launch; the batch of FP32 activations is tiny and is
-// read from L2.  This is the decode step's dense contraction (the engine
+// W is BF16 [N][K] (the Hugging Face [out][in] orientation, packed into
+// 16-row x 32-column blocks at load time) and is read from HBM exactly once
+// per launch; the batch of FP32 activations is tiny and is read from L2.  This is the decode step's dense contraction (the engine
 // packs one token of every active sequence into each step), so it runs on
 // the matrix cores: v_mfma_f32_16x16x32_bf16 with W rows as the A operand
 // (each lane streams 16-byte pieces of one row) and the batch as the B
@@ -27,9 +27,10 @@
 //               sequence's position); q -> FP32 buffer, k and v -> BF16
 //               (nearest even) into the sequence's page at its position
 //               (the KV append).
-//   EPI_RESID   out = resid + y (output projection, down projection).
+//   EPI_RESID   out = resid + y (output projection, down projection), also
+//               written packed for the next projection.
 //   EPI_SWIGLU  each 16-row group = 8 gate rows + the 8 matching up rows:
-//               a = silu(gate) * up.
+//               a = silu(gate) * up, written packed for the down projection.
 //   EPI_LOGITS  FP32 logits (optional store) and, per tile and sequence,
 //               the largest logit packed with its index; a small kernel
 //               then reduces the tiles to the token ids.
@@ -45,6 +46,15 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Raw buffer descriptor over `bytes` bytes at p (gfx9 dword 3: 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
 }
@@ -58,23 +68,7 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int n) {
   return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n);
 }
 
-// Matrix row of MFMA row m (0..15) of row group g in tile t, or -1.
-template <int EPI, int RG>
-__device__ __forceinline__ int tile_row(const GemmArgs& a, int t, int g, int m) {
-  if (EPI == EPI_QKV) {
-    // tile t: head t/4, RoPE pairs j = 8*(t%4) + i (rows j and j + 32)
-    const int j0 = 8 * (t & 3);
-    return (t >> 2) * kHeadDim + (m < 8 ? j0 + m : 32 + j0 + (m - 8));
-  }
-  if (EPI == EPI_SWIGLU) {
-    const int i = 8 * (t * RG + g) + (m & 7);
-    return i < a.I ? (m < 8 ? i : a.I + i) : -1;
-  }
-  const int n = (t * RG + g) * 16 + m;
-  return n < a.N ? n : -1;
-}
-
-template <int CT, int RG, int NW, int EPI>
+template <int CT, int RG, int NW, int EPI, bool XPLAIN>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int U = 2;        // 32-wide K steps per pipeline stage
@@ -95,23 +89,36 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   const int s0 = w * spw;
   const int s1 = min(s0 + spw, steps);
 
-  // A operand rows (row l % 16 of each group) and B operand columns
-  // (column l % 16 of each column group); K offset 8 * (l / 16) in a step.
-  // Rows past N and columns past B read row 0 / column 0 and are never stored.
+  // Buffer loads: one descriptor per operand in scalar registers, a fixed
+  // per-lane byte offset in a vector register, and the step's offset as a
+  // scalar, so the loop carries no vector address arithmetic (which would
+  // otherwise make the prefetch wait on its own registers).  W is packed:
+  // a 16-row group's step is one contiguous 1 KiB block in lane order.  X is
+  // packed (a lane's 8 values of a step are 32 contiguous bytes) except for
+  // a caller's plain [B][K] input.  Every instruction thus reads contiguous
+  // memory: spreading one instruction over 16 rows of a large matrix costs
+  // one address translation per row and serialises the L1 TLB.
+  // Groups past the matrix read its last group; columns past B read zeros
+  // or column 0; neither is ever stored.
   const int koff = 8 * (l >> 4);
-  const uint16_t* wrow[RG];
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(a.W, (uint32_t)a.w_groups * (uint32_t)a.K * 32u);
+  const __amdgpu_buffer_rsrc_t xres =
+      make_rsrc(a.X, (uint32_t)(XPLAIN ? a.B : (a.B + 15) / 16 * 16) * (uint32_t)a.K * 4u);
+  const __amdgpu_buffer_rsrc_t xwres = make_rsrc(NORM ? a.xw : a.W, (uint32_t)a.K * 2u);
+  int woff[RG];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const int n = tile_row<EPI, RG>(a, t, g, l & 15);
-    wrow[g] = a.W + (size_t)(n >= 0 ? n : 0) * a.K + koff;
-  }
-  const float* xrow[CT];
+  for (int g = 0; g < RG; ++g) woff[g] = (min(t * RG + g, a.w_groups - 1) * steps * 64 + l) * 16;
+  int xoff[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
-    const int b = 16 * c + (l & 15);
-    xrow[c] = a.X + (size_t)(b < a.B ? b : 0) * a.K + koff;
+    if (XPLAIN) {
+      const int b = 16 * c + (l & 15);
+      xoff[c] = ((b < a.B ? b : 0) * a.K + koff) * 4;
+    } else {
+      xoff[c] = (c * steps * 64 + l) * 32;
+    }
   }
-  const uint16_t* xwp = NORM ? a.xw + koff : nullptr;
+  const int xwoff = koff * 2;
 
   f32x4 acc[RG][CT];
 #pragma unroll
@@ -136,13 +143,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     for (int u = 0; u < U; ++u) {
       const int k = min(st + u, s1 - 1) * 32;
 #pragma unroll
-      for (int g = 0; g < RG; ++g) S.w[u][g] = __builtin_nontemporal_load((const u32x4*)(wrow[g] + k));
+      for (int g = 0; g < RG; ++g) S.w[u][g] = bload(wres, woff[g], k * 32);
+      const int xs = XPLAIN ? k * 4 : k * 64;
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        S.x[u][c][0] = *(const float4*)(xrow[c] + k);
-        S.x[u][c][1] = *(const float4*)(xrow[c] + k + 4);
+        S.x[u][c][0] = __builtin_bit_cast(float4, bload(xres, xoff[c], xs));
+        S.x[u][c][1] = __builtin_bit_cast(float4, bload(xres, xoff[c] + 16, xs));
       }
-      if (NORM) S.xw[u] = *(const uint4*)(xwp + k);
+      if (NORM) S.xw[u] = __builtin_bit_cast(uint4, bload(xwres, xwoff, k * 2));
     }
   };
   auto compute = [&](const Stage& S, int st) {
@@ -228,7 +236,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       const int n = t * R + row;
       if (n < a.N) {
         const size_t o = (size_t)c * a.N + n;
-        a.out[o] = a.resid[o] + tile[c * TS + row];
+        const float v = a.resid[o] + tile[c * TS + row];
+        a.out[o] = v;
+        if (a.out_packed) a.out_packed[packed_act_index(c, n, a.N)] = v;
       }
     }
   } else if (EPI == EPI_QKV) {
@@ -288,7 +298,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       const float rs = 1.0f / sqrtf(ssq_col[c] / (float)a.K + a.eps);
       const float gv = tile[c * TS + 16 * g + m] * rs;
       const float uv = tile[c * TS + 16 * g + 8 + m] * rs;
-      a.act[(size_t)c * a.I + i] = gv / (1.0f + expf(-gv)) * uv;
+      a.act[packed_act_index(c, i, a.I)] = gv / (1.0f + expf(-gv)) * uv;
     }
   } else {  // EPI_LOGITS
     for (int i = tid; i < R * a.B; i += NT) {
@@ -333,9 +343,9 @@ __global__ void argmax_finalize_kernel(const unsigned long long* part, int tiles
   if (threadIdx.x == 0) next_tok[c] = (int32_t)(0xffffffffu - (uint32_t)(sm[0] & 0xffffffffull));
 }
 
-template <int CT, int RG, int NW, int EPI>
+template <int CT, int RG, int NW, int EPI, bool XPLAIN = false>
 hipError_t go(const GemmArgs& a, int tiles, hipStream_t st) {
-  gemm_kernel<CT, RG, NW, EPI><<<tiles, NW * 64, 0, st>>>(a);
+  gemm_kernel<CT, RG, NW, EPI, XPLAIN><<<tiles, NW * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -346,7 +356,10 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
   const bool one = p.ct == 1;
   switch (epi) {
     case EPI_QKV:
-      e = one ? go<1, 1, 8, EPI_QKV>(a, p.tiles, st) : go<2, 1, 8, EPI_QKV>(a, p.tiles, st);
+      if (a.x_plain)
+        e = one ? go<1, 1, 8, EPI_QKV, true>(a, p.tiles, st) : go<2, 1, 8, EPI_QKV, true>(a, p.tiles, st);
+      else
+        e = one ? go<1, 1, 8, EPI_QKV>(a, p.tiles, st) : go<2, 1, 8, EPI_QKV>(a, p.tiles, st);
       break;
     case EPI_RESID:
       e = one ? go<1, 1, 16, EPI_RESID>(a, p.tiles, st) : go<2, 1, 16, EPI_RESID>(a, p.tiles, st);

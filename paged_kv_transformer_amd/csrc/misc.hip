@@ -1,5 +1,5 @@
 // Small kernels of the decode path: the standalone KV append, the embedding
-// gather, the RoPE cos/sin table and a workspace fill.
+// gather, the weight packing, the RoPE cos/sin table and a workspace fill.
 #include "pkv_dev.h"
 
 namespace pkv {
@@ -29,19 +29,50 @@ __global__ void kv_append_kernel(uint16_t* pool, int64_t page_elems, int32_t num
   }
 }
 
-// x[b] = E[token[b]] widened from BF16 to FP32 (the engine's embedding gather).
+// x[b] = E[token[b]] widened from BF16 to FP32 (the engine's embedding
+// gather), read from the packed embedding (which is also the tied LM head)
+// and written both plain and packed (the first projection's input).  One
+// thread per 8 consecutive elements (H is a multiple of 64): one 16-byte
+// load, no loop.
 __global__ void embed_kernel(const uint16_t* E, int V, int H, const int32_t* tok, float* x,
-                             uint32_t* err) {
-  const int b = blockIdx.x;
+                             float* xp, uint32_t* err) {
+  const int b = blockIdx.y;
+  const int k = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (k >= H) return;
   const int t = tok[b];
-  float* xr = x + (size_t)b * H;
+  float4* xr = (float4*)(x + (size_t)b * H + k);
+  float4* xq = (float4*)(xp + packed_act_index(b, k, H));
+  float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
   if ((unsigned)t >= (unsigned)V) {
-    if (threadIdx.x == 0) set_error(err, ERR_TOKEN);
-    for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = 0.f;
-    return;
+    if (k == 0) set_error(err, ERR_TOKEN);
+  } else {
+    // packed block (group t / 16, step k / 32), lane 16 ((k % 32) / 8) + t % 16
+    const int64_t e = ((((int64_t)(t >> 4) * (H >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (t & 15)) << 3);
+    const uint4 w = *(const uint4*)(E + e);
+    lo = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+    hi = make_float4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w));
   }
-  const uint16_t* er = E + (size_t)t * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) xr[i] = __uint_as_float((uint32_t)er[i] << 16);
+  xr[0] = lo;
+  xr[1] = hi;
+  xq[0] = lo;
+  xq[1] = hi;
+}
+
+// Packs a row-major [rows][cols] BF16 matrix (cols a multiple of 32): one
+// thread per 16-byte lane chunk of a 1 KiB block (group G, step s, lane l).
+__global__ void pack_weight_kernel(const uint16_t* src, int rows, int cols, int kind,
+                                   uint16_t* dst, int64_t chunks) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  const int S = cols >> 5;
+  const int l = (int)(c & 63);
+  const int64_t gs = c >> 6;
+  const int s = (int)(gs % S);
+  const int G = (int)(gs / S);
+  const int r = packed_row(kind, rows, G, l & 15);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (r >= 0) v = *(const uint4*)(src + (size_t)r * cols + 32 * s + 8 * (l >> 4));
+  *(uint4*)(dst + (c << 3)) = v;
 }
 
 // cos/sin of p * theta^(-2j/D) in double, rounded to FP32.
@@ -74,9 +105,18 @@ hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_page
   return hipGetLastError();
 }
 
-hipError_t launch_embed(const uint16_t* E, int V, int H, const int32_t* tok, float* x, int batch,
-                        uint32_t* err, hipStream_t st) {
-  embed_kernel<<<batch, 256, 0, st>>>(E, V, H, tok, x, err);
+hipError_t launch_embed(const uint16_t* E_packed, int V, int H, const int32_t* tok, float* x,
+                        float* x_packed, int batch, uint32_t* err, hipStream_t st) {
+  const dim3 grid((H / 8 + 255) / 256, batch);
+  embed_kernel<<<grid, 256, 0, st>>>(E_packed, V, H, tok, x, x_packed, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weight(const uint16_t* src, int rows, int cols, int kind, uint16_t* dst,
+                              hipStream_t st) {
+  const int64_t chunks = packed_weight_elems(rows, cols, kind) / 8;
+  pack_weight_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>(src, rows, cols, kind, dst,
+                                                                       chunks);
   return hipGetLastError();
 }
 

@@ -33,6 +33,49 @@ __device__ __forceinline__ void set_error(uint32_t* err, uint32_t bits) {
   __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------- packed layouts ---
+//
+// Weights (BF16), packed once at load time: the matrix is cut into groups
+// of 16 rows (rows past the end are zero) and each group's K into 32-wide
+// steps; block (group G, step s) is 1 KiB holding, for lane l = 16 i + m,
+// the 8 values W[row(G, m)][32 s + 8 i .. + 8].  A wave streams a group's
+// K range as contiguous 1 KiB blocks, already in the A-operand layout of
+// v_mfma_f32_16x16x32_bf16.  row(G, m) depends on the layout kind:
+enum PackKind { PACK_ROWS = 0, PACK_QKV = 1, PACK_GATE_UP = 2 };
+
+// Matrix row held by row m (0..15) of 16-row group G, or -1 (zero rows).
+__host__ __device__ inline int packed_row(int kind, int rows, int G, int m) {
+  if (kind == PACK_QKV) {
+    // group G: head G / 4, RoPE pairs j = 8 (G % 4) + i, rows j and j + 32
+    const int j0 = 8 * (G & 3);
+    const int r = (G >> 2) * kHeadDim + (m < 8 ? j0 + m : 32 + j0 + (m - 8));
+    return r < rows ? r : -1;
+  }
+  if (kind == PACK_GATE_UP) {
+    // group G: gate rows i .. i + 7 then the matching up rows (I = rows / 2)
+    const int I = rows / 2, i = 8 * G + (m & 7);
+    return i < I ? (m < 8 ? i : I + i) : -1;
+  }
+  const int r = 16 * G + m;
+  return r < rows ? r : -1;
+}
+
+inline int64_t packed_weight_elems(int rows, int cols, int kind) {
+  const int per = kind == PACK_GATE_UP ? 8 : 16;  // matrix rows of each kind per group
+  const int64_t groups = kind == PACK_GATE_UP ? ((rows / 2) + per - 1) / per : (rows + per - 1) / per;
+  return groups * 16 * (int64_t)cols;
+}
+
+// Activations (FP32) that feed a projection, [B][K] re-laid out so that a
+// lane's B operand of one step is 32 contiguous bytes: column block cb of
+// 16 columns, step s, lane l = 16 i + c holds X[16 cb + c][32 s + 8 i .. + 8].
+__host__ __device__ inline int64_t packed_act_index(int b, int k, int K) {
+  const int S = K >> 5;
+  return ((((int64_t)(b >> 4) * S + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (b & 15)) << 3) + (k & 7);
+}
+
+inline int64_t packed_act_elems(int B, int K) { return (int64_t)((B + 15) / 16) * 16 * K; }
+
 // --------------------------------------------------------- arguments ---
 
 struct AttnArgs {
@@ -45,7 +88,8 @@ struct AttnArgs {
   const int32_t* lens;     // [B]: attention length, or position (len_add = 1)
   int32_t len_add;
   float scale;
-  float* out;              // [B][Hq][D] FP32
+  float* out;              // [B][Hq][D] FP32, or packed as [B][Hq * D] if out_packed
+  int32_t out_packed;
   float* part;             // split partial records [B][Hkv][max_splits][kAttnRec]
   uint32_t* err;
   int32_t Hq, Hkv, G;
@@ -55,15 +99,19 @@ struct AttnArgs {
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 struct GemmArgs {
-  const uint16_t* W;       // [N][K] BF16 bits, row-major
-  const float* X;          // [B][K] FP32 activations
+  const uint16_t* W;       // packed BF16 weights of N rows x K
+  const float* X;          // FP32 activations, packed ([B][K] if x_plain)
+  int32_t x_plain;         // X is a plain row-major [B][K] array
   const uint16_t* xw;      // RMSNorm weight [K] (epilogues that normalise)
   int32_t N, K, B;
+  int32_t w_groups;        // 16-row groups in the packed W
   float eps;
   uint32_t* err;
-  // EPI_RESID: out[b][n] = resid[b][n] + y
+  // EPI_RESID: out[b][n] = resid[b][n] + y (plain), and packed into
+  // out_packed (if not null) for the next projection
   float* out;
   const float* resid;
+  float* out_packed;
   // EPI_QKV
   float* q_out;            // [B][Hq][D]
   uint16_t* pool;
@@ -76,7 +124,7 @@ struct GemmArgs {
   const float* rsin;
   int32_t max_pos;
   int32_t Hq, Hkv;
-  // EPI_SWIGLU: act[b][i], i < I
+  // EPI_SWIGLU: act[b][i], i < I, packed (the down projection's input)
   float* act;
   int32_t I;
   // EPI_LOGITS
@@ -126,7 +174,7 @@ inline GemmPlan plan_gemm(int epi, int N, int B) {
 }
 
 struct WsLayout {
-  size_t err, q, o, h1, act, x;
+  size_t err, q, o_p, h1, h1_p, act_p, x, x_p;
   size_t attn_part, amax_part;
   size_t total;
 };
@@ -142,10 +190,12 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_p
   w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_pages) * kAttnRec);
   if (layer) {
     w.q = take(sizeof(float) * (size_t)B * Hq * kHeadDim);
-    w.o = take(sizeof(float) * (size_t)B * Hq * kHeadDim);
+    w.o_p = take(sizeof(float) * (size_t)packed_act_elems(B, Hq * kHeadDim));
     w.h1 = take(sizeof(float) * (size_t)B * H);
-    w.act = take(sizeof(float) * (size_t)B * I);
+    w.h1_p = take(sizeof(float) * (size_t)packed_act_elems(B, H));
+    w.act_p = take(sizeof(float) * (size_t)packed_act_elems(B, I));
     w.x = take(sizeof(float) * (size_t)B * H);
+    w.x_p = take(sizeof(float) * (size_t)packed_act_elems(B, H));
     const int Bc = B < kGemmMaxCols ? B : kGemmMaxCols;
     const GemmPlan lm = plan_gemm(EPI_LOGITS, V, Bc);
     w.amax_part = take(sizeof(unsigned long long) * (size_t)lm.tiles * (Bc > 0 ? Bc : 1));
@@ -164,8 +214,10 @@ hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_page
                             const int32_t* bt, int32_t bt_stride, const int32_t* pos,
                             const uint16_t* k, const uint16_t* v, int batch, int Hkv,
                             hipStream_t st);
-hipError_t launch_embed(const uint16_t* E, int V, int H, const int32_t* tok, float* x,
-                        int batch, uint32_t* err, hipStream_t st);
+hipError_t launch_embed(const uint16_t* E_packed, int V, int H, const int32_t* tok, float* x,
+                        float* x_packed, int batch, uint32_t* err, hipStream_t st);
+hipError_t launch_pack_weight(const uint16_t* src, int rows, int cols, int kind, uint16_t* dst,
+                              hipStream_t st);
 hipError_t launch_rope_table(double theta, int D, int max_pos, float* c, float* s,
                              hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
