@@ -172,8 +172,8 @@ int kv_append(const pkv_pool *pool, const int32_t *block_table,
  * in the pool (work is split on logical pages).  workspace: at least
  * pkv_attention_workspace_bytes(...) bytes, initialised once.
  * Errors: -EINVAL (NULL, Hq % Hkv != 0, batch < 0, max_pages < 1),
- * -ENOTSUP (Hq / Hkv > 16), -ENOSPC (workspace), -EIO; device errors
- * PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH.
+ * -ENOTSUP (Hq / Hkv > 16, batch > 65535, max_pages > 524280), -ENOSPC
+ * (workspace), -EIO; device errors PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH.
  */
 int paged_gqa_decode(const pkv_pool *pool, const uint16_t *q,
 		     int32_t num_q_heads, const int32_t *block_table,

@@ -71,7 +71,7 @@ int check_layer_call(const pkv_config* cfg, const pkv_pool* pool, const float* r
   if (rc) return rc;
   if (pool->num_kv_heads != cfg->num_key_value_heads) return -EINVAL;
   if (batch < 0 || max_pages < 1) return -EINVAL;
-  if (batch > 65535) return -ENOTSUP;
+  if (batch > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
   if (!rope_cos || !rope_sin || !bt || !positions || !ws) return -EINVAL;
   if (!aligned(ws, 256)) return -EINVAL;
   const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
@@ -281,7 +281,7 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   rc = check_heads(num_q_heads, pool->num_kv_heads);
   if (rc) return rc;
   if (batch < 0 || max_pages < 1) return -EINVAL;
-  if (batch > 65535) return -ENOTSUP;
+  if (batch > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
   if (batch == 0) return 0;
   if (!q || !block_table || !context_lens || !out || !workspace) return -EINVAL;
   if (!aligned(workspace, 256) || !isfinite(scale)) return -EINVAL;

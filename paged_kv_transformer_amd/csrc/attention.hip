@@ -21,11 +21,17 @@
 // keeps (m, l, O); waves and then splits are merged with the log-sum-exp
 // rule m = max m_i, l = sum l_i e^(m_i - m), O = sum O_i e^(m_i - m), in a
 // fixed order, so the result depends only on the logical page sequence
-// (never on where pages sit in the pool).  A sequence that fits one split
-// is finished by its workgroup; otherwise every split leaves its (m, l, O)
-// record and a second, small kernel merges them: workgroups never wait on
-// one another (on this GPU a cross-workgroup handoff inside a kernel costs
-// more than the extra launch).
+// (never on where pages sit in the pool).  When the block table allows a
+// single split, the workgroup finishes its sequence; otherwise every split
+// leaves its (m, l, O) record and a second, small kernel merges them:
+// workgroups never wait on one another (on this GPU a cross-workgroup
+// handoff inside a kernel costs more than the extra launch).
+//
+// Latency matters as much as bandwidth here (a 16-sequence call moves tens
+// of MB, a few microseconds at HBM speed), so every dependent round trip is
+// counted: the length and block-table entries are loaded together, then
+// all K, V and q loads of a wave are issued back to back before any use,
+// and the merge kernel reads nothing but its records.
 #include "pkv_dev.h"
 
 namespace pkv {
@@ -81,60 +87,56 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
   __shared__ float sm_l[4][16];
   __shared__ float sm_o[4][16][kHeadDim + 1];
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int kvh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, grp = l >> 4;
   const int G = a.G;
 
-  int n = a.lens[b] + a.len_add;
-  if (n < 0 || n > a.bt_stride * kPageTokens) {
-    if (split == 0) {
-      if (tid == 0) set_error(a.err, ERR_LENGTH);
+  // ---- the length and this wave's block-table entries (index clamped to
+  // the table row; entries past the sequence are masked below), in flight
+  // together: the empty asm makes the entries live before the length test,
+  // so they are not sunk below it into a second round trip.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
+  int page[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) page[i] = btrow[min(split * CP + 4 * i + wu, a.bt_stride - 1)];
+  const int n = a.lens[b] + a.len_add;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) asm volatile("" ::"s"(page[i]));
+  // With one split per sequence (max_splits == 1) the workgroup writes the
+  // output itself; otherwise every workgroup leaves a record, an empty one
+  // (m = -inf) when it has no tokens, and the merge kernel writes every
+  // output.
+  const bool single = a.max_splits == 1;
+  float* rec = a.part + (((size_t)b * a.Hkv + kvh) * a.max_splits + split) * kAttnRec;
+  const bool bad_len = n < 0 || n > a.bt_stride * kPageTokens;
+  if (bad_len && split == 0 && tid == 0) set_error(a.err, ERR_LENGTH);
+  const int npages = bad_len ? 0 : (n + kPageTokens - 1) / kPageTokens;
+  const int ns = npages > 0 ? (npages + CP - 1) / CP : 1;
+  if (npages == 0 || split >= ns) {
+    if (single) {
       for (int i = tid; i < G * kHeadDim; i += 256) store_out(a, b, kvh, i, 0.f);
+    } else if (tid < G) {
+      rec[tid] = -INFINITY;
     }
     return;
   }
-  const int npages = (n + kPageTokens - 1) / kPageTokens;
-  const int ns = npages > 0 ? (npages + CP - 1) / CP : 1;
-  if (split >= ns) return;
-  if (n == 0) {
-    for (int i = tid; i < G * kHeadDim; i += 256) store_out(a, b, kvh, i, 0.f);
-    return;
-  }
 
-  // ---- issue every load of this wave up front, unconditionally (addresses
-  // are clamped to valid memory; invalid pages are masked afterwards), so
-  // all of them are in flight together: block-table entries, then per page
-  // K (2 x 16 B) and V (4 x 8 B), then this lane's q values.
-  int page[PW];
+  // ---- every remaining load of the wave, issued back to back before any
+  // use (the scheduling barrier keeps the compiler from interleaving them
+  // with the arithmetic): q, then per page K (2 x 16 B) and V (4 x 8 B).  A
+  // page past the sequence or outside the pool reads page 0 and is masked.
   int lpv[PW];
-  const int wu = __builtin_amdgcn_readfirstlane(w);
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int lp = split * CP + 4 * i + wu;  // uniform across the wave
-    page[i] = a.bt[(size_t)b * a.bt_stride + min(lp, npages - 1)];
-  }
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const int lp = split * CP + 4 * i + wu;
     const bool live = lp < npages;
     const bool ok = (unsigned)page[i] < (unsigned)a.num_pages;
-    if (live && !ok && l == 0) set_error(a.err, ERR_PAGE);
+    bad |= live && !ok;
     lpv[i] = live && ok ? lp : -1;
     page[i] = live && ok ? page[i] : 0;
-  }
-  u32x4 kr[PW][2];
-  u32x2 vr[PW][4];
-  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * kHeadDim;
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
-    const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * kHeadDim + 8 * grp;
-    kr[i][0] = *(const u32x4*)kp;
-    kr[i][1] = *(const u32x4*)(kp + 32);
-    const uint16_t* vp = pg + vblk + ((int64_t)kvh * kHeadDim + col) * kPageTokens + 4 * grp;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
   }
   // q^T operand (prescaled): lane holds head g = col, dims 8*grp + e + 32*h;
   // lanes past the group read head 0 of the group and use zeros
@@ -145,6 +147,25 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
     load_q8(qp, qv[0]);
     load_q8(qp + 32, qv[1]);
   }
+  u32x4 kr[PW][2];
+  u32x2 vr[PW][4];
+  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
+    const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * kHeadDim + 8 * grp;
+    kr[i][0] = *(const u32x4*)kp;
+    kr[i][1] = *(const u32x4*)(kp + 32);
+  }
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
+    const uint16_t* vp = pg + vblk + ((int64_t)kvh * kHeadDim + col) * kPageTokens + 4 * grp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (bad && l == 0) set_error(a.err, ERR_PAGE);
   bf16x8 qh[2], ql[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -224,7 +245,6 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
     }
   __syncthreads();
 
-  float* rec = a.part + (((size_t)b * a.Hkv + kvh) * a.max_splits + split) * kAttnRec;
   for (int idx = tid; idx < G * kHeadDim; idx += 256) {
     const int g = idx >> 6, d = idx & 63;
     const float M = fmaxf(fmaxf(sm_m[0][g], sm_m[1][g]), fmaxf(sm_m[2][g], sm_m[3][g]));
@@ -236,7 +256,7 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
       L += e * sm_l[ww][g];
       O += e * sm_o[ww][g][d];
     }
-    if (ns == 1) {
+    if (single) {
       store_out(a, b, kvh, idx, L > 0.f ? O / L : 0.f);
     } else {
       if (d == 0) {
@@ -248,62 +268,63 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
   }
 }
 
-// Merge of the split records of every (sequence, kv head) that took more
-// than one split; sequences that fit one split were finished by their only
-// workgroup.  The records come from the previous kernel on the stream.
+// Merge of the split records of every (sequence, kv head), launched when
+// max_splits > 1; the records come from the previous kernel on the stream.
+// A split with no tokens left an empty record (m = -inf), so the merge needs
+// neither the lengths nor any other input than the records.  One thread per
+// output (head g, dim d) combines the splits in order, 16 at a time: the
+// m, l and O of 16 splits are loaded together (split indexes clamped to the
+// record array and masked past it), so up to 16 splits cost one round of
+// loads.  The kernel arguments are read in one batch on entry.
 __global__ __launch_bounds__(256) void attention_merge_kernel(const AttnArgs a) {
-  constexpr int CP = kAttnPagesPerSplit;
-  __shared__ float sm_M[16], sm_invL[16];
+  constexpr int CH = 16;
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int n = a.lens[b] + a.len_add;
-  if (n <= 0 || n > a.bt_stride * kPageTokens) return;
-  const int ns = ((n + kPageTokens - 1) / kPageTokens + CP - 1) / CP;
-  if (ns <= 1) return;
-  const int G = a.G;
-  const int tid = threadIdx.x;
-  const float* rec0 = a.part + ((size_t)b * a.Hkv + kvh) * a.max_splits * kAttnRec;
-  // 1. per head: M = max_s m_s and 1 / sum_s e^(m_s - M) l_s, 16 lanes per
-  //    head, each over splits j, j + 16, ... (a fixed order)
-  {
-    const int g = tid >> 4, j = tid & 15;
-    const bool on = g < G;
-    float M = -INFINITY;
-    if (on)
-      for (int sp = j; sp < ns; sp += 16) M = fmaxf(M, rec0[(size_t)sp * kAttnRec + g]);
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float L = 0.f;
-    if (on)
-      for (int sp = j; sp < ns; sp += 16) {
-        const float m = rec0[(size_t)sp * kAttnRec + g];
-        L += (m == -INFINITY ? 0.f : expf(m - M)) * rec0[(size_t)sp * kAttnRec + 16 + g];
-      }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) L += __shfl_xor(L, o);
-    if (on && j == 0) {
-      sm_M[g] = M;
-      sm_invL[g] = L > 0.f ? 1.f / L : 0.f;
-    }
-  }
-  __syncthreads();
-  // 2. outputs: o = sum_s e^(m_s - M) O_s / L, loads of the splits unrolled
+  const int G = a.G, tid = threadIdx.x, S = a.max_splits;
+  asm volatile("" ::"s"(a.part), "s"(a.out), "s"(a.Hq), "s"(a.Hkv), "s"(a.G), "s"(a.max_splits),
+               "s"(a.out_packed));
+  const float* rec0 = a.part + ((size_t)b * a.Hkv + kvh) * S * kAttnRec;
   for (int idx = tid; idx < G * kHeadDim; idx += 256) {
     const int g = idx >> 6;
-    const float M = sm_M[g];
-    float O = 0.f;
-#pragma unroll 8
-    for (int sp = 0; sp < ns; ++sp) {
-      const float m = rec0[(size_t)sp * kAttnRec + g];
-      O += (m == -INFINITY ? 0.f : expf(m - M)) * rec0[(size_t)sp * kAttnRec + 32 + idx];
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int c0 = 0; c0 < S; c0 += CH) {
+      float m[CH], lv[CH], ov[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const float* r = rec0 + (size_t)min(c0 + j, S - 1) * kAttnRec;
+        m[j] = r[g];
+        lv[j] = r[16 + g];
+        ov[j] = r[32 + idx];
+      }
+      float Mc = M;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        m[j] = c0 + j < S ? m[j] : -INFINITY;
+        Mc = fmaxf(Mc, m[j]);
+      }
+      const float sc = M == -INFINITY ? 0.f : expf(M - Mc);
+      L *= sc;
+      O *= sc;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const bool on = m[j] != -INFINITY;
+        const float e = on ? expf(m[j] - Mc) : 0.f;
+        L += on ? e * lv[j] : 0.f;
+        O += on ? e * ov[j] : 0.f;
+      }
+      M = Mc;
     }
-    store_out(a, b, kvh, idx, O * sm_invL[g]);
+    store_out(a, b, kvh, idx, L > 0.f ? O / L : 0.f);
   }
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int batch, bool q_is_bf16, hipStream_t st) {
-  const dim3 grid(a.max_splits, a.Hkv, batch);
+  // kv head fastest: workgroups go to the 8 XCDs round-robin in launch
+  // order, so every XCD gets the same mix of sequences and splits (with
+  // the split fastest, the XCDs holding the low splits of every sequence
+  // would get most of the non-empty workgroups)
+  const dim3 grid(a.Hkv, batch, a.max_splits);
   if (q_is_bf16)
     paged_attention_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
   else
