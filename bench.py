@@ -15,15 +15,27 @@ residual, RMSNorm, SwiGLU, down + residual], final norm, LM head, argmax),
 replayed from a HIP graph; inputs are resident in HBM before timing.
 
 Reported (one JSON line): decode tokens/s for the step; the paged
-attention kernel's achieved HBM GB/s against the 8 TB/s peak (its
-algorithmic bytes per launch over its average launch time, HIP events on
-its stream); the whole step's algorithmic bytes over the step time; and
-the CPU oracle timed on a bounded sample of the same workload.
+attention call's achieved HBM GB/s against the 8 TB/s peak (its
+algorithmic bytes over its average duration: the call's two kernels,
+attention and split merge, replayed from a HIP graph over the 16 layers'
+tables and timed with HIP events on that stream); the whole step's
+algorithmic bytes over the step time; the batch-1 decoder layer (Llama
+shape, context 1024) against its weight-streaming roofline; and the CPU
+oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-  python bench.py --attention-only   (the attention launches alone, plus a
-                                      copy kernel of known size: the run
-                                      that rocprofv3 counters are taken on)
+  python bench.py --attention-only   (the attention calls alone, launched
+                                      one by one, then a 256 MiB device copy
+                                      of known size: the run that rocprofv3
+                                      counters are taken on)
+  python bench.py --traffic-summary FETCH.csv WRITE.csv
+                                     (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+                                      counter_collection.csv files of two
+                                      --attention-only runs -> the HBM
+                                      traffic per attention call, scaled by
+                                      what the copy reads, written to
+                                      profiles/paged_attention_bench_traffic.json
+                                      or --traffic-out PATH)
 """
 import argparse
 import hashlib
@@ -41,6 +53,7 @@ METRIC = "decode tokens/s + paged-attn HBM GB/s (% of peak), Llama-1B shape, bat
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_attention_bench_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "paged_kv_transformer_amd", "csrc", "attention.hip")
+COPY_BYTES = 256 << 20
 
 
 def log(*a):
@@ -120,48 +133,99 @@ class Setup:
                         self.next, self.ws)
 
 
-def time_attention(torch, pkv, synth, S, rounds, warmup):
-    """Per-launch times (ms) of the paged attention kernel over the step's
-    16 layers' block tables (distinct pages per layer), HIP events on its
-    stream around each launch."""
-    wl, shape = S.wl, S.shape
-    B = wl.batch
-    q = pkv.to_device(synth.bf16_normal(1002, "q", (B, shape.heads, shape.head_dim)))
-    lens = pkv.to_device(wl.lens)
-    out = torch.empty((B, shape.heads, shape.head_dim), dtype=torch.float32, device="cuda")
-    ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(shape.heads, shape.kv_heads, B, wl.max_pages))
-    bts = [S.bts[l].contiguous() for l in range(shape.layers)]
+class AttentionCalls:
+    """paged_gqa_decode over the step's 16 layers' block tables (distinct
+    pages per layer), BF16 q, FP32 output."""
+
+    def __init__(self, torch, pkv, synth, S):
+        wl, shape = S.wl, S.shape
+        B = wl.batch
+        self.pkv, self.S = pkv, S
+        self.q = pkv.to_device(synth.bf16_normal(1002, "q", (B, shape.heads, shape.head_dim)))
+        self.lens = pkv.to_device(wl.lens)
+        self.out = torch.empty((B, shape.heads, shape.head_dim), dtype=torch.float32, device="cuda")
+        self.ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(shape.heads, shape.kv_heads, B,
+                                                                    wl.max_pages))
+        self.bts = [S.bts[l].contiguous() for l in range(shape.layers)]
+        self.layers = shape.layers
+
+    def launch(self, l, stream):
+        self.pkv.paged_gqa_decode(self.S.pool, self.q, self.bts[l], self.lens, 0.125, self.out, self.ws,
+                                  stream)
+
+
+def time_attention(torch, pkv, synth, S, rounds, reps=10):
+    """Average duration (ms) of one paged_gqa_decode call: `rounds` passes
+    over the 16 layers' tables captured in a HIP graph, replayed `reps`
+    times between two HIP events on the replay stream."""
+    A = AttentionCalls(torch, pkv, synth, S)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        for l in range(A.layers):
+            A.launch(l, cap)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(rounds):
+                for l in range(A.layers):
+                    A.launch(l, cap)
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-
-    def launch(l):
-        pkv.paged_gqa_decode(S.pool, q, bts[l], lens, 0.125, out, ws, stream)
-
-    for _ in range(warmup):
-        for l in range(shape.layers):
-            launch(l)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(rounds * shape.layers)]
-    i = 0
-    for _ in range(rounds):
-        for l in range(shape.layers):
-            ev[i][0].record(stream)
-            launch(l)
-            ev[i][1].record(stream)
-            i += 1
-    torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in ev])
-    # back-to-back launches between two events (includes the launch gaps)
+    for _ in range(2):
+        graph.replay()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(rounds):
-        for l in range(shape.layers):
-            launch(l)
+    for _ in range(reps):
+        graph.replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    b2b = e0.elapsed_time(e1) / (rounds * shape.layers)
+    assert pkv.device_error(A.ws) == 0
+    return e0.elapsed_time(e1) / (reps * rounds * A.layers), reps * rounds * A.layers
+
+
+def time_layer_b1(torch, pkv, synth, S, reps=10):
+    """Batch-1 decoder layer (the step's layer weights, context 1024): the
+    16 layers' decoder_layer_decode calls captured in a HIP graph; returns
+    (ms per layer, algorithmic bytes per layer)."""
+    shape = S.shape
+    wl = synth.c3_step()
+    pool_t = pkv.to_device(wl.pool)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    bts = [pkv.to_device(wl.block_tables[l]) for l in range(shape.layers)]
+    pos = pkv.to_device(wl.positions)
+    hidden = torch.randn((1, shape.hidden), dtype=torch.float32, device="cuda")
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(S.cfg, 1, wl.max_pages))
+    m = S.model
+
+    def run(stream):
+        for l in range(shape.layers):
+            pkv.decoder_layer_decode(S.cfg, m.layers[l], m.rope_cos, m.rope_sin, pool, bts[l], pos, hidden,
+                                     ws, stream)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        run(cap)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            run(cap)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
     assert pkv.device_error(ws) == 0
-    return per, b2b
+    n = int(wl.positions[0]) + 1
+    layer_bytes = (2 * shape.layer_param_count() + attention_bytes([n - 1], shape.heads, shape.kv_heads, 4)
+                   + shape.kv_heads * shape.head_dim * 2 * 2 + 2 * shape.hidden * 4)
+    return e0.elapsed_time(e1) / (reps * shape.layers), layer_bytes
 
 
 def cpu_baseline(S, seqs):
@@ -176,19 +240,70 @@ def cpu_baseline(S, seqs):
 
 
 def attention_only(torch, pkv, synth, rounds):
-    """Launch sequence for the hardware-counter runs: the attention kernel
-    over the 16 layers' tables, then a copy of known size."""
+    """Launch sequence for the hardware-counter runs: the attention calls
+    over the 16 layers' tables, one by one, then a device copy of known
+    size (the counters' calibration)."""
     S = Setup(torch, pkv, synth)
-    per, _ = time_attention(torch, pkv, synth, S, rounds, 1)
-    n = 256 << 20
+    A = AttentionCalls(torch, pkv, synth, S)
+    stream = torch.cuda.current_stream()
+    for _ in range(rounds):
+        for l in range(A.layers):
+            A.launch(l, stream)
+    torch.cuda.synchronize()
+    assert pkv.device_error(A.ws) == 0
+    n = COPY_BYTES
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
     abytes = attention_bytes(S.wl.lens, S.shape.heads, S.shape.kv_heads, 2)
-    print("attention-only: %d launches, mean %.2f us, %d algorithmic bytes per launch; "
-          "copy calibration: 3 x %d bytes read + written" % (len(per), per.mean() * 1e3, abytes, n), flush=True)
+    print("attention-only: %d calls, %d algorithmic bytes per call; copy calibration: 3 x %d bytes "
+          "read + written" % (rounds * A.layers, abytes, n), flush=True)
+
+
+def _counter_values(path):
+    """Counter values per (kernel name, counter) from a rocprofv3
+    counter_collection.csv (one row per dispatch and counter)."""
+    import csv
+    vals = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            key = (row.get("Kernel_Name", ""), row.get("Counter_Name", ""))
+            vals.setdefault(key, []).append(float(row["Counter_Value"]))
+    return vals
+
+
+def traffic_summary(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the attention
+    kernels, scaled by what the same counters read for the 256 MiB copy,
+    summed per paged_gqa_decode call -> TRAFFIC_FILE."""
+    out = {"attention_source_sha": source_sha(ATTN_SOURCE), "copy_bytes": COPY_BYTES}
+    for cname, path, key in (("FETCH_SIZE", fetch_csv, "fetch"), ("WRITE_SIZE", write_csv, "write")):
+        vals = _counter_values(path)
+        # the calibration copy is the largest device copy of the run
+        copy = [max(v) for (k, c), v in vals.items() if c == cname and "copyBuffer" in k]
+        assert copy, "no device copy in %s" % path
+        copy_kib = max(copy)
+        scale = COPY_BYTES / (copy_kib * 1024.0)
+        per_call = 0.0
+        kernels = {}
+        for (k, c), v in vals.items():
+            if c != cname:
+                continue
+            short = k.replace("pkv::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            if short.startswith("paged_attention_kernel") or short.startswith("attention_merge_kernel"):
+                m = sum(v) / len(v)
+                kernels[short] = {"mean_kib_per_dispatch": round(m, 1), "dispatches": len(v),
+                                  "bytes_scaled": round(m * 1024.0 * scale)}
+                per_call += m * 1024.0 * scale
+        out[key + "_copy_kib"] = round(copy_kib, 1)
+        out[key + "_scale"] = round(scale, 4)
+        out[key + "_kernels"] = kernels
+        out[key + "_bytes_per_launch"] = int(round(per_call))
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -196,12 +311,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--attn-rounds", type=int, default=20)
+    ap.add_argument("--attn-rounds", type=int, default=4)
     ap.add_argument("--cpu-seqs", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch the step directly, no HIP graph")
     ap.add_argument("--attention-only", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
+    ap.add_argument("--no-layer-b1", action="store_true")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, out_path=args.traffic_out)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only (the path runs on a single MI355X); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -258,15 +379,24 @@ def main():
     assert pkv.device_error(S.ws) == 0
     assert torch.equal(S.next, ref_next), "replayed steps changed the next tokens"
 
-    # paged attention kernel: achieved HBM rate against the peak
-    per, b2b = time_attention(torch, pkv, synth, S, args.attn_rounds, 3)
+    # paged attention call: achieved HBM rate against the peak
+    attn_ms, calls = time_attention(torch, pkv, synth, S, args.attn_rounds)
     abytes = attention_bytes(wl.lens, shape.heads, shape.kv_heads, 2)
-    attn_ms = float(per.mean())
     achieved = abytes / (attn_ms * 1e-3) / 1e9
-    log("attention: %.2f us per launch (events), %.2f us back-to-back, %.1f MB -> %.0f GB/s" % (
-        attn_ms * 1e3, b2b * 1e3, abytes / 1e6, achieved))
+    log("attention: %.2f us per call (graph, %d calls), %.1f MB -> %.0f GB/s" % (
+        attn_ms * 1e3, calls, abytes / 1e6, achieved))
     sbytes = step_bytes(shape, wl.lens)
     step_gbs = sbytes / (ms * 1e-3) / 1e9
+    layer_b1 = None
+    if not args.no_layer_b1:
+        l_ms, l_bytes = time_layer_b1(torch, pkv, synth, S)
+        l_gbs = l_bytes / (l_ms * 1e-3) / 1e9
+        log("batch-1 layer: %.2f us, %.1f MB -> %.0f GB/s" % (l_ms * 1e3, l_bytes / 1e6, l_gbs))
+        layer_b1 = {"workload": "decoder_layer_decode, llama-3.2-1b-shape layer, batch 1, context 1024, "
+                                "16 layers' weights in turn (HIP graph)",
+                    "bound": "hbm", "algorithmic_bytes": int(l_bytes), "us_per_layer": round(l_ms * 1e3, 3),
+                    "achieved": round(l_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(l_gbs / HBM_PEAK_GBS, 4)}
 
     result = {
         "metric": METRIC,
@@ -290,7 +420,8 @@ def main():
             "pool_pages": int(wl.num_pages), "page_tokens": 16, "hip_graph": not args.eager,
         },
         "roofline": {
-            "kernel": "paged_attention_kernel (paged_gqa_decode on each layer's tables)",
+            "kernel": "paged_gqa_decode (paged_attention_kernel + attention_merge_kernel) on each "
+                      "layer's tables",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -299,13 +430,13 @@ def main():
             "traffic": load_traffic(abytes),
             "algorithmic_bytes_per_launch": abytes,
             "avg_launch_us": round(attn_ms * 1e3, 3),
-            "back_to_back_us": round(b2b * 1e3, 3),
-            "launches": int(len(per)),
+            "launches": int(calls),
         },
         "step_roofline": {
             "bound": "hbm", "algorithmic_bytes": int(sbytes), "achieved": round(step_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
         },
+        "layer_b1_roofline": layer_b1,
         "cpu_baseline": None,
     }
 
