@@ -195,7 +195,8 @@ int paged_gqa_decode(const pkv_pool *pool, const uint16_t *q,
  *   [batch][max_pages].  rope_cos/rope_sin [max_position_embeddings][D/2].
  * Contractions accumulate in FP32 with FP32 activations (split into two
  * BF16 halves for the matrix cores).  Errors: as paged_gqa_decode plus
- * -ENOTSUP (H or I not a multiple of 64); device errors PKV_DEVERR_PAGE,
+ * -ENOTSUP (H or I not a multiple of 64 or above 65536, a weight matrix
+ * above 2 GiB); device errors PKV_DEVERR_PAGE,
  * PKV_DEVERR_LENGTH, PKV_DEVERR_ROPE.
  */
 int decoder_layer_decode(const pkv_config *cfg, const pkv_layer_weights *w,

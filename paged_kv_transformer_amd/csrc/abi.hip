@@ -39,6 +39,13 @@ int check_cfg(const pkv_config* c) {
   if (c->hidden_size < 1 || c->intermediate_size < 1 || c->max_position_embeddings < 1)
     return -EINVAL;
   if (c->hidden_size % 64 != 0 || c->intermediate_size % 64 != 0) return -ENOTSUP;
+  // the kernels address every weight matrix and activation buffer through a
+  // 32-bit byte range
+  if (c->hidden_size > kMaxDim || c->intermediate_size > kMaxDim) return -ENOTSUP;
+  const int64_t H = c->hidden_size, I = c->intermediate_size;
+  const int64_t qkv_rows = (int64_t)(c->num_attention_heads + 2 * c->num_key_value_heads) * kHeadDim;
+  if (c->vocab_size > 0 && (int64_t)c->vocab_size * H * 2 > kMaxMatrixBytes) return -ENOTSUP;
+  if (qkv_rows * H * 2 > kMaxMatrixBytes || 2 * I * H * 2 > kMaxMatrixBytes) return -ENOTSUP;
   if (!(c->rms_norm_eps >= 0.f) || !isfinite(c->rms_norm_eps)) return -EINVAL;
   if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return -EINVAL;
   return 0;
@@ -90,7 +97,9 @@ int gemm_batched(int epi, int N, int batch, const GemmArgs& base, F setup, hipSt
     GemmArgs a = base;
     a.B = bc;
     setup(a, b0);
-    if (int rc = io(launch_gemm(epi, a, plan_gemm(epi, N, bc), st))) return rc;
+    const GemmPlan p = plan_gemm(epi, N, bc, a.K);
+    a.ksplit = p.ks;
+    if (int rc = io(launch_gemm(epi, a, p, st))) return rc;
   }
   return 0;
 }
@@ -182,6 +191,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
       c.out = h1 + (size_t)b0 * H;
       c.out_packed = packed_at(h1_p, b0, H);
       c.resid = hidden + (size_t)b0 * H;
+      c.part = at<float>(ws, L.gemm_part);
     }, st);
     if (rc) return rc;
   }
@@ -214,6 +224,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
       c.out = hidden + (size_t)b0 * H;
       c.out_packed = packed_at(x_p, b0, H);
       c.resid = h1 + (size_t)b0 * H;
+      c.part = at<float>(ws, L.gemm_part);
     }, st);
     if (rc) return rc;
   }

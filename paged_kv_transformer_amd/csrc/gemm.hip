@@ -51,6 +51,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// A byte offset past every activation descriptor: they cover at most 32
+// batch columns of at most 65536 FP32 values, 8 MiB.
+constexpr int kOutOfRange = 0x40000000;
+
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
@@ -83,11 +87,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
-  const int t = blockIdx.x;
+  // workgroup = (row tile t, K split ks); the split's 32-wide K steps are
+  // shared out over the waves
+  const int nks = EPI == EPI_RESID ? a.ksplit : 1;
+  const int t = blockIdx.x / nks;
+  const int ksi = blockIdx.x - t * nks;
   const int steps = a.K >> 5;
-  const int spw = (steps + NW - 1) / NW;
-  const int s0 = w * spw;
-  const int s1 = min(s0 + spw, steps);
+  const int sps = (steps + nks - 1) / nks;
+  const int ks0 = ksi * sps;
+  const int ks1 = min(ks0 + sps, steps);
+  const int spw = (ks1 - ks0 + NW - 1) / NW;
+  const int s0 = ks0 + w * spw;
+  const int s1 = min(s0 + spw, ks1);
 
   // Buffer loads: one descriptor per operand in scalar registers, a fixed
   // per-lane byte offset in a vector register, and the step's offset as a
@@ -108,15 +119,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   int woff[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) woff[g] = (min(t * RG + g, a.w_groups - 1) * steps * 64 + l) * 16;
+  // Lanes of batch columns past B get an offset beyond the descriptor's
+  // range: buffer loads there return zeros without a memory request, so a
+  // small batch reads only its own activations.
   int xoff[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
-    if (XPLAIN) {
-      const int b = 16 * c + (l & 15);
-      xoff[c] = ((b < a.B ? b : 0) * a.K + koff) * 4;
-    } else {
+    const int b = 16 * c + (l & 15);
+    if (b >= a.B)
+      xoff[c] = kOutOfRange;
+    else if (XPLAIN)
+      xoff[c] = (b * a.K + koff) * 4;
+    else
       xoff[c] = (c * steps * 64 + l) * 32;
-    }
   }
   const int xwoff = koff * 2;
 
@@ -236,9 +251,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       const int n = t * R + row;
       if (n < a.N) {
         const size_t o = (size_t)c * a.N + n;
-        const float v = a.resid[o] + tile[c * TS + row];
-        a.out[o] = v;
-        if (a.out_packed) a.out_packed[packed_act_index(c, n, a.N)] = v;
+        if (nks > 1) {
+          a.part[(size_t)ksi * a.B * a.N + o] = tile[c * TS + row];
+        } else {
+          const float v = a.resid[o] + tile[c * TS + row];
+          a.out[o] = v;
+          if (a.out_packed) a.out_packed[packed_act_index(c, n, a.N)] = v;
+        }
       }
     }
   } else if (EPI == EPI_QKV) {
@@ -324,6 +343,39 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   }
 }
 
+// out = resid + the K splits' partial sums, added in split order (so the
+// result does not depend on which workgroup finished first), plain and
+// packed.  One thread per 4 consecutive outputs of one batch column; the
+// partials of 16 splits are loaded together (split index clamped, masked).
+__global__ __launch_bounds__(64) void resid_reduce_kernel(const float* part, int nks, int B, int N,
+                                                           const float* resid, float* out,
+                                                           float* out_packed) {
+  constexpr int CH = 16;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n4 = N >> 2;
+  if (i >= B * n4) return;
+  const int c = i / n4, n = (i - c * n4) * 4;
+  const size_t o = (size_t)c * N + n;
+  const size_t stride = (size_t)B * N;
+  float4 v = *(const float4*)(resid + o);
+  for (int s0 = 0; s0 < nks; s0 += CH) {
+    float4 p[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) p[j] = *(const float4*)(part + (size_t)min(s0 + j, nks - 1) * stride + o);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (s0 + j < nks) {
+        v.x += p[j].x;
+        v.y += p[j].y;
+        v.z += p[j].z;
+        v.w += p[j].w;
+      }
+    }
+  }
+  *(float4*)(out + o) = v;
+  if (out_packed) *(float4*)(out_packed + packed_act_index(c, n, N)) = v;
+}
+
 // Token id per sequence: the largest packed key over the LM head's tiles.
 __global__ void argmax_finalize_kernel(const unsigned long long* part, int tiles, int B,
                                        int32_t* next_tok) {
@@ -362,13 +414,25 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
         e = one ? go<1, 1, 8, EPI_QKV>(a, p.tiles, st) : go<2, 1, 8, EPI_QKV>(a, p.tiles, st);
       break;
     case EPI_RESID:
-      e = one ? go<1, 1, 16, EPI_RESID>(a, p.tiles, st) : go<2, 1, 16, EPI_RESID>(a, p.tiles, st);
+      if (p.ks > 1) {
+        e = one ? go<1, 2, 4, EPI_RESID>(a, p.tiles * p.ks, st)
+                : go<2, 2, 4, EPI_RESID>(a, p.tiles * p.ks, st);
+        if (e != hipSuccess) return e;
+        // small blocks: the partial sums are a few MB, spread over enough
+        // workgroups that no CU streams more than a few KB of them
+        const int n = a.B * (a.N / 4);
+        resid_reduce_kernel<<<(n + 63) / 64, 64, 0, st>>>(a.part, p.ks, a.B, a.N, a.resid, a.out,
+                                                          a.out_packed);
+        e = hipGetLastError();
+      } else {
+        e = one ? go<1, 1, 8, EPI_RESID>(a, p.tiles, st) : go<2, 1, 8, EPI_RESID>(a, p.tiles, st);
+      }
       break;
     case EPI_SWIGLU:
       e = one ? go<1, 2, 4, EPI_SWIGLU>(a, p.tiles, st) : go<2, 1, 4, EPI_SWIGLU>(a, p.tiles, st);
       break;
     case EPI_LOGITS:
-      e = one ? go<1, 4, 4, EPI_LOGITS>(a, p.tiles, st) : go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st);
+      e = one ? go<1, 2, 4, EPI_LOGITS>(a, p.tiles, st) : go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st);
       if (e != hipSuccess) return e;
       argmax_finalize_kernel<<<a.B, 256, 0, st>>>(a.amax_part, p.tiles, a.B, a.next_tok);
       e = hipGetLastError();

@@ -108,10 +108,14 @@ struct GemmArgs {
   float eps;
   uint32_t* err;
   // EPI_RESID: out[b][n] = resid[b][n] + y (plain), and packed into
-  // out_packed (if not null) for the next projection
+  // out_packed (if not null) for the next projection.  With ksplit > 1 the
+  // workgroups of K split s write their sums to part[s][b][n] and a reduce
+  // kernel adds resid and the splits in split order.
   float* out;
   const float* resid;
   float* out_packed;
+  float* part;
+  int32_t ksplit;
   // EPI_QKV
   float* q_out;            // [B][Hq][D]
   uint16_t* pool;
@@ -146,36 +150,75 @@ inline int attn_max_splits(int max_pages) {
 }
 
 // A GEMM launch: `rg` groups of 16 output rows per workgroup, `nw` waves
-// splitting K inside the workgroup, `ct` groups of 16 batch columns.
+// splitting K inside the workgroup, `ct` groups of 16 batch columns, `ks`
+// workgroups splitting K per row tile (tiles * ks workgroups in all).
 struct GemmPlan {
-  int tiles, ct, rg, nw;
+  int tiles, ct, rg, nw, ks;
 };
 
 constexpr int kGemmMaxCols = 32;  // batch columns per launch (ct <= 2)
+constexpr int kMaxDim = 65536;    // largest hidden / intermediate size
+constexpr int64_t kMaxMatrixBytes = (int64_t)1 << 31;  // largest weight matrix
 
 inline int gemm_ct(int B) { return B <= 16 ? 1 : 2; }
 
-inline int gemm_rows_per_tile(int epi, int ct) {
-  if (epi == EPI_QKV || epi == EPI_RESID) return 16;
-  return ct == 1 ? (epi == EPI_LOGITS ? 64 : 32) : 16;
+// A residual projection whose row tiles alone give few workgroups and whose
+// K is long (the down projection) splits K over workgroups: about 512
+// workgroups keep enough weight bytes in flight, where one workgroup per
+// 16-row tile would leave half the chip idle.
+constexpr int kSplitMinK = 4096;
+constexpr int kSplitTargetWgs = 512;
+constexpr int kSplitMinSteps = 8;  // 32-wide K steps per split, at least
+
+inline bool gemm_split(int epi, int N, int K) {
+  return epi == EPI_RESID && K >= kSplitMinK && (N + 15) / 16 < kSplitTargetWgs / 2;
 }
 
-inline GemmPlan plan_gemm(int epi, int N, int B) {
+inline int gemm_rows_per_tile(int epi, int ct, bool split) {
+  if (split) return 32;
+  if (epi == EPI_QKV || epi == EPI_RESID) return 16;
+  return ct == 1 ? 32 : 16;
+}
+
+inline GemmPlan plan_gemm(int epi, int N, int B, int K) {
   GemmPlan p;
   p.ct = gemm_ct(B);
-  const int R = gemm_rows_per_tile(epi, p.ct);
+  const bool split = gemm_split(epi, N, K);
+  const int R = gemm_rows_per_tile(epi, p.ct, split);
   p.rg = R / 16;
-  p.nw = epi == EPI_RESID ? 16 : (epi == EPI_QKV ? 8 : 4);
+  p.nw = split ? 4 : (epi == EPI_RESID || epi == EPI_QKV ? 8 : 4);
   // the gate/up tile holds R/2 gate rows and the R/2 matching up rows
   const int rows = epi == EPI_SWIGLU ? N / 2 : N;
   const int per = epi == EPI_SWIGLU ? R / 2 : R;
   p.tiles = (rows + per - 1) / per;
+  p.ks = 1;
+  if (split) {
+    const int steps = K / 32;
+    int ks = kSplitTargetWgs / p.tiles;
+    if (ks > steps / kSplitMinSteps) ks = steps / kSplitMinSteps;
+    p.ks = ks < 1 ? 1 : ks;
+  }
   return p;
+}
+
+// Floats of split partial sums a residual projection needs for any launch
+// of at most Bc columns (the split count depends on the column tiling, so
+// both tilings' largest launches are checked).
+inline size_t gemm_part_floats(int N, int Bc, int K) {
+  size_t most = 0;
+  const int cand[2] = {Bc < 16 ? Bc : 16, Bc};
+  for (int b : cand) {
+    if (b < 1) continue;
+    const GemmPlan p = plan_gemm(EPI_RESID, N, b, K);
+    const size_t f = p.ks > 1 ? (size_t)p.ks * b * N : 0;
+    most = f > most ? f : most;
+  }
+  return most;
 }
 
 struct WsLayout {
   size_t err, q, o_p, h1, h1_p, act_p, x, x_p;
-  size_t attn_part, amax_part;
+  size_t attn_part, amax_part, gemm_part;
   size_t total;
 };
 
@@ -197,8 +240,11 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_p
     w.x = take(sizeof(float) * (size_t)B * H);
     w.x_p = take(sizeof(float) * (size_t)packed_act_elems(B, H));
     const int Bc = B < kGemmMaxCols ? B : kGemmMaxCols;
-    const GemmPlan lm = plan_gemm(EPI_LOGITS, V, Bc);
+    const GemmPlan lm = plan_gemm(EPI_LOGITS, V, Bc, H);
     w.amax_part = take(sizeof(unsigned long long) * (size_t)lm.tiles * (Bc > 0 ? Bc : 1));
+    const size_t po = gemm_part_floats(H, Bc, Hq * kHeadDim);
+    const size_t pd = gemm_part_floats(H, Bc, I);
+    w.gemm_part = take(sizeof(float) * (po > pd ? po : pd));
   }
   w.total = off;
   return w;

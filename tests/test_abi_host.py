@@ -70,6 +70,8 @@ def test_paged_gqa_decode_validation():
     assert L.paged_gqa_decode(*args(hq=8 * 17)) == ENOTSUP     # group of 17
     assert L.paged_gqa_decode(*args(b=-1)) == EINVAL
     assert L.paged_gqa_decode(*args(mp=0)) == EINVAL
+    assert L.paged_gqa_decode(*args(b=65536)) == ENOTSUP       # grid y limit
+    assert L.paged_gqa_decode(*args(mp=8 * 65535 + 1)) == ENOTSUP  # more than 65535 splits
     assert L.paged_gqa_decode(*args(wsb=ws_need - 1)) == ENOSPC
     assert L.paged_gqa_decode(*args(ws=FAKE + 4)) == EINVAL
     assert L.paged_gqa_decode(*args(scale=float("nan"))) == EINVAL
@@ -100,6 +102,10 @@ def test_layer_and_step_validation():
     assert layer(c=_cfg(head_dim=128)) == ENOTSUP
     assert layer(c=_cfg(hidden_size=2000)) == ENOTSUP
     assert layer(c=_cfg(intermediate_size=100)) == ENOTSUP
+    assert layer(c=_cfg(intermediate_size=65536 + 64)) == ENOTSUP   # past the 32-bit byte ranges
+    assert layer(c=_cfg(hidden_size=65536 + 64)) == ENOTSUP
+    assert layer(c=_cfg(hidden_size=16384, intermediate_size=65536)) == ENOTSUP  # gate/up over 2 GiB
+    assert layer(c=_cfg(vocab_size=600000)) == ENOTSUP         # tied embedding over 2 GiB
     assert layer(c=_cfg(num_key_value_heads=3)) == EINVAL
     assert layer(c=_cfg(rms_norm_eps=float("nan"))) == EINVAL
     assert layer(pool=_pool(hkv=2)) == EINVAL                  # pool heads != config heads

@@ -63,6 +63,21 @@ def test_layer_tiny_shapes(batch, hkv, heads):
     _check_layer(shape, lw, hidden, wl)
 
 
+@pytest.mark.parametrize("batch,inter", [(1, 4096), (5, 4352), (16, 8192), (33, 4352)])
+def test_layer_split_k_down_projection(batch, inter):
+    """Down projections with K >= 4096 split K over workgroups and add the
+    splits in a second kernel; 4352 (136 K steps) gives 17 splits, more than
+    one round of the reduce kernel's 16-split loads; batch 33 also takes the
+    two-column-tile path."""
+    shape = synth.tiny_shape(hidden=192, heads=4, kv_heads=2, inter=inter, name="tiny-split")
+    seed = 300 + batch
+    positions = synth.rng(seed, "lens").integers(0, 100, size=batch).astype(np.int32)
+    wl = synth.decode_workload("tiny-split", shape, seed, positions, layers=1)
+    lw = synth.layer_weights(shape, seed, 0, sigma=0.05, norm_sigma=0.3)
+    hidden = synth.rng(seed, "hidden").standard_normal((batch, shape.hidden)).astype(np.float32)
+    _check_layer(shape, lw, hidden, wl)
+
+
 def _check_step(shape, weights, wl, tokens, seqs=None, want_logits=True):
     geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
     logits, nxt, pool_after, err = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions,
