@@ -80,14 +80,18 @@ __device__ __forceinline__ u32x2 keep_first(u32x2 v, int nv) {
 }
 
 template <typename QT>
-__global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const AttnArgs a) {
   constexpr int PW = kAttnPW;
   constexpr int CP = kAttnPagesPerSplit;
-  __shared__ float sm_m[4][16];
-  __shared__ float sm_l[4][16];
-  __shared__ float sm_o[4][16][kHeadDim + 1];
+  constexpr int NW = kAttnWaves;
+  constexpr int NT = NW * 64;
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ float sm_o[NW][16][kHeadDim + 1];
 
-  const int kvh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  // the highest splits are launched first: only long sequences have them,
+  // and starting the longest work first keeps it out of the kernel's tail
+  const int kvh = blockIdx.x, b = blockIdx.y, split = a.max_splits - 1 - (int)blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, grp = l >> 4;
   const int G = a.G;
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
   const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
   int page[PW];
 #pragma unroll
-  for (int i = 0; i < PW; ++i) page[i] = btrow[min(split * CP + 4 * i + wu, a.bt_stride - 1)];
+  for (int i = 0; i < PW; ++i) page[i] = btrow[min(split * CP + NW * i + wu, a.bt_stride - 1)];
   const int n = a.lens[b] + a.len_add;
 #pragma unroll
   for (int i = 0; i < PW; ++i) asm volatile("" ::"s"(page[i]));
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
   const int ns = npages > 0 ? (npages + CP - 1) / CP : 1;
   if (npages == 0 || split >= ns) {
     if (single) {
-      for (int i = tid; i < G * kHeadDim; i += 256) store_out(a, b, kvh, i, 0.f);
+      for (int i = tid; i < G * kHeadDim; i += NT) store_out(a, b, kvh, i, 0.f);
     } else if (tid < G) {
       rec[tid] = -INFINITY;
     }
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const int lp = split * CP + 4 * i + wu;  // uniform across the wave
+    const int lp = split * CP + NW * i + wu;  // uniform across the wave
     const bool live = lp < npages;
     const bool ok = (unsigned)page[i] < (unsigned)a.num_pages;
     bad |= live && !ok;
@@ -245,12 +249,14 @@ __global__ __launch_bounds__(256) void paged_attention_kernel(const AttnArgs a) 
     }
   __syncthreads();
 
-  for (int idx = tid; idx < G * kHeadDim; idx += 256) {
+  for (int idx = tid; idx < G * kHeadDim; idx += NT) {
     const int g = idx >> 6, d = idx & 63;
-    const float M = fmaxf(fmaxf(sm_m[0][g], sm_m[1][g]), fmaxf(sm_m[2][g], sm_m[3][g]));
+    float M = sm_m[0][g];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][g]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const float mw = sm_m[ww][g];
       const float e = mw == -INFINITY ? 0.f : expf(mw - M);
       L += e * sm_l[ww][g];
@@ -326,9 +332,9 @@ hipError_t launch_attention(const AttnArgs& a, int batch, bool q_is_bf16, hipStr
   // would get most of the non-empty workgroups)
   const dim3 grid(a.Hkv, batch, a.max_splits);
   if (q_is_bf16)
-    paged_attention_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
+    paged_attention_kernel<uint16_t><<<grid, kAttnWaves * 64, 0, st>>>(a);
   else
-    paged_attention_kernel<float><<<grid, 256, 0, st>>>(a);
+    paged_attention_kernel<float><<<grid, kAttnWaves * 64, 0, st>>>(a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits <= 1) return e;
   attention_merge_kernel<<<dim3(a.Hkv, batch), 256, 0, st>>>(a);

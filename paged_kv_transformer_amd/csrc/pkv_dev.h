@@ -139,9 +139,14 @@ struct GemmArgs {
 
 // ------------------------------------------------------------ plans ---
 
-// Attention: 4 waves per workgroup, kAttnPW pages per wave per split.
+// Attention: kAttnWaves waves per workgroup, kAttnPW pages per wave per
+// split.
+#ifndef PKV_ATTN_WAVES
+#define PKV_ATTN_WAVES 4
+#endif
+constexpr int kAttnWaves = PKV_ATTN_WAVES;
 constexpr int kAttnPW = 2;
-constexpr int kAttnPagesPerSplit = 4 * kAttnPW;
+constexpr int kAttnPagesPerSplit = kAttnWaves * kAttnPW;
 // One split's partial record: m[16], l[16], o[16][64] floats.
 constexpr int kAttnRec = 16 + 16 + 16 * kHeadDim;
 
