@@ -88,8 +88,9 @@ def check_pool_after(got, want, base):
     return float(np.abs(g - w).max(initial=0.0)), rms
 
 
-def step_gpu(shape, weights, pool_np, bts, positions, tokens, want_logits=True, max_pos=None):
-    """decode_step; returns (logits or None, next_tokens, pool_after, err)."""
+def step_gpu(shape, weights, pool_np, bts, positions, tokens, want_logits=True, max_pos=None,
+             want_pool=True):
+    """decode_step; returns (logits or None, next_tokens, pool_after or None, err)."""
     B = len(positions)
     mp = max_pos or int(max(positions)) + 1
     cfg = pkv.make_config(shape, max_pos=mp)
@@ -103,7 +104,8 @@ def step_gpu(shape, weights, pool_np, bts, positions, tokens, want_logits=True, 
     pkv.decode_step(cfg, model, pool, dev(bts), dev(np.asarray(positions, np.int32)),
                     dev(np.asarray(tokens, np.int32)), logits, nxt, ws)
     err = pkv.device_error(ws)
-    return (None if logits is None else logits.cpu().numpy()), nxt.cpu().numpy(), host_u16(pool_t), err
+    pool_after = host_u16(pool_t) if want_pool else None
+    return (None if logits is None else logits.cpu().numpy()), nxt.cpu().numpy(), pool_after, err
 
 
 def check_argmax_rule(ref_logits, got_tokens, gap=1e-3):

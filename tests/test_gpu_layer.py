@@ -81,7 +81,7 @@ def test_layer_split_k_down_projection(batch, inter):
 def _check_step(shape, weights, wl, tokens, seqs=None, want_logits=True):
     geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
     logits, nxt, pool_after, err = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions,
-                                            tokens, want_logits)
+                                            tokens, want_logits, want_pool=False)
     assert err == 0
     ref_logits, ref_tok, _, _ = oracle.decode_step_paged(shape, weights, wl.pool, geo, wl.block_tables,
                                                          wl.positions, tokens, seqs)
@@ -123,3 +123,12 @@ def test_step_c4_llama_shape_batch64_sampled():
     order = np.argsort(wl.positions)
     seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
     _check_step(wl.shape, weights, wl, wl.extra["tokens"], seqs=seqs)
+
+
+def test_step_c5_qwen_shape_batch128_long_context_sampled():
+    """24-layer Qwen2.5-0.5B-shaped step at batch 128, every sequence at 4096
+    cached tokens (257 pages of each of 24 layers, a 6 GiB pool of randomly
+    permuted 8 KiB pages); the oracle checks the first and last sequences."""
+    wl = synth.c5_step()
+    weights = synth.model_weights(wl.shape, 1005)
+    _check_step(wl.shape, weights, wl, wl.extra["tokens"], seqs=[0, len(wl.positions) - 1])
