@@ -380,11 +380,18 @@ __global__ __launch_bounds__(64) void resid_reduce_kernel(const float* part, int
 __global__ void argmax_finalize_kernel(const unsigned long long* part, int tiles, int B,
                                        int32_t* next_tok) {
   __shared__ unsigned long long sm[256];
+  constexpr int U = 16;  // keys loaded together per thread
   const int c = blockIdx.x;
   unsigned long long best = 0ull;
-  for (int t = threadIdx.x; t < tiles; t += blockDim.x) {
-    const unsigned long long k = part[(size_t)t * B + c];
-    best = k > best ? k : best;
+  for (int t0 = threadIdx.x; t0 < tiles; t0 += blockDim.x * U) {
+    unsigned long long k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * blockDim.x;
+      k[u] = part[(size_t)min(t, tiles - 1) * B + c];  // clamped: loads issue unconditionally
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) best = k[u] > best ? k[u] : best;  // a repeated key changes nothing
   }
   sm[threadIdx.x] = best;
   __syncthreads();
