@@ -17,9 +17,11 @@
 // split into two BF16 halves (hi + lo) so that the products keep ~16
 // significant bits on both sides; the accumulation is FP32.
 //
-// Softmax: each wave takes the maximum over its pages, exponentiates, and
-// keeps (m, l, O); waves and then splits are merged with the log-sum-exp
-// rule m = max m_i, l = sum l_i e^(m_i - m), O = sum O_i e^(m_i - m), in a
+// Softmax: scores are kept in base-2 units (q is prescaled by the
+// attention scale times log2 e), so e^x becomes the hardware 2^x.  Each wave
+// takes the maximum over its pages, exponentiates, and keeps (m, l, O);
+// waves and then splits are merged with the log-sum-exp rule m = max m_i,
+// l = sum l_i 2^(m_i - m), O = sum O_i 2^(m_i - m), in a
 // fixed order, so the result depends only on the logical page sequence
 // (never on where pages sit in the pool).  When the block table allows a
 // single split, the workgroup finishes its sequence; otherwise every split
@@ -40,6 +42,8 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Eight consecutive q values (BF16 bits or FP32) as FP32, vector loads.
 __device__ __forceinline__ void load_q8(const uint16_t* p, float (&v)[8]) {
@@ -170,18 +174,24 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
   }
   __builtin_amdgcn_sched_barrier(0);
   if (bad && l == 0) set_error(a.err, ERR_PAGE);
+  // scores are kept in base-2 units (q prescaled by scale * log2 e), so
+  // every exponential is one hardware 2^x
+  const float qscale = a.scale * kLog2e;
   bf16x8 qh[2], ql[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = col < G ? qv[h][e] * a.scale : 0.f;
+      const float v = col < G ? qv[h][e] * qscale : 0.f;
       const __bf16 hi = (__bf16)v;
       qh[h][e] = hi;
       ql[h][e] = (__bf16)(v - (float)hi);
     }
 
   // ---- scores: lane holds S[t = 4*grp + r][g = col] of each page
+  bool full[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) full[i] = lpv[i] >= 0 && (lpv[i] + 1) * kPageTokens <= n;
   f32x4 s[PW];
   float mx = -INFINITY;
 #pragma unroll
@@ -191,26 +201,32 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
     acc = mfma_k32(kr[i][0], ql[0], acc);
     acc = mfma_k32(kr[i][1], qh[1], acc);
     acc = mfma_k32(kr[i][1], ql[1], acc);
+    // a full page (every page of a sequence but its last) needs no mask;
+    // the test is uniform across the wave
+    if (!full[i]) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = lpv[i] * kPageTokens + 4 * grp + r;
-      const bool ok = lpv[i] >= 0 && t < n;
-      acc[r] = ok ? acc[r] : -INFINITY;
-      mx = fmaxf(mx, acc[r]);
+      for (int r = 0; r < 4; ++r) {
+        const int t = lpv[i] * kPageTokens + 4 * grp + r;
+        acc[r] = lpv[i] >= 0 && t < n ? acc[r] : -INFINITY;
+      }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[r]);
     s[i] = acc;
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-  // ---- P = exp(S - m) split hi/lo; row sums
+  // ---- P = 2^(S - m) split hi/lo; row sums.  Masked scores are -inf and
+  // give 0; a wave with no token at all (m = -inf) subtracts 0 instead.
+  const float msub = mx == -INFINITY ? 0.f : mx;
   float lsum = 0.f;
   s16x4 ph[PW], pl[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = s[i][r] == -INFINITY ? 0.f : expf(s[i][r] - mx);
+      const float p = __builtin_amdgcn_exp2f(s[i][r] - msub);
       lsum += p;
       const __bf16 hi = (__bf16)p;
       ph[i][r] = __builtin_bit_cast(short, hi);
@@ -226,7 +242,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     // unused slots of a partial page may hold anything (NaN included): zero them
-    const int nv = lpv[i] < 0 ? 0 : n - (lpv[i] * kPageTokens + 4 * grp);
+    const int nv = full[i] ? 4 : (lpv[i] < 0 ? 0 : n - (lpv[i] * kPageTokens + 4 * grp));
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const s16x4 vb = __builtin_bit_cast(s16x4, keep_first(vr[i][c], nv));
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       const float mw = sm_m[ww][g];
-      const float e = mw == -INFINITY ? 0.f : expf(mw - M);
+      const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L += e * sm_l[ww][g];
       O += e * sm_o[ww][g][d];
     }
@@ -307,13 +323,13 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(const AttnArgs a) 
         m[j] = c0 + j < S ? m[j] : -INFINITY;
         Mc = fmaxf(Mc, m[j]);
       }
-      const float sc = M == -INFINITY ? 0.f : expf(M - Mc);
+      const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
       L *= sc;
       O *= sc;
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         const bool on = m[j] != -INFINITY;
-        const float e = on ? expf(m[j] - Mc) : 0.f;
+        const float e = on ? __builtin_amdgcn_exp2f(m[j] - Mc) : 0.f;
         L += on ? e * lv[j] : 0.f;
         O += on ? e * ov[j] : 0.f;
       }
