@@ -116,7 +116,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   const int H = cfg->hidden_size, Hq = cfg->num_attention_heads;
   const int Hkv = cfg->num_key_value_heads, I = cfg->intermediate_size;
   const int QD = Hq * kHeadDim;
-  float* q = at<float>(ws, L.q);
+  uint16_t* q = at<uint16_t>(ws, L.q);  // [B][Hq][2][D] BF16 hi, lo
   float* o_p = at<float>(ws, L.o_p);
   float* h1 = at<float>(ws, L.h1);
   float* h1_p = at<float>(ws, L.h1_p);
@@ -149,7 +149,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.Hkv = Hkv;
     rc = gemm_batched(EPI_QKV, a.N, batch, a, [&](GemmArgs& c, int b0) {
       c.X = hidden_packed ? packed_at(const_cast<float*>(hidden_packed), b0, H) : hidden + (size_t)b0 * H;
-      c.q_out = q + (size_t)b0 * QD;
+      c.q_split = q + (size_t)b0 * 2 * QD;
       c.bt = bt + (size_t)b0 * max_pages;
       c.pos = pos + b0;
     }, st);
@@ -176,7 +176,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.Hkv = Hkv;
     a.G = Hq / Hkv;
     a.max_splits = attn_max_splits(max_pages);
-    if ((rc = io(launch_attention(a, batch, false, st)))) return rc;
+    if ((rc = io(launch_attention(a, batch, kQSplit, st)))) return rc;
   }
 
   // 3. output projection + residual: h1 = x + W_o o
@@ -315,7 +315,7 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   a.Hkv = pool->num_kv_heads;
   a.G = num_q_heads / pool->num_kv_heads;
   a.max_splits = attn_max_splits(max_pages);
-  return io(launch_attention(a, batch, true, (hipStream_t)stream));
+  return io(launch_attention(a, batch, kQBf16, (hipStream_t)stream));
 }
 
 int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,

@@ -45,18 +45,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Eight consecutive q values (BF16 bits or FP32) as FP32, vector loads.
-__device__ __forceinline__ void load_q8(const uint16_t* p, float (&v)[8]) {
-  const uint4 w = *(const uint4*)p;
-  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-}
-__device__ __forceinline__ void load_q8(const float* p, float (&v)[8]) {
-  const float4 x0 = *(const float4*)p, x1 = *(const float4*)(p + 4);
-  v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-  v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
-}
-
 __device__ __forceinline__ f32x4 mfma_k32(u32x4 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
@@ -83,8 +71,9 @@ __device__ __forceinline__ u32x2 keep_first(u32x2 v, int nv) {
   return r;
 }
 
-template <typename QT>
-__global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const AttnArgs a) {
+template <int QM>
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 5))) void
+paged_attention_kernel(const AttnArgs a) {
   constexpr int PW = kAttnPW;
   constexpr int CP = kAttnPagesPerSplit;
   constexpr int NW = kAttnWaves;
@@ -146,14 +135,19 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
     lpv[i] = live && ok ? lp : -1;
     page[i] = live && ok ? page[i] : 0;
   }
-  // q^T operand (prescaled): lane holds head g = col, dims 8*grp + e + 32*h;
-  // lanes past the group read head 0 of the group and use zeros
-  float qv[2][8];
-  {
-    const int gq = col < G ? col : 0;
-    const QT* qp = (const QT*)a.q + ((size_t)b * a.Hq + (size_t)kvh * G + gq) * kHeadDim + 8 * grp;
-    load_q8(qp, qv[0]);
-    load_q8(qp + 32, qv[1]);
+  // q^T operand: lane holds head g = col, dims 8*grp + e + 32*h; lanes past
+  // the group read head 0 of the group and use zeros.  Both q formats are
+  // the matrix operand as loaded: BF16 q, or an FP32 q's BF16 hi and lo
+  // halves (two products per block).
+  constexpr bool kSplitQ = QM == kQSplit;
+  const int gq = col < G ? col : 0;
+  const size_t qhead = (size_t)b * a.Hq + (size_t)kvh * G + gq;
+  const uint16_t* qp = a.q + qhead * (kSplitQ ? 2 : 1) * kHeadDim + 8 * grp;
+  u32x4 qraw[2], qlraw[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    qraw[h] = *(const u32x4*)(qp + 32 * h);
+    if (kSplitQ) qlraw[h] = *(const u32x4*)(qp + kHeadDim + 32 * h);
   }
   u32x4 kr[PW][2];
   u32x2 vr[PW][4];
@@ -174,19 +168,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
   }
   __builtin_amdgcn_sched_barrier(0);
   if (bad && l == 0) set_error(a.err, ERR_PAGE);
-  // scores are kept in base-2 units (q prescaled by scale * log2 e), so
-  // every exponential is one hardware 2^x
-  const float qscale = a.scale * kLog2e;
+  // The scores q.K come out unscaled; the softmax applies scale * log2 e in
+  // the exponent, so that every exponential is one hardware 2^x and the
+  // maxima m kept in the records are in base-2 units.
+  const float c2 = a.scale * kLog2e;
   bf16x8 qh[2], ql[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = col < G ? qv[h][e] * qscale : 0.f;
-      const __bf16 hi = (__bf16)v;
-      qh[h][e] = hi;
-      ql[h][e] = (__bf16)(v - (float)hi);
-    }
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qh[h] = __builtin_bit_cast(bf16x8, col < G ? qraw[h] : z);
+    if (kSplitQ) ql[h] = __builtin_bit_cast(bf16x8, col < G ? qlraw[h] : z);
+  }
 
   // ---- scores: lane holds S[t = 4*grp + r][g = col] of each page
   bool full[PW];
@@ -198,9 +190,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
   for (int i = 0; i < PW; ++i) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = mfma_k32(kr[i][0], qh[0], acc);
-    acc = mfma_k32(kr[i][0], ql[0], acc);
+    if (kSplitQ) acc = mfma_k32(kr[i][0], ql[0], acc);
     acc = mfma_k32(kr[i][1], qh[1], acc);
-    acc = mfma_k32(kr[i][1], ql[1], acc);
+    if (kSplitQ) acc = mfma_k32(kr[i][1], ql[1], acc);
     // a full page (every page of a sequence but its last) needs no mask;
     // the test is uniform across the wave
     if (!full[i]) {
@@ -217,16 +209,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-  // ---- P = 2^(S - m) split hi/lo; row sums.  Masked scores are -inf and
-  // give 0; a wave with no token at all (m = -inf) subtracts 0 instead.
+  // ---- P = 2^((S - m) scale log2 e) split hi/lo; row sums.  Masked scores
+  // are -inf and give 0; a wave with no token at all (m = -inf) subtracts 0.
   const float msub = mx == -INFINITY ? 0.f : mx;
+  const float m2 = mx == -INFINITY ? -INFINITY : mx * c2;  // base-2 units
   float lsum = 0.f;
   s16x4 ph[PW], pl[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[i][r] - msub);
+      const float p = __builtin_amdgcn_exp2f((s[i][r] - msub) * c2);
       lsum += p;
       const __bf16 hi = (__bf16)p;
       ph[i][r] = __builtin_bit_cast(short, hi);
@@ -253,7 +246,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attention_kernel(const 
 
   // ---- merge the four waves
   if (grp == 0) {
-    sm_m[w][col] = mx;
+    sm_m[w][col] = m2;
     sm_l[w][col] = lsum;
   }
 #pragma unroll
@@ -341,16 +334,16 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(const AttnArgs a) 
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, int batch, bool q_is_bf16, hipStream_t st) {
+hipError_t launch_attention(const AttnArgs& a, int batch, int qmode, hipStream_t st) {
   // kv head fastest: workgroups go to the 8 XCDs round-robin in launch
   // order, so every XCD gets the same mix of sequences and splits (with
   // the split fastest, the XCDs holding the low splits of every sequence
   // would get most of the non-empty workgroups)
   const dim3 grid(a.Hkv, batch, a.max_splits);
-  if (q_is_bf16)
-    paged_attention_kernel<uint16_t><<<grid, kAttnWaves * 64, 0, st>>>(a);
+  if (qmode == kQSplit)
+    paged_attention_kernel<kQSplit><<<grid, kAttnWaves * 64, 0, st>>>(a);
   else
-    paged_attention_kernel<float><<<grid, kAttnWaves * 64, 0, st>>>(a);
+    paged_attention_kernel<kQBf16><<<grid, kAttnWaves * 64, 0, st>>>(a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits <= 1) return e;
   attention_merge_kernel<<<dim3(a.Hkv, batch), 256, 0, st>>>(a);

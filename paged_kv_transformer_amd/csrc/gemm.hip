@@ -24,7 +24,8 @@
 // Fused epilogues:
 //   EPI_QKV     16 rows = 8 RoPE pairs (j, j+32) of one head: RoPE on q and
 //               k heads (angle from the FP32 cos/sin tables at the
-//               sequence's position); q -> FP32 buffer, k and v -> BF16
+//               sequence's position); q -> BF16 hi + lo halves (the
+//               attention's matrix operand, ~16 bits), k and v -> BF16
 //               (nearest even) into the sequence's page at its position
 //               (the KV append).
 //   EPI_RESID   out = resid + y (output projection, down projection), also
@@ -282,9 +283,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         y1 = __fadd_rn(__fmul_rn(x0, sn), __fmul_rn(x1, cs));
       }
       if (is_q) {
-        float* qo = a.q_out + ((size_t)c * a.Hq + hd) * kHeadDim;
-        qo[j] = y0;
-        qo[j + 32] = y1;
+        // q leaves as the attention's matrix operand: BF16 hi and lo halves
+        uint16_t* qo = a.q_split + ((size_t)c * a.Hq + hd) * 2 * kHeadDim;
+        const uint16_t h0 = to_bf16_bits(y0), h1 = to_bf16_bits(y1);
+        qo[j] = h0;
+        qo[j + 32] = h1;
+        qo[kHeadDim + j] = to_bf16_bits(y0 - bf16_lo(h0));
+        qo[kHeadDim + j + 32] = to_bf16_bits(y1 - bf16_lo(h1));
       } else {
         if (p < 0 || p / kPageTokens >= a.bt_stride) {
           set_error(a.err, ERR_LENGTH);

@@ -79,7 +79,7 @@ inline int64_t packed_act_elems(int B, int K) { return (int64_t)((B + 15) / 16) 
 // --------------------------------------------------------- arguments ---
 
 struct AttnArgs {
-  const void* q;           // [B][Hq][D], BF16 bits or FP32 (template)
+  const uint16_t* q;       // BF16: [B][Hq][D], or [B][Hq][2][D] hi/lo split (kQSplit)
   const uint16_t* pool;    // page pool base
   int64_t page_elems;      // BF16 elements per page
   int32_t num_pages;
@@ -117,7 +117,7 @@ struct GemmArgs {
   float* part;
   int32_t ksplit;
   // EPI_QKV
-  float* q_out;            // [B][Hq][D]
+  uint16_t* q_split;       // [B][Hq][2][D]: each head's q as BF16 hi, then lo
   uint16_t* pool;
   int64_t page_elems;
   int32_t num_pages;
@@ -237,7 +237,7 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_p
   w.err = take(256);
   w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_pages) * kAttnRec);
   if (layer) {
-    w.q = take(sizeof(float) * (size_t)B * Hq * kHeadDim);
+    w.q = take(sizeof(float) * (size_t)B * Hq * kHeadDim);  // BF16 hi + lo per value
     w.o_p = take(sizeof(float) * (size_t)packed_act_elems(B, Hq * kHeadDim));
     w.h1 = take(sizeof(float) * (size_t)B * H);
     w.h1_p = take(sizeof(float) * (size_t)packed_act_elems(B, H));
@@ -259,7 +259,10 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_p
 
 // Each returns hipSuccess or the launch error.
 // The split kernel, then the merge of sequences that took several splits.
-hipError_t launch_attention(const AttnArgs& a, int batch, bool q_is_bf16, hipStream_t st);
+// q formats of the attention kernel
+constexpr int kQBf16 = 0;   // BF16 q, the matrix operand as it is
+constexpr int kQSplit = 1;  // an FP32 q stored as BF16 hi and lo halves
+hipError_t launch_attention(const AttnArgs& a, int batch, int qmode, hipStream_t st);
 hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_t st);
 hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_pages,
                             const int32_t* bt, int32_t bt_stride, const int32_t* pos,
