@@ -171,13 +171,17 @@ paged_attention_kernel(const AttnArgs a) {
   // The scores q.K come out unscaled; the softmax applies scale * log2 e in
   // the exponent, so that every exponential is one hardware 2^x and the
   // maxima m kept in the records are in base-2 units.
-  const float c2 = a.scale * kLog2e;
+  // A negative scale flips the sign of q instead (exact in BF16), so that
+  // the factor in the exponent is never negative and the row maximum of the
+  // raw scores is the maximum of the scaled ones.
+  const float c2 = fabsf(a.scale) * kLog2e;
+  const unsigned sgn = a.scale < 0.f ? 0x80008000u : 0u;
   bf16x8 qh[2], ql[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    qh[h] = __builtin_bit_cast(bf16x8, col < G ? qraw[h] : z);
-    if (kSplitQ) ql[h] = __builtin_bit_cast(bf16x8, col < G ? qlraw[h] : z);
+    qh[h] = __builtin_bit_cast(bf16x8, col < G ? qraw[h] ^ sgn : z);
+    if (kSplitQ) ql[h] = __builtin_bit_cast(bf16x8, col < G ? qlraw[h] ^ sgn : z);
   }
 
   // ---- scores: lane holds S[t = 4*grp + r][g = col] of each page
@@ -219,7 +223,10 @@ paged_attention_kernel(const AttnArgs a) {
   for (int i = 0; i < PW; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f((s[i][r] - msub) * c2);
+      float x = (s[i][r] - msub) * c2;
+      // masked scores stay -inf (a zero scale would otherwise make them NaN)
+      if (!full[i]) x = s[i][r] == -INFINITY ? -INFINITY : x;
+      const float p = __builtin_amdgcn_exp2f(x);
       lsum += p;
       const __bf16 hi = (__bf16)p;
       ph[i][r] = __builtin_bit_cast(short, hi);

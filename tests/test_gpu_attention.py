@@ -87,15 +87,26 @@ CASES = [
 
 @pytest.mark.parametrize("Hq,Hkv,lens,max_pages", CASES)
 def test_attention_small_cases(Hq, Hkv, lens, max_pages):
-    say("attention", Hq, Hkv, lens, max_pages)
+    _small_case(Hq, Hkv, lens, max_pages, 0.125)
+
+
+@pytest.mark.parametrize("scale", [0.2, -0.125, 0.0])
+def test_attention_other_scales(scale):
+    """Any finite scale: a larger one, a negative one (the softmax favours
+    the most negative scores) and zero (every token weighs the same)."""
+    _small_case(8, 2, [1, 15, 16, 17, 300], 20, scale)
+
+
+def _small_case(Hq, Hkv, lens, max_pages, scale):
+    say("attention", Hq, Hkv, lens, max_pages, scale)
     lens = np.asarray(lens, dtype=np.int32)
     pe = synth.page_elems(Hkv)
     npages = int(synth.pages_for(lens).sum()) + 5
     pool = synth.random_pool(21, npages, pe)
     bt = synth.block_tables(22, 1, lens, npages, max_pages=max_pages)[0]
     q = synth.bf16_normal(23, "q", (len(lens), Hq, 64))
-    out, err = attention_gpu(pool, Hkv, q, bt, lens, 0.125)
-    ref = attention_oracle(pool, Hkv, q, bt, lens, 0.125)
+    out, err = attention_gpu(pool, Hkv, q, bt, lens, scale)
+    ref = attention_oracle(pool, Hkv, q, bt, lens, scale)
     assert err == 0
     assert np.abs(out - ref).max() <= ATOL
     assert np.all(out[lens == 0] == 0)
