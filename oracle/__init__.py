@@ -26,6 +26,9 @@ Parity pins (what each function is checked against, in tests/):
                          V [head][d][slot]
   layer, step            float64 brute force with a materialised softmax on
                          tiny shapes; all-zero weights leave x unchanged
+  prefill                float64 brute force of the whole prompt at once with a
+                         causal mask (last logits, argmax, every K/V row
+                         written); a one-token prefill equals a decode step
   argmax                 numpy.argmax (first maximum)
 Full-size layer and step outputs have no printed values on the source pages:
 beyond the pins above they are "parity unpinned".
@@ -314,3 +317,30 @@ def decode_step_paged(shape, weights, pool, geo, block_tables, positions, tokens
             logits[b] = lg
         nxt[b] = best
     return logits, nxt, k_new, v_new
+
+
+def prefill_paged(shape, weights, pool, geo, block_tables, start_pos, tokens, want_logits=True):
+    """Prefill of one sequence's prompt: tokens[t] sits at position
+    start_pos + t, and tokens 0..start_pos-1 are already in the pool.  The
+    plain definition of causal prefill is the prompt run one token at a time:
+    each token is a decode step of this sequence at its own position whose
+    K and V are appended to the pool before the next token runs ("Inference
+    from Scratch", dense causal prefill and page-pool bullets: prefill fills
+    the prompt's pages, attention is causal).  block_tables [L, max_pages]
+    is this sequence's table per layer.  Returns (logits of the last token
+    [V] or None, its argmax, the pool after every append)."""
+    pool = np.array(_u16(pool), copy=True)
+    L = shape.layers
+    lg = best = None
+    for t, tok in enumerate(np.asarray(tokens)):
+        p = int(start_pos) + t
+        x = embed(weights["embed"], int(tok))
+        for l in range(L):
+            kc, vc = pool_gather(pool, geo, block_tables[l], p)
+            kc = np.concatenate([kc, np.zeros((1, kc.shape[1]), np.float32)])
+            vc = np.concatenate([vc, np.zeros((1, vc.shape[1]), np.float32)])
+            x, k_bits, v_bits = layer_decode(shape, weights["layers"][l], x, kc, vc, p)
+            pool_append(pool, geo, block_tables[l], p, k_bits, v_bits)
+        if t == len(tokens) - 1:
+            lg, best = lm_head(weights["embed"], weights["final_norm"], shape.eps, x)
+    return (lg if want_logits else None), best, pool

@@ -121,3 +121,43 @@ def online_softmax_attention(q, K, V, scale, block):
         acc = acc * alpha + p @ V[t0:t0 + block]
         m = m_new
     return acc / l
+
+
+def prefill(shape, weights, pool, bts, start, tokens):
+    """Float64 prefill of one sequence's whole prompt at once: tokens[t] at
+    position start + t over a cache of `start` tokens (bts [L, max_pages]).
+    Every layer projects all prompt tokens together and applies causal
+    attention through a materialised mask over [start + T] keys.  Returns
+    (logits of the last token, [(K, V) BF16-rounded [T, hkv, D] per layer])."""
+    H, hq, hkv, D, I = shape.hidden, shape.heads, shape.kv_heads, shape.head_dim, shape.inter
+    tokens = np.asarray(tokens)
+    T = len(tokens)
+    E = bf16_bits_to_f64(weights["embed"])
+    X = E[tokens].copy()                                    # [T, H]
+    pos = start + np.arange(T)
+    written = []
+    for l in range(shape.layers):
+        W = {k: bf16_bits_to_f64(v) for k, v in weights["layers"][l].items()}
+        K0, V0 = gather(pool, hkv, D, bts[l], start)         # [start, hkv, D]
+        QKV = rmsnorm(X, W["attn_norm"], shape.eps) @ W["w_qkv"].T
+        Q = QKV[:, :hq * D].reshape(T, hq, D)
+        K = QKV[:, hq * D:(hq + hkv) * D].reshape(T, hkv, D)
+        V = QKV[:, (hq + hkv) * D:].reshape(T, hkv, D)
+        Q = np.stack([rope(Q[t], pos[t], shape.theta) for t in range(T)])
+        K = bf16_round_f64(np.stack([rope(K[t], pos[t], shape.theta) for t in range(T)]))
+        V = bf16_round_f64(V)
+        written.append((K, V))
+        Kall = np.repeat(np.concatenate([K0, K]), hq // hkv, axis=1)   # [start+T, hq, D]
+        Vall = np.repeat(np.concatenate([V0, V]), hq // hkv, axis=1)
+        S = np.einsum("thd,nhd->thn", Q, Kall) / np.sqrt(D)
+        causal = np.arange(start + T)[None, :] > pos[:, None]        # key after the query
+        S = np.where(causal[:, None, :], -np.inf, S)
+        P = np.exp(S - S.max(axis=2, keepdims=True))
+        P = P / P.sum(axis=2, keepdims=True)
+        O = np.einsum("thn,nhd->thd", P, Vall).reshape(T, hq * D)
+        H1 = X + O @ W["w_o"].T
+        GU = rmsnorm(H1, W["mlp_norm"], shape.eps) @ W["w_gate_up"].T
+        G, U = GU[:, :I], GU[:, I:]
+        X = H1 + (G / (1.0 + np.exp(-G)) * U) @ W["w_down"].T
+    logits = E @ rmsnorm(X[-1], bf16_bits_to_f64(weights["final_norm"]), shape.eps)
+    return logits, written

@@ -391,3 +391,52 @@ def test_swiglu_gate_then_up():
     out_sw, _, _ = oracle.layer_decode(shape, sw, x, np.zeros((1, kvd), np.float32),
                                        np.zeros((1, kvd), np.float32), 0)
     assert not np.array_equal(out, x) and not np.allclose(out, out_sw)
+
+
+# ------------------------------------------------------------- prefill ---
+
+def _prefill_inputs(seed, start, T):
+    shape = TINY
+    wts = synth.model_weights(shape, seed, sigma=0.3, norm_sigma=0.3)
+    wl = synth.decode_workload("tiny-prefill", shape, seed, [start + T - 1], num_pages=40)
+    tokens = synth.rng(seed, "tokens").integers(0, shape.vocab, size=T)
+    return shape, wts, wl.pool, wl.block_tables[:, 0], tokens
+
+
+@pytest.mark.parametrize("start,T", [(0, 21), (7, 25)])
+def test_prefill_matches_float64_causal_brute_force(start, T):
+    """The oracle's prefill (one decode step per prompt token) against the
+    whole prompt computed at once in float64 with a causal mask: last
+    token's logits, its argmax, and every K/V row written to the pool."""
+    shape, wts, pool, bts, tokens = _prefill_inputs(11 + start, start, T)
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
+    logits, best, pool_after = oracle.prefill_paged(shape, wts, pool, geo, bts, start, tokens)
+    ref_logits, written = brute.prefill(shape, wts, pool, bts, start, tokens)
+    np.testing.assert_allclose(logits, ref_logits, rtol=1e-5, atol=1e-5)
+    top2 = np.sort(ref_logits)[-2:]
+    if top2[1] - top2[0] > 1e-4:
+        assert best == int(np.argmax(ref_logits))
+    kv_view, vv_view = brute.pool_view(pool_after, shape.kv_heads, shape.head_dim)
+    touched = np.zeros(pool.shape, dtype=bool)
+    tv, vv_t = brute.pool_view(touched, shape.kv_heads, shape.head_dim)
+    for l in range(shape.layers):
+        K, V = written[l]
+        for t in range(T):
+            p = start + t
+            page, slot = bts[l][p // 16], p % 16
+            got_k = brute.bf16_bits_to_f64(kv_view[page, :, slot, :])
+            got_v = brute.bf16_bits_to_f64(vv_view[page, :, :, slot])
+            # one BF16 ulp at most (FP32 vs float64 values before rounding)
+            np.testing.assert_allclose(got_k, K[t], rtol=2 ** -7, atol=1e-6)
+            np.testing.assert_allclose(got_v, V[t], rtol=2 ** -7, atol=1e-6)
+            tv[page, :, slot, :] = True
+            vv_t[page, :, :, slot] = True
+    assert np.array_equal(pool_after[~touched], pool[~touched])
+
+
+def test_prefill_of_one_token_is_a_decode_step():
+    shape, wts, pool, bts, tokens = _prefill_inputs(13, 30, 1)
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
+    logits, best, _ = oracle.prefill_paged(shape, wts, pool, geo, bts, 30, tokens)
+    ref, nxt, _, _ = oracle.decode_step_paged(shape, wts, pool, geo, bts[:, None], [30], tokens)
+    assert np.array_equal(logits, ref[0]) and best == nxt[0]
