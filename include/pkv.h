@@ -225,6 +225,38 @@ int decode_step(const pkv_config *cfg, const pkv_model_weights *w,
 		void *stream);
 
 /*
+ * prefill — dense causal prefill of one sequence's prompt into the pool
+ * ("Inference from Scratch": prefill fills the prompt's pages, attention is
+ * causal; one prompt at a time).  token_ids[t] is at position
+ * start_pos + t; positions 0 .. start_pos-1 must already be in the pool.
+ * Every layer projects all num_tokens tokens together, appends their BF16
+ * K and V to the sequence's pages, and lets token t attend to positions
+ * 0 .. start_pos + t.  Afterwards the final RMSNorm and the tied LM head
+ * give the last token's FP32 logits and next_token[0] = their argmax.  The
+ * arithmetic of every token is that of a decode step of this sequence at
+ * its position, so the pages it writes equal those num_tokens successive
+ * decode_step calls would write.
+ *   block_tables [num_layers][max_pages]: this sequence's table per layer,
+ *   mapping every page up to position start_pos + num_tokens - 1.
+ *   token_ids [num_tokens] (device), logits [vocab_size] FP32 or NULL,
+ *   next_token [1] int32.  workspace: at least
+ *   pkv_prefill_workspace_bytes(cfg, num_tokens, max_pages) bytes.
+ * num_tokens == 0 is a no-op.  Errors: -EINVAL (NULL, negative sizes,
+ * start_pos + num_tokens past the table or the RoPE table), -ENOTSUP
+ * (num_tokens > 65535, unsupported sizes as decoder_layer_decode),
+ * -ENOSPC (workspace), -EIO; device errors as decode_step.
+ */
+int prefill(const pkv_config *cfg, const pkv_model_weights *w,
+	    const pkv_pool *pool, const int32_t *block_tables,
+	    int32_t max_pages, int32_t start_pos, const int32_t *token_ids,
+	    int32_t num_tokens, float *logits, int32_t *next_token,
+	    void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes prefill needs (0 for an invalid config or size). */
+size_t pkv_prefill_workspace_bytes(const pkv_config *cfg, int32_t num_tokens,
+				   int32_t max_pages);
+
+/*
  * Packed weight layout (used by every matrix the projections stream): the
  * matrix is cut into groups of 16 rows and its columns into 32-wide steps;
  * block (group G, step s) is 1 KiB, and its 16-byte chunk l = 16 i + m

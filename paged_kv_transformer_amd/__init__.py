@@ -78,6 +78,9 @@ def lib():
                                                     P, P, PP, P, I32, P, I32, P, P, SZ, P]),
             "decode_step": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights), PP, P,
                                            I32, P, P, I32, P, P, P, SZ, P]),
+            "prefill": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights), PP, P, I32, I32,
+                                       P, I32, P, P, P, SZ, P]),
+            "pkv_prefill_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32]),
             "pkv_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32]),
             "pkv_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
             "pkv_workspace_init": (ctypes.c_int, [P, SZ, P]),
@@ -274,6 +277,24 @@ def decode_step(cfg, model, pool, block_tables, positions, token_ids, logits, ne
         _dev(positions, (torch.int32,), "positions"), _dev(token_ids, (torch.int32,), "token_ids"), B,
         None if logits is None else _dev(logits, (torch.float32,), "logits"),
         _dev(next_tokens, (torch.int32,), "next_tokens"), _dev(workspace, (torch.uint8,), "workspace"),
+        workspace.numel(), _stream(stream)))
+
+
+def prefill_workspace_bytes(cfg, num_tokens, max_pages):
+    return lib().pkv_prefill_workspace_bytes(ctypes.byref(cfg), num_tokens, max_pages)
+
+
+def prefill(cfg, model, pool, block_tables, start_pos, token_ids, logits, next_token, workspace,
+            stream=None):
+    """Prefill of one sequence: block_tables [L, max_pages] (its table per
+    layer), token_ids [T] at positions start_pos ..; logits [V] FP32 or None
+    (the last token's), next_token [1] int32."""
+    _check("prefill", lib().prefill(
+        ctypes.byref(cfg), ctypes.byref(model.c), ctypes.byref(pool),
+        _dev(block_tables, (torch.int32,), "block_tables"), block_tables.shape[-1], int(start_pos),
+        _dev(token_ids, (torch.int32,), "token_ids"), token_ids.numel(),
+        None if logits is None else _dev(logits, (torch.float32,), "logits"),
+        _dev(next_token, (torch.int32,), "next_token"), _dev(workspace, (torch.uint8,), "workspace"),
         workspace.numel(), _stream(stream)))
 
 

@@ -111,8 +111,8 @@ float* packed_at(float* base, int b0, int K) { return base + packed_act_index(b0
 // projection; hidden_packed, if given, is hidden already packed.
 int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* rope_cos,
               const float* rope_sin, const pkv_pool* pool, const int32_t* bt, int32_t max_pages,
-              const int32_t* pos, int32_t batch, float* hidden, const float* hidden_packed,
-              void* ws, const WsLayout& L, hipStream_t st) {
+              int32_t bt_row, const int32_t* pos, int32_t batch, float* hidden,
+              const float* hidden_packed, void* ws, const WsLayout& L, hipStream_t st) {
   const int H = cfg->hidden_size, Hq = cfg->num_attention_heads;
   const int Hkv = cfg->num_key_value_heads, I = cfg->intermediate_size;
   const int QD = Hq * kHeadDim;
@@ -142,6 +142,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.page_elems = pool->page_bytes / 2;
     a.num_pages = pool->num_pages;
     a.bt_stride = max_pages;
+    a.bt_row = bt_row;
     a.rcos = rope_cos;
     a.rsin = rope_sin;
     a.max_pos = cfg->max_position_embeddings;
@@ -150,7 +151,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     rc = gemm_batched(EPI_QKV, a.N, batch, a, [&](GemmArgs& c, int b0) {
       c.X = hidden_packed ? packed_at(const_cast<float*>(hidden_packed), b0, H) : hidden + (size_t)b0 * H;
       c.q_split = q + (size_t)b0 * 2 * QD;
-      c.bt = bt + (size_t)b0 * max_pages;
+      c.bt = bt + (size_t)b0 * bt_row;
       c.pos = pos + b0;
     }, st);
     if (rc) return rc;
@@ -165,6 +166,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.num_pages = pool->num_pages;
     a.bt = bt;
     a.bt_stride = max_pages;
+    a.bt_row = bt_row;
     a.lens = pos;
     a.len_add = 1;
     a.scale = 1.0f / sqrtf((float)kHeadDim);
@@ -305,6 +307,7 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   a.num_pages = pool->num_pages;
   a.bt = block_table;
   a.bt_stride = max_pages;
+  a.bt_row = max_pages;
   a.lens = context_lens;
   a.len_add = 0;
   a.scale = scale;
@@ -333,8 +336,8 @@ int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
   const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
                                cfg->num_key_value_heads, cfg->intermediate_size,
                                cfg->vocab_size, max_pages, true);
-  return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, positions, batch,
-                   hidden, nullptr, workspace, L, (hipStream_t)stream);
+  return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, max_pages, positions,
+                   batch, hidden, nullptr, workspace, L, (hipStream_t)stream);
 }
 
 int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* pool,
@@ -363,8 +366,8 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
   if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, x_p, batch, err, st)))) return rc;
   for (int l = 0; l < cfg->num_hidden_layers; ++l) {
     rc = run_layer(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool,
-                   block_tables + (size_t)l * batch * max_pages, max_pages, positions, batch, x,
-                   x_p, workspace, L, st);
+                   block_tables + (size_t)l * batch * max_pages, max_pages, max_pages, positions,
+                   batch, x, x_p, workspace, L, st);
     if (rc) return rc;
   }
   GemmArgs a{};
@@ -383,6 +386,84 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
   }, st);
   if (rc) return rc;
   return 0;
+}
+
+// Prefill workspace: the layer workspace of a batch of num_tokens columns,
+// then the prompt's positions.
+static size_t prefill_pos_offset(const pkv_config* cfg, int32_t num_tokens, int32_t max_pages) {
+  return ws_layout(num_tokens, cfg->hidden_size, cfg->num_attention_heads,
+                   cfg->num_key_value_heads, cfg->intermediate_size, cfg->vocab_size, max_pages,
+                   true)
+      .total;
+}
+
+size_t pkv_prefill_workspace_bytes(const pkv_config* cfg, int32_t num_tokens, int32_t max_pages) {
+  if (check_cfg(cfg) || num_tokens < 1 || max_pages < 1) return 0;
+  return prefill_pos_offset(cfg, num_tokens, max_pages) + align256(sizeof(int32_t) * num_tokens);
+}
+
+int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* pool,
+            const int32_t* block_tables, int32_t max_pages, int32_t start_pos,
+            const int32_t* token_ids, int32_t num_tokens, float* logits, int32_t* next_token,
+            void* workspace, size_t ws_bytes, void* stream) {
+  if (!w) return -EINVAL;
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  rc = check_pool(pool);
+  if (rc) return rc;
+  if (pool->num_kv_heads != cfg->num_key_value_heads) return -EINVAL;
+  if (num_tokens < 0 || max_pages < 1 || start_pos < 0) return -EINVAL;
+  if (num_tokens > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
+  if (num_tokens == 0) return 0;
+  if ((int64_t)start_pos + num_tokens > (int64_t)max_pages * kPageTokens ||
+      (int64_t)start_pos + num_tokens > cfg->max_position_embeddings)
+    return -EINVAL;
+  if (cfg->num_hidden_layers < 1 || cfg->vocab_size < 1) return -EINVAL;
+  if (!w->embed || !w->final_norm || !w->layers || !w->rope_cos || !w->rope_sin) return -EINVAL;
+  if (!block_tables || !token_ids || !next_token || !workspace) return -EINVAL;
+  if (!aligned(workspace, 256)) return -EINVAL;
+  for (int l = 0; l < cfg->num_hidden_layers; ++l)
+    if ((rc = check_layer_weights(&w->layers[l]))) return rc;
+  if (ws_bytes < pkv_prefill_workspace_bytes(cfg, num_tokens, max_pages)) return -ENOSPC;
+
+  const hipStream_t st = (hipStream_t)stream;
+  const int H = cfg->hidden_size, V = cfg->vocab_size, T = num_tokens;
+  const WsLayout L = ws_layout(T, H, cfg->num_attention_heads, cfg->num_key_value_heads,
+                               cfg->intermediate_size, V, max_pages, true);
+  int32_t* pos = at<int32_t>(workspace, L.total);
+  float* x = at<float>(workspace, L.x);
+  float* x_p = at<float>(workspace, L.x_p);
+  uint32_t* err = at<uint32_t>(workspace, L.err);
+
+  // the prompt is a batch of T queries of one sequence: token t at position
+  // start_pos + t, all sharing the sequence's table row (row stride 0), so
+  // that each query attends causally to positions 0 .. start_pos + t
+  if ((rc = io(launch_iota(pos, T, start_pos, st)))) return rc;
+  if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, x_p, T, err, st)))) return rc;
+  for (int l = 0; l < cfg->num_hidden_layers; ++l) {
+    rc = run_layer(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool,
+                   block_tables + (size_t)l * max_pages, max_pages, 0, pos, T, x, x_p, workspace,
+                   L, st);
+    if (rc) return rc;
+  }
+  // final norm, LM head and argmax of the last prompt token only
+  GemmArgs a{};
+  a.W = w->embed;
+  a.w_groups = (V + 15) / 16;
+  a.xw = w->final_norm;
+  a.N = V;
+  a.K = H;
+  a.B = 1;
+  a.eps = cfg->rms_norm_eps;
+  a.err = err;
+  a.amax_part = at<unsigned long long>(workspace, L.amax_part);
+  a.X = x + (size_t)(T - 1) * H;
+  a.x_plain = 1;
+  a.logits = logits;
+  a.next_tok = next_token;
+  const GemmPlan p = plan_gemm(EPI_LOGITS, V, 1, H);
+  a.ksplit = p.ks;
+  return io(launch_gemm(EPI_LOGITS, a, p, st));
 }
 
 size_t pkv_packed_weight_bytes(int32_t rows, int32_t cols, int32_t layout) {

@@ -94,7 +94,7 @@ paged_attention_kernel(const AttnArgs a) {
   // together: the empty asm makes the entries live before the length test,
   // so they are not sunk below it into a second round trip.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int32_t* btrow = a.bt + (size_t)b * a.bt_stride;
+  const int32_t* btrow = a.bt + (size_t)b * a.bt_row;
   int page[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) page[i] = btrow[min(split * CP + NW * i + wu, a.bt_stride - 1)];

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
           set_error(a.err, ERR_LENGTH);
           continue;
         }
-        const int page = a.bt[(size_t)c * a.bt_stride + p / kPageTokens];
+        const int page = a.bt[(size_t)c * a.bt_row + p / kPageTokens];
         if ((unsigned)page >= (unsigned)a.num_pages) {
           set_error(a.err, ERR_PAGE);
           continue;
@@ -448,7 +448,10 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
       e = one ? go<1, 2, 4, EPI_SWIGLU>(a, p.tiles, st) : go<2, 1, 4, EPI_SWIGLU>(a, p.tiles, st);
       break;
     case EPI_LOGITS:
-      e = one ? go<1, 2, 4, EPI_LOGITS>(a, p.tiles, st) : go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st);
+      if (a.x_plain)  // one plain activation row (the last prompt token)
+        e = one ? go<1, 2, 4, EPI_LOGITS, true>(a, p.tiles, st) : hipErrorInvalidValue;
+      else
+        e = one ? go<1, 2, 4, EPI_LOGITS>(a, p.tiles, st) : go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st);
       if (e != hipSuccess) return e;
       argmax_finalize_kernel<<<a.B, 256, 0, st>>>(a.amax_part, p.tiles, a.B, a.next_tok);
       e = hipGetLastError();

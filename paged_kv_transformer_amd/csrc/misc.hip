@@ -87,6 +87,11 @@ __global__ void rope_table_kernel(double theta, int D, int max_pos, float* c, fl
   s[idx] = (float)sin(ang);
 }
 
+__global__ void iota_kernel(int32_t* p, int n, int start) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = start + i;
+}
+
 __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
@@ -125,6 +130,11 @@ hipError_t launch_rope_table(double theta, int D, int max_pos, float* c, float* 
   const int64_t n = (int64_t)max_pos * (D / 2);
   const int blocks = (int)((n + 255) / 256);
   rope_table_kernel<<<blocks, 256, 0, st>>>(theta, D, max_pos, c, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_iota(int32_t* p, int n, int start, hipStream_t st) {
+  iota_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n, start);
   return hipGetLastError();
 }
 

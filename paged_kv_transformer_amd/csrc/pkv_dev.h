@@ -83,8 +83,9 @@ struct AttnArgs {
   const uint16_t* pool;    // page pool base
   int64_t page_elems;      // BF16 elements per page
   int32_t num_pages;
-  const int32_t* bt;       // [B][bt_stride]
-  int32_t bt_stride;       // max_pages
+  const int32_t* bt;       // sequence b's table starts at bt + b * bt_row
+  int32_t bt_stride;       // table width (max_pages)
+  int32_t bt_row;          // elements between sequences' rows (0: one shared row)
   const int32_t* lens;     // [B]: attention length, or position (len_add = 1)
   int32_t len_add;
   float scale;
@@ -122,7 +123,8 @@ struct GemmArgs {
   int64_t page_elems;
   int32_t num_pages;
   const int32_t* bt;
-  int32_t bt_stride;
+  int32_t bt_stride;       // table width (max_pages)
+  int32_t bt_row;          // elements between columns' rows (0: one shared row)
   const int32_t* pos;
   const float* rcos;
   const float* rsin;
@@ -275,5 +277,6 @@ hipError_t launch_pack_weight(const uint16_t* src, int rows, int cols, int kind,
 hipError_t launch_rope_table(double theta, int D, int max_pos, float* c, float* s,
                              hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_iota(int32_t* p, int n, int start, hipStream_t st);
 
 }  // namespace pkv
