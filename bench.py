@@ -228,6 +228,59 @@ def time_layer_b1(torch, pkv, synth, S, reps=10):
     return e0.elapsed_time(e1) / (reps * shape.layers), layer_bytes
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(shape, start, T):
+    """Algorithmic FLOPs of one prefill: every prompt token through every
+    layer's projections (2 per weight), causal attention (QK and PV, 2 each
+    per head dim and attended key), and the LM head for the last token."""
+    proj = 2 * (shape.layer_param_count() - 2 * shape.hidden) * T
+    keys = sum(start + t + 1 for t in range(T))
+    attn = 4 * shape.heads * shape.head_dim * keys
+    return shape.layers * (proj + attn) + 2 * shape.vocab * shape.hidden
+
+
+def time_prefill(torch, pkv, synth, S, T=512, reps=5):
+    """One prompt of T tokens of a fresh sequence (positions 0..T-1), the
+    step's model weights, captured in a HIP graph; returns (ms, flops)."""
+    shape = S.shape
+    wl = synth.decode_workload("prefill", shape, 1007, [T - 1])
+    pool_t = pkv.to_device(wl.pool)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    bts = pkv.to_device(np.ascontiguousarray(wl.block_tables[:, 0]))
+    tokens = pkv.to_device(synth.rng(1007, "prompt").integers(0, shape.vocab, size=T).astype(np.int32))
+    if T > S.max_pos:
+        raise SystemExit("prefill of %d tokens exceeds the model's %d rotary positions" % (T, S.max_pos))
+    cfg, model = S.cfg, S.model
+    ws = pkv.alloc_workspace(pkv.prefill_workspace_bytes(cfg, T, bts.shape[1]))
+    logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def run(stream):
+        pkv.prefill(cfg, model, pool, bts, 0, tokens, logits, nxt, ws, stream)
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        run(cap)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            run(cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert pkv.device_error(ws) == 0
+    return e0.elapsed_time(e1) / reps, prefill_flops(shape, 0, T)
+
+
 def cpu_baseline(S, seqs):
     import oracle
     wl = S.wl
@@ -319,6 +372,7 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     ap.add_argument("--no-layer-b1", action="store_true")
+    ap.add_argument("--prefill-tokens", type=int, default=512, help="0 skips the prefill timing")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, out_path=args.traffic_out)
@@ -398,6 +452,19 @@ def main():
                     "achieved": round(l_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(l_gbs / HBM_PEAK_GBS, 4)}
 
+    prefill = None
+    if args.prefill_tokens > 0:
+        p_ms, p_flops = time_prefill(torch, pkv, synth, S, args.prefill_tokens)
+        p_tf = p_flops / (p_ms * 1e-3) / 1e12
+        log("prefill: %d tokens in %.3f ms (%.0f tokens/s), %.2f TFLOP/s" % (
+            args.prefill_tokens, p_ms, args.prefill_tokens / (p_ms * 1e-3), p_tf))
+        prefill = {"workload": "prefill of one %d-token prompt from position 0, llama-3.2-1b-shape, "
+                               "HIP graph" % args.prefill_tokens,
+                   "tokens_per_s": round(args.prefill_tokens / (p_ms * 1e-3), 1), "ms": round(p_ms, 3),
+                   "bound": "mfma", "algorithmic_flops": int(p_flops), "achieved": round(p_tf, 2),
+                   "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": round(p_tf / MFMA_BF16_PEAK_TFLOPS, 5)}
+
     result = {
         "metric": METRIC,
         "value": round(B / (ms * 1e-3), 1),
@@ -437,6 +504,7 @@ def main():
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
         },
         "layer_b1_roofline": layer_b1,
+        "prefill": prefill,
         "cpu_baseline": None,
     }
 

@@ -58,3 +58,13 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert t["fetch_bytes_per_launch"] == round((1100.0 + 100.0) * 1024 * 0.8)
     assert t["write_bytes_per_launch"] == round(48.0 * 1024)
     assert t["attention_source_sha"] == bench.source_sha(bench.ATTN_SOURCE)
+
+
+def test_prefill_flops_counts_projections_causal_attention_and_one_head_row():
+    s = synth.tiny_shape(hidden=128, layers=3, heads=4, kv_heads=2, inter=256, vocab=1000)
+    start, T = 5, 3
+    H, D = s.hidden, s.head_dim
+    per_token = 2 * ((s.heads + 2 * s.kv_heads) * D * H + s.heads * D * H + 3 * s.inter * H)
+    keys = (start + 1) + (start + 2) + (start + 3)
+    per_layer = T * per_token + 4 * s.heads * D * keys
+    assert bench.prefill_flops(s, start, T) == s.layers * per_layer + 2 * s.vocab * H
