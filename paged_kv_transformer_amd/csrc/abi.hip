@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/pkv.h: argument validation
 // (pure host code, run before any HIP call), workspace carving and the
 // launch sequence of each entry point.  Every step of the computation runs
-// in the kernels of attention.hip, gemm.hip and misc.hip.
+// in the kernels of attention.hip, gemm.hip, prefill.hip and misc.hip.
 #include <errno.h>
 #include <math.h>
 #include <stdint.h>
@@ -388,18 +388,33 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
   return 0;
 }
 
-// Prefill workspace: the layer workspace of a batch of num_tokens columns,
-// then the prompt's positions.
-static size_t prefill_pos_offset(const pkv_config* cfg, int32_t num_tokens, int32_t max_pages) {
-  return ws_layout(num_tokens, cfg->hidden_size, cfg->num_attention_heads,
-                   cfg->num_key_value_heads, cfg->intermediate_size, cfg->vocab_size, max_pages,
-                   true)
-      .total;
+// Prefill workspace: error word, the prompt's FP32 hidden rows, the packed
+// BF16 hi/lo projection inputs (normed rows, attention output, SwiGLU
+// output), q and the LM head's per-tile maxima.
+struct PrefillLayout {
+  size_t err, x, xb, q, ob, act, amax, total;
+};
+
+static PrefillLayout prefill_layout(const pkv_config* cfg, int32_t T) {
+  const size_t H = cfg->hidden_size, I = cfg->intermediate_size;
+  const size_t QD = (size_t)cfg->num_attention_heads * kHeadDim;
+  PrefillLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  L.err = take(256);
+  L.x = take(sizeof(float) * T * H);
+  L.xb = take(2 * (size_t)packed_pair_elems(T, (int)H));
+  L.q = take(2 * (size_t)T * QD * 2);
+  L.ob = take(2 * (size_t)packed_pair_elems(T, (int)QD));
+  L.act = take(2 * (size_t)packed_pair_elems(T, (int)I));
+  L.amax = take(sizeof(unsigned long long) * plan_gemm(EPI_LOGITS, cfg->vocab_size, 1, H).tiles);
+  L.total = off;
+  return L;
 }
 
 size_t pkv_prefill_workspace_bytes(const pkv_config* cfg, int32_t num_tokens, int32_t max_pages) {
   if (check_cfg(cfg) || num_tokens < 1 || max_pages < 1) return 0;
-  return prefill_pos_offset(cfg, num_tokens, max_pages) + align256(sizeof(int32_t) * num_tokens);
+  return prefill_layout(cfg, num_tokens).total;
 }
 
 int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* pool,
@@ -413,7 +428,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   if (rc) return rc;
   if (pool->num_kv_heads != cfg->num_key_value_heads) return -EINVAL;
   if (num_tokens < 0 || max_pages < 1 || start_pos < 0) return -EINVAL;
-  if (num_tokens > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
+  if (num_tokens > 65535) return -ENOTSUP;
   if (num_tokens == 0) return 0;
   if ((int64_t)start_pos + num_tokens > (int64_t)max_pages * kPageTokens ||
       (int64_t)start_pos + num_tokens > cfg->max_position_embeddings)
@@ -424,27 +439,109 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   if (!aligned(workspace, 256)) return -EINVAL;
   for (int l = 0; l < cfg->num_hidden_layers; ++l)
     if ((rc = check_layer_weights(&w->layers[l]))) return rc;
+  const int H = cfg->hidden_size, V = cfg->vocab_size, T = num_tokens;
+  const int Hq = cfg->num_attention_heads, Hkv = cfg->num_key_value_heads;
+  const int I = cfg->intermediate_size, QD = Hq * kHeadDim;
+  // the projections address their packed BF16 hi/lo inputs through a
+  // 32-bit byte range
+  const int64_t widest = H > I ? (H > QD ? H : QD) : (I > QD ? I : QD);
+  if (2 * packed_pair_elems(T, (int)widest) > kMaxMatrixBytes) return -ENOTSUP;
   if (ws_bytes < pkv_prefill_workspace_bytes(cfg, num_tokens, max_pages)) return -ENOSPC;
 
   const hipStream_t st = (hipStream_t)stream;
-  const int H = cfg->hidden_size, V = cfg->vocab_size, T = num_tokens;
-  const WsLayout L = ws_layout(T, H, cfg->num_attention_heads, cfg->num_key_value_heads,
-                               cfg->intermediate_size, V, max_pages, true);
-  int32_t* pos = at<int32_t>(workspace, L.total);
+  const PrefillLayout L = prefill_layout(cfg, T);
   float* x = at<float>(workspace, L.x);
-  float* x_p = at<float>(workspace, L.x_p);
+  uint16_t* xb = at<uint16_t>(workspace, L.xb);
+  uint16_t* q = at<uint16_t>(workspace, L.q);
+  uint16_t* ob = at<uint16_t>(workspace, L.ob);
+  uint16_t* act = at<uint16_t>(workspace, L.act);
   uint32_t* err = at<uint32_t>(workspace, L.err);
+  const float eps = cfg->rms_norm_eps;
 
-  // the prompt is a batch of T queries of one sequence: token t at position
-  // start_pos + t, all sharing the sequence's table row (row stride 0), so
-  // that each query attends causally to positions 0 .. start_pos + t
-  if ((rc = io(launch_iota(pos, T, start_pos, st)))) return rc;
-  if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, x_p, T, err, st)))) return rc;
+  if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, nullptr, T, err, st)))) return rc;
   for (int l = 0; l < cfg->num_hidden_layers; ++l) {
-    rc = run_layer(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool,
-                   block_tables + (size_t)l * max_pages, max_pages, 0, pos, T, x, x_p, workspace,
-                   L, st);
-    if (rc) return rc;
+    const pkv_layer_weights* lw = &w->layers[l];
+    const int32_t* bt = block_tables + (size_t)l * max_pages;
+    PgemmArgs base{};
+    base.T = T;
+    base.err = err;
+
+    // RMSNorm, QKV + RoPE at start_pos + t, K/V into the prompt's pages
+    if ((rc = io(launch_prefill_norm(x, lw->attn_norm, H, T, eps, xb, st)))) return rc;
+    {
+      PgemmArgs a = base;
+      a.W = lw->w_qkv;
+      a.w_groups = (Hq + 2 * Hkv) * 4;
+      a.X = xb;
+      a.N = (Hq + 2 * Hkv) * kHeadDim;
+      a.K = H;
+      a.q_split = q;
+      a.pool = (uint16_t*)pool->base;
+      a.page_elems = pool->page_bytes / 2;
+      a.num_pages = pool->num_pages;
+      a.bt = bt;
+      a.start_pos = start_pos;
+      a.rcos = w->rope_cos;
+      a.rsin = w->rope_sin;
+      a.Hq = Hq;
+      a.Hkv = Hkv;
+      if ((rc = io(launch_prefill_gemm(EPI_QKV, a, st)))) return rc;
+    }
+    // causal attention over positions 0 .. start_pos + t
+    {
+      PattnArgs a{};
+      a.q = q;
+      a.pool = (const uint16_t*)pool->base;
+      a.page_elems = pool->page_bytes / 2;
+      a.num_pages = pool->num_pages;
+      a.bt = bt;
+      a.start_pos = start_pos;
+      a.T = T;
+      a.scale = 1.0f / sqrtf((float)kHeadDim);
+      a.out = ob;
+      a.err = err;
+      a.Hq = Hq;
+      a.Hkv = Hkv;
+      a.G = Hq / Hkv;
+      if ((rc = io(launch_prefill_attention(a, st)))) return rc;
+    }
+    // x += W_o o
+    {
+      PgemmArgs a = base;
+      a.W = lw->w_o;
+      a.w_groups = H / 16;
+      a.X = ob;
+      a.N = H;
+      a.K = QD;
+      a.out = x;
+      a.resid = x;
+      if ((rc = io(launch_prefill_gemm(EPI_RESID, a, st)))) return rc;
+    }
+    // RMSNorm, gate/up, SwiGLU
+    if ((rc = io(launch_prefill_norm(x, lw->mlp_norm, H, T, eps, xb, st)))) return rc;
+    {
+      PgemmArgs a = base;
+      a.W = lw->w_gate_up;
+      a.w_groups = I / 8;
+      a.X = xb;
+      a.N = 2 * I;
+      a.K = H;
+      a.act = act;
+      a.I = I;
+      if ((rc = io(launch_prefill_gemm(EPI_SWIGLU, a, st)))) return rc;
+    }
+    // x += W_down a
+    {
+      PgemmArgs a = base;
+      a.W = lw->w_down;
+      a.w_groups = H / 16;
+      a.X = act;
+      a.N = H;
+      a.K = I;
+      a.out = x;
+      a.resid = x;
+      if ((rc = io(launch_prefill_gemm(EPI_RESID, a, st)))) return rc;
+    }
   }
   // final norm, LM head and argmax of the last prompt token only
   GemmArgs a{};
@@ -454,9 +551,9 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   a.N = V;
   a.K = H;
   a.B = 1;
-  a.eps = cfg->rms_norm_eps;
+  a.eps = eps;
   a.err = err;
-  a.amax_part = at<unsigned long long>(workspace, L.amax_part);
+  a.amax_part = at<unsigned long long>(workspace, L.amax);
   a.X = x + (size_t)(T - 1) * H;
   a.x_plain = 1;
   a.logits = logits;

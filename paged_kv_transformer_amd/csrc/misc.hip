@@ -31,9 +31,9 @@ __global__ void kv_append_kernel(uint16_t* pool, int64_t page_elems, int32_t num
 
 // x[b] = E[token[b]] widened from BF16 to FP32 (the engine's embedding
 // gather), read from the packed embedding (which is also the tied LM head)
-// and written both plain and packed (the first projection's input).  One
-// thread per 8 consecutive elements (H is a multiple of 64): one 16-byte
-// load, no loop.
+// and written plain and, if xp is given, packed (the first projection's
+// input).  One thread per 8 consecutive elements (H is a multiple of 64):
+// one 16-byte load, no loop.
 __global__ void embed_kernel(const uint16_t* E, int V, int H, const int32_t* tok, float* x,
                              float* xp, uint32_t* err) {
   const int b = blockIdx.y;
@@ -41,7 +41,6 @@ __global__ void embed_kernel(const uint16_t* E, int V, int H, const int32_t* tok
   if (k >= H) return;
   const int t = tok[b];
   float4* xr = (float4*)(x + (size_t)b * H + k);
-  float4* xq = (float4*)(xp + packed_act_index(b, k, H));
   float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
   if ((unsigned)t >= (unsigned)V) {
     if (k == 0) set_error(err, ERR_TOKEN);
@@ -54,8 +53,11 @@ __global__ void embed_kernel(const uint16_t* E, int V, int H, const int32_t* tok
   }
   xr[0] = lo;
   xr[1] = hi;
-  xq[0] = lo;
-  xq[1] = hi;
+  if (xp) {
+    float4* xq = (float4*)(xp + packed_act_index(b, k, H));
+    xq[0] = lo;
+    xq[1] = hi;
+  }
 }
 
 // Packs a row-major [rows][cols] BF16 matrix (cols a multiple of 32): one
@@ -85,11 +87,6 @@ __global__ void rope_table_kernel(double theta, int D, int max_pos, float* c, fl
   const double ang = (double)p * inv_freq;
   c[idx] = (float)cos(ang);
   s[idx] = (float)sin(ang);
-}
-
-__global__ void iota_kernel(int32_t* p, int n, int start) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = start + i;
 }
 
 __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
@@ -130,11 +127,6 @@ hipError_t launch_rope_table(double theta, int D, int max_pos, float* c, float* 
   const int64_t n = (int64_t)max_pos * (D / 2);
   const int blocks = (int)((n + 255) / 256);
   rope_table_kernel<<<blocks, 256, 0, st>>>(theta, D, max_pos, c, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_iota(int32_t* p, int n, int start, hipStream_t st) {
-  iota_kernel<<<(n + 255) / 256, 256, 0, st>>>(p, n, start);
   return hipGetLastError();
 }
 

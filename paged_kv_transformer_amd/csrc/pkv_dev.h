@@ -139,6 +139,79 @@ struct GemmArgs {
   int32_t* next_tok;             // [B]
 };
 
+// Prefill of one sequence's prompt of T tokens.  Activations feeding a
+// projection are FP32 values stored as two BF16 halves x = hi + lo (~16
+// significant bits, as the decode projections keep), packed like the
+// weights with tokens in place of rows: token group c (16 tokens), step s,
+// half h: a 1 KiB block whose 16-byte chunk l = 16 i + m holds
+// half h of X[16 c + m][32 s + 8 i .. + 8]; a step's hi block is followed by
+// its lo block.  Both operands of the matrix-core product are thus
+// contiguous 1 KiB blocks.  Tokens T .. 16 ceil(T / 16) - 1 are padding.
+__host__ __device__ inline int64_t packed_pair_index(int t, int k, int K, int h) {
+  const int S = K >> 5;
+  return (((((int64_t)(t >> 4) * S + (k >> 5)) * 2 + h) * 64 + ((k & 31) >> 3) * 16 + (t & 15)) << 3) +
+         (k & 7);
+}
+
+inline int64_t packed_pair_elems(int T, int K) { return (int64_t)((T + 15) / 16) * 16 * K * 2; }
+
+struct PgemmArgs {
+  const uint16_t* W;       // packed BF16 weights, w_groups 16-row groups x K
+  int32_t w_groups;
+  const uint16_t* X;       // packed BF16 hi/lo activation pairs
+  int32_t N, K, T;
+  uint32_t* err;
+  // EPI_RESID: out[t][n] = resid[t][n] + y, plain [T][N] (out may be resid)
+  float* out;
+  const float* resid;
+  // EPI_QKV: q as BF16 hi, lo halves [T][Hq][2][D]; k, v into the pages of
+  // positions start_pos + t through the sequence's table bt
+  uint16_t* q_split;
+  uint16_t* pool;
+  int64_t page_elems;
+  int32_t num_pages;
+  const int32_t* bt;
+  int32_t start_pos;
+  const float* rcos;
+  const float* rsin;
+  int32_t Hq, Hkv;
+  // EPI_SWIGLU: act = silu(gate) * up, packed BF16 hi/lo pairs
+  uint16_t* act;
+  int32_t I;
+};
+
+struct PattnArgs {
+  const uint16_t* q;       // [T][Hq][2][D] BF16 hi, lo
+  const uint16_t* pool;
+  int64_t page_elems;
+  int32_t num_pages;
+  const int32_t* bt;       // the sequence's table for this layer
+  int32_t start_pos, T;
+  float scale;
+  uint16_t* out;           // packed BF16 hi/lo pairs (the output projection's input)
+  uint32_t* err;
+  int32_t Hq, Hkv, G;
+};
+
+// A prefill GEMM tile: 2 x 2 waves, each 16 rg rows by 16 cg tokens.
+struct PgemmPlan {
+  int rg, cg, tiles;
+};
+
+inline PgemmPlan plan_prefill_gemm(int w_groups, int T) {
+  // the largest wave tile that still gives about one workgroup per compute
+  // unit; smaller ones only where the projection is too small for that
+  static const int cand[3][2] = {{4, 4}, {2, 4}, {2, 2}};
+  PgemmPlan p{};
+  for (const auto& c : cand) {
+    p.rg = c[0];
+    p.cg = c[1];
+    p.tiles = ((w_groups + 2 * p.rg - 1) / (2 * p.rg)) * ((T + 32 * p.cg - 1) / (32 * p.cg));
+    if (p.tiles >= 240) break;
+  }
+  return p;
+}
+
 // ------------------------------------------------------------ plans ---
 
 // Attention: kAttnWaves waves per workgroup, kAttnPW pages per wave per
@@ -277,6 +350,11 @@ hipError_t launch_pack_weight(const uint16_t* src, int rows, int cols, int kind,
 hipError_t launch_rope_table(double theta, int D, int max_pos, float* c, float* s,
                              hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
-hipError_t launch_iota(int32_t* p, int n, int start, hipStream_t st);
+// prefill: RMSNorm (xw, or none if null) of plain FP32 rows into packed
+// BF16 hi/lo pairs
+hipError_t launch_prefill_norm(const float* x, const uint16_t* xw, int K, int T, float eps,
+                               uint16_t* out, hipStream_t st);
+hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, hipStream_t st);
+hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st);
 
 }  // namespace pkv

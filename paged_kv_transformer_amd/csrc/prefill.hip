@@ -1,0 +1,563 @@
+// Dense causal prefill of one sequence's prompt, gfx950.
+//
+// Prefill pushes all T prompt tokens of a sequence through each layer
+// together ("Inference from Scratch": prefill is the step before decode and
+// fills the prompt's pages).  Its projections are real matrix products,
+// T tokens by N rows by K, so they run as tiled matrix-core GEMMs that
+// reuse every weight block across a tile of tokens, rather than as the
+// decode step's weight-streaming kernel.  Activations entering a projection
+// are FP32 values carried as two BF16 halves (hi + lo, ~16 significant bits:
+// with plain BF16 activations the error compounds over the layers of a
+// 16-layer model to several percent of the logits' RMS), produced packed in
+// the same 1 KiB block order as the weights, so a workgroup moves both
+// operands as whole blocks and every matrix-core operand is one 16-byte read
+// per lane.
+//
+//   prefill_norm_kernel       RMSNorm of FP32 rows -> packed BF16 hi/lo
+//   prefill_gemm_kernel       128 x 128 (or smaller) output tiles; epilogues
+//                             as the decode projections: RoPE + q split +
+//                             K/V page writes, residual add, SwiGLU
+//   prefill_attention_kernel  causal paged attention: each wave takes up to
+//                             16 (token, head) query columns of one kv head
+//                             and walks the pages 0 .. its last position
+#include "pkv_dev.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma_k32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
+}
+
+// ------------------------------------------------------------- norm ---
+// Eight FP32 values as BF16 hi halves and the BF16 rounding of what remains.
+__device__ __forceinline__ void split8(const float* v, uint4& hi, uint4& lo) {
+  uint16_t h[8];
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = to_bf16_bits(v[e]);
+    r[e] = v[e] - bf16_lo(h[e]);
+  }
+  hi = make_uint4((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16),
+                  (uint32_t)h[4] | ((uint32_t)h[5] << 16), (uint32_t)h[6] | ((uint32_t)h[7] << 16));
+  lo = make_uint4(pack2(r[0], r[1]), pack2(r[2], r[3]), pack2(r[4], r[5]), pack2(r[6], r[7]));
+}
+
+// One workgroup per (padded) token row: out = x * rs * xw as hi/lo pairs,
+// rs = 1 / sqrt(mean x^2 + eps); padding rows are zeros.
+__global__ __launch_bounds__(256) void prefill_norm_kernel(const float* x, const uint16_t* xw,
+                                                           int K, int T, float eps, uint16_t* out) {
+  __shared__ float part[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (t >= T) {
+    for (int k = 8 * tid; k < K; k += 8 * 256) {
+      *(uint4*)(out + packed_pair_index(t, k, K, 0)) = make_uint4(0u, 0u, 0u, 0u);
+      *(uint4*)(out + packed_pair_index(t, k, K, 1)) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
+  const float* row = x + (size_t)t * K;
+  float ss = 0.f;
+  for (int k = 8 * tid; k < K; k += 8 * 256) {
+    const float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
+          b.w * b.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float rs = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)K + eps);
+  for (int k = 8 * tid; k < K; k += 8 * 256) {
+    const float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    if (xw) {
+      const uint4 w = *(const uint4*)(xw + k);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] *= bf16_lo(ww[e]);
+        v[2 * e + 1] *= bf16_hi(ww[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= rs;
+    uint4 hi, lo;
+    split8(v, hi, lo);
+    *(uint4*)(out + packed_pair_index(t, k, K, 0)) = hi;
+    *(uint4*)(out + packed_pair_index(t, k, K, 1)) = lo;
+  }
+}
+
+// ------------------------------------------------------------- GEMM ---
+// One global -> LDS copy of a 1 KiB block by a wave (buffer_load_dwordx4 ...
+// lds: lane l's 16 bytes land at LDS byte address lds + 16 l, the block's
+// own order).  M0 carries the wave's LDS address; the statement sets it
+// itself (nothing else in these kernels uses M0).  The load is counted by
+// vmcnt like any
+// buffer load and is waited for explicitly (wait_stages): the compiler does
+// not see it, so it adds no conservative wait of its own before LDS reads.
+// An offset past the descriptor's range reads zeros.
+__device__ __forceinline__ void lds_copy16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
+// Raw buffer descriptor words over `bytes` bytes at p (32-bit data format).
+__device__ __forceinline__ i32x4 rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  return (i32x4){(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `pend` stages of LPW copies each are still in flight.
+template <int LPW, int K>
+__device__ __forceinline__ void wait_stages(int pend) {
+  if constexpr (K == 0) {
+    wait_vm<0>();
+  } else {
+    if (pend >= K)
+      wait_vm<K * LPW>();
+    else
+      wait_stages<LPW, K - 1>(pend);
+  }
+}
+
+// y[t][n] = sum_k W[n][k] X[t][k].  A workgroup of 4 waves (2 x 2) owns
+// 32 RG rows by 32 CG tokens; each wave a 16 RG x 16 CG sub-tile held as
+// RG x CG accumulator tiles of v_mfma_f32_16x16x32_bf16 (W block as the A
+// operand, the X hi and lo blocks as two B operands).  A stage is one
+// 32-wide K step: 2 RG W blocks and 2 CG (hi, lo) X block pairs, copied
+// straight from global memory into a ring of NSTG stages in LDS, so that
+// NSTG - 1 stages of loads are in flight while a stage is multiplied (the
+// latency of a load under load is far longer than one stage's products).
+// Workgroups are mapped to tiles XCD by XCD, so the token tiles of one row
+// tile run on one XCD and share its L2 copy of the weights.  Out-of-range
+// row and token groups read zeros and are never stored.
+template <int RG, int CG>
+struct PgemmShape {
+  static constexpr int AR = 2 * RG;        // row groups per tile
+  static constexpr int BC = 2 * CG;        // token groups per tile
+  static constexpr int NA = AR;            // W blocks per stage
+  static constexpr int NB = AR + 2 * BC;   // blocks per stage
+  static constexpr int LPW = NB / 4;       // copies per wave per stage
+  static constexpr int NSTG = NB * 6 <= 144 ? 6 : 144 / NB;  // ring of at most 144 KiB
+};
+
+template <int EPI, int RG, int CG>
+__global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
+  using SH = PgemmShape<RG, CG>;
+  constexpr int AR = SH::AR, BC = SH::BC, NA = SH::NA, NB = SH::NB, LPW = SH::LPW;
+  constexpr int NSTG = SH::NSTG;
+  static_assert(NA % 4 == 0 && NB % 4 == 0, "stage blocks split evenly over the waves");
+  static_assert((NSTG - 2) * LPW <= 63, "vmcnt range");
+  __shared__ u32x4 ring[NSTG][NB][64];
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w & 1, wc = w >> 1;
+  const int nrt = (a.w_groups + AR - 1) / AR;
+  const int ntt = (a.T + 16 * BC - 1) / (16 * BC);
+  const int ntiles = nrt * ntt;
+  // workgroup id -> tile: ids i, i + 8, i + 16 .. (one XCD) take consecutive tiles
+  const int id = blockIdx.x;
+  const int per = ntiles >> 3, rem = ntiles & 7, xcd = id & 7, slot0 = id >> 3;
+  const int tile = xcd < rem ? xcd * (per + 1) + slot0 : rem * (per + 1) + (xcd - rem) * per + slot0;
+  const int rt = tile / ntt, tt = tile - rt * ntt;
+  const int S = a.K >> 5;
+  const int g0 = rt * AR, c0 = tt * BC;
+
+  const i32x4 wres = rsrc_words(a.W, (uint32_t)a.w_groups * (uint32_t)S * 1024u);
+  const i32x4 xres = rsrc_words(a.X, (uint32_t)((a.T + 15) / 16) * (uint32_t)S * 2048u);
+  // wave w copies blocks j = 4 i + w of each stage: W row group j for
+  // i < NA / 4, then X block j - NA = 2 c + h (token group c, half h)
+  uint32_t boff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int j = 4 * i + w;
+    if (i < NA / 4) {
+      boff[i] = (uint32_t)(g0 + j) * S * 1024u + l * 16;
+    } else {
+      const int jb = j - NA;
+      boff[i] = (uint32_t)(c0 + (jb >> 1)) * S * 2048u + (jb & 1) * 1024u + l * 16;
+    }
+  }
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[0][0][0];
+  auto issue = [&](int st) {
+    const uint32_t base = ring0 + (uint32_t)((st % NSTG) * NB) * 1024u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const bool isw = i < NA / 4;
+      lds_copy16(base + (uint32_t)(4 * i + w) * 1024u, boff[i] + (uint32_t)st * (isw ? 1024u : 2048u),
+                 isw ? wres : xres);
+    }
+  };
+
+  f32x4 acc[RG][CG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int c = 0; c < CG; ++c) acc[r][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int st = 0; st < NSTG - 1 && st < S; ++st) issue(st);
+  for (int st = 0; st < S; ++st) {
+    // this wave's copies of stage st have landed, then everyone's; every
+    // wave is also done with stage st - 1, whose slot is refilled next
+    wait_stages<LPW, NSTG - 2>(min(NSTG - 2, S - 1 - st));
+    __syncthreads();
+    if (st + NSTG - 1 < S) issue(st + NSTG - 1);
+    const int sl = st % NSTG;
+    u32x4 af[RG], bh[CG], bl[CG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) af[r] = ring[sl][wr * RG + r][l];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      bh[c] = ring[sl][NA + 2 * (wc * CG + c)][l];
+      bl[c] = ring[sl][NA + 2 * (wc * CG + c) + 1][l];
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        acc[r][c] = mfma_k32(af[r], bh[c], acc[r][c]);
+        acc[r][c] = mfma_k32(af[r], bl[c], acc[r][c]);
+      }
+  }
+
+  // ---- epilogues: lane holds rows 16 G + 4 grp + e (e = 0..3) of token
+  // 16 tg + col for each accumulator tile
+  const int grp = l >> 4, col = l & 15;
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const int G = g0 + wr * RG + r;
+      const int t = 16 * (c0 + wc * CG + c) + col;
+      const f32x4 v = acc[r][c];
+      if (EPI == EPI_RESID) {
+        if (G < a.w_groups && t < a.T) {
+          const size_t o = (size_t)t * a.N + 16 * G + 4 * grp;
+          const float4 rv = *(const float4*)(a.resid + o);
+          *(float4*)(a.out + o) = make_float4(rv.x + v[0], rv.y + v[1], rv.z + v[2], rv.w + v[3]);
+        }
+      } else if (EPI == EPI_SWIGLU) {
+        // rows 0..7 of a group are gate rows, 8..15 the matching up rows:
+        // lane l holds gate rows, lane l + 32 the up rows of the same token
+        f32x4 up;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) up[e] = __shfl_xor(v[e], 32);
+        const int i0 = 8 * G + 4 * grp;
+        if (l < 32 && t < a.T && i0 < a.I) {
+          uint16_t h[4];
+          float lo[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float y = v[e] / (1.0f + expf(-v[e])) * up[e];
+            h[e] = to_bf16_bits(y);
+            lo[e] = y - bf16_lo(h[e]);
+          }
+          *(u32x2*)(a.act + packed_pair_index(t, i0, a.I, 0)) =
+              (u32x2){(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+          *(u32x2*)(a.act + packed_pair_index(t, i0, a.I, 1)) =
+              (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+        }
+      } else if (EPI == EPI_QKV) {
+        // group G: head G / 4, RoPE pairs j = 8 (G % 4) + m, rows j (lanes
+        // 0..31) and j + 32 (lanes 32..63, the same j in lane l - 32)
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = __shfl_xor(v[e], 32);
+        const int hd = G >> 2;
+        if (hd < a.Hq + 2 * a.Hkv && t < a.T) {
+          const bool first = l < 32;
+          const int jb = 8 * (G & 3) + 4 * (grp & 1);
+          const int jj = first ? jb : jb + 32;
+          const int p = a.start_pos + t;
+          const bool is_q = hd < a.Hq, is_k = !is_q && hd < a.Hq + a.Hkv;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = v[e];
+            if (is_q || is_k) {
+              const float x0 = first ? v[e] : pv[e], x1 = first ? pv[e] : v[e];
+              const float cs = a.rcos[(size_t)p * 32 + jb + e];
+              const float sn = a.rsin[(size_t)p * 32 + jb + e];
+              y[e] = first ? __fsub_rn(__fmul_rn(x0, cs), __fmul_rn(x1, sn))
+                           : __fadd_rn(__fmul_rn(x0, sn), __fmul_rn(x1, cs));
+            }
+          }
+          if (is_q) {
+            uint16_t* qo = a.q_split + ((size_t)t * a.Hq + hd) * 2 * kHeadDim + jj;
+            uint16_t h[4];
+            float lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              h[e] = to_bf16_bits(y[e]);
+              lo[e] = y[e] - bf16_lo(h[e]);
+            }
+            *(u32x2*)qo = (u32x2){(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                  (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+            *(u32x2*)(qo + kHeadDim) = (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+          } else {
+            const int page = a.bt[p / kPageTokens];
+            if ((unsigned)page >= (unsigned)a.num_pages) {
+              set_error(a.err, ERR_PAGE);
+            } else {
+              uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
+              const int slot = p % kPageTokens;
+              if (is_k) {
+                uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * kHeadDim + jj;
+                *(u32x2*)kp = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
+              } else {
+                uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * kHeadDim +
+                               ((int64_t)(hd - a.Hq - a.Hkv) * kHeadDim + jj) * kPageTokens + slot;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vp[e * kPageTokens] = to_bf16_bits(y[e]);
+              }
+            }
+          }
+        }
+      }
+    }
+}
+
+// -------------------------------------------------------- attention ---
+// Causal paged attention of the prompt.  A wave's 16 query columns are
+// (token, head) pairs: tpw = 16 / G consecutive tokens times the G heads of
+// one kv head, column = G * (token - t0) + head.  For each page the wave
+// forms S^T[key][column] = K q^T (v_mfma_f32_16x16x32_bf16, q as BF16 hi
+// and lo halves) and then O[column][d] += P[column][key] V[key][d]
+// (v_mfma_f32_16x16x16_bf16, P as hi and lo halves); the score tile's
+// register layout is the P operand's, and V is stored [d][slot] in the
+// page.  Key position kp is visible to a column whose position is at least
+// kp.  The softmax is online in base 2 (scale * log2 e applied in the
+// exponent), rescaling O whenever a column's maximum grows; two pages per
+// rescale, the next two pages' loads in flight meanwhile.  Workgroups with
+// the latest tokens (the most pages) are launched first.
+constexpr int kPW = 2;
+
+__global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs a) {
+  const int kvh = blockIdx.y;
+  const int blk = gridDim.x - 1 - blockIdx.x;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = l & 15, grp = l >> 4;
+  const int G = a.G, tpw = 16 / G;
+  const int t0 = (blk * 4 + w) * tpw;
+  if (t0 >= a.T) return;
+  const int tend = min(t0 + tpw, a.T);
+  const int pmax = a.start_pos + tend - 1;  // the wave's last position
+  const int npages = pmax / kPageTokens + 1;
+  const int pmin = a.start_pos + t0;        // its first: keys up to here need no mask
+
+  // this lane's query column
+  const int tk = col / G, gh = col - tk * G;
+  const bool cval = col < tpw * G && t0 + tk < a.T;
+  const int lim = cval ? a.start_pos + t0 + tk : -1;
+  const float c2 = fabsf(a.scale) * kLog2e;
+  const unsigned sgn = a.scale < 0.f ? 0x80008000u : 0u;
+  u32x4 qh[2], ql[2];
+  {
+    const uint16_t* qp =
+        a.q + ((size_t)(cval ? t0 + tk : 0) * a.Hq + (size_t)kvh * G + gh) * 2 * kHeadDim + 8 * grp;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 hv = *(const u32x4*)(qp + 32 * h), lv = *(const u32x4*)(qp + kHeadDim + 32 * h);
+      qh[h] = cval ? hv ^ sgn : z;
+      ql[h] = cval ? lv ^ sgn : z;
+    }
+  }
+
+  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * kHeadDim;
+  struct Chunk {
+    u32x4 k[kPW][2];
+    u32x2 v[kPW][4];
+  };
+  bool bad = false;
+  auto load = [&](Chunk& C, int lp0) {
+#pragma unroll
+    for (int i = 0; i < kPW; ++i) {
+      int page = a.bt[min(lp0 + i, npages - 1)];
+      const bool ok = (unsigned)page < (unsigned)a.num_pages;
+      bad |= !ok;
+      page = ok ? page : 0;
+      const uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
+      const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * kHeadDim + 8 * grp;
+      C.k[i][0] = *(const u32x4*)kp;
+      C.k[i][1] = *(const u32x4*)(kp + 32);
+      const uint16_t* vp = pg + vblk + ((int64_t)kvh * kHeadDim + col) * kPageTokens + 4 * grp;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) C.v[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
+    }
+  };
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](const Chunk& C, int lp0) {
+    f32x4 s[kPW];
+    bool full[kPW];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPW; ++i) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_k32(C.k[i][0], qh[0], acc);
+      acc = mfma_k32(C.k[i][0], ql[0], acc);
+      acc = mfma_k32(C.k[i][1], qh[1], acc);
+      acc = mfma_k32(C.k[i][1], ql[1], acc);
+      const int kp0 = (lp0 + i) * kPageTokens;
+      full[i] = kp0 + kPageTokens - 1 <= pmin;  // uniform
+      if (!full[i]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = kp0 + 4 * grp + r <= lim ? acc[r] : -INFINITY;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[r]);
+      s[i] = acc;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float msub = mn == -INFINITY ? 0.f : mn;
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+    m = mn;
+    float ps = 0.f;
+    s16x4 ph[kPW], pl[kPW];
+#pragma unroll
+    for (int i = 0; i < kPW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = (s[i][r] - msub) * c2;
+        if (!full[i]) x = s[i][r] == -INFINITY ? -INFINITY : x;
+        const float p = __builtin_amdgcn_exp2f(x);
+        ps += p;
+        const __bf16 hi = (__bf16)p;
+        ph[i][r] = __builtin_bit_cast(short, hi);
+        pl[i][r] = __builtin_bit_cast(short, (__bf16)(p - (float)hi));
+      }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    lsum = lsum * alpha + ps;
+    // O row 4 grp + r belongs to column 4 grp + r: its factor lives in lane 4 grp + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c][r] *= ar;
+    }
+#pragma unroll
+    for (int i = 0; i < kPW; ++i) {
+      // slots past the wave's last position may hold anything: zero them
+      const int nv = pmax - ((lp0 + i) * kPageTokens + 4 * grp) + 1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x2 vv = C.v[i][c];
+        if (nv < 4) {
+          vv.x = nv >= 2 ? vv.x : (nv == 1 ? (vv.x & 0xffffu) : 0u);
+          vv.y = nv == 3 ? (vv.y & 0xffffu) : 0u;
+        }
+        const s16x4 vb = __builtin_bit_cast(s16x4, vv);
+        o[c] = mfma_k16(ph[i], vb, o[c]);
+        o[c] = mfma_k16(pl[i], vb, o[c]);
+      }
+    }
+  };
+
+  {
+    Chunk A, B;
+    load(A, 0);
+    for (int lp = 0;; lp += 2 * kPW) {
+      if (lp + kPW < npages) load(B, lp + kPW);
+      step(A, lp);
+      if (lp + kPW >= npages) break;
+      if (lp + 2 * kPW < npages) load(A, lp + 2 * kPW);
+      step(B, lp + kPW);
+      if (lp + 2 * kPW >= npages) break;
+    }
+  }
+  if (bad && l == 0) set_error(a.err, ERR_PAGE);
+
+  // ---- O / l, stored as BF16 hi/lo pairs into the output projection's
+  // packed input
+  const int QD = a.Hq * kHeadDim;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * grp + r;
+    const float lr = __shfl(lsum, g);
+    const int t = t0 + g / G, h = kvh * G + g % G;
+    if (g < tpw * G && t < a.T) {
+      const float inv = 1.0f / lr;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float y = o[c][r] * inv;
+        const uint16_t hb = to_bf16_bits(y);
+        const int k = h * kHeadDim + col + 16 * c;
+        a.out[packed_pair_index(t, k, QD, 0)] = hb;
+        a.out[packed_pair_index(t, k, QD, 1)] = to_bf16_bits(y - bf16_lo(hb));
+      }
+    }
+  }
+}
+
+template <int EPI>
+hipError_t launch_pg(const PgemmArgs& a, hipStream_t st) {
+  const PgemmPlan p = plan_prefill_gemm(a.w_groups, a.T);
+  if (p.rg == 4 && p.cg == 4)
+    prefill_gemm_kernel<EPI, 4, 4><<<p.tiles, 256, 0, st>>>(a);
+  else if (p.rg == 2 && p.cg == 4)
+    prefill_gemm_kernel<EPI, 2, 4><<<p.tiles, 256, 0, st>>>(a);
+  else
+    prefill_gemm_kernel<EPI, 2, 2><<<p.tiles, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_norm(const float* x, const uint16_t* xw, int K, int T, float eps,
+                               uint16_t* out, hipStream_t st) {
+  prefill_norm_kernel<<<(T + 15) / 16 * 16, 256, 0, st>>>(x, xw, K, T, eps, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, hipStream_t st) {
+  if (a.K % 32 != 0 || a.T < 1) return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_QKV: return launch_pg<EPI_QKV>(a, st);
+    case EPI_RESID: return launch_pg<EPI_RESID>(a, st);
+    case EPI_SWIGLU: return launch_pg<EPI_SWIGLU>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st) {
+  const int tpw = 16 / a.G;
+  const dim3 grid((a.T + 4 * tpw - 1) / (4 * tpw), a.Hkv);
+  prefill_attention_kernel<<<grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

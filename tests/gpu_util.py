@@ -69,20 +69,33 @@ def expected_pool_after(pool_np, geo, bt, positions, k_new, v_new, seqs=None):
 APPEND_REL = 1e-3
 
 
-def check_pool_after(got, want, base):
+def appended_mask(pool_np, geo, rows, positions):
+    """Pool elements the appends of `positions` (through table rows `rows`)
+    write, found by the oracle's own append of marker values on a zero pool."""
+    z = np.zeros(pool_np.shape, np.uint16)
+    one = np.full(geo.kv_heads * geo.head_dim, 0x3F80, np.uint16)
+    for row, p in zip(rows, positions):
+        oracle.pool_append(z, geo, row, int(p), one, one)
+    return z != 0
+
+
+def check_pool_after(got, want, base, rel=APPEND_REL, touched=None):
     """Bytes the step did not append must be untouched.  An appended BF16
     value is the rounding of an FP32 contraction whose last bits differ
     between the two paths (summation order, the two-half BF16 split of the
     activations), so it must lie within one BF16 ulp of the oracle's value or
-    within APPEND_REL * RMS(appended values) of it: near zero an ulp is far
-    smaller than the contraction's absolute error."""
-    touched = want != base
+    within rel * RMS(appended values) of it: near zero an ulp is far smaller
+    than the contraction's absolute error.  rel is APPEND_REL for the decode
+    step, whose activations keep ~16 bits.  touched: the appended elements
+    (default: where the oracle's pool differs from the base)."""
+    if touched is None:
+        touched = want != base
     assert np.array_equal(got[~touched], base[~touched]), "pool bytes outside the appended slots changed"
     g = oracle.bf16_to_f32(got[touched]).astype(np.float64)
     w = oracle.bf16_to_f32(want[touched]).astype(np.float64)
     ulp = np.abs(w) * 2.0 ** -7 + 1e-38
     rms = float(np.sqrt(np.mean(w * w))) if w.size else 0.0
-    bad = np.abs(g - w) > np.maximum(ulp, APPEND_REL * rms)
+    bad = np.abs(g - w) > np.maximum(ulp, rel * rms)
     assert not bad.any(), "appended K/V: %d values off by up to %.3g (RMS %.3g)" % (
         int(bad.sum()), float(np.abs(g - w).max()), rms)
     return float(np.abs(g - w).max(initial=0.0)), rms
