@@ -229,22 +229,25 @@ int decode_step(const pkv_config *cfg, const pkv_model_weights *w,
  * ("Inference from Scratch": prefill fills the prompt's pages, attention is
  * causal; one prompt at a time).  token_ids[t] is at position
  * start_pos + t; positions 0 .. start_pos-1 must already be in the pool.
- * Every layer projects all num_tokens tokens together, appends their BF16
- * K and V to the sequence's pages, and lets token t attend to positions
- * 0 .. start_pos + t.  Afterwards the final RMSNorm and the tied LM head
- * give the last token's FP32 logits and next_token[0] = their argmax.  The
- * arithmetic of every token is that of a decode step of this sequence at
- * its position, so the pages it writes equal those num_tokens successive
- * decode_step calls would write.
+ * Every layer projects all num_tokens tokens together (tiled matrix-core
+ * GEMMs over the prompt), appends their BF16 K and V to the sequence's
+ * pages exactly where kv_append would put them, and lets token t attend to
+ * positions 0 .. start_pos + t.  Afterwards the final RMSNorm and the tied
+ * LM head give the last token's FP32 logits and next_token[0] = their
+ * argmax.  The result is that of num_tokens successive decode steps of this
+ * sequence up to FP32 summation order (activations keep ~16 significant
+ * bits, as in decode_step).
  *   block_tables [num_layers][max_pages]: this sequence's table per layer,
  *   mapping every page up to position start_pos + num_tokens - 1.
  *   token_ids [num_tokens] (device), logits [vocab_size] FP32 or NULL,
  *   next_token [1] int32.  workspace: at least
  *   pkv_prefill_workspace_bytes(cfg, num_tokens, max_pages) bytes.
+ * The RoPE tables must cover start_pos + num_tokens positions.
  * num_tokens == 0 is a no-op.  Errors: -EINVAL (NULL, negative sizes,
- * start_pos + num_tokens past the table or the RoPE table), -ENOTSUP
- * (num_tokens > 65535, unsupported sizes as decoder_layer_decode),
- * -ENOSPC (workspace), -EIO; device errors as decode_step.
+ * start_pos + num_tokens past the table or max_position_embeddings),
+ * -ENOTSUP (num_tokens > 65535, a prompt whose packed activations exceed
+ * 2 GiB, unsupported sizes as decoder_layer_decode), -ENOSPC (workspace),
+ * -EIO; device errors (ERR_PAGE, ERR_TOKEN) as decode_step.
  */
 int prefill(const pkv_config *cfg, const pkv_model_weights *w,
 	    const pkv_pool *pool, const int32_t *block_tables,
