@@ -392,8 +392,16 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
 // BF16 hi/lo projection inputs (normed rows, attention output, SwiGLU
 // output), q and the LM head's per-tile maxima.
 struct PrefillLayout {
-  size_t err, x, xb, q, ob, act, amax, total;
+  size_t err, x, xb, q, ob, act, part, amax, total;
 };
+
+// The two residual projections of a prefill layer (output, down).
+static PgemmPlan prefill_o_plan(const pkv_config* cfg, int32_t T) {
+  return plan_prefill_gemm(cfg->hidden_size / 16, T, cfg->num_attention_heads * kHeadDim, true);
+}
+static PgemmPlan prefill_down_plan(const pkv_config* cfg, int32_t T) {
+  return plan_prefill_gemm(cfg->hidden_size / 16, T, cfg->intermediate_size, true);
+}
 
 static PrefillLayout prefill_layout(const pkv_config* cfg, int32_t T) {
   const size_t H = cfg->hidden_size, I = cfg->intermediate_size;
@@ -407,6 +415,8 @@ static PrefillLayout prefill_layout(const pkv_config* cfg, int32_t T) {
   L.q = take(2 * (size_t)T * QD * 2);
   L.ob = take(2 * (size_t)packed_pair_elems(T, (int)QD));
   L.act = take(2 * (size_t)packed_pair_elems(T, (int)I));
+  const int ks_o = prefill_o_plan(cfg, T).ks, ks_d = prefill_down_plan(cfg, T).ks;
+  L.part = take(sizeof(float) * (size_t)(ks_o > ks_d ? ks_o : ks_d) * T * H);
   L.amax = take(sizeof(unsigned long long) * plan_gemm(EPI_LOGITS, cfg->vocab_size, 1, H).tiles);
   L.total = off;
   return L;
@@ -458,7 +468,16 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   uint32_t* err = at<uint32_t>(workspace, L.err);
   const float eps = cfg->rms_norm_eps;
 
+  float* part = at<float>(workspace, L.part);
+  const PgemmPlan p_qkv = plan_prefill_gemm((Hq + 2 * Hkv) * 4, T, H, false);
+  const PgemmPlan p_o = prefill_o_plan(cfg, T);
+  const PgemmPlan p_gu = plan_prefill_gemm(I / 8, T, H, false);
+  const PgemmPlan p_down = prefill_down_plan(cfg, T);
+
+  // x = E[tokens]; the first layer's RMSNorm; every later RMSNorm is done by
+  // the residual kernel that finishes the row before it
   if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, nullptr, T, err, st)))) return rc;
+  if ((rc = io(launch_prefill_norm(x, w->layers[0].attn_norm, H, T, eps, xb, st)))) return rc;
   for (int l = 0; l < cfg->num_hidden_layers; ++l) {
     const pkv_layer_weights* lw = &w->layers[l];
     const int32_t* bt = block_tables + (size_t)l * max_pages;
@@ -466,8 +485,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
     base.T = T;
     base.err = err;
 
-    // RMSNorm, QKV + RoPE at start_pos + t, K/V into the prompt's pages
-    if ((rc = io(launch_prefill_norm(x, lw->attn_norm, H, T, eps, xb, st)))) return rc;
+    // QKV + RoPE at start_pos + t, K/V into the prompt's pages
     {
       PgemmArgs a = base;
       a.W = lw->w_qkv;
@@ -485,7 +503,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.rsin = w->rope_sin;
       a.Hq = Hq;
       a.Hkv = Hkv;
-      if ((rc = io(launch_prefill_gemm(EPI_QKV, a, st)))) return rc;
+      if ((rc = io(launch_prefill_gemm(EPI_QKV, a, p_qkv, st)))) return rc;
     }
     // causal attention over positions 0 .. start_pos + t
     {
@@ -505,7 +523,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.G = Hq / Hkv;
       if ((rc = io(launch_prefill_attention(a, st)))) return rc;
     }
-    // x += W_o o
+    // x += W_o o, then the MLP's RMSNorm
     {
       PgemmArgs a = base;
       a.W = lw->w_o;
@@ -513,12 +531,12 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.X = ob;
       a.N = H;
       a.K = QD;
-      a.out = x;
-      a.resid = x;
-      if ((rc = io(launch_prefill_gemm(EPI_RESID, a, st)))) return rc;
+      a.part = part;
+      a.ksplit = p_o.ks;
+      if ((rc = io(launch_prefill_gemm(EPI_RESID, a, p_o, st)))) return rc;
+      if ((rc = io(launch_prefill_resid(x, part, p_o.ks, T, H, lw->mlp_norm, eps, xb, st)))) return rc;
     }
-    // RMSNorm, gate/up, SwiGLU
-    if ((rc = io(launch_prefill_norm(x, lw->mlp_norm, H, T, eps, xb, st)))) return rc;
+    // gate/up, SwiGLU
     {
       PgemmArgs a = base;
       a.W = lw->w_gate_up;
@@ -528,9 +546,9 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.K = H;
       a.act = act;
       a.I = I;
-      if ((rc = io(launch_prefill_gemm(EPI_SWIGLU, a, st)))) return rc;
+      if ((rc = io(launch_prefill_gemm(EPI_SWIGLU, a, p_gu, st)))) return rc;
     }
-    // x += W_down a
+    // x += W_down a, then the next layer's attention RMSNorm
     {
       PgemmArgs a = base;
       a.W = lw->w_down;
@@ -538,9 +556,11 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.X = act;
       a.N = H;
       a.K = I;
-      a.out = x;
-      a.resid = x;
-      if ((rc = io(launch_prefill_gemm(EPI_RESID, a, st)))) return rc;
+      a.part = part;
+      a.ksplit = p_down.ks;
+      if ((rc = io(launch_prefill_gemm(EPI_RESID, a, p_down, st)))) return rc;
+      const uint16_t* nw = l + 1 < cfg->num_hidden_layers ? w->layers[l + 1].attn_norm : nullptr;
+      if ((rc = io(launch_prefill_resid(x, part, p_down.ks, T, H, nw, eps, xb, st)))) return rc;
     }
   }
   // final norm, LM head and argmax of the last prompt token only

@@ -161,9 +161,11 @@ struct PgemmArgs {
   const uint16_t* X;       // packed BF16 hi/lo activation pairs
   int32_t N, K, T;
   uint32_t* err;
-  // EPI_RESID: out[t][n] = resid[t][n] + y, plain [T][N] (out may be resid)
-  float* out;
-  const float* resid;
+  // EPI_RESID: workgroups of K split s write their sums y_s to
+  // part[s][t][n] (plain [ksplit][T][N]); a per-token kernel then adds the
+  // residual and the splits in split order
+  float* part;
+  int32_t ksplit;
   // EPI_QKV: q as BF16 hi, lo halves [T][Hq][2][D]; k, v into the pages of
   // positions start_pos + t through the sequence's table bt
   uint16_t* q_split;
@@ -193,21 +195,46 @@ struct PattnArgs {
   int32_t Hq, Hkv, G;
 };
 
-// A prefill GEMM tile: 2 x 2 waves, each 16 rg rows by 16 cg tokens.
+// A prefill GEMM launch: 2 x 2 waves per workgroup, each 16 rg rows by
+// 16 cg tokens, and ks workgroups splitting K per tile (tiles * ks in all).
 struct PgemmPlan {
-  int rg, cg, tiles;
+  int rg, cg, tiles, ks;
 };
 
-inline PgemmPlan plan_prefill_gemm(int w_groups, int T) {
-  // the largest wave tile that still gives about one workgroup per compute
-  // unit; smaller ones only where the projection is too small for that
-  static const int cand[3][2] = {{4, 4}, {2, 4}, {2, 2}};
+constexpr int kPfTargetWgs = 240;     // about one workgroup per compute unit
+constexpr int kPfMinSplitSteps = 16;  // 32-wide K steps per split, at least
+
+inline int pf_tiles(int w_groups, int T, int rg, int cg) {
+  return ((w_groups + 2 * rg - 1) / (2 * rg)) * ((T + 32 * cg - 1) / (32 * cg));
+}
+
+// Tile shape (and K split) of a prefill projection.  Large tiles read each
+// operand byte fewer times; where they give too few workgroups, a residual
+// projection (can_split) splits K instead, and the other epilogues, which
+// need whole sums, take smaller tiles.
+inline PgemmPlan plan_prefill_gemm(int w_groups, int T, int K, bool can_split) {
   PgemmPlan p{};
+  if (can_split) {
+    static const int cand[2][2] = {{8, 4}, {4, 4}};
+    const int steps = K / 32;
+    for (const auto& c : cand) {
+      p.rg = c[0];
+      p.cg = c[1];
+      p.tiles = pf_tiles(w_groups, T, p.rg, p.cg);
+      int ks = (kPfTargetWgs + p.tiles - 1) / p.tiles;
+      const int most = steps / kPfMinSplitSteps > 1 ? steps / kPfMinSplitSteps : 1;
+      p.ks = ks < most ? ks : most;
+      if (p.tiles * p.ks >= kPfTargetWgs) break;
+    }
+    return p;
+  }
+  static const int cand[4][2] = {{8, 4}, {4, 4}, {2, 4}, {2, 2}};
+  p.ks = 1;
   for (const auto& c : cand) {
     p.rg = c[0];
     p.cg = c[1];
-    p.tiles = ((w_groups + 2 * p.rg - 1) / (2 * p.rg)) * ((T + 32 * p.cg - 1) / (32 * p.cg));
-    if (p.tiles >= 240) break;
+    p.tiles = pf_tiles(w_groups, T, p.rg, p.cg);
+    if (p.tiles >= kPfTargetWgs) break;
   }
   return p;
 }
@@ -354,7 +381,11 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 // BF16 hi/lo pairs
 hipError_t launch_prefill_norm(const float* x, const uint16_t* xw, int K, int T, float eps,
                                uint16_t* out, hipStream_t st);
-hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, hipStream_t st);
+hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, const PgemmPlan& p, hipStream_t st);
+// x[t] += sum over splits of part[s][t] (in split order); then, if nw is
+// given, the RMSNorm of the new row into packed hi/lo pairs xb
+hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int N,
+                                const uint16_t* nw, float eps, uint16_t* xb, hipStream_t st);
 hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st);
 
 }  // namespace pkv

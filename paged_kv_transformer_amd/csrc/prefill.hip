@@ -14,9 +14,11 @@
 // per lane.
 //
 //   prefill_norm_kernel       RMSNorm of FP32 rows -> packed BF16 hi/lo
-//   prefill_gemm_kernel       128 x 128 (or smaller) output tiles; epilogues
+//   prefill_gemm_kernel       256 x 128 (or smaller) output tiles; epilogues
 //                             as the decode projections: RoPE + q split +
-//                             K/V page writes, residual add, SwiGLU
+//                             K/V page writes, SwiGLU, or (residual
+//                             projections) K-split partial sums
+//   prefill_resid_kernel      residual + partial sums, then the next RMSNorm
 //   prefill_attention_kernel  causal paged attention: each wave takes up to
 //                             16 (token, head) query columns of one kv head
 //                             and walks the pages 0 .. its last position
@@ -179,13 +181,19 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
   const int wr = w & 1, wc = w >> 1;
   const int nrt = (a.w_groups + AR - 1) / AR;
   const int ntt = (a.T + 16 * BC - 1) / (16 * BC);
-  const int ntiles = nrt * ntt;
-  // workgroup id -> tile: ids i, i + 8, i + 16 .. (one XCD) take consecutive tiles
+  const int nks = EPI == EPI_RESID ? a.ksplit : 1;
+  const int nwork = nrt * nks * ntt;
+  // workgroup id -> work item (row tile, K split, token tile), token tile
+  // fastest: ids i, i + 8, i + 16 .. (one XCD) take consecutive items, so
+  // the token tiles sharing one slice of weights run on one XCD
   const int id = blockIdx.x;
-  const int per = ntiles >> 3, rem = ntiles & 7, xcd = id & 7, slot0 = id >> 3;
-  const int tile = xcd < rem ? xcd * (per + 1) + slot0 : rem * (per + 1) + (xcd - rem) * per + slot0;
-  const int rt = tile / ntt, tt = tile - rt * ntt;
+  const int per = nwork >> 3, rem = nwork & 7, xcd = id & 7, slot0 = id >> 3;
+  const int item = xcd < rem ? xcd * (per + 1) + slot0 : rem * (per + 1) + (xcd - rem) * per + slot0;
+  const int rt = item / (nks * ntt);
+  const int ksi = (item / ntt) % nks, tt = item % ntt;
   const int S = a.K >> 5;
+  const int sps = (S + nks - 1) / nks;
+  const int s0 = ksi * sps, ns = min(S, s0 + sps) - s0;  // this split's K steps
   const int g0 = rt * AR, c0 = tt * BC;
 
   const i32x4 wres = rsrc_words(a.W, (uint32_t)a.w_groups * (uint32_t)S * 1024u);
@@ -204,12 +212,14 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
     }
   }
   const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[0][0][0];
+  // stage st (0 .. ns - 1) is K step s0 + st
   auto issue = [&](int st) {
     const uint32_t base = ring0 + (uint32_t)((st % NSTG) * NB) * 1024u;
+    const uint32_t ks = (uint32_t)(s0 + st);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const bool isw = i < NA / 4;
-      lds_copy16(base + (uint32_t)(4 * i + w) * 1024u, boff[i] + (uint32_t)st * (isw ? 1024u : 2048u),
+      lds_copy16(base + (uint32_t)(4 * i + w) * 1024u, boff[i] + ks * (isw ? 1024u : 2048u),
                  isw ? wres : xres);
     }
   };
@@ -220,13 +230,13 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
 #pragma unroll
     for (int c = 0; c < CG; ++c) acc[r][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  for (int st = 0; st < NSTG - 1 && st < S; ++st) issue(st);
-  for (int st = 0; st < S; ++st) {
+  for (int st = 0; st < NSTG - 1 && st < ns; ++st) issue(st);
+  for (int st = 0; st < ns; ++st) {
     // this wave's copies of stage st have landed, then everyone's; every
     // wave is also done with stage st - 1, whose slot is refilled next
-    wait_stages<LPW, NSTG - 2>(min(NSTG - 2, S - 1 - st));
+    wait_stages<LPW, NSTG - 2>(min(NSTG - 2, ns - 1 - st));
     __syncthreads();
-    if (st + NSTG - 1 < S) issue(st + NSTG - 1);
+    if (st + NSTG - 1 < ns) issue(st + NSTG - 1);
     const int sl = st % NSTG;
     u32x4 af[RG], bh[CG], bl[CG];
 #pragma unroll
@@ -257,9 +267,8 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
       const f32x4 v = acc[r][c];
       if (EPI == EPI_RESID) {
         if (G < a.w_groups && t < a.T) {
-          const size_t o = (size_t)t * a.N + 16 * G + 4 * grp;
-          const float4 rv = *(const float4*)(a.resid + o);
-          *(float4*)(a.out + o) = make_float4(rv.x + v[0], rv.y + v[1], rv.z + v[2], rv.w + v[3]);
+          const size_t o = ((size_t)ksi * a.T + t) * a.N + 16 * G + 4 * grp;
+          *(float4*)(a.part + o) = make_float4(v[0], v[1], v[2], v[3]);
         }
       } else if (EPI == EPI_SWIGLU) {
         // rows 0..7 of a group are gate rows, 8..15 the matching up rows:
@@ -340,6 +349,62 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
         }
       }
     }
+}
+
+// ------------------------------------------------- residual + norm ---
+// One workgroup per token row: x[t] += sum_s part[s][t] (splits in order,
+// so the result does not depend on scheduling), then, if nw is given, the
+// next RMSNorm of the new row into packed hi/lo pairs (padding rows zero).
+// Each thread owns 8 consecutive columns per 2048, in both passes, so its
+// second pass re-reads only what it wrote itself.
+__global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const float* part, int ks,
+                                                            int T, int N, const uint16_t* nw,
+                                                            float eps, uint16_t* xb) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (t >= T) {
+    for (int k = 8 * tid; k < N; k += 8 * 256) {
+      *(uint4*)(xb + packed_pair_index(t, k, N, 0)) = make_uint4(0u, 0u, 0u, 0u);
+      *(uint4*)(xb + packed_pair_index(t, k, N, 1)) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
+  float* row = x + (size_t)t * N;
+  const size_t split = (size_t)T * N;
+  float ss = 0.f;
+  for (int k = 8 * tid; k < N; k += 8 * 256) {
+    float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
+    for (int sp = 0; sp < ks; ++sp) {
+      const float* pr = part + sp * split + (size_t)t * N + k;
+      const float4 pa = *(const float4*)pr, pb = *(const float4*)(pr + 4);
+      a.x += pa.x; a.y += pa.y; a.z += pa.z; a.w += pa.w;
+      b.x += pb.x; b.y += pb.y; b.z += pb.z; b.w += pb.w;
+    }
+    *(float4*)(row + k) = a;
+    *(float4*)(row + k + 4) = b;
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
+          b.w * b.w;
+  }
+  if (!nw) return;
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float rs = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+  for (int k = 8 * tid; k < N; k += 8 * 256) {
+    const float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint4 w = *(const uint4*)(nw + k);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = v[2 * e] * bf16_lo(ww[e]) * rs;
+      v[2 * e + 1] = v[2 * e + 1] * bf16_hi(ww[e]) * rs;
+    }
+    uint4 hi, lo;
+    split8(v, hi, lo);
+    *(uint4*)(xb + packed_pair_index(t, k, N, 0)) = hi;
+    *(uint4*)(xb + packed_pair_index(t, k, N, 1)) = lo;
+  }
 }
 
 // -------------------------------------------------------- attention ---
@@ -524,14 +589,18 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
 }
 
 template <int EPI>
-hipError_t launch_pg(const PgemmArgs& a, hipStream_t st) {
-  const PgemmPlan p = plan_prefill_gemm(a.w_groups, a.T);
-  if (p.rg == 4 && p.cg == 4)
-    prefill_gemm_kernel<EPI, 4, 4><<<p.tiles, 256, 0, st>>>(a);
+hipError_t launch_pg(const PgemmArgs& a, const PgemmPlan& p, hipStream_t st) {
+  const int wgs = p.tiles * (EPI == EPI_RESID ? p.ks : 1);
+  if (p.rg == 8 && p.cg == 4)
+    prefill_gemm_kernel<EPI, 8, 4><<<wgs, 256, 0, st>>>(a);
+  else if (p.rg == 4 && p.cg == 4)
+    prefill_gemm_kernel<EPI, 4, 4><<<wgs, 256, 0, st>>>(a);
   else if (p.rg == 2 && p.cg == 4)
-    prefill_gemm_kernel<EPI, 2, 4><<<p.tiles, 256, 0, st>>>(a);
+    prefill_gemm_kernel<EPI, 2, 4><<<wgs, 256, 0, st>>>(a);
+  else if (p.rg == 2 && p.cg == 2)
+    prefill_gemm_kernel<EPI, 2, 2><<<wgs, 256, 0, st>>>(a);
   else
-    prefill_gemm_kernel<EPI, 2, 2><<<p.tiles, 256, 0, st>>>(a);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -543,14 +612,22 @@ hipError_t launch_prefill_norm(const float* x, const uint16_t* xw, int K, int T,
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, hipStream_t st) {
+hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, const PgemmPlan& p, hipStream_t st) {
   if (a.K % 32 != 0 || a.T < 1) return hipErrorInvalidValue;
+  if (epi == EPI_RESID && a.ksplit != p.ks) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_QKV: return launch_pg<EPI_QKV>(a, st);
-    case EPI_RESID: return launch_pg<EPI_RESID>(a, st);
-    case EPI_SWIGLU: return launch_pg<EPI_SWIGLU>(a, st);
+    case EPI_QKV: return launch_pg<EPI_QKV>(a, p, st);
+    case EPI_RESID: return launch_pg<EPI_RESID>(a, p, st);
+    case EPI_SWIGLU: return launch_pg<EPI_SWIGLU>(a, p, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int N,
+                                const uint16_t* nw, float eps, uint16_t* xb, hipStream_t st) {
+  const int rows = nw ? (T + 15) / 16 * 16 : T;
+  prefill_resid_kernel<<<rows, 256, 0, st>>>(x, part, ks, T, N, nw, eps, xb);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st) {

@@ -104,13 +104,14 @@ def test_prefill_group_sizes(heads, kv_heads):
     _oracle_check(shape, w, pool, bts, start, tokens, logits, nxt, pool_after, "G=%d" % (heads // kv_heads))
 
 
-def test_prefill_wide_tiles_match_oracle():
-    """A 250-token prompt through an 8192-wide MLP: the gate/up projection
+@pytest.mark.parametrize("start,T", [(3, 250), (0, 400)])
+def test_prefill_wide_tiles_match_oracle(start, T):
+    """Prompts through an 8192-wide MLP.  250 tokens: the gate/up projection
     takes the 128 x 128 tile (128 row tiles x 2 token tiles, the second
-    ragged); the others the smaller tiles."""
+    ragged); 400 tokens: the 256 x 128 tile (64 x 4, the last ragged); the
+    other projections the smaller tiles."""
     shape = synth.tiny_shape(hidden=256, layers=1, heads=4, kv_heads=2, inter=8192, vocab=1000)
-    start, T = 3, 250
-    w, pool, bts, tokens = _inputs(shape, 91, start, T)
+    w, pool, bts, tokens = _inputs(shape, 91 + T, start, T)
     logits, nxt, pool_after, err = prefill_gpu(shape, w, pool, bts, start, tokens)
     assert err == 0
     _oracle_check(shape, w, pool, bts, start, tokens, logits, nxt, pool_after, "wide")
