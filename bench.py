@@ -281,6 +281,23 @@ def time_prefill(torch, pkv, synth, S, T=512, reps=5):
     return e0.elapsed_time(e1) / reps, prefill_flops(shape, 0, T)
 
 
+class PrefillSetup:
+    """The step's model weights (same seed) without the decode workload."""
+
+    def __init__(self, pkv, synth, T):
+        self.shape = synth.LLAMA1B
+        self.max_pos = T
+        self.cfg = pkv.make_config(self.shape, max_pos=T)
+        self.model = pkv.upload_model(synth.model_weights(self.shape, 1002), self.shape.theta, T)
+
+
+def prefill_only(torch, pkv, synth, T):
+    ms, flops = time_prefill(torch, pkv, synth, PrefillSetup(pkv, synth, T), T)
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({"prefill_tokens": T, "ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                      "algorithmic_tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 5)}))
+
+
 def cpu_baseline(S, seqs):
     import oracle
     wl = S.wl
@@ -373,6 +390,8 @@ def main():
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     ap.add_argument("--no-layer-b1", action="store_true")
     ap.add_argument("--prefill-tokens", type=int, default=512, help="0 skips the prefill timing")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time the prefill alone (the step's model, no decode workload)")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, out_path=args.traffic_out)
@@ -392,6 +411,9 @@ def main():
     torch.cuda.set_device(0)
     if args.attention_only:
         attention_only(torch, pkv, synth, args.attn_rounds)
+        return
+    if args.prefill_only:
+        prefill_only(torch, pkv, synth, args.prefill_tokens)
         return
 
     S = Setup(torch, pkv, synth, with_host=not args.no_cpu_baseline)

@@ -374,6 +374,7 @@ __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const floa
   float ss = 0.f;
   for (int k = 8 * tid; k < N; k += 8 * 256) {
     float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
+#pragma unroll 8
     for (int sp = 0; sp < ks; ++sp) {
       const float* pr = part + sp * split + (size_t)t * N + k;
       const float4 pa = *(const float4*)pr, pb = *(const float4*)(pr + 4);
