@@ -4,10 +4,11 @@ TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package; the product path
 (``paged_kv_transformer_amd``) never does, and this package never imports it.
 
-The arithmetic lives in ``oracle.c`` (FP32, single thread, contiguous
-per-layer cache, two-pass softmax).  This module only marshals numpy arrays
-into it and loops over sequences, layers and tokens; every step of a batch
-is the plain per-sequence computation repeated.
+The decode arithmetic lives in ``oracle.c`` (FP32, single thread, contiguous
+per-layer cache, two-pass softmax).  This module marshals numpy arrays into
+it and loops over sequences, layers and tokens; every step of a batch is the
+plain per-sequence computation repeated.  The sampler after the LM head is
+plain numpy in float64 (a sort and a cumulative sum).
 
 Parity pins (what each function is checked against, in tests/):
   bf16 rounding          torch's round-to-nearest-even conversion, and
@@ -30,6 +31,12 @@ Parity pins (what each function is checked against, in tests/):
                          causal mask (last logits, argmax, every K/V row
                          written); a one-token prefill equals a decode step
   argmax                 numpy.argmax (first maximum)
+  sample_token           closed forms: temperature 0, top-k 1 or top-p 0 give
+                         the argmax; equal logits give token floor(u V); a
+                         geometric distribution fixes the nucleus (the token
+                         that crosses top-p is kept) and the renormalised
+                         inverse CDF; temperature T on l equals 1 on l / T; a
+                         grid of u reproduces the kept probabilities
 Full-size layer and step outputs have no printed values on the source pages:
 beyond the pins above they are "parity unpinned".
 """
@@ -344,3 +351,70 @@ def prefill_paged(shape, weights, pool, geo, block_tables, start_pos, tokens, wa
         if t == len(tokens) - 1:
             lg, best = lm_head(weights["embed"], weights["final_norm"], shape.eps, x)
     return (lg if want_logits else None), best, pool
+
+
+# -------------------------------------------------------------- sampling ---
+
+# Decisions of the sampler within this much probability mass (of a total
+# of 1) of a boundary may go either way in a computation that is correct to
+# FP32 rounding: the probabilities of a vocabulary-sized softmax come out of
+# exponentials of arguments up to ~30 in magnitude, whose FP32 rounding moves
+# each probability by up to ~2e-6 of itself.
+SAMPLE_EPS = 1e-5
+
+
+def sample_token(logits, temperature, top_p, top_k, u, eps=SAMPLE_EPS):
+    """Sampling of one sequence's next token from its logits ("手写LLM推理引擎"
+    §3.3 logits post-processing and §2.4 decoding strategies; llmc 五 plans
+    temperature / top-k / top-p after greedy):
+      1. z = logits / temperature; temperature <= 0 is greedy (first argmax);
+      2. p = softmax(z);
+      3. top-p: order the tokens by decreasing p (equal logits: lower index
+         first) and keep the smallest prefix whose cumulative probability
+         reaches top_p (at least one token; top_p >= 1 keeps all);
+      4. then top-k: keep at most top_k of them (top_k <= 0: no limit);
+      5. renormalise p over the kept tokens and return the first kept token,
+         in vocabulary order, whose cumulative probability exceeds u (u in
+         [0, 1), the uniform draw, an input).
+    float64 throughout.  Returns (token, acceptable): acceptable holds every
+    token a computation within eps of these decisions (the nucleus boundary
+    and the inverse-CDF step) could also return."""
+    l = np.asarray(logits, dtype=np.float64)
+    V = l.size
+    if temperature <= 0.0:
+        t = int(np.argmax(l))
+        return t, {t}
+    e = np.exp((l - l.max()) / float(temperature))
+    p = e / e.sum()
+    order = np.lexsort((np.arange(V), -l))
+    cum = np.cumsum(p[order])
+
+    def prefix_len(target):
+        if target >= 1.0:
+            return V
+        if target <= 0.0:
+            return 1
+        return min(V, int(np.searchsorted(cum, target, side="left")) + 1)
+
+    def limit(n):
+        return n if top_k <= 0 else min(n, int(top_k))
+
+    def draw(n, uu):
+        kept = np.sort(order[:n])
+        c = np.cumsum(p[kept] / p[kept].sum())
+        return kept, c, min(int(np.searchsorted(c, uu, side="right")), n - 1)
+
+    L = limit(prefix_len(top_p))
+    kept, c, i = draw(L, u)
+    token = int(kept[i])
+    acceptable = set()
+    lens = {L}
+    if 0.0 < top_p < 1.0:
+        lens |= {limit(prefix_len(top_p - eps)), limit(prefix_len(top_p + eps))}
+        lens |= set(range(min(lens), max(lens) + 1))
+    for n in sorted(lens):
+        kn, cn, _ = draw(n, u)
+        lo = int(np.searchsorted(cn, u - eps, side="right"))
+        hi = int(np.searchsorted(cn, u + eps, side="right"))
+        acceptable |= {int(kn[j]) for j in range(min(lo, n - 1), min(hi, n - 1) + 1)}
+    return token, acceptable
