@@ -260,6 +260,39 @@ size_t pkv_prefill_workspace_bytes(const pkv_config *cfg, int32_t num_tokens,
 				   int32_t max_pages);
 
 /*
+ * sample_tokens — draw each sequence's next token from its logits, the
+ * decoding step after the LM head ("手写LLM推理引擎" §3.3 logits
+ * post-processing: temperature, softmax, top-p, a multinomial draw; §2.4:
+ * top-p keeps the smallest set of tokens whose cumulative probability
+ * reaches p; llmc 五: temperature / top-k / top-p after greedy).  For
+ * sequence b:
+ *   z = logits[b] / temperature[b]; p = softmax(z);
+ *   nucleus = the smallest prefix of the tokens by decreasing p (equal
+ *   logits: lower index first) whose cumulative p reaches top_p[b] (at least
+ *   one token; top_p >= 1 keeps all), then at most top_k[b] of them
+ *   (top_k <= 0: no limit);
+ *   tokens[b] = the first nucleus token, in vocabulary order, whose
+ *   cumulative p renormalised over the nucleus exceeds u[b] in [0, 1).
+ * temperature[b] <= 0 is greedy (the first maximum).  u is the caller's
+ * uniform draw, so the random stream is the caller's; the result is a
+ * deterministic function of the inputs (probabilities are summed in 64-bit
+ * fixed point, 2^-32 of the largest one).
+ *   logits [batch][vocab] FP32 (device; finite values or -inf, at least one
+ *   finite per row), temperature, top_p, u [batch] FP32, top_k [batch]
+ *   int32, tokens [batch] int32 (device).  workspace: at least
+ *   pkv_sample_workspace_bytes(batch, vocab) bytes, 256-byte aligned.
+ * batch == 0 is a no-op.  Errors: -EINVAL (NULL, misaligned workspace,
+ * vocab < 1, batch < 0), -ENOTSUP (batch > 65535), -ENOSPC, -EIO.
+ */
+int sample_tokens(const float *logits, int32_t batch, int32_t vocab,
+		  const float *temperature, const float *top_p,
+		  const int32_t *top_k, const float *u, int32_t *tokens,
+		  void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes sample_tokens needs (0 for bad sizes). */
+size_t pkv_sample_workspace_bytes(int32_t batch, int32_t vocab);
+
+/*
  * Packed weight layout (used by every matrix the projections stream): the
  * matrix is cut into groups of 16 rows and its columns into 32-wide steps;
  * block (group G, step s) is 1 KiB, and its 16-byte chunk l = 16 i + m

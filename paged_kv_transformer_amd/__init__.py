@@ -81,6 +81,8 @@ def lib():
             "prefill": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights), PP, P, I32, I32,
                                        P, I32, P, P, P, SZ, P]),
             "pkv_prefill_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32]),
+            "sample_tokens": (ctypes.c_int, [P, I32, I32, P, P, P, P, P, P, SZ, P]),
+            "pkv_sample_workspace_bytes": (SZ, [I32, I32]),
             "pkv_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32]),
             "pkv_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
             "pkv_workspace_init": (ctypes.c_int, [P, SZ, P]),
@@ -299,6 +301,21 @@ def prefill(cfg, model, pool, block_tables, start_pos, token_ids, logits, next_t
 
 
 # ------------------------------------------------------- host -> device ---
+
+def sample_workspace_bytes(batch, vocab):
+    return lib().pkv_sample_workspace_bytes(batch, vocab)
+
+
+def sample_tokens(logits, temperature, top_p, top_k, u, tokens, workspace, stream=None):
+    """logits [B, V] FP32; temperature, top_p, u [B] FP32; top_k [B] int32;
+    tokens [B] int32 (written)."""
+    B, V = logits.shape
+    _check("sample_tokens", lib().sample_tokens(
+        _dev(logits, (torch.float32,), "logits"), B, V, _dev(temperature, (torch.float32,), "temperature"),
+        _dev(top_p, (torch.float32,), "top_p"), _dev(top_k, (torch.int32,), "top_k"),
+        _dev(u, (torch.float32,), "u"), _dev(tokens, (torch.int32,), "tokens"),
+        _dev(workspace, (torch.uint8,), "workspace"), workspace.numel(), _stream(stream)))
+
 
 def to_device(a, device="cuda"):
     """numpy array -> contiguous device tensor (uint16 BF16 bits -> int16)."""

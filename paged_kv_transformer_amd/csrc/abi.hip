@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/pkv.h: argument validation
 // (pure host code, run before any HIP call), workspace carving and the
 // launch sequence of each entry point.  Every step of the computation runs
-// in the kernels of attention.hip, gemm.hip, prefill.hip and misc.hip.
+// in the kernels of attention.hip, gemm.hip, prefill.hip, sample.hip and misc.hip.
 #include <errno.h>
 #include <math.h>
 #include <stdint.h>
@@ -581,6 +581,29 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   const GemmPlan p = plan_gemm(EPI_LOGITS, V, 1, H);
   a.ksplit = p.ks;
   return io(launch_gemm(EPI_LOGITS, a, p, st));
+}
+
+size_t pkv_sample_workspace_bytes(int32_t batch, int32_t vocab) {
+  if (batch < 1 || vocab < 1 || batch > 65535) return 0;
+  int chunk;
+  const int W = sample_chunks(batch, vocab, &chunk);
+  return sample_ws_carve(nullptr, batch, W).bytes;
+}
+
+int sample_tokens(const float* logits, int32_t batch, int32_t vocab, const float* temperature,
+                  const float* top_p, const int32_t* top_k, const float* u, int32_t* tokens,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  if (batch < 0 || vocab < 1) return -EINVAL;
+  if (batch > 65535) return -ENOTSUP;
+  if (batch == 0) return 0;
+  if (!logits || !temperature || !top_p || !top_k || !u || !tokens || !workspace) return -EINVAL;
+  if (!aligned(workspace, 256)) return -EINVAL;
+  if (ws_bytes < pkv_sample_workspace_bytes(batch, vocab)) return -ENOSPC;
+  int chunk;
+  const int W = sample_chunks(batch, vocab, &chunk);
+  const SampleWs ws = sample_ws_carve(workspace, batch, W);
+  return io(launch_sample(logits, batch, vocab, temperature, top_p, top_k, u, tokens, ws, W, chunk,
+                          (hipStream_t)stream));
 }
 
 size_t pkv_packed_weight_bytes(int32_t rows, int32_t cols, int32_t layout) {

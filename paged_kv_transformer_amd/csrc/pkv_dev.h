@@ -239,6 +239,27 @@ inline PgemmPlan plan_prefill_gemm(int w_groups, int T, int K, bool can_split) {
   return p;
 }
 
+// Sampling after the LM head: per-sequence workspace of the radix select
+// (three levels of 2048-bucket count and fixed-point mass histograms), the
+// choice records passed between its launches, and per-chunk partials.
+constexpr int kSampleChoiceBytes = 24;
+struct SampleWs {
+  uint32_t* cnt;      // [B][3][2048]
+  uint64_t* mass;     // [B][3][2048]
+  uint64_t* sum;      // [B] softmax normaliser (fixed point)
+  void* choice;       // [2][B] choice records
+  float* wmax;        // [B][W] chunk maxima
+  uint64_t* wmass;    // [B][W] chunk mass above the threshold
+  uint32_t* wties;    // [B][W] chunk ties at the threshold
+  size_t bytes;
+};
+SampleWs sample_ws_carve(void* base, int B, int W);
+// workgroups per sequence for B sequences of V logits; *chunk = logits each
+int sample_chunks(int B, int V, int* chunk);
+hipError_t launch_sample(const float* logits, int B, int V, const float* temperature,
+                         const float* top_p, const int32_t* top_k, const float* u, int32_t* tokens,
+                         const SampleWs& ws, int W, int chunk, hipStream_t st);
+
 // ------------------------------------------------------------ plans ---
 
 // Attention: kAttnWaves waves per workgroup, kAttnPW pages per wave per

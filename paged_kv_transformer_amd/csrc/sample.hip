@@ -1,0 +1,502 @@
+// Sampling of each sequence's next token from its FP32 logits, gfx950.
+//
+// The decoding step after the LM head ("手写LLM推理引擎" §3.3 logits
+// post-processing, §2.4 decoding strategies; llmc 五 plans temperature,
+// top-k and top-p after greedy): z = logits / T, p = softmax(z), the
+// nucleus = the smallest prefix of the tokens by decreasing p (equal logits:
+// lower index first) whose cumulative p reaches top_p, capped at top_k
+// tokens, then the first kept token in vocabulary order whose renormalised
+// cumulative p exceeds the draw u (an input, so the caller owns the random
+// stream).  T <= 0 is greedy.
+//
+// Nothing is sorted.  The nucleus is found by a radix select on an
+// order-preserving 32-bit key of the logit (larger logit, larger key): three
+// digits (11, 11, 10 bits), each a histogram of (token count, probability
+// mass) over the tokens whose higher digits match the choice so far, then a
+// descending scan for the first bucket where the count reaches top_k or the
+// mass reaches top_p.  Probability mass is fixed point, p~ = 2^((l - max) T'
+// log2 e) * 2^32 as a 64-bit integer, so every sum is an integer sum:
+// exact, independent of the order in which workgroups add, and the same on
+// every replay.
+//
+// A batch of B sequences runs on B x W workgroups, each taking one chunk of
+// the vocabulary (the logits of a 16-sequence batch are 8 MB, and one
+// workgroup per sequence would leave most of the chip idle).  Workgroups
+// never wait on each other; the six launches are:
+//   K0 chunk maxima                       (and clears the level-1 sums)
+//   K1 normaliser + level-1 histogram     (clears level 2)
+//   K2 level-1 choice + level-2 histogram (clears level 3)
+//   K3 level-2 choice + level-3 histogram
+//   K4 level-3 choice (threshold key, ties kept) + per-chunk kept mass
+//   K5 the draw: the chunk holding u, then the token inside it
+// Each choice is made by every workgroup alike and stored by workgroup 0 of
+// the sequence for the next launch.
+#include "pkv_dev.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kSThreads = 256;
+constexpr int kBuckets = 2048;
+constexpr float kLog2eS = 1.4426950408889634f;
+
+// Order-preserving key of an FP32 value (finite or -inf): larger value,
+// larger key; -0 takes the key of +0, since the two are equal logits.
+__device__ __forceinline__ uint32_t skey(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int digit(uint32_t key, int level) {
+  return level == 0 ? (int)(key >> 21) : level == 1 ? (int)((key >> 10) & 2047u) : (int)(key & 1023u);
+}
+
+// Key bits a level's digit sits below: a token is a candidate of level L if
+// its key agrees with the prefix on the bits of levels 0 .. L-1.
+__device__ __forceinline__ bool in_prefix(uint32_t key, int level, uint32_t prefix) {
+  return level == 0 || (level == 1 ? (key >> 21) == prefix : (key >> 10) == prefix);
+}
+
+struct SArgs {
+  const float* logits;
+  int32_t B, V;
+  const float* temperature;
+  const float* top_p;
+  const int32_t* top_k;
+  const float* u;
+  int32_t* tokens;
+  SampleWs w;
+  int32_t W, chunk;  // workgroups per sequence, logits per workgroup
+};
+
+__device__ __forceinline__ float inv_temp(const SArgs& a, int b) {
+  const float T = a.temperature[b];
+  return T > 0.f ? kLog2eS / T : 0.f;  // greedy: every token mass 1, top_k 1
+}
+
+__device__ __forceinline__ uint64_t fixed_mass(float l, float m, float c) {
+  // (0, 1]; a -inf logit gives 0 (also when greedy, where -inf * 0 is NaN)
+  const float x = (l - m) * c;
+  const float e = x == x ? __builtin_amdgcn_exp2f(x) : 0.f;
+  return (uint64_t)(e * 4294967296.0f);
+}
+
+// The chunk of workgroup (b, w): elements [e0, e1) of sequence b; thread t
+// takes E consecutive ones.
+struct Chunk {
+  const float* row;
+  int e0, e1, E;
+};
+
+__device__ __forceinline__ Chunk chunk_of(const SArgs& a, int b, int w) {
+  Chunk c;
+  c.row = a.logits + (size_t)b * a.V;
+  c.e0 = w * a.chunk;
+  c.e1 = min(a.V, c.e0 + a.chunk);
+  c.E = a.chunk / kSThreads;
+  return c;
+}
+
+// Clears `n` 32-bit words of `p` with the workgroups of one sequence.
+__device__ __forceinline__ void clear_words(uint32_t* p, int n, int w, int W) {
+  for (int i = w * kSThreads + (int)threadIdx.x; i < n; i += W * kSThreads) p[i] = 0u;
+}
+
+// ---- per-sequence choice state, stored between launches
+struct Choice {
+  uint32_t prefix;    // key bits fixed so far
+  uint32_t k_rem;     // tokens still to take, by count
+  uint64_t m_rem;     // mass still to reach
+  uint64_t m_above;   // mass of the tokens already known to be kept
+};
+static_assert(sizeof(Choice) == kSampleChoiceBytes, "choice record size");
+
+__device__ __forceinline__ Choice* choices(const SampleWs& w) { return (Choice*)w.choice; }
+
+// Scan a histogram from the top bucket down for the first bucket where the
+// count reaches k_rem or the mass reaches m_rem; update the choice.  Every
+// thread of the workgroup calls it and gets the same result.
+__device__ Choice choose(const uint32_t* cnt, const uint64_t* mass, Choice c, int bits) {
+  __shared__ uint32_t s_cnt[kSThreads];
+  __shared__ uint64_t s_mass[kSThreads];
+  __shared__ Choice s_out;
+  constexpr int PER = kBuckets / kSThreads;  // 8 buckets per thread, top first
+  const int t = threadIdx.x;
+  const int top = kBuckets - 1 - PER * t;
+  if (t == 0) s_out = c;  // replaced below; kept only if no bucket qualifies
+  uint32_t lc = 0;
+  uint64_t lm = 0;
+  for (int i = 0; i < PER; ++i) {
+    lc += cnt[top - i];
+    lm += mass[top - i];
+  }
+  s_cnt[t] = lc;
+  s_mass[t] = lm;
+  __syncthreads();
+  // inclusive scan over threads (thread order = descending buckets)
+  for (int off = 1; off < kSThreads; off <<= 1) {
+    const uint32_t oc = t >= off ? s_cnt[t - off] : 0u;
+    const uint64_t om = t >= off ? s_mass[t - off] : 0ull;
+    __syncthreads();
+    s_cnt[t] += oc;
+    s_mass[t] += om;
+    __syncthreads();
+  }
+  const uint32_t inc_c = s_cnt[t];
+  const uint64_t inc_m = s_mass[t];
+  const uint32_t exc_c = inc_c - lc;
+  const uint64_t exc_m = inc_m - lm;
+  const bool before = exc_c >= c.k_rem || exc_m >= c.m_rem;
+  const bool after = inc_c >= c.k_rem || inc_m >= c.m_rem;
+  if (!before && after) {
+    uint32_t cc = exc_c;
+    uint64_t cm = exc_m;
+    for (int i = 0; i < PER; ++i) {
+      const int bk = top - i;
+      if (cc + cnt[bk] >= c.k_rem || cm + mass[bk] >= c.m_rem) {
+        Choice o;
+        o.prefix = (c.prefix << bits) | (uint32_t)bk;
+        o.k_rem = c.k_rem - cc;
+        o.m_rem = c.m_rem - cm;
+        o.m_above = c.m_above + cm;
+        s_out = o;
+        break;
+      }
+      cc += cnt[bk];
+      cm += mass[bk];
+    }
+  }
+  __syncthreads();
+  const Choice o = s_out;
+  __syncthreads();
+  return o;
+}
+
+// Histogram of one level over a chunk into LDS, then added to the sequence's
+// global histogram (integer atomics: order-independent).
+__device__ void histogram(const SArgs& a, const Chunk& ch, int level, uint32_t prefix, float m,
+                          float c, uint32_t* gcnt, uint64_t* gmass, uint64_t* gsum) {
+  __shared__ uint32_t h_cnt[kBuckets];
+  __shared__ uint64_t h_mass[kBuckets];
+  __shared__ uint64_t h_sum;
+  const int t = threadIdx.x;
+  for (int i = t; i < kBuckets; i += kSThreads) {
+    h_cnt[i] = 0u;
+    h_mass[i] = 0ull;
+  }
+  if (t == 0) h_sum = 0ull;
+  __syncthreads();
+  uint64_t ls = 0;
+  const int base = ch.e0 + t * ch.E;
+  for (int j = 0; j < ch.E; ++j) {
+    const int e = base + j;
+    if (e >= ch.e1) break;
+    const float l = ch.row[e];
+    const uint32_t key = skey(l);
+    const uint64_t f = fixed_mass(l, m, c);
+    ls += f;
+    if (in_prefix(key, level, prefix)) {
+      const int d = digit(key, level);
+      atomicAdd(&h_cnt[d], 1u);
+      atomicAdd((unsigned long long*)&h_mass[d], (unsigned long long)f);
+    }
+  }
+  if (gsum) atomicAdd((unsigned long long*)&h_sum, (unsigned long long)ls);
+  __syncthreads();
+  for (int i = t; i < kBuckets; i += kSThreads)
+    if (h_cnt[i]) {
+      atomicAdd(&gcnt[i], h_cnt[i]);
+      atomicAdd((unsigned long long*)&gmass[i], (unsigned long long)h_mass[i]);
+    }
+  if (gsum && t == 0) atomicAdd((unsigned long long*)gsum, (unsigned long long)h_sum);
+}
+
+__device__ __forceinline__ float seq_max(const SArgs& a, int b) {
+  float m = -INFINITY;
+  for (int i = 0; i < a.W; ++i) m = fmaxf(m, a.w.wmax[(size_t)b * a.W + i]);
+  return m;
+}
+
+__global__ __launch_bounds__(kSThreads) void sample_k0(const SArgs a) {
+  __shared__ float red[kSThreads / 64];
+  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  const Chunk ch = chunk_of(a, b, w);
+  float m = -INFINITY;
+  const int base = ch.e0 + t * ch.E;
+  for (int j = 0; j < ch.E; ++j) {
+    const int e = base + j;
+    if (e < ch.e1) m = fmaxf(m, ch.row[e]);
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  if (t == 0) {
+    float r = red[0];
+    for (int i = 1; i < kSThreads / 64; ++i) r = fmaxf(r, red[i]);
+    a.w.wmax[(size_t)b * a.W + w] = r;
+  }
+  clear_words((uint32_t*)(a.w.cnt + (size_t)b * 3 * kBuckets), kBuckets, w, a.W);
+  clear_words((uint32_t*)(a.w.mass + (size_t)b * 3 * kBuckets), 2 * kBuckets, w, a.W);
+  if (w == 0 && t == 0) a.w.sum[b] = 0ull;
+}
+
+__global__ __launch_bounds__(kSThreads) void sample_k1(const SArgs a) {
+  const int b = blockIdx.y, w = blockIdx.x;
+  const Chunk ch = chunk_of(a, b, w);
+  const float m = seq_max(a, b), c = inv_temp(a, b);
+  histogram(a, ch, 0, 0u, m, c, a.w.cnt + (size_t)b * 3 * kBuckets,
+            a.w.mass + (size_t)b * 3 * kBuckets, a.w.sum + b);
+  clear_words((uint32_t*)(a.w.cnt + ((size_t)b * 3 + 1) * kBuckets), kBuckets, w, a.W);
+  clear_words((uint32_t*)(a.w.mass + ((size_t)b * 3 + 1) * kBuckets), 2 * kBuckets, w, a.W);
+}
+
+// The choice before level 0: the count and mass budgets of the nucleus.
+__device__ Choice initial_choice(const SArgs& a, int b) {
+  Choice c;
+  c.prefix = 0u;
+  c.m_above = 0ull;
+  const bool greedy = !(a.temperature[b] > 0.f);
+  const int k = a.top_k[b];
+  c.k_rem = greedy ? 1u : (k > 0 && k < a.V ? (uint32_t)k : (uint32_t)a.V);
+  const float p = a.top_p[b];
+  if (greedy || p >= 1.f) {
+    c.m_rem = ~0ull;
+  } else {
+    const double target = ceil((double)(p > 0.f ? p : 0.f) * (double)a.w.sum[b]);
+    c.m_rem = target < 1.0 ? 1ull : (uint64_t)target;
+  }
+  return c;
+}
+
+__global__ __launch_bounds__(kSThreads) void sample_k2(const SArgs a) {
+  const int b = blockIdx.y, w = blockIdx.x;
+  const Chunk ch = chunk_of(a, b, w);
+  const float m = seq_max(a, b), c = inv_temp(a, b);
+  const Choice c1 = choose(a.w.cnt + (size_t)b * 3 * kBuckets, a.w.mass + (size_t)b * 3 * kBuckets,
+                           initial_choice(a, b), 11);
+  if (w == 0 && threadIdx.x == 0) choices(a.w)[b] = c1;
+  histogram(a, ch, 1, c1.prefix, m, c, a.w.cnt + ((size_t)b * 3 + 1) * kBuckets,
+            a.w.mass + ((size_t)b * 3 + 1) * kBuckets, nullptr);
+  clear_words((uint32_t*)(a.w.cnt + ((size_t)b * 3 + 2) * kBuckets), kBuckets, w, a.W);
+  clear_words((uint32_t*)(a.w.mass + ((size_t)b * 3 + 2) * kBuckets), 2 * kBuckets, w, a.W);
+}
+
+__global__ __launch_bounds__(kSThreads) void sample_k3(const SArgs a) {
+  const int b = blockIdx.y, w = blockIdx.x;
+  const Chunk ch = chunk_of(a, b, w);
+  const float m = seq_max(a, b), c = inv_temp(a, b);
+  const Choice c2 = choose(a.w.cnt + ((size_t)b * 3 + 1) * kBuckets,
+                           a.w.mass + ((size_t)b * 3 + 1) * kBuckets, choices(a.w)[b], 11);
+  if (w == 0 && threadIdx.x == 0) choices(a.w)[a.B + b] = c2;
+  histogram(a, ch, 2, c2.prefix, m, c, a.w.cnt + ((size_t)b * 3 + 2) * kBuckets,
+            a.w.mass + ((size_t)b * 3 + 2) * kBuckets, nullptr);
+}
+
+// The nucleus, final: every token with key > tau, and the first `ties`
+// tokens (vocabulary order) with key == tau, each of mass f_tau.
+struct Nucleus {
+  uint32_t tau, ties;
+  uint64_t f_tau, m_above;
+};
+
+__device__ Nucleus nucleus(const SArgs& a, int b) {
+  const uint32_t* cnt3 = a.w.cnt + ((size_t)b * 3 + 2) * kBuckets;
+  const uint64_t* mass3 = a.w.mass + ((size_t)b * 3 + 2) * kBuckets;
+  const Choice c3 = choose(cnt3, mass3, choices(a.w)[a.B + b], 10);
+  const uint32_t d = c3.prefix & 1023u;
+  const uint32_t n = cnt3[d];
+  const uint64_t f = n ? mass3[d] / n : 0ull;  // equal keys, equal masses
+  uint32_t t = c3.k_rem;
+  if (f > 0 && c3.m_rem <= mass3[d]) {
+    const uint64_t need = (c3.m_rem + f - 1) / f;
+    t = need < t ? (uint32_t)need : t;
+  }
+  Nucleus r;
+  r.tau = c3.prefix;
+  r.ties = t < n ? t : n;
+  r.f_tau = f;
+  r.m_above = c3.m_above;
+  return r;
+}
+
+// K4: per chunk, the mass of its tokens above tau and its count of ties.
+__global__ __launch_bounds__(kSThreads) void sample_k4(const SArgs a) {
+  __shared__ uint64_t s_m[kSThreads / 64];
+  __shared__ uint32_t s_t[kSThreads / 64];
+  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  const Chunk ch = chunk_of(a, b, w);
+  const float m = seq_max(a, b), c = inv_temp(a, b);
+  const Nucleus nu = nucleus(a, b);
+  uint64_t mg = 0;
+  uint32_t ties = 0;
+  const int base = ch.e0 + t * ch.E;
+  for (int j = 0; j < ch.E; ++j) {
+    const int e = base + j;
+    if (e >= ch.e1) break;
+    const float l = ch.row[e];
+    const uint32_t key = skey(l);
+    if (key > nu.tau) mg += fixed_mass(l, m, c);
+    ties += key == nu.tau;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mg += __shfl_xor(mg, o);
+    ties += __shfl_xor(ties, o);
+  }
+  if ((t & 63) == 0) {
+    s_m[t >> 6] = mg;
+    s_t[t >> 6] = ties;
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint64_t sm = 0;
+    uint32_t st = 0;
+    for (int i = 0; i < kSThreads / 64; ++i) {
+      sm += s_m[i];
+      st += s_t[i];
+    }
+    a.w.wmass[(size_t)b * a.W + w] = sm;
+    a.w.wties[(size_t)b * a.W + w] = st;
+  }
+}
+
+// K5: the draw.  r = floor(u * S_kept); the kept tokens in vocabulary order
+// are walked chunk by chunk, then thread by thread, then element by element
+// until their cumulative mass exceeds r.
+__global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
+  __shared__ uint64_t s_m[kSThreads];
+  __shared__ uint32_t s_t[kSThreads];
+  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  const Nucleus nu = nucleus(a, b);
+  // kept mass of every chunk, and where this chunk's starts
+  uint64_t total = 0, before = 0, mine = 0;
+  uint32_t ties_before = 0, tie_acc = 0;
+  for (int i = 0; i < a.W; ++i) {
+    const uint32_t ti = a.w.wties[(size_t)b * a.W + i];
+    const uint32_t kt = tie_acc >= nu.ties ? 0u : min(ti, nu.ties - tie_acc);
+    const uint64_t km = a.w.wmass[(size_t)b * a.W + i] + (uint64_t)kt * nu.f_tau;
+    if (i < w) {
+      before += km;
+      ties_before += ti;
+    }
+    if (i == w) mine = km;
+    total += km;
+    tie_acc += ti;
+  }
+  const float uu = fminf(fmaxf(a.u[b], 0.f), 1.f);
+  uint64_t r = (uint64_t)floor((double)uu * (double)total);
+  if (r >= total) r = total - 1;
+  if (!(r >= before && r < before + mine)) return;  // the draw is not in this chunk
+  const Chunk ch = chunk_of(a, b, w);
+  const float m = seq_max(a, b), c = inv_temp(a, b);
+  // this thread's ties (key == tau), scanned over the threads in vocabulary
+  // order: which of them are kept depends on the ties before it
+  uint32_t lt = 0;
+  const int base = ch.e0 + t * ch.E;
+  for (int j = 0; j < ch.E; ++j) {
+    const int e = base + j;
+    if (e >= ch.e1) break;
+    lt += skey(ch.row[e]) == nu.tau;
+  }
+  s_t[t] = lt;
+  __syncthreads();
+  for (int off = 1; off < kSThreads; off <<= 1) {
+    const uint32_t ot = t >= off ? s_t[t - off] : 0u;
+    __syncthreads();
+    s_t[t] += ot;
+    __syncthreads();
+  }
+  // its kept mass, then scanned the same way
+  const uint32_t tb = ties_before + s_t[t] - lt;
+  uint64_t km = 0;
+  uint32_t tk = 0;
+  for (int j = 0; j < ch.E; ++j) {
+    const int e = base + j;
+    if (e >= ch.e1) break;
+    const uint32_t key = skey(ch.row[e]);
+    if (key == nu.tau) km += (tb + tk++ < nu.ties) ? nu.f_tau : 0ull;
+    else if (key > nu.tau) km += fixed_mass(ch.row[e], m, c);
+  }
+  __syncthreads();
+  s_m[t] = km;
+  __syncthreads();
+  for (int off = 1; off < kSThreads; off <<= 1) {
+    const uint64_t om = t >= off ? s_m[t - off] : 0ull;
+    __syncthreads();
+    s_m[t] += om;
+    __syncthreads();
+  }
+  const uint64_t excl = before + s_m[t] - km;
+  if (!(r >= excl && r < excl + km)) return;
+  uint64_t acc = excl;
+  tk = 0;
+  for (int j = 0; j < ch.E; ++j) {
+    const int e = base + j;
+    if (e >= ch.e1) break;
+    const float l = ch.row[e];
+    const uint32_t key = skey(l);
+    uint64_t f = 0;
+    if (key == nu.tau) f = (tb + tk++ < nu.ties) ? nu.f_tau : 0ull;
+    else if (key > nu.tau) f = fixed_mass(l, m, c);
+    acc += f;
+    if (acc > r) {
+      a.tokens[b] = e;
+      return;
+    }
+  }
+}
+
+}  // namespace
+
+SampleWs sample_ws_carve(void* base, int B, int W) {
+  SampleWs w{};
+  const uintptr_t p = (uintptr_t)base;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return (void*)(p + at); };
+  w.cnt = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * 3 * kBuckets);
+  w.mass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * 3 * kBuckets);
+  w.sum = (uint64_t*)take(sizeof(uint64_t) * (size_t)B);
+  w.choice = (void*)take(sizeof(Choice) * (size_t)B * 2);
+  w.wmax = (float*)take(sizeof(float) * (size_t)B * W);
+  w.wmass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * W);
+  w.wties = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * W);
+  w.bytes = off;
+  return w;
+}
+
+int sample_chunks(int B, int V, int* chunk) {
+  int W = (512 + B - 1) / B;
+  if (W > 64) W = 64;
+  if (W < 1) W = 1;
+  int ch = (V + W - 1) / W;
+  ch = (ch + 1023) / 1024 * 1024;
+  *chunk = ch;
+  return (V + ch - 1) / ch;
+}
+
+hipError_t launch_sample(const float* logits, int B, int V, const float* temperature,
+                         const float* top_p, const int32_t* top_k, const float* u, int32_t* tokens,
+                         const SampleWs& ws, int W, int chunk, hipStream_t st) {
+  SArgs a{};
+  a.logits = logits;
+  a.B = B;
+  a.V = V;
+  a.temperature = temperature;
+  a.top_p = top_p;
+  a.top_k = top_k;
+  a.u = u;
+  a.tokens = tokens;
+  a.w = ws;
+  a.W = W;
+  a.chunk = chunk;
+  const dim3 grid(W, B);
+  sample_k0<<<grid, kSThreads, 0, st>>>(a);
+  sample_k1<<<grid, kSThreads, 0, st>>>(a);
+  sample_k2<<<grid, kSThreads, 0, st>>>(a);
+  sample_k3<<<grid, kSThreads, 0, st>>>(a);
+  sample_k4<<<grid, kSThreads, 0, st>>>(a);
+  sample_k5<<<grid, kSThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -30,7 +30,7 @@ PAGE_TOKENS = 16
 _ID = {"embed": 1, "final_norm": 2, "attn_norm": 10, "w_qkv": 11, "w_o": 12,
        "mlp_norm": 13, "w_gate_up": 14, "w_down": 15, "hidden": 20, "tokens": 21,
        "lens": 22, "pool": 23, "perm": 24, "q": 25, "k_new": 26, "v_new": 27,
-       "prompt": 28}
+       "prompt": 28, "logits": 29, "sample": 30}
 
 LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
 
