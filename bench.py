@@ -231,6 +231,40 @@ def time_layer_b1(torch, pkv, synth, S, reps=10):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def time_sampling(torch, pkv, synth, S, rounds=8, reps=10):
+    """sample_tokens on the step's own logits [B][V] (temperature 1, top-p
+    0.9, no top-k, seeded draws), captured rounds times in a HIP graph;
+    returns (us per call, algorithmic bytes per call)."""
+    B, V = S.logits.shape
+    r = synth.rng(1002, "sample")
+    T = torch.ones(B, dtype=torch.float32, device="cuda")
+    p = torch.full((B,), 0.9, dtype=torch.float32, device="cuda")
+    k = torch.zeros(B, dtype=torch.int32, device="cuda")
+    u = torch.from_numpy(r.random(size=B).astype(np.float32)).cuda()
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = pkv.alloc_workspace(pkv.sample_workspace_bytes(B, V))
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        pkv.sample_tokens(S.logits, T, p, k, u, out, ws, cap)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(rounds):
+                pkv.sample_tokens(S.logits, T, p, k, u, out, ws, cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    # the logits once, the per-sequence parameters and the tokens
+    return e0.elapsed_time(e1) * 1e3 / (reps * rounds), B * V * 4 + B * 4 * 5
+
+
 def prefill_flops(shape, start, T):
     """Algorithmic FLOPs of one prefill: every prompt token through every
     layer's projections (2 per weight), causal attention (QK and PV, 2 each
@@ -474,6 +508,14 @@ def main():
                     "achieved": round(l_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(l_gbs / HBM_PEAK_GBS, 4)}
 
+    s_us, s_bytes = time_sampling(torch, pkv, synth, S)
+    log("sampling: %.2f us per call (graph), %.1f MB -> %.0f GB/s" % (s_us, s_bytes / 1e6, s_bytes / (s_us * 1e3)))
+    sampling = {"workload": "sample_tokens on the step's logits, %d x %d FP32, temperature 1, top-p 0.9, "
+                            "HIP graph" % tuple(S.logits.shape),
+                "us": round(s_us, 3), "bound": "hbm", "algorithmic_bytes": s_bytes,
+                "achieved": round(s_bytes / (s_us * 1e3), 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(s_bytes / (s_us * 1e3) / HBM_PEAK_GBS, 5)}
+
     prefill = None
     if args.prefill_tokens > 0:
         p_ms, p_flops = time_prefill(torch, pkv, synth, S, args.prefill_tokens)
@@ -527,6 +569,7 @@ def main():
         },
         "layer_b1_roofline": layer_b1,
         "prefill": prefill,
+        "sampling": sampling,
         "cpu_baseline": None,
     }
 

@@ -82,8 +82,10 @@ __device__ __forceinline__ uint64_t fixed_mass(float l, float m, float c) {
   return (uint64_t)(e * 4294967296.0f);
 }
 
-// The chunk of workgroup (b, w): elements [e0, e1) of sequence b; thread t
-// takes E consecutive ones.
+// The chunk of workgroup (b, w): elements [e0, e1) of sequence b.  Passes
+// whose result does not depend on order read it coalesced (thread t takes
+// e0 + t, e0 + t + 256, ...); the draw, which walks vocabulary order, gives
+// thread t the E consecutive elements from e0 + t E.
 struct Chunk {
   const float* row;
   int e0, e1, E;
@@ -103,6 +105,25 @@ __device__ __forceinline__ void clear_words(uint32_t* p, int n, int w, int W) {
   for (int i = w * kSThreads + (int)threadIdx.x; i < n; i += W * kSThreads) p[i] = 0u;
 }
 
+// Inclusive scan over the workgroup's threads in thread order: within a
+// wave by shuffles, then the sums of the waves before (one barrier pair).
+template <typename T>
+__device__ __forceinline__ T wg_scan(T v) {
+  __shared__ T s_wave[kSThreads / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) s_wave[wv] = v;
+  __syncthreads();
+  T add = 0;
+  for (int i = 0; i < wv; ++i) add += s_wave[i];
+  __syncthreads();
+  return v + add;
+}
+
 // ---- per-sequence choice state, stored between launches
 struct Choice {
   uint32_t prefix;    // key bits fixed so far
@@ -118,8 +139,6 @@ __device__ __forceinline__ Choice* choices(const SampleWs& w) { return (Choice*)
 // count reaches k_rem or the mass reaches m_rem; update the choice.  Every
 // thread of the workgroup calls it and gets the same result.
 __device__ Choice choose(const uint32_t* cnt, const uint64_t* mass, Choice c, int bits) {
-  __shared__ uint32_t s_cnt[kSThreads];
-  __shared__ uint64_t s_mass[kSThreads];
   __shared__ Choice s_out;
   constexpr int PER = kBuckets / kSThreads;  // 8 buckets per thread, top first
   const int t = threadIdx.x;
@@ -131,20 +150,9 @@ __device__ Choice choose(const uint32_t* cnt, const uint64_t* mass, Choice c, in
     lc += cnt[top - i];
     lm += mass[top - i];
   }
-  s_cnt[t] = lc;
-  s_mass[t] = lm;
-  __syncthreads();
-  // inclusive scan over threads (thread order = descending buckets)
-  for (int off = 1; off < kSThreads; off <<= 1) {
-    const uint32_t oc = t >= off ? s_cnt[t - off] : 0u;
-    const uint64_t om = t >= off ? s_mass[t - off] : 0ull;
-    __syncthreads();
-    s_cnt[t] += oc;
-    s_mass[t] += om;
-    __syncthreads();
-  }
-  const uint32_t inc_c = s_cnt[t];
-  const uint64_t inc_m = s_mass[t];
+  // inclusive scans over threads (thread order = descending buckets)
+  const uint32_t inc_c = wg_scan(lc);
+  const uint64_t inc_m = wg_scan(lm);
   const uint32_t exc_c = inc_c - lc;
   const uint64_t exc_m = inc_m - lm;
   const bool before = exc_c >= c.k_rem || exc_m >= c.m_rem;
@@ -188,18 +196,25 @@ __device__ void histogram(const SArgs& a, const Chunk& ch, int level, uint32_t p
   if (t == 0) h_sum = 0ull;
   __syncthreads();
   uint64_t ls = 0;
-  const int base = ch.e0 + t * ch.E;
-  for (int j = 0; j < ch.E; ++j) {
-    const int e = base + j;
-    if (e >= ch.e1) break;
-    const float l = ch.row[e];
-    const uint32_t key = skey(l);
-    const uint64_t f = fixed_mass(l, m, c);
-    ls += f;
-    if (in_prefix(key, level, prefix)) {
-      const int d = digit(key, level);
-      atomicAdd(&h_cnt[d], 1u);
-      atomicAdd((unsigned long long*)&h_mass[d], (unsigned long long)f);
+  for (int e0 = ch.e0 + t; e0 < ch.e1; e0 += 8 * kSThreads) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i * kSThreads;
+      v[i] = e < ch.e1 ? ch.row[e] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (e0 + i * kSThreads >= ch.e1) break;
+      const float l = v[i];
+      const uint32_t key = skey(l);
+      const uint64_t f = fixed_mass(l, m, c);
+      ls += f;
+      if (in_prefix(key, level, prefix)) {
+        const int d = digit(key, level);
+        atomicAdd(&h_cnt[d], 1u);
+        atomicAdd((unsigned long long*)&h_mass[d], (unsigned long long)f);
+      }
     }
   }
   if (gsum) atomicAdd((unsigned long long*)&h_sum, (unsigned long long)ls);
@@ -212,10 +227,19 @@ __device__ void histogram(const SArgs& a, const Chunk& ch, int level, uint32_t p
   if (gsum && t == 0) atomicAdd((unsigned long long*)gsum, (unsigned long long)h_sum);
 }
 
-__device__ __forceinline__ float seq_max(const SArgs& a, int b) {
-  float m = -INFINITY;
-  for (int i = 0; i < a.W; ++i) m = fmaxf(m, a.w.wmax[(size_t)b * a.W + i]);
-  return m;
+// The sequence's maximum logit from K0's chunk maxima: one load per chunk
+// by as many threads, one round trip (W <= 64).
+__device__ float seq_max(const SArgs& a, int b) {
+  __shared__ float s_res;
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const float v = t < a.W ? a.w.wmax[(size_t)b * a.W + t] : -INFINITY;
+    float m = v;
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (t == 0) s_res = m;
+  }
+  __syncthreads();
+  return s_res;
 }
 
 __global__ __launch_bounds__(kSThreads) void sample_k0(const SArgs a) {
@@ -223,10 +247,15 @@ __global__ __launch_bounds__(kSThreads) void sample_k0(const SArgs a) {
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const Chunk ch = chunk_of(a, b, w);
   float m = -INFINITY;
-  const int base = ch.e0 + t * ch.E;
-  for (int j = 0; j < ch.E; ++j) {
-    const int e = base + j;
-    if (e < ch.e1) m = fmaxf(m, ch.row[e]);
+  for (int e0 = ch.e0 + t; e0 < ch.e1; e0 += 8 * kSThreads) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i * kSThreads;
+      v[i] = e < ch.e1 ? ch.row[e] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, v[i]);
   }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((t & 63) == 0) red[t >> 6] = m;
@@ -299,6 +328,13 @@ struct Nucleus {
   uint32_t tau, ties;
   uint64_t f_tau, m_above;
 };
+static_assert(sizeof(Nucleus) <= kSampleChoiceBytes, "nucleus record size");
+
+// K4 stores each sequence's nucleus for K5, in the third third of the
+// choice records ([3][B] records of kSampleChoiceBytes).
+__device__ __forceinline__ Nucleus* nuclei(const SampleWs& w, int B) {
+  return (Nucleus*)((char*)w.choice + (size_t)2 * B * kSampleChoiceBytes);
+}
 
 __device__ Nucleus nucleus(const SArgs& a, int b) {
   const uint32_t* cnt3 = a.w.cnt + ((size_t)b * 3 + 2) * kBuckets;
@@ -328,16 +364,23 @@ __global__ __launch_bounds__(kSThreads) void sample_k4(const SArgs a) {
   const Chunk ch = chunk_of(a, b, w);
   const float m = seq_max(a, b), c = inv_temp(a, b);
   const Nucleus nu = nucleus(a, b);
+  if (w == 0 && t == 0) nuclei(a.w, a.B)[b] = nu;
   uint64_t mg = 0;
   uint32_t ties = 0;
-  const int base = ch.e0 + t * ch.E;
-  for (int j = 0; j < ch.E; ++j) {
-    const int e = base + j;
-    if (e >= ch.e1) break;
-    const float l = ch.row[e];
-    const uint32_t key = skey(l);
-    if (key > nu.tau) mg += fixed_mass(l, m, c);
-    ties += key == nu.tau;
+  for (int e0 = ch.e0 + t; e0 < ch.e1; e0 += 8 * kSThreads) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + i * kSThreads;
+      v[i] = e < ch.e1 ? ch.row[e] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (e0 + i * kSThreads >= ch.e1) break;
+      const uint32_t key = skey(v[i]);
+      if (key > nu.tau) mg += fixed_mass(v[i], m, c);
+      ties += key == nu.tau;
+    }
   }
   for (int o = 32; o > 0; o >>= 1) {
     mg += __shfl_xor(mg, o);
@@ -364,17 +407,24 @@ __global__ __launch_bounds__(kSThreads) void sample_k4(const SArgs a) {
 // are walked chunk by chunk, then thread by thread, then element by element
 // until their cumulative mass exceeds r.
 __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
-  __shared__ uint64_t s_m[kSThreads];
-  __shared__ uint32_t s_t[kSThreads];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
-  const Nucleus nu = nucleus(a, b);
-  // kept mass of every chunk, and where this chunk's starts
+  const Nucleus nu = nuclei(a.w, a.B)[b];
+  // kept mass of every chunk (chunk i keeps its ties while the ties of
+  // chunks before it number fewer than nu.ties), and where this chunk's
+  // starts; the per-chunk records come in with one load per thread
+  __shared__ uint64_t s_wm[64];
+  __shared__ uint32_t s_wt[64];
+  if (t < 64) {
+    s_wm[t] = t < a.W ? a.w.wmass[(size_t)b * a.W + t] : 0ull;
+    s_wt[t] = t < a.W ? a.w.wties[(size_t)b * a.W + t] : 0u;
+  }
+  __syncthreads();
   uint64_t total = 0, before = 0, mine = 0;
   uint32_t ties_before = 0, tie_acc = 0;
   for (int i = 0; i < a.W; ++i) {
-    const uint32_t ti = a.w.wties[(size_t)b * a.W + i];
+    const uint32_t ti = s_wt[i];
     const uint32_t kt = tie_acc >= nu.ties ? 0u : min(ti, nu.ties - tie_acc);
-    const uint64_t km = a.w.wmass[(size_t)b * a.W + i] + (uint64_t)kt * nu.f_tau;
+    const uint64_t km = s_wm[i] + (uint64_t)kt * nu.f_tau;
     if (i < w) {
       before += km;
       ties_before += ti;
@@ -391,57 +441,52 @@ __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
   const float m = seq_max(a, b), c = inv_temp(a, b);
   // this thread's ties (key == tau), scanned over the threads in vocabulary
   // order: which of them are kept depends on the ties before it
-  uint32_t lt = 0;
   const int base = ch.e0 + t * ch.E;
-  for (int j = 0; j < ch.E; ++j) {
-    const int e = base + j;
-    if (e >= ch.e1) break;
-    lt += skey(ch.row[e]) == nu.tau;
+  const int end = min(base + ch.E, ch.e1);
+  // this thread's elements, 8 loads in flight at a time
+  auto load8 = [&](int e0, float* v) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = e0 + i < end ? ch.row[e0 + i] : -INFINITY;
+  };
+  uint32_t lt = 0;
+  for (int e0 = base; e0 < end; e0 += 8) {
+    float v[8];
+    load8(e0, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lt += e0 + i < end && skey(v[i]) == nu.tau;
   }
-  s_t[t] = lt;
-  __syncthreads();
-  for (int off = 1; off < kSThreads; off <<= 1) {
-    const uint32_t ot = t >= off ? s_t[t - off] : 0u;
-    __syncthreads();
-    s_t[t] += ot;
-    __syncthreads();
-  }
+  const uint32_t lt_inc = wg_scan(lt);
   // its kept mass, then scanned the same way
-  const uint32_t tb = ties_before + s_t[t] - lt;
+  const uint32_t tb = ties_before + lt_inc - lt;
+  // mass of element e (in vocabulary order within the thread): kept ties
+  // are counted by tk
+  auto kept_mass = [&](float l, uint32_t& tk) -> uint64_t {
+    const uint32_t key = skey(l);
+    if (key == nu.tau) return (tb + tk++ < nu.ties) ? nu.f_tau : 0ull;
+    return key > nu.tau ? fixed_mass(l, m, c) : 0ull;
+  };
   uint64_t km = 0;
   uint32_t tk = 0;
-  for (int j = 0; j < ch.E; ++j) {
-    const int e = base + j;
-    if (e >= ch.e1) break;
-    const uint32_t key = skey(ch.row[e]);
-    if (key == nu.tau) km += (tb + tk++ < nu.ties) ? nu.f_tau : 0ull;
-    else if (key > nu.tau) km += fixed_mass(ch.row[e], m, c);
+  for (int e0 = base; e0 < end; e0 += 8) {
+    float v[8];
+    load8(e0, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (e0 + i < end) km += kept_mass(v[i], tk);
   }
-  __syncthreads();
-  s_m[t] = km;
-  __syncthreads();
-  for (int off = 1; off < kSThreads; off <<= 1) {
-    const uint64_t om = t >= off ? s_m[t - off] : 0ull;
-    __syncthreads();
-    s_m[t] += om;
-    __syncthreads();
-  }
-  const uint64_t excl = before + s_m[t] - km;
+  const uint64_t excl = before + wg_scan(km) - km;
   if (!(r >= excl && r < excl + km)) return;
   uint64_t acc = excl;
   tk = 0;
-  for (int j = 0; j < ch.E; ++j) {
-    const int e = base + j;
-    if (e >= ch.e1) break;
-    const float l = ch.row[e];
-    const uint32_t key = skey(l);
-    uint64_t f = 0;
-    if (key == nu.tau) f = (tb + tk++ < nu.ties) ? nu.f_tau : 0ull;
-    else if (key > nu.tau) f = fixed_mass(l, m, c);
-    acc += f;
-    if (acc > r) {
-      a.tokens[b] = e;
-      return;
+  for (int e0 = base; e0 < end; e0 += 8) {
+    float v[8];
+    load8(e0, v);
+    for (int i = 0; i < 8 && e0 + i < end; ++i) {
+      acc += kept_mass(v[i], tk);
+      if (acc > r) {
+        a.tokens[b] = e0 + i;
+        return;
+      }
     }
   }
 }
@@ -456,7 +501,7 @@ SampleWs sample_ws_carve(void* base, int B, int W) {
   w.cnt = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * 3 * kBuckets);
   w.mass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * 3 * kBuckets);
   w.sum = (uint64_t*)take(sizeof(uint64_t) * (size_t)B);
-  w.choice = (void*)take(sizeof(Choice) * (size_t)B * 2);
+  w.choice = (void*)take((size_t)kSampleChoiceBytes * B * 3);
   w.wmax = (float*)take(sizeof(float) * (size_t)B * W);
   w.wmass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * W);
   w.wties = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * W);
