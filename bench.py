@@ -101,20 +101,30 @@ def load_traffic(bytes_per_launch):
             "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
 
 
+class HostInputs:
+    """The workload's host arrays (drawn before the GPU is touched, so the
+    oracle's worker processes can be forked from a GPU-free process)."""
+
+    def __init__(self, synth):
+        t0 = time.time()
+        self.wl = synth.bench_step()
+        self.shape = self.wl.shape
+        self.weights = synth.model_weights(self.shape, 1002)
+        log("inputs drawn in %.1fs (pool %d pages, %.0f MiB)" % (
+            time.time() - t0, self.wl.num_pages, self.wl.pool.nbytes / 2 ** 20))
+
+
 class Setup:
     """Device-resident inputs of the workload."""
 
-    def __init__(self, torch, pkv, synth, with_host=False):
-        t0 = time.time()
-        wl = synth.bench_step()
-        shape = wl.shape
+    def __init__(self, torch, pkv, synth, host):
+        wl, shape = host.wl, host.shape
         self.wl, self.shape = wl, shape
-        self.weights = synth.model_weights(shape, 1002)
-        log("inputs drawn in %.1fs (pool %d pages, %.0f MiB)" % (
-            time.time() - t0, wl.num_pages, wl.pool.nbytes / 2 ** 20))
+        self.weights = host.weights
         self.max_pos = int(wl.positions.max()) + 1
         self.cfg = pkv.make_config(shape, max_pos=self.max_pos)
-        self.model = pkv.upload_model(self.weights, shape.theta, self.max_pos)
+        # RoPE tables for 4097 positions: the batch-64 step reuses this model
+        self.model = pkv.upload_model(self.weights, shape.theta, max(self.max_pos, 4097))
         self.pool_t = pkv.to_device(wl.pool)
         self.pool = pkv.kv_pool_create(self.pool_t, shape.kv_heads)
         self.bts = pkv.to_device(wl.block_tables)
@@ -125,8 +135,6 @@ class Setup:
         self.next = torch.empty(B, dtype=torch.int32, device="cuda")
         self.ws = pkv.alloc_workspace(pkv.workspace_bytes(self.cfg, B, wl.max_pages))
         torch.cuda.synchronize()
-        if not with_host:
-            self.weights = None
 
     def step(self, pkv):
         pkv.decode_step(self.cfg, self.model, self.pool, self.bts, self.pos, self.tokens, self.logits,
@@ -231,6 +239,110 @@ def time_layer_b1(torch, pkv, synth, S, reps=10):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def pct(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.percentile(a, 50)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def timed_replays(torch, run, reps):
+    """Each replay between its own pair of events on the current stream: (ms list)."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def capture(torch, fn):
+    """fn(stream) run once eagerly, then captured in a HIP graph."""
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        fn(cap)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            fn(cap)
+    torch.cuda.synchronize()
+    return graph
+
+
+def layer_bytes(shape, n_attend, q_bytes=4):
+    """One decoder layer at batch 1 attending n_attend cached tokens plus the new one."""
+    return (2 * shape.layer_param_count() + attention_bytes([n_attend + 1], shape.heads, shape.kv_heads, q_bytes)
+            + shape.kv_heads * shape.head_dim * 2 * 2 + 2 * shape.hidden * 4)
+
+
+def time_layer_c1(torch, pkv, synth, reps=20):
+    """The Qwen2.5-0.5B layer at batch 1, position 127, as a chain of 16
+    distinct layers (16 weight draws, 16 page sets) in one HIP graph, so the
+    layer's 30 MB are not served from the Infinity Cache; per-layer time =
+    replay / 16.  Returns (list of per-layer ms per replay, bytes per layer)."""
+    shape = synth.QWEN05
+    L = 16
+    wl = synth.decode_workload("c1 chain", shape, 1001, [127], layers=L)
+    layers = [pkv.upload_layer(synth.layer_weights(shape, 1001, l)) for l in range(L)]
+    c, sn = pkv.rope_table(shape.theta, 128)
+    cfg = pkv.make_config(shape, max_pos=128, layers=1)
+    pool_t = pkv.to_device(wl.pool)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    bts = [pkv.to_device(wl.block_tables[l]) for l in range(L)]
+    pos = pkv.to_device(wl.positions)
+    hidden = torch.from_numpy(synth.rng(1001, "hidden").standard_normal((1, shape.hidden), dtype=np.float32)).cuda()
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, 1, wl.max_pages))
+
+    def run(stream):
+        for l in range(L):
+            pkv.decoder_layer_decode(cfg, layers[l], c, sn, pool, bts[l], pos, hidden, ws, stream)
+
+    graph = capture(torch, run)
+    for _ in range(3):
+        graph.replay()
+    ms = timed_replays(torch, graph.replay, reps)
+    assert pkv.device_error(ws) == 0
+    return [m / L for m in ms], layer_bytes(shape, 127)
+
+
+def time_step_cfg(torch, pkv, synth, wl, shape, model, max_pos, reps=10):
+    """decode_step of a workload in a HIP graph: (ms list, step bytes)."""
+    cfg = pkv.make_config(shape, max_pos=max_pos)
+    pool_t = pkv.to_device(wl.pool)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    bts = pkv.to_device(wl.block_tables)
+    pos = pkv.to_device(wl.positions)
+    tok = pkv.to_device(wl.extra["tokens"])
+    B = wl.batch
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, wl.max_pages))
+    graph = capture(torch, lambda st: pkv.decode_step(cfg, model, pool, bts, pos, tok, logits, nxt, ws, st))
+    for _ in range(2):
+        graph.replay()
+    ms = timed_replays(torch, graph.replay, reps)
+    assert pkv.device_error(ws) == 0
+    del pool_t
+    return ms, step_bytes(shape, wl.lens)
+
+
+def ceilings(torch, nbytes=1 << 30, reps=10):
+    """Plain streaming rates on this GPU: a device copy (bytes read + written)
+    and a read-only reduction (torch's own kernels), 1 GiB each."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+    y = torch.empty_like(x)
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    y.copy_(x)
+    torch.sum(x, dim=0, out=out)
+    torch.cuda.synchronize()
+    cp = timed_replays(torch, lambda: y.copy_(x), reps)
+    rd = timed_replays(torch, lambda: torch.sum(x, dim=0, out=out), reps)
+    del x, y
+    return 2 * nbytes / (min(cp) * 1e-3) / 1e9, nbytes / (min(rd) * 1e-3) / 1e9
+
+
 def time_sampling(torch, pkv, synth, S, rounds=8, reps=10):
     """sample_tokens on the step's own logits [B][V] (temperature 1, top-p
     0.9, no top-k, seeded draws), captured rounds times in a HIP graph;
@@ -332,15 +444,45 @@ def prefill_only(torch, pkv, synth, T):
                       "algorithmic_tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 5)}))
 
 
-def cpu_baseline(S, seqs):
+_CPU_STATE = None
+
+
+def _oracle_seq(b):
+    """The oracle's full step for sequence b of the bench workload (worker)."""
     import oracle
-    wl = S.wl
-    geo = oracle.PoolGeometry(S.shape.kv_heads, S.shape.head_dim)
-    t0 = time.perf_counter()
-    _, nxt, _, _ = oracle.decode_step_paged(S.shape, S.weights, wl.pool, geo, wl.block_tables,
-                                            wl.positions, wl.extra["tokens"], seqs=seqs)
-    dt = time.perf_counter() - t0
-    return dt, nxt
+    shape, weights, wl = _CPU_STATE
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
+    _, nxt, _, _ = oracle.decode_step_paged(shape, weights, wl.pool, geo, wl.block_tables,
+                                            wl.positions, wl.extra["tokens"], seqs=[b])
+    return int(nxt[b])
+
+
+def _pin_core0():
+    os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+
+
+def cpu_baseline(host, single_seqs):
+    """The oracle on this host's cores, in forked worker processes: one
+    process pinned to one core over `single_seqs` sequences, then one process
+    per core (at most 16) over every sequence of the batch.  Returns
+    (single seconds, tokens), (all-cores seconds, processes, tokens)."""
+    import multiprocessing as mp
+    import oracle
+    global _CPU_STATE
+    oracle._load()  # build / load the C oracle once, before forking
+    _CPU_STATE = (host.shape, host.weights, host.wl)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(1, initializer=_pin_core0) as pool:
+        t0 = time.perf_counter()
+        single = pool.map(_oracle_seq, single_seqs, chunksize=1)
+        d1 = time.perf_counter() - t0
+    B = host.wl.batch
+    n = max(1, min(16, len(os.sched_getaffinity(0)), B))
+    with ctx.Pool(n) as pool:
+        t0 = time.perf_counter()
+        allt = pool.map(_oracle_seq, range(B), chunksize=1)
+        dn = time.perf_counter() - t0
+    return (d1, single), (dn, n, allt)
 
 
 def attention_only(torch, pkv, synth, rounds):
@@ -423,6 +565,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     ap.add_argument("--no-layer-b1", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the c1 layer chain, the batch-64/128 steps and the copy ceilings")
     ap.add_argument("--prefill-tokens", type=int, default=512, help="0 skips the prefill timing")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the prefill alone (the step's model, no decode workload)")
@@ -439,18 +583,30 @@ def main():
     import paged_kv_transformer_amd as pkv
     import synth
 
+    if args.attention_only or args.prefill_only:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(2)
+        torch.cuda.set_device(0)
+        if args.attention_only:
+            attention_only(torch, pkv, synth, args.attn_rounds)
+        else:
+            prefill_only(torch, pkv, synth, args.prefill_tokens)
+        return
+
+    host = HostInputs(synth)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle first, in processes forked before this one touches the GPU
+        single_seqs = list(range(min(args.cpu_seqs, host.wl.batch)))
+        cpu = cpu_baseline(host, single_seqs)
+        log("oracle: %d sequences on 1 core in %.1fs; %d sequences on %d processes in %.1fs" % (
+            len(single_seqs), cpu[0][0], host.wl.batch, cpu[1][1], cpu[1][0]))
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
-    if args.attention_only:
-        attention_only(torch, pkv, synth, args.attn_rounds)
-        return
-    if args.prefill_only:
-        prefill_only(torch, pkv, synth, args.prefill_tokens)
-        return
-
-    S = Setup(torch, pkv, synth, with_host=not args.no_cpu_baseline)
+    S = Setup(torch, pkv, synth, host)
     shape, wl = S.shape, S.wl
     B = wl.batch
 
@@ -486,6 +642,7 @@ def main():
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
     log("step: %.3f ms (events), %.3f ms (wall)" % (ms, wall * 1e3 / args.steps))
+    step_pct = pct(timed_replays(torch, run, max(args.steps, 20)))
     assert pkv.device_error(S.ws) == 0
     assert torch.equal(S.next, ref_next), "replayed steps changed the next tokens"
 
@@ -515,6 +672,41 @@ def main():
                 "us": round(s_us, 3), "bound": "hbm", "algorithmic_bytes": s_bytes,
                 "achieved": round(s_bytes / (s_us * 1e3), 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(s_bytes / (s_us * 1e3) / HBM_PEAK_GBS, 5)}
+
+    extra = {}
+    if not args.no_extra_configs:
+        c1_ms, c1_bytes = time_layer_c1(torch, pkv, synth)
+        c1_us = float(np.median(c1_ms)) * 1e3
+        c1_gbs = c1_bytes / (c1_us * 1e3)
+        log("c1 layer chain: %.2f us per layer (median), %.2f MB -> %.0f GB/s" % (c1_us, c1_bytes / 1e6, c1_gbs))
+        extra["layer_c1"] = {
+            "workload": "decoder_layer_decode, qwen2.5-0.5b-shape layer, batch 1, position 127, "
+                        "16 distinct layers chained in one HIP graph (per-layer = replay / 16)",
+            "bound": "hbm", "algorithmic_bytes": int(c1_bytes), "us_per_layer": pct([m * 1e3 for m in c1_ms]),
+            "achieved": round(c1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(c1_gbs / HBM_PEAK_GBS, 4), "gate_frac": 0.6}
+        for name, mk, shp, model_fn in (
+                ("step_c4", synth.c4_step, synth.LLAMA1B, lambda: S.model),
+                ("step_c5", synth.c5_step, synth.QWEN05,
+                 lambda: pkv.upload_model(synth.model_weights(synth.QWEN05, 1005), synth.QWEN05.theta, 4097))):
+            wlx = mk()
+            mp_ = int(wlx.positions.max()) + 1
+            model = model_fn()
+            xs, xb = time_step_cfg(torch, pkv, synth, wlx, shp, model, mp_)
+            xm = float(np.median(xs))
+            log("%s: %.3f ms per step (median), batch %d -> %.0f tokens/s, %.0f GB/s" % (
+                name, xm, wlx.batch, wlx.batch / (xm * 1e-3), xb / (xm * 1e-3) / 1e9))
+            extra[name] = {"workload": wlx.name, "batch": int(wlx.batch), "ms_per_step": pct(xs),
+                           "tokens_per_s": round(wlx.batch / (xm * 1e-3), 1), "bound": "hbm",
+                           "algorithmic_bytes": int(xb), "achieved": round(xb / (xm * 1e-3) / 1e9, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(xb / (xm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del model, wlx
+            torch.cuda.empty_cache()
+        cp_gbs, rd_gbs = ceilings(torch)
+        log("ceilings: device copy %.0f GB/s (read + write), read-only reduction %.0f GB/s" % (cp_gbs, rd_gbs))
+        extra["ceiling"] = {"copy_gbs": round(cp_gbs, 1), "read_gbs": round(rd_gbs, 1),
+                            "note": "1 GiB torch copy (bytes read + written) and torch.sum, best of 10"}
 
     prefill = None
     if args.prefill_tokens > 0:
@@ -567,22 +759,28 @@ def main():
             "bound": "hbm", "algorithmic_bytes": int(sbytes), "achieved": round(step_gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
         },
+        "step_ms_percentiles": step_pct,
         "layer_b1_roofline": layer_b1,
         "prefill": prefill,
         "sampling": sampling,
+        **extra,
         "cpu_baseline": None,
     }
 
-    if not args.no_cpu_baseline:
-        seqs = list(range(min(args.cpu_seqs, B)))
-        dt, nxt = cpu_baseline(S, seqs)
+    if cpu is not None:
+        (d1, single), (dn, n, allt) = cpu
+        seqs = list(range(len(single)))
         got = S.next.cpu().numpy()
-        log("oracle: %d sequences in %.1fs; tokens %s vs GPU %s" % (len(seqs), dt, nxt[seqs].tolist(),
-                                                                      got[seqs].tolist()))
+        log("oracle tokens %s vs GPU %s" % (allt, got.tolist()))
         result["cpu_baseline"] = {
-            "value": round(len(seqs) / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "value": round(len(seqs) / d1, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "the full 16-layer step (embedding, layers, LM head, argmax) for sequences %s "
-                      "of the batch, single-threaded FP32 C oracle; %.1f s" % (seqs, dt),
+                      "of the batch, single-threaded FP32 C oracle in one process pinned to one core; "
+                      "%.1f s" % (seqs, d1),
+            "all_cores": {"value": round(len(allt) / dn, 4), "unit": "tokens/s", "cores": n,
+                          "sample": "all %d sequences of the step, one oracle process per core, %.1f s"
+                                    % (len(allt), dn)},
+            "oracle_matches_gpu_tokens": int(sum(int(a == b) for a, b in zip(allt, got.tolist()))),
         }
     print(json.dumps(result), flush=True)
 
