@@ -68,6 +68,8 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
+size_t layer_ws_bytes(const pkv_config* c, int batch, int max_pages);
+
 // Common checks of decoder_layer_decode / decode_step.
 int check_layer_call(const pkv_config* cfg, const pkv_pool* pool, const float* rope_cos,
                      const float* rope_sin, const int32_t* bt, int32_t max_pages,
@@ -81,10 +83,7 @@ int check_layer_call(const pkv_config* cfg, const pkv_pool* pool, const float* r
   if (batch > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
   if (!rope_cos || !rope_sin || !bt || !positions || !ws) return -EINVAL;
   if (!aligned(ws, 256)) return -EINVAL;
-  const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
-                               cfg->num_key_value_heads, cfg->intermediate_size,
-                               cfg->vocab_size, max_pages, true);
-  if (ws_bytes < L.total) return -ENOSPC;
+  if (ws_bytes < layer_ws_bytes(cfg, batch, max_pages)) return -ENOSPC;
   return 0;
 }
 
@@ -233,6 +232,174 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Large batches (kTiledMinBatch sequences or more): the projections run as
+// the tiled matrix-core GEMMs of the prefill path, which read every weight
+// once per step and keep the activations in LDS, where the weight-streaming
+// kernel would re-read 64 FP32 activation columns from L2 for every 16 weight
+// rows.  Activations travel as packed BF16 hi/lo pairs; each residual
+// projection splits K into FP32 partials and one per-token kernel adds the
+// residual and the splits and applies the next RMSNorm.
+constexpr int kTiledMinBatch = 64;
+
+struct TiledLayout {
+  size_t err, attn_part, q, x, xb, ob, act, part, amax, total;
+};
+
+PgemmPlan tiled_o_plan(const pkv_config* c, int B) {
+  return plan_prefill_gemm(c->hidden_size / 16, B, c->num_attention_heads * kHeadDim, true);
+}
+PgemmPlan tiled_down_plan(const pkv_config* c, int B) {
+  return plan_prefill_gemm(c->hidden_size / 16, B, c->intermediate_size, true);
+}
+PgemmPlan tiled_lm_plan(const pkv_config* c, int B) {
+  return plan_prefill_gemm((c->vocab_size + 15) / 16, B, c->hidden_size, false);
+}
+
+// Row tiles of the tiled LM head (each leaves two argmax keys per token).
+int lm_row_tiles(const pkv_config* c, int B) {
+  const PgemmPlan p = tiled_lm_plan(c, B);
+  const int groups = (c->vocab_size + 15) / 16;
+  return (groups + 2 * p.rg - 1) / (2 * p.rg);
+}
+
+TiledLayout tiled_layout(const pkv_config* c, int B, int max_pages) {
+  const size_t H = c->hidden_size, I = c->intermediate_size;
+  const size_t QD = (size_t)c->num_attention_heads * kHeadDim;
+  TiledLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+  L.err = take(256);
+  L.attn_part = take(sizeof(float) * (size_t)B * c->num_key_value_heads * attn_max_splits(max_pages) *
+                     kAttnRec);
+  L.q = take(2 * (size_t)B * QD * 2);
+  L.x = take(sizeof(float) * B * H);
+  L.xb = take(2 * (size_t)packed_pair_elems(B, (int)H));
+  L.ob = take(2 * (size_t)packed_pair_elems(B, (int)QD));
+  L.act = take(2 * (size_t)packed_pair_elems(B, (int)I));
+  const int ks = tiled_o_plan(c, B).ks > tiled_down_plan(c, B).ks ? tiled_o_plan(c, B).ks
+                                                                    : tiled_down_plan(c, B).ks;
+  L.part = take(sizeof(float) * (size_t)ks * B * H);
+  if (c->vocab_size > 0) L.amax = take(sizeof(unsigned long long) * 2 * (size_t)lm_row_tiles(c, B) * B);
+  L.total = off;
+  return L;
+}
+
+// Workspace bytes of a layer call or step of `batch` sequences.
+size_t layer_ws_bytes(const pkv_config* c, int batch, int max_pages) {
+  if (batch >= kTiledMinBatch) return tiled_layout(c, batch, max_pages).total;
+  return ws_layout(batch, c->hidden_size, c->num_attention_heads, c->num_key_value_heads,
+                   c->intermediate_size, c->vocab_size, max_pages, true)
+      .total;
+}
+
+// One decoder layer over a large batch.  xb holds RMSNorm(x) (attention
+// norm) as hi/lo pairs on entry; x [B][H] FP32 is updated in place, and xb
+// holds RMSNorm(x, next_norm) on exit if next_norm is given.
+int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const float* rope_cos,
+                    const float* rope_sin, const pkv_pool* pool, const int32_t* bt, int32_t max_pages,
+                    const int32_t* pos, int32_t B, float* x, const uint16_t* next_norm, void* ws,
+                    const TiledLayout& L, hipStream_t st) {
+  const int H = cfg->hidden_size, Hq = cfg->num_attention_heads;
+  const int Hkv = cfg->num_key_value_heads, I = cfg->intermediate_size;
+  const int QD = Hq * kHeadDim;
+  const float eps = cfg->rms_norm_eps;
+  uint16_t* q = at<uint16_t>(ws, L.q);
+  uint16_t* xb = at<uint16_t>(ws, L.xb);
+  uint16_t* ob = at<uint16_t>(ws, L.ob);
+  uint16_t* act = at<uint16_t>(ws, L.act);
+  float* part = at<float>(ws, L.part);
+  uint32_t* err = at<uint32_t>(ws, L.err);
+  int rc;
+  PgemmArgs base{};
+  base.T = B;
+  base.err = err;
+  {
+    PgemmArgs a = base;
+    a.W = w->w_qkv;
+    a.w_groups = (Hq + 2 * Hkv) * 4;
+    a.X = xb;
+    a.N = (Hq + 2 * Hkv) * kHeadDim;
+    a.K = H;
+    a.q_split = q;
+    a.pool = (uint16_t*)pool->base;
+    a.page_elems = pool->page_bytes / 2;
+    a.num_pages = pool->num_pages;
+    a.bt = bt;
+    a.bt_row = max_pages;
+    a.bt_stride = max_pages;
+    a.pos = pos;
+    a.max_pos = cfg->max_position_embeddings;
+    a.rcos = rope_cos;
+    a.rsin = rope_sin;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    if ((rc = io(launch_prefill_gemm(EPI_QKV, a, plan_prefill_gemm(a.w_groups, B, H, false), st))))
+      return rc;
+  }
+  {
+    AttnArgs a{};
+    a.q = q;
+    a.pool = (const uint16_t*)pool->base;
+    a.page_elems = pool->page_bytes / 2;
+    a.num_pages = pool->num_pages;
+    a.bt = bt;
+    a.bt_stride = max_pages;
+    a.bt_row = max_pages;
+    a.lens = pos;
+    a.len_add = 1;
+    a.scale = 1.0f / sqrtf((float)kHeadDim);
+    a.out = (float*)ob;
+    a.out_packed = 2;
+    a.part = at<float>(ws, L.attn_part);
+    a.err = err;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.max_splits = attn_max_splits(max_pages);
+    if ((rc = io(launch_attention(a, B, kQSplit, st)))) return rc;
+  }
+  {
+    const PgemmPlan p = tiled_o_plan(cfg, B);
+    PgemmArgs a = base;
+    a.W = w->w_o;
+    a.w_groups = H / 16;
+    a.X = ob;
+    a.N = H;
+    a.K = QD;
+    a.part = part;
+    a.ksplit = p.ks;
+    if ((rc = io(launch_prefill_gemm(EPI_RESID, a, p, st)))) return rc;
+    if ((rc = io(launch_prefill_resid(x, part, p.ks, B, H, w->mlp_norm, eps, xb, st)))) return rc;
+  }
+  {
+    PgemmArgs a = base;
+    a.W = w->w_gate_up;
+    a.w_groups = I / 8;
+    a.X = xb;
+    a.N = 2 * I;
+    a.K = H;
+    a.act = act;
+    a.I = I;
+    if ((rc = io(launch_prefill_gemm(EPI_SWIGLU, a, plan_prefill_gemm(a.w_groups, B, H, false), st))))
+      return rc;
+  }
+  {
+    const PgemmPlan p = tiled_down_plan(cfg, B);
+    PgemmArgs a = base;
+    a.W = w->w_down;
+    a.w_groups = H / 16;
+    a.X = act;
+    a.N = H;
+    a.K = I;
+    a.part = part;
+    a.ksplit = p.ks;
+    if ((rc = io(launch_prefill_gemm(EPI_RESID, a, p, st)))) return rc;
+    if ((rc = io(launch_prefill_resid(x, part, p.ks, B, H, next_norm, eps, xb, st)))) return rc;
+  }
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -280,9 +447,7 @@ size_t pkv_attention_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, 
 
 size_t pkv_workspace_bytes(const pkv_config* cfg, int32_t batch, int32_t max_pages) {
   if (check_cfg(cfg) || batch < 0 || max_pages < 1) return 0;
-  return ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads, cfg->num_key_value_heads,
-                   cfg->intermediate_size, cfg->vocab_size, max_pages, true)
-      .total;
+  return layer_ws_bytes(cfg, batch, max_pages);
 }
 
 int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_heads,
@@ -333,11 +498,20 @@ int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
   if (rc) return rc;
   if (!hidden) return -EINVAL;
   if (batch == 0) return 0;
+  const hipStream_t st = (hipStream_t)stream;
+  if (batch >= kTiledMinBatch) {
+    const TiledLayout T = tiled_layout(cfg, batch, max_pages);
+    if ((rc = io(launch_prefill_norm(hidden, w->attn_norm, cfg->hidden_size, batch, cfg->rms_norm_eps,
+                                     at<uint16_t>(workspace, T.xb), st))))
+      return rc;
+    return run_layer_tiled(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, positions, batch,
+                           hidden, nullptr, workspace, T, st);
+  }
   const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
                                cfg->num_key_value_heads, cfg->intermediate_size,
                                cfg->vocab_size, max_pages, true);
   return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, max_pages, positions,
-                   batch, hidden, nullptr, workspace, L, (hipStream_t)stream);
+                   batch, hidden, nullptr, workspace, L, st);
 }
 
 int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* pool,
@@ -357,6 +531,36 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
   if (batch == 0) return 0;
   const hipStream_t st = (hipStream_t)stream;
   const int H = cfg->hidden_size, V = cfg->vocab_size;
+  if (batch >= kTiledMinBatch) {
+    const TiledLayout T = tiled_layout(cfg, batch, max_pages);
+    float* x = at<float>(workspace, T.x);
+    uint16_t* xb = at<uint16_t>(workspace, T.xb);
+    uint32_t* err = at<uint32_t>(workspace, T.err);
+    const int nl = cfg->num_hidden_layers;
+    if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, nullptr, batch, err, st)))) return rc;
+    if ((rc = io(launch_prefill_norm(x, w->layers[0].attn_norm, H, batch, cfg->rms_norm_eps, xb, st))))
+      return rc;
+    for (int l = 0; l < nl; ++l) {
+      const uint16_t* nn = l + 1 < nl ? w->layers[l + 1].attn_norm : w->final_norm;
+      rc = run_layer_tiled(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool,
+                           block_tables + (size_t)l * batch * max_pages, max_pages, positions, batch, x,
+                           nn, workspace, T, st);
+      if (rc) return rc;
+    }
+    // LM head on the final-normed rows, FP32 logits, argmax
+    PgemmArgs a{};
+    a.W = w->embed;
+    a.w_groups = (V + 15) / 16;
+    a.X = xb;
+    a.N = V;
+    a.K = H;
+    a.T = batch;
+    a.err = err;
+    a.logits = logits;
+    a.amax_part = at<unsigned long long>(workspace, T.amax);
+    if ((rc = io(launch_prefill_gemm(EPI_LOGITS, a, tiled_lm_plan(cfg, batch), st)))) return rc;
+    return io(launch_argmax_finalize(a.amax_part, 2 * lm_row_tiles(cfg, batch), batch, next_tokens, st));
+  }
   const WsLayout L = ws_layout(batch, H, cfg->num_attention_heads, cfg->num_key_value_heads,
                                cfg->intermediate_size, V, max_pages, true);
   float* x = at<float>(workspace, L.x);
@@ -498,7 +702,11 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.page_elems = pool->page_bytes / 2;
       a.num_pages = pool->num_pages;
       a.bt = bt;
+      a.bt_row = 0;
+      a.bt_stride = max_pages;
+      a.pos = nullptr;
       a.start_pos = start_pos;
+      a.max_pos = cfg->max_position_embeddings;
       a.rcos = w->rope_cos;
       a.rsin = w->rope_sin;
       a.Hq = Hq;

@@ -53,13 +53,22 @@ __device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
 }
 
 // Output element idx = g * D + d of kv head kvh of sequence b: plain
-// [B][Hq][D], or packed as the output projection's input ([B][Hq * D]).
+// [B][Hq][D], or packed as the output projection's input ([B][Hq * D]):
+// FP32 for the weight-streaming projection, BF16 hi/lo pairs for the tiled
+// one.
 __device__ __forceinline__ void store_out(const AttnArgs& a, int b, int kvh, int idx, float v) {
   const int k = kvh * a.G * kHeadDim + idx;
-  if (a.out_packed)
-    a.out[packed_act_index(b, k, a.Hq * kHeadDim)] = v;
-  else
-    a.out[(size_t)b * a.Hq * kHeadDim + k] = v;
+  const int QD = a.Hq * kHeadDim;
+  if (a.out_packed == 2) {
+    uint16_t* o = (uint16_t*)a.out;
+    const uint16_t h = to_bf16_bits(v);
+    o[packed_pair_index(b, k, QD, 0)] = h;
+    o[packed_pair_index(b, k, QD, 1)] = to_bf16_bits(v - bf16_lo(h));
+  } else if (a.out_packed) {
+    a.out[packed_act_index(b, k, QD)] = v;
+  } else {
+    a.out[(size_t)b * QD + k] = v;
+  }
 }
 
 // Keep the first `nv` of the four BF16 values in v (the rest -> +0).

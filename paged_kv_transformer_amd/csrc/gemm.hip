@@ -52,8 +52,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// A byte offset past every activation descriptor: they cover at most 32
-// batch columns of at most 65536 FP32 values, 8 MiB.
+// A byte offset past every activation descriptor: they cover at most 64
+// batch columns of at most 65536 FP32 values, 16 MiB.
 constexpr int kOutOfRange = 0x40000000;
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -421,18 +421,23 @@ hipError_t go(const GemmArgs& a, int tiles, hipStream_t st) {
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_t st) {
   hipError_t e = hipErrorInvalidValue;
-  const bool one = p.ct == 1;
+  const int ct = p.ct;
   switch (epi) {
     case EPI_QKV:
       if (a.x_plain)
-        e = one ? go<1, 1, 8, EPI_QKV, true>(a, p.tiles, st) : go<2, 1, 8, EPI_QKV, true>(a, p.tiles, st);
+        e = ct == 1 ? go<1, 1, 8, EPI_QKV, true>(a, p.tiles, st)
+            : ct == 2 ? go<2, 1, 8, EPI_QKV, true>(a, p.tiles, st)
+                      : go<4, 1, 8, EPI_QKV, true>(a, p.tiles, st);
       else
-        e = one ? go<1, 1, 8, EPI_QKV>(a, p.tiles, st) : go<2, 1, 8, EPI_QKV>(a, p.tiles, st);
+        e = ct == 1 ? go<1, 1, 8, EPI_QKV>(a, p.tiles, st)
+            : ct == 2 ? go<2, 1, 8, EPI_QKV>(a, p.tiles, st)
+                      : go<4, 1, 8, EPI_QKV>(a, p.tiles, st);
       break;
     case EPI_RESID:
       if (p.ks > 1) {
-        e = one ? go<1, 2, 4, EPI_RESID>(a, p.tiles * p.ks, st)
-                : go<2, 2, 4, EPI_RESID>(a, p.tiles * p.ks, st);
+        e = ct == 1 ? go<1, 2, 4, EPI_RESID>(a, p.tiles * p.ks, st)
+            : ct == 2 ? go<2, 2, 4, EPI_RESID>(a, p.tiles * p.ks, st)
+                      : go<4, 1, 4, EPI_RESID>(a, p.tiles * p.ks, st);
         if (e != hipSuccess) return e;
         // small blocks: the partial sums are a few MB, spread over enough
         // workgroups that no CU streams more than a few KB of them
@@ -441,17 +446,23 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
                                                           a.out_packed);
         e = hipGetLastError();
       } else {
-        e = one ? go<1, 1, 8, EPI_RESID>(a, p.tiles, st) : go<2, 1, 8, EPI_RESID>(a, p.tiles, st);
+        e = ct == 1 ? go<1, 1, 8, EPI_RESID>(a, p.tiles, st)
+            : ct == 2 ? go<2, 1, 8, EPI_RESID>(a, p.tiles, st)
+                      : go<4, 1, 8, EPI_RESID>(a, p.tiles, st);
       }
       break;
     case EPI_SWIGLU:
-      e = one ? go<1, 2, 4, EPI_SWIGLU>(a, p.tiles, st) : go<2, 1, 4, EPI_SWIGLU>(a, p.tiles, st);
+      e = ct == 1 ? go<1, 2, 4, EPI_SWIGLU>(a, p.tiles, st)
+          : ct == 2 ? go<2, 1, 4, EPI_SWIGLU>(a, p.tiles, st)
+                    : go<4, 1, 4, EPI_SWIGLU>(a, p.tiles, st);
       break;
     case EPI_LOGITS:
       if (a.x_plain)  // one plain activation row (the last prompt token)
-        e = one ? go<1, 2, 4, EPI_LOGITS, true>(a, p.tiles, st) : hipErrorInvalidValue;
+        e = ct == 1 ? go<1, 2, 4, EPI_LOGITS, true>(a, p.tiles, st) : hipErrorInvalidValue;
       else
-        e = one ? go<1, 2, 4, EPI_LOGITS>(a, p.tiles, st) : go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st);
+        e = ct == 1 ? go<1, 2, 4, EPI_LOGITS>(a, p.tiles, st)
+            : ct == 2 ? go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st)
+                      : go<4, 1, 4, EPI_LOGITS>(a, p.tiles, st);
       if (e != hipSuccess) return e;
       argmax_finalize_kernel<<<a.B, 256, 0, st>>>(a.amax_part, p.tiles, a.B, a.next_tok);
       e = hipGetLastError();
@@ -460,6 +471,12 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
       break;
   }
   return e;
+}
+
+hipError_t launch_argmax_finalize(const unsigned long long* part, int tiles, int B, int32_t* next_tok,
+                                  hipStream_t st) {
+  argmax_finalize_kernel<<<B, 256, 0, st>>>(part, tiles, B, next_tok);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

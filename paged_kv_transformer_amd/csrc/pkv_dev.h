@@ -89,8 +89,8 @@ struct AttnArgs {
   const int32_t* lens;     // [B]: attention length, or position (len_add = 1)
   int32_t len_add;
   float scale;
-  float* out;              // [B][Hq][D] FP32, or packed as [B][Hq * D] if out_packed
-  int32_t out_packed;
+  float* out;              // out_packed 0: [B][Hq][D] FP32; 1: packed FP32 [B][Hq * D]
+  int32_t out_packed;      // (packed_act_index); 2: packed BF16 hi/lo pairs (packed_pair_index)
   float* part;             // split partial records [B][Hkv][max_splits][kAttnRec]
   uint32_t* err;
   int32_t Hq, Hkv, G;
@@ -167,19 +167,28 @@ struct PgemmArgs {
   float* part;
   int32_t ksplit;
   // EPI_QKV: q as BF16 hi, lo halves [T][Hq][2][D]; k, v into the pages of
-  // positions start_pos + t through the sequence's table bt
+  // position pos[t] (or start_pos + t if pos is null) through the table row
+  // bt + t * bt_row (bt_row 0: one sequence's table); positions outside
+  // [0, max_pos) or past the table's bt_stride pages set device errors
   uint16_t* q_split;
   uint16_t* pool;
   int64_t page_elems;
   int32_t num_pages;
   const int32_t* bt;
-  int32_t start_pos;
+  int32_t bt_row, bt_stride;
+  const int32_t* pos;
+  int32_t start_pos, max_pos;
   const float* rcos;
   const float* rsin;
   int32_t Hq, Hkv;
   // EPI_SWIGLU: act = silu(gate) * up, packed BF16 hi/lo pairs
   uint16_t* act;
   int32_t I;
+  // EPI_LOGITS: FP32 logits [T][N] (if not null) and, per token and
+  // half row tile (2 per tile), the largest logit packed with its index:
+  // amax_part[2 * row_tiles][T], reduced by the argmax kernel
+  float* logits;
+  unsigned long long* amax_part;
 };
 
 struct PattnArgs {
@@ -247,7 +256,7 @@ struct SampleWs {
   uint32_t* cnt;      // [B][3][2048]
   uint64_t* mass;     // [B][3][2048]
   uint64_t* sum;      // [B] softmax normaliser (fixed point)
-  void* choice;       // [2][B] choice records
+  void* choice;       // [3][B] records: choices after levels 1, 2; the nucleus
   float* wmax;        // [B][W] chunk maxima
   uint64_t* wmass;    // [B][W] chunk mass above the threshold
   uint32_t* wties;    // [B][W] chunk ties at the threshold
@@ -284,11 +293,13 @@ struct GemmPlan {
   int tiles, ct, rg, nw, ks;
 };
 
-constexpr int kGemmMaxCols = 32;  // batch columns per launch (ct <= 2)
+constexpr int kGemmMaxCols = 64;  // batch columns per launch (ct <= 4)
 constexpr int kMaxDim = 65536;    // largest hidden / intermediate size
 constexpr int64_t kMaxMatrixBytes = (int64_t)1 << 31;  // largest weight matrix
 
-inline int gemm_ct(int B) { return B <= 16 ? 1 : 2; }
+// 16-column groups per launch: the weights stream once per launch, so a
+// batch of 64 reads them once
+inline int gemm_ct(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
 
 // A residual projection whose row tiles alone give few workgroups and whose
 // K is long (the down projection) splits K over workgroups: about 512
@@ -303,6 +314,7 @@ inline bool gemm_split(int epi, int N, int K) {
 }
 
 inline int gemm_rows_per_tile(int epi, int ct, bool split) {
+  if (ct == 4) return 16;  // 4 column groups: one row group keeps the registers in bounds
   if (split) return 32;
   if (epi == EPI_QKV || epi == EPI_RESID) return 16;
   return ct == 1 ? 32 : 16;
@@ -403,6 +415,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_prefill_norm(const float* x, const uint16_t* xw, int K, int T, float eps,
                                uint16_t* out, hipStream_t st);
 hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, const PgemmPlan& p, hipStream_t st);
+// argmax over the per-tile keys of EPI_LOGITS (either GEMM): one token per column
+hipError_t launch_argmax_finalize(const unsigned long long* part, int tiles, int B, int32_t* next_tok,
+                                  hipStream_t st);
 // x[t] += sum over splits of part[s][t] (in split order); then, if nw is
 // given, the RMSNorm of the new row into packed hi/lo pairs xb
 hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int N,

@@ -46,6 +46,15 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
 }
 
+// Order-preserving map of an FP32 logit to 32 bits, paired with the inverted
+// index: the 64-bit maximum is the largest logit and, among equal ones, the
+// lowest index.
+__device__ __forceinline__ unsigned long long logit_key(float v, int n) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)n);
+}
+
 // ------------------------------------------------------------- norm ---
 // Eight FP32 values as BF16 hi halves and the BF16 rounding of what remains.
 __device__ __forceinline__ void split8(const float* v, uint4& hi, uint4& lo) {
@@ -258,6 +267,36 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
   // ---- epilogues: lane holds rows 16 G + 4 grp + e (e = 0..3) of token
   // 16 tg + col for each accumulator tile
   const int grp = l >> 4, col = l & 15;
+  if (EPI == EPI_LOGITS) {
+    // FP32 logits, and per token the largest logit of this wave's rows
+    // packed with its index (the lower index wins ties); the two waves of a
+    // token half write the two key slots of this row tile
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const int t = 16 * (c0 + wc * CG + c) + col;
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const int G = g0 + wr * RG + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = 16 * G + 4 * grp + e;
+          if (n < a.N) {
+            const float v = acc[r][c][e];
+            if (a.logits && t < a.T) a.logits[(size_t)t * a.N + n] = v;
+            const unsigned long long key = logit_key(v, n);
+            best = key > best ? key : best;
+          }
+        }
+      }
+      unsigned long long o = __shfl_xor(best, 16);
+      best = o > best ? o : best;
+      o = __shfl_xor(best, 32);
+      best = o > best ? o : best;
+      if (grp == 0 && t < a.T) a.amax_part[(size_t)(2 * rt + wr) * a.T + t] = best;
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < RG; ++r)
 #pragma unroll
@@ -298,12 +337,21 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = __shfl_xor(v[e], 32);
         const int hd = G >> 2;
-        if (hd < a.Hq + 2 * a.Hkv && t < a.T) {
+        const int p = t < a.T ? (a.pos ? a.pos[t] : a.start_pos + t) : 0;
+        const bool is_q = hd < a.Hq, is_k = !is_q && hd < a.Hq + a.Hkv;
+        bool ok = hd < a.Hq + 2 * a.Hkv && t < a.T;
+        if (ok && (is_q || is_k) && (p < 0 || p >= a.max_pos)) {
+          set_error(a.err, ERR_ROPE);
+          ok = false;
+        }
+        if (ok && !is_q && (p < 0 || p / kPageTokens >= a.bt_stride)) {
+          set_error(a.err, ERR_LENGTH);
+          ok = false;
+        }
+        if (ok) {
           const bool first = l < 32;
           const int jb = 8 * (G & 3) + 4 * (grp & 1);
           const int jj = first ? jb : jb + 32;
-          const int p = a.start_pos + t;
-          const bool is_q = hd < a.Hq, is_k = !is_q && hd < a.Hq + a.Hkv;
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -329,7 +377,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
             *(u32x2*)(qo + kHeadDim) = (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
           } else {
-            const int page = a.bt[p / kPageTokens];
+            const int page = a.bt[(size_t)t * a.bt_row + p / kPageTokens];
             if ((unsigned)page >= (unsigned)a.num_pages) {
               set_error(a.err, ERR_PAGE);
             } else {
@@ -620,6 +668,7 @@ hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, const PgemmPlan& p, 
     case EPI_QKV: return launch_pg<EPI_QKV>(a, p, st);
     case EPI_RESID: return launch_pg<EPI_RESID>(a, p, st);
     case EPI_SWIGLU: return launch_pg<EPI_SWIGLU>(a, p, st);
+    case EPI_LOGITS: return launch_pg<EPI_LOGITS>(a, p, st);
     default: return hipErrorInvalidValue;
   }
 }

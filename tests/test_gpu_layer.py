@@ -63,12 +63,12 @@ def test_layer_tiny_shapes(batch, hkv, heads):
     _check_layer(shape, lw, hidden, wl)
 
 
-@pytest.mark.parametrize("batch,inter", [(1, 4096), (5, 4352), (16, 8192), (33, 4352)])
+@pytest.mark.parametrize("batch,inter", [(1, 4096), (5, 4352), (16, 8192), (33, 4352), (64, 4352)])
 def test_layer_split_k_down_projection(batch, inter):
     """Down projections with K >= 4096 split K over workgroups and add the
     splits in a second kernel; 4352 (136 K steps) gives 17 splits, more than
     one round of the reduce kernel's 16-split loads; batch 33 also takes the
-    two-column-tile path."""
+    two-column-tile path, batch 64 the tiled large-batch path."""
     shape = synth.tiny_shape(hidden=192, heads=4, kv_heads=2, inter=inter, name="tiny-split")
     seed = 300 + batch
     positions = synth.rng(seed, "lens").integers(0, 100, size=batch).astype(np.int32)
@@ -104,6 +104,24 @@ def test_step_tiny_model():
     tokens = synth.rng(7, "tokens").integers(0, shape.vocab, size=5)
     nxt = _check_step(shape, weights, wl, tokens)
     # the same step without logits gives the same tokens
+    _, nxt2, _, _ = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions, tokens,
+                             want_logits=False)
+    assert np.array_equal(nxt, nxt2)
+
+
+@pytest.mark.parametrize("batch", [64, 100])
+def test_step_tiny_model_large_batch(batch):
+    """Batches of 64 and more take the tiled projections and the tiled LM
+    head (logits and per-tile argmax keys): every sequence against the
+    oracle, and the same tokens without logits."""
+    shape = synth.tiny_shape(hidden=128, layers=3, heads=4, kv_heads=2, inter=256, vocab=1000)
+    seed = 70 + batch
+    positions = synth.rng(seed, "lens").integers(0, 300, size=batch).astype(np.int32)
+    positions[:3] = [0, 15, 16]
+    weights = synth.model_weights(shape, seed, sigma=0.05, norm_sigma=0.3)
+    wl = synth.decode_workload("tiny-step", shape, seed, positions)
+    tokens = synth.rng(seed, "tokens").integers(0, shape.vocab, size=batch)
+    nxt = _check_step(shape, weights, wl, tokens)
     _, nxt2, _, _ = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions, tokens,
                              want_logits=False)
     assert np.array_equal(nxt, nxt2)
