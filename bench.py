@@ -328,6 +328,32 @@ def time_step_cfg(torch, pkv, synth, wl, shape, model, max_pos, reps=10):
     return ms, step_bytes(shape, wl.lens)
 
 
+def large_batch_steps(torch, pkv, synth, llama_model=None):
+    """The batch-64 Llama step and the batch-128 Qwen step: {name: object}."""
+    out = {}
+    for name, mk, shp, model_fn in (
+            ("step_c4", synth.c4_step, synth.LLAMA1B,
+             lambda: llama_model or pkv.upload_model(synth.model_weights(synth.LLAMA1B, 1002),
+                                                     synth.LLAMA1B.theta, 4097)),
+            ("step_c5", synth.c5_step, synth.QWEN05,
+             lambda: pkv.upload_model(synth.model_weights(synth.QWEN05, 1005), synth.QWEN05.theta, 4097))):
+        wlx = mk()
+        mp_ = int(wlx.positions.max()) + 1
+        model = model_fn()
+        xs, xb = time_step_cfg(torch, pkv, synth, wlx, shp, model, mp_)
+        xm = float(np.median(xs))
+        log("%s: %.3f ms per step (median), batch %d -> %.0f tokens/s, %.0f GB/s" % (
+            name, xm, wlx.batch, wlx.batch / (xm * 1e-3), xb / (xm * 1e-3) / 1e9))
+        out[name] = {"workload": wlx.name, "batch": int(wlx.batch), "ms_per_step": pct(xs),
+                     "tokens_per_s": round(wlx.batch / (xm * 1e-3), 1), "bound": "hbm",
+                     "algorithmic_bytes": int(xb), "achieved": round(xb / (xm * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(xb / (xm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del model, wlx
+        torch.cuda.empty_cache()
+    return out
+
+
 def ceilings(torch, nbytes=1 << 30, reps=10):
     """Plain streaming rates on this GPU: a device copy (bytes read + written)
     and a read-only reduction (torch's own kernels), 1 GiB each."""
@@ -565,6 +591,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     ap.add_argument("--no-layer-b1", action="store_true")
+    ap.add_argument("--large-batch-only", action="store_true",
+                    help="time the batch-64 and batch-128 steps alone (for profiling)")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="skip the c1 layer chain, the batch-64/128 steps and the copy ceilings")
     ap.add_argument("--prefill-tokens", type=int, default=512, help="0 skips the prefill timing")
@@ -583,15 +611,17 @@ def main():
     import paged_kv_transformer_amd as pkv
     import synth
 
-    if args.attention_only or args.prefill_only:
+    if args.attention_only or args.prefill_only or args.large_batch_only:
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(2)
         torch.cuda.set_device(0)
         if args.attention_only:
             attention_only(torch, pkv, synth, args.attn_rounds)
-        else:
+        elif args.prefill_only:
             prefill_only(torch, pkv, synth, args.prefill_tokens)
+        else:
+            print(json.dumps(large_batch_steps(torch, pkv, synth)))
         return
 
     host = HostInputs(synth)
@@ -685,24 +715,7 @@ def main():
             "bound": "hbm", "algorithmic_bytes": int(c1_bytes), "us_per_layer": pct([m * 1e3 for m in c1_ms]),
             "achieved": round(c1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(c1_gbs / HBM_PEAK_GBS, 4), "gate_frac": 0.6}
-        for name, mk, shp, model_fn in (
-                ("step_c4", synth.c4_step, synth.LLAMA1B, lambda: S.model),
-                ("step_c5", synth.c5_step, synth.QWEN05,
-                 lambda: pkv.upload_model(synth.model_weights(synth.QWEN05, 1005), synth.QWEN05.theta, 4097))):
-            wlx = mk()
-            mp_ = int(wlx.positions.max()) + 1
-            model = model_fn()
-            xs, xb = time_step_cfg(torch, pkv, synth, wlx, shp, model, mp_)
-            xm = float(np.median(xs))
-            log("%s: %.3f ms per step (median), batch %d -> %.0f tokens/s, %.0f GB/s" % (
-                name, xm, wlx.batch, wlx.batch / (xm * 1e-3), xb / (xm * 1e-3) / 1e9))
-            extra[name] = {"workload": wlx.name, "batch": int(wlx.batch), "ms_per_step": pct(xs),
-                           "tokens_per_s": round(wlx.batch / (xm * 1e-3), 1), "bound": "hbm",
-                           "algorithmic_bytes": int(xb), "achieved": round(xb / (xm * 1e-3) / 1e9, 1),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(xb / (xm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-            del model, wlx
-            torch.cuda.empty_cache()
+        extra.update(large_batch_steps(torch, pkv, synth, S.model))
         cp_gbs, rd_gbs = ceilings(torch)
         log("ceilings: device copy %.0f GB/s (read + write), read-only reduction %.0f GB/s" % (cp_gbs, rd_gbs))
         extra["ceiling"] = {"copy_gbs": round(cp_gbs, 1), "read_gbs": round(rd_gbs, 1),
