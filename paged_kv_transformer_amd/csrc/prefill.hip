@@ -19,9 +19,9 @@
 //                             K/V page writes, SwiGLU, or (residual
 //                             projections) K-split partial sums
 //   prefill_resid_kernel      residual + partial sums, then the next RMSNorm
-//   prefill_attention_kernel  causal paged attention: each wave takes up to
-//                             16 (token, head) query columns of one kv head
-//                             and walks the pages 0 .. its last position
+//   prefill_attention_kernel  causal paged attention: a workgroup takes up to
+//                             16 (token, head) query columns of one kv head;
+//                             its waves split the pages 0 .. the last position
 #include "pkv_dev.h"
 
 namespace pkv {
@@ -457,33 +457,43 @@ __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const floa
 }
 
 // -------------------------------------------------------- attention ---
-// Causal paged attention of the prompt.  A wave's 16 query columns are
+// Causal paged attention of the prompt.  A workgroup's 16 query columns are
 // (token, head) pairs: tpw = 16 / G consecutive tokens times the G heads of
-// one kv head, column = G * (token - t0) + head.  For each page the wave
-// forms S^T[key][column] = K q^T (v_mfma_f32_16x16x32_bf16, q as BF16 hi
-// and lo halves) and then O[column][d] += P[column][key] V[key][d]
+// one kv head, column = G * (token - t0) + head.  Its 4 waves split the
+// pages 0 .. the last token's position into 4 contiguous ranges (a prompt
+// position attends to every page before it, so without the split one wave
+// would walk them all, one dependent round trip per two pages).  For each
+// page a wave forms S^T[key][column] = K q^T (v_mfma_f32_16x16x32_bf16, q as
+// BF16 hi and lo halves) and then O[column][d] += P[column][key] V[key][d]
 // (v_mfma_f32_16x16x16_bf16, P as hi and lo halves); the score tile's
 // register layout is the P operand's, and V is stored [d][slot] in the
 // page.  Key position kp is visible to a column whose position is at least
 // kp.  The softmax is online in base 2 (scale * log2 e applied in the
-// exponent), rescaling O whenever a column's maximum grows; two pages per
-// rescale, the next two pages' loads in flight meanwhile.  Workgroups with
-// the latest tokens (the most pages) are launched first.
+// exponent), two pages per rescale, the next two pages' loads in flight
+// meanwhile; the waves' (m, l, O) are merged in LDS in wave order by the
+// log-sum-exp rule.  Workgroups with the latest tokens (the most pages) are
+// launched first.
 constexpr int kPW = 2;
 
 __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs a) {
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  __shared__ float sm_o[4][16][kHeadDim + 1];
   const int kvh = blockIdx.y;
   const int blk = gridDim.x - 1 - blockIdx.x;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = l & 15, grp = l >> 4;
   const int G = a.G, tpw = 16 / G;
-  const int t0 = (blk * 4 + w) * tpw;
+  const int t0 = blk * tpw;
   if (t0 >= a.T) return;
   const int tend = min(t0 + tpw, a.T);
-  const int pmax = a.start_pos + tend - 1;  // the wave's last position
+  const int pmax = a.start_pos + tend - 1;  // the group's last position
   const int npages = pmax / kPageTokens + 1;
   const int pmin = a.start_pos + t0;        // its first: keys up to here need no mask
+  // this wave's pages [pb, pe)
+  const int npw = (npages + 3) / 4;
+  const int pb = w * npw, pe = min(npages, pb + npw);
 
   // this lane's query column
   const int tk = col / G, gh = col - tk * G;
@@ -510,10 +520,11 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     u32x2 v[kPW][4];
   };
   bool bad = false;
+  // pages past the wave's range read its last page and are masked
   auto load = [&](Chunk& C, int lp0) {
 #pragma unroll
     for (int i = 0; i < kPW; ++i) {
-      int page = a.bt[min(lp0 + i, npages - 1)];
+      int page = a.bt[min(lp0 + i, pe - 1)];
       const bool ok = (unsigned)page < (unsigned)a.num_pages;
       bad |= !ok;
       page = ok ? page : 0;
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
 
   auto step = [&](const Chunk& C, int lp0) {
     f32x4 s[kPW];
-    bool full[kPW];
+    bool full[kPW], inr[kPW];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kPW; ++i) {
@@ -544,10 +555,11 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
       acc = mfma_k32(C.k[i][1], qh[1], acc);
       acc = mfma_k32(C.k[i][1], ql[1], acc);
       const int kp0 = (lp0 + i) * kPageTokens;
-      full[i] = kp0 + kPageTokens - 1 <= pmin;  // uniform
+      inr[i] = lp0 + i < pe;                              // uniform
+      full[i] = inr[i] && kp0 + kPageTokens - 1 <= pmin;  // uniform
       if (!full[i]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = kp0 + 4 * grp + r <= lim ? acc[r] : -INFINITY;
+        for (int r = 0; r < 4; ++r) acc[r] = inr[i] && kp0 + 4 * grp + r <= lim ? acc[r] : -INFINITY;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[r]);
@@ -585,8 +597,9 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     }
 #pragma unroll
     for (int i = 0; i < kPW; ++i) {
-      // slots past the wave's last position may hold anything: zero them
-      const int nv = pmax - ((lp0 + i) * kPageTokens + 4 * grp) + 1;
+      // slots past the group's last position, or pages past the wave's
+      // range, may hold anything: zero them
+      const int nv = inr[i] ? pmax - ((lp0 + i) * kPageTokens + 4 * grp) + 1 : 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         u32x2 vv = C.v[i][c];
@@ -601,39 +614,54 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     }
   };
 
-  {
+  if (pb < pe) {
     Chunk A, B;
-    load(A, 0);
-    for (int lp = 0;; lp += 2 * kPW) {
-      if (lp + kPW < npages) load(B, lp + kPW);
+    load(A, pb);
+    for (int lp = pb;; lp += 2 * kPW) {
+      if (lp + kPW < pe) load(B, lp + kPW);
       step(A, lp);
-      if (lp + kPW >= npages) break;
-      if (lp + 2 * kPW < npages) load(A, lp + 2 * kPW);
+      if (lp + kPW >= pe) break;
+      if (lp + 2 * kPW < pe) load(A, lp + 2 * kPW);
       step(B, lp + kPW);
-      if (lp + 2 * kPW >= npages) break;
+      if (lp + 2 * kPW >= pe) break;
     }
   }
   if (bad && l == 0) set_error(a.err, ERR_PAGE);
 
+  // ---- the waves' (m, l, O) into LDS, merged in wave order
+  if (grp == 0) {
+    sm_m[w][col] = m;
+    sm_l[w][col] = lsum;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sm_o[w][4 * grp + r][col + 16 * c] = o[c][r];
+  __syncthreads();
+
   // ---- O / l, stored as BF16 hi/lo pairs into the output projection's
-  // packed input
+  // packed input; thread tid takes outputs (g, d) = idx / 64, idx % 64
   const int QD = a.Hq * kHeadDim;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = 4 * grp + r;
-    const float lr = __shfl(lsum, g);
+  for (int idx = tid; idx < 16 * kHeadDim; idx += 256) {
+    const int g = idx >> 6, d = idx & 63;
     const int t = t0 + g / G, h = kvh * G + g % G;
-    if (g < tpw * G && t < a.T) {
-      const float inv = 1.0f / lr;
+    if (g >= tpw * G || t >= a.T) continue;
+    float M = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float y = o[c][r] * inv;
-        const uint16_t hb = to_bf16_bits(y);
-        const int k = h * kHeadDim + col + 16 * c;
-        a.out[packed_pair_index(t, k, QD, 0)] = hb;
-        a.out[packed_pair_index(t, k, QD, 1)] = to_bf16_bits(y - bf16_lo(hb));
-      }
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float mw = sm_m[ww][g];
+      const float sc = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mw - M) * c2);
+      L += sc * sm_l[ww][g];
+      O += sc * sm_o[ww][g][d];
     }
+    const float y = O / L;
+    const uint16_t hb = to_bf16_bits(y);
+    const int k = h * kHeadDim + d;
+    a.out[packed_pair_index(t, k, QD, 0)] = hb;
+    a.out[packed_pair_index(t, k, QD, 1)] = to_bf16_bits(y - bf16_lo(hb));
   }
 }
 
@@ -682,7 +710,7 @@ hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int 
 
 hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st) {
   const int tpw = 16 / a.G;
-  const dim3 grid((a.T + 4 * tpw - 1) / (4 * tpw), a.Hkv);
+  const dim3 grid((a.T + tpw - 1) / tpw, a.Hkv);
   prefill_attention_kernel<<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
