@@ -27,7 +27,7 @@
  *     (README of llmc: every operator returns a negative errno on error):
  *       0        success
  *       -EINVAL  NULL pointer, bad shape, inconsistent sizes, misalignment
- *       -ENOTSUP head_dim != 64, page_tokens != 16, or a size outside what
+ *       -ENOTSUP head_dim not 64 or 128, page_tokens != 16, or a size outside what
  *                this version supports (stated per call)
  *       -ENOSPC  pool smaller than one page, workspace too small
  *       -EIO     the HIP runtime rejected a launch (the error is cleared)
@@ -47,7 +47,8 @@
  * as BF16, the K block [num_kv_heads][16 slots][head_dim] followed by the V
  * block [num_kv_heads][head_dim][16 slots] (V transposed, so that a page of
  * V is already the operand layout of the matrix cores).  page_bytes =
- * 2 * num_kv_heads * 16 * head_dim * 2 (32 KiB for 8 kv heads, 8 KiB for 2).
+ * 2 * num_kv_heads * 16 * head_dim * 2 (32 KiB for 8 kv heads of width 64,
+ * 64 KiB for 8 of width 128, 8 KiB for 2 of width 64).
  * Token t of a sequence lives in logical page t / 16, slot t % 16; the
  * sequence's block-table row maps the logical page to a physical page.
  * Block tables are int32 [batch][max_pages] per layer; decode_step takes
@@ -65,12 +66,13 @@ extern "C" {
 #endif
 
 #define PKV_PAGE_TOKENS 16
-#define PKV_HEAD_DIM 64
+#define PKV_HEAD_DIM 64     /* the default head width; 128 is also supported */
 
 /* Packed weight layouts (pkv_pack_weight). */
 #define PKV_PACK_ROWS 0     /* rows in order: w_o, w_down, embed / LM head   */
 #define PKV_PACK_QKV 1      /* w_qkv: the RoPE pairs of a head grouped        */
 #define PKV_PACK_GATE_UP 2  /* w_gate_up: 8 gate rows with their 8 up rows    */
+#define PKV_PACK_QKV128 3   /* w_qkv of 128-wide heads, pairs grouped alike   */
 
 /* Sticky device-error bits (pkv_device_error). */
 #define PKV_DEVERR_PAGE 1u      /* block-table entry outside [0, num_pages) */
@@ -84,7 +86,7 @@ typedef struct pkv_config {
 	int32_t num_hidden_layers;       /* layers (decode_step)              */
 	int32_t num_attention_heads;     /* Hq                                 */
 	int32_t num_key_value_heads;     /* Hkv, divides Hq                    */
-	int32_t head_dim;                /* D, must be 64                      */
+	int32_t head_dim;                /* D, 64 or 128                       */
 	int32_t intermediate_size;       /* I, multiple of 64                  */
 	int32_t vocab_size;              /* V (decode_step)                    */
 	int32_t max_position_embeddings; /* rows of the RoPE cos/sin tables    */
@@ -100,7 +102,7 @@ typedef struct pkv_pool {
 	int32_t num_pages;    /* floor(bytes / page_bytes)                        */
 	int32_t page_tokens;  /* 16                                               */
 	int32_t num_kv_heads; /* Hkv                                              */
-	int32_t head_dim;     /* 64                                               */
+	int32_t head_dim;     /* 64 or 128                                        */
 } pkv_pool;
 
 /*
@@ -110,7 +112,8 @@ typedef struct pkv_pool {
  * load time):
  *   attn_norm [H], mlp_norm [H]                  RMSNorm weights
  *   w_qkv     [(Hq + 2 Hkv) * D][H]              q rows, then k rows, then v rows;
- *                                                packed PKV_PACK_QKV
+ *                                                packed PKV_PACK_QKV (D = 64)
+ *                                                or PKV_PACK_QKV128 (D = 128)
  *   w_o       [H][Hq * D]                        packed PKV_PACK_ROWS
  *   w_gate_up [2 I][H]                           gate rows, then up rows;
  *                                                packed PKV_PACK_GATE_UP
@@ -137,7 +140,7 @@ typedef struct pkv_model_weights {
  * (the engine's shared BF16 page pool sized in bytes, its --kv-cache-mib
  * option).  No device work, no allocation; `out` is a host struct.
  * Errors: -EINVAL (NULL, misaligned base, bytes < 0, num_kv_heads < 1),
- * -ENOTSUP (head_dim != 64 or page_tokens != 16), -ENOSPC (less than one
+ * -ENOTSUP (head_dim not 64 or 128, or page_tokens != 16), -ENOSPC (less than one
  * page, or more than INT32_MAX pages).
  */
 int kv_pool_create(void *dev_base, int64_t bytes, int32_t num_kv_heads,
@@ -303,6 +306,9 @@ size_t pkv_sample_workspace_bytes(int32_t batch, int32_t vocab);
  *   PKV_PACK_QKV      head G / 4, j = 8 (G % 4) + (m % 8): row 64 head + j
  *                     for m < 8, row 64 head + 32 + j for m >= 8 (the RoPE
  *                     pairs of a head sit in one group)
+ *   PKV_PACK_QKV128   the same for 128-wide heads: head G / 8,
+ *                     j = 8 (G % 8) + (m % 8), rows 128 head + j and
+ *                     128 head + 64 + j
  *   PKV_PACK_GATE_UP  i = 8 G + (m % 8): gate row i for m < 8, up row I + i
  *                     for m >= 8 (I = rows / 2)
  * Each projection then reads whole 1 KiB blocks in the matrix-core operand
@@ -312,7 +318,8 @@ size_t pkv_sample_workspace_bytes(int32_t batch, int32_t vocab);
 /*
  * Bytes of a packed [rows][cols] matrix (0 if cols is not a positive
  * multiple of 32, rows < 1, or rows does not suit the layout: a multiple of
- * 64 for PKV_PACK_QKV, of 16 for PKV_PACK_GATE_UP).
+ * 64 for PKV_PACK_QKV, of 128 for PKV_PACK_QKV128, of 16 for
+ * PKV_PACK_GATE_UP).
  */
 size_t pkv_packed_weight_bytes(int32_t rows, int32_t cols, int32_t layout);
 
@@ -341,7 +348,8 @@ int pkv_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  * pkv_rope_table — fill cos/sin [max_pos][D/2] FP32 on the device with
  * cos(p * theta^(-2j/D)) and sin(...) evaluated in double and rounded to
  * FP32 (the article's RoPE section precomputes such tables once; here in
- * FP32 rather than FP16).  Errors: -EINVAL, -ENOTSUP (D != 64), -EIO.
+ * FP32 rather than FP16).  Errors: -EINVAL, -ENOTSUP (D not 64 or 128),
+ * -EIO.
  */
 int pkv_rope_table(float theta, int32_t head_dim, int32_t max_pos,
 		   float *cos_out, float *sin_out, void *stream);

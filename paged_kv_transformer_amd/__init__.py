@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 PAGE_TOKENS = 16
 HEAD_DIM = 64
 DEVERR_PAGE, DEVERR_LENGTH, DEVERR_ROPE, DEVERR_TOKEN = 1, 2, 4, 8
-PACK_ROWS, PACK_QKV, PACK_GATE_UP = 0, 1, 2
+PACK_ROWS, PACK_QKV, PACK_GATE_UP, PACK_QKV128 = 0, 1, 2, 3
 
 
 class PkvError(RuntimeError):
@@ -218,8 +218,8 @@ def pack_weight(src, layout, stream=None):
 # ------------------------------------------------------------- attention ---
 
 def paged_gqa_decode(pool, q, block_table, context_lens, scale, out, workspace, stream=None):
-    """q [B, Hq, 64] BF16, block_table [B, max_pages] int32, context_lens [B]
-    int32, out [B, Hq, 64] FP32 (written)."""
+    """q [B, Hq, D] BF16, block_table [B, max_pages] int32, context_lens [B]
+    int32, out [B, Hq, D] FP32 (written); D is the pool's head width."""
     B, Hq = q.shape[0], q.shape[1]
     _check("paged_gqa_decode", lib().paged_gqa_decode(
         ctypes.byref(pool), _dev(q, _BF16_DTYPES, "q"), Hq,
@@ -326,22 +326,30 @@ def to_device(a, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
-_LAYER_PACK = {"w_qkv": PACK_QKV, "w_o": PACK_ROWS, "w_gate_up": PACK_GATE_UP, "w_down": PACK_ROWS}
+def qkv_pack_kind(head_dim):
+    """Packed layout of w_qkv for heads of width head_dim (64 or 128)."""
+    if head_dim == 64:
+        return PACK_QKV
+    if head_dim == 128:
+        return PACK_QKV128
+    raise ValueError("head_dim must be 64 or 128, got %r" % (head_dim,))
 
 
-def upload_layer(lw, device="cuda"):
+def upload_layer(lw, device="cuda", head_dim=HEAD_DIM):
     """Row-major BF16 host matrices -> device, packed by the library."""
+    pack = {"w_qkv": qkv_pack_kind(head_dim), "w_o": PACK_ROWS, "w_gate_up": PACK_GATE_UP,
+            "w_down": PACK_ROWS}
     t = {}
     for k in LAYER_KEYS:
         d = to_device(lw[k], device)
-        t[k] = pack_weight(d, _LAYER_PACK[k]) if k in _LAYER_PACK else d
+        t[k] = pack_weight(d, pack[k]) if k in pack else d
     return DeviceLayer(t)
 
 
-def upload_model(weights, theta, max_pos, device="cuda"):
+def upload_model(weights, theta, max_pos, device="cuda", head_dim=HEAD_DIM):
     """weights: {'embed', 'final_norm', 'layers': [layer dicts]} of BF16 bits
     (row-major); the matrices are packed on the device."""
-    c, s = rope_table(theta, max_pos, device=device)
+    c, s = rope_table(theta, max_pos, head_dim=head_dim, device=device)
     embed = pack_weight(to_device(weights["embed"], device), PACK_ROWS)
     return DeviceModel(embed, to_device(weights["final_norm"], device),
-                       [upload_layer(lw, device) for lw in weights["layers"]], c, s)
+                       [upload_layer(lw, device, head_dim) for lw in weights["layers"]], c, s)

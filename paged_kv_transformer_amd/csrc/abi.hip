@@ -15,11 +15,14 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Supported head widths.
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+
 int check_pool(const pkv_pool* p) {
   if (!p || !p->base) return -EINVAL;
-  if (p->head_dim != kHeadDim || p->page_tokens != kPageTokens) return -ENOTSUP;
+  if (!head_dim_ok(p->head_dim) || p->page_tokens != kPageTokens) return -ENOTSUP;
   if (p->num_kv_heads < 1 || p->num_pages < 1 || p->bytes < 0) return -EINVAL;
-  if (p->page_bytes != 2LL * p->num_kv_heads * kPageTokens * kHeadDim * 2) return -EINVAL;
+  if (p->page_bytes != 2LL * p->num_kv_heads * kPageTokens * p->head_dim * 2) return -EINVAL;
   if ((int64_t)p->num_pages * p->page_bytes > p->bytes) return -EINVAL;
   if (!aligned(p->base, 256)) return -EINVAL;
   return 0;
@@ -33,7 +36,7 @@ int check_heads(int32_t Hq, int32_t Hkv) {
 
 int check_cfg(const pkv_config* c) {
   if (!c) return -EINVAL;
-  if (c->head_dim != kHeadDim) return -ENOTSUP;
+  if (!head_dim_ok(c->head_dim)) return -ENOTSUP;
   int rc = check_heads(c->num_attention_heads, c->num_key_value_heads);
   if (rc) return rc;
   if (c->hidden_size < 1 || c->intermediate_size < 1 || c->max_position_embeddings < 1)
@@ -43,7 +46,7 @@ int check_cfg(const pkv_config* c) {
   // 32-bit byte range
   if (c->hidden_size > kMaxDim || c->intermediate_size > kMaxDim) return -ENOTSUP;
   const int64_t H = c->hidden_size, I = c->intermediate_size;
-  const int64_t qkv_rows = (int64_t)(c->num_attention_heads + 2 * c->num_key_value_heads) * kHeadDim;
+  const int64_t qkv_rows = (int64_t)(c->num_attention_heads + 2 * c->num_key_value_heads) * c->head_dim;
   if (c->vocab_size > 0 && (int64_t)c->vocab_size * H * 2 > kMaxMatrixBytes) return -ENOTSUP;
   if (qkv_rows * H * 2 > kMaxMatrixBytes || 2 * I * H * 2 > kMaxMatrixBytes) return -ENOTSUP;
   if (!(c->rms_norm_eps >= 0.f) || !isfinite(c->rms_norm_eps)) return -EINVAL;
@@ -78,7 +81,8 @@ int check_layer_call(const pkv_config* cfg, const pkv_pool* pool, const float* r
   if (rc) return rc;
   rc = check_pool(pool);
   if (rc) return rc;
-  if (pool->num_kv_heads != cfg->num_key_value_heads) return -EINVAL;
+  if (pool->num_kv_heads != cfg->num_key_value_heads || pool->head_dim != cfg->head_dim)
+    return -EINVAL;
   if (batch < 0 || max_pages < 1) return -EINVAL;
   if (batch > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
   if (!rope_cos || !rope_sin || !bt || !positions || !ws) return -EINVAL;
@@ -114,7 +118,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
               const float* hidden_packed, void* ws, const WsLayout& L, hipStream_t st) {
   const int H = cfg->hidden_size, Hq = cfg->num_attention_heads;
   const int Hkv = cfg->num_key_value_heads, I = cfg->intermediate_size;
-  const int QD = Hq * kHeadDim;
+  const int D = cfg->head_dim, QD = Hq * D;
   uint16_t* q = at<uint16_t>(ws, L.q);  // [B][Hq][2][D] BF16 hi, lo
   float* o_p = at<float>(ws, L.o_p);
   float* h1 = at<float>(ws, L.h1);
@@ -132,9 +136,10 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   {
     GemmArgs a = base;
     a.W = w->w_qkv;
-    a.w_groups = (Hq + 2 * Hkv) * 4;
+    a.w_groups = (Hq + 2 * Hkv) * (D / 16);
     a.xw = w->attn_norm;
-    a.N = (Hq + 2 * Hkv) * kHeadDim;
+    a.N = (Hq + 2 * Hkv) * D;
+    a.D = D;
     a.K = H;
     a.x_plain = hidden_packed == nullptr;
     a.pool = (uint16_t*)pool->base;
@@ -168,9 +173,10 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.bt_row = bt_row;
     a.lens = pos;
     a.len_add = 1;
-    a.scale = 1.0f / sqrtf((float)kHeadDim);
+    a.scale = 1.0f / sqrtf((float)D);
     a.out = o_p;
     a.out_packed = 1;
+    a.D = D;
     a.part = at<float>(ws, L.attn_part);
     a.err = err;
     a.Hq = Hq;
@@ -247,7 +253,7 @@ struct TiledLayout {
 };
 
 PgemmPlan tiled_o_plan(const pkv_config* c, int B) {
-  return plan_prefill_gemm(c->hidden_size / 16, B, c->num_attention_heads * kHeadDim, true);
+  return plan_prefill_gemm(c->hidden_size / 16, B, c->num_attention_heads * c->head_dim, true);
 }
 PgemmPlan tiled_down_plan(const pkv_config* c, int B) {
   return plan_prefill_gemm(c->hidden_size / 16, B, c->intermediate_size, true);
@@ -265,13 +271,13 @@ int lm_row_tiles(const pkv_config* c, int B) {
 
 TiledLayout tiled_layout(const pkv_config* c, int B, int max_pages) {
   const size_t H = c->hidden_size, I = c->intermediate_size;
-  const size_t QD = (size_t)c->num_attention_heads * kHeadDim;
+  const size_t QD = (size_t)c->num_attention_heads * c->head_dim;
   TiledLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   L.err = take(256);
   L.attn_part = take(sizeof(float) * (size_t)B * c->num_key_value_heads * attn_max_splits(max_pages) *
-                     kAttnRec);
+                     attn_rec(c->head_dim));
   L.q = take(2 * (size_t)B * QD * 2);
   L.x = take(sizeof(float) * B * H);
   L.xb = take(2 * (size_t)packed_pair_elems(B, (int)H));
@@ -289,7 +295,7 @@ TiledLayout tiled_layout(const pkv_config* c, int B, int max_pages) {
 size_t layer_ws_bytes(const pkv_config* c, int batch, int max_pages) {
   if (batch >= kTiledMinBatch) return tiled_layout(c, batch, max_pages).total;
   return ws_layout(batch, c->hidden_size, c->num_attention_heads, c->num_key_value_heads,
-                   c->intermediate_size, c->vocab_size, max_pages, true)
+                   c->intermediate_size, c->vocab_size, max_pages, true, c->head_dim)
       .total;
 }
 
@@ -302,7 +308,7 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
                     const TiledLayout& L, hipStream_t st) {
   const int H = cfg->hidden_size, Hq = cfg->num_attention_heads;
   const int Hkv = cfg->num_key_value_heads, I = cfg->intermediate_size;
-  const int QD = Hq * kHeadDim;
+  const int D = cfg->head_dim, QD = Hq * D;
   const float eps = cfg->rms_norm_eps;
   uint16_t* q = at<uint16_t>(ws, L.q);
   uint16_t* xb = at<uint16_t>(ws, L.xb);
@@ -317,10 +323,11 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
   {
     PgemmArgs a = base;
     a.W = w->w_qkv;
-    a.w_groups = (Hq + 2 * Hkv) * 4;
+    a.w_groups = (Hq + 2 * Hkv) * (D / 16);
     a.X = xb;
-    a.N = (Hq + 2 * Hkv) * kHeadDim;
+    a.N = (Hq + 2 * Hkv) * D;
     a.K = H;
+    a.D = D;
     a.q_split = q;
     a.pool = (uint16_t*)pool->base;
     a.page_elems = pool->page_bytes / 2;
@@ -348,9 +355,10 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
     a.bt_row = max_pages;
     a.lens = pos;
     a.len_add = 1;
-    a.scale = 1.0f / sqrtf((float)kHeadDim);
+    a.scale = 1.0f / sqrtf((float)D);
     a.out = (float*)ob;
     a.out_packed = 2;
+    a.D = D;
     a.part = at<float>(ws, L.attn_part);
     a.err = err;
     a.Hq = Hq;
@@ -410,7 +418,7 @@ int kv_pool_create(void* dev_base, int64_t bytes, int32_t num_kv_heads, int32_t 
                    int32_t page_tokens, pkv_pool* out) {
   if (!out || !dev_base || bytes < 0 || num_kv_heads < 1) return -EINVAL;
   if (!aligned(dev_base, 256)) return -EINVAL;
-  if (head_dim != kHeadDim || page_tokens != kPageTokens) return -ENOTSUP;
+  if (!head_dim_ok(head_dim) || page_tokens != kPageTokens) return -ENOTSUP;
   const int64_t page_bytes = 2LL * num_kv_heads * page_tokens * head_dim * 2;
   const int64_t pages = bytes / page_bytes;
   if (pages < 1 || pages > INT32_MAX) return -ENOSPC;
@@ -434,15 +442,15 @@ int kv_append(const pkv_pool* pool, const int32_t* block_table, int32_t max_page
   if (!block_table || !positions || !k_new || !v_new) return -EINVAL;
   return io(launch_kv_append((uint16_t*)pool->base, pool->page_bytes / 2, pool->num_pages,
                              block_table, max_pages, positions, k_new, v_new, batch,
-                             pool->num_kv_heads, (hipStream_t)stream));
+                             pool->num_kv_heads, pool->head_dim, (hipStream_t)stream));
 }
 
 size_t pkv_attention_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                      int32_t batch, int32_t max_pages) {
-  if (check_heads(num_q_heads, num_kv_heads) || head_dim != kHeadDim || batch < 0 ||
+  if (check_heads(num_q_heads, num_kv_heads) || !head_dim_ok(head_dim) || batch < 0 ||
       max_pages < 1)
     return 0;
-  return ws_layout(batch, 0, num_q_heads, num_kv_heads, 0, 0, max_pages, false).total;
+  return ws_layout(batch, 0, num_q_heads, num_kv_heads, 0, 0, max_pages, false, head_dim).total;
 }
 
 size_t pkv_workspace_bytes(const pkv_config* cfg, int32_t batch, int32_t max_pages) {
@@ -463,7 +471,8 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   if (batch == 0) return 0;
   if (!q || !block_table || !context_lens || !out || !workspace) return -EINVAL;
   if (!aligned(workspace, 256) || !isfinite(scale)) return -EINVAL;
-  const WsLayout L = ws_layout(batch, 0, num_q_heads, pool->num_kv_heads, 0, 0, max_pages, false);
+  const WsLayout L =
+      ws_layout(batch, 0, num_q_heads, pool->num_kv_heads, 0, 0, max_pages, false, pool->head_dim);
   if (ws_bytes < L.total) return -ENOSPC;
   AttnArgs a{};
   a.q = q;
@@ -483,6 +492,7 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   a.Hkv = pool->num_kv_heads;
   a.G = num_q_heads / pool->num_kv_heads;
   a.max_splits = attn_max_splits(max_pages);
+  a.D = pool->head_dim;
   return io(launch_attention(a, batch, kQBf16, (hipStream_t)stream));
 }
 
@@ -509,7 +519,7 @@ int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
   }
   const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
                                cfg->num_key_value_heads, cfg->intermediate_size,
-                               cfg->vocab_size, max_pages, true);
+                               cfg->vocab_size, max_pages, true, cfg->head_dim);
   return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, max_pages, positions,
                    batch, hidden, nullptr, workspace, L, st);
 }
@@ -562,7 +572,7 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
     return io(launch_argmax_finalize(a.amax_part, 2 * lm_row_tiles(cfg, batch), batch, next_tokens, st));
   }
   const WsLayout L = ws_layout(batch, H, cfg->num_attention_heads, cfg->num_key_value_heads,
-                               cfg->intermediate_size, V, max_pages, true);
+                               cfg->intermediate_size, V, max_pages, true, cfg->head_dim);
   float* x = at<float>(workspace, L.x);
   float* x_p = at<float>(workspace, L.x_p);
   uint32_t* err = at<uint32_t>(workspace, L.err);
@@ -601,7 +611,7 @@ struct PrefillLayout {
 
 // The two residual projections of a prefill layer (output, down).
 static PgemmPlan prefill_o_plan(const pkv_config* cfg, int32_t T) {
-  return plan_prefill_gemm(cfg->hidden_size / 16, T, cfg->num_attention_heads * kHeadDim, true);
+  return plan_prefill_gemm(cfg->hidden_size / 16, T, cfg->num_attention_heads * cfg->head_dim, true);
 }
 static PgemmPlan prefill_down_plan(const pkv_config* cfg, int32_t T) {
   return plan_prefill_gemm(cfg->hidden_size / 16, T, cfg->intermediate_size, true);
@@ -609,7 +619,7 @@ static PgemmPlan prefill_down_plan(const pkv_config* cfg, int32_t T) {
 
 static PrefillLayout prefill_layout(const pkv_config* cfg, int32_t T) {
   const size_t H = cfg->hidden_size, I = cfg->intermediate_size;
-  const size_t QD = (size_t)cfg->num_attention_heads * kHeadDim;
+  const size_t QD = (size_t)cfg->num_attention_heads * cfg->head_dim;
   PrefillLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
@@ -640,7 +650,8 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   if (rc) return rc;
   rc = check_pool(pool);
   if (rc) return rc;
-  if (pool->num_kv_heads != cfg->num_key_value_heads) return -EINVAL;
+  if (pool->num_kv_heads != cfg->num_key_value_heads || pool->head_dim != cfg->head_dim)
+    return -EINVAL;
   if (num_tokens < 0 || max_pages < 1 || start_pos < 0) return -EINVAL;
   if (num_tokens > 65535) return -ENOTSUP;
   if (num_tokens == 0) return 0;
@@ -655,7 +666,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
     if ((rc = check_layer_weights(&w->layers[l]))) return rc;
   const int H = cfg->hidden_size, V = cfg->vocab_size, T = num_tokens;
   const int Hq = cfg->num_attention_heads, Hkv = cfg->num_key_value_heads;
-  const int I = cfg->intermediate_size, QD = Hq * kHeadDim;
+  const int I = cfg->intermediate_size, D = cfg->head_dim, QD = Hq * D;
   // the projections address their packed BF16 hi/lo inputs through a
   // 32-bit byte range
   const int64_t widest = H > I ? (H > QD ? H : QD) : (I > QD ? I : QD);
@@ -673,7 +684,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   const float eps = cfg->rms_norm_eps;
 
   float* part = at<float>(workspace, L.part);
-  const PgemmPlan p_qkv = plan_prefill_gemm((Hq + 2 * Hkv) * 4, T, H, false);
+  const PgemmPlan p_qkv = plan_prefill_gemm((Hq + 2 * Hkv) * (D / 16), T, H, false);
   const PgemmPlan p_o = prefill_o_plan(cfg, T);
   const PgemmPlan p_gu = plan_prefill_gemm(I / 8, T, H, false);
   const PgemmPlan p_down = prefill_down_plan(cfg, T);
@@ -693,10 +704,11 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
     {
       PgemmArgs a = base;
       a.W = lw->w_qkv;
-      a.w_groups = (Hq + 2 * Hkv) * 4;
+      a.w_groups = (Hq + 2 * Hkv) * (D / 16);
       a.X = xb;
-      a.N = (Hq + 2 * Hkv) * kHeadDim;
+      a.N = (Hq + 2 * Hkv) * D;
       a.K = H;
+      a.D = D;
       a.q_split = q;
       a.pool = (uint16_t*)pool->base;
       a.page_elems = pool->page_bytes / 2;
@@ -723,8 +735,9 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.bt = bt;
       a.start_pos = start_pos;
       a.T = T;
-      a.scale = 1.0f / sqrtf((float)kHeadDim);
+      a.scale = 1.0f / sqrtf((float)D);
       a.out = ob;
+      a.D = D;
       a.err = err;
       a.Hq = Hq;
       a.Hkv = Hkv;
@@ -815,8 +828,9 @@ int sample_tokens(const float* logits, int32_t batch, int32_t vocab, const float
 }
 
 size_t pkv_packed_weight_bytes(int32_t rows, int32_t cols, int32_t layout) {
-  if (rows < 1 || cols < 32 || cols % 32 != 0 || layout < PACK_ROWS || layout > PACK_GATE_UP) return 0;
-  if (layout == PKV_PACK_QKV && rows % kHeadDim != 0) return 0;
+  if (rows < 1 || cols < 32 || cols % 32 != 0 || layout < PACK_ROWS || layout > PACK_QKV128) return 0;
+  if (layout == PKV_PACK_QKV && rows % 64 != 0) return 0;
+  if (layout == PKV_PACK_QKV128 && rows % 128 != 0) return 0;
   if (layout == PKV_PACK_GATE_UP && rows % 16 != 0) return 0;
   return (size_t)packed_weight_elems(rows, cols, layout) * 2;
 }
@@ -838,7 +852,7 @@ int pkv_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
 int pkv_rope_table(float theta, int32_t head_dim, int32_t max_pos, float* cos_out, float* sin_out,
                    void* stream) {
   if (!cos_out || !sin_out || max_pos < 1 || !(theta > 0.f) || !isfinite(theta)) return -EINVAL;
-  if (head_dim != kHeadDim) return -ENOTSUP;
+  if (!head_dim_ok(head_dim)) return -ENOTSUP;
   return io(launch_rope_table((double)theta, head_dim, max_pos, cos_out, sin_out,
                               (hipStream_t)stream));
 }

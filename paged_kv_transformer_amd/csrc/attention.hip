@@ -56,9 +56,10 @@ __device__ __forceinline__ f32x4 mfma_k16(s16x4 a, s16x4 b, f32x4 c) {
 // [B][Hq][D], or packed as the output projection's input ([B][Hq * D]):
 // FP32 for the weight-streaming projection, BF16 hi/lo pairs for the tiled
 // one.
+template <int D>
 __device__ __forceinline__ void store_out(const AttnArgs& a, int b, int kvh, int idx, float v) {
-  const int k = kvh * a.G * kHeadDim + idx;
-  const int QD = a.Hq * kHeadDim;
+  const int k = kvh * a.G * D + idx;
+  const int QD = a.Hq * D;
   if (a.out_packed == 2) {
     uint16_t* o = (uint16_t*)a.out;
     const uint16_t h = to_bf16_bits(v);
@@ -80,16 +81,19 @@ __device__ __forceinline__ u32x2 keep_first(u32x2 v, int nv) {
   return r;
 }
 
-template <int QM>
+template <int QM, int D>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 5))) void
 paged_attention_kernel(const AttnArgs a) {
+  constexpr int NH = D / 32;  // 32-wide q.K blocks
+  constexpr int NC = D / 16;  // 16-wide output column blocks
+  constexpr int REC = attn_rec(D);
   constexpr int PW = kAttnPW;
   constexpr int CP = kAttnPagesPerSplit;
   constexpr int NW = kAttnWaves;
   constexpr int NT = NW * 64;
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
-  __shared__ float sm_o[NW][16][kHeadDim + 1];
+  __shared__ float sm_o[NW][16][D + 1];
 
   // the highest splits are launched first: only long sequences have them,
   // and starting the longest work first keeps it out of the kernel's tail
@@ -115,14 +119,14 @@ paged_attention_kernel(const AttnArgs a) {
   // (m = -inf) when it has no tokens, and the merge kernel writes every
   // output.
   const bool single = a.max_splits == 1;
-  float* rec = a.part + (((size_t)b * a.Hkv + kvh) * a.max_splits + split) * kAttnRec;
+  float* rec = a.part + (((size_t)b * a.Hkv + kvh) * a.max_splits + split) * REC;
   const bool bad_len = n < 0 || n > a.bt_stride * kPageTokens;
   if (bad_len && split == 0 && tid == 0) set_error(a.err, ERR_LENGTH);
   const int npages = bad_len ? 0 : (n + kPageTokens - 1) / kPageTokens;
   const int ns = npages > 0 ? (npages + CP - 1) / CP : 1;
   if (npages == 0 || split >= ns) {
     if (single) {
-      for (int i = tid; i < G * kHeadDim; i += NT) store_out(a, b, kvh, i, 0.f);
+      for (int i = tid; i < G * D; i += NT) store_out<D>(a, b, kvh, i, 0.f);
     } else if (tid < G) {
       rec[tid] = -INFINITY;
     }
@@ -151,29 +155,29 @@ paged_attention_kernel(const AttnArgs a) {
   constexpr bool kSplitQ = QM == kQSplit;
   const int gq = col < G ? col : 0;
   const size_t qhead = (size_t)b * a.Hq + (size_t)kvh * G + gq;
-  const uint16_t* qp = a.q + qhead * (kSplitQ ? 2 : 1) * kHeadDim + 8 * grp;
-  u32x4 qraw[2], qlraw[2];
+  const uint16_t* qp = a.q + qhead * (kSplitQ ? 2 : 1) * D + 8 * grp;
+  u32x4 qraw[NH], qlraw[NH];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NH; ++h) {
     qraw[h] = *(const u32x4*)(qp + 32 * h);
-    if (kSplitQ) qlraw[h] = *(const u32x4*)(qp + kHeadDim + 32 * h);
+    if (kSplitQ) qlraw[h] = *(const u32x4*)(qp + D + 32 * h);
   }
-  u32x4 kr[PW][2];
-  u32x2 vr[PW][4];
-  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * kHeadDim;
+  u32x4 kr[PW][NH];
+  u32x2 vr[PW][NC];
+  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * D;
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
-    const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * kHeadDim + 8 * grp;
-    kr[i][0] = *(const u32x4*)kp;
-    kr[i][1] = *(const u32x4*)(kp + 32);
+    const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * D + 8 * grp;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) kr[i][h] = *(const u32x4*)(kp + 32 * h);
   }
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
-    const uint16_t* vp = pg + vblk + ((int64_t)kvh * kHeadDim + col) * kPageTokens + 4 * grp;
+    const uint16_t* vp = pg + vblk + ((int64_t)kvh * D + col) * kPageTokens + 4 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
+    for (int c = 0; c < NC; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (bad && l == 0) set_error(a.err, ERR_PAGE);
@@ -185,9 +189,9 @@ paged_attention_kernel(const AttnArgs a) {
   // raw scores is the maximum of the scaled ones.
   const float c2 = fabsf(a.scale) * kLog2e;
   const unsigned sgn = a.scale < 0.f ? 0x80008000u : 0u;
-  bf16x8 qh[2], ql[2];
+  bf16x8 qh[NH], ql[NH];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NH; ++h) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     qh[h] = __builtin_bit_cast(bf16x8, col < G ? qraw[h] ^ sgn : z);
     if (kSplitQ) ql[h] = __builtin_bit_cast(bf16x8, col < G ? qlraw[h] ^ sgn : z);
@@ -202,10 +206,11 @@ paged_attention_kernel(const AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma_k32(kr[i][0], qh[0], acc);
-    if (kSplitQ) acc = mfma_k32(kr[i][0], ql[0], acc);
-    acc = mfma_k32(kr[i][1], qh[1], acc);
-    if (kSplitQ) acc = mfma_k32(kr[i][1], ql[1], acc);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      acc = mfma_k32(kr[i][h], qh[h], acc);
+      if (kSplitQ) acc = mfma_k32(kr[i][h], ql[h], acc);
+    }
     // a full page (every page of a sequence but its last) needs no mask;
     // the test is uniform across the wave
     if (!full[i]) {
@@ -245,15 +250,15 @@ paged_attention_kernel(const AttnArgs a) {
   lsum += __shfl_xor(lsum, 32);
 
   // ---- O[g][d]: lane holds rows g = 4*grp + r, column d = col + 16*c
-  f32x4 o[4];
+  f32x4 o[NC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NC; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     // unused slots of a partial page may hold anything (NaN included): zero them
     const int nv = full[i] ? 4 : (lpv[i] < 0 ? 0 : n - (lpv[i] * kPageTokens + 4 * grp));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const s16x4 vb = __builtin_bit_cast(s16x4, keep_first(vr[i][c], nv));
       o[c] = mfma_k16(ph[i], vb, o[c]);
       o[c] = mfma_k16(pl[i], vb, o[c]);
@@ -266,7 +271,7 @@ paged_attention_kernel(const AttnArgs a) {
     sm_l[w][col] = lsum;
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = 4 * grp + r;
@@ -274,8 +279,8 @@ paged_attention_kernel(const AttnArgs a) {
     }
   __syncthreads();
 
-  for (int idx = tid; idx < G * kHeadDim; idx += NT) {
-    const int g = idx >> 6, d = idx & 63;
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int g = idx / D, d = idx % D;
     float M = sm_m[0][g];
 #pragma unroll
     for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sm_m[ww][g]);
@@ -288,7 +293,7 @@ paged_attention_kernel(const AttnArgs a) {
       O += e * sm_o[ww][g][d];
     }
     if (single) {
-      store_out(a, b, kvh, idx, L > 0.f ? O / L : 0.f);
+      store_out<D>(a, b, kvh, idx, L > 0.f ? O / L : 0.f);
     } else {
       if (d == 0) {
         rec[g] = M;
@@ -307,21 +312,23 @@ paged_attention_kernel(const AttnArgs a) {
 // m, l and O of 16 splits are loaded together (split indexes clamped to the
 // record array and masked past it), so up to 16 splits cost one round of
 // loads.  The kernel arguments are read in one batch on entry.
+template <int D>
 __global__ __launch_bounds__(256) void attention_merge_kernel(const AttnArgs a) {
   constexpr int CH = 16;
+  constexpr int REC = attn_rec(D);
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int G = a.G, tid = threadIdx.x, S = a.max_splits;
   asm volatile("" ::"s"(a.part), "s"(a.out), "s"(a.Hq), "s"(a.Hkv), "s"(a.G), "s"(a.max_splits),
                "s"(a.out_packed));
-  const float* rec0 = a.part + ((size_t)b * a.Hkv + kvh) * S * kAttnRec;
-  for (int idx = tid; idx < G * kHeadDim; idx += 256) {
-    const int g = idx >> 6;
+  const float* rec0 = a.part + ((size_t)b * a.Hkv + kvh) * S * REC;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int g = idx / D;
     float M = -INFINITY, L = 0.f, O = 0.f;
     for (int c0 = 0; c0 < S; c0 += CH) {
       float m[CH], lv[CH], ov[CH];
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
-        const float* r = rec0 + (size_t)min(c0 + j, S - 1) * kAttnRec;
+        const float* r = rec0 + (size_t)min(c0 + j, S - 1) * REC;
         m[j] = r[g];
         lv[j] = r[16 + g];
         ov[j] = r[32 + idx];
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(const AttnArgs a) 
       }
       M = Mc;
     }
-    store_out(a, b, kvh, idx, L > 0.f ? O / L : 0.f);
+    store_out<D>(a, b, kvh, idx, L > 0.f ? O / L : 0.f);
   }
 }
 
@@ -356,13 +363,24 @@ hipError_t launch_attention(const AttnArgs& a, int batch, int qmode, hipStream_t
   // the split fastest, the XCDs holding the low splits of every sequence
   // would get most of the non-empty workgroups)
   const dim3 grid(a.Hkv, batch, a.max_splits);
-  if (qmode == kQSplit)
-    paged_attention_kernel<kQSplit><<<grid, kAttnWaves * 64, 0, st>>>(a);
-  else
-    paged_attention_kernel<kQBf16><<<grid, kAttnWaves * 64, 0, st>>>(a);
+  if (a.D != 64 && a.D != 128) return hipErrorInvalidValue;
+  if (a.D == 64) {
+    if (qmode == kQSplit)
+      paged_attention_kernel<kQSplit, 64><<<grid, kAttnWaves * 64, 0, st>>>(a);
+    else
+      paged_attention_kernel<kQBf16, 64><<<grid, kAttnWaves * 64, 0, st>>>(a);
+  } else {
+    if (qmode == kQSplit)
+      paged_attention_kernel<kQSplit, 128><<<grid, kAttnWaves * 64, 0, st>>>(a);
+    else
+      paged_attention_kernel<kQBf16, 128><<<grid, kAttnWaves * 64, 0, st>>>(a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits <= 1) return e;
-  attention_merge_kernel<<<dim3(a.Hkv, batch), 256, 0, st>>>(a);
+  if (a.D == 64)
+    attention_merge_kernel<64><<<dim3(a.Hkv, batch), 256, 0, st>>>(a);
+  else
+    attention_merge_kernel<128><<<dim3(a.Hkv, batch), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@
 // the RMSNorm row scale 1/sqrt(mean x^2 + eps) is applied in the epilogue.
 //
 // Fused epilogues:
-//   EPI_QKV     16 rows = 8 RoPE pairs (j, j+32) of one head: RoPE on q and
+//   EPI_QKV     16 rows = 8 RoPE pairs (j, j+D/2) of one head: RoPE on q and
 //               k heads (angle from the FP32 cos/sin tables at the
 //               sequence's position); q -> BF16 hi + lo halves (the
 //               attention's matrix operand, ~16 bits), k and v -> BF16
@@ -266,7 +266,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       }
     }
   } else if (EPI == EPI_QKV) {
-    const int hd = t >> 2, j0 = 8 * (t & 3);
+    // head width D: a 16-row group holds 8 RoPE pairs (j, j + D/2) of one head
+    const int D = a.D, half = D / 2, gph = D / 16;
+    const int hd = t / gph, j0 = 8 * (t % gph);
     const bool is_q = hd < a.Hq;
     const bool is_k = !is_q && hd < a.Hq + a.Hkv;
     for (int idx = tid; idx < 8 * a.B; idx += NT) {
@@ -281,19 +283,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
           set_error(a.err, ERR_ROPE);
           continue;
         }
-        const float cs = a.rcos[(size_t)p * 32 + j];
-        const float sn = a.rsin[(size_t)p * 32 + j];
+        const float cs = a.rcos[(size_t)p * half + j];
+        const float sn = a.rsin[(size_t)p * half + j];
         y0 = __fsub_rn(__fmul_rn(x0, cs), __fmul_rn(x1, sn));
         y1 = __fadd_rn(__fmul_rn(x0, sn), __fmul_rn(x1, cs));
       }
       if (is_q) {
         // q leaves as the attention's matrix operand: BF16 hi and lo halves
-        uint16_t* qo = a.q_split + ((size_t)c * a.Hq + hd) * 2 * kHeadDim;
+        uint16_t* qo = a.q_split + ((size_t)c * a.Hq + hd) * 2 * D;
         const uint16_t h0 = to_bf16_bits(y0), h1 = to_bf16_bits(y1);
         qo[j] = h0;
-        qo[j + 32] = h1;
-        qo[kHeadDim + j] = to_bf16_bits(y0 - bf16_lo(h0));
-        qo[kHeadDim + j + 32] = to_bf16_bits(y1 - bf16_lo(h1));
+        qo[j + half] = h1;
+        qo[D + j] = to_bf16_bits(y0 - bf16_lo(h0));
+        qo[D + j + half] = to_bf16_bits(y1 - bf16_lo(h1));
       } else {
         if (p < 0 || p / kPageTokens >= a.bt_stride) {
           set_error(a.err, ERR_LENGTH);
@@ -307,14 +309,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
         const int slot = p % kPageTokens;
         if (is_k) {
-          uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * kHeadDim;
+          uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * D;
           kp[j] = to_bf16_bits(y0);
-          kp[j + 32] = to_bf16_bits(y1);
+          kp[j + half] = to_bf16_bits(y1);
         } else {
-          uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * kHeadDim +
-                         (int64_t)(hd - a.Hq - a.Hkv) * kHeadDim * kPageTokens + slot;
+          uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * D +
+                         (int64_t)(hd - a.Hq - a.Hkv) * D * kPageTokens + slot;
           vp[j * kPageTokens] = to_bf16_bits(y0);
-          vp[(j + 32) * kPageTokens] = to_bf16_bits(y1);
+          vp[(j + half) * kPageTokens] = to_bf16_bits(y1);
         }
       }
     }

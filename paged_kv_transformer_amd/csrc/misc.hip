@@ -11,7 +11,7 @@ namespace {
 // position: logical page pos / 16, slot pos % 16.
 __global__ void kv_append_kernel(uint16_t* pool, int64_t page_elems, int32_t num_pages,
                                  const int32_t* bt, int32_t bt_stride, const int32_t* pos,
-                                 const uint16_t* k, const uint16_t* v, int Hkv) {
+                                 const uint16_t* k, const uint16_t* v, int Hkv, int D) {
   const int b = blockIdx.x;
   const int p = pos[b];
   if (p < 0 || p / kPageTokens >= bt_stride) return;
@@ -19,13 +19,13 @@ __global__ void kv_append_kernel(uint16_t* pool, int64_t page_elems, int32_t num
   if ((unsigned)page >= (unsigned)num_pages) return;
   const int slot = p % kPageTokens;
   uint16_t* pg = pool + (int64_t)page * page_elems;
-  uint16_t* vblk = pg + (int64_t)Hkv * kPageTokens * kHeadDim;
-  const uint16_t* kb = k + (size_t)b * Hkv * kHeadDim;
-  const uint16_t* vb = v + (size_t)b * Hkv * kHeadDim;
-  for (int i = threadIdx.x; i < Hkv * kHeadDim; i += blockDim.x) {
-    const int h = i / kHeadDim, d = i % kHeadDim;
-    pg[((int64_t)h * kPageTokens + slot) * kHeadDim + d] = kb[i];
-    vblk[((int64_t)h * kHeadDim + d) * kPageTokens + slot] = vb[i];
+  uint16_t* vblk = pg + (int64_t)Hkv * kPageTokens * D;
+  const uint16_t* kb = k + (size_t)b * Hkv * D;
+  const uint16_t* vb = v + (size_t)b * Hkv * D;
+  for (int i = threadIdx.x; i < Hkv * D; i += blockDim.x) {
+    const int h = i / D, d = i % D;
+    pg[((int64_t)h * kPageTokens + slot) * D + d] = kb[i];
+    vblk[((int64_t)h * D + d) * kPageTokens + slot] = vb[i];
   }
 }
 
@@ -100,10 +100,10 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size
 
 hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_pages,
                             const int32_t* bt, int32_t bt_stride, const int32_t* pos,
-                            const uint16_t* k, const uint16_t* v, int batch, int Hkv,
+                            const uint16_t* k, const uint16_t* v, int batch, int Hkv, int D,
                             hipStream_t st) {
   kv_append_kernel<<<batch, 256, 0, st>>>(pool, page_elems, num_pages, bt, bt_stride, pos, k, v,
-                                          Hkv);
+                                          Hkv, D);
   return hipGetLastError();
 }
 

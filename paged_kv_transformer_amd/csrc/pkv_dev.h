@@ -10,7 +10,8 @@
 namespace pkv {
 
 constexpr int kPageTokens = 16;
-constexpr int kHeadDim = 64;
+constexpr int kHeadDim = 64;       // the default head width; 128 is also supported
+constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;      // GQA group: one 16-wide matrix-core tile
 
 enum : uint32_t { ERR_PAGE = 1u, ERR_LENGTH = 2u, ERR_ROPE = 4u, ERR_TOKEN = 8u };
@@ -41,14 +42,16 @@ __device__ __forceinline__ void set_error(uint32_t* err, uint32_t bits) {
 // the 8 values W[row(G, m)][32 s + 8 i .. + 8].  A wave streams a group's
 // K range as contiguous 1 KiB blocks, already in the A-operand layout of
 // v_mfma_f32_16x16x32_bf16.  row(G, m) depends on the layout kind:
-enum PackKind { PACK_ROWS = 0, PACK_QKV = 1, PACK_GATE_UP = 2 };
+enum PackKind { PACK_ROWS = 0, PACK_QKV = 1, PACK_GATE_UP = 2, PACK_QKV128 = 3 };
 
 // Matrix row held by row m (0..15) of 16-row group G, or -1 (zero rows).
 __host__ __device__ inline int packed_row(int kind, int rows, int G, int m) {
-  if (kind == PACK_QKV) {
-    // group G: head G / 4, RoPE pairs j = 8 (G % 4) + i, rows j and j + 32
-    const int j0 = 8 * (G & 3);
-    const int r = (G >> 2) * kHeadDim + (m < 8 ? j0 + m : 32 + j0 + (m - 8));
+  if (kind == PACK_QKV || kind == PACK_QKV128) {
+    // head width D: group G is head G / (D / 16), RoPE pairs
+    // j = 8 (G % (D / 16)) + i, rows j and j + D / 2
+    const int D = kind == PACK_QKV ? 64 : 128, gph = D / 16;
+    const int j0 = 8 * (G % gph);
+    const int r = (G / gph) * D + (m < 8 ? j0 + m : D / 2 + j0 + (m - 8));
     return r < rows ? r : -1;
   }
   if (kind == PACK_GATE_UP) {
@@ -91,10 +94,11 @@ struct AttnArgs {
   float scale;
   float* out;              // out_packed 0: [B][Hq][D] FP32; 1: packed FP32 [B][Hq * D]
   int32_t out_packed;      // (packed_act_index); 2: packed BF16 hi/lo pairs (packed_pair_index)
-  float* part;             // split partial records [B][Hkv][max_splits][kAttnRec]
+  float* part;             // split partial records [B][Hkv][max_splits][attn_rec(D)]
   uint32_t* err;
   int32_t Hq, Hkv, G;
   int32_t max_splits;
+  int32_t D;               // head width, 64 or 128
 };
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
@@ -130,6 +134,7 @@ struct GemmArgs {
   const float* rsin;
   int32_t max_pos;
   int32_t Hq, Hkv;
+  int32_t D;               // head width, 64 or 128
   // EPI_SWIGLU: act[b][i], i < I, packed (the down projection's input)
   float* act;
   int32_t I;
@@ -181,6 +186,7 @@ struct PgemmArgs {
   const float* rcos;
   const float* rsin;
   int32_t Hq, Hkv;
+  int32_t D;               // head width, 64 or 128
   // EPI_SWIGLU: act = silu(gate) * up, packed BF16 hi/lo pairs
   uint16_t* act;
   int32_t I;
@@ -202,6 +208,7 @@ struct PattnArgs {
   uint16_t* out;           // packed BF16 hi/lo pairs (the output projection's input)
   uint32_t* err;
   int32_t Hq, Hkv, G;
+  int32_t D;               // head width, 64 or 128
 };
 
 // A prefill GEMM launch: 2 x 2 waves per workgroup, each 16 rg rows by
@@ -280,7 +287,7 @@ constexpr int kAttnWaves = PKV_ATTN_WAVES;
 constexpr int kAttnPW = 2;
 constexpr int kAttnPagesPerSplit = kAttnWaves * kAttnPW;
 // One split's partial record: m[16], l[16], o[16][64] floats.
-constexpr int kAttnRec = 16 + 16 + 16 * kHeadDim;
+constexpr int attn_rec(int D) { return 16 + 16 + 16 * D; }
 
 inline int attn_max_splits(int max_pages) {
   return (max_pages + kAttnPagesPerSplit - 1) / kAttnPagesPerSplit;
@@ -365,15 +372,16 @@ struct WsLayout {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace layout.  layer == false: attention only (no activations).
-inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_pages, bool layer) {
+inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_pages, bool layer,
+                          int D = kHeadDim) {
   WsLayout w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   w.err = take(256);
-  w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_pages) * kAttnRec);
+  w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_pages) * attn_rec(D));
   if (layer) {
-    w.q = take(sizeof(float) * (size_t)B * Hq * kHeadDim);  // BF16 hi + lo per value
-    w.o_p = take(sizeof(float) * (size_t)packed_act_elems(B, Hq * kHeadDim));
+    w.q = take(sizeof(float) * (size_t)B * Hq * D);  // BF16 hi + lo per value
+    w.o_p = take(sizeof(float) * (size_t)packed_act_elems(B, Hq * D));
     w.h1 = take(sizeof(float) * (size_t)B * H);
     w.h1_p = take(sizeof(float) * (size_t)packed_act_elems(B, H));
     w.act_p = take(sizeof(float) * (size_t)packed_act_elems(B, I));
@@ -382,7 +390,7 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_p
     const int Bc = B < kGemmMaxCols ? B : kGemmMaxCols;
     const GemmPlan lm = plan_gemm(EPI_LOGITS, V, Bc, H);
     w.amax_part = take(sizeof(unsigned long long) * (size_t)lm.tiles * (Bc > 0 ? Bc : 1));
-    const size_t po = gemm_part_floats(H, Bc, Hq * kHeadDim);
+    const size_t po = gemm_part_floats(H, Bc, Hq * D);
     const size_t pd = gemm_part_floats(H, Bc, I);
     w.gemm_part = take(sizeof(float) * (po > pd ? po : pd));
   }
@@ -401,7 +409,7 @@ hipError_t launch_attention(const AttnArgs& a, int batch, int qmode, hipStream_t
 hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_t st);
 hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_pages,
                             const int32_t* bt, int32_t bt_stride, const int32_t* pos,
-                            const uint16_t* k, const uint16_t* v, int batch, int Hkv,
+                            const uint16_t* k, const uint16_t* v, int batch, int Hkv, int D,
                             hipStream_t st);
 hipError_t launch_embed(const uint16_t* E_packed, int V, int H, const int32_t* tok, float* x,
                         float* x_packed, int batch, uint32_t* err, hipStream_t st);

@@ -331,12 +331,13 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
               (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
         }
       } else if (EPI == EPI_QKV) {
-        // group G: head G / 4, RoPE pairs j = 8 (G % 4) + m, rows j (lanes
-        // 0..31) and j + 32 (lanes 32..63, the same j in lane l - 32)
+        // group G: head G / (D/16), RoPE pairs j = 8 (G % (D/16)) + m, rows
+        // j (lanes 0..31) and j + D/2 (lanes 32..63, the same j in lane l - 32)
         f32x4 pv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = __shfl_xor(v[e], 32);
-        const int hd = G >> 2;
+        const int D = a.D, half = D / 2, gph = D / 16;
+        const int hd = G / gph;
         const int p = t < a.T ? (a.pos ? a.pos[t] : a.start_pos + t) : 0;
         const bool is_q = hd < a.Hq, is_k = !is_q && hd < a.Hq + a.Hkv;
         bool ok = hd < a.Hq + 2 * a.Hkv && t < a.T;
@@ -350,22 +351,22 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
         }
         if (ok) {
           const bool first = l < 32;
-          const int jb = 8 * (G & 3) + 4 * (grp & 1);
-          const int jj = first ? jb : jb + 32;
+          const int jb = 8 * (G % gph) + 4 * (grp & 1);
+          const int jj = first ? jb : jb + half;
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             y[e] = v[e];
             if (is_q || is_k) {
               const float x0 = first ? v[e] : pv[e], x1 = first ? pv[e] : v[e];
-              const float cs = a.rcos[(size_t)p * 32 + jb + e];
-              const float sn = a.rsin[(size_t)p * 32 + jb + e];
+              const float cs = a.rcos[(size_t)p * half + jb + e];
+              const float sn = a.rsin[(size_t)p * half + jb + e];
               y[e] = first ? __fsub_rn(__fmul_rn(x0, cs), __fmul_rn(x1, sn))
                            : __fadd_rn(__fmul_rn(x0, sn), __fmul_rn(x1, cs));
             }
           }
           if (is_q) {
-            uint16_t* qo = a.q_split + ((size_t)t * a.Hq + hd) * 2 * kHeadDim + jj;
+            uint16_t* qo = a.q_split + ((size_t)t * a.Hq + hd) * 2 * D + jj;
             uint16_t h[4];
             float lo[4];
 #pragma unroll
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
             }
             *(u32x2*)qo = (u32x2){(uint32_t)h[0] | ((uint32_t)h[1] << 16),
                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-            *(u32x2*)(qo + kHeadDim) = (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+            *(u32x2*)(qo + D) = (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
           } else {
             const int page = a.bt[(size_t)t * a.bt_row + p / kPageTokens];
             if ((unsigned)page >= (unsigned)a.num_pages) {
@@ -384,11 +385,11 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
               uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
               const int slot = p % kPageTokens;
               if (is_k) {
-                uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * kHeadDim + jj;
+                uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * D + jj;
                 *(u32x2*)kp = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
               } else {
-                uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * kHeadDim +
-                               ((int64_t)(hd - a.Hq - a.Hkv) * kHeadDim + jj) * kPageTokens + slot;
+                uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * D +
+                               ((int64_t)(hd - a.Hq - a.Hkv) * D + jj) * kPageTokens + slot;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vp[e * kPageTokens] = to_bf16_bits(y[e]);
               }
@@ -475,10 +476,13 @@ __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const floa
 // launched first.
 constexpr int kPW = 2;
 
+template <int D>
 __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs a) {
+  constexpr int NH = D / 32;  // 32-wide q.K blocks
+  constexpr int NC = D / 16;  // 16-wide output column blocks
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
-  __shared__ float sm_o[4][16][kHeadDim + 1];
+  __shared__ float sm_o[4][16][D + 1];
   const int kvh = blockIdx.y;
   const int blk = gridDim.x - 1 - blockIdx.x;
   const int tid = threadIdx.x, l = tid & 63;
@@ -501,23 +505,23 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
   const int lim = cval ? a.start_pos + t0 + tk : -1;
   const float c2 = fabsf(a.scale) * kLog2e;
   const unsigned sgn = a.scale < 0.f ? 0x80008000u : 0u;
-  u32x4 qh[2], ql[2];
+  u32x4 qh[NH], ql[NH];
   {
     const uint16_t* qp =
-        a.q + ((size_t)(cval ? t0 + tk : 0) * a.Hq + (size_t)kvh * G + gh) * 2 * kHeadDim + 8 * grp;
+        a.q + ((size_t)(cval ? t0 + tk : 0) * a.Hq + (size_t)kvh * G + gh) * 2 * D + 8 * grp;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x4 hv = *(const u32x4*)(qp + 32 * h), lv = *(const u32x4*)(qp + kHeadDim + 32 * h);
+    for (int h = 0; h < NH; ++h) {
+      const u32x4 hv = *(const u32x4*)(qp + 32 * h), lv = *(const u32x4*)(qp + D + 32 * h);
       qh[h] = cval ? hv ^ sgn : z;
       ql[h] = cval ? lv ^ sgn : z;
     }
   }
 
-  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * kHeadDim;
+  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * D;
   struct Chunk {
-    u32x4 k[kPW][2];
-    u32x2 v[kPW][4];
+    u32x4 k[kPW][NH];
+    u32x2 v[kPW][NC];
   };
   bool bad = false;
   // pages past the wave's range read its last page and are masked
@@ -529,19 +533,19 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
       bad |= !ok;
       page = ok ? page : 0;
       const uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
-      const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * kHeadDim + 8 * grp;
-      C.k[i][0] = *(const u32x4*)kp;
-      C.k[i][1] = *(const u32x4*)(kp + 32);
-      const uint16_t* vp = pg + vblk + ((int64_t)kvh * kHeadDim + col) * kPageTokens + 4 * grp;
+      const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * D + 8 * grp;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) C.v[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
+      for (int h = 0; h < NH; ++h) C.k[i][h] = *(const u32x4*)(kp + 32 * h);
+      const uint16_t* vp = pg + vblk + ((int64_t)kvh * D + col) * kPageTokens + 4 * grp;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
     }
   };
 
   float m = -INFINITY, lsum = 0.f;
-  f32x4 o[4];
+  f32x4 o[NC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NC; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   auto step = [&](const Chunk& C, int lp0) {
     f32x4 s[kPW];
@@ -550,10 +554,11 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
 #pragma unroll
     for (int i = 0; i < kPW; ++i) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_k32(C.k[i][0], qh[0], acc);
-      acc = mfma_k32(C.k[i][0], ql[0], acc);
-      acc = mfma_k32(C.k[i][1], qh[1], acc);
-      acc = mfma_k32(C.k[i][1], ql[1], acc);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        acc = mfma_k32(C.k[i][h], qh[h], acc);
+        acc = mfma_k32(C.k[i][h], ql[h], acc);
+      }
       const int kp0 = (lp0 + i) * kPageTokens;
       inr[i] = lp0 + i < pe;                              // uniform
       full[i] = inr[i] && kp0 + kPageTokens - 1 <= pmin;  // uniform
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     for (int r = 0; r < 4; ++r) {
       const float ar = __shfl(alpha, 4 * grp + r);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c][r] *= ar;
+      for (int c = 0; c < NC; ++c) o[c][r] *= ar;
     }
 #pragma unroll
     for (int i = 0; i < kPW; ++i) {
@@ -601,7 +606,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
       // range, may hold anything: zero them
       const int nv = inr[i] ? pmax - ((lp0 + i) * kPageTokens + 4 * grp) + 1 : 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NC; ++c) {
         u32x2 vv = C.v[i][c];
         if (nv < 4) {
           vv.x = nv >= 2 ? vv.x : (nv == 1 ? (vv.x & 0xffffu) : 0u);
@@ -636,14 +641,14 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sm_o[w][4 * grp + r][col + 16 * c] = o[c][r];
+    for (int c = 0; c < NC; ++c) sm_o[w][4 * grp + r][col + 16 * c] = o[c][r];
   __syncthreads();
 
   // ---- O / l, stored as BF16 hi/lo pairs into the output projection's
-  // packed input; thread tid takes outputs (g, d) = idx / 64, idx % 64
-  const int QD = a.Hq * kHeadDim;
-  for (int idx = tid; idx < 16 * kHeadDim; idx += 256) {
-    const int g = idx >> 6, d = idx & 63;
+  // packed input; thread tid takes outputs (g, d) = idx / D, idx % D
+  const int QD = a.Hq * D;
+  for (int idx = tid; idx < 16 * D; idx += 256) {
+    const int g = idx / D, d = idx % D;
     const int t = t0 + g / G, h = kvh * G + g % G;
     if (g >= tpw * G || t >= a.T) continue;
     float M = -INFINITY;
@@ -659,7 +664,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     }
     const float y = O / L;
     const uint16_t hb = to_bf16_bits(y);
-    const int k = h * kHeadDim + d;
+    const int k = h * D + d;
     a.out[packed_pair_index(t, k, QD, 0)] = hb;
     a.out[packed_pair_index(t, k, QD, 1)] = to_bf16_bits(y - bf16_lo(hb));
   }
@@ -711,7 +716,12 @@ hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int 
 hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st) {
   const int tpw = 16 / a.G;
   const dim3 grid((a.T + tpw - 1) / tpw, a.Hkv);
-  prefill_attention_kernel<<<grid, 256, 0, st>>>(a);
+  if (a.D == 64)
+    prefill_attention_kernel<64><<<grid, 256, 0, st>>>(a);
+  else if (a.D == 128)
+    prefill_attention_kernel<128><<<grid, 256, 0, st>>>(a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -65,6 +65,11 @@ QWEN05 = ModelShape("qwen2.5-0.5b-shape", hidden=896, layers=24, heads=14, kv_he
 LLAMA1B = ModelShape("llama-3.2-1b-shape", hidden=2048, layers=16, heads=32, kv_heads=8,
                      head_dim=64, inter=8192, vocab=128256, eps=1e-5, theta=5e5,
                      max_pos=131072)
+# The same GQA family with 128-wide heads (the head-width variant of the
+# page geometry): Llama-3-8B's layer shape.
+LLAMA8B = ModelShape("llama-3-8b-shape", hidden=4096, layers=32, heads=32, kv_heads=8,
+                     head_dim=128, inter=14336, vocab=128256, eps=1e-5, theta=5e5,
+                     max_pos=8192)
 
 
 def tiny_shape(hidden=128, layers=2, heads=4, kv_heads=2, inter=256, vocab=1000,
@@ -150,7 +155,11 @@ def model_weights(shape, seed, sigma=0.02, norm_sigma=0.02, layers=None):
 # ------------------------------------------------------- pool and tables ---
 
 def page_elems(shape_or_kv_heads, head_dim=64, page_tokens=PAGE_TOKENS):
-    kv = shape_or_kv_heads.kv_heads if hasattr(shape_or_kv_heads, "kv_heads") else shape_or_kv_heads
+    """BF16 elements of one page; a model shape brings its own head width."""
+    if hasattr(shape_or_kv_heads, "kv_heads"):
+        kv, head_dim = shape_or_kv_heads.kv_heads, shape_or_kv_heads.head_dim
+    else:
+        kv = shape_or_kv_heads
     return 2 * kv * page_tokens * head_dim
 
 
@@ -233,18 +242,19 @@ def c2_lens(seed=1002, batch=16, max_len=2048):
     return rng(seed, "lens").integers(1, max_len + 1, size=batch).astype(np.int32)
 
 
-def c2_attention(seed=1002, batch=16, pool_bytes=128 << 20):
-    """Paged GQA attention alone, Llama-3.2-1B heads, lengths U[1,2048],
-    pages drawn from a 128 MiB pool with shuffled tables; Q N(0,1) BF16."""
-    shape = LLAMA1B
+def c2_attention(seed=1002, batch=16, pool_bytes=128 << 20, shape=LLAMA1B):
+    """Paged GQA attention alone, Llama-3.2-1B heads (or another shape's),
+    lengths U[1,2048], pages drawn from a 128 MiB pool with shuffled tables;
+    Q N(0,1) BF16, scale 1/sqrt(head_dim)."""
     lens = c2_lens(seed, batch)
     npages = pool_bytes // (page_elems(shape) * 2)
     bt = block_tables(seed, 1, lens, npages, max_pages=128)[0]
     pool = random_pool(seed, npages, page_elems(shape))
     q = bf16_normal(seed, "q", (batch, shape.heads, shape.head_dim))
-    return {"name": "paged GQA attention, 32/8 heads, d64, batch 16, lens U[1,2048], 128 MiB pool",
-            "shape": shape, "lens": lens, "num_pages": int(npages), "block_table": bt,
-            "pool": pool, "q": q, "scale": 0.125}
+    name = "paged GQA attention, %d/%d heads, d%d, batch %d, lens U[1,2048], %d MiB pool" % (
+        shape.heads, shape.kv_heads, shape.head_dim, batch, pool_bytes >> 20)
+    return {"name": name, "shape": shape, "lens": lens, "num_pages": int(npages), "block_table": bt,
+            "pool": pool, "q": q, "scale": 1.0 / float(np.sqrt(shape.head_dim))}
 
 
 def c3_step(seed=1003, with_pool=True, layers=None):

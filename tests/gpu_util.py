@@ -23,14 +23,15 @@ def host_u16(t):
 
 
 def attention_gpu(pool_np, kv_heads, q_bits, bt, lens, scale, ws=None):
-    """Run paged_gqa_decode; returns (out [B, Hq, 64] float32, device error bits)."""
-    B, Hq = q_bits.shape[0], q_bits.shape[1]
+    """Run paged_gqa_decode; returns (out [B, Hq, D] float32, device error
+    bits).  D is q's last dimension, also the pool's head width."""
+    B, Hq, D = q_bits.shape
     pool_t = dev(pool_np)
-    pool = pkv.kv_pool_create(pool_t, kv_heads)
+    pool = pkv.kv_pool_create(pool_t, kv_heads, head_dim=D)
     bt = np.ascontiguousarray(bt, dtype=np.int32)
-    out = torch.full((B, Hq, 64), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     if ws is None:
-        ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(Hq, kv_heads, B, bt.shape[1]))
+        ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(Hq, kv_heads, B, bt.shape[1], head_dim=D))
     pkv.paged_gqa_decode(pool, dev(q_bits), dev(bt), dev(np.asarray(lens, dtype=np.int32)),
                          scale, out, ws)
     err = pkv.device_error(ws)
@@ -38,7 +39,7 @@ def attention_gpu(pool_np, kv_heads, q_bits, bt, lens, scale, ws=None):
 
 
 def attention_oracle(pool_np, kv_heads, q_bits, bt, lens, scale, seqs=None):
-    geo = oracle.PoolGeometry(kv_heads, 64)
+    geo = oracle.PoolGeometry(kv_heads, q_bits.shape[2])
     return oracle.paged_attention(pool_np, geo, oracle.bf16_to_f32(q_bits), bt, lens, scale, seqs)
 
 
@@ -48,10 +49,10 @@ def layer_gpu(shape, lw, hidden, pool_np, bt, positions, max_pos=None):
     bt = np.ascontiguousarray(bt, dtype=np.int32)
     mp = max_pos or int(max(positions)) + 1
     cfg = pkv.make_config(shape, max_pos=mp, layers=1)
-    layer = pkv.upload_layer(lw)
-    c, s = pkv.rope_table(shape.theta, mp)
+    layer = pkv.upload_layer(lw, head_dim=shape.head_dim)
+    c, s = pkv.rope_table(shape.theta, mp, head_dim=shape.head_dim)
     pool_t = dev(pool_np)
-    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads, head_dim=shape.head_dim)
     h = torch.from_numpy(np.ascontiguousarray(hidden, dtype=np.float32)).cuda()
     ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bt.shape[1]))
     pkv.decoder_layer_decode(cfg, layer, c, s, pool, dev(bt), dev(np.asarray(positions, np.int32)), h, ws)
@@ -101,15 +102,48 @@ def check_pool_after(got, want, base, rel=APPEND_REL, touched=None):
     return float(np.abs(g - w).max(initial=0.0)), rms
 
 
+DEEP_KV_REL = 1e-2
+
+
+def check_prefill_pool(got, want, base, geo, bts, start, T, layers):
+    """Pool after a prefill of T tokens at start .. start + T - 1 through the
+    per-layer tables bts [layers, max_pages].  Bytes no append writes must be
+    untouched.  Layer 0's K/V come from the exact embedding rows: each within
+    one BF16 ulp of the oracle's value or APPEND_REL * RMS (check_pool_after).
+    A later layer's K/V are the BF16 rounding of a projection of a hidden
+    state that carries the earlier layers' error, including the rounding of
+    every earlier prompt token's K/V to BF16 in the pool, which may land on
+    the other neighbour in the two paths; that hidden state is held to the
+    layer bar (1e-2 of its RMS), so these values must lie within one BF16 ulp
+    plus DEEP_KV_REL * RMS of the oracle's.  Returns the per-layer max-abs
+    differences."""
+    pos = [start + t for t in range(T)]
+    masks = [appended_mask(base, geo, [bts[l]] * T, pos) for l in range(layers)]
+    every = np.logical_or.reduce(masks)
+    assert np.array_equal(got[~every], base[~every]), "pool bytes outside the appended slots changed"
+    out = []
+    for l, m in enumerate(masks):
+        g = oracle.bf16_to_f32(got[m]).astype(np.float64)
+        w = oracle.bf16_to_f32(want[m]).astype(np.float64)
+        rms = float(np.sqrt(np.mean(w * w))) if w.size else 0.0
+        ulp = np.abs(w) * 2.0 ** -7
+        bound = np.maximum(ulp, APPEND_REL * rms) if l == 0 else ulp + DEEP_KV_REL * rms
+        bad = np.abs(g - w) > bound
+        assert not bad.any(), "appended K/V of layer %d: %d values off by up to %.3g (RMS %.3g)" % (
+            l, int(bad.sum()), float(np.abs(g - w).max()), rms)
+        out.append(float(np.abs(g - w).max(initial=0.0)))
+    return out
+
+
 def step_gpu(shape, weights, pool_np, bts, positions, tokens, want_logits=True, max_pos=None,
              want_pool=True):
     """decode_step; returns (logits or None, next_tokens, pool_after or None, err)."""
     B = len(positions)
     mp = max_pos or int(max(positions)) + 1
     cfg = pkv.make_config(shape, max_pos=mp)
-    model = pkv.upload_model(weights, shape.theta, mp)
+    model = pkv.upload_model(weights, shape.theta, mp, head_dim=shape.head_dim)
     pool_t = dev(pool_np)
-    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads, head_dim=shape.head_dim)
     bts = np.ascontiguousarray(bts, dtype=np.int32)
     ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bts.shape[2]))
     logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda") if want_logits else None

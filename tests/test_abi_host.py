@@ -51,7 +51,10 @@ def test_kv_pool_create_geometry_and_errors():
     assert L.kv_pool_create(None, 1 << 20, 8, 64, 16, ctypes.byref(p)) == EINVAL
     assert L.kv_pool_create(FAKE + 8, 1 << 20, 8, 64, 16, ctypes.byref(p)) == EINVAL
     assert L.kv_pool_create(FAKE, 1 << 20, 0, 64, 16, ctypes.byref(p)) == EINVAL
-    assert L.kv_pool_create(FAKE, 1 << 20, 8, 128, 16, ctypes.byref(p)) == ENOTSUP
+    assert L.kv_pool_create(FAKE, 128 << 20, 8, 128, 16, ctypes.byref(p)) == 0
+    assert p.page_bytes == 65536 and p.num_pages == 2048 and p.head_dim == 128
+    assert L.kv_pool_create(FAKE, 1 << 20, 8, 96, 16, ctypes.byref(p)) == ENOTSUP
+    assert L.kv_pool_create(FAKE, 1 << 20, 8, 256, 16, ctypes.byref(p)) == ENOTSUP
     assert L.kv_pool_create(FAKE, 1 << 20, 8, 64, 256, ctypes.byref(p)) == ENOTSUP
     assert L.kv_pool_create(FAKE, 1000, 8, 64, 16, ctypes.byref(p)) == ENOSPC
     assert L.kv_pool_create(FAKE, 1 << 20, 8, 64, 16, None) == EINVAL
@@ -99,7 +102,8 @@ def test_layer_and_step_validation():
         return L.decoder_layer_decode(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, ctypes.byref(pool),
                                       FAKE, 128, FAKE, b, hidden, ws, wsb, None)
 
-    assert layer(c=_cfg(head_dim=128)) == ENOTSUP
+    assert layer(c=_cfg(head_dim=96)) == ENOTSUP
+    assert layer(c=_cfg(head_dim=128)) == EINVAL               # the pool's heads are 64 wide
     assert layer(c=_cfg(hidden_size=2000)) == ENOTSUP
     assert layer(c=_cfg(intermediate_size=100)) == ENOTSUP
     assert layer(c=_cfg(intermediate_size=65536 + 64)) == ENOTSUP   # past the 32-bit byte ranges
@@ -131,15 +135,30 @@ def test_layer_and_step_validation():
 
 
 def test_rope_table_and_workspace_validation():
-    assert L.pkv_rope_table(1e4, 128, 10, FAKE, FAKE, None) == ENOTSUP
+    assert L.pkv_rope_table(1e4, 96, 10, FAKE, FAKE, None) == ENOTSUP
+    assert L.pkv_rope_table(1e4, 32, 10, FAKE, FAKE, None) == ENOTSUP
     assert L.pkv_rope_table(1e4, 64, 0, FAKE, FAKE, None) == EINVAL
     assert L.pkv_rope_table(-1.0, 64, 10, FAKE, FAKE, None) == EINVAL
     assert L.pkv_rope_table(1e4, 64, 10, None, FAKE, None) == EINVAL
     assert L.pkv_workspace_init(None, 256, None) == EINVAL
     assert L.pkv_workspace_init(FAKE + 1, 256, None) == EINVAL
     assert L.pkv_device_error(None, None) == EINVAL
-    assert L.pkv_attention_workspace_bytes(32, 8, 128, 16, 128) == 0
+    assert L.pkv_attention_workspace_bytes(32, 8, 96, 16, 128) == 0
+    # the split records hold a head's FP32 partial output: twice as wide at D 128
+    w64 = L.pkv_attention_workspace_bytes(32, 8, 64, 16, 128)
+    w128 = L.pkv_attention_workspace_bytes(32, 8, 128, 16, 128)
+    assert w64 > 0 and w128 > w64
     assert L.pkv_workspace_bytes(None, 1, 1) == 0
+
+
+def test_head_dim_128_config_and_packing_sizes():
+    cfg = _cfg(head_dim=128)
+    assert L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 64) > L.pkv_workspace_bytes(ctypes.byref(_cfg()), 16, 64)
+    assert L.pkv_workspace_bytes(ctypes.byref(_cfg(head_dim=96)), 16, 64) == 0
+    assert L.pkv_packed_weight_bytes(3 * 128, 64, pkv.PACK_QKV128) == 3 * 128 * 64 * 2
+    assert L.pkv_packed_weight_bytes(3 * 64, 64, pkv.PACK_QKV128) == 0      # not whole 128-wide heads
+    assert L.pkv_packed_weight_bytes(3 * 64, 64, pkv.PACK_QKV) == 3 * 64 * 64 * 2
+    assert L.pkv_packed_weight_bytes(64, 64, 4) == 0
 
 
 def test_workspace_sizes_grow_with_batch_and_pages():

@@ -14,9 +14,10 @@ pytestmark = pytest.mark.gpu
 
 
 def row_of(layout, rows, G, m):
-    if layout == pkv.PACK_QKV:
-        j = 8 * (G % 4) + (m % 8)
-        r = 64 * (G // 4) + (j if m < 8 else 32 + j)
+    if layout in (pkv.PACK_QKV, pkv.PACK_QKV128):
+        D = 64 if layout == pkv.PACK_QKV else 128
+        j = 8 * (G % (D // 16)) + (m % 8)
+        r = D * (G // (D // 16)) + (j if m < 8 else D // 2 + j)
         return r if r < rows else -1
     if layout == pkv.PACK_GATE_UP:
         I = rows // 2
@@ -42,6 +43,7 @@ def reference_pack(W, layout):
 
 @pytest.mark.parametrize("rows,cols,layout", [
     (37, 64, pkv.PACK_ROWS), (1000, 128, pkv.PACK_ROWS), (3 * 64 * 3, 96, pkv.PACK_QKV),
+    (3 * 128 * 2, 96, pkv.PACK_QKV128),
     (2 * 48, 160, pkv.PACK_GATE_UP), (2 * 64, 64, pkv.PACK_GATE_UP),
 ])
 def test_pack_weight_matches_reference_layout(rows, cols, layout):

@@ -135,10 +135,11 @@ def test_rope_pair_zero_turns_by_position_radians():
         assert r[0, 0] == np.float32(math.cos(p)) and r[0, 32] == np.float32(math.sin(p))
 
 
-def test_rope_frequencies_and_rotate_half_pairing():
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_frequencies_and_rotate_half_pairing(D):
     # catches: adjacent pairing (2j, 2j+1), wrong exponent -2j/D, theta ignored
-    D, theta = 64, 1e6
-    for j in (0, 1, 7, 31):
+    theta = 1e6
+    for j in (0, 1, 7, D // 2 - 1):
         u = np.zeros((1, D), dtype=np.float32)
         u[0, j] = 1.0
         r = oracle.rope(u, 1, theta)[0]
@@ -275,23 +276,24 @@ def test_pool_gather_matches_reshaped_view():
     assert np.array_equal(vc, V.reshape(n, 128).astype(np.float32))
 
 
-@pytest.mark.parametrize("pos", [0, 15, 16, 31, 77])
-def test_pool_append_matches_reshaped_view(pos):
+@pytest.mark.parametrize("pos,D", [(0, 64), (15, 64), (16, 64), (31, 64), (77, 64), (0, 128),
+                                   (17, 128), (95, 128)])
+def test_pool_append_matches_reshaped_view(pos, D):
     g = _rng(18, pos)
-    geo = oracle.PoolGeometry(kv_heads=8, head_dim=64)
+    geo = oracle.PoolGeometry(kv_heads=8, head_dim=D)
     npages = 12
     pool = synth.to_bf16_bits(g.standard_normal(npages * geo.page_elems).astype(np.float32))
     bt = g.permutation(npages)[:6].astype(np.int32)
-    k = synth.to_bf16_bits(g.standard_normal(8 * 64).astype(np.float32))
-    v = synth.to_bf16_bits(g.standard_normal(8 * 64).astype(np.float32))
+    k = synth.to_bf16_bits(g.standard_normal(8 * D).astype(np.float32))
+    v = synth.to_bf16_bits(g.standard_normal(8 * D).astype(np.float32))
     want = pool.copy()
-    kv, vv = brute.pool_view(want, 8, 64)
-    kv[bt[pos // 16], :, pos % 16, :] = k.reshape(8, 64)
-    vv[bt[pos // 16], :, :, pos % 16] = v.reshape(8, 64)
+    kv, vv = brute.pool_view(want, 8, D)
+    kv[bt[pos // 16], :, pos % 16, :] = k.reshape(8, D)
+    vv[bt[pos // 16], :, :, pos % 16] = v.reshape(8, D)
     got = pool.copy()
     oracle.pool_append(got, geo, bt, pos, k, v)
     assert np.array_equal(got, want)
-    assert np.count_nonzero(got != pool) <= 2 * 8 * 64
+    assert np.count_nonzero(got != pool) <= 2 * 8 * D
 
 
 def test_paged_equals_contiguous():
@@ -319,16 +321,20 @@ TINY = synth.tiny_shape(hidden=16, layers=2, heads=4, kv_heads=2, inter=32, voca
                         head_dim=8, eps=1e-5, theta=1e4, name="brute-tiny")
 
 
-def _tiny_inputs(seed, positions):
-    shape = TINY
+def _tiny_inputs(seed, positions, shape=TINY):
     wts = synth.model_weights(shape, seed, sigma=0.3, norm_sigma=0.3)
     wl = synth.decode_workload("tiny", shape, seed, positions, num_pages=40)
     tokens = synth.rng(seed, "tokens").integers(0, shape.vocab, size=len(positions))
     return shape, wts, wl, tokens
 
 
-def test_layer_matches_float64_brute_force():
-    shape, wts, wl, _ = _tiny_inputs(5, [0, 15, 16, 39])
+TINY128 = synth.tiny_shape(hidden=32, layers=2, heads=4, kv_heads=2, inter=64, vocab=50,
+                           head_dim=128, eps=1e-5, theta=1e4, name="brute-tiny-d128")
+
+
+@pytest.mark.parametrize("shape", [TINY, TINY128], ids=["d8", "d128"])
+def test_layer_matches_float64_brute_force(shape):
+    _, wts, wl, _ = _tiny_inputs(5, [0, 15, 16, 39], shape)
     geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
     hidden = synth.rng(5, "hidden").standard_normal((4, shape.hidden)).astype(np.float32)
     out, kn, vn = oracle.layer_decode_paged(shape, wts["layers"][0], hidden, wl.pool, geo,
