@@ -27,7 +27,7 @@
  *     (README of llmc: every operator returns a negative errno on error):
  *       0        success
  *       -EINVAL  NULL pointer, bad shape, inconsistent sizes, misalignment
- *       -ENOTSUP head_dim not 64 or 128, page_tokens != 16, or a size outside what
+ *       -ENOTSUP head_dim not 64 or 128, page_tokens not 16 or 256, or a size outside what
  *                this version supports (stated per call)
  *       -ENOSPC  pool smaller than one page, workspace too small
  *       -EIO     the HIP runtime rejected a launch (the error is cleared)
@@ -43,13 +43,20 @@
  *     that share a workspace must be ordered on one stream; calls on
  *     different streams need different workspaces.
  *
- * Pool layout: physical page p starts at base + p * page_bytes and holds,
- * as BF16, the K block [num_kv_heads][16 slots][head_dim] followed by the V
- * block [num_kv_heads][head_dim][16 slots] (V transposed, so that a page of
- * V is already the operand layout of the matrix cores).  page_bytes =
- * 2 * num_kv_heads * 16 * head_dim * 2 (32 KiB for 8 kv heads of width 64,
- * 64 KiB for 8 of width 128, 8 KiB for 2 of width 64).
- * Token t of a sequence lives in logical page t / 16, slot t % 16; the
+ * Pool layout: a page of PT tokens (page_tokens: 16, the engine's page, or
+ * 256, the fixed page length of the three-stage engine's paged KV cache)
+ * holds, as BF16, a K block [num_kv_heads][PT slots][head_dim] and a V
+ * block [num_kv_heads][head_dim][PT slots] (V transposed, so that 16 slots
+ * of V are already the operand layout of the matrix cores).  With one
+ * buffer (kv_pool_create) physical page p starts at base + p * page_bytes
+ * with its K block followed by its V block, page_bytes =
+ * 2 * num_kv_heads * PT * head_dim * 2 (32 KiB for 16 tokens of 8 kv heads
+ * of width 64, 64 KiB at width 128, 8 KiB for 2 heads of width 64).  With
+ * separate K and V pools (kv_pool_create_split, as the three-stage engine
+ * keeps its K and V caches apart) page p's K block is at
+ * base + p * page_bytes and its V block at v_base + p * page_bytes,
+ * page_bytes = num_kv_heads * PT * head_dim * 2.
+ * Token t of a sequence lives in logical page t / PT, slot t % PT; the
  * sequence's block-table row maps the logical page to a physical page.
  * Block tables are int32 [batch][max_pages] per layer; decode_step takes
  * them layer-major, [num_layers][batch][max_pages].  Entries past a
@@ -76,7 +83,7 @@ extern "C" {
 
 /* Sticky device-error bits (pkv_device_error). */
 #define PKV_DEVERR_PAGE 1u      /* block-table entry outside [0, num_pages) */
-#define PKV_DEVERR_LENGTH 2u    /* length / position beyond max_pages * 16  */
+#define PKV_DEVERR_LENGTH 2u    /* length / position beyond max_pages * PT  */
 #define PKV_DEVERR_ROPE 4u      /* position >= max_position_embeddings      */
 #define PKV_DEVERR_TOKEN 8u     /* token id outside [0, vocab_size)         */
 
@@ -94,15 +101,16 @@ typedef struct pkv_config {
 	float rms_norm_eps;              /* RMSNorm epsilon (inside the root)  */
 } pkv_config;
 
-/* A view of a caller-allocated device buffer as a page pool (no ownership). */
+/* A view of caller-allocated device buffers as a page pool (no ownership). */
 typedef struct pkv_pool {
 	void *base;           /* device, 256-byte aligned                         */
 	int64_t bytes;        /* size of the buffer                               */
-	int64_t page_bytes;   /* 2 * num_kv_heads * page_tokens * head_dim * 2    */
+	int64_t page_bytes;   /* per page and buffer: K + V, or one of them      */
 	int32_t num_pages;    /* floor(bytes / page_bytes)                        */
-	int32_t page_tokens;  /* 16                                               */
+	int32_t page_tokens;  /* 16 or 256                                        */
 	int32_t num_kv_heads; /* Hkv                                              */
 	int32_t head_dim;     /* 64 or 128                                        */
+	void *v_base;         /* NULL: K and V in one buffer; else the V pool     */
 } pkv_pool;
 
 /*
@@ -140,19 +148,31 @@ typedef struct pkv_model_weights {
  * (the engine's shared BF16 page pool sized in bytes, its --kv-cache-mib
  * option).  No device work, no allocation; `out` is a host struct.
  * Errors: -EINVAL (NULL, misaligned base, bytes < 0, num_kv_heads < 1),
- * -ENOTSUP (head_dim not 64 or 128, or page_tokens != 16), -ENOSPC (less than one
- * page, or more than INT32_MAX pages).
+ * -ENOTSUP (head_dim not 64 or 128, or page_tokens not 16 or 256), -ENOSPC
+ * (less than one page, or more than INT32_MAX pages).
  */
 int kv_pool_create(void *dev_base, int64_t bytes, int32_t num_kv_heads,
 		   int32_t head_dim, int32_t page_tokens, pkv_pool *out);
+
+/*
+ * kv_pool_create_split — the same over two caller-owned device buffers of
+ * `bytes` bytes each, K blocks in k_base and V blocks in v_base, both
+ * 256-byte aligned and not overlapping (the three-stage engine's paged KV
+ * cache keeps separate K and V caches indexed by one page number, its
+ * section 3.2).  Every call that takes a pool accepts either kind.
+ * Errors: as kv_pool_create; -EINVAL also for v_base NULL or overlapping.
+ */
+int kv_pool_create_split(void *k_base, void *v_base, int64_t bytes,
+			 int32_t num_kv_heads, int32_t head_dim,
+			 int32_t page_tokens, pkv_pool *out);
 
 /*
  * kv_append — write one new token's K and V per sequence into the pool at
  * its absolute position (decode appends one token at its RoPE position).
  *   block_table [batch][max_pages] int32, positions [batch] int32,
  *   k_new, v_new [batch][Hkv][D] BF16.
- * Sequence b writes slot positions[b] % 16 of physical page
- * block_table[b][positions[b] / 16].  Bit-exact copy of the given values.
+ * Sequence b writes slot positions[b] % PT of physical page
+ * block_table[b][positions[b] / PT].  Bit-exact copy of the given values.
  * batch == 0 is a no-op.  Errors: -EINVAL, -ENOTSUP, -EIO.  This call takes
  * no workspace, so a sequence whose position or table entry is out of
  * range is skipped without a device-error report.
@@ -175,7 +195,7 @@ int kv_append(const pkv_pool *pool, const int32_t *block_table,
  * in the pool (work is split on logical pages).  workspace: at least
  * pkv_attention_workspace_bytes(...) bytes, initialised once.
  * Errors: -EINVAL (NULL, Hq % Hkv != 0, batch < 0, max_pages < 1),
- * -ENOTSUP (Hq / Hkv > 16, batch > 65535, max_pages > 524280), -ENOSPC
+ * -ENOTSUP (Hq / Hkv > 16, batch > 65535, max_pages * PT > 8388480), -ENOSPC
  * (workspace), -EIO; device errors PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH.
  */
 int paged_gqa_decode(const pkv_pool *pool, const uint16_t *q,
@@ -332,14 +352,17 @@ size_t pkv_packed_weight_bytes(int32_t rows, int32_t cols, int32_t layout);
 int pkv_pack_weight(const uint16_t *src, int32_t rows, int32_t cols,
 		    int32_t layout, uint16_t *dst, void *stream);
 
-/* Workspace bytes decoder_layer_decode / decode_step need (0 on bad args). */
+/*
+ * Workspace bytes decoder_layer_decode / decode_step need for block tables
+ * of max_pages pages of page_tokens (16 or 256) tokens (0 on bad args).
+ */
 size_t pkv_workspace_bytes(const pkv_config *cfg, int32_t batch,
-			   int32_t max_pages);
+			   int32_t max_pages, int32_t page_tokens);
 
-/* Workspace bytes paged_gqa_decode needs (0 on bad args). */
+/* Workspace bytes paged_gqa_decode needs, likewise (0 on bad args). */
 size_t pkv_attention_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads,
 				     int32_t head_dim, int32_t batch,
-				     int32_t max_pages);
+				     int32_t max_pages, int32_t page_tokens);
 
 /* Zero a workspace with a fill kernel (no memset node; graph-safe). */
 int pkv_workspace_init(void *workspace, size_t ws_bytes, void *stream);

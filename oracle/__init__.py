@@ -24,7 +24,9 @@ Parity pins (what each function is checked against, in tests/):
                          fixes the 1/sqrt(D) scale, GQA equals MHA over
                          repeated KV, float64 online softmax equals two-pass
   pool gather / append   numpy views of each page as K [head][slot][d] and
-                         V [head][d][slot]
+                         V [head][d][slot], at 16- and 256-token pages
+  split_pools /          the same views over separate K and V buffers; the
+  whole_pool             two conversions undo each other
   layer, step            float64 brute force with a materialised softmax on
                          tiny shapes; all-zero weights leave x unchanged
   prefill                float64 brute force of the whole prompt at once with a
@@ -203,6 +205,24 @@ def pool_gather(pool, geo, bt_row, n):
                             geo.page_tokens, _p(bt_row, np.int32), n,
                             _p(kc, np.float32), _p(vc, np.float32))
     return kc, vc
+
+
+def split_pools(pool, geo):
+    """The same pages as separate K and V pools (the three-stage engine's
+    paged KV cache keeps K and V in two caches indexed by one page number,
+    its section 3.2): page p of the K pool is page p's K block, page p of
+    the V pool its V block.  Returns (k_pool, v_pool), uint16 copies."""
+    half = geo.page_elems // 2
+    pages = np.asarray(_u16(pool)).reshape(-1, geo.page_elems)
+    return pages[:, :half].reshape(-1).copy(), pages[:, half:].reshape(-1).copy()
+
+
+def whole_pool(k_pool, v_pool, geo):
+    """Inverse of split_pools: page p = K pool page p, then V pool page p."""
+    half = geo.page_elems // 2
+    k = np.asarray(_u16(k_pool)).reshape(-1, half)
+    v = np.asarray(_u16(v_pool)).reshape(-1, half)
+    return np.concatenate([k, v], axis=1).reshape(-1)
 
 
 def pool_append(pool, geo, bt_row, pos, k_bits, v_bits):

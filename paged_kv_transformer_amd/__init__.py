@@ -5,7 +5,8 @@ torch supplies device memory and the stream, every step of the computation
 runs in the library's HIP kernels.  There is no fallback: if ``libpkv.so``
 is missing the first call raises.
 
-Entry points (same names as the C ABI): ``kv_pool_create``, ``kv_append``,
+Entry points (same names as the C ABI): ``kv_pool_create``,
+``kv_pool_create_split``, ``kv_append``,
 ``paged_gqa_decode``, ``decoder_layer_decode``, ``decode_step``, plus
 ``workspace_bytes``, ``attention_workspace_bytes``, ``workspace_init``,
 ``rope_table``, ``pack_weight`` and ``device_error``.
@@ -42,7 +43,8 @@ class Config(ctypes.Structure):
 class Pool(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("bytes", ctypes.c_int64), ("page_bytes", ctypes.c_int64),
                 ("num_pages", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
-                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("v_base", ctypes.c_void_p)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -72,6 +74,7 @@ def lib():
         PP = ctypes.POINTER(Pool)
         sigs = {
             "kv_pool_create": (ctypes.c_int, [P, I64, I32, I32, I32, PP]),
+            "kv_pool_create_split": (ctypes.c_int, [P, P, I64, I32, I32, I32, PP]),
             "kv_append": (ctypes.c_int, [PP, P, I32, P, P, P, I32, P]),
             "paged_gqa_decode": (ctypes.c_int, [PP, P, I32, P, I32, P, I32, F, P, P, SZ, P]),
             "decoder_layer_decode": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(LayerWeights),
@@ -83,8 +86,8 @@ def lib():
             "pkv_prefill_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32]),
             "sample_tokens": (ctypes.c_int, [P, I32, I32, P, P, P, P, P, P, SZ, P]),
             "pkv_sample_workspace_bytes": (SZ, [I32, I32]),
-            "pkv_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32]),
-            "pkv_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+            "pkv_workspace_bytes": (SZ, [ctypes.POINTER(Config), I32, I32, I32]),
+            "pkv_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
             "pkv_workspace_init": (ctypes.c_int, [P, SZ, P]),
             "pkv_rope_table": (ctypes.c_int, [F, I32, I32, P, P, P]),
             "pkv_packed_weight_bytes": (SZ, [I32, I32, I32]),
@@ -152,6 +155,23 @@ def kv_pool_create(pool_tensor, num_kv_heads, head_dim=HEAD_DIM, page_tokens=PAG
     return out
 
 
+def kv_pool_create_split(k_tensor, v_tensor, num_kv_heads, head_dim=HEAD_DIM,
+                         page_tokens=PAGE_TOKENS):
+    """Two device tensors of equal size as separate K and V pools."""
+    for t in (k_tensor, v_tensor):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("pools must be contiguous GPU tensors")
+    nbytes = k_tensor.numel() * k_tensor.element_size()
+    if v_tensor.numel() * v_tensor.element_size() != nbytes:
+        raise ValueError("the K and V pools must have the same size")
+    out = Pool()
+    _check("kv_pool_create_split", lib().kv_pool_create_split(
+        k_tensor.data_ptr(), v_tensor.data_ptr(), nbytes, num_kv_heads, head_dim, page_tokens,
+        ctypes.byref(out)))
+    out._tensor = (k_tensor, v_tensor)
+    return out
+
+
 def kv_append(pool, block_table, positions, k_new, v_new, stream=None):
     B = positions.numel()
     bt = _dev(block_table, (torch.int32,), "block_table")
@@ -162,12 +182,14 @@ def kv_append(pool, block_table, positions, k_new, v_new, stream=None):
 
 # ------------------------------------------------------------- workspace ---
 
-def attention_workspace_bytes(num_q_heads, num_kv_heads, batch, max_pages, head_dim=HEAD_DIM):
-    return lib().pkv_attention_workspace_bytes(num_q_heads, num_kv_heads, head_dim, batch, max_pages)
+def attention_workspace_bytes(num_q_heads, num_kv_heads, batch, max_pages, head_dim=HEAD_DIM,
+                              page_tokens=PAGE_TOKENS):
+    return lib().pkv_attention_workspace_bytes(num_q_heads, num_kv_heads, head_dim, batch, max_pages,
+                                               page_tokens)
 
 
-def workspace_bytes(cfg, batch, max_pages):
-    return lib().pkv_workspace_bytes(ctypes.byref(cfg), batch, max_pages)
+def workspace_bytes(cfg, batch, max_pages, page_tokens=PAGE_TOKENS):
+    return lib().pkv_workspace_bytes(ctypes.byref(cfg), batch, max_pages, page_tokens)
 
 
 def alloc_workspace(nbytes, device="cuda", stream=None):

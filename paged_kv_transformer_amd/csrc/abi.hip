@@ -15,17 +15,37 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Supported head widths.
+// Supported head widths and page sizes.
 bool head_dim_ok(int D) { return D == 64 || D == 128; }
+bool page_tokens_ok(int pt) { return pt == 16 || pt == 256; }
+int pt_shift(int pt) { return pt == 256 ? 4 : 0; }
+
+// A block table of max_pages pages as 16-token attention tiles.
+int64_t table_tiles(int32_t max_pages, int32_t page_tokens) {
+  return (int64_t)max_pages << pt_shift(page_tokens);
+}
 
 int check_pool(const pkv_pool* p) {
   if (!p || !p->base) return -EINVAL;
-  if (!head_dim_ok(p->head_dim) || p->page_tokens != kPageTokens) return -ENOTSUP;
+  if (!head_dim_ok(p->head_dim) || !page_tokens_ok(p->page_tokens)) return -ENOTSUP;
   if (p->num_kv_heads < 1 || p->num_pages < 1 || p->bytes < 0) return -EINVAL;
-  if (p->page_bytes != 2LL * p->num_kv_heads * kPageTokens * p->head_dim * 2) return -EINVAL;
+  const int64_t block = 2LL * p->num_kv_heads * p->page_tokens * p->head_dim;  // bytes of K (or V)
+  if (p->page_bytes != (p->v_base ? block : 2 * block)) return -EINVAL;
   if ((int64_t)p->num_pages * p->page_bytes > p->bytes) return -EINVAL;
-  if (!aligned(p->base, 256)) return -EINVAL;
+  if (!aligned(p->base, 256) || !aligned(p->v_base, 256)) return -EINVAL;
   return 0;
+}
+
+// The kernels' view of a pool: whole pages in one buffer, or K and V pools.
+PoolView pool_view(const pkv_pool* p) {
+  PoolView v{};
+  const int64_t block = (int64_t)p->num_kv_heads * p->page_tokens * p->head_dim;  // elements
+  v.k = (uint16_t*)p->base;
+  v.v = p->v_base ? (uint16_t*)p->v_base : v.k + block;
+  v.stride = p->v_base ? block : 2 * block;
+  v.num_pages = p->num_pages;
+  v.pt_shift = pt_shift(p->page_tokens);
+  return v;
 }
 
 int check_heads(int32_t Hq, int32_t Hkv) {
@@ -71,7 +91,7 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
-size_t layer_ws_bytes(const pkv_config* c, int batch, int max_pages);
+size_t layer_ws_bytes(const pkv_config* c, int batch, int64_t max_tiles);
 
 // Common checks of decoder_layer_decode / decode_step.
 int check_layer_call(const pkv_config* cfg, const pkv_pool* pool, const float* rope_cos,
@@ -84,10 +104,11 @@ int check_layer_call(const pkv_config* cfg, const pkv_pool* pool, const float* r
   if (pool->num_kv_heads != cfg->num_key_value_heads || pool->head_dim != cfg->head_dim)
     return -EINVAL;
   if (batch < 0 || max_pages < 1) return -EINVAL;
-  if (batch > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
+  const int64_t tiles = table_tiles(max_pages, pool->page_tokens);
+  if (batch > 65535 || attn_max_splits(tiles) > 65535) return -ENOTSUP;
   if (!rope_cos || !rope_sin || !bt || !positions || !ws) return -EINVAL;
   if (!aligned(ws, 256)) return -EINVAL;
-  if (ws_bytes < layer_ws_bytes(cfg, batch, max_pages)) return -ENOSPC;
+  if (ws_bytes < layer_ws_bytes(cfg, batch, tiles)) return -ENOSPC;
   return 0;
 }
 
@@ -142,9 +163,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.D = D;
     a.K = H;
     a.x_plain = hidden_packed == nullptr;
-    a.pool = (uint16_t*)pool->base;
-    a.page_elems = pool->page_bytes / 2;
-    a.num_pages = pool->num_pages;
+    a.pv = pool_view(pool);
     a.bt_stride = max_pages;
     a.bt_row = bt_row;
     a.rcos = rope_cos;
@@ -165,9 +184,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
   {
     AttnArgs a{};
     a.q = q;
-    a.pool = (const uint16_t*)pool->base;
-    a.page_elems = pool->page_bytes / 2;
-    a.num_pages = pool->num_pages;
+    a.pv = pool_view(pool);
     a.bt = bt;
     a.bt_stride = max_pages;
     a.bt_row = bt_row;
@@ -182,7 +199,7 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = Hq / Hkv;
-    a.max_splits = attn_max_splits(max_pages);
+    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens));
     if ((rc = io(launch_attention(a, batch, kQSplit, st)))) return rc;
   }
 
@@ -269,14 +286,14 @@ int lm_row_tiles(const pkv_config* c, int B) {
   return (groups + 2 * p.rg - 1) / (2 * p.rg);
 }
 
-TiledLayout tiled_layout(const pkv_config* c, int B, int max_pages) {
+TiledLayout tiled_layout(const pkv_config* c, int B, int64_t max_tiles) {
   const size_t H = c->hidden_size, I = c->intermediate_size;
   const size_t QD = (size_t)c->num_attention_heads * c->head_dim;
   TiledLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   L.err = take(256);
-  L.attn_part = take(sizeof(float) * (size_t)B * c->num_key_value_heads * attn_max_splits(max_pages) *
+  L.attn_part = take(sizeof(float) * (size_t)B * c->num_key_value_heads * attn_max_splits(max_tiles) *
                      attn_rec(c->head_dim));
   L.q = take(2 * (size_t)B * QD * 2);
   L.x = take(sizeof(float) * B * H);
@@ -292,10 +309,10 @@ TiledLayout tiled_layout(const pkv_config* c, int B, int max_pages) {
 }
 
 // Workspace bytes of a layer call or step of `batch` sequences.
-size_t layer_ws_bytes(const pkv_config* c, int batch, int max_pages) {
-  if (batch >= kTiledMinBatch) return tiled_layout(c, batch, max_pages).total;
+size_t layer_ws_bytes(const pkv_config* c, int batch, int64_t max_tiles) {
+  if (batch >= kTiledMinBatch) return tiled_layout(c, batch, max_tiles).total;
   return ws_layout(batch, c->hidden_size, c->num_attention_heads, c->num_key_value_heads,
-                   c->intermediate_size, c->vocab_size, max_pages, true, c->head_dim)
+                   c->intermediate_size, c->vocab_size, max_tiles, true, c->head_dim)
       .total;
 }
 
@@ -329,9 +346,7 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
     a.K = H;
     a.D = D;
     a.q_split = q;
-    a.pool = (uint16_t*)pool->base;
-    a.page_elems = pool->page_bytes / 2;
-    a.num_pages = pool->num_pages;
+    a.pv = pool_view(pool);
     a.bt = bt;
     a.bt_row = max_pages;
     a.bt_stride = max_pages;
@@ -347,9 +362,7 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
   {
     AttnArgs a{};
     a.q = q;
-    a.pool = (const uint16_t*)pool->base;
-    a.page_elems = pool->page_bytes / 2;
-    a.num_pages = pool->num_pages;
+    a.pv = pool_view(pool);
     a.bt = bt;
     a.bt_stride = max_pages;
     a.bt_row = max_pages;
@@ -364,7 +377,7 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = Hq / Hkv;
-    a.max_splits = attn_max_splits(max_pages);
+    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens));
     if ((rc = io(launch_attention(a, B, kQSplit, st)))) return rc;
   }
   {
@@ -414,22 +427,46 @@ extern "C" {
 
 const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
 
-int kv_pool_create(void* dev_base, int64_t bytes, int32_t num_kv_heads, int32_t head_dim,
-                   int32_t page_tokens, pkv_pool* out) {
-  if (!out || !dev_base || bytes < 0 || num_kv_heads < 1) return -EINVAL;
-  if (!aligned(dev_base, 256)) return -EINVAL;
-  if (!head_dim_ok(head_dim) || page_tokens != kPageTokens) return -ENOTSUP;
-  const int64_t page_bytes = 2LL * num_kv_heads * page_tokens * head_dim * 2;
+}  // extern "C"
+
+namespace {
+
+// Both pool constructors: v_base null for whole pages in one buffer.
+int make_pool(void* k_base, void* v_base, int64_t bytes, int32_t num_kv_heads, int32_t head_dim,
+              int32_t page_tokens, pkv_pool* out) {
+  if (!out || !k_base || bytes < 0 || num_kv_heads < 1) return -EINVAL;
+  if (!aligned(k_base, 256) || !aligned(v_base, 256)) return -EINVAL;
+  if (!head_dim_ok(head_dim) || !page_tokens_ok(page_tokens)) return -ENOTSUP;
+  const int64_t block = 2LL * num_kv_heads * page_tokens * head_dim;  // bytes of K (or V)
+  const int64_t page_bytes = v_base ? block : 2 * block;
   const int64_t pages = bytes / page_bytes;
   if (pages < 1 || pages > INT32_MAX) return -ENOSPC;
-  out->base = dev_base;
+  out->base = k_base;
   out->bytes = bytes;
   out->page_bytes = page_bytes;
   out->num_pages = (int32_t)pages;
   out->page_tokens = page_tokens;
   out->num_kv_heads = num_kv_heads;
   out->head_dim = head_dim;
+  out->v_base = v_base;
   return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_pool_create(void* dev_base, int64_t bytes, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t page_tokens, pkv_pool* out) {
+  return make_pool(dev_base, nullptr, bytes, num_kv_heads, head_dim, page_tokens, out);
+}
+
+int kv_pool_create_split(void* k_base, void* v_base, int64_t bytes, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t page_tokens, pkv_pool* out) {
+  if (!v_base || k_base == v_base) return -EINVAL;
+  const uintptr_t k0 = (uintptr_t)k_base, v0 = (uintptr_t)v_base;
+  if (bytes > 0 && k0 < v0 + (uint64_t)bytes && v0 < k0 + (uint64_t)bytes) return -EINVAL;
+  return make_pool(k_base, v_base, bytes, num_kv_heads, head_dim, page_tokens, out);
 }
 
 int kv_append(const pkv_pool* pool, const int32_t* block_table, int32_t max_pages,
@@ -440,22 +477,24 @@ int kv_append(const pkv_pool* pool, const int32_t* block_table, int32_t max_page
   if (batch < 0 || max_pages < 1) return -EINVAL;
   if (batch == 0) return 0;
   if (!block_table || !positions || !k_new || !v_new) return -EINVAL;
-  return io(launch_kv_append((uint16_t*)pool->base, pool->page_bytes / 2, pool->num_pages,
-                             block_table, max_pages, positions, k_new, v_new, batch,
-                             pool->num_kv_heads, pool->head_dim, (hipStream_t)stream));
+  return io(launch_kv_append(pool_view(pool), block_table, max_pages, positions, k_new, v_new,
+                             batch, pool->num_kv_heads, pool->head_dim, (hipStream_t)stream));
 }
 
 size_t pkv_attention_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                     int32_t batch, int32_t max_pages) {
-  if (check_heads(num_q_heads, num_kv_heads) || !head_dim_ok(head_dim) || batch < 0 ||
-      max_pages < 1)
+                                     int32_t batch, int32_t max_pages, int32_t page_tokens) {
+  if (check_heads(num_q_heads, num_kv_heads) || !head_dim_ok(head_dim) ||
+      !page_tokens_ok(page_tokens) || batch < 0 || max_pages < 1)
     return 0;
-  return ws_layout(batch, 0, num_q_heads, num_kv_heads, 0, 0, max_pages, false, head_dim).total;
+  return ws_layout(batch, 0, num_q_heads, num_kv_heads, 0, 0, table_tiles(max_pages, page_tokens),
+                   false, head_dim)
+      .total;
 }
 
-size_t pkv_workspace_bytes(const pkv_config* cfg, int32_t batch, int32_t max_pages) {
-  if (check_cfg(cfg) || batch < 0 || max_pages < 1) return 0;
-  return layer_ws_bytes(cfg, batch, max_pages);
+size_t pkv_workspace_bytes(const pkv_config* cfg, int32_t batch, int32_t max_pages,
+                           int32_t page_tokens) {
+  if (check_cfg(cfg) || batch < 0 || max_pages < 1 || !page_tokens_ok(page_tokens)) return 0;
+  return layer_ws_bytes(cfg, batch, table_tiles(max_pages, page_tokens));
 }
 
 int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_heads,
@@ -467,18 +506,17 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   rc = check_heads(num_q_heads, pool->num_kv_heads);
   if (rc) return rc;
   if (batch < 0 || max_pages < 1) return -EINVAL;
-  if (batch > 65535 || attn_max_splits(max_pages) > 65535) return -ENOTSUP;
+  const int64_t tiles = table_tiles(max_pages, pool->page_tokens);
+  if (batch > 65535 || attn_max_splits(tiles) > 65535) return -ENOTSUP;
   if (batch == 0) return 0;
   if (!q || !block_table || !context_lens || !out || !workspace) return -EINVAL;
   if (!aligned(workspace, 256) || !isfinite(scale)) return -EINVAL;
   const WsLayout L =
-      ws_layout(batch, 0, num_q_heads, pool->num_kv_heads, 0, 0, max_pages, false, pool->head_dim);
+      ws_layout(batch, 0, num_q_heads, pool->num_kv_heads, 0, 0, tiles, false, pool->head_dim);
   if (ws_bytes < L.total) return -ENOSPC;
   AttnArgs a{};
   a.q = q;
-  a.pool = (const uint16_t*)pool->base;
-  a.page_elems = pool->page_bytes / 2;
-  a.num_pages = pool->num_pages;
+  a.pv = pool_view(pool);
   a.bt = block_table;
   a.bt_stride = max_pages;
   a.bt_row = max_pages;
@@ -491,7 +529,7 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   a.Hq = num_q_heads;
   a.Hkv = pool->num_kv_heads;
   a.G = num_q_heads / pool->num_kv_heads;
-  a.max_splits = attn_max_splits(max_pages);
+  a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens));
   a.D = pool->head_dim;
   return io(launch_attention(a, batch, kQBf16, (hipStream_t)stream));
 }
@@ -510,7 +548,7 @@ int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
   if (batch == 0) return 0;
   const hipStream_t st = (hipStream_t)stream;
   if (batch >= kTiledMinBatch) {
-    const TiledLayout T = tiled_layout(cfg, batch, max_pages);
+    const TiledLayout T = tiled_layout(cfg, batch, table_tiles(max_pages, pool->page_tokens));
     if ((rc = io(launch_prefill_norm(hidden, w->attn_norm, cfg->hidden_size, batch, cfg->rms_norm_eps,
                                      at<uint16_t>(workspace, T.xb), st))))
       return rc;
@@ -518,8 +556,8 @@ int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
                            hidden, nullptr, workspace, T, st);
   }
   const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
-                               cfg->num_key_value_heads, cfg->intermediate_size,
-                               cfg->vocab_size, max_pages, true, cfg->head_dim);
+                               cfg->num_key_value_heads, cfg->intermediate_size, cfg->vocab_size,
+                               table_tiles(max_pages, pool->page_tokens), true, cfg->head_dim);
   return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, max_pages, positions,
                    batch, hidden, nullptr, workspace, L, st);
 }
@@ -542,7 +580,7 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
   const hipStream_t st = (hipStream_t)stream;
   const int H = cfg->hidden_size, V = cfg->vocab_size;
   if (batch >= kTiledMinBatch) {
-    const TiledLayout T = tiled_layout(cfg, batch, max_pages);
+    const TiledLayout T = tiled_layout(cfg, batch, table_tiles(max_pages, pool->page_tokens));
     float* x = at<float>(workspace, T.x);
     uint16_t* xb = at<uint16_t>(workspace, T.xb);
     uint32_t* err = at<uint32_t>(workspace, T.err);
@@ -572,7 +610,8 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
     return io(launch_argmax_finalize(a.amax_part, 2 * lm_row_tiles(cfg, batch), batch, next_tokens, st));
   }
   const WsLayout L = ws_layout(batch, H, cfg->num_attention_heads, cfg->num_key_value_heads,
-                               cfg->intermediate_size, V, max_pages, true, cfg->head_dim);
+                               cfg->intermediate_size, V, table_tiles(max_pages, pool->page_tokens),
+                               true, cfg->head_dim);
   float* x = at<float>(workspace, L.x);
   float* x_p = at<float>(workspace, L.x_p);
   uint32_t* err = at<uint32_t>(workspace, L.err);
@@ -655,7 +694,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   if (num_tokens < 0 || max_pages < 1 || start_pos < 0) return -EINVAL;
   if (num_tokens > 65535) return -ENOTSUP;
   if (num_tokens == 0) return 0;
-  if ((int64_t)start_pos + num_tokens > (int64_t)max_pages * kPageTokens ||
+  if ((int64_t)start_pos + num_tokens > (int64_t)max_pages * pool->page_tokens ||
       (int64_t)start_pos + num_tokens > cfg->max_position_embeddings)
     return -EINVAL;
   if (cfg->num_hidden_layers < 1 || cfg->vocab_size < 1) return -EINVAL;
@@ -710,9 +749,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.K = H;
       a.D = D;
       a.q_split = q;
-      a.pool = (uint16_t*)pool->base;
-      a.page_elems = pool->page_bytes / 2;
-      a.num_pages = pool->num_pages;
+      a.pv = pool_view(pool);
       a.bt = bt;
       a.bt_row = 0;
       a.bt_stride = max_pages;
@@ -729,9 +766,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
     {
       PattnArgs a{};
       a.q = q;
-      a.pool = (const uint16_t*)pool->base;
-      a.page_elems = pool->page_bytes / 2;
-      a.num_pages = pool->num_pages;
+      a.pv = pool_view(pool);
       a.bt = bt;
       a.start_pos = start_pos;
       a.T = T;

@@ -106,11 +106,14 @@ paged_attention_kernel(const AttnArgs a) {
   // the table row; entries past the sequence are masked below), in flight
   // together: the empty asm makes the entries live before the length test,
   // so they are not sunk below it into a second round trip.
+  // Tiles are 16 tokens; a page holds 1 << sh of them (sh = 0 or 4).
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int sh = a.pv.pt_shift, PT = kTile << sh;
   const int32_t* btrow = a.bt + (size_t)b * a.bt_row;
   int page[PW];
 #pragma unroll
-  for (int i = 0; i < PW; ++i) page[i] = btrow[min(split * CP + NW * i + wu, a.bt_stride - 1)];
+  for (int i = 0; i < PW; ++i)
+    page[i] = btrow[min((split * CP + NW * i + wu) >> sh, a.bt_stride - 1)];
   const int n = a.lens[b] + a.len_add;
 #pragma unroll
   for (int i = 0; i < PW; ++i) asm volatile("" ::"s"(page[i]));
@@ -120,9 +123,9 @@ paged_attention_kernel(const AttnArgs a) {
   // output.
   const bool single = a.max_splits == 1;
   float* rec = a.part + (((size_t)b * a.Hkv + kvh) * a.max_splits + split) * REC;
-  const bool bad_len = n < 0 || n > a.bt_stride * kPageTokens;
+  const bool bad_len = n < 0 || (int64_t)n > (int64_t)a.bt_stride * PT;
   if (bad_len && split == 0 && tid == 0) set_error(a.err, ERR_LENGTH);
-  const int npages = bad_len ? 0 : (n + kPageTokens - 1) / kPageTokens;
+  const int npages = bad_len ? 0 : (n + kTile - 1) / kTile;  // tiles
   const int ns = npages > 0 ? (npages + CP - 1) / CP : 1;
   if (npages == 0 || split >= ns) {
     if (single) {
@@ -143,7 +146,7 @@ paged_attention_kernel(const AttnArgs a) {
   for (int i = 0; i < PW; ++i) {
     const int lp = split * CP + NW * i + wu;  // uniform across the wave
     const bool live = lp < npages;
-    const bool ok = (unsigned)page[i] < (unsigned)a.num_pages;
+    const bool ok = (unsigned)page[i] < (unsigned)a.pv.num_pages;
     bad |= live && !ok;
     lpv[i] = live && ok ? lp : -1;
     page[i] = live && ok ? page[i] : 0;
@@ -162,22 +165,23 @@ paged_attention_kernel(const AttnArgs a) {
     qraw[h] = *(const u32x4*)(qp + 32 * h);
     if (kSplitQ) qlraw[h] = *(const u32x4*)(qp + D + 32 * h);
   }
+  // the tile's first slot in its page
+  int sub[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) sub[i] = ((split * CP + NW * i + wu) & ((1 << sh) - 1)) * kTile;
   u32x4 kr[PW][NH];
   u32x2 vr[PW][NC];
-  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * D;
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
-    const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * D + 8 * grp;
+    const uint16_t* kp = a.pv.k + pv_k_index(a.pv, page[i], kvh, sub[i] + col, D) + 8 * grp;
 #pragma unroll
     for (int h = 0; h < NH; ++h) kr[i][h] = *(const u32x4*)(kp + 32 * h);
   }
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const uint16_t* pg = a.pool + (int64_t)page[i] * a.page_elems;
-    const uint16_t* vp = pg + vblk + ((int64_t)kvh * D + col) * kPageTokens + 4 * grp;
+    const uint16_t* vp = a.pv.v + pv_v_index(a.pv, page[i], kvh, col, sub[i], D) + 4 * grp;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
+    for (int c = 0; c < NC; ++c) vr[i][c] = *(const u32x2*)(vp + (int64_t)c * 16 * PT);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (bad && l == 0) set_error(a.err, ERR_PAGE);
@@ -200,7 +204,7 @@ paged_attention_kernel(const AttnArgs a) {
   // ---- scores: lane holds S[t = 4*grp + r][g = col] of each page
   bool full[PW];
 #pragma unroll
-  for (int i = 0; i < PW; ++i) full[i] = lpv[i] >= 0 && (lpv[i] + 1) * kPageTokens <= n;
+  for (int i = 0; i < PW; ++i) full[i] = lpv[i] >= 0 && (lpv[i] + 1) * kTile <= n;
   f32x4 s[PW];
   float mx = -INFINITY;
 #pragma unroll
@@ -216,7 +220,7 @@ paged_attention_kernel(const AttnArgs a) {
     if (!full[i]) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = lpv[i] * kPageTokens + 4 * grp + r;
+        const int t = lpv[i] * kTile + 4 * grp + r;
         acc[r] = lpv[i] >= 0 && t < n ? acc[r] : -INFINITY;
       }
     }
@@ -256,7 +260,7 @@ paged_attention_kernel(const AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     // unused slots of a partial page may hold anything (NaN included): zero them
-    const int nv = full[i] ? 4 : (lpv[i] < 0 ? 0 : n - (lpv[i] * kPageTokens + 4 * grp));
+    const int nv = full[i] ? 4 : (lpv[i] < 0 ? 0 : n - (lpv[i] * kTile + 4 * grp));
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const s16x4 vb = __builtin_bit_cast(s16x4, keep_first(vr[i][c], nv));

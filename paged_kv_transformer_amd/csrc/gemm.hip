@@ -297,26 +297,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         qo[D + j] = to_bf16_bits(y0 - bf16_lo(h0));
         qo[D + j + half] = to_bf16_bits(y1 - bf16_lo(h1));
       } else {
-        if (p < 0 || p / kPageTokens >= a.bt_stride) {
+        const int psh = 4 + a.pv.pt_shift, PT = 1 << psh;  // page tokens
+        if (p < 0 || (p >> psh) >= a.bt_stride) {
           set_error(a.err, ERR_LENGTH);
           continue;
         }
-        const int page = a.bt[(size_t)c * a.bt_row + p / kPageTokens];
-        if ((unsigned)page >= (unsigned)a.num_pages) {
+        const int page = a.bt[(size_t)c * a.bt_row + (p >> psh)];
+        if ((unsigned)page >= (unsigned)a.pv.num_pages) {
           set_error(a.err, ERR_PAGE);
           continue;
         }
-        uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
-        const int slot = p % kPageTokens;
+        const int slot = p & (PT - 1);
         if (is_k) {
-          uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * D;
+          uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, hd - a.Hq, slot, D);
           kp[j] = to_bf16_bits(y0);
           kp[j + half] = to_bf16_bits(y1);
         } else {
-          uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * D +
-                         (int64_t)(hd - a.Hq - a.Hkv) * D * kPageTokens + slot;
-          vp[j * kPageTokens] = to_bf16_bits(y0);
-          vp[(j + half) * kPageTokens] = to_bf16_bits(y1);
+          uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, 0, slot, D);
+          vp[(int64_t)j * PT] = to_bf16_bits(y0);
+          vp[(int64_t)(j + half) * PT] = to_bf16_bits(y1);
         }
       }
     }

@@ -9,23 +9,22 @@ namespace {
 // K block at [head][slot][d]) and V (into the V block at [head][d][slot]).
 // The engine's decode appends one token per sequence at its absolute
 // position: logical page pos / 16, slot pos % 16.
-__global__ void kv_append_kernel(uint16_t* pool, int64_t page_elems, int32_t num_pages,
-                                 const int32_t* bt, int32_t bt_stride, const int32_t* pos,
-                                 const uint16_t* k, const uint16_t* v, int Hkv, int D) {
+__global__ void kv_append_kernel(const PoolView pv, const int32_t* bt, int32_t bt_stride,
+                                 const int32_t* pos, const uint16_t* k, const uint16_t* v, int Hkv,
+                                 int D) {
   const int b = blockIdx.x;
   const int p = pos[b];
-  if (p < 0 || p / kPageTokens >= bt_stride) return;
-  const int page = bt[(size_t)b * bt_stride + p / kPageTokens];
-  if ((unsigned)page >= (unsigned)num_pages) return;
-  const int slot = p % kPageTokens;
-  uint16_t* pg = pool + (int64_t)page * page_elems;
-  uint16_t* vblk = pg + (int64_t)Hkv * kPageTokens * D;
+  const int psh = 4 + pv.pt_shift;  // log2 of the page's tokens
+  if (p < 0 || (p >> psh) >= bt_stride) return;
+  const int page = bt[(size_t)b * bt_stride + (p >> psh)];
+  if ((unsigned)page >= (unsigned)pv.num_pages) return;
+  const int slot = p & ((1 << psh) - 1);
   const uint16_t* kb = k + (size_t)b * Hkv * D;
   const uint16_t* vb = v + (size_t)b * Hkv * D;
   for (int i = threadIdx.x; i < Hkv * D; i += blockDim.x) {
     const int h = i / D, d = i % D;
-    pg[((int64_t)h * kPageTokens + slot) * D + d] = kb[i];
-    vblk[((int64_t)h * D + d) * kPageTokens + slot] = vb[i];
+    pv.k[pv_k_index(pv, page, h, slot, D) + d] = kb[i];
+    pv.v[pv_v_index(pv, page, h, d, slot, D)] = vb[i];
   }
 }
 
@@ -98,12 +97,10 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size
 
 }  // namespace
 
-hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_pages,
-                            const int32_t* bt, int32_t bt_stride, const int32_t* pos,
-                            const uint16_t* k, const uint16_t* v, int batch, int Hkv, int D,
-                            hipStream_t st) {
-  kv_append_kernel<<<batch, 256, 0, st>>>(pool, page_elems, num_pages, bt, bt_stride, pos, k, v,
-                                          Hkv, D);
+hipError_t launch_kv_append(const PoolView& pv, const int32_t* bt, int32_t bt_stride,
+                            const int32_t* pos, const uint16_t* k, const uint16_t* v, int batch,
+                            int Hkv, int D, hipStream_t st) {
+  kv_append_kernel<<<batch, 256, 0, st>>>(pv, bt, bt_stride, pos, k, v, Hkv, D);
   return hipGetLastError();
 }
 

@@ -9,7 +9,8 @@
 
 namespace pkv {
 
-constexpr int kPageTokens = 16;
+constexpr int kPageTokens = 16;   // the default page size; 256 is also supported
+constexpr int kTile = 16;          // tokens of one attention tile (one matrix-core tile)
 constexpr int kHeadDim = 64;       // the default head width; 128 is also supported
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;      // GQA group: one 16-wide matrix-core tile
@@ -81,11 +82,30 @@ inline int64_t packed_act_elems(int B, int K) { return (int64_t)((B + 15) / 16) 
 
 // --------------------------------------------------------- arguments ---
 
+// Where the pages live.  Page p of PT = kTile << pt_shift tokens holds a K
+// block [Hkv][PT][D] at k + p * stride and a V block [Hkv][D][PT] at
+// v + p * stride: one buffer of whole pages (v = k + the K block,
+// stride = both blocks), or separate K and V pools (stride = one block).
+struct PoolView {
+  uint16_t* k;
+  uint16_t* v;
+  int64_t stride;      // BF16 elements from one page to the next
+  int32_t num_pages;
+  int32_t pt_shift;    // log2(PT / 16): 0 (16-token pages) or 4 (256)
+};
+
+// Element d of token `slot`'s K (kv head h) and V of page `page`.
+__host__ __device__ inline int64_t pv_k_index(const PoolView& p, int page, int h, int slot, int D) {
+  return (int64_t)page * p.stride + ((int64_t)h * (kTile << p.pt_shift) + slot) * D;
+}
+__host__ __device__ inline int64_t pv_v_index(const PoolView& p, int page, int h, int d, int slot,
+                                               int D) {
+  return (int64_t)page * p.stride + ((int64_t)h * D + d) * (kTile << p.pt_shift) + slot;
+}
+
 struct AttnArgs {
   const uint16_t* q;       // BF16: [B][Hq][D], or [B][Hq][2][D] hi/lo split (kQSplit)
-  const uint16_t* pool;    // page pool base
-  int64_t page_elems;      // BF16 elements per page
-  int32_t num_pages;
+  PoolView pv;
   const int32_t* bt;       // sequence b's table starts at bt + b * bt_row
   int32_t bt_stride;       // table width (max_pages)
   int32_t bt_row;          // elements between sequences' rows (0: one shared row)
@@ -123,9 +143,7 @@ struct GemmArgs {
   int32_t ksplit;
   // EPI_QKV
   uint16_t* q_split;       // [B][Hq][2][D]: each head's q as BF16 hi, then lo
-  uint16_t* pool;
-  int64_t page_elems;
-  int32_t num_pages;
+  PoolView pv;
   const int32_t* bt;
   int32_t bt_stride;       // table width (max_pages)
   int32_t bt_row;          // elements between columns' rows (0: one shared row)
@@ -176,9 +194,7 @@ struct PgemmArgs {
   // bt + t * bt_row (bt_row 0: one sequence's table); positions outside
   // [0, max_pos) or past the table's bt_stride pages set device errors
   uint16_t* q_split;
-  uint16_t* pool;
-  int64_t page_elems;
-  int32_t num_pages;
+  PoolView pv;
   const int32_t* bt;
   int32_t bt_row, bt_stride;
   const int32_t* pos;
@@ -199,9 +215,7 @@ struct PgemmArgs {
 
 struct PattnArgs {
   const uint16_t* q;       // [T][Hq][2][D] BF16 hi, lo
-  const uint16_t* pool;
-  int64_t page_elems;
-  int32_t num_pages;
+  PoolView pv;
   const int32_t* bt;       // the sequence's table for this layer
   int32_t start_pos, T;
   float scale;
@@ -289,8 +303,10 @@ constexpr int kAttnPagesPerSplit = kAttnWaves * kAttnPW;
 // One split's partial record: m[16], l[16], o[16][64] floats.
 constexpr int attn_rec(int D) { return 16 + 16 + 16 * D; }
 
-inline int attn_max_splits(int max_pages) {
-  return (max_pages + kAttnPagesPerSplit - 1) / kAttnPagesPerSplit;
+// Splits of a block table of max_tiles 16-token tiles (max_pages pages of
+// 16 << pt_shift tokens: max_tiles = max_pages << pt_shift).
+inline int attn_max_splits(int64_t max_tiles) {
+  return (int)((max_tiles + kAttnPagesPerSplit - 1) / kAttnPagesPerSplit);
 }
 
 // A GEMM launch: `rg` groups of 16 output rows per workgroup, `nw` waves
@@ -372,13 +388,14 @@ struct WsLayout {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Workspace layout.  layer == false: attention only (no activations).
-inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int max_pages, bool layer,
+// max_tiles: the block table's width in 16-token tiles.
+inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int64_t max_tiles, bool layer,
                           int D = kHeadDim) {
   WsLayout w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
   w.err = take(256);
-  w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_pages) * attn_rec(D));
+  w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_tiles) * attn_rec(D));
   if (layer) {
     w.q = take(sizeof(float) * (size_t)B * Hq * D);  // BF16 hi + lo per value
     w.o_p = take(sizeof(float) * (size_t)packed_act_elems(B, Hq * D));
@@ -407,10 +424,9 @@ constexpr int kQBf16 = 0;   // BF16 q, the matrix operand as it is
 constexpr int kQSplit = 1;  // an FP32 q stored as BF16 hi and lo halves
 hipError_t launch_attention(const AttnArgs& a, int batch, int qmode, hipStream_t st);
 hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_t st);
-hipError_t launch_kv_append(uint16_t* pool, int64_t page_elems, int32_t num_pages,
-                            const int32_t* bt, int32_t bt_stride, const int32_t* pos,
-                            const uint16_t* k, const uint16_t* v, int batch, int Hkv, int D,
-                            hipStream_t st);
+hipError_t launch_kv_append(const PoolView& pv, const int32_t* bt, int32_t bt_stride,
+                            const int32_t* pos, const uint16_t* k, const uint16_t* v, int batch,
+                            int Hkv, int D, hipStream_t st);
 hipError_t launch_embed(const uint16_t* E_packed, int V, int H, const int32_t* tok, float* x,
                         float* x_packed, int batch, uint32_t* err, hipStream_t st);
 hipError_t launch_pack_weight(const uint16_t* src, int rows, int cols, int kind, uint16_t* dst,

@@ -345,7 +345,8 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
           set_error(a.err, ERR_ROPE);
           ok = false;
         }
-        if (ok && !is_q && (p < 0 || p / kPageTokens >= a.bt_stride)) {
+        const int psh = 4 + a.pv.pt_shift, PT = 1 << psh;  // page tokens
+        if (ok && !is_q && (p < 0 || (p >> psh) >= a.bt_stride)) {
           set_error(a.err, ERR_LENGTH);
           ok = false;
         }
@@ -378,20 +379,18 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
             *(u32x2*)(qo + D) = (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
           } else {
-            const int page = a.bt[(size_t)t * a.bt_row + p / kPageTokens];
-            if ((unsigned)page >= (unsigned)a.num_pages) {
+            const int page = a.bt[(size_t)t * a.bt_row + (p >> psh)];
+            if ((unsigned)page >= (unsigned)a.pv.num_pages) {
               set_error(a.err, ERR_PAGE);
             } else {
-              uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
-              const int slot = p % kPageTokens;
+              const int slot = p & (PT - 1);
               if (is_k) {
-                uint16_t* kp = pg + ((int64_t)(hd - a.Hq) * kPageTokens + slot) * D + jj;
+                uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, hd - a.Hq, slot, D) + jj;
                 *(u32x2*)kp = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
               } else {
-                uint16_t* vp = pg + (int64_t)a.Hkv * kPageTokens * D +
-                               ((int64_t)(hd - a.Hq - a.Hkv) * D + jj) * kPageTokens + slot;
+                uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, jj, slot, D);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vp[e * kPageTokens] = to_bf16_bits(y[e]);
+                for (int e = 0; e < 4; ++e) vp[(int64_t)e * PT] = to_bf16_bits(y[e]);
               }
             }
           }
@@ -493,9 +492,10 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
   if (t0 >= a.T) return;
   const int tend = min(t0 + tpw, a.T);
   const int pmax = a.start_pos + tend - 1;  // the group's last position
-  const int npages = pmax / kPageTokens + 1;
+  const int npages = pmax / kTile + 1;      // 16-token tiles
   const int pmin = a.start_pos + t0;        // its first: keys up to here need no mask
-  // this wave's pages [pb, pe)
+  // this wave's tiles [pb, pe); a page holds 1 << sh tiles
+  const int sh = a.pv.pt_shift, PT = kTile << sh;
   const int npw = (npages + 3) / 4;
   const int pb = w * npw, pe = min(npages, pb + npw);
 
@@ -518,27 +518,27 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     }
   }
 
-  const int64_t vblk = (int64_t)a.Hkv * kPageTokens * D;
   struct Chunk {
     u32x4 k[kPW][NH];
     u32x2 v[kPW][NC];
   };
   bool bad = false;
-  // pages past the wave's range read its last page and are masked
+  // tiles past the wave's range read its last tile and are masked
   auto load = [&](Chunk& C, int lp0) {
 #pragma unroll
     for (int i = 0; i < kPW; ++i) {
-      int page = a.bt[min(lp0 + i, pe - 1)];
-      const bool ok = (unsigned)page < (unsigned)a.num_pages;
+      const int lt = min(lp0 + i, pe - 1);
+      int page = a.bt[lt >> sh];
+      const int sub = (lt & ((1 << sh) - 1)) * kTile;
+      const bool ok = (unsigned)page < (unsigned)a.pv.num_pages;
       bad |= !ok;
       page = ok ? page : 0;
-      const uint16_t* pg = a.pool + (int64_t)page * a.page_elems;
-      const uint16_t* kp = pg + ((int64_t)kvh * kPageTokens + col) * D + 8 * grp;
+      const uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, kvh, sub + col, D) + 8 * grp;
 #pragma unroll
       for (int h = 0; h < NH; ++h) C.k[i][h] = *(const u32x4*)(kp + 32 * h);
-      const uint16_t* vp = pg + vblk + ((int64_t)kvh * D + col) * kPageTokens + 4 * grp;
+      const uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, kvh, col, sub, D) + 4 * grp;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vp + c * 16 * kPageTokens);
+      for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vp + (int64_t)c * 16 * PT);
     }
   };
 
@@ -559,9 +559,9 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
         acc = mfma_k32(C.k[i][h], qh[h], acc);
         acc = mfma_k32(C.k[i][h], ql[h], acc);
       }
-      const int kp0 = (lp0 + i) * kPageTokens;
+      const int kp0 = (lp0 + i) * kTile;
       inr[i] = lp0 + i < pe;                              // uniform
-      full[i] = inr[i] && kp0 + kPageTokens - 1 <= pmin;  // uniform
+      full[i] = inr[i] && kp0 + kTile - 1 <= pmin;  // uniform
       if (!full[i]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = inr[i] && kp0 + 4 * grp + r <= lim ? acc[r] : -INFINITY;
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     for (int i = 0; i < kPW; ++i) {
       // slots past the group's last position, or pages past the wave's
       // range, may hold anything: zero them
-      const int nv = inr[i] ? pmax - ((lp0 + i) * kPageTokens + 4 * grp) + 1 : 0;
+      const int nv = inr[i] ? pmax - ((lp0 + i) * kTile + 4 * grp) + 1 : 0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         u32x2 vv = C.v[i][c];

@@ -30,7 +30,7 @@ PAGE_TOKENS = 16
 _ID = {"embed": 1, "final_norm": 2, "attn_norm": 10, "w_qkv": 11, "w_o": 12,
        "mlp_norm": 13, "w_gate_up": 14, "w_down": 15, "hidden": 20, "tokens": 21,
        "lens": 22, "pool": 23, "perm": 24, "q": 25, "k_new": 26, "v_new": 27,
-       "prompt": 28, "logits": 29, "sample": 30}
+       "prompt": 28, "logits": 29, "sample": 30, "pool_k": 31, "pool_v": 32}
 
 LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
 
@@ -168,16 +168,22 @@ def random_pool(seed, num_pages, elems_per_page):
     return bf16_normal(seed, "pool", (num_pages * elems_per_page,))
 
 
-def pages_for(n_tokens):
-    return (np.asarray(n_tokens, dtype=np.int64) + PAGE_TOKENS - 1) // PAGE_TOKENS
+def random_split_pools(seed, num_pages, elems_per_page):
+    """Separate K and V pools (half a page each per page) as N(0,1) BF16."""
+    half = num_pages * elems_per_page // 2
+    return bf16_normal(seed, "pool_k", (half,)), bf16_normal(seed, "pool_v", (half,))
 
 
-def block_tables(seed, layers, n_tokens, num_pages, max_pages=None, fill=-1):
+def pages_for(n_tokens, page_tokens=PAGE_TOKENS):
+    return (np.asarray(n_tokens, dtype=np.int64) + page_tokens - 1) // page_tokens
+
+
+def block_tables(seed, layers, n_tokens, num_pages, max_pages=None, fill=-1, page_tokens=PAGE_TOKENS):
     """int32 [layers, B, max_pages]: the (layer, seq, logical page) entries
     that hold tokens 0..n_b-1 take physical pages from one random
     permutation of the pool, in that order; the other entries are `fill`."""
     n_tokens = np.asarray(n_tokens, dtype=np.int64)
-    need = pages_for(n_tokens)
+    need = pages_for(n_tokens, page_tokens)
     if max_pages is None:
         max_pages = int(max(1, need.max()))
     total = int(need.sum()) * layers
@@ -205,6 +211,7 @@ class Workload:
     block_tables: np.ndarray       # int32 [L, B, max_pages]
     pool: np.ndarray = None        # uint16 [num_pages * page_elems]
     extra: dict = field(default_factory=dict)
+    page_tokens: int = PAGE_TOKENS
 
     @property
     def max_pages(self):
@@ -216,16 +223,16 @@ class Workload:
 
 
 def decode_workload(name, shape, seed, positions, layers=None, num_pages=None,
-                    max_pages=None, with_pool=True):
+                    max_pages=None, with_pool=True, page_tokens=PAGE_TOKENS):
     """Inputs for a decode step: token p_b is new, 0..p_b-1 are cached in the
     pool.  The pool is sized to fit unless num_pages is given."""
     positions = np.asarray(positions, dtype=np.int32)
     L = shape.layers if layers is None else layers
-    need = int(pages_for(positions + 1).sum()) * L
+    need = int(pages_for(positions + 1, page_tokens).sum()) * L
     npages = need if num_pages is None else num_pages
-    bt = block_tables(seed, L, positions + 1, npages, max_pages)
-    pool = random_pool(seed, npages, page_elems(shape)) if with_pool else None
-    return Workload(name, shape, len(positions), positions, npages, bt, pool)
+    bt = block_tables(seed, L, positions + 1, npages, max_pages, page_tokens=page_tokens)
+    pool = random_pool(seed, npages, page_elems(shape, page_tokens=page_tokens)) if with_pool else None
+    return Workload(name, shape, len(positions), positions, npages, bt, pool, page_tokens=page_tokens)
 
 
 def c1_layer(seed=1001):
@@ -242,19 +249,21 @@ def c2_lens(seed=1002, batch=16, max_len=2048):
     return rng(seed, "lens").integers(1, max_len + 1, size=batch).astype(np.int32)
 
 
-def c2_attention(seed=1002, batch=16, pool_bytes=128 << 20, shape=LLAMA1B):
+def c2_attention(seed=1002, batch=16, pool_bytes=128 << 20, shape=LLAMA1B, page_tokens=PAGE_TOKENS):
     """Paged GQA attention alone, Llama-3.2-1B heads (or another shape's),
-    lengths U[1,2048], pages drawn from a 128 MiB pool with shuffled tables;
-    Q N(0,1) BF16, scale 1/sqrt(head_dim)."""
+    lengths U[1,2048], pages of page_tokens tokens drawn from a 128 MiB pool
+    with shuffled tables; Q N(0,1) BF16, scale 1/sqrt(head_dim)."""
     lens = c2_lens(seed, batch)
-    npages = pool_bytes // (page_elems(shape) * 2)
-    bt = block_tables(seed, 1, lens, npages, max_pages=128)[0]
-    pool = random_pool(seed, npages, page_elems(shape))
+    pe = page_elems(shape, page_tokens=page_tokens)
+    npages = pool_bytes // (pe * 2)
+    bt = block_tables(seed, 1, lens, npages, max_pages=2048 // page_tokens, page_tokens=page_tokens)[0]
+    pool = random_pool(seed, npages, pe)
     q = bf16_normal(seed, "q", (batch, shape.heads, shape.head_dim))
-    name = "paged GQA attention, %d/%d heads, d%d, batch %d, lens U[1,2048], %d MiB pool" % (
-        shape.heads, shape.kv_heads, shape.head_dim, batch, pool_bytes >> 20)
+    name = "paged GQA attention, %d/%d heads, d%d, batch %d, lens U[1,2048], %d-token pages, %d MiB pool" % (
+        shape.heads, shape.kv_heads, shape.head_dim, batch, page_tokens, pool_bytes >> 20)
     return {"name": name, "shape": shape, "lens": lens, "num_pages": int(npages), "block_table": bt,
-            "pool": pool, "q": q, "scale": 1.0 / float(np.sqrt(shape.head_dim))}
+            "pool": pool, "q": q, "scale": 1.0 / float(np.sqrt(shape.head_dim)),
+            "page_tokens": page_tokens}
 
 
 def c3_step(seed=1003, with_pool=True, layers=None):

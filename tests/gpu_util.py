@@ -22,42 +22,62 @@ def host_u16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def attention_gpu(pool_np, kv_heads, q_bits, bt, lens, scale, ws=None):
+def device_pool(pool_np, kv_heads, head_dim=64, page_tokens=16):
+    """The pool on the GPU: pool_np is one array of whole pages, or a
+    (k_pool, v_pool) pair for separate K and V pools.  Returns (pkv Pool,
+    a reader of the device pool as whole pages: the separate pools are put
+    back together by the oracle's layout definition)."""
+    geo = oracle.PoolGeometry(kv_heads, head_dim, page_tokens)
+    if isinstance(pool_np, tuple):
+        kt, vt = dev(pool_np[0]), dev(pool_np[1])
+        P = pkv.kv_pool_create_split(kt, vt, kv_heads, head_dim=head_dim, page_tokens=page_tokens)
+        return P, lambda: oracle.whole_pool(host_u16(kt), host_u16(vt), geo)
+    t = dev(pool_np)
+    P = pkv.kv_pool_create(t, kv_heads, head_dim=head_dim, page_tokens=page_tokens)
+    return P, lambda: host_u16(t)
+
+
+def whole(pool_np, geo):
+    """The oracle's input: whole pages (separate pools put together)."""
+    return oracle.whole_pool(pool_np[0], pool_np[1], geo) if isinstance(pool_np, tuple) else pool_np
+
+
+def attention_gpu(pool_np, kv_heads, q_bits, bt, lens, scale, ws=None, page_tokens=16):
     """Run paged_gqa_decode; returns (out [B, Hq, D] float32, device error
     bits).  D is q's last dimension, also the pool's head width."""
     B, Hq, D = q_bits.shape
-    pool_t = dev(pool_np)
-    pool = pkv.kv_pool_create(pool_t, kv_heads, head_dim=D)
+    pool, _ = device_pool(pool_np, kv_heads, D, page_tokens)
     bt = np.ascontiguousarray(bt, dtype=np.int32)
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
     if ws is None:
-        ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(Hq, kv_heads, B, bt.shape[1], head_dim=D))
+        ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(Hq, kv_heads, B, bt.shape[1], head_dim=D,
+                                                               page_tokens=page_tokens))
     pkv.paged_gqa_decode(pool, dev(q_bits), dev(bt), dev(np.asarray(lens, dtype=np.int32)),
                          scale, out, ws)
     err = pkv.device_error(ws)
     return out.cpu().numpy(), err
 
 
-def attention_oracle(pool_np, kv_heads, q_bits, bt, lens, scale, seqs=None):
-    geo = oracle.PoolGeometry(kv_heads, q_bits.shape[2])
-    return oracle.paged_attention(pool_np, geo, oracle.bf16_to_f32(q_bits), bt, lens, scale, seqs)
+def attention_oracle(pool_np, kv_heads, q_bits, bt, lens, scale, seqs=None, page_tokens=16):
+    geo = oracle.PoolGeometry(kv_heads, q_bits.shape[2], page_tokens)
+    return oracle.paged_attention(whole(pool_np, geo), geo, oracle.bf16_to_f32(q_bits), bt, lens, scale, seqs)
 
 
-def layer_gpu(shape, lw, hidden, pool_np, bt, positions, max_pos=None):
-    """decoder_layer_decode on one layer; returns (hidden_out, pool_after, err)."""
+def layer_gpu(shape, lw, hidden, pool_np, bt, positions, max_pos=None, page_tokens=16):
+    """decoder_layer_decode on one layer; returns (hidden_out, pool_after as
+    whole pages, err)."""
     B = len(positions)
     bt = np.ascontiguousarray(bt, dtype=np.int32)
     mp = max_pos or int(max(positions)) + 1
     cfg = pkv.make_config(shape, max_pos=mp, layers=1)
     layer = pkv.upload_layer(lw, head_dim=shape.head_dim)
     c, s = pkv.rope_table(shape.theta, mp, head_dim=shape.head_dim)
-    pool_t = dev(pool_np)
-    pool = pkv.kv_pool_create(pool_t, shape.kv_heads, head_dim=shape.head_dim)
+    pool, read_pool = device_pool(pool_np, shape.kv_heads, shape.head_dim, page_tokens)
     h = torch.from_numpy(np.ascontiguousarray(hidden, dtype=np.float32)).cuda()
-    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bt.shape[1]))
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bt.shape[1], page_tokens))
     pkv.decoder_layer_decode(cfg, layer, c, s, pool, dev(bt), dev(np.asarray(positions, np.int32)), h, ws)
     err = pkv.device_error(ws)
-    return h.cpu().numpy(), host_u16(pool_t), err
+    return h.cpu().numpy(), read_pool(), err
 
 
 def expected_pool_after(pool_np, geo, bt, positions, k_new, v_new, seqs=None):
@@ -136,22 +156,22 @@ def check_prefill_pool(got, want, base, geo, bts, start, T, layers):
 
 
 def step_gpu(shape, weights, pool_np, bts, positions, tokens, want_logits=True, max_pos=None,
-             want_pool=True):
-    """decode_step; returns (logits or None, next_tokens, pool_after or None, err)."""
+             want_pool=True, page_tokens=16):
+    """decode_step; returns (logits or None, next_tokens, pool_after (whole
+    pages) or None, err)."""
     B = len(positions)
     mp = max_pos or int(max(positions)) + 1
     cfg = pkv.make_config(shape, max_pos=mp)
     model = pkv.upload_model(weights, shape.theta, mp, head_dim=shape.head_dim)
-    pool_t = dev(pool_np)
-    pool = pkv.kv_pool_create(pool_t, shape.kv_heads, head_dim=shape.head_dim)
+    pool, read_pool = device_pool(pool_np, shape.kv_heads, shape.head_dim, page_tokens)
     bts = np.ascontiguousarray(bts, dtype=np.int32)
-    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bts.shape[2]))
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, bts.shape[2], page_tokens))
     logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda") if want_logits else None
     nxt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
     pkv.decode_step(cfg, model, pool, dev(bts), dev(np.asarray(positions, np.int32)),
                     dev(np.asarray(tokens, np.int32)), logits, nxt, ws)
     err = pkv.device_error(ws)
-    pool_after = host_u16(pool_t) if want_pool else None
+    pool_after = read_pool() if want_pool else None
     return (None if logits is None else logits.cpu().numpy()), nxt.cpu().numpy(), pool_after, err
 
 

@@ -55,14 +55,41 @@ def test_kv_pool_create_geometry_and_errors():
     assert p.page_bytes == 65536 and p.num_pages == 2048 and p.head_dim == 128
     assert L.kv_pool_create(FAKE, 1 << 20, 8, 96, 16, ctypes.byref(p)) == ENOTSUP
     assert L.kv_pool_create(FAKE, 1 << 20, 8, 256, 16, ctypes.byref(p)) == ENOTSUP
-    assert L.kv_pool_create(FAKE, 1 << 20, 8, 64, 256, ctypes.byref(p)) == ENOTSUP
+    assert L.kv_pool_create(FAKE, 1 << 20, 8, 64, 128, ctypes.byref(p)) == ENOTSUP
     assert L.kv_pool_create(FAKE, 1000, 8, 64, 16, ctypes.byref(p)) == ENOSPC
     assert L.kv_pool_create(FAKE, 1 << 20, 8, 64, 16, None) == EINVAL
 
 
+def test_page_sizes_and_split_pools():
+    p = pkv.Pool()
+    # 256-token pages: 16 times the bytes of a 16-token page
+    assert L.kv_pool_create(FAKE, 128 << 20, 8, 64, 256, ctypes.byref(p)) == 0
+    assert p.page_bytes == 16 * 32768 and p.num_pages == 256 and p.page_tokens == 256
+    assert not p.v_base
+    assert L.kv_pool_create(FAKE, 128 << 20, 8, 64, 32, ctypes.byref(p)) == ENOTSUP
+    # separate K and V pools: each page of each pool holds one block
+    V = FAKE + (1 << 30)
+    assert L.kv_pool_create_split(FAKE, V, 64 << 20, 8, 64, 16, ctypes.byref(p)) == 0
+    assert p.page_bytes == 16384 and p.num_pages == 4096 and p.v_base == V
+    assert L.kv_pool_create_split(FAKE, V, 64 << 20, 8, 128, 256, ctypes.byref(p)) == 0
+    assert p.page_bytes == 8 * 256 * 128 * 2 and p.num_pages == 128
+    assert L.kv_pool_create_split(FAKE, None, 64 << 20, 8, 64, 16, ctypes.byref(p)) == EINVAL
+    assert L.kv_pool_create_split(FAKE, FAKE, 64 << 20, 8, 64, 16, ctypes.byref(p)) == EINVAL
+    assert L.kv_pool_create_split(FAKE, FAKE + (32 << 20), 64 << 20, 8, 64, 16,
+                                  ctypes.byref(p)) == EINVAL              # overlapping
+    assert L.kv_pool_create_split(FAKE, V + 8, 64 << 20, 8, 64, 16, ctypes.byref(p)) == EINVAL
+    # a table of 8 pages of 256 tokens needs the splits of 128 pages of 16
+    assert (L.pkv_attention_workspace_bytes(32, 8, 64, 16, 8, 256)
+            == L.pkv_attention_workspace_bytes(32, 8, 64, 16, 128, 16))
+    assert L.pkv_attention_workspace_bytes(32, 8, 64, 16, 8, 64) == 0
+    cfg = _cfg()
+    assert (L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 8, 256)
+            == L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 128, 16))
+
+
 def test_paged_gqa_decode_validation():
     p = _pool()
-    ws_need = L.pkv_attention_workspace_bytes(32, 8, 64, 16, 128)
+    ws_need = L.pkv_attention_workspace_bytes(32, 8, 64, 16, 128, 16)
     assert ws_need > 0
     args = lambda **kw: [ctypes.byref(kw.get("pool", p)), kw.get("q", FAKE), kw.get("hq", 32),
                          kw.get("bt", FAKE), kw.get("mp", 128), kw.get("lens", FAKE), kw.get("b", 16),
@@ -95,7 +122,7 @@ def test_layer_and_step_validation():
     p = _pool()
     lw = pkv.LayerWeights(*([FAKE] * 6))
     cfg = _cfg()
-    need = L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 128)
+    need = L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 128, 16)
     assert need > 0
 
     def layer(c=cfg, w=lw, pool=p, b=16, wsb=need, ws=FAKE, hidden=FAKE):
@@ -143,18 +170,18 @@ def test_rope_table_and_workspace_validation():
     assert L.pkv_workspace_init(None, 256, None) == EINVAL
     assert L.pkv_workspace_init(FAKE + 1, 256, None) == EINVAL
     assert L.pkv_device_error(None, None) == EINVAL
-    assert L.pkv_attention_workspace_bytes(32, 8, 96, 16, 128) == 0
+    assert L.pkv_attention_workspace_bytes(32, 8, 96, 16, 128, 16) == 0
     # the split records hold a head's FP32 partial output: twice as wide at D 128
-    w64 = L.pkv_attention_workspace_bytes(32, 8, 64, 16, 128)
-    w128 = L.pkv_attention_workspace_bytes(32, 8, 128, 16, 128)
+    w64 = L.pkv_attention_workspace_bytes(32, 8, 64, 16, 128, 16)
+    w128 = L.pkv_attention_workspace_bytes(32, 8, 128, 16, 128, 16)
     assert w64 > 0 and w128 > w64
-    assert L.pkv_workspace_bytes(None, 1, 1) == 0
+    assert L.pkv_workspace_bytes(None, 1, 1, 16) == 0
 
 
 def test_head_dim_128_config_and_packing_sizes():
     cfg = _cfg(head_dim=128)
-    assert L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 64) > L.pkv_workspace_bytes(ctypes.byref(_cfg()), 16, 64)
-    assert L.pkv_workspace_bytes(ctypes.byref(_cfg(head_dim=96)), 16, 64) == 0
+    assert L.pkv_workspace_bytes(ctypes.byref(cfg), 16, 64, 16) > L.pkv_workspace_bytes(ctypes.byref(_cfg()), 16, 64, 16)
+    assert L.pkv_workspace_bytes(ctypes.byref(_cfg(head_dim=96)), 16, 64, 16) == 0
     assert L.pkv_packed_weight_bytes(3 * 128, 64, pkv.PACK_QKV128) == 3 * 128 * 64 * 2
     assert L.pkv_packed_weight_bytes(3 * 64, 64, pkv.PACK_QKV128) == 0      # not whole 128-wide heads
     assert L.pkv_packed_weight_bytes(3 * 64, 64, pkv.PACK_QKV) == 3 * 64 * 64 * 2
@@ -163,8 +190,8 @@ def test_head_dim_128_config_and_packing_sizes():
 
 def test_workspace_sizes_grow_with_batch_and_pages():
     cfg = _cfg()
-    a = L.pkv_workspace_bytes(ctypes.byref(cfg), 1, 64)
-    b = L.pkv_workspace_bytes(ctypes.byref(cfg), 64, 64)
-    c = L.pkv_workspace_bytes(ctypes.byref(cfg), 64, 128)
+    a = L.pkv_workspace_bytes(ctypes.byref(cfg), 1, 64, 16)
+    b = L.pkv_workspace_bytes(ctypes.byref(cfg), 64, 64, 16)
+    c = L.pkv_workspace_bytes(ctypes.byref(cfg), 64, 128, 16)
     assert 0 < a < b < c
     assert all(x % 256 == 0 for x in (a, b, c))

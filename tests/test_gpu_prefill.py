@@ -22,7 +22,7 @@ import torch
 import oracle
 import paged_kv_transformer_amd as pkv
 import synth
-from gpu_util import APPEND_REL, check_argmax_rule, check_prefill_pool, dev, host_u16, say
+from gpu_util import APPEND_REL, check_argmax_rule, check_prefill_pool, dev, device_pool, host_u16, say
 
 pytestmark = pytest.mark.gpu
 
@@ -41,20 +41,21 @@ def _inputs(shape, seed, start, T, weights=None):
     return w, wl.pool, wl.block_tables[:, 0], tokens
 
 
-def prefill_gpu(shape, weights, pool_np, bts, start, tokens, model=None):
+def prefill_gpu(shape, weights, pool_np, bts, start, tokens, model=None, page_tokens=16):
+    """prefill through the C ABI; returns (logits, next token, pool after as
+    whole pages, device error bits).  pool_np: whole pages or a (K, V) pair."""
     T = len(tokens)
     mp = start + T
     cfg = pkv.make_config(shape, max_pos=mp)
     model = model or pkv.upload_model(weights, shape.theta, mp, head_dim=shape.head_dim)
-    pool_t = dev(pool_np)
-    pool = pkv.kv_pool_create(pool_t, shape.kv_heads, head_dim=shape.head_dim)
+    pool, read_pool = device_pool(pool_np, shape.kv_heads, shape.head_dim, page_tokens)
     bts = np.ascontiguousarray(bts, dtype=np.int32)
     ws = pkv.alloc_workspace(pkv.prefill_workspace_bytes(cfg, T, bts.shape[1]))
     logits = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
     nxt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     pkv.prefill(cfg, model, pool, dev(bts), start, dev(tokens), logits, nxt, ws)
     err = pkv.device_error(ws)
-    return logits.cpu().numpy(), int(nxt.cpu()[0]), host_u16(pool_t), err
+    return logits.cpu().numpy(), int(nxt.cpu()[0]), read_pool(), err
 
 
 def _oracle_check(shape, w, pool, bts, start, tokens, logits, nxt, pool_after, label):

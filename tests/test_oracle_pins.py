@@ -296,6 +296,41 @@ def test_pool_append_matches_reshaped_view(pos, D):
     assert np.count_nonzero(got != pool) <= 2 * 8 * D
 
 
+@pytest.mark.parametrize("T,D", [(16, 64), (256, 64), (256, 128)])
+def test_pool_gather_any_page_size_matches_reshaped_view(T, D):
+    g = _rng(20, T, D)
+    geo = oracle.PoolGeometry(kv_heads=2, head_dim=D, page_tokens=T)
+    npages = 6
+    pool = synth.to_bf16_bits(g.standard_normal(npages * geo.page_elems).astype(np.float32))
+    bt = g.permutation(npages)[:4].astype(np.int32)
+    n = 3 * T + 5
+    kc, vc = oracle.pool_gather(pool, geo, bt, n)
+    K, V = brute.gather(pool, 2, D, bt, n, page_tokens=T)
+    assert np.array_equal(kc, K.reshape(n, 2 * D).astype(np.float32))
+    assert np.array_equal(vc, V.reshape(n, 2 * D).astype(np.float32))
+    # append at a slot in the middle of a 256-token page
+    pos = n - 3
+    k = synth.to_bf16_bits(g.standard_normal(2 * D).astype(np.float32))
+    v = synth.to_bf16_bits(g.standard_normal(2 * D).astype(np.float32))
+    got = pool.copy()
+    oracle.pool_append(got, geo, bt, pos, k, v)
+    want = pool.copy()
+    kv, vv = brute.pool_view(want, 2, D, T)
+    kv[bt[pos // T], :, pos % T, :] = k.reshape(2, D)
+    vv[bt[pos // T], :, :, pos % T] = v.reshape(2, D)
+    assert np.array_equal(got, want)
+
+
+def test_split_pools_are_the_page_blocks():
+    g = _rng(21)
+    geo = oracle.PoolGeometry(kv_heads=2, head_dim=64, page_tokens=256)
+    pool = synth.to_bf16_bits(g.standard_normal(3 * geo.page_elems).astype(np.float32))
+    kp, vp = oracle.split_pools(pool, geo)
+    kv, vv = brute.pool_view(pool, 2, 64, 256)
+    assert np.array_equal(kp, kv.reshape(-1)) and np.array_equal(vp, vv.reshape(-1))
+    assert np.array_equal(oracle.whole_pool(kp, vp, geo), pool)
+
+
 def test_paged_equals_contiguous():
     # identity table over a contiguous copy vs a random permutation of pages
     g = _rng(19)
