@@ -60,12 +60,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attention_bytes(lens, Hq, Hkv, q_bytes, D=64):
+def attention_bytes(lens, Hq, Hkv, q_bytes, D=64, page_tokens=16):
     """Algorithmic bytes of one paged attention call: every attended token's
     K and V (BF16), q in, FP32 out, one block-table entry per page."""
     lens = np.asarray(lens, dtype=np.int64)
     B = len(lens)
-    return int((lens * Hkv * D * 2 * 2).sum() + B * Hq * D * (q_bytes + 4) + ((lens + 15) // 16).sum() * 4)
+    return int((lens * Hkv * D * 2 * 2).sum() + B * Hq * D * (q_bytes + 4)
+               + ((lens + page_tokens - 1) // page_tokens).sum() * 4)
+
+
+def decode_layer_bytes(shape, lens):
+    """Algorithmic bytes of one decoder layer over a batch: the weights once,
+    the attention (FP32 q inside the layer) over lens[b] tokens, the
+    appended K/V and the hidden state in and out."""
+    B, H = len(lens), shape.hidden
+    return (2 * shape.layer_param_count()
+            + attention_bytes(lens, shape.heads, shape.kv_heads, 4, shape.head_dim)
+            + B * shape.kv_heads * shape.head_dim * 2 * 2 + 2 * B * H * 4)
 
 
 def step_bytes(shape, lens, logits=True):
@@ -73,9 +84,7 @@ def step_bytes(shape, lens, logits=True):
     attention (FP32 q inside the layer), the appended K/V, the hidden state
     in and out of each layer, the embedding rows, the LM head, the logits."""
     B, H, V = len(lens), shape.hidden, shape.vocab
-    layer = (2 * (shape.layer_param_count())
-             + attention_bytes(lens, shape.heads, shape.kv_heads, 4)
-             + B * shape.kv_heads * shape.head_dim * 2 * 2 + 2 * B * H * 4)
+    layer = decode_layer_bytes(shape, lens)
     return shape.layers * layer + B * H * 2 + 2 * V * H + H * 2 + (B * V * 4 if logits else 0)
 
 
@@ -354,6 +363,122 @@ def large_batch_steps(torch, pkv, synth, llama_model=None):
     return out
 
 
+def page_geometries(torch, pkv, synth, rounds=4, reps=10, L=16):
+    """paged_gqa_decode on the step's attention workload (batch 16, lengths
+    U[1,2048], BF16 q) in every pool geometry: pages of 16 or 256 tokens,
+    one buffer or separate K and V pools, at head width 64 (Llama-3.2-1B
+    heads, 32/8) and 128 (Llama-3-8B heads, 32/8).  Each call reads one of L
+    block tables with distinct pages (as the layers of a step do), so no
+    call finds its pages in cache; rounds x L calls are captured in a HIP
+    graph.  The pool holds seeded N(0,1) BF16 values drawn on the device.
+    Returns {"d64": {geometry: object}, "d128": ...}."""
+    out = {}
+    lens = synth.c2_lens(1002, 16)
+    B = len(lens)
+    lens_t = pkv.to_device(lens)
+    for shape in (synth.LLAMA1B, synth.LLAMA8B):
+        D, Hq, Hkv = shape.head_dim, shape.heads, shape.kv_heads
+        res = {}
+        for PT in (16, 256):
+            npages = int(synth.pages_for(lens, PT).sum()) * L
+            bt = synth.block_tables(1002, L, lens, npages, max_pages=2048 // PT, page_tokens=PT)
+            bts = [pkv.to_device(bt[l]) for l in range(L)]
+            pe = synth.page_elems(shape, page_tokens=PT)
+            abytes = attention_bytes(lens, Hq, Hkv, 2, D, PT)
+            for split in (False, True):
+                gen = torch.Generator(device="cuda").manual_seed(1002)
+                if split:
+                    kt = torch.randn(npages * pe // 2, generator=gen, device="cuda").to(torch.bfloat16)
+                    vt = torch.randn(npages * pe // 2, generator=gen, device="cuda").to(torch.bfloat16)
+                    pool = pkv.kv_pool_create_split(kt, vt, Hkv, head_dim=D, page_tokens=PT)
+                else:
+                    pt = torch.randn(npages * pe, generator=gen, device="cuda").to(torch.bfloat16)
+                    pool = pkv.kv_pool_create(pt, Hkv, head_dim=D, page_tokens=PT)
+                q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+                o = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+                ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(Hq, Hkv, B, bt.shape[2], head_dim=D,
+                                                                       page_tokens=PT))
+
+                def run(st):
+                    for _ in range(rounds):
+                        for l in range(L):
+                            pkv.paged_gqa_decode(pool, q, bts[l], lens_t, 1.0 / np.sqrt(D), o, ws, st)
+
+                graph = capture(torch, run)
+                for _ in range(2):
+                    graph.replay()
+                ms = timed_replays(torch, graph.replay, reps)
+                assert pkv.device_error(ws) == 0
+                us = float(np.median(ms)) * 1e3 / (rounds * L)
+                gbs = abytes / (us * 1e3)
+                name = "pt%d_%s" % (PT, "split" if split else "whole")
+                log("attention d%d %s: %.2f us per call, %.0f GB/s" % (D, name, us, gbs))
+                res[name] = {"us_per_call": round(us, 3), "algorithmic_bytes": int(abytes),
+                             "achieved": round(gbs, 1), "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                del graph, pool, q, o, ws
+                if split:
+                    del kt, vt
+                else:
+                    del pt
+                torch.cuda.empty_cache()
+        out["d%d" % D] = res
+    out["workload"] = ("paged_gqa_decode, 32/8 heads, batch 16, lengths U[1,2048] (seed 1002), "
+                       "%d tables of distinct pages per graph pass; d64 Llama-3.2-1B heads, d128 "
+                       "Llama-3-8B heads; pt16/pt256: page tokens; whole: K and V blocks in one "
+                       "buffer, split: separate K and V pools" % L)
+    out["peak"] = HBM_PEAK_GBS
+    return out
+
+
+def time_layer_llama8b(torch, pkv, synth, reps=10, L=4):
+    """decoder_layer_decode of Llama-3-8B-shaped layers (hidden 4096, 32/8
+    heads of width 128, SwiGLU 14336) at batch 16, attention lengths
+    U[1,2048]: L distinct layers (weights and page sets) chained in one HIP
+    graph, so the 436 MB of each layer's weights come from HBM.  Returns an
+    object for the JSON line."""
+    shape = synth.LLAMA8B
+    lens = synth.c2_lens(1002, 16)
+    positions = (lens - 1).astype(np.int32)
+    wl = synth.decode_workload("8b layers", shape, 1010, positions, layers=L, with_pool=False)
+    layers = [pkv.upload_layer(synth.layer_weights(shape, 1010, l), head_dim=128) for l in range(L)]
+    mp = int(positions.max()) + 1
+    c, sn = pkv.rope_table(shape.theta, mp, head_dim=128)
+    cfg = pkv.make_config(shape, max_pos=mp, layers=1)
+    gen = torch.Generator(device="cuda").manual_seed(1010)
+    pool_t = torch.randn(wl.num_pages * synth.page_elems(shape), generator=gen,
+                         device="cuda").to(torch.bfloat16)
+    pool = pkv.kv_pool_create(pool_t, shape.kv_heads, head_dim=128)
+    bts = [pkv.to_device(wl.block_tables[l]) for l in range(L)]
+    pos = pkv.to_device(positions)
+    B = len(positions)
+    hidden = torch.randn((B, shape.hidden), generator=gen, device="cuda")
+    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, B, wl.max_pages))
+
+    def run(stream):
+        for l in range(L):
+            pkv.decoder_layer_decode(cfg, layers[l], c, sn, pool, bts[l], pos, hidden, ws, stream)
+
+    graph = capture(torch, run)
+    for _ in range(2):
+        graph.replay()
+    ms = timed_replays(torch, graph.replay, reps)
+    assert pkv.device_error(ws) == 0
+    us = [m * 1e3 / L for m in ms]
+    nbytes = decode_layer_bytes(shape, lens)
+    gbs = nbytes / (float(np.median(us)) * 1e3)
+    log("llama-8b-shape layer, batch 16: %.1f us per layer (median), %.1f MB -> %.0f GB/s" % (
+        float(np.median(us)), nbytes / 1e6, gbs))
+    del graph, layers, pool_t
+    torch.cuda.empty_cache()
+    return {"workload": "decoder_layer_decode, llama-3-8b-shape layer (head width 128), batch 16, "
+                        "attention lengths U[1,2048] (seed 1002), %d distinct layers chained in one "
+                        "HIP graph (per-layer = replay / %d)" % (L, L),
+            "bound": "hbm", "algorithmic_bytes": int(nbytes), "us_per_layer": pct(us),
+            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def ceilings(torch, nbytes=1 << 30, reps=10):
     """Plain streaming rates on this GPU: a device copy (bytes read + written)
     and a read-only reduction (torch's own kernels), 1 GiB each."""
@@ -596,6 +721,8 @@ def main():
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="skip the c1 layer chain, the batch-64/128 steps and the copy ceilings")
     ap.add_argument("--prefill-tokens", type=int, default=512, help="0 skips the prefill timing")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="time the page-geometry variants and the head-width-128 layer alone")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the prefill alone (the step's model, no decode workload)")
     args = ap.parse_args()
@@ -611,7 +738,7 @@ def main():
     import paged_kv_transformer_amd as pkv
     import synth
 
-    if args.attention_only or args.prefill_only or args.large_batch_only:
+    if args.attention_only or args.prefill_only or args.large_batch_only or args.variants_only:
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(2)
@@ -620,6 +747,9 @@ def main():
             attention_only(torch, pkv, synth, args.attn_rounds)
         elif args.prefill_only:
             prefill_only(torch, pkv, synth, args.prefill_tokens)
+        elif args.variants_only:
+            print(json.dumps({"page_geometry": page_geometries(torch, pkv, synth),
+                              "layer_llama8b": time_layer_llama8b(torch, pkv, synth)}))
         else:
             print(json.dumps(large_batch_steps(torch, pkv, synth)))
         return
@@ -716,6 +846,8 @@ def main():
             "achieved": round(c1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(c1_gbs / HBM_PEAK_GBS, 4), "gate_frac": 0.6}
         extra.update(large_batch_steps(torch, pkv, synth, S.model))
+        extra["page_geometry"] = page_geometries(torch, pkv, synth)
+        extra["layer_llama8b"] = time_layer_llama8b(torch, pkv, synth)
         cp_gbs, rd_gbs = ceilings(torch)
         log("ceilings: device copy %.0f GB/s (read + write), read-only reduction %.0f GB/s" % (cp_gbs, rd_gbs))
         extra["ceiling"] = {"copy_gbs": round(cp_gbs, 1), "read_gbs": round(rd_gbs, 1),

@@ -45,6 +45,7 @@ PoolView pool_view(const pkv_pool* p) {
   v.stride = p->v_base ? block : 2 * block;
   v.num_pages = p->num_pages;
   v.pt_shift = pt_shift(p->page_tokens);
+  v.hkv = p->num_kv_heads;
   return v;
 }
 

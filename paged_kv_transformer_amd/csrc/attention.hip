@@ -181,7 +181,7 @@ paged_attention_kernel(const AttnArgs a) {
   for (int i = 0; i < PW; ++i) {
     const uint16_t* vp = a.pv.v + pv_v_index(a.pv, page[i], kvh, col, sub[i], D) + 4 * grp;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[i][c] = *(const u32x2*)(vp + (int64_t)c * 16 * PT);
+    for (int c = 0; c < NC; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kTile);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (bad && l == 0) set_error(a.err, ERR_PAGE);

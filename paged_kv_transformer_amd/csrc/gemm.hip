@@ -314,8 +314,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
           kp[j + half] = to_bf16_bits(y1);
         } else {
           uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, 0, slot, D);
-          vp[(int64_t)j * PT] = to_bf16_bits(y0);
-          vp[(int64_t)(j + half) * PT] = to_bf16_bits(y1);
+          vp[j * kTile] = to_bf16_bits(y0);
+          vp[(j + half) * kTile] = to_bf16_bits(y1);
         }
       }
     }

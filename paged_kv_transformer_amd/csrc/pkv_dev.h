@@ -83,24 +83,29 @@ inline int64_t packed_act_elems(int B, int K) { return (int64_t)((B + 15) / 16) 
 // --------------------------------------------------------- arguments ---
 
 // Where the pages live.  Page p of PT = kTile << pt_shift tokens holds a K
-// block [Hkv][PT][D] at k + p * stride and a V block [Hkv][D][PT] at
-// v + p * stride: one buffer of whole pages (v = k + the K block,
-// stride = both blocks), or separate K and V pools (stride = one block).
+// block [Hkv][PT][D] at k + p * stride and a V block at v + p * stride:
+// one buffer of whole pages (v = k + the K block, stride = both blocks),
+// or separate K and V pools (stride = one block).  The V block is stored
+// in 16-token tiles, [PT / 16][Hkv][D][16]: a tile's V for one kv head is
+// one contiguous [D][16] operand whatever the page size.
 struct PoolView {
   uint16_t* k;
   uint16_t* v;
   int64_t stride;      // BF16 elements from one page to the next
   int32_t num_pages;
   int32_t pt_shift;    // log2(PT / 16): 0 (16-token pages) or 4 (256)
+  int32_t hkv;         // kv heads
 };
 
 // Element d of token `slot`'s K (kv head h) and V of page `page`.
 __host__ __device__ inline int64_t pv_k_index(const PoolView& p, int page, int h, int slot, int D) {
   return (int64_t)page * p.stride + ((int64_t)h * (kTile << p.pt_shift) + slot) * D;
 }
+// V of dimension d, token `slot`; dimension d + 1 is kTile elements further.
 __host__ __device__ inline int64_t pv_v_index(const PoolView& p, int page, int h, int d, int slot,
                                                int D) {
-  return (int64_t)page * p.stride + ((int64_t)h * D + d) * (kTile << p.pt_shift) + slot;
+  return (int64_t)page * p.stride + (((int64_t)(slot >> 4) * p.hkv + h) * D + d) * kTile +
+         (slot & (kTile - 1));
 }
 
 struct AttnArgs {

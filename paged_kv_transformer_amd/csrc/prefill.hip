@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
               } else {
                 uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, jj, slot, D);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vp[(int64_t)e * PT] = to_bf16_bits(y[e]);
+                for (int e = 0; e < 4; ++e) vp[e * kTile] = to_bf16_bits(y[e]);
               }
             }
           }
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
   const int npages = pmax / kTile + 1;      // 16-token tiles
   const int pmin = a.start_pos + t0;        // its first: keys up to here need no mask
   // this wave's tiles [pb, pe); a page holds 1 << sh tiles
-  const int sh = a.pv.pt_shift, PT = kTile << sh;
+  const int sh = a.pv.pt_shift;
   const int npw = (npages + 3) / 4;
   const int pb = w * npw, pe = min(npages, pb + npw);
 
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
       for (int h = 0; h < NH; ++h) C.k[i][h] = *(const u32x4*)(kp + 32 * h);
       const uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, kvh, col, sub, D) + 4 * grp;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vp + (int64_t)c * 16 * PT);
+      for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vp + c * 16 * kTile);
     }
   };
 

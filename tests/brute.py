@@ -50,11 +50,12 @@ def softmax_attention(q, K, V, scale):
 
 
 def pool_view(pool, kv_heads, head_dim, page_tokens=16):
-    """Views (K [page][head][slot][d], V [page][head][d][slot]) of the pool."""
+    """Views of the pool's pages: K [page][head][slot][d] and V
+    [page][tile][head][d][s], token slot = 16 tile + s (16-token tiles)."""
     blk = kv_heads * page_tokens * head_dim
     pages = np.asarray(pool).reshape(-1, 2 * blk)
     return (pages[:, :blk].reshape(-1, kv_heads, page_tokens, head_dim),
-            pages[:, blk:].reshape(-1, kv_heads, head_dim, page_tokens))
+            pages[:, blk:].reshape(-1, page_tokens // 16, kv_heads, head_dim, 16))
 
 
 def gather(pool, kv_heads, head_dim, bt_row, n, page_tokens=16):
@@ -64,7 +65,7 @@ def gather(pool, kv_heads, head_dim, bt_row, n, page_tokens=16):
     pages = np.asarray(bt_row)[t // page_tokens]
     slots = t % page_tokens
     K = bf16_bits_to_f64(kv[pages, :, slots, :])
-    V = bf16_bits_to_f64(vv[pages, :, :, slots])
+    V = bf16_bits_to_f64(vv[pages, slots // 16, :, :, slots % 16])
     return K, V
 
 

@@ -116,13 +116,14 @@ def test_attention_same_tokens_same_bits_in_every_geometry():
     for PT in (16, 256):
         npages = int(synth.pages_for(lens, PT).sum())
         bt = synth.block_tables(53, 1, lens, npages, page_tokens=PT)[0]
-        # pages as numpy views: K [page][head][slot][d], V [page][head][d][slot]
+        # pages as numpy arrays: K [page][head][slot][d], V in 16-token
+        # tiles [page][tile][head][d][slot % 16]
         kp = np.zeros((npages, Hkv, PT, D), np.uint16)
-        vp = np.zeros((npages, Hkv, D, PT), np.uint16)
+        vp = np.zeros((npages, PT // 16, Hkv, D, 16), np.uint16)
         for b, n in enumerate(lens):
             t = np.arange(n)
             kp[bt[b][t // PT], :, t % PT, :] = K[b, :n].reshape(n, Hkv, D)
-            vp[bt[b][t // PT], :, :, t % PT] = V[b, :n].reshape(n, Hkv, D)
+            vp[bt[b][t // PT], (t % PT) // 16, :, :, t % 16] = V[b, :n].reshape(n, Hkv, D)
         pages = np.concatenate([kp.reshape(npages, -1), vp.reshape(npages, -1)], axis=1)
         for p in (pages.reshape(-1), (kp.reshape(-1), vp.reshape(-1))):
             out, err = attention_gpu(p, Hkv, q, bt, lens, 0.125, page_tokens=PT)

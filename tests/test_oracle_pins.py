@@ -289,7 +289,7 @@ def test_pool_append_matches_reshaped_view(pos, D):
     want = pool.copy()
     kv, vv = brute.pool_view(want, 8, D)
     kv[bt[pos // 16], :, pos % 16, :] = k.reshape(8, D)
-    vv[bt[pos // 16], :, :, pos % 16] = v.reshape(8, D)
+    vv[bt[pos // 16], 0, :, :, pos % 16] = v.reshape(8, D)
     got = pool.copy()
     oracle.pool_append(got, geo, bt, pos, k, v)
     assert np.array_equal(got, want)
@@ -317,7 +317,7 @@ def test_pool_gather_any_page_size_matches_reshaped_view(T, D):
     want = pool.copy()
     kv, vv = brute.pool_view(want, 2, D, T)
     kv[bt[pos // T], :, pos % T, :] = k.reshape(2, D)
-    vv[bt[pos // T], :, :, pos % T] = v.reshape(2, D)
+    vv[bt[pos // T], (pos % T) // 16, :, :, pos % 16] = v.reshape(2, D)
     assert np.array_equal(got, want)
 
 
@@ -466,12 +466,12 @@ def test_prefill_matches_float64_causal_brute_force(start, T):
             p = start + t
             page, slot = bts[l][p // 16], p % 16
             got_k = brute.bf16_bits_to_f64(kv_view[page, :, slot, :])
-            got_v = brute.bf16_bits_to_f64(vv_view[page, :, :, slot])
+            got_v = brute.bf16_bits_to_f64(vv_view[page, 0, :, :, slot])
             # one BF16 ulp at most (FP32 vs float64 values before rounding)
             np.testing.assert_allclose(got_k, K[t], rtol=2 ** -7, atol=1e-6)
             np.testing.assert_allclose(got_v, V[t], rtol=2 ** -7, atol=1e-6)
             tv[page, :, slot, :] = True
-            vv_t[page, :, :, slot] = True
+            vv_t[page, 0, :, :, slot] = True
     assert np.array_equal(pool_after[~touched], pool[~touched])
 
 
