@@ -640,7 +640,7 @@ def attention_only(torch, pkv, synth, rounds):
     """Launch sequence for the hardware-counter runs: the attention calls
     over the 16 layers' tables, one by one, then a device copy of known
     size (the counters' calibration)."""
-    S = Setup(torch, pkv, synth)
+    S = Setup(torch, pkv, synth, HostInputs(synth))
     A = AttentionCalls(torch, pkv, synth, S)
     stream = torch.cuda.current_stream()
     for _ in range(rounds):
