@@ -270,6 +270,30 @@ struct TiledLayout {
   size_t err, attn_part, q, x, xb, ob, act, part, amax, total;
 };
 
+// The tiled QKV projection of T tokens: one launch with the RoPE/append
+// epilogue, or (too few tiles) K split into FP32 partials (`part`) + the
+// finish kernel.  `a` holds every QKV argument; part must hold
+// qkv_part_floats(...) floats.
+PgemmPlan tiled_qkv_plan(const pkv_config* c, int T) {
+  return plan_prefill_gemm((c->num_attention_heads + 2 * c->num_key_value_heads) * (c->head_dim / 16), T,
+                           c->hidden_size, false);
+}
+size_t qkv_part_floats(const pkv_config* c, int T) {
+  const int ks = qkv_splits(tiled_qkv_plan(c, T), c->hidden_size);
+  return ks > 1 ? (size_t)ks * T * (c->num_attention_heads + 2 * c->num_key_value_heads) * c->head_dim : 0;
+}
+hipError_t launch_tiled_qkv(const pkv_config* c, PgemmArgs a, float* part, hipStream_t st) {
+  PgemmPlan p = tiled_qkv_plan(c, a.T);
+  const int ks = qkv_splits(p, a.K);
+  if (ks == 1) return launch_prefill_gemm(EPI_QKV, a, p, st);
+  p.ks = ks;
+  a.part = part;
+  a.ksplit = ks;
+  const hipError_t e = launch_prefill_gemm(EPI_RESID, a, p, st);
+  if (e != hipSuccess) return e;
+  return launch_qkv_finish(part, ks, a, st);
+}
+
 PgemmPlan tiled_o_plan(const pkv_config* c, int B) {
   return plan_prefill_gemm(c->hidden_size / 16, B, c->num_attention_heads * c->head_dim, true);
 }
@@ -303,7 +327,8 @@ TiledLayout tiled_layout(const pkv_config* c, int B, int64_t max_tiles) {
   L.act = take(2 * (size_t)packed_pair_elems(B, (int)I));
   const int ks = tiled_o_plan(c, B).ks > tiled_down_plan(c, B).ks ? tiled_o_plan(c, B).ks
                                                                     : tiled_down_plan(c, B).ks;
-  L.part = take(sizeof(float) * (size_t)ks * B * H);
+  const size_t pq = qkv_part_floats(c, B);
+  L.part = take(sizeof(float) * ((size_t)ks * B * H > pq ? (size_t)ks * B * H : pq));
   if (c->vocab_size > 0) L.amax = take(sizeof(unsigned long long) * 2 * (size_t)lm_row_tiles(c, B) * B);
   L.total = off;
   return L;
@@ -357,8 +382,7 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
     a.rsin = rope_sin;
     a.Hq = Hq;
     a.Hkv = Hkv;
-    if ((rc = io(launch_prefill_gemm(EPI_QKV, a, plan_prefill_gemm(a.w_groups, B, H, false), st))))
-      return rc;
+    if ((rc = io(launch_tiled_qkv(cfg, a, part, st)))) return rc;
   }
   {
     AttnArgs a{};
@@ -670,7 +694,8 @@ static PrefillLayout prefill_layout(const pkv_config* cfg, int32_t T) {
   L.ob = take(2 * (size_t)packed_pair_elems(T, (int)QD));
   L.act = take(2 * (size_t)packed_pair_elems(T, (int)I));
   const int ks_o = prefill_o_plan(cfg, T).ks, ks_d = prefill_down_plan(cfg, T).ks;
-  L.part = take(sizeof(float) * (size_t)(ks_o > ks_d ? ks_o : ks_d) * T * H);
+  const size_t pr = (size_t)(ks_o > ks_d ? ks_o : ks_d) * T * H, pq = qkv_part_floats(cfg, T);
+  L.part = take(sizeof(float) * (pr > pq ? pr : pq));
   L.amax = take(sizeof(unsigned long long) * plan_gemm(EPI_LOGITS, cfg->vocab_size, 1, H).tiles);
   L.total = off;
   return L;
@@ -724,7 +749,6 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
   const float eps = cfg->rms_norm_eps;
 
   float* part = at<float>(workspace, L.part);
-  const PgemmPlan p_qkv = plan_prefill_gemm((Hq + 2 * Hkv) * (D / 16), T, H, false);
   const PgemmPlan p_o = prefill_o_plan(cfg, T);
   const PgemmPlan p_gu = plan_prefill_gemm(I / 8, T, H, false);
   const PgemmPlan p_down = prefill_down_plan(cfg, T);
@@ -761,7 +785,7 @@ int prefill(const pkv_config* cfg, const pkv_model_weights* w, const pkv_pool* p
       a.rsin = w->rope_sin;
       a.Hq = Hq;
       a.Hkv = Hkv;
-      if ((rc = io(launch_prefill_gemm(EPI_QKV, a, p_qkv, st)))) return rc;
+      if ((rc = io(launch_tiled_qkv(cfg, a, part, st)))) return rc;
     }
     // causal attention over positions 0 .. start_pos + t
     {

@@ -266,12 +266,26 @@ inline PgemmPlan plan_prefill_gemm(int w_groups, int T, int K, bool can_split) {
   static const int cand[4][2] = {{8, 4}, {4, 4}, {2, 4}, {2, 2}};
   p.ks = 1;
   for (const auto& c : cand) {
+    // 64-row tiles 128 tokens wide for at most 64 tokens: the 64-token
+    // tiles of the same rows give as many workgroups without the empty half
+    if (c[0] == 2 && c[1] == 4 && T <= 64) continue;
     p.rg = c[0];
     p.cg = c[1];
     p.tiles = pf_tiles(w_groups, T, p.rg, p.cg);
     if (p.tiles >= kPfTargetWgs) break;
   }
   return p;
+}
+
+// K splits of the tiled QKV projection: 1 when its row and token tiles
+// alone give at least half the target workgroups; otherwise enough to reach
+// the target, at least 8 K steps each.  The split sums are finished by
+// qkv_finish_kernel (RoPE needs whole sums).
+inline int qkv_splits(const PgemmPlan& p, int K) {
+  if (p.tiles * 2 >= kPfTargetWgs) return 1;
+  const int most = (K / 32) / 8;
+  const int ks = (kPfTargetWgs + p.tiles - 1) / p.tiles;
+  return ks < most ? (ks > 1 ? ks : 1) : (most > 1 ? most : 1);
 }
 
 // Sampling after the LM head: per-sequence workspace of the radix select
@@ -449,6 +463,8 @@ hipError_t launch_argmax_finalize(const unsigned long long* part, int tiles, int
                                   hipStream_t st);
 // x[t] += sum over splits of part[s][t] (in split order); then, if nw is
 // given, the RMSNorm of the new row into packed hi/lo pairs xb
+// Split QKV: add the K splits' partial sums, then RoPE, q halves, K/V append.
+hipError_t launch_qkv_finish(const float* part, int ks, const PgemmArgs& a, hipStream_t st);
 hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int N,
                                 const uint16_t* nw, float eps, uint16_t* xb, hipStream_t st);
 hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st);

@@ -399,6 +399,73 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
     }
 }
 
+// ------------------------------------------------ split QKV finish ---
+// The QKV projection with K split over workgroups (too few row tiles to
+// fill the chip otherwise): the splits' partial sums part[s][t][n] (n in
+// the packed row order: group G = head * D/16 + j / 8 holds pair element j
+// in row j % 8 and j + D/2 in row 8 + j % 8) are added in split order, then
+// RoPE, the q halves and the K/V append as in the projection's own
+// epilogue.  One thread per (token, head, pair j).
+__global__ __launch_bounds__(256) void qkv_finish_kernel(const float* part, int ks,
+                                                         const PgemmArgs a) {
+  const int D = a.D, half = D >> 1, gph = D >> 4;
+  const int heads = a.Hq + 2 * a.Hkv;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.T * heads * half) return;
+  const int t = (int)(idx / (heads * half));
+  const int r = (int)(idx - (int64_t)t * heads * half);
+  const int hd = r / half, j = r - hd * half;
+  const int n0 = 16 * (hd * gph + (j >> 3)) + (j & 7), n1 = n0 + 8;
+  const size_t N = (size_t)heads * D;
+  float x0 = 0.f, x1 = 0.f;
+  for (int sp = 0; sp < ks; ++sp) {
+    const float* ps = part + ((size_t)sp * a.T + t) * N;
+    x0 += ps[n0];
+    x1 += ps[n1];
+  }
+  const int p = a.pos ? a.pos[t] : a.start_pos + t;
+  const bool is_q = hd < a.Hq, is_k = !is_q && hd < a.Hq + a.Hkv;
+  float y0 = x0, y1 = x1;
+  if (is_q || is_k) {
+    if (p < 0 || p >= a.max_pos) {
+      set_error(a.err, ERR_ROPE);
+      return;
+    }
+    const float cs = a.rcos[(size_t)p * half + j], sn = a.rsin[(size_t)p * half + j];
+    y0 = __fsub_rn(__fmul_rn(x0, cs), __fmul_rn(x1, sn));
+    y1 = __fadd_rn(__fmul_rn(x0, sn), __fmul_rn(x1, cs));
+  }
+  if (is_q) {
+    uint16_t* qo = a.q_split + ((size_t)t * a.Hq + hd) * 2 * D;
+    const uint16_t h0 = to_bf16_bits(y0), h1 = to_bf16_bits(y1);
+    qo[j] = h0;
+    qo[j + half] = h1;
+    qo[D + j] = to_bf16_bits(y0 - bf16_lo(h0));
+    qo[D + j + half] = to_bf16_bits(y1 - bf16_lo(h1));
+    return;
+  }
+  const int psh = 4 + a.pv.pt_shift;  // log2 of the page's tokens
+  if (p < 0 || (p >> psh) >= a.bt_stride) {
+    set_error(a.err, ERR_LENGTH);
+    return;
+  }
+  const int page = a.bt[(size_t)t * a.bt_row + (p >> psh)];
+  if ((unsigned)page >= (unsigned)a.pv.num_pages) {
+    set_error(a.err, ERR_PAGE);
+    return;
+  }
+  const int slot = p & ((1 << psh) - 1);
+  if (is_k) {
+    uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, hd - a.Hq, slot, D);
+    kp[j] = to_bf16_bits(y0);
+    kp[j + half] = to_bf16_bits(y1);
+  } else {
+    uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, 0, slot, D);
+    vp[j * kTile] = to_bf16_bits(y0);
+    vp[(j + half) * kTile] = to_bf16_bits(y1);
+  }
+}
+
 // ------------------------------------------------- residual + norm ---
 // One workgroup per token row: x[t] += sum_s part[s][t] (splits in order,
 // so the result does not depend on scheduling), then, if nw is given, the
@@ -704,6 +771,12 @@ hipError_t launch_prefill_gemm(int epi, const PgemmArgs& a, const PgemmPlan& p, 
     case EPI_LOGITS: return launch_pg<EPI_LOGITS>(a, p, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_qkv_finish(const float* part, int ks, const PgemmArgs& a, hipStream_t st) {
+  const int64_t n = (int64_t)a.T * (a.Hq + 2 * a.Hkv) * (a.D / 2);
+  qkv_finish_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(part, ks, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int N,

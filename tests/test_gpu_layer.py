@@ -78,6 +78,22 @@ def test_layer_split_k_down_projection(batch, inter):
     _check_layer(shape, lw, hidden, wl)
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_layer_tiled_split_qkv(head_dim):
+    """Batch 70 takes the tiled projections; with hidden 512 the QKV
+    projection has too few row tiles to fill the chip, so it splits K into
+    partial sums finished (RoPE, q halves, K/V append) by a second kernel."""
+    shape = synth.tiny_shape(hidden=512, heads=4, kv_heads=2, inter=512, head_dim=head_dim,
+                             name="tiny-split-qkv")
+    batch, seed = 70, 350 + head_dim
+    positions = synth.rng(seed, "lens").integers(0, 300, size=batch).astype(np.int32)
+    positions[:3] = [0, 15, 16]
+    wl = synth.decode_workload("tiny-split-qkv", shape, seed, positions, layers=1)
+    lw = synth.layer_weights(shape, seed, 0, sigma=0.05, norm_sigma=0.3)
+    hidden = synth.rng(seed, "hidden").standard_normal((batch, shape.hidden)).astype(np.float32)
+    _check_layer(shape, lw, hidden, wl)
+
+
 def _check_step(shape, weights, wl, tokens, seqs=None, want_logits=True):
     geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
     logits, nxt, pool_after, err = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions,

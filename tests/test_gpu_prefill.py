@@ -78,6 +78,19 @@ def test_prefill_tiny_model_matches_oracle(start, T):
     _oracle_check(shape, w, pool, bts, start, tokens, logits, nxt, pool_after, "tiny")
 
 
+@pytest.mark.parametrize("head_dim,T", [(64, 40), (128, 23)])
+def test_prefill_split_qkv_matches_oracle(head_dim, T):
+    """Hidden 512 with a short prompt: the QKV projection splits K into
+    partial sums and a second kernel finishes RoPE, q and the K/V append."""
+    shape = synth.tiny_shape(hidden=512, layers=2, heads=4, kv_heads=2, inter=512, vocab=700,
+                             head_dim=head_dim)
+    start = 3
+    w, pool, bts, tokens = _inputs(shape, 60 + head_dim, start, T)
+    logits, nxt, pool_after, err = prefill_gpu(shape, w, pool, bts, start, tokens)
+    assert err == 0
+    _oracle_check(shape, w, pool, bts, start, tokens, logits, nxt, pool_after, "split-qkv")
+
+
 @pytest.mark.parametrize("heads,kv_heads", [(2, 2), (14, 2), (16, 1)])
 def test_prefill_group_sizes(heads, kv_heads):
     """GQA groups of 1, 7 and 16 heads: 16, 2 and 1 tokens per wave."""
