@@ -237,7 +237,11 @@ struct PgemmPlan {
 };
 
 constexpr int kPfTargetWgs = 240;     // about one workgroup per compute unit
-constexpr int kPfMinSplitSteps = 16;  // 32-wide K steps per split, at least
+// 32-wide K steps per split, at least: 8 for decode-sized batches (up to
+// 128 tokens), whose few row tiles need many splits to fill the chip; 16
+// for prompts, whose token tiles already do
+constexpr int kPfMinSplitSteps = 8;
+constexpr int kPfMinSplitStepsLong = 16;
 
 inline int pf_tiles(int w_groups, int T, int rg, int cg) {
   return ((w_groups + 2 * rg - 1) / (2 * rg)) * ((T + 32 * cg - 1) / (32 * cg));
@@ -250,14 +254,16 @@ inline int pf_tiles(int w_groups, int T, int rg, int cg) {
 inline PgemmPlan plan_prefill_gemm(int w_groups, int T, int K, bool can_split) {
   PgemmPlan p{};
   if (can_split) {
-    static const int cand[2][2] = {{8, 4}, {4, 4}};
+    static const int cand[4][2] = {{8, 4}, {4, 4}, {2, 4}, {2, 2}};
     const int steps = K / 32;
+    const int min_steps = T <= 128 ? kPfMinSplitSteps : kPfMinSplitStepsLong;
     for (const auto& c : cand) {
+      if (c[0] == 2 && c[1] == 4 && T <= 64) continue;  // as below
       p.rg = c[0];
       p.cg = c[1];
       p.tiles = pf_tiles(w_groups, T, p.rg, p.cg);
       int ks = (kPfTargetWgs + p.tiles - 1) / p.tiles;
-      const int most = steps / kPfMinSplitSteps > 1 ? steps / kPfMinSplitSteps : 1;
+      const int most = steps / min_steps > 1 ? steps / min_steps : 1;
       p.ks = ks < most ? ks : most;
       if (p.tiles * p.ks >= kPfTargetWgs) break;
     }
