@@ -242,6 +242,7 @@ constexpr int kPfTargetWgs = 240;     // about one workgroup per compute unit
 // for prompts, whose token tiles already do
 constexpr int kPfMinSplitSteps = 8;
 constexpr int kPfMinSplitStepsLong = 16;
+constexpr int kPfMaxSplits = 16;
 
 inline int pf_tiles(int w_groups, int T, int rg, int cg) {
   return ((w_groups + 2 * rg - 1) / (2 * rg)) * ((T + 32 * cg - 1) / (32 * cg));
@@ -265,6 +266,9 @@ inline PgemmPlan plan_prefill_gemm(int w_groups, int T, int K, bool can_split) {
       int ks = (kPfTargetWgs + p.tiles - 1) / p.tiles;
       const int most = steps / min_steps > 1 ? steps / min_steps : 1;
       p.ks = ks < most ? ks : most;
+      // more partials than this cost the residual kernel that adds them more
+      // than the extra workgroups gain
+      if (p.ks > kPfMaxSplits) p.ks = kPfMaxSplits;
       if (p.tiles * p.ks >= kPfTargetWgs) break;
     }
     return p;
