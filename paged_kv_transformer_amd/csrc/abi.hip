@@ -200,7 +200,8 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = Hq / Hkv;
-    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens));
+    a.pw = attn_pw(batch, a.Hkv, table_tiles(max_pages, pool->page_tokens));
+    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens), a.pw);
     if ((rc = io(launch_attention(a, batch, kQSplit, st)))) return rc;
   }
 
@@ -402,7 +403,8 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.G = Hq / Hkv;
-    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens));
+    a.pw = attn_pw(B, a.Hkv, table_tiles(max_pages, pool->page_tokens));
+    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens), a.pw);
     if ((rc = io(launch_attention(a, B, kQSplit, st)))) return rc;
   }
   {
@@ -554,7 +556,8 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
   a.Hq = num_q_heads;
   a.Hkv = pool->num_kv_heads;
   a.G = num_q_heads / pool->num_kv_heads;
-  a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens));
+  a.pw = attn_pw(batch, a.Hkv, table_tiles(max_pages, pool->page_tokens));
+    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens), a.pw);
   a.D = pool->head_dim;
   return io(launch_attention(a, batch, kQBf16, (hipStream_t)stream));
 }

@@ -4,10 +4,13 @@
 // decode attention: every query head walks its sequence's pages through
 // the block table and accumulates softmax-weighted values without gathering
 // a contiguous prefix or storing scores.  Here one workgroup takes one
-// (sequence, kv head, split of 8 logical pages); its 4 waves take 2 pages
-// each.  The whole GQA group of the kv head shares every page load.
+// (sequence, kv head, split of 8 16-token tiles); its 4 waves take 2 tiles
+// each.  Calls of many sequences (at least kAttnLargeWgs such workgroups)
+// take 4 tiles per wave and 16 per split instead: half the workgroups and
+// split records, more loads in flight per wave.  The whole GQA group of the
+// kv head shares every tile load.
 //
-// One 16-token page is exactly one matrix-core tile:
+// One 16-token tile is exactly one matrix-core tile:
 //   scores  S[t][g] = sum_d K[t][d] * q[g][d]      v_mfma_f32_16x16x32_bf16 x4
 //   output  O[g][d] += sum_t P[g][t] * V[t][d]     v_mfma_f32_16x16x16_bf16 x8
 // The score tile comes out of the first product in exactly the register
@@ -81,14 +84,13 @@ __device__ __forceinline__ u32x2 keep_first(u32x2 v, int nv) {
   return r;
 }
 
-template <int QM, int D>
+template <int QM, int D, int PW>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 5))) void
 paged_attention_kernel(const AttnArgs a) {
   constexpr int NH = D / 32;  // 32-wide q.K blocks
   constexpr int NC = D / 16;  // 16-wide output column blocks
   constexpr int REC = attn_rec(D);
-  constexpr int PW = kAttnPW;
-  constexpr int CP = kAttnPagesPerSplit;
+  constexpr int CP = kAttnWaves * PW;  // tiles per split
   constexpr int NW = kAttnWaves;
   constexpr int NT = NW * 64;
   __shared__ float sm_m[NW][16];
@@ -368,16 +370,25 @@ hipError_t launch_attention(const AttnArgs& a, int batch, int qmode, hipStream_t
   // would get most of the non-empty workgroups)
   const dim3 grid(a.Hkv, batch, a.max_splits);
   if (a.D != 64 && a.D != 128) return hipErrorInvalidValue;
+  if (a.pw != kAttnPW && a.pw != kAttnPWLarge) return hipErrorInvalidValue;
+  const bool large = a.pw == kAttnPWLarge;
+  const int nt = kAttnWaves * 64;
   if (a.D == 64) {
-    if (qmode == kQSplit)
-      paged_attention_kernel<kQSplit, 64><<<grid, kAttnWaves * 64, 0, st>>>(a);
-    else
-      paged_attention_kernel<kQBf16, 64><<<grid, kAttnWaves * 64, 0, st>>>(a);
+    if (qmode == kQSplit) {
+      if (large) paged_attention_kernel<kQSplit, 64, kAttnPWLarge><<<grid, nt, 0, st>>>(a);
+      else paged_attention_kernel<kQSplit, 64, kAttnPW><<<grid, nt, 0, st>>>(a);
+    } else {
+      if (large) paged_attention_kernel<kQBf16, 64, kAttnPWLarge><<<grid, nt, 0, st>>>(a);
+      else paged_attention_kernel<kQBf16, 64, kAttnPW><<<grid, nt, 0, st>>>(a);
+    }
   } else {
-    if (qmode == kQSplit)
-      paged_attention_kernel<kQSplit, 128><<<grid, kAttnWaves * 64, 0, st>>>(a);
-    else
-      paged_attention_kernel<kQBf16, 128><<<grid, kAttnWaves * 64, 0, st>>>(a);
+    if (qmode == kQSplit) {
+      if (large) paged_attention_kernel<kQSplit, 128, kAttnPWLarge><<<grid, nt, 0, st>>>(a);
+      else paged_attention_kernel<kQSplit, 128, kAttnPW><<<grid, nt, 0, st>>>(a);
+    } else {
+      if (large) paged_attention_kernel<kQBf16, 128, kAttnPWLarge><<<grid, nt, 0, st>>>(a);
+      else paged_attention_kernel<kQBf16, 128, kAttnPW><<<grid, nt, 0, st>>>(a);
+    }
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits <= 1) return e;

@@ -122,7 +122,8 @@ struct AttnArgs {
   float* part;             // split partial records [B][Hkv][max_splits][attn_rec(D)]
   uint32_t* err;
   int32_t Hq, Hkv, G;
-  int32_t max_splits;
+  int32_t max_splits;      // splits per sequence: the table's tiles / (kAttnWaves * pw)
+  int32_t pw;              // tiles per wave (kAttnPW or kAttnPWLarge)
   int32_t D;               // head width, 64 or 128
 };
 
@@ -327,15 +328,26 @@ hipError_t launch_sample(const float* logits, int B, int V, const float* tempera
 #define PKV_ATTN_WAVES 4
 #endif
 constexpr int kAttnWaves = PKV_ATTN_WAVES;
-constexpr int kAttnPW = 2;
+constexpr int kAttnPW = 2;       // tiles per wave of a small call
+constexpr int kAttnPWLarge = 4;  // tiles per wave of a large one
 constexpr int kAttnPagesPerSplit = kAttnWaves * kAttnPW;
+// From this many workgroups at kAttnPW (batch x kv heads x splits of the
+// table) a call takes kAttnPWLarge tiles per wave: half the workgroups,
+// records and merge work, more loads in flight per wave.  Below it the
+// shorter waves finish sooner.
+constexpr int64_t kAttnLargeWgs = 4096;
 // One split's partial record: m[16], l[16], o[16][64] floats.
 constexpr int attn_rec(int D) { return 16 + 16 + 16 * D; }
 
 // Splits of a block table of max_tiles 16-token tiles (max_pages pages of
 // 16 << pt_shift tokens: max_tiles = max_pages << pt_shift).
-inline int attn_max_splits(int64_t max_tiles) {
-  return (int)((max_tiles + kAttnPagesPerSplit - 1) / kAttnPagesPerSplit);
+inline int attn_max_splits(int64_t max_tiles, int pw = kAttnPW) {
+  const int cp = kAttnWaves * pw;
+  return (int)((max_tiles + cp - 1) / cp);
+}
+// Tiles per wave of a call over `batch` sequences of Hkv kv heads.
+inline int attn_pw(int batch, int Hkv, int64_t max_tiles) {
+  return (int64_t)batch * Hkv * attn_max_splits(max_tiles) >= kAttnLargeWgs ? kAttnPWLarge : kAttnPW;
 }
 
 // A GEMM launch: `rg` groups of 16 output rows per workgroup, `nw` waves

@@ -112,6 +112,26 @@ def _small_case(Hq, Hkv, lens, max_pages, scale):
     assert np.all(out[lens == 0] == 0)
 
 
+def test_attention_large_call_four_tiles_per_wave():
+    """64 sequences x 8 kv heads over a 128-page table: enough workgroups
+    that the call takes 4 tiles per wave (16 per split); lengths U[1,2048]
+    plus the edge lengths of a 16-tile split."""
+    Hq, Hkv, B = 32, 8, 64
+    lens = synth.rng(81, "lens").integers(1, 2049, size=B).astype(np.int32)
+    lens[:8] = [1, 16, 255, 256, 257, 512, 2047, 2048]
+    pe = synth.page_elems(Hkv)
+    npages = int(synth.pages_for(lens).sum())
+    pool = synth.random_pool(82, npages, pe)
+    bt = synth.block_tables(83, 1, lens, npages, max_pages=128)[0]
+    q = synth.bf16_normal(84, "q", (B, Hq, 64))
+    out, err = attention_gpu(pool, Hkv, q, bt, lens, 0.125)
+    ref = attention_oracle(pool, Hkv, q, bt, lens, 0.125)
+    assert err == 0
+    diff = np.abs(out - ref).max()
+    say("large call max-abs %.3g" % diff)
+    assert diff <= ATOL
+
+
 def test_attention_paged_equals_contiguous_bitwise():
     Hq, Hkv = 32, 8
     lens = np.array([1, 200, 1500, 2048], dtype=np.int32)

@@ -76,6 +76,23 @@ def test_attention_d128_llama8b_heads_full_size():
     assert diff <= ATOL
 
 
+def test_attention_d128_large_call():
+    """48 sequences x 8 kv heads over a 128-page table take 4 tiles per wave."""
+    Hq, Hkv, B = 32, 8, 48
+    lens = synth.rng(91, "lens").integers(1, 2049, size=B).astype(np.int32)
+    lens[:4] = [1, 256, 257, 2048]
+    pe = synth.page_elems(Hkv, head_dim=D)
+    npages = int(synth.pages_for(lens).sum())
+    pool = synth.random_pool(92, npages, pe)
+    bt = synth.block_tables(93, 1, lens, npages, max_pages=128)[0]
+    q = synth.bf16_normal(94, "q", (B, Hq, D))
+    scale = 1.0 / np.sqrt(D)
+    out, err = attention_gpu(pool, Hkv, q, bt, lens, scale)
+    ref = attention_oracle(pool, Hkv, q, bt, lens, scale)
+    assert err == 0
+    assert np.abs(out - ref).max() <= ATOL
+
+
 @pytest.mark.parametrize("Hq,Hkv,lens,max_pages", [
     (4, 1, [1], 1),
     (4, 2, [0, 1, 2, 15, 16, 17], 4),
