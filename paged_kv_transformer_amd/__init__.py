@@ -132,6 +132,55 @@ def _dev(t, dtypes, what):
     return t.data_ptr()
 
 
+# The library takes plain pointers and cannot see how large a buffer is: the
+# wrappers check every tensor against the elements the call reads or writes
+# before anything reaches the device (a short buffer would otherwise be
+# read or written past its end).
+
+def _at_least(t, n, what):
+    if t.numel() < n:
+        raise ValueError("%s holds %d elements; the call uses %d" % (what, t.numel(), n))
+
+
+def _table(t, rows, what):
+    """A block table [rows or more, max_pages]."""
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < 1:
+        raise ValueError("%s must be [>= %d, max_pages], got %s" % (what, rows, tuple(t.shape)))
+
+
+def _bytes_at_least(t, nbytes, what):
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes; the call reads %d" % (what, t.numel() * t.element_size(), nbytes))
+
+
+def _check_layer(cfg, layer, what="layer"):
+    H, I, D = cfg.hidden_size, cfg.intermediate_size, cfg.head_dim
+    QKV = (cfg.num_attention_heads + 2 * cfg.num_key_value_heads) * D
+    need = {"attn_norm": 2 * H, "mlp_norm": 2 * H,
+            "w_qkv": packed_weight_bytes(QKV, H, qkv_pack_kind(D) if D in (64, 128) else PACK_QKV),
+            "w_o": packed_weight_bytes(H, cfg.num_attention_heads * D, PACK_ROWS),
+            "w_gate_up": packed_weight_bytes(2 * I, H, PACK_GATE_UP),
+            "w_down": packed_weight_bytes(H, I, PACK_ROWS)}
+    for k, n in need.items():
+        _bytes_at_least(layer.tensors[k], n, "%s.%s" % (what, k))
+
+
+def _check_rope(cfg, rope_cos, rope_sin):
+    n = cfg.max_position_embeddings * (cfg.head_dim // 2)
+    _at_least(rope_cos, n, "rope_cos")
+    _at_least(rope_sin, n, "rope_sin")
+
+
+def _check_model(cfg, model):
+    if len(model.layers) < cfg.num_hidden_layers:
+        raise ValueError("the model has %d layers, the config %d" % (len(model.layers), cfg.num_hidden_layers))
+    _bytes_at_least(model.embed, packed_weight_bytes(cfg.vocab_size, cfg.hidden_size, PACK_ROWS), "embed")
+    _at_least(model.final_norm, cfg.hidden_size, "final_norm")
+    _check_rope(cfg, model.rope_cos, model.rope_sin)
+    for l in range(cfg.num_hidden_layers):
+        _check_layer(cfg, model.layers[l], "layer %d" % l)
+
+
 def make_config(shape, max_pos=None, layers=None):
     """Config from any object with the llmc header fields' meaning
     (hidden, layers, heads, kv_heads, head_dim, inter, vocab, max_pos,
@@ -174,6 +223,9 @@ def kv_pool_create_split(k_tensor, v_tensor, num_kv_heads, head_dim=HEAD_DIM,
 
 def kv_append(pool, block_table, positions, k_new, v_new, stream=None):
     B = positions.numel()
+    _table(block_table, B, "block_table")
+    _at_least(k_new, B * pool.num_kv_heads * pool.head_dim, "k_new")
+    _at_least(v_new, B * pool.num_kv_heads * pool.head_dim, "v_new")
     bt = _dev(block_table, (torch.int32,), "block_table")
     _check("kv_append", lib().kv_append(
         ctypes.byref(pool), bt, block_table.shape[-1], _dev(positions, (torch.int32,), "positions"),
@@ -227,6 +279,8 @@ def packed_weight_bytes(rows, cols, layout):
 def pack_weight(src, layout, stream=None):
     """Packed copy (int16 device tensor) of a row-major BF16 [rows, cols]
     device matrix, in the projections' tiled layout."""
+    if src.dim() != 2:
+        raise ValueError("src must be a [rows, cols] matrix, got %s" % (tuple(src.shape),))
     rows, cols = src.shape
     nbytes = packed_weight_bytes(rows, cols, layout)
     if nbytes == 0:
@@ -242,7 +296,12 @@ def pack_weight(src, layout, stream=None):
 def paged_gqa_decode(pool, q, block_table, context_lens, scale, out, workspace, stream=None):
     """q [B, Hq, D] BF16, block_table [B, max_pages] int32, context_lens [B]
     int32, out [B, Hq, D] FP32 (written); D is the pool's head width."""
+    if q.dim() != 3 or q.shape[2] != pool.head_dim:
+        raise ValueError("q must be [B, Hq, %d], got %s" % (pool.head_dim, tuple(q.shape)))
     B, Hq = q.shape[0], q.shape[1]
+    _table(block_table, B, "block_table")
+    _at_least(context_lens, B, "context_lens")
+    _at_least(out, B * Hq * pool.head_dim, "out")
     _check("paged_gqa_decode", lib().paged_gqa_decode(
         ctypes.byref(pool), _dev(q, _BF16_DTYPES, "q"), Hq,
         _dev(block_table, (torch.int32,), "block_table"), block_table.shape[-1],
@@ -283,6 +342,10 @@ def decoder_layer_decode(cfg, layer, rope_cos, rope_sin, pool, block_table, posi
                          workspace, stream=None):
     """hidden [B, H] FP32 is updated in place; block_table [B, max_pages]."""
     B = positions.numel()
+    _table(block_table, B, "block_table")
+    _at_least(hidden, B * cfg.hidden_size, "hidden")
+    _check_rope(cfg, rope_cos, rope_sin)
+    _check_layer(cfg, layer)
     _check("decoder_layer_decode", lib().decoder_layer_decode(
         ctypes.byref(cfg), ctypes.byref(layer.c), _dev(rope_cos, (torch.float32,), "rope_cos"),
         _dev(rope_sin, (torch.float32,), "rope_sin"), ctypes.byref(pool),
@@ -295,6 +358,14 @@ def decode_step(cfg, model, pool, block_tables, positions, token_ids, logits, ne
                 workspace, stream=None):
     """block_tables [L, B, max_pages]; logits [B, V] FP32 or None."""
     B = positions.numel()
+    L = cfg.num_hidden_layers
+    if block_tables.dim() != 3 or block_tables.shape[0] < L or block_tables.shape[1] != B:
+        raise ValueError("block_tables must be [>= %d, %d, max_pages], got %s" % (L, B, tuple(block_tables.shape)))
+    _at_least(token_ids, B, "token_ids")
+    _at_least(next_tokens, B, "next_tokens")
+    if logits is not None:
+        _at_least(logits, B * cfg.vocab_size, "logits")
+    _check_model(cfg, model)
     _check("decode_step", lib().decode_step(
         ctypes.byref(cfg), ctypes.byref(model.c), ctypes.byref(pool),
         _dev(block_tables, (torch.int32,), "block_tables"), block_tables.shape[-1],
@@ -313,6 +384,12 @@ def prefill(cfg, model, pool, block_tables, start_pos, token_ids, logits, next_t
     """Prefill of one sequence: block_tables [L, max_pages] (its table per
     layer), token_ids [T] at positions start_pos ..; logits [V] FP32 or None
     (the last token's), next_token [1] int32."""
+    L = cfg.num_hidden_layers
+    _table(block_tables, L, "block_tables")
+    _at_least(next_token, 1, "next_token")
+    if logits is not None:
+        _at_least(logits, cfg.vocab_size, "logits")
+    _check_model(cfg, model)
     _check("prefill", lib().prefill(
         ctypes.byref(cfg), ctypes.byref(model.c), ctypes.byref(pool),
         _dev(block_tables, (torch.int32,), "block_tables"), block_tables.shape[-1], int(start_pos),
@@ -331,7 +408,12 @@ def sample_workspace_bytes(batch, vocab):
 def sample_tokens(logits, temperature, top_p, top_k, u, tokens, workspace, stream=None):
     """logits [B, V] FP32; temperature, top_p, u [B] FP32; top_k [B] int32;
     tokens [B] int32 (written)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V], got %s" % (tuple(logits.shape),))
     B, V = logits.shape
+    for t, what in ((temperature, "temperature"), (top_p, "top_p"), (top_k, "top_k"), (u, "u"),
+                    (tokens, "tokens")):
+        _at_least(t, B, what)
     _check("sample_tokens", lib().sample_tokens(
         _dev(logits, (torch.float32,), "logits"), B, V, _dev(temperature, (torch.float32,), "temperature"),
         _dev(top_p, (torch.float32,), "top_p"), _dev(top_k, (torch.int32,), "top_k"),
