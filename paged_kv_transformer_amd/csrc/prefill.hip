@@ -166,28 +166,34 @@ __device__ __forceinline__ void wait_stages(int pend) {
 // Workgroups are mapped to tiles XCD by XCD, so the token tiles of one row
 // tile run on one XCD and share its L2 copy of the weights.  Out-of-range
 // row and token groups read zeros and are never stored.
-template <int RG, int CG>
+// WR wave rows by 2 wave columns: each wave owns RG row groups (16 RG
+// rows) by CG token groups.  The tall tiles run with WR = 4 (8 waves, two
+// per SIMD, so one wave's LDS operand reads overlap the other's products);
+// the small ones and the LM head with WR = 2.
+template <int RG, int CG, int WR>
 struct PgemmShape {
-  static constexpr int AR = 2 * RG;        // row groups per tile
+  static constexpr int NW = 2 * WR;        // waves
+  static constexpr int AR = WR * RG;       // row groups per tile
   static constexpr int BC = 2 * CG;        // token groups per tile
   static constexpr int NA = AR;            // W blocks per stage
   static constexpr int NB = AR + 2 * BC;   // blocks per stage
-  static constexpr int LPW = NB / 4;       // copies per wave per stage
+  static constexpr int LPW = NB / NW;      // copies per wave per stage
   static constexpr int NSTG = NB * 6 <= 144 ? 6 : 144 / NB;  // ring of at most 144 KiB
 };
 
-template <int EPI, int RG, int CG>
-__global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
-  using SH = PgemmShape<RG, CG>;
-  constexpr int AR = SH::AR, BC = SH::BC, NA = SH::NA, NB = SH::NB, LPW = SH::LPW;
+template <int EPI, int RG, int CG, int WR>
+__global__ __launch_bounds__(128 * WR) void prefill_gemm_kernel(const PgemmArgs a) {
+  using SH = PgemmShape<RG, CG, WR>;
+  constexpr int AR = SH::AR, BC = SH::BC, NA = SH::NA, NB = SH::NB, LPW = SH::LPW, NW = SH::NW;
   constexpr int NSTG = SH::NSTG;
-  static_assert(NA % 4 == 0 && NB % 4 == 0, "stage blocks split evenly over the waves");
+  static_assert(NA % NW == 0 && NB % NW == 0, "stage blocks split evenly over the waves");
   static_assert((NSTG - 2) * LPW <= 63, "vmcnt range");
+  static_assert(EPI != EPI_LOGITS || WR == 2, "the argmax keys assume two wave rows");
   __shared__ u32x4 ring[NSTG][NB][64];
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = w & 1, wc = w >> 1;
+  const int wr = w % WR, wc = w / WR;
   const int nrt = (a.w_groups + AR - 1) / AR;
   const int ntt = (a.T + 16 * BC - 1) / (16 * BC);
   const int nks = EPI == EPI_RESID ? a.ksplit : 1;
@@ -207,13 +213,13 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
 
   const i32x4 wres = rsrc_words(a.W, (uint32_t)a.w_groups * (uint32_t)S * 1024u);
   const i32x4 xres = rsrc_words(a.X, (uint32_t)((a.T + 15) / 16) * (uint32_t)S * 2048u);
-  // wave w copies blocks j = 4 i + w of each stage: W row group j for
-  // i < NA / 4, then X block j - NA = 2 c + h (token group c, half h)
+  // wave w copies blocks j = NW i + w of each stage: W row group j for
+  // i < NA / NW, then X block j - NA = 2 c + h (token group c, half h)
   uint32_t boff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int j = 4 * i + w;
-    if (i < NA / 4) {
+    const int j = NW * i + w;
+    if (i < NA / NW) {
       boff[i] = (uint32_t)(g0 + j) * S * 1024u + l * 16;
     } else {
       const int jb = j - NA;
@@ -227,8 +233,8 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const PgemmArgs a) {
     const uint32_t ks = (uint32_t)(s0 + st);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const bool isw = i < NA / 4;
-      lds_copy16(base + (uint32_t)(4 * i + w) * 1024u, boff[i] + ks * (isw ? 1024u : 2048u),
+      const bool isw = i < NA / NW;
+      lds_copy16(base + (uint32_t)(NW * i + w) * 1024u, boff[i] + ks * (isw ? 1024u : 2048u),
                  isw ? wres : xres);
     }
   };
@@ -737,19 +743,28 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
   }
 }
 
+// A plan's (rg, cg) names the workgroup tile as 32 rg rows by 32 cg tokens;
+// the 256- and 128-row tiles run on 8 waves (4 x 2), the others on 4.
 template <int EPI>
 hipError_t launch_pg(const PgemmArgs& a, const PgemmPlan& p, hipStream_t st) {
   const int wgs = p.tiles * (EPI == EPI_RESID ? p.ks : 1);
-  if (p.rg == 8 && p.cg == 4)
-    prefill_gemm_kernel<EPI, 8, 4><<<wgs, 256, 0, st>>>(a);
-  else if (p.rg == 4 && p.cg == 4)
-    prefill_gemm_kernel<EPI, 4, 4><<<wgs, 256, 0, st>>>(a);
-  else if (p.rg == 2 && p.cg == 4)
-    prefill_gemm_kernel<EPI, 2, 4><<<wgs, 256, 0, st>>>(a);
-  else if (p.rg == 2 && p.cg == 2)
-    prefill_gemm_kernel<EPI, 2, 2><<<wgs, 256, 0, st>>>(a);
-  else
+  if (p.rg == 8 && p.cg == 4) {
+    if constexpr (EPI != EPI_LOGITS)
+      prefill_gemm_kernel<EPI, 4, 4, 4><<<wgs, 512, 0, st>>>(a);
+    else
+      prefill_gemm_kernel<EPI, 8, 4, 2><<<wgs, 256, 0, st>>>(a);
+  } else if (p.rg == 4 && p.cg == 4) {
+    if constexpr (EPI != EPI_LOGITS)
+      prefill_gemm_kernel<EPI, 2, 4, 4><<<wgs, 512, 0, st>>>(a);
+    else
+      prefill_gemm_kernel<EPI, 4, 4, 2><<<wgs, 256, 0, st>>>(a);
+  } else if (p.rg == 2 && p.cg == 4) {
+    prefill_gemm_kernel<EPI, 2, 4, 2><<<wgs, 256, 0, st>>>(a);
+  } else if (p.rg == 2 && p.cg == 2) {
+    prefill_gemm_kernel<EPI, 2, 2, 2><<<wgs, 256, 0, st>>>(a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
