@@ -338,9 +338,13 @@ def time_step_cfg(torch, pkv, synth, wl, shape, model, max_pos, reps=10):
 
 
 def large_batch_steps(torch, pkv, synth, llama_model=None):
-    """The batch-64 Llama step and the batch-128 Qwen step: {name: object}."""
+    """The batch-1 and batch-64 Llama steps and the batch-128 Qwen step:
+    {name: object}."""
     out = {}
     for name, mk, shp, model_fn in (
+            ("step_c3", synth.c3_step, synth.LLAMA1B,
+             lambda: llama_model or pkv.upload_model(synth.model_weights(synth.LLAMA1B, 1002),
+                                                     synth.LLAMA1B.theta, 4097)),
             ("step_c4", synth.c4_step, synth.LLAMA1B,
              lambda: llama_model or pkv.upload_model(synth.model_weights(synth.LLAMA1B, 1002),
                                                      synth.LLAMA1B.theta, 4097)),
