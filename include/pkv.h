@@ -194,8 +194,10 @@ int kv_append(const pkv_pool *pool, const int32_t *block_table,
  * Query head h reads kv head h / (num_q_heads / Hkv).  For every head:
  *   out = sum_t softmax_t(scale * q.K_t) V_t  over t < n.
  * n == 0 gives zeros.  The result does not depend on where the pages lie
- * in the pool (work is split on logical pages).  workspace: at least
- * pkv_attention_workspace_bytes(...) bytes, initialised once.
+ * in the pool, on the page size or on the pool kind (work is split on
+ * 16-token tiles of the logical sequence).  D is the pool's head width.
+ * workspace: at least pkv_attention_workspace_bytes(...) bytes for the
+ * pool's head width and page size, initialised once.
  * Errors: -EINVAL (NULL, Hq % Hkv != 0, batch < 0, max_pages < 1),
  * -ENOTSUP (Hq / Hkv > 16, batch > 65535, max_pages * PT > 8388480), -ENOSPC
  * (workspace), -EIO; device errors PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH.
@@ -220,9 +222,11 @@ int paged_gqa_decode(const pkv_pool *pool, const uint16_t *q,
  *   [batch][max_pages].  rope_cos/rope_sin [max_position_embeddings][D/2].
  * Contractions accumulate in FP32 with FP32 activations (split into two
  * BF16 halves for the matrix cores).  Errors: as paged_gqa_decode plus
+ * -EINVAL (the pool's kv heads or head width differ from the config's),
  * -ENOTSUP (H or I not a multiple of 64 or above 65536, a weight matrix
- * above 2 GiB); device errors PKV_DEVERR_PAGE,
- * PKV_DEVERR_LENGTH, PKV_DEVERR_ROPE.
+ * above 2 GiB); device errors PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH,
+ * PKV_DEVERR_ROPE.  workspace: at least pkv_workspace_bytes(cfg, batch,
+ * max_pages, pool page size) bytes, initialised once.
  */
 int decoder_layer_decode(const pkv_config *cfg, const pkv_layer_weights *w,
 			 const float *rope_cos, const float *rope_sin,
@@ -272,7 +276,8 @@ int decode_step(const pkv_config *cfg, const pkv_model_weights *w,
  * start_pos + num_tokens past the table or max_position_embeddings),
  * -ENOTSUP (num_tokens > 65535, a prompt whose packed activations exceed
  * 2 GiB, unsupported sizes as decoder_layer_decode), -ENOSPC (workspace),
- * -EIO; device errors (ERR_PAGE, ERR_TOKEN) as decode_step.
+ * -EIO; device errors PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH, PKV_DEVERR_ROPE and
+ * PKV_DEVERR_TOKEN as decode_step.
  */
 int prefill(const pkv_config *cfg, const pkv_model_weights *w,
 	    const pkv_pool *pool, const int32_t *block_tables,
