@@ -206,7 +206,7 @@ def time_layer_b1(torch, pkv, synth, S, reps=10):
     16 layers' decoder_layer_decode calls captured in a HIP graph; returns
     (ms per layer, algorithmic bytes per layer)."""
     shape = S.shape
-    wl = synth.c3_step()
+    wl = synth.llama1b_step_b1()
     pool_t = pkv.to_device(wl.pool)
     pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
     bts = [pkv.to_device(wl.block_tables[l]) for l in range(shape.layers)]
@@ -286,14 +286,14 @@ def layer_bytes(shape, n_attend, q_bytes=4):
             + shape.kv_heads * shape.head_dim * 2 * 2 + 2 * shape.hidden * 4)
 
 
-def time_layer_c1(torch, pkv, synth, reps=20):
+def time_layer_qwen05_b1(torch, pkv, synth, reps=20):
     """The Qwen2.5-0.5B layer at batch 1, position 127, as a chain of 16
     distinct layers (16 weight draws, 16 page sets) in one HIP graph, so the
     layer's 30 MB are not served from the Infinity Cache; per-layer time =
     replay / 16.  Returns (list of per-layer ms per replay, bytes per layer)."""
     shape = synth.QWEN05
     L = 16
-    wl = synth.decode_workload("c1 chain", shape, 1001, [127], layers=L)
+    wl = synth.decode_workload("qwen0.5b layer chain", shape, 1001, [127], layers=L)
     layers = [pkv.upload_layer(synth.layer_weights(shape, 1001, l)) for l in range(L)]
     c, sn = pkv.rope_table(shape.theta, 128)
     cfg = pkv.make_config(shape, max_pos=128, layers=1)
@@ -342,13 +342,13 @@ def large_batch_steps(torch, pkv, synth, llama_model=None):
     {name: object}."""
     out = {}
     for name, mk, shp, model_fn in (
-            ("step_c3", synth.c3_step, synth.LLAMA1B,
+            ("step_llama1b_b1", synth.llama1b_step_b1, synth.LLAMA1B,
              lambda: llama_model or pkv.upload_model(synth.model_weights(synth.LLAMA1B, 1002),
                                                      synth.LLAMA1B.theta, 4097)),
-            ("step_c4", synth.c4_step, synth.LLAMA1B,
+            ("step_llama1b_b64", synth.llama1b_step_b64, synth.LLAMA1B,
              lambda: llama_model or pkv.upload_model(synth.model_weights(synth.LLAMA1B, 1002),
                                                      synth.LLAMA1B.theta, 4097)),
-            ("step_c5", synth.c5_step, synth.QWEN05,
+            ("step_qwen05_b128", synth.qwen05_step_b128, synth.QWEN05,
              lambda: pkv.upload_model(synth.model_weights(synth.QWEN05, 1005), synth.QWEN05.theta, 4097))):
         wlx = mk()
         mp_ = int(wlx.positions.max()) + 1
@@ -377,7 +377,7 @@ def page_geometries(torch, pkv, synth, rounds=4, reps=10, L=16):
     graph.  The pool holds seeded N(0,1) BF16 values drawn on the device.
     Returns {"d64": {geometry: object}, "d128": ...}."""
     out = {}
-    lens = synth.c2_lens(1002, 16)
+    lens = synth.attention_lens(1002, 16)
     B = len(lens)
     lens_t = pkv.to_device(lens)
     for shape in (synth.LLAMA1B, synth.LLAMA8B):
@@ -442,7 +442,7 @@ def time_layer_llama8b(torch, pkv, synth, reps=10, L=4):
     graph, so the 436 MB of each layer's weights come from HBM.  Returns an
     object for the JSON line."""
     shape = synth.LLAMA8B
-    lens = synth.c2_lens(1002, 16)
+    lens = synth.attention_lens(1002, 16)
     positions = (lens - 1).astype(np.int32)
     wl = synth.decode_workload("8b layers", shape, 1010, positions, layers=L, with_pool=False)
     layers = [pkv.upload_layer(synth.layer_weights(shape, 1010, l), head_dim=128) for l in range(L)]
@@ -723,7 +723,7 @@ def main():
     ap.add_argument("--large-batch-only", action="store_true",
                     help="time the batch-64 and batch-128 steps alone (for profiling)")
     ap.add_argument("--no-extra-configs", action="store_true",
-                    help="skip the c1 layer chain, the batch-64/128 steps and the copy ceilings")
+                    help="skip the qwen0.5b layer chain, the batch-64/128 steps and the copy ceilings")
     ap.add_argument("--prefill-tokens", type=int, default=512, help="0 skips the prefill timing")
     ap.add_argument("--variants-only", action="store_true",
                     help="time the page-geometry variants and the head-width-128 layer alone")
@@ -839,16 +839,16 @@ def main():
 
     extra = {}
     if not args.no_extra_configs:
-        c1_ms, c1_bytes = time_layer_c1(torch, pkv, synth)
-        c1_us = float(np.median(c1_ms)) * 1e3
-        c1_gbs = c1_bytes / (c1_us * 1e3)
-        log("c1 layer chain: %.2f us per layer (median), %.2f MB -> %.0f GB/s" % (c1_us, c1_bytes / 1e6, c1_gbs))
-        extra["layer_c1"] = {
+        lq_ms, lq_bytes = time_layer_qwen05_b1(torch, pkv, synth)
+        lq_us = float(np.median(lq_ms)) * 1e3
+        lq_gbs = lq_bytes / (lq_us * 1e3)
+        log("qwen0.5b layer chain: %.2f us per layer (median), %.2f MB -> %.0f GB/s" % (lq_us, lq_bytes / 1e6, lq_gbs))
+        extra["layer_qwen05_b1"] = {
             "workload": "decoder_layer_decode, qwen2.5-0.5b-shape layer, batch 1, position 127, "
                         "16 distinct layers chained in one HIP graph (per-layer = replay / 16)",
-            "bound": "hbm", "algorithmic_bytes": int(c1_bytes), "us_per_layer": pct([m * 1e3 for m in c1_ms]),
-            "achieved": round(c1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(c1_gbs / HBM_PEAK_GBS, 4), "gate_frac": 0.6}
+            "bound": "hbm", "algorithmic_bytes": int(lq_bytes), "us_per_layer": pct([m * 1e3 for m in lq_ms]),
+            "achieved": round(lq_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(lq_gbs / HBM_PEAK_GBS, 4), "gate_frac": 0.6}
         extra.update(large_batch_steps(torch, pkv, synth, S.model))
         extra["page_geometry"] = page_geometries(torch, pkv, synth)
         extra["layer_llama8b"] = time_layer_llama8b(torch, pkv, synth)

@@ -235,7 +235,7 @@ def decode_workload(name, shape, seed, positions, layers=None, num_pages=None,
     return Workload(name, shape, len(positions), positions, npages, bt, pool, page_tokens=page_tokens)
 
 
-def c1_layer(seed=1001):
+def qwen05_layer_b1(seed=1001):
     """One Qwen2.5-0.5B-shaped layer, batch 1, 127 cached + 1 new, 64-page pool."""
     shape = QWEN05
     wl = decode_workload("qwen2.5-0.5b-shape layer, batch 1, 127 cached + 1 new",
@@ -245,15 +245,15 @@ def c1_layer(seed=1001):
     return wl
 
 
-def c2_lens(seed=1002, batch=16, max_len=2048):
+def attention_lens(seed=1002, batch=16, max_len=2048):
     return rng(seed, "lens").integers(1, max_len + 1, size=batch).astype(np.int32)
 
 
-def c2_attention(seed=1002, batch=16, pool_bytes=128 << 20, shape=LLAMA1B, page_tokens=PAGE_TOKENS):
+def attention_workload(seed=1002, batch=16, pool_bytes=128 << 20, shape=LLAMA1B, page_tokens=PAGE_TOKENS):
     """Paged GQA attention alone, Llama-3.2-1B heads (or another shape's),
     lengths U[1,2048], pages of page_tokens tokens drawn from a 128 MiB pool
     with shuffled tables; Q N(0,1) BF16, scale 1/sqrt(head_dim)."""
-    lens = c2_lens(seed, batch)
+    lens = attention_lens(seed, batch)
     pe = page_elems(shape, page_tokens=page_tokens)
     npages = pool_bytes // (pe * 2)
     bt = block_tables(seed, 1, lens, npages, max_pages=2048 // page_tokens, page_tokens=page_tokens)[0]
@@ -266,7 +266,7 @@ def c2_attention(seed=1002, batch=16, pool_bytes=128 << 20, shape=LLAMA1B, page_
             "page_tokens": page_tokens}
 
 
-def c3_step(seed=1003, with_pool=True, layers=None):
+def llama1b_step_b1(seed=1003, with_pool=True, layers=None):
     shape = LLAMA1B
     L = shape.layers if layers is None else layers
     wl = decode_workload("llama-3.2-1b-shape 16-layer step, batch 1, context 1024",
@@ -275,20 +275,20 @@ def c3_step(seed=1003, with_pool=True, layers=None):
     return wl
 
 
-def c4_positions(seed=1004, batch=64):
+def llama1b_b64_positions(seed=1004, batch=64):
     return (rng(seed, "lens").integers(64, 2049, size=batch) - 1).astype(np.int32)
 
 
-def c4_step(seed=1004, batch=64, with_pool=True, layers=None):
+def llama1b_step_b64(seed=1004, batch=64, with_pool=True, layers=None):
     shape = LLAMA1B
     L = shape.layers if layers is None else layers
     wl = decode_workload("llama-3.2-1b-shape 16-layer step, batch 64, context U[64,2048]",
-                         shape, seed, c4_positions(seed, batch), layers=L, with_pool=with_pool)
+                         shape, seed, llama1b_b64_positions(seed, batch), layers=L, with_pool=with_pool)
     wl.extra["tokens"] = rng(seed, "tokens").integers(0, shape.vocab, size=batch).astype(np.int32)
     return wl
 
 
-def c5_step(seed=1005, batch=128, with_pool=True, layers=None):
+def qwen05_step_b128(seed=1005, batch=128, with_pool=True, layers=None):
     shape = QWEN05
     L = shape.layers if layers is None else layers
     wl = decode_workload("qwen2.5-0.5b-shape 24-layer step, batch 128, 4096 cached + 1 new",
@@ -303,7 +303,7 @@ def bench_step(seed=1002, batch=16, with_pool=True, layers=None):
     lengths are the paged-attention workload's draw (U[1,2048])."""
     shape = LLAMA1B
     L = shape.layers if layers is None else layers
-    positions = c2_lens(seed, batch) - 1
+    positions = attention_lens(seed, batch) - 1
     wl = decode_workload("llama-3.2-1b-shape 16-layer decode step, batch 16, "
                          "attention lengths U[1,2048] (the paged-attention draw)",
                          shape, seed, positions, layers=L, with_pool=with_pool)

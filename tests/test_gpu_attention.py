@@ -63,13 +63,13 @@ def test_kv_append_bit_exact(kv_heads, positions):
 
 def test_attention_c2_full_size():
     """Paged GQA attention, 32/8 heads, batch 16, lengths U[1,2048], 128 MiB pool."""
-    w = synth.c2_attention()
-    say("c2 attention, lens", w["lens"].tolist())
+    w = synth.attention_workload()
+    say("attention, lens", w["lens"].tolist())
     out, err = attention_gpu(w["pool"], 8, w["q"], w["block_table"], w["lens"], w["scale"])
     ref = attention_oracle(w["pool"], 8, w["q"], w["block_table"], w["lens"], w["scale"])
     assert err == 0
     diff = np.abs(out - ref).max()
-    say("c2 max-abs error %.3g" % diff)
+    say("attention max-abs error %.3g" % diff)
     assert diff <= ATOL
 
 
@@ -200,7 +200,7 @@ def test_attention_ignores_nan_in_unused_slots():
 
 
 def test_attention_workspace_reuse_is_deterministic():
-    w = synth.c2_attention(batch=4)
+    w = synth.attention_workload(batch=4)
     ws = pkv.alloc_workspace(pkv.attention_workspace_bytes(32, 8, 4, 128))
     a, _ = attention_gpu(w["pool"], 8, w["q"], w["block_table"], w["lens"], 0.125, ws=ws)
     b, _ = attention_gpu(w["pool"], 8, w["q"], w["block_table"], w["lens"], 0.125, ws=ws)

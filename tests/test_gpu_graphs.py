@@ -81,7 +81,7 @@ def test_decode_step_replays_match_eager(batch):
 
 
 def test_paged_attention_replays_match_eager():
-    w = synth.c2_attention(batch=8)
+    w = synth.attention_workload(batch=8)
     B, Hq = 8, 32
     lens = w["lens"]
     pool_t = dev(w["pool"])

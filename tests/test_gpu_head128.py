@@ -66,7 +66,7 @@ def test_kv_append_d128_bit_exact(kv_heads, positions):
 def test_attention_d128_llama8b_heads_full_size():
     """32/8 heads of width 128, batch 16, lengths U[1,2048], 128 MiB pool of
     64 KiB pages, shuffled tables."""
-    w = synth.c2_attention(shape=synth.LLAMA8B)
+    w = synth.attention_workload(shape=synth.LLAMA8B)
     say(w["name"], "lens", w["lens"].tolist())
     out, err = attention_gpu(w["pool"], 8, w["q"], w["block_table"], w["lens"], w["scale"])
     ref = attention_oracle(w["pool"], 8, w["q"], w["block_table"], w["lens"], w["scale"])

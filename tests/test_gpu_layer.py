@@ -42,7 +42,7 @@ def _check_layer(shape, lw, hidden, wl, seqs=None):
 
 def test_layer_c1_qwen_shape():
     """One Qwen2.5-0.5B-shaped layer, batch 1, 127 cached + 1 new, 64-page pool."""
-    wl = synth.c1_layer()
+    wl = synth.qwen05_layer_b1()
     _check_layer(wl.shape, wl.extra["weights"], wl.extra["hidden"], wl)
 
 
@@ -143,26 +143,26 @@ def test_step_tiny_model_large_batch(batch):
     assert np.array_equal(nxt, nxt2)
 
 
-def test_step_c3_llama_shape_batch1():
+def test_step_llama_shape_batch1():
     """16-layer Llama-3.2-1B-shaped step, batch 1, context 1024."""
-    wl = synth.c3_step()
+    wl = synth.llama1b_step_b1()
     weights = synth.model_weights(wl.shape, 1003)
     _check_step(wl.shape, weights, wl, wl.extra["tokens"])
 
 
-def test_step_c4_llama_shape_batch64_sampled():
+def test_step_llama_shape_batch64_sampled():
     """Batch 64, context U[64,2048]; the oracle checks a sample of sequences."""
-    wl = synth.c4_step()
+    wl = synth.llama1b_step_b64()
     weights = synth.model_weights(wl.shape, 1004)
     order = np.argsort(wl.positions)
     seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
     _check_step(wl.shape, weights, wl, wl.extra["tokens"], seqs=seqs)
 
 
-def test_step_c5_qwen_shape_batch128_long_context_sampled():
+def test_step_qwen_shape_batch128_long_context_sampled():
     """24-layer Qwen2.5-0.5B-shaped step at batch 128, every sequence at 4096
     cached tokens (257 pages of each of 24 layers, a 6 GiB pool of randomly
     permuted 8 KiB pages); the oracle checks the first and last sequences."""
-    wl = synth.c5_step()
+    wl = synth.qwen05_step_b128()
     weights = synth.model_weights(wl.shape, 1005)
     _check_step(wl.shape, weights, wl, wl.extra["tokens"], seqs=[0, len(wl.positions) - 1])

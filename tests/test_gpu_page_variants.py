@@ -90,7 +90,7 @@ def test_attention_full_size_256_token_pages(D):
     """32/8 heads, batch 16, lengths U[1,2048], 128 MiB pool of 256-token
     pages with shuffled tables."""
     shape = synth.LLAMA1B if D == 64 else synth.LLAMA8B
-    w = synth.c2_attention(shape=shape, page_tokens=256)
+    w = synth.attention_workload(shape=shape, page_tokens=256)
     say(w["name"])
     out, err = attention_gpu(w["pool"], 8, w["q"], w["block_table"], w["lens"], w["scale"],
                              page_tokens=256)
