@@ -208,9 +208,52 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     }
   };
 
+  // Epilogue inputs whose addresses do not depend on the products (the
+  // sequence's position, then its RoPE row and the page that takes the
+  // appended slot; the residual) are loaded around the first weight stage,
+  // so their round trips overlap the weight stream instead of following it.
+  // This thread's first epilogue item is idx = tid.  Indices are clamped
+  // here and validated where the values are used.
+  constexpr int NT = NW * 64;
+  int pf_p = 0, pf_page = 0;
+  float pf_r = 0.f, pf_cs = 1.f, pf_sn = 0.f;
+  int hd = 0, j0 = 0;
+  bool is_q = false, is_k = false;
+  if constexpr (EPI == EPI_QKV) {
+    const int gph = a.D / 16;  // 16-row groups per head
+    hd = t / gph;
+    j0 = 8 * (t % gph);
+    is_q = hd < a.Hq;
+    is_k = !is_q && hd < a.Hq + a.Hkv;
+    if (tid < 8 * a.B) pf_p = a.pos[tid >> 3];
+  }
+  if constexpr (EPI == EPI_RESID) {
+    if (nks == 1 && tid < R * a.B) {
+      const int n = t * R + tid % R;
+      if (n < a.N) pf_r = a.resid[(size_t)(tid / R) * a.N + n];
+    }
+  }
+  auto prefetch2 = [&]() {
+    if constexpr (EPI == EPI_QKV) {
+      if (tid < 8 * a.B) {
+        const int j = j0 + (tid & 7), half = a.D / 2;
+        const int pc = max(pf_p, 0);
+        if ((is_q || is_k) && a.max_pos > 0) {
+          const size_t r = (size_t)min(pc, a.max_pos - 1) * half + j;
+          pf_cs = a.rcos[r];
+          pf_sn = a.rsin[r];
+        }
+        if (!is_q && a.bt_stride > 0)
+          pf_page = a.bt[(size_t)(tid >> 3) * a.bt_row + min(pc >> (4 + a.pv.pt_shift), a.bt_stride - 1)];
+      }
+    }
+  };
+
+  if (s0 >= s1) prefetch2();
   if (s0 < s1) {
     Stage A, B;
     load(A, s0);
+    prefetch2();
     for (int st = s0;; st += 2 * U) {
       load(B, st + U);
       compute(A, st);
@@ -249,7 +292,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   __syncthreads();
 
   // ---- epilogues
-  constexpr int NT = NW * 64;
   if (EPI == EPI_RESID) {
     for (int i = tid; i < R * a.B; i += NT) {
       const int c = i / R, row = i % R;
@@ -259,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         if (nks > 1) {
           a.part[(size_t)ksi * a.B * a.N + o] = tile[c * TS + row];
         } else {
-          const float v = a.resid[o] + tile[c * TS + row];
+          const float v = (i == tid ? pf_r : a.resid[o]) + tile[c * TS + row];
           a.out[o] = v;
           if (a.out_packed) a.out_packed[packed_act_index(c, n, a.N)] = v;
         }
@@ -267,24 +309,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
     }
   } else if (EPI == EPI_QKV) {
     // head width D: a 16-row group holds 8 RoPE pairs (j, j + D/2) of one head
-    const int D = a.D, half = D / 2, gph = D / 16;
-    const int hd = t / gph, j0 = 8 * (t % gph);
-    const bool is_q = hd < a.Hq;
-    const bool is_k = !is_q && hd < a.Hq + a.Hkv;
+    const int D = a.D, half = D / 2;
     for (int idx = tid; idx < 8 * a.B; idx += NT) {
       const int c = idx >> 3, i = idx & 7, j = j0 + i;
+      const bool first = idx == tid;
       const float rs = 1.0f / sqrtf(ssq_col[c] / (float)a.K + a.eps);
       const float x0 = tile[c * TS + i] * rs;
       const float x1 = tile[c * TS + 8 + i] * rs;
-      const int p = a.pos[c];
+      const int p = first ? pf_p : a.pos[c];
       float y0 = x0, y1 = x1;
       if (is_q || is_k) {
         if (p < 0 || p >= a.max_pos) {
           set_error(a.err, ERR_ROPE);
           continue;
         }
-        const float cs = a.rcos[(size_t)p * half + j];
-        const float sn = a.rsin[(size_t)p * half + j];
+        const float cs = first ? pf_cs : a.rcos[(size_t)p * half + j];
+        const float sn = first ? pf_sn : a.rsin[(size_t)p * half + j];
         y0 = __fsub_rn(__fmul_rn(x0, cs), __fmul_rn(x1, sn));
         y1 = __fadd_rn(__fmul_rn(x0, sn), __fmul_rn(x1, cs));
       }
@@ -302,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
           set_error(a.err, ERR_LENGTH);
           continue;
         }
-        const int page = a.bt[(size_t)c * a.bt_row + (p >> psh)];
+        const int page = first ? pf_page : a.bt[(size_t)c * a.bt_row + (p >> psh)];
         if ((unsigned)page >= (unsigned)a.pv.num_pages) {
           set_error(a.err, ERR_PAGE);
           continue;
