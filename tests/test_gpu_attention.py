@@ -61,7 +61,7 @@ def test_kv_append_bit_exact(kv_heads, positions):
     assert np.array_equal(host_u16(pool_t), want)
 
 
-def test_attention_c2_full_size():
+def test_attention_full_size_llama1b_heads_batch16():
     """Paged GQA attention, 32/8 heads, batch 16, lengths U[1,2048], 128 MiB pool."""
     w = synth.attention_workload()
     say("attention, lens", w["lens"].tolist())

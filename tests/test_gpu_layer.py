@@ -40,7 +40,7 @@ def _check_layer(shape, lw, hidden, wl, seqs=None):
     return diff
 
 
-def test_layer_c1_qwen_shape():
+def test_layer_qwen_shape_batch1():
     """One Qwen2.5-0.5B-shaped layer, batch 1, 127 cached + 1 new, 64-page pool."""
     wl = synth.qwen05_layer_b1()
     _check_layer(wl.shape, wl.extra["weights"], wl.extra["hidden"], wl)
