@@ -82,6 +82,8 @@ CASES = [
     (16, 1, [77, 300], 20),
     (8, 8, [33, 513], 40),
     (6, 2, [16, 160, 161], 11),
+    (8, 2, [64, 63, 1], 4),          # a sequence fills its whole block table
+    (8, 1, [16384, 5], 1024),        # 128 splits of one sequence in the merge
 ]
 
 
