@@ -28,6 +28,11 @@ oracle timed on a bounded sample of the same workload.
                                       one by one, then a 256 MiB device copy
                                       of known size: the run that rocprofv3
                                       counters are taken on)
+  python bench.py --step-counters    (3 eager batch-16 steps, then the same
+                                      copy: the step's counter runs)
+  python bench.py --counter-table FETCH.csv WRITE.csv
+                                     (every library kernel's scaled FETCH_SIZE
+                                      and WRITE_SIZE per dispatch, markdown)
   python bench.py --traffic-summary FETCH.csv WRITE.csv
                                      (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
                                       counter_collection.csv files of two
@@ -663,6 +668,48 @@ def attention_only(torch, pkv, synth, rounds):
           "read + written" % (rounds * A.layers, abytes, n), flush=True)
 
 
+def step_counters(torch, pkv, synth, steps=3):
+    """Launch sequence for the hardware-counter runs of the step: `steps`
+    eager decode steps of the batch-16 workload (each kernel its own
+    dispatch), then the counters' calibration copy."""
+    S = Setup(torch, pkv, synth, HostInputs(synth))
+    for _ in range(steps):
+        S.step(pkv)
+    torch.cuda.synchronize()
+    assert pkv.device_error(S.ws) == 0
+    n = COPY_BYTES
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("step-counters: %d eager steps; copy calibration: 3 x %d bytes read + written" % (steps, n),
+          flush=True)
+
+
+def counter_table(fetch_csv, write_csv):
+    """Every library kernel's FETCH_SIZE and WRITE_SIZE per dispatch, each
+    scaled by what the counter reads for the calibration copy, as a
+    markdown table (MB per dispatch)."""
+    rows = {}
+    for cname, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = _counter_values(path)
+        copy = [max(v) for (k, c), v in vals.items() if c == cname and "copyBuffer" in k]
+        assert copy, "no device copy in %s" % path
+        scale = COPY_BYTES / (max(copy) * 1024.0)
+        for (k, c), v in vals.items():
+            if c != cname or "pkv::" not in k:
+                continue
+            short = k.replace("pkv::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            r = rows.setdefault(short, {})
+            r["n"] = len(v)
+            r[cname] = sum(v) / len(v) * 1024.0 * scale / 1e6
+    print("| kernel | dispatches | fetch MB / dispatch | write MB / dispatch |")
+    print("|---|---:|---:|---:|")
+    for k, r in sorted(rows.items(), key=lambda kv: -kv[1].get("FETCH_SIZE", 0.0) * kv[1]["n"]):
+        print("| %s | %d | %.3f | %.3f |" % (k, r["n"], r.get("FETCH_SIZE", 0.0), r.get("WRITE_SIZE", 0.0)))
+
+
 def _counter_values(path):
     """Counter values per (kernel name, counter) from a rocprofv3
     counter_collection.csv (one row per dispatch and counter)."""
@@ -717,6 +764,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch the step directly, no HIP graph")
     ap.add_argument("--attention-only", action="store_true")
+    ap.add_argument("--step-counters", action="store_true",
+                    help="3 eager batch-16 steps and the calibration copy (for counter runs)")
+    ap.add_argument("--counter-table", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="per-kernel scaled FETCH_SIZE / WRITE_SIZE of a counter run")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE)
     ap.add_argument("--no-layer-b1", action="store_true")
@@ -733,6 +784,9 @@ def main():
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, out_path=args.traffic_out)
         return
+    if args.counter_table:
+        counter_table(*args.counter_table)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only (the path runs on a single MI355X); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -742,13 +796,16 @@ def main():
     import paged_kv_transformer_amd as pkv
     import synth
 
-    if args.attention_only or args.prefill_only or args.large_batch_only or args.variants_only:
+    if (args.attention_only or args.prefill_only or args.large_batch_only or args.variants_only
+            or args.step_counters):
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(2)
         torch.cuda.set_device(0)
         if args.attention_only:
             attention_only(torch, pkv, synth, args.attn_rounds)
+        elif args.step_counters:
+            step_counters(torch, pkv, synth)
         elif args.prefill_only:
             prefill_only(torch, pkv, synth, args.prefill_tokens)
         elif args.variants_only:
