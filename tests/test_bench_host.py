@@ -60,6 +60,28 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     assert t["attention_source_sha"] == bench.source_sha(bench.ATTN_SOURCE)
 
 
+def test_counter_table_scales_each_library_kernel(tmp_path, capsys):
+    mib = bench.COPY_BYTES / 2.0 ** 20
+    gate = "void pkv::(anonymous namespace)::gemm_kernel<1, 2, 4, 2, false>(pkv::GemmArgs)"
+    red = "pkv::(anonymous namespace)::resid_reduce_kernel(float const*, int, int, int, float const*, float*, float*)"
+    # the copy reads as half its size (scale 2) for FETCH, its size for WRITE;
+    # torch's own kernels are left out
+    _write_counters(tmp_path / "f.csv", [
+        ("__amd_rocclr_copyBuffer", "FETCH_SIZE", 0.5 * mib * 1024),
+        (gate, "FETCH_SIZE", 1000.0), (gate, "FETCH_SIZE", 3000.0), (red, "FETCH_SIZE", 10.0),
+        ("at::native::vectorized_elementwise_kernel", "FETCH_SIZE", 5.0)])
+    _write_counters(tmp_path / "w.csv", [
+        ("__amd_rocclr_copyBuffer", "WRITE_SIZE", mib * 1024),
+        (gate, "WRITE_SIZE", 100.0), (gate, "WRITE_SIZE", 100.0), (red, "WRITE_SIZE", 20.0)])
+    bench.counter_table(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    lines = capsys.readouterr().out.strip().splitlines()
+    rows = {ln.split("|")[1].strip(): ln for ln in lines[2:]}
+    assert set(rows) == {"gemm_kernel<1, 2, 4, 2, false>", "resid_reduce_kernel"}
+    g = [c.strip() for c in rows["gemm_kernel<1, 2, 4, 2, false>"].split("|")[2:5]]
+    assert g == ["2", "%.3f" % (2000.0 * 1024 * 2 / 1e6), "%.3f" % (100.0 * 1024 / 1e6)]
+    assert lines[2].startswith("| gemm_kernel")  # largest fetch first
+
+
 def test_prefill_flops_counts_projections_causal_attention_and_one_head_row():
     s = synth.tiny_shape(hidden=128, layers=3, heads=4, kv_heads=2, inter=256, vocab=1000)
     start, T = 5, 3
