@@ -476,11 +476,12 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
   switch (epi) {
     case EPI_QKV:
       if (a.x_plain)
-        e = ct == 1 ? go<1, 1, 8, EPI_QKV, true>(a, p.tiles, st)
+        e = ct == 1 ? (p.nw == 4 ? go<1, 1, 4, EPI_QKV, true>(a, p.tiles, st)
+                                 : go<1, 1, 8, EPI_QKV, true>(a, p.tiles, st))
             : ct == 2 ? go<2, 1, 8, EPI_QKV, true>(a, p.tiles, st)
                       : go<4, 1, 8, EPI_QKV, true>(a, p.tiles, st);
       else
-        e = ct == 1 ? go<1, 1, 8, EPI_QKV>(a, p.tiles, st)
+        e = ct == 1 ? (p.nw == 4 ? go<1, 1, 4, EPI_QKV>(a, p.tiles, st) : go<1, 1, 8, EPI_QKV>(a, p.tiles, st))
             : ct == 2 ? go<2, 1, 8, EPI_QKV>(a, p.tiles, st)
                       : go<4, 1, 8, EPI_QKV>(a, p.tiles, st);
       break;
@@ -497,7 +498,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
                                                           a.out_packed);
         e = hipGetLastError();
       } else {
-        e = ct == 1 ? go<1, 1, 8, EPI_RESID>(a, p.tiles, st)
+        e = ct == 1 ? (p.nw == 4 ? go<1, 1, 4, EPI_RESID>(a, p.tiles, st) : go<1, 1, 8, EPI_RESID>(a, p.tiles, st))
             : ct == 2 ? go<2, 1, 8, EPI_RESID>(a, p.tiles, st)
                       : go<4, 1, 8, EPI_RESID>(a, p.tiles, st);
       }

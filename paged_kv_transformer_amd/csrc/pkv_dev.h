@@ -372,6 +372,11 @@ inline int gemm_ct(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
 constexpr int kSplitMinK = 4096;
 constexpr int kSplitTargetWgs = 512;
 constexpr int kSplitMinSteps = 8;  // 32-wide K steps per split, at least
+// The QKV and O launches of one 16-column group (one 16-row tile per
+// workgroup) run 8 waves for a few sequences and 4 from this many on:
+// measured 1 % faster per batch-16 step with 4, 2 % slower per batch-1
+// layer (the threshold between the two is not measured).
+constexpr int kGemmFourWaveCols = 9;
 
 inline bool gemm_split(int epi, int N, int K) {
   return epi == EPI_RESID && K >= kSplitMinK && (N + 15) / 16 < kSplitTargetWgs / 2;
@@ -390,7 +395,8 @@ inline GemmPlan plan_gemm(int epi, int N, int B, int K) {
   const bool split = gemm_split(epi, N, K);
   const int R = gemm_rows_per_tile(epi, p.ct, split);
   p.rg = R / 16;
-  p.nw = split ? 4 : (epi == EPI_RESID || epi == EPI_QKV ? 8 : 4);
+  p.nw = split ? 4
+         : (epi == EPI_RESID || epi == EPI_QKV ? (p.ct == 1 && B >= kGemmFourWaveCols ? 4 : 8) : 4);
   // the gate/up tile holds R/2 gate rows and the R/2 matching up rows
   const int rows = epi == EPI_SWIGLU ? N / 2 : N;
   const int per = epi == EPI_SWIGLU ? R / 2 : R;
