@@ -46,8 +46,8 @@ def test_layer_qwen_shape_batch1():
     _check_layer(wl.shape, wl.extra["weights"], wl.extra["hidden"], wl)
 
 
-@pytest.mark.parametrize("batch,hkv,heads", [(1, 2, 4), (3, 2, 14), (17, 1, 16), (40, 4, 8),
-                                             (70, 2, 4), (130, 2, 4)])
+@pytest.mark.parametrize("batch,hkv,heads", [(1, 2, 4), (3, 2, 14), (9, 2, 4), (16, 2, 14), (17, 1, 16),
+                                             (40, 4, 8), (70, 2, 4), (130, 2, 4)])
 def test_layer_tiny_shapes(batch, hkv, heads):
     shape = synth.tiny_shape(hidden=192, heads=heads, kv_heads=hkv, inter=384, name="tiny-layer")
     seed = 100 + batch
