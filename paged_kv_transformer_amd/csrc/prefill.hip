@@ -608,6 +608,11 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
     u32x2 v[kPW][NC];
   };
   bool bad = false;
+  // A lane's element offsets inside a tile do not change from tile to tile
+  // (K: slot col, dims 8 grp..; V: dim col, slots 4 grp..): the address of a
+  // load is the tile's base, uniform across the wave, plus these.
+  const uint32_t klane = (uint32_t)(col * D + 8 * grp);
+  const uint32_t vlane = (uint32_t)(col * kTile + 4 * grp);
   // tiles past the wave's range read its last tile and are masked
   auto load = [&](Chunk& C, int lp0) {
 #pragma unroll
@@ -618,12 +623,12 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
       const bool ok = (unsigned)page < (unsigned)a.pv.num_pages;
       bad |= !ok;
       page = ok ? page : 0;
-      const uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, kvh, sub + col, D) + 8 * grp;
+      const uint16_t* kb = a.pv.k + pv_k_index(a.pv, page, kvh, sub, D);
 #pragma unroll
-      for (int h = 0; h < NH; ++h) C.k[i][h] = *(const u32x4*)(kp + 32 * h);
-      const uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, kvh, col, sub, D) + 4 * grp;
+      for (int h = 0; h < NH; ++h) C.k[i][h] = *(const u32x4*)(kb + klane + 32 * h);
+      const uint16_t* vb = a.pv.v + pv_v_index(a.pv, page, kvh, 0, sub, D);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vp + c * 16 * kTile);
+      for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vb + vlane + c * 16 * kTile);
     }
   };
 
