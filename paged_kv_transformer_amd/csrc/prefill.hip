@@ -559,6 +559,10 @@ __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const floa
 // log-sum-exp rule.  Workgroups with the latest tokens (the most pages) are
 // launched first.
 constexpr int kPW = 2;
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs a) {
@@ -637,7 +641,11 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const Chunk& C, int lp0) {
+  // MASKED false: every tile of the chunk lies in the wave's range and below
+  // the group's first position, so no score, probability or V slot needs a
+  // mask (the masked variant computes the same values for such tiles).
+  auto step = [&](const Chunk& C, int lp0, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     f32x4 s[kPW];
     bool full[kPW], inr[kPW];
     float mx = -INFINITY;
@@ -650,8 +658,8 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
         acc = mfma_k32(C.k[i][h], ql[h], acc);
       }
       const int kp0 = (lp0 + i) * kTile;
-      inr[i] = lp0 + i < pe;                              // uniform
-      full[i] = inr[i] && kp0 + kTile - 1 <= pmin;  // uniform
+      inr[i] = !MASKED || lp0 + i < pe;                              // uniform
+      full[i] = !MASKED || (inr[i] && kp0 + kTile - 1 <= pmin);  // uniform
       if (!full[i]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = inr[i] && kp0 + 4 * grp + r <= lim ? acc[r] : -INFINITY;
@@ -698,7 +706,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         u32x2 vv = C.v[i][c];
-        if (nv < 4) {
+        if (MASKED && nv < 4) {
           vv.x = nv >= 2 ? vv.x : (nv == 1 ? (vv.x & 0xffffu) : 0u);
           vv.y = nv == 3 ? (vv.y & 0xffffu) : 0u;
         }
@@ -712,12 +720,20 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
   if (pb < pe) {
     Chunk A, B;
     load(A, pb);
+    // chunks starting before `lfull` hold only full tiles in range
+    const int lfull = min(pe, (pmin + 1) / kTile) - kPW + 1;
+    auto run = [&](const Chunk& C, int lp) {
+      if (lp < lfull)
+        step(C, lp, BoolC<false>{});
+      else
+        step(C, lp, BoolC<true>{});
+    };
     for (int lp = pb;; lp += 2 * kPW) {
       if (lp + kPW < pe) load(B, lp + kPW);
-      step(A, lp);
+      run(A, lp);
       if (lp + kPW >= pe) break;
       if (lp + 2 * kPW < pe) load(A, lp + 2 * kPW);
-      step(B, lp + kPW);
+      run(B, lp + kPW);
       if (lp + 2 * kPW >= pe) break;
     }
   }
