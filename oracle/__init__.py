@@ -77,7 +77,7 @@ def _load():
             "orc_pool_gather": (None, [_P, _L, _I, _I, _I, _P, _I, _P, _P]),
             "orc_pool_append": (None, [_P, _L, _I, _I, _I, _P, _I, _P, _P]),
             "orc_layer_decode": (_I, [_I, _I, _I, _I, _I, _F, _F] + [_P] * 6
-                                 + [_P, _P, _P, _I, _I, _P, _P]),
+                                 + [_P, _P, _P, _I, _I, _P, _P, _I]),
             "orc_embed": (None, [_P, _I, _I, _P]),
             "orc_lm_head": (_I, [_P, _I, _I, _P, _F, _P, _P]),
         }
@@ -243,9 +243,12 @@ def pool_append(pool, geo, bt_row, pos, k_bits, v_bits):
 _LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
 
 
-def layer_decode(shape, lw, x, kc, vc, pos):
+def layer_decode(shape, lw, x, kc, vc, pos, row_given=False):
     """One layer for one sequence.  kc/vc [cap, kv*D] float32 are updated in
-    place (row pos).  Returns (x_out, k_new_bits, v_new_bits)."""
+    place (row pos).  Returns (x_out, k_new_bits, v_new_bits).  row_given:
+    row pos already holds this token's K/V (teacher forcing in tests) and
+    attention reads it as given; the returned bits are still this layer's
+    own."""
     x = np.array(x, dtype=np.float32, copy=True)
     assert kc.dtype == np.float32 and kc.flags["C_CONTIGUOUS"]
     assert vc.dtype == np.float32 and vc.flags["C_CONTIGUOUS"]
@@ -257,7 +260,7 @@ def layer_decode(shape, lw, x, kc, vc, pos):
         shape.hidden, shape.heads, shape.kv_heads, shape.head_dim, shape.inter,
         shape.eps, shape.theta, *[_p(w, np.uint16) for w in ws],
         _p(x, np.float32), _p(kc, np.float32), _p(vc, np.float32), kc.shape[0], pos,
-        _p(k_new, np.uint16), _p(v_new, np.uint16))
+        _p(k_new, np.uint16), _p(v_new, np.uint16), int(bool(row_given)))
     if rc != 0:
         raise ValueError("position %d outside the cache of %d rows" % (pos, kc.shape[0]))
     return x, k_new, v_new

@@ -281,7 +281,8 @@ int orc_layer_decode(int H, int hq, int hkv, int D, int I, float eps,
 		     const uint16_t *w_qkv, const uint16_t *w_o,
 		     const uint16_t *mlp_norm, const uint16_t *w_gate_up,
 		     const uint16_t *w_down, float *x, float *kc, float *vc,
-		     int cap, int pos, uint16_t *k_new, uint16_t *v_new)
+		     int cap, int pos, uint16_t *k_new, uint16_t *v_new,
+		     int row_given)
 {
 	if (pos < 0 || pos >= cap)
 		return -1;
@@ -303,11 +304,19 @@ int orc_layer_decode(int H, int hq, int hkv, int D, int I, float eps,
 	orc_rope(q, hq, D, pos, theta);
 	orc_rope(k, hkv, D, pos, theta);
 
-	/* append: the cache row holds what the BF16 pool would hold */
+	/*
+	 * append: the cache row holds what the BF16 pool would hold.  With
+	 * row_given the caller has already put this token's K/V in row pos
+	 * (teacher forcing in tests: the values another implementation wrote)
+	 * and the row is left as it is; k_new / v_new still receive this
+	 * function's own values.
+	 */
 	for (int i = 0; i < kvd; i++) {
 		uint16_t kb = orc_f32_to_bf16(k[i]), vb = orc_f32_to_bf16(v[i]);
-		kc[(long)pos * kvd + i] = orc_bf16_to_f32(kb);
-		vc[(long)pos * kvd + i] = orc_bf16_to_f32(vb);
+		if (!row_given) {
+			kc[(long)pos * kvd + i] = orc_bf16_to_f32(kb);
+			vc[(long)pos * kvd + i] = orc_bf16_to_f32(vb);
+		}
 		if (k_new)
 			k_new[i] = kb;
 		if (v_new)

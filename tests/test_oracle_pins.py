@@ -481,3 +481,28 @@ def test_prefill_of_one_token_is_a_decode_step():
     logits, best, _ = oracle.prefill_paged(shape, wts, pool, geo, bts, 30, tokens)
     ref, nxt, _, _ = oracle.decode_step_paged(shape, wts, pool, geo, bts[:, None], [30], tokens)
     assert np.array_equal(logits, ref[0]) and best == nxt[0]
+
+
+def test_layer_with_a_given_cache_row():
+    """row_given: attention reads row pos as the caller wrote it.  With the
+    values the layer would write itself the result is identical; with
+    other values the returned K/V (the layer's own) are unchanged and only
+    the output moves."""
+    shape = synth.tiny_shape(hidden=64, heads=4, kv_heads=2, inter=128, head_dim=16, name="rowgiven")
+    lw = synth.layer_weights(shape, 5, 0, sigma=0.1, norm_sigma=0.2)
+    g = np.random.default_rng(6)
+    x = g.standard_normal(shape.hidden).astype(np.float32)
+    pos, kvd = 6, shape.kv_heads * shape.head_dim
+    kc = g.standard_normal((pos + 1, kvd)).astype(np.float32)
+    vc = g.standard_normal((pos + 1, kvd)).astype(np.float32)
+    y, kb, vb = oracle.layer_decode(shape, lw, x, kc.copy(), vc.copy(), pos)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[pos], vc2[pos] = oracle.bf16_to_f32(kb), oracle.bf16_to_f32(vb)
+    y2, kb2, vb2 = oracle.layer_decode(shape, lw, x, kc2, vc2, pos, row_given=True)
+    assert np.array_equal(y, y2) and np.array_equal(kb, kb2) and np.array_equal(vb, vb2)
+    kc3, vc3 = kc2.copy(), vc2.copy()
+    vc3[pos] += 0.5
+    y3, kb3, vb3 = oracle.layer_decode(shape, lw, x, kc3, vc3, pos, row_given=True)
+    assert np.array_equal(kb, kb3) and np.array_equal(vb, vb3)
+    assert not np.array_equal(y, y3)
+    assert np.array_equal(vc3[pos], vc2[pos] + 0.5)  # the given row is left as it is
