@@ -61,6 +61,40 @@ def test_kv_append_bit_exact(kv_heads, positions):
     assert np.array_equal(host_u16(pool_t), want)
 
 
+def test_kv_append_reports_bad_positions_and_pages():
+    """Four sequences: two good ones, one whose position lies past its
+    table (PKV_DEVERR_LENGTH) and one whose table entry lies outside the
+    pool (PKV_DEVERR_PAGE).  The bad ones write nothing, the good ones are
+    written exactly as the oracle's append, and the bits land in the error
+    word read by device_error."""
+    kv_heads, npages = 2, 12
+    pe = synth.page_elems(kv_heads)
+    pool = synth.random_pool(21, npages, pe)
+    bt = np.array([[3, 4], [5, 6], [7, 8], [9, npages + 40]], dtype=np.int32)
+    positions = np.array([17, 2, 32, 20], dtype=np.int32)  # seq 2: page 2 of a 2-page table
+    g = np.random.default_rng(22)
+    k = synth.to_bf16_bits(g.standard_normal((4, kv_heads * 64)).astype(np.float32))
+    v = synth.to_bf16_bits(g.standard_normal((4, kv_heads * 64)).astype(np.float32))
+    geo = oracle.PoolGeometry(kv_heads, 64)
+    want = pool.copy()
+    for b in (0, 1):
+        oracle.pool_append(want, geo, bt[b], int(positions[b]), k[b], v[b])
+    pool_t = dev(pool)
+    P = pkv.kv_pool_create(pool_t, kv_heads)
+    ws = pkv.alloc_workspace(256)
+    say("kv_append with a bad position and a bad page")
+    pkv.kv_append(P, dev(bt), dev(positions), dev(k), dev(v), dev_error=ws)
+    err = pkv.device_error(ws)
+    assert err == pkv.DEVERR_LENGTH | pkv.DEVERR_PAGE
+    assert np.array_equal(host_u16(pool_t), want)
+    assert pkv.device_error(ws) == 0  # read and cleared
+    # without an error word the same call still skips the bad sequences
+    pool_t2 = dev(pool)
+    pkv.kv_append(pkv.kv_pool_create(pool_t2, kv_heads), dev(bt), dev(positions), dev(k), dev(v))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(pool_t2), want)
+
+
 def test_attention_full_size_llama1b_heads_batch16():
     """Paged GQA attention, 32/8 heads, batch 16, lengths U[1,2048], 128 MiB pool."""
     w = synth.attention_workload()

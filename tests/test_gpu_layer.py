@@ -1,20 +1,27 @@
 """GPU parity of decoder_layer_decode and decode_step against the oracle,
-through the C ABI.  Bars: layer outputs max-abs <= 1e-2 * RMS(out); each
-appended K/V value within one BF16 ulp of the oracle's or within 1e-3 of the
-appended values' RMS, and the rest of the pool untouched; logits max-abs
-<= 1e-2 * RMS(logits); the argmax identical wherever the oracle's top-2
-logit gap exceeds 1e-3."""
+through the C ABI.  Bars: layer outputs max-abs <= 1e-2 * RMS(out), and
+the stricter bar on the layer's own contribution, max-abs <= 1e-3 *
+RMS(out - hidden) (the residual delta; without it the N(0,1) residual would
+hide a twenty-fold regression); each appended K/V value within one BF16 ulp
+of the oracle's or within 1e-3 of the appended values' RMS, and the rest of
+the pool untouched; logits max-abs <= 4e-4 for the full-size model (the
+budget under which no argmax with a top-2 gap above 1e-3 can flip) and
+<= 5e-3 * RMS(logits) for the small test models, whose weights are drawn
+2.5 times wider and whose norm gains vary 15 times more than the full-size
+models' to drive larger activations; the argmax identical wherever the
+oracle's top-2 logit gap exceeds 1e-3.  The full-size batch-16, batch-64
+and batch-128 steps are compared, every sequence, with stored oracle
+outputs in test_gpu_golden.py."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_util import (check_argmax_rule, check_pool_after, expected_pool_after, layer_gpu, say,
+from gpu_util import (DELTA_TOL, LAYER_TOL, LOGIT_ABS, TINY_LOGIT_REL, check_argmax_rule, check_pool_after, expected_pool_after, layer_gpu, say,
                       step_gpu)
 
 pytestmark = pytest.mark.gpu
 
-LAYER_TOL = 1e-2
 
 
 def _rms(a):
@@ -33,6 +40,7 @@ def _check_layer(shape, lw, hidden, wl, seqs=None):
     say("layer %s B=%d: max-abs %.3g, RMS(out) %.3g, error/RMS(delta) %.3g"
         % (shape.name, len(wl.positions), diff, _rms(ref[rows]), delta_err))
     assert diff <= LAYER_TOL * _rms(ref[rows])
+    assert delta_err <= DELTA_TOL
     want = expected_pool_after(wl.pool, geo, bt, wl.positions, k_new, v_new, seqs)
     if seqs is None:
         kv_diff, kv_rms = check_pool_after(pool_after, want, wl.pool)
@@ -94,7 +102,7 @@ def test_layer_tiled_split_qkv(head_dim):
     _check_layer(shape, lw, hidden, wl)
 
 
-def _check_step(shape, weights, wl, tokens, seqs=None, want_logits=True):
+def _check_step(shape, weights, wl, tokens, seqs=None, want_logits=True, logit_abs=None):
     geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
     logits, nxt, pool_after, err = step_gpu(shape, weights, wl.pool, wl.block_tables, wl.positions,
                                             tokens, want_logits, want_pool=False)
@@ -105,10 +113,17 @@ def _check_step(shape, weights, wl, tokens, seqs=None, want_logits=True):
     checked = check_argmax_rule(ref_logits[rows], nxt[rows])
     msg = "step %s B=%d rows=%s: argmax checked %d/%d" % (shape.name, len(tokens), rows, checked, len(rows))
     if logits is not None:
-        diff = np.abs(logits[rows] - ref_logits[rows]).max()
-        msg += ", max|dlogit| %.3g (RMS %.3g)" % (diff, _rms(ref_logits[rows]))
-        assert diff <= LAYER_TOL * _rms(ref_logits[rows])
-    say(msg)
+        per_row = np.abs(logits[rows] - ref_logits[rows]).max(axis=1)
+        diff = float(per_row.max())
+        worst = np.argsort(per_row)[::-1][:4]
+        msg += ", max|dlogit| %.3g (RMS %.3g), worst rows %s" % (
+            diff, _rms(ref_logits[rows]), ["%d@p%d:%.3g" % (rows[i], int(wl.positions[rows[i]]), per_row[i])
+                                          for i in worst])
+        bar = logit_abs if logit_abs is not None else TINY_LOGIT_REL * _rms(ref_logits[rows])
+        say(msg)
+        assert diff <= bar, "max|dlogit| %.3g > %.3g" % (diff, bar)
+    else:
+        say(msg)
     return nxt
 
 
@@ -147,22 +162,4 @@ def test_step_llama_shape_batch1():
     """16-layer Llama-3.2-1B-shaped step, batch 1, context 1024."""
     wl = synth.llama1b_step_b1()
     weights = synth.model_weights(wl.shape, 1003)
-    _check_step(wl.shape, weights, wl, wl.extra["tokens"])
-
-
-def test_step_llama_shape_batch64_sampled():
-    """Batch 64, context U[64,2048]; the oracle checks a sample of sequences."""
-    wl = synth.llama1b_step_b64()
-    weights = synth.model_weights(wl.shape, 1004)
-    order = np.argsort(wl.positions)
-    seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
-    _check_step(wl.shape, weights, wl, wl.extra["tokens"], seqs=seqs)
-
-
-def test_step_qwen_shape_batch128_long_context_sampled():
-    """24-layer Qwen2.5-0.5B-shaped step at batch 128, every sequence at 4096
-    cached tokens (257 pages of each of 24 layers, a 6 GiB pool of randomly
-    permuted 8 KiB pages); the oracle checks the first and last sequences."""
-    wl = synth.qwen05_step_b128()
-    weights = synth.model_weights(wl.shape, 1005)
-    _check_step(wl.shape, weights, wl, wl.extra["tokens"], seqs=[0, len(wl.positions) - 1])
+    _check_step(wl.shape, weights, wl, wl.extra["tokens"], logit_abs=LOGIT_ABS)

@@ -2,19 +2,19 @@
 C ABI.  Prefill's projections take their activations as BF16 hi + lo halves
 (~16 significant bits, as the decode projections do), so its bars are the
 decode path's:
-  * the last token's logits max-abs <= 1e-2 * RMS(logits), and the argmax
-    identical wherever the oracle's top-2 gap exceeds 1e-3;
-  * every layer-0 K/V value written within one BF16 ulp or 1e-3 * RMS of
-    the oracle's (its inputs are exact embedding rows); a later layer's
-    within one ulp plus 1e-2 * RMS (it inherits the hidden state's error,
-    held to the layer bar, including earlier prompt tokens' K/V rounded to
-    BF16 on the other side of a rounding boundary); every other pool byte
-    untouched;
+  * the last token's logits: max-abs <= 4e-4 for the full-size model,
+    <= 5e-3 * RMS(logits) for the small test models (gpu_util's bars), and
+    the argmax identical wherever the oracle's top-2 gap exceeds 1e-3;
+  * every layer's K/V of every prompt token within one BF16 ulp or 1e-3 *
+    RMS of the oracle's, the oracle being fed the GPU's own K/V of the
+    earlier positions (teacher forcing: a token's K/V at a later layer then
+    depend on earlier tokens only through values both sides share, so a
+    BF16 rounding that fell on the other neighbour in an earlier token
+    cannot spread); every other pool byte untouched;
   * placement, bitwise: the pool after prefill equals the original pool with
     the prefill's own K/V values written by kv_append at start_pos + t.
-At the Llama-1B shape and the 512-token prompt that bench.py times, sampled
-layer-0 K/V are checked against the oracle token by token, and the last
-logits against prefill of the first 511 tokens followed by a decode step."""
+The 512-token prompt that bench.py times is compared with stored oracle
+outputs in test_gpu_golden.py."""
 import numpy as np
 import pytest
 import torch
@@ -22,12 +22,11 @@ import torch
 import oracle
 import paged_kv_transformer_amd as pkv
 import synth
-from gpu_util import APPEND_REL, check_argmax_rule, check_prefill_pool, dev, device_pool, host_u16, say
+from gpu_util import assert_logits, check_argmax_rule, check_prefill_pool, dev, device_pool, host_u16, prompt_kv_bits, say
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-2
-PF_APPEND_REL = APPEND_REL
 
 
 def _rms(a):
@@ -58,14 +57,13 @@ def prefill_gpu(shape, weights, pool_np, bts, start, tokens, model=None, page_to
     return logits.cpu().numpy(), int(nxt.cpu()[0]), read_pool(), err
 
 
-def _oracle_check(shape, w, pool, bts, start, tokens, logits, nxt, pool_after, label):
+def _oracle_check(shape, w, pool, bts, start, tokens, logits, nxt, pool_after, label, full_size=False):
     geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
-    ref, ref_tok, ref_pool = oracle.prefill_paged(shape, w, pool, geo, bts, start, tokens)
-    diff = np.abs(logits - ref).max()
-    kv_err = check_prefill_pool(pool_after, ref_pool, pool, geo, bts, start, len(tokens), shape.layers)
-    say("prefill %s start %d T %d: max|dlogit| %.3g (RMS %.3g), max|dKV| per layer %s" % (
-        label, start, len(tokens), diff, _rms(ref), ["%.3g" % e for e in kv_err]))
-    assert diff <= TOL * _rms(ref)
+    ref, ref_tok, _ = oracle.prefill_paged(shape, w, pool, geo, bts, start, tokens)
+    kv_err = check_prefill_pool(pool_after, pool, geo, bts, start, tokens, shape, w)
+    say("prefill %s start %d T %d: teacher-forced max|dKV| per layer %s" % (
+        label, start, len(tokens), ["%.3g" % e for e in kv_err]))
+    assert_logits(logits, ref, "prefill %s start %d T %d" % (label, start, len(tokens)), full_size)
     check_argmax_rule(ref[None], np.array([nxt]))
 
 
@@ -121,9 +119,9 @@ def _prompt_kv(pool, geo, bts, start, T):
     per layer: [L][T][Hkv][D] each."""
     ks, vs = [], []
     for l in range(bts.shape[0]):
-        kc, vc = oracle.pool_gather(pool, geo, bts[l], start + T)
-        ks.append(oracle.f32_to_bf16(kc[start:]).reshape(T, geo.kv_heads, geo.head_dim))
-        vs.append(oracle.f32_to_bf16(vc[start:]).reshape(T, geo.kv_heads, geo.head_dim))
+        k, v = prompt_kv_bits(pool, geo, bts[l], start, T)
+        ks.append(k.reshape(T, geo.kv_heads, geo.head_dim))
+        vs.append(v.reshape(T, geo.kv_heads, geo.head_dim))
     return ks, vs
 
 
@@ -155,51 +153,4 @@ def test_prefill_llama_shape_4_tokens_after_1006():
     _, pool, bts, tokens = _inputs(shape, 1006, 1006, 4, weights=w)
     logits, nxt, pool_after, err = prefill_gpu(shape, w, pool, bts, 1006, tokens)
     assert err == 0
-    _oracle_check(shape, w, pool, bts, 1006, tokens, logits, nxt, pool_after, "llama")
-
-
-def test_prefill_llama_512_sampled_kv_and_decode_consistency():
-    """The prefill bench.py times: Llama-1B shape, 512 tokens from position 0,
-    its weights, prompt and pool.  Layer-0 K/V of sampled tokens against the
-    oracle (they depend on the token alone); the last logits against prefill
-    of the first 511 tokens followed by a decode step of the last one."""
-    shape = synth.LLAMA1B
-    T = 512
-    w = synth.model_weights(shape, 1002)
-    wl = synth.decode_workload("prefill", shape, 1007, [T - 1])
-    pool, bts = wl.pool, np.ascontiguousarray(wl.block_tables[:, 0])
-    tokens = synth.rng(1007, "prompt").integers(0, shape.vocab, size=T).astype(np.int32)
-    model = pkv.upload_model(w, shape.theta, T, head_dim=shape.head_dim)
-    logits, nxt, pool_a, err = prefill_gpu(shape, w, pool, bts, 0, tokens, model)
-    assert err == 0
-    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
-    ks, vs = _prompt_kv(pool_a, geo, bts[:1], 0, T)
-    got, want = [], []
-    for t in (0, 1, 15, 16, 200, 383, 511):
-        x = oracle.embed(w["embed"], int(tokens[t]))
-        zero = np.zeros((t + 1, shape.kv_heads * shape.head_dim), np.float32)
-        _, kb, vb = oracle.layer_decode(shape, w["layers"][0], x, zero, zero.copy(), t)
-        want += [oracle.bf16_to_f32(kb).ravel(), oracle.bf16_to_f32(vb).ravel()]
-        got += [oracle.bf16_to_f32(ks[0][t]).ravel(), oracle.bf16_to_f32(vs[0][t]).ravel()]
-    g, r = np.concatenate(got).astype(np.float64), np.concatenate(want).astype(np.float64)
-    bound = np.maximum(np.abs(r) * 2.0 ** -7, PF_APPEND_REL * _rms(r))
-    say("prefill llama 512: sampled layer-0 K/V max|d| %.3g (RMS %.3g)" % (np.abs(g - r).max(), _rms(r)))
-    assert (np.abs(g - r) <= bound).all()
-
-    # prefill of 511 tokens, then the last token as a decode step
-    _, _, pool_b, err = prefill_gpu(shape, w, pool, bts, 0, tokens[:T - 1], model)
-    assert err == 0
-    cfg = pkv.make_config(shape, max_pos=T)
-    pool_t = dev(pool_b)
-    kpool = pkv.kv_pool_create(pool_t, shape.kv_heads, head_dim=shape.head_dim)
-    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, 1, bts.shape[1]))
-    ref = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
-    nref = torch.empty(1, dtype=torch.int32, device="cuda")
-    pkv.decode_step(cfg, model, kpool, dev(np.ascontiguousarray(bts[:, None, :])),
-                    dev(np.array([T - 1], np.int32)), dev(tokens[T - 1:]), ref, nref, ws)
-    assert pkv.device_error(ws) == 0
-    ref = ref.cpu().numpy()[0]
-    diff = np.abs(logits - ref).max()
-    say("prefill llama 512 vs prefill 511 + decode: max|dlogit| %.3g (RMS %.3g)" % (diff, _rms(ref)))
-    assert diff <= TOL * _rms(ref)
-    check_argmax_rule(ref[None], np.array([nxt]))
+    _oracle_check(shape, w, pool, bts, 1006, tokens, logits, nxt, pool_after, "llama", full_size=True)
