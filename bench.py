@@ -780,6 +780,8 @@ def main():
                     help="time the page-geometry variants and the head-width-128 layer alone")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the prefill alone (the step's model, no decode workload)")
+    ap.add_argument("--qwen-layer-only", action="store_true",
+                    help="time the qwen2.5-0.5b-shape batch-1 layer chain alone (for profiling)")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, out_path=args.traffic_out)
@@ -797,7 +799,7 @@ def main():
     import synth
 
     if (args.attention_only or args.prefill_only or args.large_batch_only or args.variants_only
-            or args.step_counters):
+            or args.step_counters or args.qwen_layer_only):
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(2)
@@ -808,6 +810,11 @@ def main():
             step_counters(torch, pkv, synth)
         elif args.prefill_only:
             prefill_only(torch, pkv, synth, args.prefill_tokens)
+        elif args.qwen_layer_only:
+            lq_ms, lq_bytes = time_layer_qwen05_b1(torch, pkv, synth)
+            lq_us = float(np.median(lq_ms)) * 1e3
+            print(json.dumps({"layer_qwen05_b1_us": round(lq_us, 3), "algorithmic_bytes": int(lq_bytes),
+                              "achieved_gbs": round(lq_bytes / (lq_us * 1e3), 1)}), flush=True)
         elif args.variants_only:
             print(json.dumps({"page_geometry": page_geometries(torch, pkv, synth),
                               "layer_llama8b": time_layer_llama8b(torch, pkv, synth)}))

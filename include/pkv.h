@@ -3,16 +3,18 @@
  *
  * The library computes the batched decode step of a Llama/Qwen-style
  * grouped-query-attention decoder over one shared BF16 KV page pool, as the
- * "Inference from Scratch" engine summary describes it (wpnews page "Hours
- * of YouTube and 85 handtyped pages of notes on LLM Inference"): a shared
- * BF16 page pool with 16 tokens of K and V per physical page and a block
- * table per sequence and layer; decode appends each new token at its
- * absolute RoPE position; direct paged decode attention with FP32 online
- * softmax that streams each sequence's pages without gathering a contiguous
- * prefix or storing scores; batched decode packing one token per active
- * sequence; final RMSNorm, tied embedding / LM head to FP32 logits and GPU
- * argmax.  The configuration fields are those of llmc's binary header
- * (README of llmc, section "binary format v2", config header).
+ * "Inference from Scratch" engine summary describes it (page "Hours of
+ * YouTube and 85 handtyped pages of notes on LLM Inference", its feature
+ * bullets on the page pool, paged attention, batched decode and the final
+ * norm): pages of 16 tokens of BF16 K and V, one block table per sequence
+ * and layer; each decode step writes the new token's K and V at its
+ * absolute RoPE position; attention reads the cached pages in place through
+ * the block table, keeping the softmax running in FP32, so neither a copied
+ * contiguous cache nor a score matrix ever exists; every active sequence
+ * contributes one token to a step; a final RMSNorm and the tied embedding
+ * matrix give FP32 logits, whose argmax is taken on the GPU.  The
+ * configuration fields are those of llmc's binary header (README of llmc,
+ * section "binary format v2", config header).
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).  BF16 data are
@@ -175,20 +177,24 @@ int kv_pool_create_split(void *k_base, void *v_base, int64_t bytes,
  *   k_new, v_new [batch][Hkv][D] BF16.
  * Sequence b writes slot positions[b] % PT of physical page
  * block_table[b][positions[b] / PT].  Bit-exact copy of the given values.
- * batch == 0 is a no-op.  Errors: -EINVAL, -ENOTSUP, -EIO.  This call takes
- * no workspace, so a sequence whose position or table entry is out of
- * range is skipped without a device-error report.
+ * A sequence whose position is negative or past the table
+ * (PKV_DEVERR_LENGTH) or whose table entry lies outside [0, num_pages)
+ * (PKV_DEVERR_PAGE) writes nothing; the bit is ORed into *dev_error, a
+ * device word the caller owns (for instance the first word of a workspace,
+ * read and cleared with pkv_device_error), or dropped if dev_error is NULL.
+ * batch == 0 is a no-op.  Errors: -EINVAL, -ENOTSUP, -EIO.
  */
 int kv_append(const pkv_pool *pool, const int32_t *block_table,
 	      int32_t max_pages, const int32_t *positions,
 	      const uint16_t *k_new, const uint16_t *v_new, int32_t batch,
-	      void *stream);
+	      uint32_t *dev_error, void *stream);
 
 /*
- * paged_gqa_decode — direct paged decode attention with FP32 online softmax
- * (the engine's "direct paged decode attention": each query head streams
- * its sequence's cached pages and accumulates weighted values without
- * gathering a contiguous prefix or storing attention scores).
+ * paged_gqa_decode — decode attention read straight from the pages, with an
+ * FP32 online softmax ("Inference from Scratch" summary, paged-attention
+ * bullet: the kernel walks a sequence's block table and folds every cached
+ * token into a running maximum, normaliser and weighted sum of V, so the
+ * pages are never copied into one buffer and no score is written out).
  *   q [batch][num_q_heads][D] BF16, context_lens [batch] int32 (tokens
  *   0..n-1 are attended), out [batch][num_q_heads][D] FP32.
  * Query head h reads kv head h / (num_q_heads / Hkv).  For every head:

@@ -75,7 +75,7 @@ def lib():
         sigs = {
             "kv_pool_create": (ctypes.c_int, [P, I64, I32, I32, I32, PP]),
             "kv_pool_create_split": (ctypes.c_int, [P, P, I64, I32, I32, I32, PP]),
-            "kv_append": (ctypes.c_int, [PP, P, I32, P, P, P, I32, P]),
+            "kv_append": (ctypes.c_int, [PP, P, I32, P, P, P, I32, P, P]),
             "paged_gqa_decode": (ctypes.c_int, [PP, P, I32, P, I32, P, I32, F, P, P, SZ, P]),
             "decoder_layer_decode": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(LayerWeights),
                                                     P, P, PP, P, I32, P, I32, P, P, SZ, P]),
@@ -221,15 +221,22 @@ def kv_pool_create_split(k_tensor, v_tensor, num_kv_heads, head_dim=HEAD_DIM,
     return out
 
 
-def kv_append(pool, block_table, positions, k_new, v_new, stream=None):
+def kv_append(pool, block_table, positions, k_new, v_new, stream=None, dev_error=None):
+    """dev_error: None, or a device tensor (a workspace from
+    alloc_workspace, read with device_error) whose first 32-bit word takes
+    the PKV_DEVERR_* bits of sequences that could not be written."""
     B = positions.numel()
     _table(block_table, B, "block_table")
     _at_least(k_new, B * pool.num_kv_heads * pool.head_dim, "k_new")
     _at_least(v_new, B * pool.num_kv_heads * pool.head_dim, "v_new")
     bt = _dev(block_table, (torch.int32,), "block_table")
+    err = None
+    if dev_error is not None:
+        _bytes_at_least(dev_error, 4, "dev_error")
+        err = _dev(dev_error, (torch.uint8, torch.int32), "dev_error")
     _check("kv_append", lib().kv_append(
         ctypes.byref(pool), bt, block_table.shape[-1], _dev(positions, (torch.int32,), "positions"),
-        _dev(k_new, _BF16_DTYPES, "k_new"), _dev(v_new, _BF16_DTYPES, "v_new"), B, _stream(stream)))
+        _dev(k_new, _BF16_DTYPES, "k_new"), _dev(v_new, _BF16_DTYPES, "v_new"), B, err, _stream(stream)))
 
 
 # ------------------------------------------------------------- workspace ---

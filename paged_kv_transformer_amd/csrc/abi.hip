@@ -450,6 +450,42 @@ int run_layer_tiled(const pkv_config* cfg, const pkv_layer_weights* w, const flo
 
 }  // namespace
 
+namespace pkv {
+
+int prepare_attention_call(const pkv_pool* pool, const uint16_t* q, int32_t num_q_heads,
+                           const int32_t* block_table, int32_t max_pages, const int32_t* context_lens,
+                           int32_t batch, float scale, float* out, AttnArgs* args) {
+  int rc = check_pool(pool);
+  if (rc) return rc;
+  rc = check_heads(num_q_heads, pool->num_kv_heads);
+  if (rc) return rc;
+  if (batch < 0 || max_pages < 1) return -EINVAL;
+  const int64_t tiles = table_tiles(max_pages, pool->page_tokens);
+  if (batch > 65535 || attn_max_splits(tiles) > 65535) return -ENOTSUP;
+  if (batch == 0) return 0;
+  if (!q || !block_table || !context_lens || !out || !isfinite(scale)) return -EINVAL;
+  AttnArgs a{};
+  a.q = q;
+  a.pv = pool_view(pool);
+  a.bt = block_table;
+  a.bt_stride = max_pages;
+  a.bt_row = max_pages;
+  a.lens = context_lens;
+  a.len_add = 0;
+  a.scale = scale;
+  a.out = out;
+  a.Hq = num_q_heads;
+  a.Hkv = pool->num_kv_heads;
+  a.G = num_q_heads / pool->num_kv_heads;
+  a.pw = attn_pw(batch, a.Hkv, tiles);
+  a.max_splits = attn_max_splits(tiles, a.pw);
+  a.D = pool->head_dim;
+  *args = a;
+  return 0;
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
@@ -498,14 +534,16 @@ int kv_pool_create_split(void* k_base, void* v_base, int64_t bytes, int32_t num_
 
 int kv_append(const pkv_pool* pool, const int32_t* block_table, int32_t max_pages,
               const int32_t* positions, const uint16_t* k_new, const uint16_t* v_new,
-              int32_t batch, void* stream) {
+              int32_t batch, uint32_t* dev_error, void* stream) {
   int rc = check_pool(pool);
   if (rc) return rc;
   if (batch < 0 || max_pages < 1) return -EINVAL;
   if (batch == 0) return 0;
   if (!block_table || !positions || !k_new || !v_new) return -EINVAL;
+  if (!aligned(dev_error, 4)) return -EINVAL;
   return io(launch_kv_append(pool_view(pool), block_table, max_pages, positions, k_new, v_new,
-                             batch, pool->num_kv_heads, pool->head_dim, (hipStream_t)stream));
+                             batch, pool->num_kv_heads, pool->head_dim, dev_error,
+                             (hipStream_t)stream));
 }
 
 size_t pkv_attention_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -528,37 +566,17 @@ int paged_gqa_decode(const pkv_pool* pool, const uint16_t* q, int32_t num_q_head
                      const int32_t* block_table, int32_t max_pages, const int32_t* context_lens,
                      int32_t batch, float scale, float* out, void* workspace, size_t ws_bytes,
                      void* stream) {
-  int rc = check_pool(pool);
-  if (rc) return rc;
-  rc = check_heads(num_q_heads, pool->num_kv_heads);
-  if (rc) return rc;
-  if (batch < 0 || max_pages < 1) return -EINVAL;
-  const int64_t tiles = table_tiles(max_pages, pool->page_tokens);
-  if (batch > 65535 || attn_max_splits(tiles) > 65535) return -ENOTSUP;
-  if (batch == 0) return 0;
-  if (!q || !block_table || !context_lens || !out || !workspace) return -EINVAL;
-  if (!aligned(workspace, 256) || !isfinite(scale)) return -EINVAL;
-  const WsLayout L =
-      ws_layout(batch, 0, num_q_heads, pool->num_kv_heads, 0, 0, tiles, false, pool->head_dim);
-  if (ws_bytes < L.total) return -ENOSPC;
   AttnArgs a{};
-  a.q = q;
-  a.pv = pool_view(pool);
-  a.bt = block_table;
-  a.bt_stride = max_pages;
-  a.bt_row = max_pages;
-  a.lens = context_lens;
-  a.len_add = 0;
-  a.scale = scale;
-  a.out = out;
+  int rc = prepare_attention_call(pool, q, num_q_heads, block_table, max_pages, context_lens, batch,
+                                  scale, out, &a);
+  if (rc || batch == 0) return rc;
+  if (!workspace) return -EINVAL;
+  if (!aligned(workspace, 256)) return -EINVAL;
+  const WsLayout L = ws_layout(batch, 0, num_q_heads, pool->num_kv_heads, 0, 0,
+                               table_tiles(max_pages, pool->page_tokens), false, pool->head_dim);
+  if (ws_bytes < L.total) return -ENOSPC;
   a.part = at<float>(workspace, L.attn_part);
   a.err = at<uint32_t>(workspace, L.err);
-  a.Hq = num_q_heads;
-  a.Hkv = pool->num_kv_heads;
-  a.G = num_q_heads / pool->num_kv_heads;
-  a.pw = attn_pw(batch, a.Hkv, table_tiles(max_pages, pool->page_tokens));
-    a.max_splits = attn_max_splits(table_tiles(max_pages, pool->page_tokens), a.pw);
-  a.D = pool->head_dim;
   return io(launch_attention(a, batch, kQBf16, (hipStream_t)stream));
 }
 

@@ -1,9 +1,10 @@
 // Direct paged GQA decode attention with FP32 online softmax, gfx950.
 //
-// The operation is the "Inference from Scratch" engine's direct paged
-// decode attention: every query head walks its sequence's pages through
-// the block table and accumulates softmax-weighted values without gathering
-// a contiguous prefix or storing scores.  Here one workgroup takes one
+// The operation is the paged decode attention of the "Inference from
+// Scratch" engine summary (its paged-attention bullet): the cached tokens
+// are read where the block table says they are, folded into a running
+// softmax, and no copy of the prefix or of the scores is ever made.  Here
+// one workgroup takes one
 // (sequence, kv head, split of 8 16-token tiles); its 4 waves take 2 tiles
 // each.  Calls of many sequences (at least kAttnLargeWgs such workgroups)
 // take 4 tiles per wave and 16 per split instead: half the workgroups and

@@ -8,16 +8,24 @@ namespace {
 // One workgroup per sequence: copy the new token's K ([Hkv][D], into the
 // K block at [head][slot][d]) and V (into the V block at [head][d][slot]).
 // The engine's decode appends one token per sequence at its absolute
-// position: logical page pos / 16, slot pos % 16.
+// position: logical page pos / 16, slot pos % 16.  A position outside the
+// table or a table entry outside the pool writes nothing and sets its bit
+// in the caller's error word (if any); the workgroup then exits.
 __global__ void kv_append_kernel(const PoolView pv, const int32_t* bt, int32_t bt_stride,
                                  const int32_t* pos, const uint16_t* k, const uint16_t* v, int Hkv,
-                                 int D) {
+                                 int D, uint32_t* err) {
   const int b = blockIdx.x;
   const int p = pos[b];
   const int psh = 4 + pv.pt_shift;  // log2 of the page's tokens
-  if (p < 0 || (p >> psh) >= bt_stride) return;
+  if (p < 0 || (p >> psh) >= bt_stride) {
+    if (err && threadIdx.x == 0) set_error(err, ERR_LENGTH);
+    return;
+  }
   const int page = bt[(size_t)b * bt_stride + (p >> psh)];
-  if ((unsigned)page >= (unsigned)pv.num_pages) return;
+  if ((unsigned)page >= (unsigned)pv.num_pages) {
+    if (err && threadIdx.x == 0) set_error(err, ERR_PAGE);
+    return;
+  }
   const int slot = p & ((1 << psh) - 1);
   const uint16_t* kb = k + (size_t)b * Hkv * D;
   const uint16_t* vb = v + (size_t)b * Hkv * D;
@@ -99,8 +107,8 @@ __global__ void fill_zero_kernel(uint4* p, size_t n16, unsigned char* tail, size
 
 hipError_t launch_kv_append(const PoolView& pv, const int32_t* bt, int32_t bt_stride,
                             const int32_t* pos, const uint16_t* k, const uint16_t* v, int batch,
-                            int Hkv, int D, hipStream_t st) {
-  kv_append_kernel<<<batch, 256, 0, st>>>(pv, bt, bt_stride, pos, k, v, Hkv, D);
+                            int Hkv, int D, uint32_t* err, hipStream_t st) {
+  kv_append_kernel<<<batch, 256, 0, st>>>(pv, bt, bt_stride, pos, k, v, Hkv, D, err);
   return hipGetLastError();
 }
 

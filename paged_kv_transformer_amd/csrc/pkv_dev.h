@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct pkv_pool;
+
 namespace pkv {
 
 constexpr int kPageTokens = 16;   // the default page size; 256 is also supported
@@ -470,10 +472,15 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int64_t m
 constexpr int kQBf16 = 0;   // BF16 q, the matrix operand as it is
 constexpr int kQSplit = 1;  // an FP32 q stored as BF16 hi and lo halves
 hipError_t launch_attention(const AttnArgs& a, int batch, int qmode, hipStream_t st);
+// Bytes of split records an attention call with these arguments writes
+// (0 when every sequence fits one split).
+inline size_t attention_record_bytes(const AttnArgs& a, int batch) {
+  return a.max_splits > 1 ? sizeof(float) * (size_t)batch * a.Hkv * a.max_splits * attn_rec(a.D) : 0;
+}
 hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_t st);
 hipError_t launch_kv_append(const PoolView& pv, const int32_t* bt, int32_t bt_stride,
                             const int32_t* pos, const uint16_t* k, const uint16_t* v, int batch,
-                            int Hkv, int D, hipStream_t st);
+                            int Hkv, int D, uint32_t* err, hipStream_t st);
 hipError_t launch_embed(const uint16_t* E_packed, int V, int H, const int32_t* tok, float* x,
                         float* x_packed, int batch, uint32_t* err, hipStream_t st);
 hipError_t launch_pack_weight(const uint16_t* src, int rows, int cols, int kind, uint16_t* dst,
@@ -496,5 +503,13 @@ hipError_t launch_qkv_finish(const float* part, int ks, const PgemmArgs& a, hipS
 hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int N,
                                 const uint16_t* nw, float eps, uint16_t* xb, hipStream_t st);
 hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st);
+
+// Host: validation of a paged_gqa_decode call's arguments other than its
+// scratch, and its kernel arguments except `part` and `err`.  Returns 0 or a
+// negative errno (the entry point's contract); batch 0 returns 0 with *args
+// untouched.
+int prepare_attention_call(const pkv_pool* pool, const uint16_t* q, int32_t num_q_heads,
+                           const int32_t* block_table, int32_t max_pages, const int32_t* context_lens,
+                           int32_t batch, float scale, float* out, AttnArgs* args);
 
 }  // namespace pkv
