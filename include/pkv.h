@@ -215,6 +215,31 @@ int paged_gqa_decode(const pkv_pool *pool, const uint16_t *q,
 		     size_t ws_bytes, void *stream);
 
 /*
+ * paged_gqa_decode_noalloc — paged_gqa_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * paged_gqa_decode, without the workspace: the split records live in a
+ * fixed device array of PKV_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends, and the device-error bits
+ * (PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH) are ORed into *dev_error, a 4-byte
+ * device word the caller owns and clears.  The call allocates nothing and
+ * frees nothing.  All calls on one GPU share its array: calls that overlap
+ * on one GPU (other streams, other threads) race and must not be issued.
+ * Errors: as paged_gqa_decode, with -EINVAL for a NULL or misaligned
+ * dev_error and -ENOSPC when the call's split records would exceed the array
+ * (batch * Hkv * splits * (32 + 16 * D) * 4 bytes, splits = the table's
+ * 16-token tiles / 8, or / 16 from 4096 workgroups; e.g. 16 sequences of 8
+ * kv heads of width 64 over 2048-token tables take 8.65 MB); -EIO if the
+ * array's device address cannot be found.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int paged_gqa_decode_noalloc(const pkv_pool *pool, const uint16_t *q,
+			     int32_t num_q_heads, const int32_t *block_table,
+			     int32_t max_pages, const int32_t *context_lens,
+			     int32_t batch, float scale, float *out,
+			     uint32_t *dev_error, void *stream);
+
+/*
  * decoder_layer_decode — one decoder layer for a batch of sequences, each
  * with one new token at positions[b] (tokens 0..positions[b]-1 already in
  * the pool).  In order (the engine's layer op list):

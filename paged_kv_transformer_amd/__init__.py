@@ -77,6 +77,7 @@ def lib():
             "kv_pool_create_split": (ctypes.c_int, [P, P, I64, I32, I32, I32, PP]),
             "kv_append": (ctypes.c_int, [PP, P, I32, P, P, P, I32, P, P]),
             "paged_gqa_decode": (ctypes.c_int, [PP, P, I32, P, I32, P, I32, F, P, P, SZ, P]),
+            "paged_gqa_decode_noalloc": (ctypes.c_int, [PP, P, I32, P, I32, P, I32, F, P, P, P]),
             "decoder_layer_decode": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(LayerWeights),
                                                     P, P, PP, P, I32, P, I32, P, P, SZ, P]),
             "decode_step": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.POINTER(ModelWeights), PP, P,
@@ -315,6 +316,30 @@ def paged_gqa_decode(pool, q, block_table, context_lens, scale, out, workspace, 
         _dev(context_lens, (torch.int32,), "context_lens"), B, scale,
         _dev(out, (torch.float32,), "out"), _dev(workspace, (torch.uint8,), "workspace"),
         workspace.numel(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def paged_gqa_decode_noalloc(pool, q, block_table, context_lens, scale, out, dev_error, stream=None):
+    """paged_gqa_decode without a workspace: the library's own per-GPU
+    scratch array holds the split records (calls that overlap on one GPU
+    race on it); dev_error is a device tensor of at least 4 bytes whose first
+    32-bit word takes the PKV_DEVERR_* bits (a workspace from
+    alloc_workspace, read and cleared with device_error, will do)."""
+    if q.dim() != 3 or q.shape[2] != pool.head_dim:
+        raise ValueError("q must be [B, Hq, %d], got %s" % (pool.head_dim, tuple(q.shape)))
+    B, Hq = q.shape[0], q.shape[1]
+    _table(block_table, B, "block_table")
+    _at_least(context_lens, B, "context_lens")
+    _at_least(out, B * Hq * pool.head_dim, "out")
+    _bytes_at_least(dev_error, 4, "dev_error")
+    _check("paged_gqa_decode_noalloc", lib().paged_gqa_decode_noalloc(
+        ctypes.byref(pool), _dev(q, _BF16_DTYPES, "q"), Hq,
+        _dev(block_table, (torch.int32,), "block_table"), block_table.shape[-1],
+        _dev(context_lens, (torch.int32,), "context_lens"), B, scale,
+        _dev(out, (torch.float32,), "out"), _dev(dev_error, (torch.uint8, torch.int32), "dev_error"),
+        _stream(stream)))
 
 
 # ---------------------------------------------------------------- layers ---

@@ -111,6 +111,30 @@ def test_paged_gqa_decode_validation():
     assert L.paged_gqa_decode(*args(pool=bad)) == ENOTSUP
 
 
+def test_paged_gqa_decode_noalloc_validation():
+    """The allocation-free variant validates like paged_gqa_decode, needs
+    an error word, and refuses calls whose split records exceed its fixed
+    scratch array, all before any HIP call."""
+    p = _pool(pages=4096)
+    args = lambda **kw: [ctypes.byref(kw.get("pool", p)), kw.get("q", FAKE), kw.get("hq", 32),
+                         kw.get("bt", FAKE), kw.get("mp", 128), kw.get("lens", FAKE), kw.get("b", 16),
+                         kw.get("scale", 0.125), kw.get("out", FAKE), kw.get("err", FAKE), None]
+    f = L.paged_gqa_decode_noalloc
+    assert f(*args(q=None)) == EINVAL
+    assert f(*args(err=None)) == EINVAL
+    assert f(*args(err=FAKE + 2)) == EINVAL
+    assert f(*args(hq=30)) == EINVAL
+    assert f(*args(hq=8 * 17)) == ENOTSUP
+    assert f(*args(b=65536)) == ENOTSUP
+    assert f(*args(scale=float("inf"))) == EINVAL
+    assert f(*args(b=0)) == 0
+    # 64 sequences x 8 kv heads over 2048-token tables: 8 splits of
+    # 4224-byte records = 17.3 MB > PKV_NOALLOC_SCRATCH_BYTES (16 MiB)
+    assert pkv.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert f(*args(b=64)) == ENOSPC
+    assert f(*args(b=64, mp=8192)) == ENOSPC
+
+
 def _cfg(**kw):
     c = pkv.Config(2048, 16, 32, 8, 64, 8192, 128256, 4096, 5e5, 1e-5)
     for k, v in kw.items():
