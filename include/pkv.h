@@ -421,6 +421,34 @@ int pkv_rope_table(float theta, int32_t head_dim, int32_t max_pos,
  */
 int pkv_device_error(void *workspace, void *stream);
 
+/*
+ * Measurement helpers: kernels that do none of the method's arithmetic, so
+ * that the path's kernels can be read against what the memory system and
+ * the launch path give on the same GPU.  None of them writes memory (sink
+ * is a device float the kernels never store to in practice; it only keeps
+ * the loads alive).
+ *   pkv_probe_read        one launch that streams `bytes` bytes at buf
+ *                         (16-byte aligned, a multiple of 16) once with
+ *                         16-byte non-temporal loads over `workgroups`
+ *                         workgroups of 256 threads: the practical read
+ *                         ceiling of a launch of that size.
+ *   pkv_probe_paged_read  one launch with paged_gqa_decode's grid that
+ *                         issues exactly that call's K and V loads for the
+ *                         same pool, table and lengths, and no arithmetic:
+ *                         the ceiling of the call's data phase.
+ *   pkv_probe_empty       `launches` empty kernels of `workgroups` one-wave
+ *                         workgroups: the cost of a launch.
+ * Errors: -EINVAL for NULL, misaligned or out-of-range arguments (the paged
+ * probe validates as paged_gqa_decode), -EIO.
+ */
+int pkv_probe_read(const void *buf, int64_t bytes, int32_t workgroups,
+		   float *sink, void *stream);
+int pkv_probe_paged_read(const pkv_pool *pool, int32_t num_q_heads,
+			 const int32_t *block_table, int32_t max_pages,
+			 const int32_t *context_lens, int32_t batch,
+			 float *sink, void *stream);
+int pkv_probe_empty(int32_t launches, int32_t workgroups, void *stream);
+
 /* Library version string (host). */
 const char *pkv_version(void);
 

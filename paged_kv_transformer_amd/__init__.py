@@ -94,6 +94,9 @@ def lib():
             "pkv_packed_weight_bytes": (SZ, [I32, I32, I32]),
             "pkv_pack_weight": (ctypes.c_int, [P, I32, I32, I32, P, P]),
             "pkv_device_error": (ctypes.c_int, [P, P]),
+            "pkv_probe_read": (ctypes.c_int, [P, I64, I32, P, P]),
+            "pkv_probe_paged_read": (ctypes.c_int, [PP, I32, P, I32, P, I32, P, P]),
+            "pkv_probe_empty": (ctypes.c_int, [I32, I32, P]),
             "pkv_version": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sigs.items():
@@ -267,6 +270,29 @@ def workspace_init(ws, stream=None):
 def device_error(ws, stream=None):
     return _check("pkv_device_error", lib().pkv_device_error(
         _dev(ws, (torch.uint8,), "workspace"), _stream(stream)))
+
+
+def probe_read(buf, sink, workgroups=1024, nbytes=None, stream=None):
+    """Stream nbytes (default: all) of the device tensor buf once (a
+    measurement kernel: no arithmetic, no stores)."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check("pkv_probe_read", lib().pkv_probe_read(buf.data_ptr(), n, workgroups,
+                                                  _dev(sink, (torch.float32,), "sink"), _stream(stream)))
+
+
+def probe_paged_read(pool, num_q_heads, block_table, context_lens, sink, stream=None):
+    """The K/V loads of one paged_gqa_decode call, without its arithmetic."""
+    B = context_lens.numel()
+    _table(block_table, B, "block_table")
+    _check("pkv_probe_paged_read", lib().pkv_probe_paged_read(
+        ctypes.byref(pool), num_q_heads, _dev(block_table, (torch.int32,), "block_table"),
+        block_table.shape[-1], _dev(context_lens, (torch.int32,), "context_lens"), B,
+        _dev(sink, (torch.float32,), "sink"), _stream(stream)))
+
+
+def probe_empty(launches, workgroups=1, stream=None):
+    """`launches` empty kernels (the cost of a launch)."""
+    _check("pkv_probe_empty", lib().pkv_probe_empty(launches, workgroups, _stream(stream)))
 
 
 def rope_table(theta, max_pos, head_dim=HEAD_DIM, device="cuda", stream=None):

@@ -938,6 +938,28 @@ int pkv_rope_table(float theta, int32_t head_dim, int32_t max_pos, float* cos_ou
                               (hipStream_t)stream));
 }
 
+int pkv_probe_read(const void* buf, int64_t bytes, int32_t workgroups, float* sink, void* stream) {
+  if (!buf || !sink || !aligned(buf, 16) || bytes < 16 || bytes % 16 != 0) return -EINVAL;
+  if (workgroups < 1 || workgroups > 1 << 20) return -EINVAL;
+  return io(launch_probe_read(buf, bytes, workgroups, sink, (hipStream_t)stream));
+}
+
+int pkv_probe_paged_read(const pkv_pool* pool, int32_t num_q_heads, const int32_t* block_table,
+                         int32_t max_pages, const int32_t* context_lens, int32_t batch, float* sink,
+                         void* stream) {
+  AttnArgs a{};
+  const uint16_t* any = (const uint16_t*)sink;  // q and out are not read or written
+  int rc = prepare_attention_call(pool, any, num_q_heads, block_table, max_pages, context_lens, batch,
+                                  1.0f, sink, &a);
+  if (rc || batch == 0) return rc;
+  return io(launch_probe_paged_read(a, batch, sink, (hipStream_t)stream));
+}
+
+int pkv_probe_empty(int32_t launches, int32_t workgroups, void* stream) {
+  if (launches < 0 || workgroups < 1 || workgroups > 1 << 20) return -EINVAL;
+  return io(launch_probe_empty(launches, workgroups, (hipStream_t)stream));
+}
+
 int pkv_device_error(void* workspace, void* stream) {
   if (!workspace || !aligned(workspace, 256)) return -EINVAL;
   const hipStream_t st = (hipStream_t)stream;

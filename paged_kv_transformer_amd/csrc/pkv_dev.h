@@ -504,6 +504,12 @@ hipError_t launch_prefill_resid(float* x, const float* part, int ks, int T, int 
                                 const uint16_t* nw, float eps, uint16_t* xb, hipStream_t st);
 hipError_t launch_prefill_attention(const PattnArgs& a, hipStream_t st);
 
+// Measurement kernels (probe.hip): a streaming read of `bytes`, the K/V
+// loads of one attention call without its arithmetic, and empty launches.
+hipError_t launch_probe_read(const void* buf, int64_t bytes, int workgroups, float* sink, hipStream_t st);
+hipError_t launch_probe_paged_read(const AttnArgs& a, int batch, float* sink, hipStream_t st);
+hipError_t launch_probe_empty(int launches, int workgroups, hipStream_t st);
+
 // Host: validation of a paged_gqa_decode call's arguments other than its
 // scratch, and its kernel arguments except `part` and `err`.  Returns 0 or a
 // negative errno (the entry point's contract); batch 0 returns 0 with *args
