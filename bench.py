@@ -872,6 +872,25 @@ def step_counters(torch, pkv, synth, steps=3):
           flush=True)
 
 
+def decode_only(torch, pkv, synth, args):
+    """The batch-16 step, the attention call and the two batch-1 layers,
+    each from a HIP graph (a quick line for tuning and profiling)."""
+    S = Setup(torch, pkv, synth, HostInputs(synth))
+    graph = capture(torch, lambda st: pkv.decode_step(S.cfg, S.model, S.pool, S.bts, S.pos, S.tokens, S.logits,
+                                                      S.next, S.ws, st))
+    for _ in range(20):
+        graph.replay()
+    step = float(np.median(timed_replays(torch, graph.replay, 100)))
+    attn_ms, _ = time_attention(torch, pkv, synth, S, args.attn_rounds)
+    l_ms, _ = time_layer_b1(torch, pkv, synth, S)
+    lq_ms, _, _, lq_n = time_layer_qwen05_b1(torch, pkv, synth)
+    out = {"step_b16_ms": round(step, 4), "attention_us": round(attn_ms * 1e3, 3),
+           "layer_llama1b_b1_us": round(l_ms * 1e3, 3), "layer_qwen05_b1_us": round(float(np.median(lq_ms)) * 1e3, 3),
+           "qwen_launches_per_layer": lq_n}
+    assert pkv.device_error(S.ws) == 0
+    print(json.dumps(out), flush=True)
+
+
 def counter_table(fetch_csv, write_csv):
     """Every library kernel's FETCH_SIZE and WRITE_SIZE per dispatch, each
     scaled by what the counter reads for the calibration copy, as a
@@ -967,6 +986,8 @@ def main():
                     help="time the prefill alone (the step's model, no decode workload)")
     ap.add_argument("--qwen-layer-only", action="store_true",
                     help="time the qwen2.5-0.5b-shape batch-1 layer chain alone (for profiling)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time the batch-16 step, the attention call and the batch-1 layers alone")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, out_path=args.traffic_out)
@@ -984,7 +1005,7 @@ def main():
     import synth
 
     if (args.attention_only or args.prefill_only or args.large_batch_only or args.variants_only
-            or args.step_counters or args.qwen_layer_only):
+            or args.step_counters or args.qwen_layer_only or args.decode_only):
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(2)
@@ -995,6 +1016,8 @@ def main():
             step_counters(torch, pkv, synth)
         elif args.prefill_only:
             prefill_only(torch, pkv, synth, args.prefill_tokens)
+        elif args.decode_only:
+            decode_only(torch, pkv, synth, args)
         elif args.qwen_layer_only:
             lq_ms, lq_bytes, _, lq_n = time_layer_qwen05_b1(torch, pkv, synth)
             lq_us = float(np.median(lq_ms)) * 1e3

@@ -47,11 +47,15 @@
  *
  * Pool layout: a page of PT tokens (page_tokens: 16, the engine's page, or
  * 256, the fixed page length of the three-stage engine's paged KV cache)
- * holds, as BF16, a K block [num_kv_heads][PT slots][head_dim] and a V
- * block in 16-token tiles, [PT / 16][num_kv_heads][head_dim][16 slots]
- * (V transposed within a tile, so that a tile of V is already the operand
- * layout of the matrix cores and is contiguous at any page size; for
- * 16-token pages the V block is [num_kv_heads][head_dim][16]).  With one
+ * holds, as BF16, a K block and a V block, both in 16-token tiles so that a
+ * tile of one kv head is one contiguous matrix-core operand at any page
+ * size:
+ *   K [PT / 16][num_kv_heads][head_dim / 8][16 slots][8 dims]: each token's
+ *     dimensions in chunks of 8, the 16 slots' chunk c side by side (the
+ *     score product's operand, read 1 KiB per load instruction);
+ *   V [PT / 16][num_kv_heads][head_dim][16 slots]: V transposed within a
+ *     tile (the value product's operand).
+ * With one
  * buffer (kv_pool_create) physical page p starts at base + p * page_bytes
  * with its K block followed by its V block, page_bytes =
  * 2 * num_kv_heads * PT * head_dim * 2 (32 KiB for 16 tokens of 8 kv heads

@@ -23,9 +23,9 @@ Parity pins (what each function is checked against, in tests/):
                          a dominant key gives its V, two-token closed form
                          fixes the 1/sqrt(D) scale, GQA equals MHA over
                          repeated KV, float64 online softmax equals two-pass
-  pool gather / append   numpy views of each page as K [head][slot][d] and
-                         V [tile][head][d][slot % 16] (16-token tiles), at
-                         16- and 256-token pages
+  pool gather / append   numpy views of each page as K [tile][head][d / 8]
+                         [slot % 16][d % 8] and V [tile][head][d][slot % 16]
+                         (16-token tiles), at 16- and 256-token pages
   split_pools /          the same views over separate K and V buffers; the
   whole_pool             two conversions undo each other
   layer, step            float64 brute force with a materialised softmax on
@@ -186,8 +186,8 @@ def attention(q, kc, vc, kv_heads, scale):
 
 class PoolGeometry:
     """Page geometry: T tokens per page; per page the BF16 K block
-    [kv head][slot][d] followed by the V block in 16-token tiles
-    [slot / 16][kv head][d][slot % 16] ([kv head][d][slot] when T = 16)."""
+    followed by the V block, both in 16-token tiles: K [slot / 16][kv head]
+    [d / 8][slot % 16][d % 8], V [slot / 16][kv head][d][slot % 16]."""
 
     def __init__(self, kv_heads, head_dim, page_tokens=16):
         self.kv_heads = kv_heads

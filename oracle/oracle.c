@@ -38,10 +38,10 @@
  *   - Argmax returns the lowest index among equal maxima.
  *
  * Pool page layout (the boundary's stated layout, implemented here on its
- * own): a physical page of T tokens holds, as BF16, first the K block
- * [kv head][slot 0..T-1][d], then the V block in 16-token tiles,
- * [slot / 16][kv head][d][slot % 16] (V transposed within each tile; for
- * T = 16 that is [kv head][d][slot]).
+ * own): a physical page of T tokens holds, as BF16, first the K block, then
+ * the V block, both in 16-token tiles: K [slot / 16][kv head][d / 8]
+ * [slot % 16][d % 8] (each token's dimensions in chunks of 8) and V
+ * [slot / 16][kv head][d][slot % 16] (V transposed within each tile).
  */
 #include <math.h>
 #include <stdint.h>
@@ -216,16 +216,17 @@ void orc_attention(const float *q, const float *kc, const float *vc, int n,
 
 /*
  * Element offset of (page, K or V, kv head g, slot, d) inside the pool:
- * K at [g][slot][d] from the page start, V at [slot / 16][g][d][slot % 16]
- * after the hkv * T * D elements of the K block.
+ * K at [slot / 16][g][d / 8][slot % 16][d % 8] from the page start, V at
+ * [slot / 16][g][d][slot % 16] after the hkv * T * D elements of the K
+ * block.
  */
 static long pool_offset(long page_elems, int hkv, int T, int D, int page,
 			int kv, int g, int slot, int d)
 {
 	long start = (long)page * page_elems;
-	if (kv == 0)
-		return start + ((long)g * T + slot) * D + d;
 	int tile = slot / 16, s = slot % 16;
+	if (kv == 0)
+		return start + ((((long)tile * hkv + g) * (D / 8) + d / 8) * 16 + s) * 8 + d % 8;
 	return start + (long)hkv * T * D + (((long)tile * hkv + g) * D + d) * 16 + s;
 }
 

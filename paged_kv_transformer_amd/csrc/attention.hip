@@ -180,9 +180,12 @@ paged_attention_kernel(const AttnArgs a) {
   u32x2 vr[PW][NC];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const uint16_t* kp = a.pv.k + pv_k_index(a.pv, page[i], kvh, sub[i] + col, D) + 8 * grp;
+    // lane l = 16 grp + col holds slot col, dims 32 h + 8 grp ..: chunk
+    // 4 h + grp of the tile, 16 bytes at (chunk * 16 + col) * 8 elements,
+    // so a load instruction reads 1 KiB contiguously
+    const uint16_t* kp = a.pv.k + pv_k_elem(a.pv, page[i], kvh, sub[i], 0, D) + 8 * l;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) kr[i][h] = __builtin_nontemporal_load((const u32x4*)(kp + 32 * h));
+    for (int h = 0; h < NH; ++h) kr[i][h] = __builtin_nontemporal_load((const u32x4*)(kp + 512 * h));
   }
 #pragma unroll
   for (int i = 0; i < PW; ++i) {

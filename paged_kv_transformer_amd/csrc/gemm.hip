@@ -359,9 +359,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
         }
         const int slot = p & (PT - 1);
         if (is_k) {
-          uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, hd - a.Hq, slot, D);
-          kp[j] = to_bf16_bits(y0);
-          kp[j + half] = to_bf16_bits(y1);
+          a.pv.k[pv_k_elem(a.pv, page, hd - a.Hq, slot, j, D)] = to_bf16_bits(y0);
+          a.pv.k[pv_k_elem(a.pv, page, hd - a.Hq, slot, j + half, D)] = to_bf16_bits(y1);
         } else {
           uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, 0, slot, D);
           vp[j * kTile] = to_bf16_bits(y0);

@@ -5,8 +5,8 @@
 namespace pkv {
 namespace {
 
-// One workgroup per sequence: copy the new token's K ([Hkv][D], into the
-// K block at [head][slot][d]) and V (into the V block at [head][d][slot]).
+// One workgroup per sequence: copy the new token's K and V ([Hkv][D] each)
+// into its slot of the page's K and V tiles.
 // The engine's decode appends one token per sequence at its absolute
 // position: logical page pos / 16, slot pos % 16.  A position outside the
 // table or a table entry outside the pool writes nothing and sets its bit
@@ -31,7 +31,7 @@ __global__ void kv_append_kernel(const PoolView pv, const int32_t* bt, int32_t b
   const uint16_t* vb = v + (size_t)b * Hkv * D;
   for (int i = threadIdx.x; i < Hkv * D; i += blockDim.x) {
     const int h = i / D, d = i % D;
-    pv.k[pv_k_index(pv, page, h, slot, D) + d] = kb[i];
+    pv.k[pv_k_elem(pv, page, h, slot, d, D)] = kb[i];
     pv.v[pv_v_index(pv, page, h, d, slot, D)] = vb[i];
   }
 }

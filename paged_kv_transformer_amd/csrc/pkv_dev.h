@@ -85,11 +85,16 @@ inline int64_t packed_act_elems(int B, int K) { return (int64_t)((B + 15) / 16) 
 // --------------------------------------------------------- arguments ---
 
 // Where the pages live.  Page p of PT = kTile << pt_shift tokens holds a K
-// block [Hkv][PT][D] at k + p * stride and a V block at v + p * stride:
-// one buffer of whole pages (v = k + the K block, stride = both blocks),
-// or separate K and V pools (stride = one block).  The V block is stored
-// in 16-token tiles, [PT / 16][Hkv][D][16]: a tile's V for one kv head is
-// one contiguous [D][16] operand whatever the page size.
+// block at k + p * stride and a V block at v + p * stride: one buffer of
+// whole pages (v = k + the K block, stride = both blocks), or separate K and
+// V pools (stride = one block).  Both blocks are stored in 16-token tiles,
+// so that a tile of one kv head is one contiguous matrix-core operand
+// whatever the page size:
+//   K [PT / 16][Hkv][D / 8][16 slots][8 dims]  (dims in chunks of 8: a
+//     lane's 16-byte A operand of the score product is one chunk of one
+//     slot, and a wave's 64 lanes read 1 KiB contiguously);
+//   V [PT / 16][Hkv][D][16 slots]              (V transposed: a lane's
+//     4-token B operand of the value product is 8 contiguous bytes).
 struct PoolView {
   uint16_t* k;
   uint16_t* v;
@@ -99,9 +104,12 @@ struct PoolView {
   int32_t hkv;         // kv heads
 };
 
-// Element d of token `slot`'s K (kv head h) and V of page `page`.
-__host__ __device__ inline int64_t pv_k_index(const PoolView& p, int page, int h, int slot, int D) {
-  return (int64_t)page * p.stride + ((int64_t)h * (kTile << p.pt_shift) + slot) * D;
+// Dimension d of token `slot`'s K (kv head h) of page `page`; dimensions
+// d .. d | 7 follow contiguously.
+__host__ __device__ inline int64_t pv_k_elem(const PoolView& p, int page, int h, int slot, int d, int D) {
+  return (int64_t)page * p.stride +
+         (((((int64_t)(slot >> 4) * p.hkv + h) * (D >> 3) + (d >> 3)) * kTile + (slot & (kTile - 1))) << 3) +
+         (d & 7);
 }
 // V of dimension d, token `slot`; dimension d + 1 is kTile elements further.
 __host__ __device__ inline int64_t pv_v_index(const PoolView& p, int page, int h, int d, int slot,

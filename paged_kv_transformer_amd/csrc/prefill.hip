@@ -403,7 +403,8 @@ __global__ __launch_bounds__(128 * WR) void prefill_gemm_kernel(const PgemmArgs 
             } else {
               const int slot = p & (PT - 1);
               if (is_k) {
-                uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, hd - a.Hq, slot, D) + jj;
+                // jj is a multiple of 4: its 4 dims lie in one 8-dim chunk
+                uint16_t* kp = a.pv.k + pv_k_elem(a.pv, page, hd - a.Hq, slot, jj, D);
                 *(u32x2*)kp = (u32x2){pack2(y[0], y[1]), pack2(y[2], y[3])};
               } else {
                 uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, jj, slot, D);
@@ -474,9 +475,8 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* part, int 
   }
   const int slot = p & ((1 << psh) - 1);
   if (is_k) {
-    uint16_t* kp = a.pv.k + pv_k_index(a.pv, page, hd - a.Hq, slot, D);
-    kp[j] = to_bf16_bits(y0);
-    kp[j + half] = to_bf16_bits(y1);
+    a.pv.k[pv_k_elem(a.pv, page, hd - a.Hq, slot, j, D)] = to_bf16_bits(y0);
+    a.pv.k[pv_k_elem(a.pv, page, hd - a.Hq, slot, j + half, D)] = to_bf16_bits(y1);
   } else {
     uint16_t* vp = a.pv.v + pv_v_index(a.pv, page, hd - a.Hq - a.Hkv, 0, slot, D);
     vp[j * kTile] = to_bf16_bits(y0);
@@ -613,9 +613,10 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
   };
   bool bad = false;
   // A lane's element offsets inside a tile do not change from tile to tile
-  // (K: slot col, dims 8 grp..; V: dim col, slots 4 grp..): the address of a
-  // load is the tile's base, uniform across the wave, plus these.
-  const uint32_t klane = (uint32_t)(col * D + 8 * grp);
+  // (K: slot col, dims 32 h + 8 grp.., i.e. chunk 4 h + grp, 1 KiB per
+  // block h; V: dim col, slots 4 grp..): the address of a load is the
+  // tile's base, uniform across the wave, plus these.
+  const uint32_t klane = (uint32_t)(8 * l);
   const uint32_t vlane = (uint32_t)(col * kTile + 4 * grp);
   // tiles past the wave's range read its last tile and are masked
   auto load = [&](Chunk& C, int lp0) {
@@ -627,9 +628,9 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
       const bool ok = (unsigned)page < (unsigned)a.pv.num_pages;
       bad |= !ok;
       page = ok ? page : 0;
-      const uint16_t* kb = a.pv.k + pv_k_index(a.pv, page, kvh, sub, D);
+      const uint16_t* kb = a.pv.k + pv_k_elem(a.pv, page, kvh, sub, 0, D);
 #pragma unroll
-      for (int h = 0; h < NH; ++h) C.k[i][h] = *(const u32x4*)(kb + klane + 32 * h);
+      for (int h = 0; h < NH; ++h) C.k[i][h] = *(const u32x4*)(kb + klane + 512 * h);
       const uint16_t* vb = a.pv.v + pv_v_index(a.pv, page, kvh, 0, sub, D);
 #pragma unroll
       for (int c = 0; c < NC; ++c) C.v[i][c] = *(const u32x2*)(vb + vlane + c * 16 * kTile);

@@ -76,9 +76,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void probe_paged_read_kernel(const
   u32x2 vr[PW][NC];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const uint16_t* kp = a.pv.k + pv_k_index(a.pv, page[i], kvh, sub[i] + col, D) + 8 * grp;
+    const uint16_t* kp = a.pv.k + pv_k_elem(a.pv, page[i], kvh, sub[i], 0, D) + 8 * l;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) kr[i][h] = __builtin_nontemporal_load((const u32x4*)(kp + 32 * h));
+    for (int h = 0; h < NH; ++h) kr[i][h] = __builtin_nontemporal_load((const u32x4*)(kp + 512 * h));
   }
 #pragma unroll
   for (int i = 0; i < PW; ++i) {

@@ -50,12 +50,18 @@ def softmax_attention(q, K, V, scale):
 
 
 def pool_view(pool, kv_heads, head_dim, page_tokens=16):
-    """Views of the pool's pages: K [page][head][slot][d] and V
-    [page][tile][head][d][s], token slot = 16 tile + s (16-token tiles)."""
+    """Views of the pool's pages (writable, no copy), token slot = 16 tile +
+    s (16-token tiles): K [page][tile][head][c][s][e] with d = 8 c + e, and V
+    [page][tile][head][d][s]."""
     blk = kv_heads * page_tokens * head_dim
     pages = np.asarray(pool).reshape(-1, 2 * blk)
-    return (pages[:, :blk].reshape(-1, kv_heads, page_tokens, head_dim),
+    return (pages[:, :blk].reshape(-1, page_tokens // 16, kv_heads, head_dim // 8, 16, 8),
             pages[:, blk:].reshape(-1, page_tokens // 16, kv_heads, head_dim, 16))
+
+
+def k_of(kv, page, slot):
+    """The K view's [head][d] entries of one token (a writable view)."""
+    return kv[page, slot // 16, :, :, slot % 16, :]
 
 
 def gather(pool, kv_heads, head_dim, bt_row, n, page_tokens=16):
@@ -64,7 +70,7 @@ def gather(pool, kv_heads, head_dim, bt_row, n, page_tokens=16):
     t = np.arange(n)
     pages = np.asarray(bt_row)[t // page_tokens]
     slots = t % page_tokens
-    K = bf16_bits_to_f64(kv[pages, :, slots, :])
+    K = bf16_bits_to_f64(kv[pages, slots // 16, :, :, slots % 16, :]).reshape(n, kv_heads, head_dim)
     V = bf16_bits_to_f64(vv[pages, slots // 16, :, :, slots % 16])
     return K, V
 

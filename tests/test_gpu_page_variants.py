@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import brute
 import oracle
 import paged_kv_transformer_amd as pkv
 import synth
@@ -117,16 +118,17 @@ def test_attention_same_tokens_same_bits_in_every_geometry():
     for PT in (16, 256):
         npages = int(synth.pages_for(lens, PT).sum())
         bt = synth.block_tables(53, 1, lens, npages, page_tokens=PT)[0]
-        # pages as numpy arrays: K [page][head][slot][d], V in 16-token
-        # tiles [page][tile][head][d][slot % 16]
-        kp = np.zeros((npages, Hkv, PT, D), np.uint16)
-        vp = np.zeros((npages, PT // 16, Hkv, D, 16), np.uint16)
+        # the pages through the numpy views of the page layout (16-token
+        # tiles: K [page][tile][head][d / 8][slot % 16][d % 8], V
+        # [page][tile][head][d][slot % 16])
+        pages = np.zeros(npages * 2 * Hkv * PT * D, np.uint16)
+        kv, vv = brute.pool_view(pages, Hkv, D, PT)
         for b, n in enumerate(lens):
             t = np.arange(n)
-            kp[bt[b][t // PT], :, t % PT, :] = K[b, :n].reshape(n, Hkv, D)
-            vp[bt[b][t // PT], (t % PT) // 16, :, :, t % 16] = V[b, :n].reshape(n, Hkv, D)
-        pages = np.concatenate([kp.reshape(npages, -1), vp.reshape(npages, -1)], axis=1)
-        for p in (pages.reshape(-1), (kp.reshape(-1), vp.reshape(-1))):
+            kv[bt[b][t // PT], (t % PT) // 16, :, :, t % 16, :] = K[b, :n].reshape(n, Hkv, D // 8, 8)
+            vv[bt[b][t // PT], (t % PT) // 16, :, :, t % 16] = V[b, :n].reshape(n, Hkv, D)
+        geo = oracle.PoolGeometry(Hkv, D, PT)
+        for p in (pages, oracle.split_pools(pages, geo)):
             out, err = attention_gpu(p, Hkv, q, bt, lens, 0.125, page_tokens=PT)
             assert err == 0
             outs.append(out)

@@ -288,7 +288,7 @@ def test_pool_append_matches_reshaped_view(pos, D):
     v = synth.to_bf16_bits(g.standard_normal(8 * D).astype(np.float32))
     want = pool.copy()
     kv, vv = brute.pool_view(want, 8, D)
-    kv[bt[pos // 16], :, pos % 16, :] = k.reshape(8, D)
+    brute.k_of(kv, bt[pos // 16], pos % 16)[...] = k.reshape(8, D // 8, 8)
     vv[bt[pos // 16], 0, :, :, pos % 16] = v.reshape(8, D)
     got = pool.copy()
     oracle.pool_append(got, geo, bt, pos, k, v)
@@ -316,7 +316,7 @@ def test_pool_gather_any_page_size_matches_reshaped_view(T, D):
     oracle.pool_append(got, geo, bt, pos, k, v)
     want = pool.copy()
     kv, vv = brute.pool_view(want, 2, D, T)
-    kv[bt[pos // T], :, pos % T, :] = k.reshape(2, D)
+    brute.k_of(kv, bt[pos // T], pos % T)[...] = k.reshape(2, D // 8, 8)
     vv[bt[pos // T], (pos % T) // 16, :, :, pos % 16] = v.reshape(2, D)
     assert np.array_equal(got, want)
 
@@ -465,12 +465,12 @@ def test_prefill_matches_float64_causal_brute_force(start, T):
         for t in range(T):
             p = start + t
             page, slot = bts[l][p // 16], p % 16
-            got_k = brute.bf16_bits_to_f64(kv_view[page, :, slot, :])
+            got_k = brute.bf16_bits_to_f64(brute.k_of(kv_view, page, slot)).reshape(shape.kv_heads, -1)
             got_v = brute.bf16_bits_to_f64(vv_view[page, 0, :, :, slot])
             # one BF16 ulp at most (FP32 vs float64 values before rounding)
             np.testing.assert_allclose(got_k, K[t], rtol=2 ** -7, atol=1e-6)
             np.testing.assert_allclose(got_v, V[t], rtol=2 ** -7, atol=1e-6)
-            tv[page, :, slot, :] = True
+            brute.k_of(tv, page, slot)[...] = True
             vv_t[page, 0, :, :, slot] = True
     assert np.array_equal(pool_after[~touched], pool[~touched])
 
