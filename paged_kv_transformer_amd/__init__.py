@@ -17,7 +17,9 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# The library this binding loads: the in-tree build, or another build of the
+# same sources named by PKV_LIBRARY (the host-sanitized libpkv_san.so).
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PAGE_TOKENS = 16
 HEAD_DIM = 64
@@ -68,7 +70,7 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libpkv.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+            raise RuntimeError("the HIP library is not built (%s); run __graft_entry__.build()" % LIB_PATH)
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         PP = ctypes.POINTER(Pool)

@@ -29,10 +29,22 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *sources(), "-o", tmp]
+# A host-sanitized build (python build.py --sanitize -> libpkv_san.so):
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only
+# (argument validation, workspace carving, launch planning); the gfx950 code
+# is built as usual.  Load it with PKV_LIBRARY=<path to libpkv_san.so> and
+# clang's ASan runtime preloaded (libclang_rt.asan-x86_64.so of the ROCm
+# LLVM, ASAN_OPTIONS=detect_leaks=0).
+SAN_LIB = os.path.join(HERE, "libpkv_san.so")
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    lib = SAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *(SANITIZE if sanitize else []), "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(HERE, "csrc"), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,9 +54,10 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + msgs)
     if msgs.strip() and verbose:
         print(msgs, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys as _sys
+    print(build(verbose=True, sanitize="--sanitize" in _sys.argv))
