@@ -376,11 +376,17 @@ constexpr int64_t kMaxMatrixBytes = (int64_t)1 << 31;  // largest weight matrix
 inline int gemm_ct(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
 
 // A residual projection whose row tiles alone give few workgroups and whose
-// K is long (the down projection) splits K over workgroups: about 512
-// workgroups keep enough weight bytes in flight, where one workgroup per
-// 16-row tile would leave half the chip idle.
+// K is long (the down projection) splits K over workgroups (up to about one
+// workgroup per compute unit), where one workgroup per row tile would leave
+// most of the chip idle.
 constexpr int kSplitMinK = 4096;
 constexpr int kSplitTargetWgs = 512;
+// The split count aims at one workgroup per compute unit (256): one round,
+// with no second, partly filled one.  Measured per split count of the
+// Llama-shape down projection (64 row tiles) on the batch-16 step: 2, 3, 4,
+// 6, 8 splits give 1.021, 0.991, 0.962, 0.995, 0.969 ms; the batch-1 Qwen
+// layer (28 tiles): 4, 6, 9, 18 splits give 27.8, 27.6, 27.2, 28.2 us.
+constexpr int kSplitRoundWgs = 256;
 constexpr int kSplitMinSteps = 8;  // 32-wide K steps per split, at least
 // The QKV and O launches of one 16-column group (one 16-row tile per
 // workgroup) run 8 waves for a few sequences and 4 from this many on:
@@ -414,7 +420,7 @@ inline GemmPlan plan_gemm(int epi, int N, int B, int K) {
   p.ks = 1;
   if (split) {
     const int steps = K / 32;
-    int ks = kSplitTargetWgs / p.tiles;
+    int ks = kSplitRoundWgs / p.tiles;
     if (ks > steps / kSplitMinSteps) ks = steps / kSplitMinSteps;
     p.ks = ks < 1 ? 1 : ks;
   }
