@@ -884,9 +884,12 @@ def decode_only(torch, pkv, synth, args):
     attn_ms, _ = time_attention(torch, pkv, synth, S, args.attn_rounds)
     l_ms, _ = time_layer_b1(torch, pkv, synth, S)
     lq_ms, _, _, lq_n = time_layer_qwen05_b1(torch, pkv, synth)
-    out = {"step_b16_ms": round(step, 4), "attention_us": round(attn_ms * 1e3, 3),
+    samp_us, _ = time_sampling(torch, pkv, synth, S)
+    wl1 = synth.llama1b_step_b1()
+    s1, _ = time_step_cfg(torch, pkv, synth, wl1, synth.LLAMA1B, S.model, int(wl1.positions.max()) + 1)
+    out = {"step_b16_ms": round(step, 4), "attention_us": round(attn_ms * 1e3, 3), "sampling_us": round(samp_us, 2),
            "layer_llama1b_b1_us": round(l_ms * 1e3, 3), "layer_qwen05_b1_us": round(float(np.median(lq_ms)) * 1e3, 3),
-           "qwen_launches_per_layer": lq_n}
+           "qwen_launches_per_layer": lq_n, "step_llama1b_b1_ms": round(float(np.median(s1)), 4)}
     assert pkv.device_error(S.ws) == 0
     print(json.dumps(out), flush=True)
 

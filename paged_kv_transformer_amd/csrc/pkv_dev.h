@@ -316,7 +316,7 @@ constexpr int kSampleChoiceBytes = 24;
 struct SampleWs {
   uint32_t* cnt;      // [B][3][2048]
   uint64_t* mass;     // [B][3][2048]
-  uint64_t* sum;      // [B] softmax normaliser (fixed point)
+  uint64_t* sum;      // [B][W] the softmax normaliser's per-chunk parts (fixed point)
   void* choice;       // [3][B] records: choices after levels 1, 2; the nucleus
   float* wmax;        // [B][W] chunk maxima
   uint64_t* wmass;    // [B][W] chunk mass above the threshold

@@ -79,7 +79,20 @@ __device__ __forceinline__ uint64_t fixed_mass(float l, float m, float c) {
   // (0, 1]; a -inf logit gives 0 (also when greedy, where -inf * 0 is NaN)
   const float x = (l - m) * c;
   const float e = x == x ? __builtin_amdgcn_exp2f(x) : 0.f;
-  return (uint64_t)(e * 4294967296.0f);
+  // e * 2^32 truncated; below 2^32 one 32-bit conversion does it
+  const float f = e * 4294967296.0f;
+  return f >= 4294967296.0f ? (1ull << 32) : (uint64_t)(uint32_t)f;
+}
+
+// A sequence sampled by top-p alone (temperature > 0, no top-k cap, top_p <
+// 1) reaches its mass budget no later than its count budget (all V tokens)
+// in every bucket scan, so the first two levels need no token counts: the
+// choices are the same without them, and each histogram update is one
+// atomic instead of two.  The last level keeps its counts (the ties of the
+// threshold key are counted there).
+__device__ __forceinline__ bool mass_only(const SArgs& a, int b) {
+  const int k = a.top_k[b];
+  return a.temperature[b] > 0.f && !(k > 0 && k < a.V) && a.top_p[b] < 1.f;
 }
 
 // The chunk of workgroup (b, w): elements [e0, e1) of sequence b.  Passes
@@ -98,6 +111,23 @@ __device__ __forceinline__ Chunk chunk_of(const SArgs& a, int b, int w) {
   c.e1 = min(a.V, c.e0 + a.chunk);
   c.E = a.chunk / kSThreads;
   return c;
+}
+
+// Latency is most of a launch's time here (a chunk is 8-128 KB), so every
+// kernel issues its first batch of logits, and the few values its
+// decisions need (the chunk maxima, the previous level's histogram, the
+// choice records), back to back before it waits for any of them: one round
+// trip instead of one per dependent step.  kSBatch logits per thread are in
+// flight per batch (a 4096-logit chunk is one batch).
+constexpr int kSBatch = 16;
+
+// Thread t's next batch in pass order: e, e + 256, ...; -inf past the chunk.
+__device__ __forceinline__ void load_batch(const Chunk& ch, int e, float (&v)[kSBatch]) {
+#pragma unroll
+  for (int i = 0; i < kSBatch; ++i) {
+    const int x = e + i * kSThreads;
+    v[i] = x < ch.e1 ? ch.row[x] : -INFINITY;
+  }
 }
 
 // Clears `n` 32-bit words of `p` with the workgroups of one sequence.
@@ -135,20 +165,52 @@ static_assert(sizeof(Choice) == kSampleChoiceBytes, "choice record size");
 
 __device__ __forceinline__ Choice* choices(const SampleWs& w) { return (Choice*)w.choice; }
 
+// Level L's global histogram of sequence b.
+__device__ __forceinline__ size_t hist_at(int b, int level) { return ((size_t)b * 3 + level) * kBuckets; }
+
+// A thread's share of a histogram for choose(): the 8 buckets from
+// top = 2047 - 8t downwards, loaded together.
+constexpr int kPer = kBuckets / kSThreads;
+struct HistPart {
+  uint32_t cnt[kPer];
+  uint64_t mass[kPer];
+};
+
+__device__ __forceinline__ void load_hist_part(const uint32_t* cnt, const uint64_t* mass, HistPart& h) {
+  const int top = kBuckets - 1 - kPer * (int)threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    h.cnt[i] = cnt[top - i];
+    h.mass[i] = mass[top - i];
+  }
+}
+
+// A choice and the count and mass of the bucket it took.
+struct Chosen {
+  Choice c;
+  uint32_t n;
+  uint64_t f;
+};
+
 // Scan a histogram from the top bucket down for the first bucket where the
 // count reaches k_rem or the mass reaches m_rem; update the choice.  Every
-// thread of the workgroup calls it and gets the same result.
-__device__ Choice choose(const uint32_t* cnt, const uint64_t* mass, Choice c, int bits) {
-  __shared__ Choice s_out;
-  constexpr int PER = kBuckets / kSThreads;  // 8 buckets per thread, top first
+// thread of the workgroup calls it with its HistPart and gets the same
+// result.
+__device__ Chosen choose(const HistPart& h, Choice c, int bits) {
+  __shared__ Chosen s_out;
   const int t = threadIdx.x;
-  const int top = kBuckets - 1 - PER * t;
-  if (t == 0) s_out = c;  // replaced below; kept only if no bucket qualifies
+  const int top = kBuckets - 1 - kPer * t;
+  if (t == 0) {  // replaced below; kept only if no bucket qualifies
+    s_out.c = c;
+    s_out.n = 0u;
+    s_out.f = 0ull;
+  }
   uint32_t lc = 0;
   uint64_t lm = 0;
-  for (int i = 0; i < PER; ++i) {
-    lc += cnt[top - i];
-    lm += mass[top - i];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    lc += h.cnt[i];
+    lm += h.mass[i];
   }
   // inclusive scans over threads (thread order = descending buckets)
   const uint32_t inc_c = wg_scan(lc);
@@ -160,81 +222,39 @@ __device__ Choice choose(const uint32_t* cnt, const uint64_t* mass, Choice c, in
   if (!before && after) {
     uint32_t cc = exc_c;
     uint64_t cm = exc_m;
-    for (int i = 0; i < PER; ++i) {
-      const int bk = top - i;
-      if (cc + cnt[bk] >= c.k_rem || cm + mass[bk] >= c.m_rem) {
-        Choice o;
-        o.prefix = (c.prefix << bits) | (uint32_t)bk;
-        o.k_rem = c.k_rem - cc;
-        o.m_rem = c.m_rem - cm;
-        o.m_above = c.m_above + cm;
+    for (int i = 0; i < kPer; ++i) {
+      if (cc + h.cnt[i] >= c.k_rem || cm + h.mass[i] >= c.m_rem) {
+        Chosen o;
+        o.c.prefix = (c.prefix << bits) | (uint32_t)(top - i);
+        o.c.k_rem = c.k_rem - cc;
+        o.c.m_rem = c.m_rem - cm;
+        o.c.m_above = c.m_above + cm;
+        o.n = h.cnt[i];
+        o.f = h.mass[i];
         s_out = o;
         break;
       }
-      cc += cnt[bk];
-      cm += mass[bk];
+      cc += h.cnt[i];
+      cm += h.mass[i];
     }
   }
   __syncthreads();
-  const Choice o = s_out;
+  const Chosen o = s_out;
   __syncthreads();
   return o;
 }
 
-// Histogram of one level over a chunk into LDS, then added to the sequence's
-// global histogram (integer atomics: order-independent).
-__device__ void histogram(const SArgs& a, const Chunk& ch, int level, uint32_t prefix, float m,
-                          float c, uint32_t* gcnt, uint64_t* gmass, uint64_t* gsum) {
-  __shared__ uint32_t h_cnt[kBuckets];
-  __shared__ uint64_t h_mass[kBuckets];
-  __shared__ uint64_t h_sum;
+// The sequence's maximum logit from K0's chunk maxima (W <= 64): wmax_ld is
+// thread t's chunk maximum (t < 64), loaded with the first batch.
+__device__ __forceinline__ float load_wmax(const SArgs& a, int b) {
   const int t = threadIdx.x;
-  for (int i = t; i < kBuckets; i += kSThreads) {
-    h_cnt[i] = 0u;
-    h_mass[i] = 0ull;
-  }
-  if (t == 0) h_sum = 0ull;
-  __syncthreads();
-  uint64_t ls = 0;
-  for (int e0 = ch.e0 + t; e0 < ch.e1; e0 += 8 * kSThreads) {
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = e0 + i * kSThreads;
-      v[i] = e < ch.e1 ? ch.row[e] : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (e0 + i * kSThreads >= ch.e1) break;
-      const float l = v[i];
-      const uint32_t key = skey(l);
-      const uint64_t f = fixed_mass(l, m, c);
-      ls += f;
-      if (in_prefix(key, level, prefix)) {
-        const int d = digit(key, level);
-        atomicAdd(&h_cnt[d], 1u);
-        atomicAdd((unsigned long long*)&h_mass[d], (unsigned long long)f);
-      }
-    }
-  }
-  if (gsum) atomicAdd((unsigned long long*)&h_sum, (unsigned long long)ls);
-  __syncthreads();
-  for (int i = t; i < kBuckets; i += kSThreads)
-    if (h_cnt[i]) {
-      atomicAdd(&gcnt[i], h_cnt[i]);
-      atomicAdd((unsigned long long*)&gmass[i], (unsigned long long)h_mass[i]);
-    }
-  if (gsum && t == 0) atomicAdd((unsigned long long*)gsum, (unsigned long long)h_sum);
+  return t < 64 && t < a.W ? a.w.wmax[(size_t)b * a.W + t] : -INFINITY;
 }
-
-// The sequence's maximum logit from K0's chunk maxima: one load per chunk
-// by as many threads, one round trip (W <= 64).
-__device__ float seq_max(const SArgs& a, int b) {
+__device__ float seq_max(float wmax_ld) {
   __shared__ float s_res;
   const int t = threadIdx.x;
   if (t < 64) {
-    const float v = t < a.W ? a.w.wmax[(size_t)b * a.W + t] : -INFINITY;
-    float m = v;
+    float m = wmax_ld;
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if (t == 0) s_res = m;
   }
@@ -242,20 +262,81 @@ __device__ float seq_max(const SArgs& a, int b) {
   return s_res;
 }
 
+// The sequence's normaliser from K1's per-chunk parts (W <= 64), part =
+// thread t's part (t < 64): an integer sum, the same in any order.
+__device__ uint64_t seq_sum(uint64_t part) {
+  __shared__ uint64_t s_res;
+  const int t = threadIdx.x;
+  if (t < 64) {
+    uint64_t v = part;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (t == 0) s_res = v;
+  }
+  __syncthreads();
+  return s_res;
+}
+
+// Histogram of one level over a chunk into LDS, then added to the sequence's
+// global histogram (integer atomics: order-independent).  v holds the
+// thread's first batch (elements ch.e0 + t + 256 i), already in flight.
+__device__ void histogram(const Chunk& ch, float (&v)[kSBatch], int level, uint32_t prefix, float m,
+                          float c, bool counts, uint32_t* gcnt, uint64_t* gmass, uint64_t* gsum) {
+  __shared__ uint32_t h_cnt[kBuckets];
+  __shared__ uint64_t h_mass[kBuckets];
+  __shared__ uint64_t h_sum[kSThreads / 64];
+  const int t = threadIdx.x;
+  for (int i = t; i < kBuckets; i += kSThreads) {
+    h_cnt[i] = 0u;
+    h_mass[i] = 0ull;
+  }
+  __syncthreads();
+  uint64_t ls = 0;
+  for (int e0 = ch.e0 + t;;) {
+#pragma unroll
+    for (int i = 0; i < kSBatch; ++i) {
+      if (e0 + i * kSThreads >= ch.e1) break;
+      const float l = v[i];
+      const uint32_t key = skey(l);
+      const uint64_t f = fixed_mass(l, m, c);
+      ls += f;
+      if (in_prefix(key, level, prefix)) {
+        const int d = digit(key, level);
+        if (counts) atomicAdd(&h_cnt[d], 1u);
+        atomicAdd((unsigned long long*)&h_mass[d], (unsigned long long)f);
+      }
+    }
+    e0 += kSBatch * kSThreads;
+    if (e0 >= ch.e1) break;
+    load_batch(ch, e0, v);
+  }
+  // the chunk's part of the normaliser: a wave sum, then the 4 waves' in
+  // order, stored in the chunk's own slot (no atomics on one shared word)
+  if (gsum) {
+    for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+    if ((t & 63) == 0) h_sum[t >> 6] = ls;
+  }
+  __syncthreads();
+  for (int i = t; i < kBuckets; i += kSThreads) {
+    if (h_cnt[i]) atomicAdd(&gcnt[i], h_cnt[i]);
+    if (h_mass[i]) atomicAdd((unsigned long long*)&gmass[i], (unsigned long long)h_mass[i]);
+  }
+  if (gsum && t == 0) {
+    uint64_t v = 0;
+    for (int i = 0; i < kSThreads / 64; ++i) v += h_sum[i];
+    *gsum = v;
+  }
+}
+
 __global__ __launch_bounds__(kSThreads) void sample_k0(const SArgs a) {
   __shared__ float red[kSThreads / 64];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const Chunk ch = chunk_of(a, b, w);
   float m = -INFINITY;
-  for (int e0 = ch.e0 + t; e0 < ch.e1; e0 += 8 * kSThreads) {
-    float v[8];
+  for (int e0 = ch.e0 + t; e0 < ch.e1; e0 += kSBatch * kSThreads) {
+    float v[kSBatch];
+    load_batch(ch, e0, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = e0 + i * kSThreads;
-      v[i] = e < ch.e1 ? ch.row[e] : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, v[i]);
+    for (int i = 0; i < kSBatch; ++i) m = fmaxf(m, v[i]);
   }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((t & 63) == 0) red[t >> 6] = m;
@@ -265,23 +346,28 @@ __global__ __launch_bounds__(kSThreads) void sample_k0(const SArgs a) {
     for (int i = 1; i < kSThreads / 64; ++i) r = fmaxf(r, red[i]);
     a.w.wmax[(size_t)b * a.W + w] = r;
   }
-  clear_words((uint32_t*)(a.w.cnt + (size_t)b * 3 * kBuckets), kBuckets, w, a.W);
-  clear_words((uint32_t*)(a.w.mass + (size_t)b * 3 * kBuckets), 2 * kBuckets, w, a.W);
-  if (w == 0 && t == 0) a.w.sum[b] = 0ull;
+  clear_words((uint32_t*)(a.w.cnt + hist_at(b, 0)), kBuckets, w, a.W);
+  clear_words((uint32_t*)(a.w.mass + hist_at(b, 0)), 2 * kBuckets, w, a.W);
 }
 
 __global__ __launch_bounds__(kSThreads) void sample_k1(const SArgs a) {
   const int b = blockIdx.y, w = blockIdx.x;
   const Chunk ch = chunk_of(a, b, w);
-  const float m = seq_max(a, b), c = inv_temp(a, b);
-  histogram(a, ch, 0, 0u, m, c, a.w.cnt + (size_t)b * 3 * kBuckets,
-            a.w.mass + (size_t)b * 3 * kBuckets, a.w.sum + b);
-  clear_words((uint32_t*)(a.w.cnt + ((size_t)b * 3 + 1) * kBuckets), kBuckets, w, a.W);
-  clear_words((uint32_t*)(a.w.mass + ((size_t)b * 3 + 1) * kBuckets), 2 * kBuckets, w, a.W);
+  float v[kSBatch];
+  load_batch(ch, ch.e0 + (int)threadIdx.x, v);
+  const float wm = load_wmax(a, b);
+  const float c = inv_temp(a, b);
+  __builtin_amdgcn_sched_barrier(0);
+  const float m = seq_max(wm);
+  histogram(ch, v, 0, 0u, m, c, !mass_only(a, b), a.w.cnt + hist_at(b, 0), a.w.mass + hist_at(b, 0),
+            a.w.sum + (size_t)b * a.W + w);
+  clear_words((uint32_t*)(a.w.cnt + hist_at(b, 1)), kBuckets, w, a.W);
+  clear_words((uint32_t*)(a.w.mass + hist_at(b, 1)), 2 * kBuckets, w, a.W);
 }
 
 // The choice before level 0: the count and mass budgets of the nucleus.
-__device__ Choice initial_choice(const SArgs& a, int b) {
+// sum: the sequence's normaliser (fixed point).
+__device__ Choice initial_choice(const SArgs& a, int b, uint64_t sum) {
   Choice c;
   c.prefix = 0u;
   c.m_above = 0ull;
@@ -292,7 +378,7 @@ __device__ Choice initial_choice(const SArgs& a, int b) {
   if (greedy || p >= 1.f) {
     c.m_rem = ~0ull;
   } else {
-    const double target = ceil((double)(p > 0.f ? p : 0.f) * (double)a.w.sum[b]);
+    const double target = ceil((double)(p > 0.f ? p : 0.f) * (double)sum);
     c.m_rem = target < 1.0 ? 1ull : (uint64_t)target;
   }
   return c;
@@ -301,25 +387,41 @@ __device__ Choice initial_choice(const SArgs& a, int b) {
 __global__ __launch_bounds__(kSThreads) void sample_k2(const SArgs a) {
   const int b = blockIdx.y, w = blockIdx.x;
   const Chunk ch = chunk_of(a, b, w);
-  const float m = seq_max(a, b), c = inv_temp(a, b);
-  const Choice c1 = choose(a.w.cnt + (size_t)b * 3 * kBuckets, a.w.mass + (size_t)b * 3 * kBuckets,
-                           initial_choice(a, b), 11);
+  float v[kSBatch];
+  load_batch(ch, ch.e0 + (int)threadIdx.x, v);
+  const float wm = load_wmax(a, b);
+  HistPart hp;
+  load_hist_part(a.w.cnt + hist_at(b, 0), a.w.mass + hist_at(b, 0), hp);
+  const int t = threadIdx.x;
+  const uint64_t sum_part = t < 64 && t < a.W ? a.w.sum[(size_t)b * a.W + t] : 0ull;
+  const float c = inv_temp(a, b);
+  __builtin_amdgcn_sched_barrier(0);
+  const float m = seq_max(wm);
+  const uint64_t sum = seq_sum(sum_part);
+  const Choice c1 = choose(hp, initial_choice(a, b, sum), 11).c;
   if (w == 0 && threadIdx.x == 0) choices(a.w)[b] = c1;
-  histogram(a, ch, 1, c1.prefix, m, c, a.w.cnt + ((size_t)b * 3 + 1) * kBuckets,
-            a.w.mass + ((size_t)b * 3 + 1) * kBuckets, nullptr);
-  clear_words((uint32_t*)(a.w.cnt + ((size_t)b * 3 + 2) * kBuckets), kBuckets, w, a.W);
-  clear_words((uint32_t*)(a.w.mass + ((size_t)b * 3 + 2) * kBuckets), 2 * kBuckets, w, a.W);
+  histogram(ch, v, 1, c1.prefix, m, c, !mass_only(a, b), a.w.cnt + hist_at(b, 1),
+            a.w.mass + hist_at(b, 1), nullptr);
+  clear_words((uint32_t*)(a.w.cnt + hist_at(b, 2)), kBuckets, w, a.W);
+  clear_words((uint32_t*)(a.w.mass + hist_at(b, 2)), 2 * kBuckets, w, a.W);
 }
 
 __global__ __launch_bounds__(kSThreads) void sample_k3(const SArgs a) {
   const int b = blockIdx.y, w = blockIdx.x;
   const Chunk ch = chunk_of(a, b, w);
-  const float m = seq_max(a, b), c = inv_temp(a, b);
-  const Choice c2 = choose(a.w.cnt + ((size_t)b * 3 + 1) * kBuckets,
-                           a.w.mass + ((size_t)b * 3 + 1) * kBuckets, choices(a.w)[b], 11);
+  float v[kSBatch];
+  load_batch(ch, ch.e0 + (int)threadIdx.x, v);
+  const float wm = load_wmax(a, b);
+  HistPart hp;
+  load_hist_part(a.w.cnt + hist_at(b, 1), a.w.mass + hist_at(b, 1), hp);
+  const Choice prev = choices(a.w)[b];
+  const float c = inv_temp(a, b);
+  __builtin_amdgcn_sched_barrier(0);
+  const float m = seq_max(wm);
+  const Choice c2 = choose(hp, prev, 11).c;
   if (w == 0 && threadIdx.x == 0) choices(a.w)[a.B + b] = c2;
-  histogram(a, ch, 2, c2.prefix, m, c, a.w.cnt + ((size_t)b * 3 + 2) * kBuckets,
-            a.w.mass + ((size_t)b * 3 + 2) * kBuckets, nullptr);
+  histogram(ch, v, 2, c2.prefix, m, c, true, a.w.cnt + hist_at(b, 2),
+            a.w.mass + hist_at(b, 2), nullptr);
 }
 
 // The nucleus, final: every token with key > tau, and the first `ties`
@@ -336,15 +438,15 @@ __device__ __forceinline__ Nucleus* nuclei(const SampleWs& w, int B) {
   return (Nucleus*)((char*)w.choice + (size_t)2 * B * kSampleChoiceBytes);
 }
 
-__device__ Nucleus nucleus(const SArgs& a, int b) {
-  const uint32_t* cnt3 = a.w.cnt + ((size_t)b * 3 + 2) * kBuckets;
-  const uint64_t* mass3 = a.w.mass + ((size_t)b * 3 + 2) * kBuckets;
-  const Choice c3 = choose(cnt3, mass3, choices(a.w)[a.B + b], 10);
-  const uint32_t d = c3.prefix & 1023u;
-  const uint32_t n = cnt3[d];
-  const uint64_t f = n ? mass3[d] / n : 0ull;  // equal keys, equal masses
+// The level-3 choice (hp: the thread's part of the level-3 histogram,
+// prev: the choice after level 2) as the final nucleus.
+__device__ Nucleus nucleus(const HistPart& hp, const Choice& prev) {
+  const Chosen ch3 = choose(hp, prev, 10);
+  const Choice& c3 = ch3.c;
+  const uint32_t n = ch3.n;
+  const uint64_t f = n ? ch3.f / n : 0ull;  // equal keys, equal masses
   uint32_t t = c3.k_rem;
-  if (f > 0 && c3.m_rem <= mass3[d]) {
+  if (f > 0 && c3.m_rem <= ch3.f) {
     const uint64_t need = (c3.m_rem + f - 1) / f;
     t = need < t ? (uint32_t)need : t;
   }
@@ -362,25 +464,30 @@ __global__ __launch_bounds__(kSThreads) void sample_k4(const SArgs a) {
   __shared__ uint32_t s_t[kSThreads / 64];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const Chunk ch = chunk_of(a, b, w);
-  const float m = seq_max(a, b), c = inv_temp(a, b);
-  const Nucleus nu = nucleus(a, b);
+  float v[kSBatch];
+  load_batch(ch, ch.e0 + t, v);
+  const float wm = load_wmax(a, b);
+  HistPart hp;
+  load_hist_part(a.w.cnt + hist_at(b, 2), a.w.mass + hist_at(b, 2), hp);
+  const Choice prev = choices(a.w)[a.B + b];
+  const float c = inv_temp(a, b);
+  __builtin_amdgcn_sched_barrier(0);
+  const float m = seq_max(wm);
+  const Nucleus nu = nucleus(hp, prev);
   if (w == 0 && t == 0) nuclei(a.w, a.B)[b] = nu;
   uint64_t mg = 0;
   uint32_t ties = 0;
-  for (int e0 = ch.e0 + t; e0 < ch.e1; e0 += 8 * kSThreads) {
-    float v[8];
+  for (int e0 = ch.e0 + t;;) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = e0 + i * kSThreads;
-      v[i] = e < ch.e1 ? ch.row[e] : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kSBatch; ++i) {
       if (e0 + i * kSThreads >= ch.e1) break;
       const uint32_t key = skey(v[i]);
       if (key > nu.tau) mg += fixed_mass(v[i], m, c);
       ties += key == nu.tau;
     }
+    e0 += kSBatch * kSThreads;
+    if (e0 >= ch.e1) break;
+    load_batch(ch, e0, v);
   }
   for (int o = 32; o > 0; o >>= 1) {
     mg += __shfl_xor(mg, o);
@@ -405,10 +512,40 @@ __global__ __launch_bounds__(kSThreads) void sample_k4(const SArgs a) {
 
 // K5: the draw.  r = floor(u * S_kept); the kept tokens in vocabulary order
 // are walked chunk by chunk, then thread by thread, then element by element
-// until their cumulative mass exceeds r.
+// until their cumulative mass exceeds r.  Every workgroup loads its own
+// elements with the per-chunk records (most of them then find that the draw
+// is elsewhere and exit), so the one that holds the draw has its data in
+// registers when it learns so.
 __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  const Chunk ch = chunk_of(a, b, w);
+  // this thread's elements in vocabulary order: [base, end)
+  const int base = ch.e0 + t * ch.E;
+  const int end = min(base + ch.E, ch.e1);
+  const bool in_regs = ch.E <= kSBatch;
+  float v[kSBatch];
+  if (in_regs) {
+    // 16-byte loads where the row is 16-byte aligned (base is a multiple
+    // of 4: chunks are multiples of 1024 and E of 4); otherwise, and for
+    // the vocabulary's last partial quad, element by element
+    const bool vec = ((uintptr_t)ch.row & 15u) == 0;
+#pragma unroll
+    for (int i = 0; i < kSBatch; i += 4) {
+      if (vec && base + i + 3 < end) {
+        const float4 q = *(const float4*)(ch.row + base + i);
+        v[i] = q.x;
+        v[i + 1] = q.y;
+        v[i + 2] = q.z;
+        v[i + 3] = q.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[i + j] = base + i + j < end ? ch.row[base + i + j] : -INFINITY;
+      }
+    }
+  }
   const Nucleus nu = nuclei(a.w, a.B)[b];
+  const float wm = load_wmax(a, b);
+  const float c = inv_temp(a, b);
   // kept mass of every chunk (chunk i keeps its ties while the ties of
   // chunks before it number fewer than nu.ties), and where this chunk's
   // starts; the per-chunk records come in with one load per thread
@@ -418,7 +555,8 @@ __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
     s_wm[t] = t < a.W ? a.w.wmass[(size_t)b * a.W + t] : 0ull;
     s_wt[t] = t < a.W ? a.w.wties[(size_t)b * a.W + t] : 0u;
   }
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  const float m = seq_max(wm);  // (its barrier also publishes s_wm, s_wt)
   uint64_t total = 0, before = 0, mine = 0;
   uint32_t ties_before = 0, tie_acc = 0;
   for (int i = 0; i < a.W; ++i) {
@@ -437,28 +575,29 @@ __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
   uint64_t r = (uint64_t)floor((double)uu * (double)total);
   if (r >= total) r = total - 1;
   if (!(r >= before && r < before + mine)) return;  // the draw is not in this chunk
-  const Chunk ch = chunk_of(a, b, w);
-  const float m = seq_max(a, b), c = inv_temp(a, b);
+  // element j of this thread (vocabulary order), from registers or reloaded
+  auto elem = [&](int j) -> float {
+    if (in_regs) {
+      float x = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kSBatch; ++i) x = i == j ? v[i] : x;
+      return x;
+    }
+    return ch.row[base + j];
+  };
+  const int n_el = end - base;  // may be <= 0 past the vocabulary
   // this thread's ties (key == tau), scanned over the threads in vocabulary
   // order: which of them are kept depends on the ties before it
-  const int base = ch.e0 + t * ch.E;
-  const int end = min(base + ch.E, ch.e1);
-  // this thread's elements, 8 loads in flight at a time
-  auto load8 = [&](int e0, float* v) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = e0 + i < end ? ch.row[e0 + i] : -INFINITY;
-  };
   uint32_t lt = 0;
-  for (int e0 = base; e0 < end; e0 += 8) {
-    float v[8];
-    load8(e0, v);
+  if (in_regs) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lt += e0 + i < end && skey(v[i]) == nu.tau;
+    for (int i = 0; i < kSBatch; ++i) lt += i < n_el && skey(v[i]) == nu.tau;
+  } else {
+    for (int j = 0; j < n_el; ++j) lt += skey(ch.row[base + j]) == nu.tau;
   }
   const uint32_t lt_inc = wg_scan(lt);
-  // its kept mass, then scanned the same way
   const uint32_t tb = ties_before + lt_inc - lt;
-  // mass of element e (in vocabulary order within the thread): kept ties
+  // mass of element l (in vocabulary order within the thread): kept ties
   // are counted by tk
   auto kept_mass = [&](float l, uint32_t& tk) -> uint64_t {
     const uint32_t key = skey(l);
@@ -467,26 +606,22 @@ __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
   };
   uint64_t km = 0;
   uint32_t tk = 0;
-  for (int e0 = base; e0 < end; e0 += 8) {
-    float v[8];
-    load8(e0, v);
+  if (in_regs) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (e0 + i < end) km += kept_mass(v[i], tk);
+    for (int i = 0; i < kSBatch; ++i)
+      if (i < n_el) km += kept_mass(v[i], tk);
+  } else {
+    for (int j = 0; j < n_el; ++j) km += kept_mass(ch.row[base + j], tk);
   }
   const uint64_t excl = before + wg_scan(km) - km;
   if (!(r >= excl && r < excl + km)) return;
   uint64_t acc = excl;
   tk = 0;
-  for (int e0 = base; e0 < end; e0 += 8) {
-    float v[8];
-    load8(e0, v);
-    for (int i = 0; i < 8 && e0 + i < end; ++i) {
-      acc += kept_mass(v[i], tk);
-      if (acc > r) {
-        a.tokens[b] = e0 + i;
-        return;
-      }
+  for (int j = 0; j < n_el; ++j) {
+    acc += kept_mass(elem(j), tk);
+    if (acc > r) {
+      a.tokens[b] = base + j;
+      return;
     }
   }
 }
@@ -500,7 +635,7 @@ SampleWs sample_ws_carve(void* base, int B, int W) {
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return (void*)(p + at); };
   w.cnt = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * 3 * kBuckets);
   w.mass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * 3 * kBuckets);
-  w.sum = (uint64_t*)take(sizeof(uint64_t) * (size_t)B);
+  w.sum = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * W);
   w.choice = (void*)take((size_t)kSampleChoiceBytes * B * 3);
   w.wmax = (float*)take(sizeof(float) * (size_t)B * W);
   w.wmass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * W);
