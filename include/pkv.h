@@ -55,9 +55,8 @@
  *     score product's operand, read 1 KiB per load instruction);
  *   V [PT / 16][num_kv_heads][head_dim][16 slots]: V transposed within a
  *     tile (the value product's operand).
- * With one
- * buffer (kv_pool_create) physical page p starts at base + p * page_bytes
- * with its K block followed by its V block, page_bytes =
+ * With one buffer (kv_pool_create) physical page p starts at
+ * base + p * page_bytes with its K block followed by its V block, page_bytes =
  * 2 * num_kv_heads * PT * head_dim * 2 (32 KiB for 16 tokens of 8 kv heads
  * of width 64, 64 KiB at width 128, 8 KiB for 2 heads of width 64).  With
  * separate K and V pools (kv_pool_create_split, as the three-stage engine

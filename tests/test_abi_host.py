@@ -219,3 +219,22 @@ def test_workspace_sizes_grow_with_batch_and_pages():
     c = L.pkv_workspace_bytes(ctypes.byref(cfg), 64, 128, 16)
     assert 0 < a < b < c
     assert all(x % 256 == 0 for x in (a, b, c))
+
+
+def test_measurement_probes_reject_bad_arguments():
+    """The probes validate like every other entry point, before any HIP
+    call: buffer, alignment, byte count and workgroup count; the paged-read
+    probe takes the attention call's own checks."""
+    assert L.pkv_probe_read(None, 1024, 4, FAKE, None) == EINVAL
+    assert L.pkv_probe_read(FAKE + 4, 1024, 4, FAKE, None) == EINVAL     # not 16-byte aligned
+    assert L.pkv_probe_read(FAKE, 1000, 4, FAKE, None) == EINVAL         # not whole 16-byte chunks
+    assert L.pkv_probe_read(FAKE, 0, 4, FAKE, None) == EINVAL
+    assert L.pkv_probe_read(FAKE, 1024, 0, FAKE, None) == EINVAL
+    assert L.pkv_probe_read(FAKE, 1024, 4, None, None) == EINVAL
+    assert L.pkv_probe_empty(-1, 1, None) == EINVAL
+    assert L.pkv_probe_empty(1, 0, None) == EINVAL
+    pool = _pool()
+    assert L.pkv_probe_paged_read(ctypes.byref(pool), 30, FAKE, 8, FAKE, 4, FAKE, None) == EINVAL  # 30 % 8
+    assert L.pkv_probe_paged_read(ctypes.byref(pool), 32, None, 8, FAKE, 4, FAKE, None) == EINVAL
+    assert L.pkv_probe_paged_read(ctypes.byref(pool), 32, FAKE, 0, FAKE, 4, FAKE, None) == EINVAL
+    assert L.pkv_probe_paged_read(ctypes.byref(pool), 32, FAKE, 8, FAKE, 0, FAKE, None) == 0  # nothing to do
