@@ -13,8 +13,12 @@ compare the HIP path with what it writes, for every sequence of:
   prefill_llama1b_t512  the benchmark's prefill: one 512-token prompt from
                      position 0 through the Llama-3.2-1B-shape model (weights
                      seed 1002, prompt and pool seed 1007)
+  layer_llama8b_b16  one Llama-3-8B-shaped decoder layer (head width 128),
+                     batch 16, contexts U[1,1024] (seed 1010)
 
-What is stored per sequence (a decode step) or for the prompt (prefill):
+What is stored per sequence (a decode step or layer) or for the prompt (prefill):
+  * a layer: its whole output row and the new token's appended K and V (as
+    for a step, one layer);
   * the oracle's argmax and the gap between its two largest logits;
   * the RMS of all logits, and the logits at a fixed sample of indices: the
     16 largest (descending, lower index first among equals) followed by 256
@@ -114,6 +118,48 @@ def step_golden(wl, weights, procs, seqs=None):
     for key in ("token", "gap", "logit_rms"):
         out[key] = np.asarray([r[key] for r in res], np.int32 if key == "token" else np.float64)
     for key in ("logit_idx", "logit_val", "k", "v", "k_rms", "v_rms"):
+        out[key] = np.stack([r[key] for r in res])
+    return out
+
+
+def layer8b_inputs():
+    """One Llama-3-8B-shaped layer (hidden 4096, 32/8 heads of width 128,
+    SwiGLU 14336) at batch 16, positions U[0,1024) (seed 1010): (shape,
+    workload, layer weights, hidden [16][4096])."""
+    shape = synth.LLAMA8B
+    batch, seed = 16, 1010
+    positions = synth.rng(seed, "lens").integers(0, 1024, size=batch).astype(np.int32)
+    wl = synth.decode_workload("d128 8b layer", shape, seed, positions, layers=1)
+    lw = synth.layer_weights(shape, seed, 0)
+    hidden = synth.rng(seed, "hidden").standard_normal((batch, shape.hidden)).astype(np.float32)
+    return shape, wl, lw, hidden
+
+
+_LSTATE = None
+
+
+def _one_layer_sequence(b):
+    shape, wl, lw, hidden = _LSTATE
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
+    out, k_new, v_new = oracle.layer_decode_paged(shape, lw, hidden, wl.pool, geo, wl.block_tables[0],
+                                                  wl.positions, [b])
+    kvi = kv_sample_index(shape.kv_heads * shape.head_dim)
+    return {"out": out[b].astype(np.float32), "k": k_new[b][kvi], "v": v_new[b][kvi],
+            "k_rms": np.float32(rms(oracle.bf16_to_f32(k_new[b]))),
+            "v_rms": np.float32(rms(oracle.bf16_to_f32(v_new[b])))}
+
+
+def layer_golden(shape, wl, lw, hidden, procs):
+    """Oracle outputs of one decoder layer for every sequence."""
+    import multiprocessing as mp
+    global _LSTATE
+    oracle._load()
+    _LSTATE = (shape, wl, lw, hidden)
+    with mp.get_context("fork").Pool(procs) as pool:
+        res = pool.map(_one_layer_sequence, list(range(wl.batch)), chunksize=1)
+    out = {"seqs": np.arange(wl.batch, dtype=np.int32), "kv_idx": kv_sample_index(shape.kv_heads * shape.head_dim),
+           "positions": np.asarray(wl.positions, np.int32)}
+    for key in ("out", "k", "v", "k_rms", "v_rms"):
         out[key] = np.stack([r[key] for r in res])
     return out
 
@@ -228,7 +274,7 @@ def main():
     ap.add_argument("--only", nargs="*", default=None)
     ap.add_argument("--procs", type=int, default=max(1, (os.cpu_count() or 2) - 1))
     args = ap.parse_args()
-    names = list(STEPS) + ["prefill_llama1b_t512"]
+    names = list(STEPS) + ["prefill_llama1b_t512", "layer_llama8b_b16"]
     for name in names:
         if args.only and name not in args.only:
             continue
@@ -239,6 +285,9 @@ def main():
             weights = synth.model_weights(wl.shape, wseed)
             out = step_golden(wl, weights, args.procs)
             del wl
+        elif name == "layer_llama8b_b16":
+            shape, wl, lw, hidden = layer8b_inputs()
+            out = layer_golden(shape, wl, lw, hidden, args.procs)
         else:
             shape, weights, pool, bts, tokens = prefill_inputs()
             out = prefill_golden(shape, weights, pool, bts, 0, tokens, args.procs)

@@ -5,7 +5,9 @@ them, checked on the CPU against the oracle itself:
   * sequences of the stored benchmark step recomputed by the oracle give
     exactly the stored values;
   * every stored file holds every sequence of its workload, and the
-    prefill's stored prompt is the benchmark's."""
+    prefill's stored prompt is the benchmark's;
+  * a sequence of the stored Llama-3-8B-shaped layer recomputed by the
+    oracle gives exactly the stored output and K/V samples."""
 import numpy as np
 import pytest
 
@@ -60,3 +62,14 @@ def test_stored_prefill_prompt_is_the_benchmark_prompt():
     tokens = synth.rng(1007, "prompt").integers(0, synth.LLAMA1B.vocab, size=512).astype(np.int32)
     assert np.array_equal(g["tokens"], tokens) and int(g["start"]) == 0
     assert g["k0"].shape == (512, make_golden.KV_SAMPLES)
+
+
+def test_stored_llama8b_layer_is_the_oracle_output():
+    g = np.load(make_golden.path_of("layer_llama8b_b16"), allow_pickle=False)
+    shape, wl, lw, hidden = make_golden.layer8b_inputs()
+    assert list(g["seqs"]) == list(range(16)) and np.array_equal(g["positions"], wl.positions)
+    assert g["out"].shape == (16, shape.hidden) and g["k"].shape == (16, make_golden.KV_SAMPLES)
+    make_golden._LSTATE = (shape, wl, lw, hidden)
+    r = make_golden._one_layer_sequence(5)
+    for key in ("out", "k", "v", "k_rms", "v_rms"):
+        assert np.array_equal(r[key], g[key][5]), key

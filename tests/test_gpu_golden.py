@@ -23,7 +23,9 @@ and every sequence is compared:
     of the earlier positions (teacher forcing), at the same bar.
 The three steps are the benchmark's (Llama-3.2-1B shape, batch 16, lengths
 U[1,2048]), batch 64 with contexts U[64,2048] (the tiled projections), and
-the 24-layer Qwen2.5-0.5B shape at batch 128 with 4096 cached tokens each."""
+the 24-layer Qwen2.5-0.5B shape at batch 128 with 4096 cached tokens each;
+and one Llama-3-8B-shaped layer (head width 128) at batch 16, every output
+row against the stored oracle output."""
 import os
 
 import numpy as np
@@ -34,7 +36,7 @@ import oracle
 import paged_kv_transformer_amd as pkv
 import synth
 from golden import make_golden
-from gpu_util import check_kv_values, dev, say, teacher_forced_prefill_kv
+from gpu_util import assert_layer_out, check_kv_values, dev, layer_gpu, say, teacher_forced_prefill_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -161,6 +163,30 @@ def test_step_every_sequence_against_stored_oracle(name):
             worst = max(worst, d1, d2)
     say("%s: appended K/V of %d layers x %d sequences, max-abs %.3g at the samples" % (
         name, shape.layers, B, worst))
+
+
+def test_layer_llama8b_every_sequence_against_stored_oracle():
+    """One Llama-3-8B-shaped layer (head width 128), batch 16, contexts
+    U[1,1024]: every sequence's output row against the stored oracle output
+    (max-abs <= 1e-2 RMS(out) and <= 1e-3 RMS(out - hidden)) and its appended
+    K/V at the sample positions (one BF16 ulp or 1e-3 of the vector's RMS)."""
+    gold = _load("layer_llama8b_b16")
+    shape, wl, lw, hidden = make_golden.layer8b_inputs()
+    assert np.array_equal(gold["positions"], wl.positions)
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim)
+    bt = wl.block_tables[0]
+    got, pool_after, err = layer_gpu(shape, lw, hidden, wl.pool, bt, wl.positions)
+    assert err == 0
+    assert_layer_out(got, gold["out"], hidden, "layer %s B=%d (stored oracle)" % (shape.name, wl.batch))
+    sample = gold["kv_idx"].astype(np.int64)
+    worst = 0.0
+    for b in range(wl.batch):
+        ki, vi = appended_index(geo, bt[b], int(wl.positions[b]), sample)
+        worst = max(worst, check_kv_values(pool_after[ki], gold["k"][b], rms=float(gold["k_rms"][b]),
+                                           what="8b layer K seq %d" % b)[0])
+        worst = max(worst, check_kv_values(pool_after[vi], gold["v"][b], rms=float(gold["v_rms"][b]),
+                                           what="8b layer V seq %d" % b)[0])
+    say("8b layer: appended K/V of %d sequences, max-abs %.3g at the samples" % (wl.batch, worst))
 
 
 def test_prefill_512_against_stored_oracle():

@@ -175,7 +175,9 @@ def test_layer_d128_tiny_shapes(batch, hkv, heads):
 
 def test_layer_d128_llama8b_shape_sampled():
     """One Llama-3-8B-shaped layer (hidden 4096, 32/8 heads of 128, SwiGLU
-    14336), batch 16, contexts U[1,1024]; four sequences against the oracle."""
+    14336), batch 16, contexts U[1,1024]; four sequences against the oracle
+    computed here (every sequence is compared with the stored oracle outputs
+    in test_gpu_golden.py)."""
     shape = synth.LLAMA8B
     batch, seed = 16, 1010
     positions = synth.rng(seed, "lens").integers(0, 1024, size=batch).astype(np.int32)
