@@ -889,7 +889,7 @@ size_t pkv_sample_workspace_bytes(int32_t batch, int32_t vocab) {
   if (batch < 1 || vocab < 1 || batch > 65535) return 0;
   int chunk;
   const int W = sample_chunks(batch, vocab, &chunk);
-  return sample_ws_carve(nullptr, batch, W).bytes;
+  return sample_ws_carve(nullptr, batch, W, chunk).bytes;
 }
 
 int sample_tokens(const float* logits, int32_t batch, int32_t vocab, const float* temperature,
@@ -903,7 +903,7 @@ int sample_tokens(const float* logits, int32_t batch, int32_t vocab, const float
   if (ws_bytes < pkv_sample_workspace_bytes(batch, vocab)) return -ENOSPC;
   int chunk;
   const int W = sample_chunks(batch, vocab, &chunk);
-  const SampleWs ws = sample_ws_carve(workspace, batch, W);
+  const SampleWs ws = sample_ws_carve(workspace, batch, W, chunk);
   return io(launch_sample(logits, batch, vocab, temperature, top_p, top_k, u, tokens, ws, W, chunk,
                           (hipStream_t)stream));
 }

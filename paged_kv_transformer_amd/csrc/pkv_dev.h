@@ -310,20 +310,22 @@ inline int qkv_splits(const PgemmPlan& p, int K) {
 }
 
 // Sampling after the LM head: per-sequence workspace of the radix select
-// (three levels of 2048-bucket count and fixed-point mass histograms), the
-// choice records passed between its launches, and per-chunk partials.
+// (the first level's 2048-bucket count and fixed-point mass histograms, the
+// tokens of the bucket it chooses, which the later levels select from), the
+// choice record passed between its launches, and per-chunk partials.
 constexpr int kSampleChoiceBytes = 24;
 struct SampleWs {
-  uint32_t* cnt;      // [B][3][2048]
-  uint64_t* mass;     // [B][3][2048]
+  uint32_t* cnt;      // [B][2048] first-level token counts
+  uint64_t* mass;     // [B][2048] first-level masses
   uint64_t* sum;      // [B][W] the softmax normaliser's per-chunk parts (fixed point)
-  void* choice;       // [3][B] records: choices after levels 1, 2; the nucleus
+  void* choice;       // [B] records: the choice after the first level
   float* wmax;        // [B][W] chunk maxima
-  uint64_t* wmass;    // [B][W] chunk mass above the threshold
-  uint32_t* wties;    // [B][W] chunk ties at the threshold
+  uint64_t* wmass;    // [B][W] chunk mass above the chosen first-level bucket
+  uint32_t* ncand;    // [B][W] per chunk, its tokens in the chosen first-level bucket
+  uint32_t* cand;     // [B][W][chunk][2] their (key, vocabulary index), per chunk
   size_t bytes;
 };
-SampleWs sample_ws_carve(void* base, int B, int W);
+SampleWs sample_ws_carve(void* base, int B, int W, int chunk);
 // workgroups per sequence for B sequences of V logits; *chunk = logits each
 int sample_chunks(int B, int V, int* chunk);
 hipError_t launch_sample(const float* logits, int B, int V, const float* temperature,

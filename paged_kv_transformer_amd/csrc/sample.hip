@@ -21,22 +21,28 @@
 //
 // A batch of B sequences runs on B x W workgroups, each taking one chunk of
 // the vocabulary (the logits of a 16-sequence batch are 8 MB, and one
-// workgroup per sequence would leave most of the chip idle).  Workgroups
-// never wait on each other; the six launches are:
-//   K0 chunk maxima                       (and clears the level-1 sums)
-//   K1 normaliser + level-1 histogram     (clears level 2)
-//   K2 level-1 choice + level-2 histogram (clears level 3)
-//   K3 level-2 choice + level-3 histogram
-//   K4 level-3 choice (threshold key, ties kept) + per-chunk kept mass
-//   K5 the draw: the chunk holding u, then the token inside it
-// Each choice is made by every workgroup alike and stored by workgroup 0 of
-// the sequence for the next launch.
+// workgroup per sequence would leave most of the chip idle), until the
+// first level has chosen its bucket; each chunk then writes its tokens in
+// that bucket (a few thousand per sequence) to its own segment of a
+// per-sequence candidate list, and one 1024-thread workgroup per sequence
+// finishes from the list.  Workgroups never wait on each other; the four
+// launches are:
+//   K0 chunk maxima                  (clears the first-level histogram)
+//   K1 normaliser + first-level histogram
+//   K2 first-level choice; per chunk, the mass above the chosen bucket, and
+//      the bucket's tokens written to the chunk's segment of the list
+//   K3 per sequence: the second and third levels over the candidates (the
+//      threshold key and how many of its ties are kept), each chunk's kept
+//      mass, and the draw: the chunk holding u, then the token inside it
+// The first-level choice is made by every workgroup of K2 alike and stored
+// by workgroup 0 of the sequence for K3.
 #include "pkv_dev.h"
 
 namespace pkv {
 namespace {
 
 constexpr int kSThreads = 256;
+constexpr int kFThreads = 1024;  // the finishing launch: one workgroup per sequence
 constexpr int kBuckets = 2048;
 constexpr float kLog2eS = 1.4426950408889634f;
 
@@ -104,12 +110,13 @@ struct Chunk {
   int e0, e1, E;
 };
 
+template <int NT = kSThreads>
 __device__ __forceinline__ Chunk chunk_of(const SArgs& a, int b, int w) {
   Chunk c;
   c.row = a.logits + (size_t)b * a.V;
   c.e0 = w * a.chunk;
   c.e1 = min(a.V, c.e0 + a.chunk);
-  c.E = a.chunk / kSThreads;
+  c.E = a.chunk / NT;
   return c;
 }
 
@@ -135,23 +142,73 @@ __device__ __forceinline__ void clear_words(uint32_t* p, int n, int w, int W) {
   for (int i = w * kSThreads + (int)threadIdx.x; i < n; i += W * kSThreads) p[i] = 0u;
 }
 
-// Inclusive scan over the workgroup's threads in thread order: within a
-// wave by shuffles, then the sums of the waves before (one barrier pair).
+// Inclusive scan over a wave's 64 lanes by data-parallel-primitive moves:
+// within each 16-lane row by shifts of 1, 2, 4 and 8 lanes (lanes shifted
+// in from outside the row read 0), then lane 15's sum into rows 1 and 3 and
+// lane 31's into rows 2 and 3.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_z(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, true);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_z(uint64_t v) {
+  const uint32_t lo = dpp_z<CTRL, ROW_MASK>((uint32_t)v);
+  const uint32_t hi = dpp_z<CTRL, ROW_MASK>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
 template <typename T>
+__device__ __forceinline__ T wave_scan(T v) {
+  v += dpp_z<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_z<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_z<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_z<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_z<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp_z<0x143, 0xc>(v);  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ uint64_t lane63(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive scan over the workgroup's threads in thread order: within each
+// wave, then the sums of the waves before (one barrier pair).
+template <typename T, int NT = kSThreads>
 __device__ __forceinline__ T wg_scan(T v) {
-  __shared__ T s_wave[kSThreads / 64];
+  __shared__ T s_wave[NT / 64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
+  v = wave_scan(v);
   if (lane == 63) s_wave[wv] = v;
   __syncthreads();
   T add = 0;
   for (int i = 0; i < wv; ++i) add += s_wave[i];
   __syncthreads();
   return v + add;
+}
+
+// The same for a (count, mass) pair, sharing the barriers.
+template <int NT>
+__device__ __forceinline__ void wg_scan2(uint32_t& c, uint64_t& m) {
+  __shared__ uint32_t s_c[NT / 64];
+  __shared__ uint64_t s_m[NT / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  c = wave_scan(c);
+  m = wave_scan(m);
+  if (lane == 63) {
+    s_c[wv] = c;
+    s_m[wv] = m;
+  }
+  __syncthreads();
+  uint32_t ac = 0;
+  uint64_t am = 0;
+  for (int i = 0; i < wv; ++i) {
+    ac += s_c[i];
+    am += s_m[i];
+  }
+  __syncthreads();
+  c += ac;
+  m += am;
 }
 
 // ---- per-sequence choice state, stored between launches
@@ -165,21 +222,25 @@ static_assert(sizeof(Choice) == kSampleChoiceBytes, "choice record size");
 
 __device__ __forceinline__ Choice* choices(const SampleWs& w) { return (Choice*)w.choice; }
 
-// Level L's global histogram of sequence b.
-__device__ __forceinline__ size_t hist_at(int b, int level) { return ((size_t)b * 3 + level) * kBuckets; }
+// The first-level histogram of sequence b.
+__device__ __forceinline__ size_t hist_at(int b) { return (size_t)b * kBuckets; }
 
-// A thread's share of a histogram for choose(): the 8 buckets from
-// top = 2047 - 8t downwards, loaded together.
-constexpr int kPer = kBuckets / kSThreads;
-struct HistPart {
-  uint32_t cnt[kPer];
-  uint64_t mass[kPer];
+// A thread's share of a histogram for choose(): the kBuckets / NT buckets
+// from top = 2047 - (kBuckets / NT) t downwards, loaded together.
+template <int NT>
+struct HistPartT {
+  static constexpr int P = kBuckets / NT;
+  uint32_t cnt[P];
+  uint64_t mass[P];
 };
+using HistPart = HistPartT<kSThreads>;
 
-__device__ __forceinline__ void load_hist_part(const uint32_t* cnt, const uint64_t* mass, HistPart& h) {
-  const int top = kBuckets - 1 - kPer * (int)threadIdx.x;
+template <int NT>
+__device__ __forceinline__ void load_hist_part(const uint32_t* cnt, const uint64_t* mass, HistPartT<NT>& h) {
+  constexpr int P = HistPartT<NT>::P;
+  const int top = kBuckets - 1 - P * (int)threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  for (int i = 0; i < P; ++i) {
     h.cnt[i] = cnt[top - i];
     h.mass[i] = mass[top - i];
   }
@@ -196,7 +257,9 @@ struct Chosen {
 // count reaches k_rem or the mass reaches m_rem; update the choice.  Every
 // thread of the workgroup calls it with its HistPart and gets the same
 // result.
-__device__ Chosen choose(const HistPart& h, Choice c, int bits) {
+template <int NT>
+__device__ __forceinline__ Chosen choose(const HistPartT<NT>& h, Choice c, int bits) {
+  constexpr int kPer = HistPartT<NT>::P;
   __shared__ Chosen s_out;
   const int t = threadIdx.x;
   const int top = kBuckets - 1 - kPer * t;
@@ -213,17 +276,22 @@ __device__ Chosen choose(const HistPart& h, Choice c, int bits) {
     lm += h.mass[i];
   }
   // inclusive scans over threads (thread order = descending buckets)
-  const uint32_t inc_c = wg_scan(lc);
-  const uint64_t inc_m = wg_scan(lm);
+  uint32_t inc_c = lc;
+  uint64_t inc_m = lm;
+  wg_scan2<NT>(inc_c, inc_m);
   const uint32_t exc_c = inc_c - lc;
   const uint64_t exc_m = inc_m - lm;
   const bool before = exc_c >= c.k_rem || exc_m >= c.m_rem;
   const bool after = inc_c >= c.k_rem || inc_m >= c.m_rem;
   if (!before && after) {
+    // unrolled with constant indices, so the thread's part stays in
+    // registers
     uint32_t cc = exc_c;
     uint64_t cm = exc_m;
+    bool found = false;
+#pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      if (cc + h.cnt[i] >= c.k_rem || cm + h.mass[i] >= c.m_rem) {
+      if (!found && (cc + h.cnt[i] >= c.k_rem || cm + h.mass[i] >= c.m_rem)) {
         Chosen o;
         o.c.prefix = (c.prefix << bits) | (uint32_t)(top - i);
         o.c.k_rem = c.k_rem - cc;
@@ -232,7 +300,7 @@ __device__ Chosen choose(const HistPart& h, Choice c, int bits) {
         o.n = h.cnt[i];
         o.f = h.mass[i];
         s_out = o;
-        break;
+        found = true;
       }
       cc += h.cnt[i];
       cm += h.mass[i];
@@ -346,8 +414,8 @@ __global__ __launch_bounds__(kSThreads) void sample_k0(const SArgs a) {
     for (int i = 1; i < kSThreads / 64; ++i) r = fmaxf(r, red[i]);
     a.w.wmax[(size_t)b * a.W + w] = r;
   }
-  clear_words((uint32_t*)(a.w.cnt + hist_at(b, 0)), kBuckets, w, a.W);
-  clear_words((uint32_t*)(a.w.mass + hist_at(b, 0)), 2 * kBuckets, w, a.W);
+  clear_words(a.w.cnt + hist_at(b), kBuckets, w, a.W);
+  clear_words((uint32_t*)(a.w.mass + hist_at(b)), 2 * kBuckets, w, a.W);
 }
 
 __global__ __launch_bounds__(kSThreads) void sample_k1(const SArgs a) {
@@ -359,10 +427,8 @@ __global__ __launch_bounds__(kSThreads) void sample_k1(const SArgs a) {
   const float c = inv_temp(a, b);
   __builtin_amdgcn_sched_barrier(0);
   const float m = seq_max(wm);
-  histogram(ch, v, 0, 0u, m, c, !mass_only(a, b), a.w.cnt + hist_at(b, 0), a.w.mass + hist_at(b, 0),
+  histogram(ch, v, 0, 0u, m, c, !mass_only(a, b), a.w.cnt + hist_at(b), a.w.mass + hist_at(b),
             a.w.sum + (size_t)b * a.W + w);
-  clear_words((uint32_t*)(a.w.cnt + hist_at(b, 1)), kBuckets, w, a.W);
-  clear_words((uint32_t*)(a.w.mass + hist_at(b, 1)), 2 * kBuckets, w, a.W);
 }
 
 // The choice before level 0: the count and mass budgets of the nucleus.
@@ -384,44 +450,76 @@ __device__ Choice initial_choice(const SArgs& a, int b, uint64_t sum) {
   return c;
 }
 
+// The logit an order-preserving key was made from (-0 comes back as +0,
+// an equal logit of the same mass).
+__device__ __forceinline__ float key_logit(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// K2: the first-level choice; this chunk's mass above the chosen bucket
+// and its tokens inside the bucket (its candidates), both stored for K3:
+// the candidates in the chunk's own segment of the sequence's list, with
+// their number.
 __global__ __launch_bounds__(kSThreads) void sample_k2(const SArgs a) {
-  const int b = blockIdx.y, w = blockIdx.x;
+  __shared__ uint64_t s_m[kSThreads / 64];
+  __shared__ uint32_t s_tot;
+  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const Chunk ch = chunk_of(a, b, w);
   float v[kSBatch];
-  load_batch(ch, ch.e0 + (int)threadIdx.x, v);
+  load_batch(ch, ch.e0 + t, v);
   const float wm = load_wmax(a, b);
   HistPart hp;
-  load_hist_part(a.w.cnt + hist_at(b, 0), a.w.mass + hist_at(b, 0), hp);
-  const int t = threadIdx.x;
+  load_hist_part(a.w.cnt + hist_at(b), a.w.mass + hist_at(b), hp);
   const uint64_t sum_part = t < 64 && t < a.W ? a.w.sum[(size_t)b * a.W + t] : 0ull;
   const float c = inv_temp(a, b);
   __builtin_amdgcn_sched_barrier(0);
   const float m = seq_max(wm);
   const uint64_t sum = seq_sum(sum_part);
-  const Choice c1 = choose(hp, initial_choice(a, b, sum), 11).c;
-  if (w == 0 && threadIdx.x == 0) choices(a.w)[b] = c1;
-  histogram(ch, v, 1, c1.prefix, m, c, !mass_only(a, b), a.w.cnt + hist_at(b, 1),
-            a.w.mass + hist_at(b, 1), nullptr);
-  clear_words((uint32_t*)(a.w.cnt + hist_at(b, 2)), kBuckets, w, a.W);
-  clear_words((uint32_t*)(a.w.mass + hist_at(b, 2)), 2 * kBuckets, w, a.W);
-}
-
-__global__ __launch_bounds__(kSThreads) void sample_k3(const SArgs a) {
-  const int b = blockIdx.y, w = blockIdx.x;
-  const Chunk ch = chunk_of(a, b, w);
-  float v[kSBatch];
-  load_batch(ch, ch.e0 + (int)threadIdx.x, v);
-  const float wm = load_wmax(a, b);
-  HistPart hp;
-  load_hist_part(a.w.cnt + hist_at(b, 1), a.w.mass + hist_at(b, 1), hp);
-  const Choice prev = choices(a.w)[b];
-  const float c = inv_temp(a, b);
-  __builtin_amdgcn_sched_barrier(0);
-  const float m = seq_max(wm);
-  const Choice c2 = choose(hp, prev, 11).c;
-  if (w == 0 && threadIdx.x == 0) choices(a.w)[a.B + b] = c2;
-  histogram(ch, v, 2, c2.prefix, m, c, true, a.w.cnt + hist_at(b, 2),
-            a.w.mass + hist_at(b, 2), nullptr);
+  const Choice c1 = choose<kSThreads>(hp, initial_choice(a, b, sum), 11).c;
+  if (w == 0 && t == 0) choices(a.w)[b] = c1;
+  uint32_t* seg = a.w.cand + 2 * ((size_t)b * a.W + w) * a.chunk;
+  uint32_t nseg = 0;
+  uint64_t above = 0;
+  // batches start at the same element offset in every thread, so every
+  // thread takes the same number of trips through the scan's barriers
+  for (int base = ch.e0;;) {
+    const int e0 = base + t;
+    uint32_t mine = 0;  // bit i: element e0 + 256 i is a candidate
+#pragma unroll
+    for (int i = 0; i < kSBatch; ++i) {
+      if (e0 + i * kSThreads < ch.e1) {
+        const uint32_t top = skey(v[i]) >> 21;
+        if (top > c1.prefix) above += fixed_mass(v[i], m, c);
+        mine |= (top == c1.prefix ? 1u : 0u) << i;
+      }
+    }
+    const uint32_t n = (uint32_t)__builtin_popcount(mine);
+    const uint32_t inc = wg_scan(n);
+    uint32_t slot = nseg + inc - n;
+#pragma unroll
+    for (int i = 0; i < kSBatch; ++i) {
+      if (((mine >> i) & 1u) && slot < (uint32_t)a.chunk) {  // (a chunk's tokens fit its segment)
+        *(uint2*)(seg + 2 * (size_t)slot) = make_uint2(skey(v[i]), (uint32_t)(e0 + i * kSThreads));
+        ++slot;
+      }
+    }
+    if (t == kSThreads - 1) s_tot = inc;
+    __syncthreads();
+    nseg += s_tot;
+    base += kSBatch * kSThreads;
+    if (base >= ch.e1) break;
+    __syncthreads();  // s_tot is rewritten by the next batch
+    load_batch(ch, base + t, v);
+  }
+  for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o);
+  if ((t & 63) == 0) s_m[t >> 6] = above;
+  __syncthreads();
+  if (t == 0) {
+    uint64_t sm = 0;
+    for (int i = 0; i < kSThreads / 64; ++i) sm += s_m[i];
+    a.w.wmass[(size_t)b * a.W + w] = sm;
+    a.w.ncand[(size_t)b * a.W + w] = min(nseg, (uint32_t)a.chunk);
+  }
 }
 
 // The nucleus, final: every token with key > tau, and the first `ties`
@@ -430,18 +528,12 @@ struct Nucleus {
   uint32_t tau, ties;
   uint64_t f_tau, m_above;
 };
-static_assert(sizeof(Nucleus) <= kSampleChoiceBytes, "nucleus record size");
 
-// K4 stores each sequence's nucleus for K5, in the third third of the
-// choice records ([3][B] records of kSampleChoiceBytes).
-__device__ __forceinline__ Nucleus* nuclei(const SampleWs& w, int B) {
-  return (Nucleus*)((char*)w.choice + (size_t)2 * B * kSampleChoiceBytes);
-}
-
-// The level-3 choice (hp: the thread's part of the level-3 histogram,
-// prev: the choice after level 2) as the final nucleus.
-__device__ Nucleus nucleus(const HistPart& hp, const Choice& prev) {
-  const Chosen ch3 = choose(hp, prev, 10);
+// The last level's choice (hp: the thread's part of the last level's
+// histogram, prev: the choice before it) as the final nucleus.
+template <int NT>
+__device__ __forceinline__ Nucleus nucleus(const HistPartT<NT>& hp, const Choice& prev) {
+  const Chosen ch3 = choose<NT>(hp, prev, 10);
   const Choice& c3 = ch3.c;
   const uint32_t n = ch3.n;
   const uint64_t f = n ? ch3.f / n : 0ull;  // equal keys, equal masses
@@ -458,123 +550,143 @@ __device__ Nucleus nucleus(const HistPart& hp, const Choice& prev) {
   return r;
 }
 
-// K4: per chunk, the mass of its tokens above tau and its count of ties.
-__global__ __launch_bounds__(kSThreads) void sample_k4(const SArgs a) {
-  __shared__ uint64_t s_m[kSThreads / 64];
-  __shared__ uint32_t s_t[kSThreads / 64];
-  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
-  const Chunk ch = chunk_of(a, b, w);
-  float v[kSBatch];
-  load_batch(ch, ch.e0 + t, v);
-  const float wm = load_wmax(a, b);
-  HistPart hp;
-  load_hist_part(a.w.cnt + hist_at(b, 2), a.w.mass + hist_at(b, 2), hp);
-  const Choice prev = choices(a.w)[a.B + b];
-  const float c = inv_temp(a, b);
-  __builtin_amdgcn_sched_barrier(0);
-  const float m = seq_max(wm);
-  const Nucleus nu = nucleus(hp, prev);
-  if (w == 0 && t == 0) nuclei(a.w, a.B)[b] = nu;
-  uint64_t mg = 0;
-  uint32_t ties = 0;
-  for (int e0 = ch.e0 + t;;) {
+// A sequence's candidates as K3 sees them: the list is the chunks'
+// segments one after another (entry j lies in the segment s with off[s] <=
+// j < off[s + 1]).  Thread t holds the q consecutive entries from j0 = t q
+// in registers, loaded once; a list longer than 256 kCandRegs entries has
+// its remainder read again, in batches, by every pass that walks it.
+constexpr int kCandRegs = 8;
+struct CandList {
+  const uint32_t* p;    // the sequence's segments, [W][chunk][2] (key, index)
+  const uint32_t* off;  // LDS: segment starts, off[W] = n
+  int W, chunk;
+  uint32_t n, q, j0;
+  uint32_t key[kCandRegs], idx[kCandRegs];
+};
+
+// The segment holding entry j < n: the last s with off[s] <= j.
+__device__ __forceinline__ int seg_of(const CandList& L, uint32_t j) {
+  int s = 0;
 #pragma unroll
-    for (int i = 0; i < kSBatch; ++i) {
-      if (e0 + i * kSThreads >= ch.e1) break;
-      const uint32_t key = skey(v[i]);
-      if (key > nu.tau) mg += fixed_mass(v[i], m, c);
-      ties += key == nu.tau;
+  for (int step = 32; step > 0; step >>= 1)
+    if (s + step < L.W && L.off[s + step] <= j) s += step;
+  return s;
+}
+
+__device__ __forceinline__ uint2 cand_entry(const CandList& L, int s, uint32_t j) {
+  return *(const uint2*)(L.p + 2 * ((size_t)s * L.chunk + (j - L.off[s])));
+}
+
+__device__ __forceinline__ void load_cands(CandList& L) {
+  const uint32_t t = threadIdx.x;
+  L.q = (L.n + kFThreads - 1) / kFThreads;
+  if (L.q > (uint32_t)kCandRegs) L.q = kCandRegs;
+  L.j0 = t * L.q;
+  int s = L.j0 < L.n ? seg_of(L, L.j0) : 0;
+  uint32_t next = L.off[s + 1];  // where segment s ends
+#pragma unroll
+  for (int i = 0; i < kCandRegs; ++i) {
+    const uint32_t j = L.j0 + (uint32_t)i;
+    L.key[i] = 0u;
+    L.idx[i] = 0u;
+    if ((uint32_t)i < L.q && j < L.n) {
+      while (next <= j) next = L.off[++s + 1];  // skips empty segments
+      const uint2 e = cand_entry(L, s, j);
+      L.key[i] = e.x;
+      L.idx[i] = e.y;
     }
-    e0 += kSBatch * kSThreads;
-    if (e0 >= ch.e1) break;
-    load_batch(ch, e0, v);
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    mg += __shfl_xor(mg, o);
-    ties += __shfl_xor(ties, o);
-  }
-  if ((t & 63) == 0) {
-    s_m[t >> 6] = mg;
-    s_t[t >> 6] = ties;
-  }
-  __syncthreads();
-  if (t == 0) {
-    uint64_t sm = 0;
-    uint32_t st = 0;
-    for (int i = 0; i < kSThreads / 64; ++i) {
-      sm += s_m[i];
-      st += s_t[i];
-    }
-    a.w.wmass[(size_t)b * a.W + w] = sm;
-    a.w.wties[(size_t)b * a.W + w] = st;
   }
 }
 
-// K5: the draw.  r = floor(u * S_kept); the kept tokens in vocabulary order
-// are walked chunk by chunk, then thread by thread, then element by element
-// until their cumulative mass exceeds r.  Every workgroup loads its own
-// elements with the per-chunk records (most of them then find that the draw
-// is elsewhere and exit), so the one that holds the draw has its data in
-// registers when it learns so.
-__global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
-  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
-  const Chunk ch = chunk_of(a, b, w);
-  // this thread's elements in vocabulary order: [base, end)
+// The chunk of vocabulary index idx (chunks of `chunk` logits; inv =
+// 1 / chunk): a double-precision estimate, off by at most one, corrected.
+__device__ __forceinline__ int chunk_index(uint32_t idx, uint32_t chunk, double inv) {
+  int w = (int)((double)idx * inv);
+  if ((uint32_t)(w + 1) * chunk <= idx)
+    ++w;
+  else if ((uint32_t)w * chunk > idx)
+    --w;
+  return w;
+}
+
+// Calls f(key, index) for each of this thread's candidates.
+template <typename F>
+__device__ __forceinline__ void each_cand(const CandList& L, F f) {
+  const uint32_t t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kCandRegs; ++i)
+    if ((uint32_t)i < L.q && L.j0 + (uint32_t)i < L.n) f(L.key[i], L.idx[i]);
+  for (uint32_t b0 = (uint32_t)kCandRegs * kFThreads; b0 < L.n; b0 += (uint32_t)kSBatch * kFThreads) {
+    uint2 e[kSBatch];
+#pragma unroll
+    for (int i = 0; i < kSBatch; ++i) {
+      const uint32_t j = b0 + t + (uint32_t)i * kFThreads;
+      e[i] = j < L.n ? cand_entry(L, seg_of(L, j), j) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < kSBatch; ++i)
+      if (b0 + t + (uint32_t)i * kFThreads < L.n) f(e[i].x, e[i].y);
+  }
+}
+
+// A histogram of one level over the candidates whose key agrees with
+// `prefix` above the level's digit, in LDS (zeroed by the caller), then the
+// thread's part of it for choose().
+__device__ __forceinline__ void cand_level(const CandList& L, int level, uint32_t prefix, float m, float c, bool counts,
+                           uint32_t* h_cnt, uint64_t* h_mass, HistPartT<kFThreads>& hp) {
+  each_cand(L, [&](uint32_t key, uint32_t) {
+    if (in_prefix(key, level, prefix)) {
+      const int d = digit(key, level);
+      if (counts) atomicAdd(&h_cnt[d], 1u);
+      atomicAdd((unsigned long long*)&h_mass[d], (unsigned long long)fixed_mass(key_logit(key), m, c));
+    }
+  });
+  __syncthreads();
+  load_hist_part(h_cnt, h_mass, hp);
+}
+
+__device__ __forceinline__ void zero_hist(uint32_t* h_cnt, uint64_t* h_mass) {
+  for (int i = threadIdx.x; i < kBuckets; i += kFThreads) {
+    h_cnt[i] = 0u;
+    h_mass[i] = 0ull;
+  }
+}
+
+// Thread t's E consecutive elements of the chunk from e0 + t E, when E <=
+// kSBatch: 16-byte loads where the row is 16-byte aligned (the first is a
+// multiple of 4: chunks are multiples of 1024 and E of 4); otherwise, and
+// for the vocabulary's last partial quad, element by element.
+__device__ __forceinline__ void load_run(const Chunk& ch, float (&v)[kSBatch]) {
+  const int base = ch.e0 + (int)threadIdx.x * ch.E;
+  const int end = min(base + ch.E, ch.e1);
+  const bool vec = ((uintptr_t)ch.row & 15u) == 0;
+#pragma unroll
+  for (int i = 0; i < kSBatch; i += 4) {
+    if (vec && base + i + 3 < end) {
+      const float4 q = *(const float4*)(ch.row + base + i);
+      v[i] = q.x;
+      v[i + 1] = q.y;
+      v[i + 2] = q.z;
+      v[i + 3] = q.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[i + j] = base + i + j < end ? ch.row[base + i + j] : -INFINITY;
+    }
+  }
+}
+
+// The draw inside chunk ch of sequence b, which holds it: r in [before,
+// before + the chunk's kept mass); ties_before = ties (key == tau) in the
+// chunks before; v = load_run(ch) when E <= kSBatch.  The chunk's kept
+// tokens are walked in vocabulary order, thread by thread (thread t takes
+// the E consecutive elements from e0 + t E), then element by element, until
+// their cumulative mass exceeds r.
+__device__ __forceinline__ void draw_in_chunk(const SArgs& a, int b, const Chunk& ch, const Nucleus& nu, uint64_t before,
+                              uint32_t ties_before, uint64_t r, float m, float c, const float (&v)[kSBatch]) {
+  const int t = threadIdx.x;
   const int base = ch.e0 + t * ch.E;
   const int end = min(base + ch.E, ch.e1);
   const bool in_regs = ch.E <= kSBatch;
-  float v[kSBatch];
-  if (in_regs) {
-    // 16-byte loads where the row is 16-byte aligned (base is a multiple
-    // of 4: chunks are multiples of 1024 and E of 4); otherwise, and for
-    // the vocabulary's last partial quad, element by element
-    const bool vec = ((uintptr_t)ch.row & 15u) == 0;
-#pragma unroll
-    for (int i = 0; i < kSBatch; i += 4) {
-      if (vec && base + i + 3 < end) {
-        const float4 q = *(const float4*)(ch.row + base + i);
-        v[i] = q.x;
-        v[i + 1] = q.y;
-        v[i + 2] = q.z;
-        v[i + 3] = q.w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[i + j] = base + i + j < end ? ch.row[base + i + j] : -INFINITY;
-      }
-    }
-  }
-  const Nucleus nu = nuclei(a.w, a.B)[b];
-  const float wm = load_wmax(a, b);
-  const float c = inv_temp(a, b);
-  // kept mass of every chunk (chunk i keeps its ties while the ties of
-  // chunks before it number fewer than nu.ties), and where this chunk's
-  // starts; the per-chunk records come in with one load per thread
-  __shared__ uint64_t s_wm[64];
-  __shared__ uint32_t s_wt[64];
-  if (t < 64) {
-    s_wm[t] = t < a.W ? a.w.wmass[(size_t)b * a.W + t] : 0ull;
-    s_wt[t] = t < a.W ? a.w.wties[(size_t)b * a.W + t] : 0u;
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  const float m = seq_max(wm);  // (its barrier also publishes s_wm, s_wt)
-  uint64_t total = 0, before = 0, mine = 0;
-  uint32_t ties_before = 0, tie_acc = 0;
-  for (int i = 0; i < a.W; ++i) {
-    const uint32_t ti = s_wt[i];
-    const uint32_t kt = tie_acc >= nu.ties ? 0u : min(ti, nu.ties - tie_acc);
-    const uint64_t km = s_wm[i] + (uint64_t)kt * nu.f_tau;
-    if (i < w) {
-      before += km;
-      ties_before += ti;
-    }
-    if (i == w) mine = km;
-    total += km;
-    tie_acc += ti;
-  }
-  const float uu = fminf(fmaxf(a.u[b], 0.f), 1.f);
-  uint64_t r = (uint64_t)floor((double)uu * (double)total);
-  if (r >= total) r = total - 1;
-  if (!(r >= before && r < before + mine)) return;  // the draw is not in this chunk
   // element j of this thread (vocabulary order), from registers or reloaded
   auto elem = [&](int j) -> float {
     if (in_regs) {
@@ -595,7 +707,7 @@ __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
   } else {
     for (int j = 0; j < n_el; ++j) lt += skey(ch.row[base + j]) == nu.tau;
   }
-  const uint32_t lt_inc = wg_scan(lt);
+  const uint32_t lt_inc = wg_scan<uint32_t, kFThreads>(lt);
   const uint32_t tb = ties_before + lt_inc - lt;
   // mass of element l (in vocabulary order within the thread): kept ties
   // are counted by tk
@@ -613,7 +725,7 @@ __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
   } else {
     for (int j = 0; j < n_el; ++j) km += kept_mass(ch.row[base + j], tk);
   }
-  const uint64_t excl = before + wg_scan(km) - km;
+  const uint64_t excl = before + wg_scan<uint64_t, kFThreads>(km) - km;
   if (!(r >= excl && r < excl + km)) return;
   uint64_t acc = excl;
   tk = 0;
@@ -626,20 +738,124 @@ __global__ __launch_bounds__(kSThreads) void sample_k5(const SArgs a) {
   }
 }
 
+// K3, one workgroup per sequence: the second and third levels over the
+// candidates, the nucleus, each chunk's kept mass (K2's mass above the
+// bucket, the candidates above the threshold key, its kept ties in chunk
+// order), then r = floor(u * S_kept) and the draw in the chunk holding r.
+__global__ __launch_bounds__(kFThreads) void sample_k3(const SArgs a) {
+  __shared__ uint32_t h_cnt[kBuckets];
+  __shared__ uint64_t h_mass[kBuckets];
+  __shared__ uint32_t s_off[65];
+  __shared__ uint64_t s_km[64];  // per chunk: candidates' mass above tau, then the chunk's kept mass
+  __shared__ uint32_t s_kt[64];  // per chunk: ties (key == tau)
+  const int b = blockIdx.x, t = threadIdx.x;
+  const uint32_t n_seg = t < a.W ? a.w.ncand[(size_t)b * a.W + t] : 0u;
+  const Choice c1 = choices(a.w)[b];
+  const float wm = load_wmax(a, b);
+  const uint64_t above = t < 64 && t < a.W ? a.w.wmass[(size_t)b * a.W + t] : 0ull;
+  const float c = inv_temp(a, b);
+  __builtin_amdgcn_sched_barrier(0);
+  zero_hist(h_cnt, h_mass);
+  if (t < 64) {
+    // the segment starts: an inclusive scan of the counts over wave 0
+    s_off[t + 1] = wave_scan(n_seg);
+    if (t == 0) s_off[0] = 0u;
+    s_km[t] = 0ull;
+    s_kt[t] = 0u;
+  }
+  const float m = seq_max(wm);  // (its barrier also publishes the LDS above)
+  CandList L;
+  L.p = a.w.cand + 2 * (size_t)b * a.W * a.chunk;
+  L.off = s_off;
+  L.W = a.W;
+  L.chunk = a.chunk;
+  L.n = s_off[a.W];
+  load_cands(L);
+  HistPartT<kFThreads> hp;
+  cand_level(L, 1, c1.prefix, m, c, !mass_only(a, b), h_cnt, h_mass, hp);
+  const Choice c2 = choose<kFThreads>(hp, c1, 11).c;  // (its barriers end every thread's reads of hp)
+  zero_hist(h_cnt, h_mass);
+  __syncthreads();
+  cand_level(L, 2, c2.prefix, m, c, true, h_cnt, h_mass, hp);
+  const Nucleus nu = nucleus<kFThreads>(hp, c2);
+  // the candidates' share of each chunk's kept mass, and each chunk's ties:
+  // a thread's entries run through few segments, so it adds per run
+  const double inv_chunk = 1.0 / (double)a.chunk;
+  int cur = -1;
+  uint64_t run_m = 0;
+  uint32_t run_t = 0;
+  auto flush = [&]() {
+    if (cur >= 0) {
+      if (run_m) atomicAdd((unsigned long long*)&s_km[cur], (unsigned long long)run_m);
+      if (run_t) atomicAdd(&s_kt[cur], run_t);
+    }
+  };
+  each_cand(L, [&](uint32_t key, uint32_t idx) {
+    const int w = chunk_index(idx, (uint32_t)a.chunk, inv_chunk);
+    if (w != cur) {
+      flush();
+      cur = w;
+      run_m = 0;
+      run_t = 0;
+    }
+    if (key > nu.tau)
+      run_m += fixed_mass(key_logit(key), m, c);
+    else if (key == nu.tau)
+      ++run_t;
+  });
+  flush();
+  __syncthreads();
+  // wave 0, lane i = chunk i: the chunk's kept mass (it keeps its ties
+  // while the ties of the chunks before it number fewer than nu.ties),
+  // inclusive scans over the chunks, r = floor(u * S_kept), and the chunk
+  // holding r
+  __shared__ int s_draw;
+  __shared__ uint64_t s_before, s_r;
+  __shared__ uint32_t s_ties_before;
+  if (t < 64) {
+    const uint32_t ti = t < a.W ? s_kt[t] : 0u;
+    const uint32_t texc = wave_scan(ti) - ti;
+    const uint32_t kt = texc >= nu.ties ? 0u : min(ti, nu.ties - texc);
+    const uint64_t km = (t < a.W ? s_km[t] + above : 0ull) + (uint64_t)kt * nu.f_tau;
+    const uint64_t kinc = wave_scan(km);
+    const uint64_t total = lane63(kinc);
+    const float uu = fminf(fmaxf(a.u[b], 0.f), 1.f);
+    uint64_t r = (uint64_t)floor((double)uu * (double)total);
+    if (r >= total) r = total - 1;
+    const uint64_t kexc = kinc - km;
+    const bool here = r >= kexc && r < kinc;  // at most one lane
+    const uint64_t hit = __ballot(here);
+    if (t == 0) s_draw = hit ? __builtin_ctzll(hit) : -1;
+    if (here) {
+      s_before = kexc;
+      s_ties_before = texc;
+    }
+    if (t == 0) s_r = r;
+  }
+  __syncthreads();
+  const int wd = s_draw;
+  if (wd < 0) return;  // nothing kept (every logit -inf): no draw
+  const Chunk ch = chunk_of<kFThreads>(a, b, wd);
+  float v[kSBatch];
+  if (ch.E <= kSBatch) load_run(ch, v);
+  draw_in_chunk(a, b, ch, nu, s_before, s_ties_before, s_r, m, c, v);
+}
+
 }  // namespace
 
-SampleWs sample_ws_carve(void* base, int B, int W) {
+SampleWs sample_ws_carve(void* base, int B, int W, int chunk) {
   SampleWs w{};
   const uintptr_t p = (uintptr_t)base;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return (void*)(p + at); };
-  w.cnt = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * 3 * kBuckets);
-  w.mass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * 3 * kBuckets);
+  w.cnt = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * kBuckets);
+  w.mass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * kBuckets);
   w.sum = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * W);
-  w.choice = (void*)take((size_t)kSampleChoiceBytes * B * 3);
+  w.choice = (void*)take((size_t)kSampleChoiceBytes * B);
   w.wmax = (float*)take(sizeof(float) * (size_t)B * W);
   w.wmass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * W);
-  w.wties = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * W);
+  w.ncand = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * W);
+  w.cand = (uint32_t*)take(2 * sizeof(uint32_t) * (size_t)B * W * chunk);
   w.bytes = off;
   return w;
 }
@@ -673,9 +889,7 @@ hipError_t launch_sample(const float* logits, int B, int V, const float* tempera
   sample_k0<<<grid, kSThreads, 0, st>>>(a);
   sample_k1<<<grid, kSThreads, 0, st>>>(a);
   sample_k2<<<grid, kSThreads, 0, st>>>(a);
-  sample_k3<<<grid, kSThreads, 0, st>>>(a);
-  sample_k4<<<grid, kSThreads, 0, st>>>(a);
-  sample_k5<<<grid, kSThreads, 0, st>>>(a);
+  sample_k3<<<B, kFThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -68,6 +68,22 @@ def test_sample_ties_and_minus_inf():
     _check(logits, T, p, k, u, _run(logits, T, p, k, u), "ties")
 
 
+def test_sample_wide_first_level_bucket():
+    """Logits within a narrow band (and one row of equal logits), so most of
+    the vocabulary shares the first level's chosen bucket: the candidate
+    list is longer than the part each thread holds in registers (8192
+    entries), and the ties of the threshold key run through many chunks."""
+    B, V = 6, 50001
+    r = synth.rng(21, "logits")
+    logits = (1.0 + np.round(r.normal(size=(B, V)) * 64.0) / 65536.0).astype(np.float32)
+    logits[0] = 0.75
+    T = np.array([1.0, 1.0, 0.7, 1.0, 1.3, 1.0], np.float32)
+    p = np.array([0.5, 0.9, 0.3, 1.0, 0.95, 0.6], np.float32)
+    k = np.array([0, 0, 0, 20000, 0, 9000], np.int32)
+    u = r.random(size=B).astype(np.float32)
+    _check(logits, T, p, k, u, _run(logits, T, p, k, u), "wide bucket")
+
+
 def test_sample_grid_of_draws_one_sequence():
     """One distribution, 512 draws on a grid of u: every token the oracle's."""
     V, N = 2000, 512
