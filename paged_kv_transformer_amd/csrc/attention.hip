@@ -238,8 +238,7 @@ paged_attention_kernel(const AttnArgs a) {
     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[r]);
     s[i] = acc;
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = rows_max4(mx);
 
   // ---- P = 2^((S - m) scale log2 e) split hi/lo; row sums.  Masked scores
   // are -inf and give 0; a wave with no token at all (m = -inf) subtracts 0.
@@ -260,8 +259,7 @@ paged_attention_kernel(const AttnArgs a) {
       ph[i][r] = __builtin_bit_cast(short, hi);
       pl[i][r] = __builtin_bit_cast(short, (__bf16)(p - (float)hi));
     }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = rows_sum4(lsum);
 
   // ---- O[g][d]: lane holds rows g = 4*grp + r, column d = col + 16*c
   f32x4 o[NC];

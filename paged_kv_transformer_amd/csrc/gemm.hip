@@ -277,8 +277,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(const GemmArgs a) {
   // ---- sum the waves (in wave order) into tile[col * TS + row]
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
-    ssq[c] += __shfl_xor(ssq[c], 16);
-    ssq[c] += __shfl_xor(ssq[c], 32);
+    ssq[c] = rows_sum4(ssq[c]);
     if (l < 16) ssq_w[w][16 * c + l] = ssq[c];
 #pragma unroll
     for (int g = 0; g < RG; ++g) red[w][c][g][l] = acc[g][c];

@@ -33,6 +33,29 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Across the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
+// by the row-swap permutes: each step is one VALU instruction pair instead
+// of a round trip through the LDS crossbar, and computes what an exchange
+// with lane l ^ 16, then l ^ 32, would (the two operands of each add or max
+// are the same two values, so the result is bitwise the same).
+__device__ __forceinline__ float rows_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// The value of lane l ^ 32.
+__device__ __forceinline__ float xor32_lane(float v) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? b[0] : b[1]);
+}
+
 __device__ __forceinline__ void set_error(uint32_t* err, uint32_t bits) {
   __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(128 * WR) void prefill_gemm_kernel(const PgemmArgs 
         // lane l holds gate rows, lane l + 32 the up rows of the same token
         f32x4 up;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) up[e] = __shfl_xor(v[e], 32);
+        for (int e = 0; e < 4; ++e) up[e] = xor32_lane(v[e]);
         const int i0 = 8 * G + 4 * grp;
         if (l < 32 && t < a.T && i0 < a.I) {
           uint16_t h[4];
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(128 * WR) void prefill_gemm_kernel(const PgemmArgs 
         // j (lanes 0..31) and j + D/2 (lanes 32..63, the same j in lane l - 32)
         f32x4 pv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = __shfl_xor(v[e], 32);
+        for (int e = 0; e < 4; ++e) pv[e] = xor32_lane(v[e]);
         const int D = a.D, half = D / 2, gph = D / 16;
         const int hd = G / gph;
         const int p = t < a.T ? (a.pos ? a.pos[t] : a.start_pos + t) : 0;
@@ -669,8 +669,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[r]);
       s[i] = acc;
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max4(mx);
     const float mn = fmaxf(m, mx);
     const float msub = mn == -INFINITY ? 0.f : mn;
     const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
@@ -689,8 +688,7 @@ __global__ __launch_bounds__(256) void prefill_attention_kernel(const PattnArgs 
         ph[i][r] = __builtin_bit_cast(short, hi);
         pl[i][r] = __builtin_bit_cast(short, (__bf16)(p - (float)hi));
       }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps = rows_sum4(ps);
     lsum = lsum * alpha + ps;
     // O row 4 grp + r belongs to column 4 grp + r: its factor lives in lane 4 grp + r
 #pragma unroll
