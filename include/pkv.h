@@ -344,7 +344,9 @@ size_t pkv_prefill_workspace_bytes(const pkv_config *cfg, int32_t num_tokens,
  *   logits [batch][vocab] FP32 (device; finite values or -inf, at least one
  *   finite per row), temperature, top_p, u [batch] FP32, top_k [batch]
  *   int32, tokens [batch] int32 (device).  workspace: at least
- *   pkv_sample_workspace_bytes(batch, vocab) bytes, 256-byte aligned.
+ *   pkv_sample_workspace_bytes(batch, vocab) bytes, 256-byte aligned (about
+ *   8 bytes per logit, room for every token as a candidate of the final
+ *   selection, plus 24 KiB per sequence).
  * batch == 0 is a no-op.  Errors: -EINVAL (NULL, misaligned workspace,
  * vocab < 1, batch < 0), -ENOTSUP (batch > 65535), -ENOSPC, -EIO.
  */
