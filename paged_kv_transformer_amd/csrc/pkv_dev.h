@@ -50,6 +50,46 @@ __device__ __forceinline__ float rows_max4(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Over all 64 lanes of a wave, the result in every lane: pairs and quads
+// by quad permutes, 8 and 16 lanes by the row half-mirror and row mirror
+// (after the quads every lane of a quad holds its quad's value, so a
+// mirror adds the neighbouring quad, then the neighbouring half-row), then
+// the four rows by the row-swap permutes.  VALU only.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __uint_as_float(dpp_u<0xb1>(__float_as_uint(v)));   // quad_perm [1,0,3,2]
+  v += __uint_as_float(dpp_u<0x4e>(__float_as_uint(v)));   // quad_perm [2,3,0,1]
+  v += __uint_as_float(dpp_u<0x141>(__float_as_uint(v)));  // row_half_mirror
+  v += __uint_as_float(dpp_u<0x140>(__float_as_uint(v)));  // row_mirror
+  return rows_sum4(v);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u<0xb1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u<0x4e>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u<0x141>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u<0x140>(__float_as_uint(v))));
+  return rows_max4(v);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+  v += dpp_u64<0xb1>(v);
+  v += dpp_u64<0x4e>(v);
+  v += dpp_u64<0x141>(v);
+  v += dpp_u64<0x140>(v);
+  const auto a0 = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  const auto a1 = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+  v = (((uint64_t)a1[0] << 32) | a0[0]) + (((uint64_t)a1[1] << 32) | a0[1]);
+  const auto b0 = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  const auto b1 = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+  return (((uint64_t)b1[0] << 32) | b0[0]) + (((uint64_t)b1[1] << 32) | b0[1]);
+}
+
 // The value of lane l ^ 32.
 __device__ __forceinline__ float xor32_lane(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

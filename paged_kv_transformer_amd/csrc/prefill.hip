@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void prefill_norm_kernel(const float* x, const
     ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
           b.w * b.w;
   }
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  ss = wave_sum(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
   const float rs = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)K + eps);
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const floa
           b.w * b.w;
   }
   if (!nw) return;
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  ss = wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
   const float rs = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);

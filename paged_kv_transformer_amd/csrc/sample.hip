@@ -323,7 +323,7 @@ __device__ float seq_max(float wmax_ld) {
   const int t = threadIdx.x;
   if (t < 64) {
     float m = wmax_ld;
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    m = wave_max(m);
     if (t == 0) s_res = m;
   }
   __syncthreads();
@@ -337,7 +337,7 @@ __device__ uint64_t seq_sum(uint64_t part) {
   const int t = threadIdx.x;
   if (t < 64) {
     uint64_t v = part;
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    v = wave_sum(v);
     if (t == 0) s_res = v;
   }
   __syncthreads();
@@ -380,7 +380,7 @@ __device__ void histogram(const Chunk& ch, float (&v)[kSBatch], int level, uint3
   // the chunk's part of the normaliser: a wave sum, then the 4 waves' in
   // order, stored in the chunk's own slot (no atomics on one shared word)
   if (gsum) {
-    for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+    ls = wave_sum(ls);
     if ((t & 63) == 0) h_sum[t >> 6] = ls;
   }
   __syncthreads();
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kSThreads) void sample_k0(const SArgs a) {
 #pragma unroll
     for (int i = 0; i < kSBatch; ++i) m = fmaxf(m, v[i]);
   }
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  m = wave_max(m);
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   if (t == 0) {
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(kSThreads) void sample_k2(const SArgs a) {
     __syncthreads();  // s_tot is rewritten by the next batch
     load_batch(ch, base + t, v);
   }
-  for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o);
+  above = wave_sum(above);
   if ((t & 63) == 0) s_m[t >> 6] = above;
   __syncthreads();
   if (t == 0) {
