@@ -488,8 +488,42 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* part, int 
 // One workgroup per token row: x[t] += sum_s part[s][t] (splits in order,
 // so the result does not depend on scheduling), then, if nw is given, the
 // next RMSNorm of the new row into packed hi/lo pairs (padding rows zero).
-// Each thread owns 8 consecutive columns per 2048, in both passes, so its
-// second pass re-reads only what it wrote itself.
+// Each thread owns 8 consecutive columns per 2048.  The first kHold such
+// chunks (rows up to 4096 wide) stay in registers between the two passes,
+// and their norm weights are loaded before the sums: the second pass then
+// needs no memory round trip of its own (wider rows re-read the rest).
+constexpr int kHold = 2;
+
+__device__ __forceinline__ void resid_chunk(float* row, const float* part, size_t split, int t, int N,
+                                            int k, int ks, float4& a, float4& b) {
+  a = *(const float4*)(row + k);
+  b = *(const float4*)(row + k + 4);
+#pragma unroll 8
+  for (int sp = 0; sp < ks; ++sp) {
+    const float* pr = part + sp * split + (size_t)t * N + k;
+    const float4 pa = *(const float4*)pr, pb = *(const float4*)(pr + 4);
+    a.x += pa.x; a.y += pa.y; a.z += pa.z; a.w += pa.w;
+    b.x += pb.x; b.y += pb.y; b.z += pb.z; b.w += pb.w;
+  }
+  *(float4*)(row + k) = a;
+  *(float4*)(row + k + 4) = b;
+}
+
+__device__ __forceinline__ void norm_chunk(uint16_t* xb, int t, int N, int k, float4 a, float4 b, uint4 w,
+                                           float rs) {
+  float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = v[2 * e] * bf16_lo(ww[e]) * rs;
+    v[2 * e + 1] = v[2 * e + 1] * bf16_hi(ww[e]) * rs;
+  }
+  uint4 hi, lo;
+  split8(v, hi, lo);
+  *(uint4*)(xb + packed_pair_index(t, k, N, 0)) = hi;
+  *(uint4*)(xb + packed_pair_index(t, k, N, 1)) = lo;
+}
+
 __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const float* part, int ks,
                                                             int T, int N, const uint16_t* nw,
                                                             float eps, uint16_t* xb) {
@@ -504,18 +538,27 @@ __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const floa
   }
   float* row = x + (size_t)t * N;
   const size_t split = (size_t)T * N;
+  float4 ha[kHold], hb[kHold];
+  uint4 hw[kHold];
+#pragma unroll
+  for (int h = 0; h < kHold; ++h) {
+    const int k = 8 * tid + 2048 * h;
+    hw[h] = nw && k < N ? *(const uint4*)(nw + k) : make_uint4(0u, 0u, 0u, 0u);
+  }
   float ss = 0.f;
-  for (int k = 8 * tid; k < N; k += 8 * 256) {
-    float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
-#pragma unroll 8
-    for (int sp = 0; sp < ks; ++sp) {
-      const float* pr = part + sp * split + (size_t)t * N + k;
-      const float4 pa = *(const float4*)pr, pb = *(const float4*)(pr + 4);
-      a.x += pa.x; a.y += pa.y; a.z += pa.z; a.w += pa.w;
-      b.x += pb.x; b.y += pb.y; b.z += pb.z; b.w += pb.w;
+#pragma unroll
+  for (int h = 0; h < kHold; ++h) {
+    const int k = 8 * tid + 2048 * h;
+    if (k < N) {
+      resid_chunk(row, part, split, t, N, k, ks, ha[h], hb[h]);
+      const float4 a = ha[h], b = hb[h];
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
+            b.w * b.w;
     }
-    *(float4*)(row + k) = a;
-    *(float4*)(row + k + 4) = b;
+  }
+  for (int k = 8 * tid + 2048 * kHold; k < N; k += 8 * 256) {
+    float4 a, b;
+    resid_chunk(row, part, split, t, N, k, ks, a, b);
     ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
           b.w * b.w;
   }
@@ -524,20 +567,14 @@ __global__ __launch_bounds__(256) void prefill_resid_kernel(float* x, const floa
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
   const float rs = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
-  for (int k = 8 * tid; k < N; k += 8 * 256) {
-    const float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
-    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    const uint4 w = *(const uint4*)(nw + k);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = v[2 * e] * bf16_lo(ww[e]) * rs;
-      v[2 * e + 1] = v[2 * e + 1] * bf16_hi(ww[e]) * rs;
-    }
-    uint4 hi, lo;
-    split8(v, hi, lo);
-    *(uint4*)(xb + packed_pair_index(t, k, N, 0)) = hi;
-    *(uint4*)(xb + packed_pair_index(t, k, N, 1)) = lo;
+  for (int h = 0; h < kHold; ++h) {
+    const int k = 8 * tid + 2048 * h;
+    if (k < N) norm_chunk(xb, t, N, k, ha[h], hb[h], hw[h], rs);
+  }
+  for (int k = 8 * tid + 2048 * kHold; k < N; k += 8 * 256) {
+    const float4 a = *(const float4*)(row + k), b = *(const float4*)(row + k + 4);
+    norm_chunk(xb, t, N, k, a, b, *(const uint4*)(nw + k), rs);
   }
 }
 
