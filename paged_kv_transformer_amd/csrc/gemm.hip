@@ -508,9 +508,9 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, const GemmPlan& p, hipStream_
       break;
     case EPI_LOGITS:
       if (a.x_plain)  // one plain activation row (the last prompt token)
-        e = ct == 1 ? go<1, 2, 4, EPI_LOGITS, true>(a, p.tiles, st) : hipErrorInvalidValue;
+        e = ct == 1 && p.rg == 2 ? go<1, 2, 4, EPI_LOGITS, true>(a, p.tiles, st) : hipErrorInvalidValue;
       else
-        e = ct == 1 ? go<1, 2, 4, EPI_LOGITS>(a, p.tiles, st)
+        e = ct == 1 ? (p.rg == 4 ? go<1, 4, 4, EPI_LOGITS>(a, p.tiles, st) : go<1, 2, 4, EPI_LOGITS>(a, p.tiles, st))
             : ct == 2 ? go<2, 1, 4, EPI_LOGITS>(a, p.tiles, st)
                       : go<4, 1, 4, EPI_LOGITS>(a, p.tiles, st);
       if (e != hipSuccess) return e;
