@@ -93,6 +93,8 @@ extern "C" {
 #define PKV_DEVERR_LENGTH 2u    /* length / position beyond max_pages * PT  */
 #define PKV_DEVERR_ROPE 4u      /* position >= max_position_embeddings      */
 #define PKV_DEVERR_TOKEN 8u     /* token id outside [0, vocab_size)         */
+#define PKV_DEVERR_SYNC 16u     /* single-launch layer: a phase's input did not
+                                   arrive in time (outputs unspecified)      */
 
 /* Model configuration: the config-header fields of llmc's binary format. */
 typedef struct pkv_config {
@@ -261,6 +263,16 @@ int paged_gqa_decode_noalloc(const pkv_pool *pool, const uint16_t *q,
  * above 2 GiB); device errors PKV_DEVERR_PAGE, PKV_DEVERR_LENGTH,
  * PKV_DEVERR_ROPE.  workspace: at least pkv_workspace_bytes(cfg, batch,
  * max_pages, pool page size) bytes, initialised once.
+ * At batch 1 the layer runs as ONE launch when it fits (pkv_fused_layer_plan;
+ * the engine-building article, section 4.2, on the cost of a layer's many
+ * small launches): one workgroup per compute unit, every workgroup resident
+ * at once, the layer's weights streamed into LDS at kernel start and the
+ * phases passing their small vectors through the workspace; nothing else may
+ * occupy the GPU's compute units meanwhile, or a phase can wait past its
+ * bounded deadline (PKV_DEVERR_SYNC, outputs unspecified).  Its sums run in
+ * another order than the multi-launch path's (FP32 products of the FP32
+ * activations with the BF16 weights), so the two agree to rounding, not bit
+ * for bit.
  */
 int decoder_layer_decode(const pkv_config *cfg, const pkv_layer_weights *w,
 			 const float *rope_cos, const float *rope_sin,
@@ -453,6 +465,29 @@ int pkv_probe_paged_read(const pkv_pool *pool, int32_t num_q_heads,
 			 const int32_t *context_lens, int32_t batch,
 			 float *sink, void *stream);
 int pkv_probe_empty(int32_t launches, int32_t workgroups, void *stream);
+
+/*
+ * pkv_set_fused_layer — switch the single-launch batch-1 layer on (enable
+ * != 0, the default) or off for every later call in the process; returns
+ * the previous setting (1 or 0).  Off, batch-1 layers take the multi-launch
+ * path (six or seven kernels per layer).  Host only, no device work.
+ */
+int pkv_set_fused_layer(int32_t enable);
+
+/*
+ * pkv_fused_layer_plan — 1 if decoder_layer_decode / decode_step calls with
+ * this configuration, batch and block-table size run each layer as one
+ * launch on a GPU of `compute_units` compute units (batch 1, the layer's
+ * weights fit 32 KiB of LDS per compute wave of one workgroup per compute
+ * unit, at most one 128-token attention unit per workgroup, the phase
+ * vectors fit the kernel's 24 KiB buffer), 0 if they take the multi-launch
+ * path; -EINVAL / -ENOTSUP on bad arguments.  Host only.  The Qwen2.5-0.5B
+ * shape fits at 128-token tables on 256 compute units; the Llama-3.2-1B
+ * shape does not (123 MB of layer weights).
+ */
+int pkv_fused_layer_plan(const pkv_config *cfg, int32_t batch,
+			 int32_t max_pages, int32_t page_tokens,
+			 int32_t compute_units);
 
 /* Library version string (host). */
 const char *pkv_version(void);

@@ -9,7 +9,8 @@ Entry points (same names as the C ABI): ``kv_pool_create``,
 ``kv_pool_create_split``, ``kv_append``,
 ``paged_gqa_decode``, ``decoder_layer_decode``, ``decode_step``, plus
 ``workspace_bytes``, ``attention_workspace_bytes``, ``workspace_init``,
-``rope_table``, ``pack_weight`` and ``device_error``.
+``rope_table``, ``pack_weight``, ``device_error``, ``set_fused_layer`` and
+``fused_layer_plan``.
 """
 import ctypes
 import errno
@@ -23,7 +24,7 @@ LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path
 
 PAGE_TOKENS = 16
 HEAD_DIM = 64
-DEVERR_PAGE, DEVERR_LENGTH, DEVERR_ROPE, DEVERR_TOKEN = 1, 2, 4, 8
+DEVERR_PAGE, DEVERR_LENGTH, DEVERR_ROPE, DEVERR_TOKEN, DEVERR_SYNC = 1, 2, 4, 8, 16
 PACK_ROWS, PACK_QKV, PACK_GATE_UP, PACK_QKV128 = 0, 1, 2, 3
 
 
@@ -99,6 +100,8 @@ def lib():
             "pkv_probe_read": (ctypes.c_int, [P, I64, I32, P, P]),
             "pkv_probe_paged_read": (ctypes.c_int, [PP, I32, P, I32, P, I32, P, P]),
             "pkv_probe_empty": (ctypes.c_int, [I32, I32, P]),
+            "pkv_set_fused_layer": (ctypes.c_int, [I32]),
+            "pkv_fused_layer_plan": (ctypes.c_int, [ctypes.POINTER(Config), I32, I32, I32, I32]),
             "pkv_version": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sigs.items():
@@ -267,6 +270,18 @@ def alloc_workspace(nbytes, device="cuda", stream=None):
 def workspace_init(ws, stream=None):
     _check("pkv_workspace_init", lib().pkv_workspace_init(
         _dev(ws, (torch.uint8,), "workspace"), ws.numel(), _stream(stream)))
+
+
+def set_fused_layer(enable):
+    """Switch the single-launch batch-1 layer on or off; returns the
+    previous setting."""
+    return lib().pkv_set_fused_layer(1 if enable else 0)
+
+
+def fused_layer_plan(cfg, batch, max_pages, page_tokens=PAGE_TOKENS, compute_units=256):
+    """1 if such calls run each layer as one launch, else 0."""
+    return _check("pkv_fused_layer_plan", lib().pkv_fused_layer_plan(
+        ctypes.byref(cfg), batch, max_pages, page_tokens, compute_units))
 
 
 def device_error(ws, stream=None):

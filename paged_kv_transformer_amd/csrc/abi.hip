@@ -1,10 +1,12 @@
 // Host side of the C ABI declared in include/pkv.h: argument validation
 // (pure host code, run before any HIP call), workspace carving and the
 // launch sequence of each entry point.  Every step of the computation runs
-// in the kernels of attention.hip, gemm.hip, prefill.hip, sample.hip and misc.hip.
+// in the kernels of attention.hip, gemm.hip, fused_layer.hip, prefill.hip, sample.hip and misc.hip.
 #include <errno.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "pkv.h"
 #include "pkv_dev.h"
@@ -255,6 +257,77 @@ int run_layer(const pkv_config* cfg, const pkv_layer_weights* w, const float* ro
     if (rc) return rc;
   }
   return 0;
+}
+
+// ---------------------------------------------------------------------------
+// Batch 1: the whole layer as one launch (fused_layer.hip) when its weights
+// fit the chip's LDS and its table the kernel's attention units.  Returns 1
+// when the layer was launched, 0 when the multi-launch path must run, or a
+// negative errno.
+std::atomic<int> g_fused_layer{1};
+
+bool fused_plan_for(const pkv_config* c, int64_t max_tiles, int nwg, FusedArgs* a) {
+  // the plan depends only on the shapes: keep the last one
+  struct Key {
+    int H, Hq, Hkv, D, I, nwg;
+    int64_t tiles;
+    bool ok;
+  };
+  static thread_local Key key{-1, 0, 0, 0, 0, 0, 0, false};
+  static thread_local FusedArgs plan{};
+  const Key k{c->hidden_size, c->num_attention_heads, c->num_key_value_heads, c->head_dim,
+              c->intermediate_size, nwg, max_tiles, false};
+  if (!(key.H == k.H && key.Hq == k.Hq && key.Hkv == k.Hkv && key.D == k.D && key.I == k.I &&
+        key.nwg == k.nwg && key.tiles == k.tiles)) {
+    key = k;
+    plan = FusedArgs{};
+    key.ok = plan_fused_layer(k.H, k.Hq, k.Hkv, k.D, k.I, max_tiles, nwg, &plan);
+  }
+  if (key.ok) *a = plan;
+  return key.ok;
+}
+
+int run_layer_fused(const pkv_config* cfg, const pkv_layer_weights* w, const float* rope_cos,
+                    const float* rope_sin, const pkv_pool* pool, const int32_t* bt, int32_t max_pages,
+                    const int32_t* pos, float* hidden, float* hidden_packed, void* ws, const WsLayout& L,
+                    hipStream_t st) {
+  if (!g_fused_layer.load(std::memory_order_relaxed)) return 0;
+  const int nwg = fused_device_wgs();
+  if (nwg < 1) return 0;
+  const int64_t tiles = table_tiles(max_pages, pool->page_tokens);
+  FusedArgs a{};
+  if (!fused_plan_for(cfg, tiles, nwg, &a)) return 0;
+  const int H = cfg->hidden_size, Hq = cfg->num_attention_heads, Hkv = cfg->num_key_value_heads;
+  const int D = cfg->head_dim, I = cfg->intermediate_size;
+  a.eps = cfg->rms_norm_eps;
+  a.scale = 1.0f / sqrtf((float)D);
+  a.attn_norm = w->attn_norm;
+  a.w_qkv = w->w_qkv;
+  a.w_o = w->w_o;
+  a.mlp_norm = w->mlp_norm;
+  a.w_gu = w->w_gate_up;
+  a.w_down = w->w_down;
+  a.rcos = rope_cos;
+  a.rsin = rope_sin;
+  a.max_pos = cfg->max_position_embeddings;
+  a.pv = pool_view(pool);
+  a.bt = bt;
+  a.bt_stride = max_pages;
+  a.pos = pos;
+  a.hidden = hidden;
+  a.hidden_packed = hidden_packed;
+  a.err = at<uint32_t>(ws, L.err);
+  a.epoch = at<uint32_t>(ws, L.fused_epoch);
+  uint64_t* ll = at<uint64_t>(ws, L.fused_ll);
+  a.q = ll;
+  a.kn = a.q + (size_t)Hq * D;
+  a.vn = a.kn + (size_t)Hkv * D;
+  a.rec = a.vn + (size_t)Hkv * D;
+  a.h1 = a.rec + (size_t)Hkv * a.ns * fused_rec_len(a.G, D);
+  a.ypart = a.h1 + (size_t)kFusedCopies * H;
+  (void)I;
+  const int rc = io(launch_fused_layer(a, st));
+  return rc ? rc : 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -604,6 +677,11 @@ int decoder_layer_decode(const pkv_config* cfg, const pkv_layer_weights* w,
   const WsLayout L = ws_layout(batch, cfg->hidden_size, cfg->num_attention_heads,
                                cfg->num_key_value_heads, cfg->intermediate_size, cfg->vocab_size,
                                table_tiles(max_pages, pool->page_tokens), true, cfg->head_dim);
+  if (batch == 1) {
+    rc = run_layer_fused(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, positions, hidden,
+                         nullptr, workspace, L, st);
+    if (rc) return rc < 0 ? rc : 0;
+  }
   return run_layer(cfg, w, rope_cos, rope_sin, pool, block_table, max_pages, max_pages, positions,
                    batch, hidden, nullptr, workspace, L, st);
 }
@@ -664,9 +742,15 @@ int decode_step(const pkv_config* cfg, const pkv_model_weights* w, const pkv_poo
 
   if ((rc = io(launch_embed(w->embed, V, H, token_ids, x, x_p, batch, err, st)))) return rc;
   for (int l = 0; l < cfg->num_hidden_layers; ++l) {
-    rc = run_layer(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool,
-                   block_tables + (size_t)l * batch * max_pages, max_pages, max_pages, positions,
-                   batch, x, x_p, workspace, L, st);
+    const int32_t* btl = block_tables + (size_t)l * batch * max_pages;
+    if (batch == 1) {
+      rc = run_layer_fused(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool, btl, max_pages, positions,
+                           x, x_p, workspace, L, st);
+      if (rc < 0) return rc;
+      if (rc == 1) continue;
+    }
+    rc = run_layer(cfg, &w->layers[l], w->rope_cos, w->rope_sin, pool, btl, max_pages, max_pages,
+                   positions, batch, x, x_p, workspace, L, st);
     if (rc) return rc;
   }
   GemmArgs a{};
@@ -958,6 +1042,25 @@ int pkv_probe_paged_read(const pkv_pool* pool, int32_t num_q_heads, const int32_
 int pkv_probe_empty(int32_t launches, int32_t workgroups, void* stream) {
   if (launches < 0 || workgroups < 1 || workgroups > 1 << 20) return -EINVAL;
   return io(launch_probe_empty(launches, workgroups, (hipStream_t)stream));
+}
+
+int pkv_set_fused_layer(int32_t enable) {
+  return g_fused_layer.exchange(enable ? 1 : 0);
+}
+
+int pkv_fused_layer_plan(const pkv_config* cfg, int32_t batch, int32_t max_pages, int32_t page_tokens,
+                         int32_t compute_units) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (batch < 0 || max_pages < 1 || compute_units < 1) return -EINVAL;
+  if (!page_tokens_ok(page_tokens)) return -ENOTSUP;
+  if (batch != 1) return 0;
+  FusedArgs a{};
+  return plan_fused_layer(cfg->hidden_size, cfg->num_attention_heads, cfg->num_key_value_heads,
+                          cfg->head_dim, cfg->intermediate_size, table_tiles(max_pages, page_tokens),
+                          compute_units, &a)
+             ? 1
+             : 0;
 }
 
 int pkv_device_error(void* workspace, void* stream) {

@@ -17,7 +17,7 @@ constexpr int kHeadDim = 64;       // the default head width; 128 is also suppor
 constexpr int kMaxHeadDim = 128;
 constexpr int kMaxGroup = 16;      // GQA group: one 16-wide matrix-core tile
 
-enum : uint32_t { ERR_PAGE = 1u, ERR_LENGTH = 2u, ERR_ROPE = 4u, ERR_TOKEN = 8u };
+enum : uint32_t { ERR_PAGE = 1u, ERR_LENGTH = 2u, ERR_ROPE = 4u, ERR_TOKEN = 8u, ERR_SYNC = 16u };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -516,9 +516,107 @@ inline size_t gemm_part_floats(int N, int Bc, int K) {
   return most;
 }
 
+// ------------------------------------------------- single-launch layer ---
+//
+// A batch-1 decoder layer in one launch (fused_layer.hip): one workgroup per
+// compute unit; kFusedWaves loader waves stream the workgroup's share of the
+// layer's weights into LDS from kernel start, and as many worker waves
+// compute, passing the small vectors between the layer's phases as 8-byte
+// (value, epoch) words.
+constexpr int kFusedWaves = 4;          // worker waves (and loader waves) per workgroup
+constexpr int kFusedThreads = 2 * kFusedWaves * 64;
+constexpr int kFusedMaxHidden = 8 * kFusedWaves * 64;  // one 8-value chunk of the hidden vector per worker lane
+constexpr int kFusedCap = 33;           // 1 KiB weight slots per worker wave
+constexpr int kFusedX = 5632;           // floats of the phase-input buffer
+constexpr int kFusedMaxUnits = 8;       // units of one phase per workgroup
+constexpr int kFusedMaxWgs = 512;       // workgroups (compute units) at most
+constexpr int kFusedAttnTiles = kFusedWaves * 2;  // 16-token tiles per attention unit
+constexpr int kFusedRedRows = kFusedWaves;        // output rows per reduction unit (one per worker wave)
+// copies of the h1 exchange words: every workgroup reads them, so each copy
+// serves one eighth of the grid
+constexpr int kFusedCopies = 8;
+
+// Phases, in order: QKV; attention; O; gate/up with the down projection's
+// matching columns (each gate/up unit multiplies its 8 SwiGLU outputs into
+// a partial of the layer output); the reduction of those partials.
+enum FusedPhase { FP_QKV = 0, FP_ATT = 1, FP_O = 2, FP_GU = 3, FP_RED = 4, FP_COUNT = 5 };
+
+// Units of a phase: n units of `slots` 1 KiB weight slots each (a 16-row
+// group of the matrix over `slots` 32-wide K steps) and, for gate/up,
+// `extra` slots of the down projection (its 8 matching columns, four 16-row
+// groups per slot).
+struct FusedGeo {
+  int n, slots, extra;
+};
+
+__host__ __device__ inline FusedGeo fused_geo(int P, int H, int Hq, int Hkv, int D, int I, int ns) {
+  FusedGeo g{0, 0, 0};
+  switch (P) {
+    case FP_QKV: g = {(Hq + 2 * Hkv) * D / 16, H / 32, 0}; break;
+    case FP_ATT: g = {Hkv * ns, 0, 0}; break;
+    case FP_O: g = {H / 16, Hq * D / 32, 0}; break;
+    case FP_GU: g = {I / 8, H / 32, H / 64}; break;
+    default: g = {H / kFusedRedRows, 0, 0}; break;
+  }
+  return g;
+}
+
+// Units of phase P are dealt round-robin over the workgroups from workgroup
+// first[P]: unit u runs on workgroup (first[P] + u) mod nwg.
+__host__ __device__ inline int fused_first_unit(int wg, int first, int nwg) {
+  return ((wg - first) % nwg + nwg) % nwg;
+}
+__host__ __device__ inline int fused_unit_count(int n, int k0, int nwg) {
+  return n > k0 ? (n - k0 + nwg - 1) / nwg : 0;
+}
+// Slots of wave w among `slots` (slots j = w, w + kFusedWaves, ...).
+__host__ __device__ inline int fused_wave_slots(int slots, int w) {
+  return slots > w ? (slots - w + kFusedWaves - 1) / kFusedWaves : 0;
+}
+
+// Words of one attention split's record: m and l per head, then O.
+__host__ __device__ inline int fused_rec_len(int G, int D) { return G * (D + 2); }
+
+struct FusedArgs {
+  int32_t H, Hq, Hkv, D, I, G;
+  float eps, scale;
+  const uint16_t *attn_norm, *w_qkv, *w_o, *mlp_norm, *w_gu, *w_down;
+  const float *rcos, *rsin;
+  int32_t max_pos;
+  PoolView pv;
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* pos;
+  float* hidden;          // [H] in / out
+  float* hidden_packed;   // packed copy of the output (or null)
+  uint32_t* err;
+  uint32_t* epoch;        // [nwg] per-workgroup launch counters
+  // (value, epoch) words passed between phases: q, the new K and V rows, the
+  // attention output (or split records), h1 (kFusedCopies copies), every
+  // workgroup's partial of the layer output ([H / 4][nwg][4])
+  uint64_t *q, *kn, *vn, *rec, *h1, *ypart;
+  int32_t nwg, ns;        // workgroups, attention splits per kv head
+  int32_t first[FP_COUNT];
+};
+
+// Plan of a single-launch layer: false if the layer does not fit (then the
+// multi-launch path runs).  Host code.
+bool plan_fused_layer(int H, int Hq, int Hkv, int D, int I, int64_t max_tiles, int nwg, FusedArgs* a);
+// Words of the exchange arrays.
+inline size_t fused_ll_pairs(int H, int Hq, int Hkv, int D, int I, int ns) {
+  (void)I;
+  return (size_t)Hq * D + 2 * (size_t)Hkv * D + (size_t)Hkv * ns * fused_rec_len(Hq / Hkv, D) +
+         (size_t)kFusedCopies * H + (size_t)H * kFusedMaxWgs;
+}
+inline int fused_splits(int64_t max_tiles) { return (int)((max_tiles + kFusedAttnTiles - 1) / kFusedAttnTiles); }
+hipError_t launch_fused_layer(const FusedArgs& a, hipStream_t st);
+// Compute units of the current device if one fused workgroup fits on each, else -1.
+int fused_device_wgs();
+
 struct WsLayout {
   size_t err, q, o_p, h1, h1_p, act_p, x, x_p;
   size_t attn_part, amax_part, gemm_part;
+  size_t fused_ll, fused_epoch;  // single-launch layer (batch 1): exchange words, epochs
   size_t total;
 };
 
@@ -547,6 +645,10 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int64_t m
     const size_t po = gemm_part_floats(H, Bc, Hq * D);
     const size_t pd = gemm_part_floats(H, Bc, I);
     w.gemm_part = take(sizeof(float) * (po > pd ? po : pd));
+    if (B == 1) {
+      w.fused_ll = take(8 * fused_ll_pairs(H, Hq, Hkv, D, I, fused_splits(max_tiles)));
+      w.fused_epoch = take(4 * (size_t)kFusedMaxWgs);
+    }
   }
   w.total = off;
   return w;

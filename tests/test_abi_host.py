@@ -238,3 +238,31 @@ def test_measurement_probes_reject_bad_arguments():
     assert L.pkv_probe_paged_read(ctypes.byref(pool), 32, None, 8, FAKE, 4, FAKE, None) == EINVAL
     assert L.pkv_probe_paged_read(ctypes.byref(pool), 32, FAKE, 0, FAKE, 4, FAKE, None) == EINVAL
     assert L.pkv_probe_paged_read(ctypes.byref(pool), 32, FAKE, 8, FAKE, 0, FAKE, None) == 0  # nothing to do
+
+
+def test_fused_layer_plan_host():
+    """The single-launch batch-1 layer's plan (host only): the
+    Qwen2.5-0.5B-shaped layer fits 256 compute units at 128-token tables and
+    up to 33 pages; batches above 1, the Llama-3.2-1B-shaped layer (123 MB of
+    weights), and too few compute units for its weights take the multi-launch
+    path; bad arguments are errors.  pkv_set_fused_layer returns the previous
+    setting."""
+    import synth
+    qwen = pkv.make_config(synth.QWEN05, max_pos=4096, layers=1)
+    assert pkv.fused_layer_plan(qwen, 1, 8, 16, 256) == 1
+    assert pkv.fused_layer_plan(qwen, 1, 33, 16, 256) == 1
+    assert pkv.fused_layer_plan(qwen, 1, 1, 256, 256) == 1   # one 256-token page
+    assert pkv.fused_layer_plan(qwen, 2, 8, 16, 256) == 0
+    assert pkv.fused_layer_plan(qwen, 1, 8, 16, 64) == 0      # 30 MB of weights on 64 CUs
+    llama = pkv.make_config(synth.LLAMA1B, max_pos=4096, layers=1)
+    assert pkv.fused_layer_plan(llama, 1, 64, 16, 256) == 0
+    lib = pkv.lib()
+    assert lib.pkv_fused_layer_plan(None, 1, 8, 16, 256) == -errno.EINVAL
+    assert lib.pkv_fused_layer_plan(ctypes.byref(qwen), 1, 0, 16, 256) == -errno.EINVAL
+    assert lib.pkv_fused_layer_plan(ctypes.byref(qwen), 1, 8, 32, 256) == -errno.ENOTSUP
+    assert lib.pkv_fused_layer_plan(ctypes.byref(qwen), 1, 8, 16, 0) == -errno.EINVAL
+    prev = pkv.set_fused_layer(False)
+    try:
+        assert pkv.set_fused_layer(False) == 0
+    finally:
+        pkv.set_fused_layer(prev)
