@@ -109,7 +109,10 @@ __device__ __forceinline__ void ll_gather(__amdgpu_buffer_rsrc_t r, int nch, F m
       int word = 0;
       map(need[k] ? c : 0, word, dst[k]);
       off[k] = word * 8;
-      v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off[k], 0, kSc1);
+      // only the lane's own chunks: a load whose result is never read
+      // would make the compiler wait for every memory operation in flight
+      // before it reuses the register
+      if (need[k]) v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off[k], 0, kSc1);
     }
     uint64_t t0 = 0;
     for (int it = 0;; ++it) {
@@ -139,7 +142,7 @@ __device__ __forceinline__ void ll_gather(__amdgpu_buffer_rsrc_t r, int nch, F m
         }
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int k = 0; k < kPollBatch; ++k)
         if (need[k]) v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off[k], 0, kSc1);
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_layer_kernel(const FusedA
   constexpr int TS = NH + D / 32;  // slots of one tile (K, then V)
   constexpr int MAXT = kFusedMaxHidden / 64 / NW;  // output rows per lane in the down partial
   __shared__ u32x4 wsl[NW][kFusedCap][64];
-  __shared__ float X[kFusedX];
+  __shared__ __align__(16) float X[kFusedX];
   __shared__ float red[2][NW][kFusedMaxUnits][16];  // by phase parity
   __shared__ float ssqp[2][NW];
   __shared__ float aval[kFusedMaxUnits][8];
@@ -391,33 +394,45 @@ __global__ __launch_bounds__(kFusedThreads) void fused_layer_kernel(const FusedA
     wait_landed(&landed[w], first_slot[P] + cnt[P] * (ws + we));
     const u32x4* Xc = (const u32x4*)X;
     const int col = l & 15, ch = l >> 4;
+    // the units' products interleaved (independent accumulators, the hi
+    // and lo halves of the input in separate ones): no MFMA waits for the
+    // previous one's result
+    const int s0 = first_slot[P], su = ws + we;
+    // KU units at once (a compile-time count, so that every operand read of
+    // a K step is issued before its products), from unit k0u on
+    auto run = [&](auto KC, int k0u) {
+      constexpr int KU = decltype(KC)::value;
+      f32x4 ah[KU], al[KU];
 #pragma unroll
-    for (int k = 0; k < kFusedMaxUnits; ++k) {
-      if (k >= cnt[P]) break;
-      const int slot0 = first_slot[P] + k * (ws + we);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int j0 = 0; j0 < ws; j0 += 4) {
-        u32x4 av[4], bh[4], bl[4];
+      for (int k = 0; k < KU; ++k) ah[k] = al[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int jj = 0; jj < ws; ++jj) {
+        const int c = 4 * (w + jj * NW) + ch;
+        const u32x4 bh = Xc[2 * c], bl = Xc[2 * c + 1];
+        u32x4 av[KU];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int jj = min(j0 + u, ws - 1);
-          const int c = 4 * (w + jj * NW) + ch;
-          av[u] = wsl[w][slot0 + jj][l];
-          bh[u] = Xc[2 * c];
-          bl[u] = Xc[2 * c + 1];
-        }
+        for (int k = 0; k < KU; ++k) av[k] = wsl[w][s0 + (k0u + k) * su + jj][l];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (j0 + u >= ws) break;
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                       __builtin_bit_cast(bf16x8, bh[u]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                       __builtin_bit_cast(bf16x8, bl[u]), acc, 0, 0, 0);
+        for (int k = 0; k < KU; ++k) {
+          ah[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[k]),
+                                                         __builtin_bit_cast(bf16x8, bh), ah[k], 0, 0, 0);
+          al[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[k]),
+                                                         __builtin_bit_cast(bf16x8, bl), al[k], 0, 0, 0);
         }
       }
       if (col == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[par][w][k][4 * ch + r] = acc[r];
+        for (int k = 0; k < KU; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[par][w][k0u + k][4 * ch + r] = ah[k][r] + al[k][r];
+      }
+    };
+    // the phase's units in groups of at most four
+    for (int k0u = 0; k0u < cnt[P]; k0u += 4) {
+      switch (min(cnt[P] - k0u, 4)) {
+        case 1: run(std::integral_constant<int, 1>{}, k0u); break;
+        case 2: run(std::integral_constant<int, 2>{}, k0u); break;
+        case 3: run(std::integral_constant<int, 3>{}, k0u); break;
+        default: run(std::integral_constant<int, 4>{}, k0u); break;
       }
     }
   };
@@ -659,6 +674,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_layer_kernel(const FusedA
         o[c] = mfma_k16(pl[i], vb, o[c]);
       }
     }
+    // the wave's (m, l, O): O as [wave][d][head], heads padded to GP, so
+    // that a lane's four heads of one column are one 16-byte write
+    const int GP = G <= 4 ? 4 : (G <= 8 ? 8 : 16);
     float* sm_m = X + XS;
     float* sm_l = X + XS + NW * 16;
     float* sm_o = X + XS + 2 * NW * 16;
@@ -666,13 +684,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_layer_kernel(const FusedA
       sm_m[w * 16 + col] = m2;
       sm_l[w * 16 + col] = lsum;
     }
+    if (4 * grp < GP) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gg = 4 * grp + r;
-        if (gg < G) sm_o[(w * G + gg) * (D + 1) + col + 16 * c] = o[c][r];
-      }
+      for (int c = 0; c < NC; ++c) *(f32x4*)&sm_o[(w * D + col + 16 * c) * GP + 4 * grp] = o[c];
+    }
     worker_barrier(&wbar, gen);
     // the four waves merged in order: with one split per kv head the
     // attention output itself (o = O / L at o index kvh G D + idx),
@@ -689,7 +704,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_layer_kernel(const FusedA
         const float mw = sm_m[ww * 16 + gg];
         const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
         L += f * sm_l[ww * 16 + gg];
-        O += f * sm_o[(ww * G + gg) * (D + 1) + d];
+        O += f * sm_o[(ww * D + d) * GP + gg];
       }
       if (ns == 1) {
         ll_store(a.rec + (size_t)kvh * G * D + idx, L > 0.f ? O / L : 0.f, e);
@@ -883,7 +898,8 @@ bool plan_fused_layer(int H, int Hq, int Hkv, int D, int I, int64_t max_tiles, i
   // attention staging, the partials of the output rows a workgroup adds
   const int RL = fused_rec_len(G, D);
   const int64_t need_o = (int64_t)Hq * D + (ns > 1 ? (int64_t)Hkv * ns * RL : 0);
-  const int64_t need_att = (int64_t)G * (D + 4) + 2 * D + 2 * kFusedWaves * 16 + (int64_t)kFusedWaves * G * (D + 1);
+  const int GP = G <= 4 ? 4 : (G <= 8 ? 8 : 16);
+  const int64_t need_att = (int64_t)G * (D + 4) + 2 * D + 2 * kFusedWaves * 16 + (int64_t)kFusedWaves * D * GP;
   const int red_units = (H / kFusedRedRows + nwg - 1) / nwg;
   const int64_t need_red = (int64_t)red_units * kFusedRedRows * nwg;
   if (need_o > kFusedX || need_att > kFusedX || need_red > kFusedX || H > kFusedX) return false;
