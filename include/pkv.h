@@ -41,9 +41,13 @@
  *     skipped and the corresponding outputs are unspecified.  Read and clear
  *     the word with pkv_device_error.
  *   - A workspace must be zero-initialised once (pkv_workspace_init) before
- *     its first use; the kernels leave it ready for the next call.  Calls
- *     that share a workspace must be ordered on one stream; calls on
- *     different streams need different workspaces.
+ *     its first use; the kernels leave it ready for the next call, of any
+ *     entry point and any shape that fits it.  Its first 2304 bytes are a
+ *     header that every call's layout leaves to the error word and to the
+ *     single-launch layer's launch counters (decoder_layer_decode), whose
+ *     exchange words carry tagged launch numbers that no other stored value
+ *     has.  Calls that share a workspace must be ordered on one stream;
+ *     calls on different streams need different workspaces.
  *
  * Pool layout: a page of PT tokens (page_tokens: 16, the engine's page, or
  * 256, the fixed page length of the three-stage engine's paged KV cache)

@@ -391,7 +391,7 @@ TiledLayout tiled_layout(const pkv_config* c, int B, int64_t max_tiles) {
   TiledLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
-  L.err = take(256);
+  L.err = take(kWsHeaderBytes);
   L.attn_part = take(sizeof(float) * (size_t)B * c->num_key_value_heads * attn_max_splits(max_tiles) *
                      attn_rec(c->head_dim));
   L.q = take(2 * (size_t)B * QD * 2);
@@ -792,7 +792,7 @@ static PrefillLayout prefill_layout(const pkv_config* cfg, int32_t T) {
   PrefillLayout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
-  L.err = take(256);
+  L.err = take(kWsHeaderBytes);
   L.x = take(sizeof(float) * T * H);
   L.xb = take(2 * (size_t)packed_pair_elems(T, (int)H));
   L.q = take(2 * (size_t)T * QD * 2);

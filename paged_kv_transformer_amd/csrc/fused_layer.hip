@@ -334,7 +334,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_layer_kernel(const FusedA
   const int copy = wg % kFusedCopies;
   const uint64_t* ll0 = a.q;  // the exchange region starts at q
   const uint32_t llw = (uint32_t)(a.ypart + (size_t)H * nwg - a.q);
-  const uint32_t e = a.epoch[wg] + 1u;  // this launch's epoch
+  const uint32_t launch_no = a.epoch[wg] + 1u;  // this launch's number
+  const uint32_t e = fused_epoch_tag(launch_no);  // the epoch its words carry
   const int p = a.pos[0];
   const int psh = 4 + a.pv.pt_shift, PT = 1 << psh;
   const int half = D / 2;
@@ -880,7 +881,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_layer_kernel(const FusedA
       }
     }
   }
-  if (tid == 0) a.epoch[wg] = e;
+  if (tid == 0) a.epoch[wg] = launch_no;
 }
 
 }  // namespace

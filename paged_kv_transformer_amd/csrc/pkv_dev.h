@@ -536,6 +536,23 @@ constexpr int kFusedRedRows = kFusedWaves;        // output rows per reduction u
 // serves one eighth of the grid
 constexpr int kFusedCopies = 8;
 
+// Every workspace, whatever call it serves, starts with this header: the
+// sticky device-error word at byte 0 and, from byte kWsFusedEpochs, the
+// single-launch layer's per-workgroup launch counters.  The counters have
+// to survive the calls of other shapes and entry points that may use the
+// same workspace between two launches of that layer, so no layout puts
+// anything else there.
+constexpr size_t kWsFusedEpochs = 256;
+constexpr size_t kWsHeaderBytes = kWsFusedEpochs + 4 * (size_t)kFusedMaxWgs;
+
+// The epoch half of the single-launch layer's (value, epoch) exchange
+// words: the launch counter's low 21 bits inside a signalling-NaN bit
+// pattern.  No arithmetic result, BF16 pair, count or index that another
+// call stores in a workspace has these bits, so a word left at the same
+// place by a call of another shape never passes for the current launch's
+// (the counter itself is kept plain).
+__host__ __device__ inline uint32_t fused_epoch_tag(uint32_t n) { return 0x7FA00000u | (n & 0x1FFFFFu); }
+
 // Phases, in order: QKV; attention; O; gate/up with the down projection's
 // matching columns (each gate/up unit multiplies its 8 SwiGLU outputs into
 // a partial of the layer output); the reduction of those partials.
@@ -629,7 +646,7 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int64_t m
   WsLayout w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
-  w.err = take(256);
+  w.err = take(kWsHeaderBytes);
   w.attn_part = take(sizeof(float) * (size_t)B * Hkv * attn_max_splits(max_tiles) * attn_rec(D));
   if (layer) {
     w.q = take(sizeof(float) * (size_t)B * Hq * D);  // BF16 hi + lo per value
@@ -647,7 +664,7 @@ inline WsLayout ws_layout(int B, int H, int Hq, int Hkv, int I, int V, int64_t m
     w.gemm_part = take(sizeof(float) * (po > pd ? po : pd));
     if (B == 1) {
       w.fused_ll = take(8 * fused_ll_pairs(H, Hq, Hkv, D, I, fused_splits(max_tiles)));
-      w.fused_epoch = take(4 * (size_t)kFusedMaxWgs);
+      w.fused_epoch = kWsFusedEpochs;
     }
   }
   w.total = off;

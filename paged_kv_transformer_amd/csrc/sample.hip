@@ -846,7 +846,7 @@ __global__ __launch_bounds__(kFThreads) void sample_k3(const SArgs a) {
 SampleWs sample_ws_carve(void* base, int B, int W, int chunk) {
   SampleWs w{};
   const uintptr_t p = (uintptr_t)base;
-  size_t off = 0;
+  size_t off = kWsHeaderBytes;  // the header every workspace keeps
   auto take = [&](size_t bytes) { const size_t at = off; off = align256(off + bytes); return (void*)(p + at); };
   w.cnt = (uint32_t*)take(sizeof(uint32_t) * (size_t)B * kBuckets);
   w.mass = (uint64_t*)take(sizeof(uint64_t) * (size_t)B * kBuckets);

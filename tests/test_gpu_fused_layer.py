@@ -256,3 +256,67 @@ def test_step_qwen_batch1_single_launch_layers():
                                            want_pool=False)
     assert err == 0
     assert_logits(logits, logits_m.astype(np.float64), "single vs multi-launch layers", full_size=True)
+
+
+def test_one_workspace_across_shapes_and_entry_points():
+    """One workspace, sized for the largest call, serves in turn the
+    single-launch layer at batch 1, the multi-launch layer at batch 4 over
+    tables of up to 4 attention splits, attention alone at batch 6 with
+    another head grouping, then the first two calls again: each output is
+    bitwise that of the same call on a freshly initialised workspace.  The
+    exchange words and launch counters one call leaves behind never pass for
+    another's, whatever shape reuses their bytes."""
+    shape = synth.QWEN05
+    D, Hkv = shape.head_dim, shape.kv_heads
+    seed = 2400
+    lw = synth.layer_weights(shape, seed, 0)
+    layer = pkv.upload_layer(lw, head_dim=D)
+    mp = 600
+    cfg = pkv.make_config(shape, max_pos=mp, layers=1)
+    c, s = pkv.rope_table(shape.theta, mp, head_dim=D)
+    wl1 = synth.decode_workload("qwen-shared-ws-b1", shape, seed, [300], layers=1, num_pages=64)
+    wl4 = synth.decode_workload("qwen-shared-ws-b4", shape, seed + 1, [450, 37, 511, 260], layers=1,
+                                num_pages=256)
+    pool1, _ = device_pool(wl1.pool, Hkv, D, 16)
+    pool4, _ = device_pool(wl4.pool, Hkv, D, 16)
+    bt1, bt4 = dev(np.ascontiguousarray(wl1.block_tables[0])), dev(np.ascontiguousarray(wl4.block_tables[0]))
+    pos1, pos4 = dev(np.asarray(wl1.positions, np.int32)), dev(np.asarray(wl4.positions, np.int32))
+    h1 = synth.rng(seed, "hidden", 1).standard_normal((1, shape.hidden)).astype(np.float32)
+    h4 = synth.rng(seed, "hidden", 4).standard_normal((4, shape.hidden)).astype(np.float32)
+    # attention alone: 8 query heads over the batch-4 pool's 2 kv heads (groups of 4)
+    Hq_a, Ba = 8, 6
+    wla = synth.decode_workload("qwen-shared-ws-attn", shape, seed + 2, [700, 90, 1000, 17, 400, 1023],
+                                layers=1, num_pages=wl4.num_pages, max_pages=64, with_pool=False)
+    lens_a = dev(np.asarray(wla.positions, np.int32) + 1)
+    bta = dev(np.ascontiguousarray(wla.block_tables[0]))
+    qa = synth.rng(seed, "q", 6).standard_normal((Ba, Hq_a, D)).astype(np.float32)
+    qa_d = torch.from_numpy(qa).to(torch.bfloat16).view(torch.int16).cuda()
+    need = max(pkv.workspace_bytes(cfg, 1, bt1.shape[1]), pkv.workspace_bytes(cfg, 4, bt4.shape[1]),
+               pkv.attention_workspace_bytes(Hq_a, Hkv, Ba, bta.shape[1], head_dim=D))
+    shared = pkv.alloc_workspace(need)
+
+    def layer_call(bt, pos, pool, h, ws):
+        t = torch.from_numpy(np.ascontiguousarray(h)).cuda()
+        pkv.decoder_layer_decode(cfg, layer, c, s, pool, bt, pos, t, ws)
+        return t.cpu().numpy()
+
+    def attn_call(ws):
+        out = torch.full((Ba, Hq_a, D), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_gqa_decode(pool4, qa_d, bta, lens_a, 0.125, out, ws)
+        return out.cpu().numpy()
+
+    calls = [("layer b1 (single launch)", lambda ws: layer_call(bt1, pos1, pool1, h1, ws)),
+             ("layer b4", lambda ws: layer_call(bt4, pos4, pool4, h4, ws)),
+             ("attention b6 G4", attn_call),
+             ("layer b1 again", lambda ws: layer_call(bt1, pos1, pool1, h1, ws)),
+             ("layer b4 again", lambda ws: layer_call(bt4, pos4, pool4, h4, ws))]
+    with FusedSetting(True):
+        assert pkv.fused_layer_plan(cfg, 1, bt1.shape[1], 16, _cus()) == 1
+        for label, call in calls:
+            say("shared workspace: %s" % label)
+            got = call(shared)
+            fresh = pkv.alloc_workspace(need)
+            want = call(fresh)
+            assert pkv.device_error(fresh) == 0
+            assert np.array_equal(got, want), "%s on the shared workspace differs" % label
+    assert pkv.device_error(shared) == 0
