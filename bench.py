@@ -331,13 +331,22 @@ def layer_bytes(shape, n_attend, q_bytes=4):
             + shape.kv_heads * shape.head_dim * 2 * 2 + 2 * shape.hidden * 4)
 
 
-def time_layer_qwen05_b1(torch, pkv, synth, reps=100, cold=False):
+def time_layer_qwen05_b1(torch, pkv, synth, reps=100, cold=False, fused=True):
     """The Qwen2.5-0.5B layer at batch 1, position 127, as a chain of 16
     distinct layers (16 weight draws, 16 page sets) in one HIP graph, so the
     layer's 30 MB are not served from the Infinity Cache; per-layer time =
-    replay / 16.  Returns (list of per-layer ms per replay, bytes per layer,
-    with cold=True the microseconds of one layer call after a cache flush
-    (else None), kernel launches per layer)."""
+    replay / 16.  fused: the single-launch layer (the library's default for
+    this layer), else the multi-launch path.  Returns (list of per-layer ms
+    per replay, bytes per layer, with cold=True the microseconds of one layer
+    call after a cache flush (else None), kernel launches per layer)."""
+    prev = pkv.set_fused_layer(fused)
+    try:
+        return _time_layer_qwen05_b1(torch, pkv, synth, reps, cold)
+    finally:
+        pkv.set_fused_layer(prev)
+
+
+def _time_layer_qwen05_b1(torch, pkv, synth, reps, cold):
     shape = synth.QWEN05
     L = 16
     wl = synth.decode_workload("qwen0.5b layer chain", shape, 1001, [127], layers=L)
@@ -884,12 +893,14 @@ def decode_only(torch, pkv, synth, args):
     attn_ms, _ = time_attention(torch, pkv, synth, S, args.attn_rounds)
     l_ms, _ = time_layer_b1(torch, pkv, synth, S)
     lq_ms, _, _, lq_n = time_layer_qwen05_b1(torch, pkv, synth)
+    lm_ms, _, _, _ = time_layer_qwen05_b1(torch, pkv, synth, fused=False)
     samp_us, _ = time_sampling(torch, pkv, synth, S)
     wl1 = synth.llama1b_step_b1()
     s1, _ = time_step_cfg(torch, pkv, synth, wl1, synth.LLAMA1B, S.model, int(wl1.positions.max()) + 1)
     out = {"step_b16_ms": round(step, 4), "attention_us": round(attn_ms * 1e3, 3), "sampling_us": round(samp_us, 2),
            "layer_llama1b_b1_us": round(l_ms * 1e3, 3), "layer_qwen05_b1_us": round(float(np.median(lq_ms)) * 1e3, 3),
-           "qwen_launches_per_layer": lq_n, "step_llama1b_b1_ms": round(float(np.median(s1)), 4)}
+           "qwen_launches_per_layer": lq_n, "layer_qwen05_b1_multi_launch_us": round(float(np.median(lm_ms)) * 1e3, 3),
+           "step_llama1b_b1_ms": round(float(np.median(s1)), 4)}
     assert pkv.device_error(S.ws) == 0
     print(json.dumps(out), flush=True)
 
@@ -1023,9 +1034,12 @@ def main():
             decode_only(torch, pkv, synth, args)
         elif args.qwen_layer_only:
             lq_ms, lq_bytes, _, lq_n = time_layer_qwen05_b1(torch, pkv, synth)
+            lm_ms, _, _, lm_n = time_layer_qwen05_b1(torch, pkv, synth, fused=False)
             lq_us = float(np.median(lq_ms)) * 1e3
             print(json.dumps({"layer_qwen05_b1_us": round(lq_us, 3), "algorithmic_bytes": int(lq_bytes),
-                              "achieved_gbs": round(lq_bytes / (lq_us * 1e3), 1), "launches_per_layer": lq_n}),
+                              "achieved_gbs": round(lq_bytes / (lq_us * 1e3), 1), "launches_per_layer": lq_n,
+                              "multi_launch_us": round(float(np.median(lm_ms)) * 1e3, 3),
+                              "multi_launch_launches_per_layer": lm_n}),
                   flush=True)
         elif args.variants_only:
             print(json.dumps({"page_geometry": page_geometries(torch, pkv, synth),
@@ -1124,7 +1138,10 @@ def main():
     extra = {}
     if not args.no_extra_configs:
         lq_ms, lq_bytes, lq_cold, lq_n = time_layer_qwen05_b1(torch, pkv, synth, cold=True)
+        lm_ms, _, _, lm_n = time_layer_qwen05_b1(torch, pkv, synth, fused=False)
         lq_us = float(np.median(lq_ms)) * 1e3
+        log("qwen0.5b layer chain, multi-launch path: %.2f us per layer, %s launches per layer" % (
+            float(np.median(lm_ms)) * 1e3, lm_n))
         lq_gbs = lq_bytes / (lq_us * 1e3)
         lq_floor = None if lq_n is None else round(lq_n * floor["wg256"], 3)
         log("qwen0.5b layer chain: %.2f us per layer (median), %.2f MB -> %.0f GB/s; %s launches per layer, "
@@ -1138,8 +1155,11 @@ def main():
             "launches_per_layer": lq_n, "launch_floor_us": lq_floor,
             "data_time_at_stream_ceiling_us": None,
             "cold_single_call_us": lq_cold,
-            "note": "launch_floor_us = launches per layer x one empty launch of 256 workgroups in a graph; "
-                    "cold_single_call_us: one layer call after a 1 GiB device write"}
+            "multi_launch": {"us_per_layer": pct([m * 1e3 for m in lm_ms]), "launches_per_layer": lm_n},
+            "note": "the single-launch layer (one workgroup per compute unit); multi_launch: the same "
+                    "chain through the six-kernel path (pkv_set_fused_layer(0)); launch_floor_us = launches "
+                    "per layer x one empty launch of 256 workgroups in a graph; cold_single_call_us: one "
+                    "layer call after a 1 GiB device write"}
         extra.update(large_batch_steps(torch, pkv, synth, S.model))
         extra["page_geometry"] = page_geometries(torch, pkv, synth)
         extra["layer_llama8b"] = time_layer_llama8b(torch, pkv, synth)
