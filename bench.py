@@ -30,6 +30,9 @@ oracle timed on a bounded sample of the same workload.
                                       counters are taken on)
   python bench.py --step-counters    (3 eager batch-16 steps, then the same
                                       copy: the step's counter runs)
+  python bench.py --qwen-layer-counters
+                                     (3 eager passes of the 16-layer batch-1
+                                      Qwen chain, then the same copy)
   python bench.py --counter-table FETCH.csv WRITE.csv
                                      (every library kernel's scaled FETCH_SIZE
                                       and WRITE_SIZE per dispatch, markdown)
@@ -346,35 +349,64 @@ def time_layer_qwen05_b1(torch, pkv, synth, reps=100, cold=False, fused=True):
         pkv.set_fused_layer(prev)
 
 
-def _time_layer_qwen05_b1(torch, pkv, synth, reps, cold):
-    shape = synth.QWEN05
+class QwenChain:
+    """The Qwen2.5-0.5B layer at batch 1, position 127, as 16 distinct
+    layers (weights, page sets) on the device; run(stream) calls
+    decoder_layer_decode on each in turn."""
     L = 16
-    wl = synth.decode_workload("qwen0.5b layer chain", shape, 1001, [127], layers=L)
-    layers = [pkv.upload_layer(synth.layer_weights(shape, 1001, l)) for l in range(L)]
-    c, sn = pkv.rope_table(shape.theta, 128)
-    cfg = pkv.make_config(shape, max_pos=128, layers=1)
-    pool_t = pkv.to_device(wl.pool)
-    pool = pkv.kv_pool_create(pool_t, shape.kv_heads)
-    bts = [pkv.to_device(wl.block_tables[l]) for l in range(L)]
-    pos = pkv.to_device(wl.positions)
-    hidden = torch.from_numpy(synth.rng(1001, "hidden").standard_normal((1, shape.hidden), dtype=np.float32)).cuda()
-    ws = pkv.alloc_workspace(pkv.workspace_bytes(cfg, 1, wl.max_pages))
 
-    def run(stream):
-        for l in range(L):
-            pkv.decoder_layer_decode(cfg, layers[l], c, sn, pool, bts[l], pos, hidden, ws, stream)
+    def __init__(self, torch, pkv, synth):
+        shape = self.shape = synth.QWEN05
+        L = self.L
+        wl = synth.decode_workload("qwen0.5b layer chain", shape, 1001, [127], layers=L)
+        self.layers = [pkv.upload_layer(synth.layer_weights(shape, 1001, l)) for l in range(L)]
+        self.c, self.sn = pkv.rope_table(shape.theta, 128)
+        self.cfg = pkv.make_config(shape, max_pos=128, layers=1)
+        self.pool_t = pkv.to_device(wl.pool)
+        self.pool = pkv.kv_pool_create(self.pool_t, shape.kv_heads)
+        self.bts = [pkv.to_device(wl.block_tables[l]) for l in range(L)]
+        self.pos = pkv.to_device(wl.positions)
+        self.hidden = torch.from_numpy(
+            synth.rng(1001, "hidden").standard_normal((1, shape.hidden), dtype=np.float32)).cuda()
+        self.ws = pkv.alloc_workspace(pkv.workspace_bytes(self.cfg, 1, wl.max_pages))
+        self.pkv = pkv
 
-    graph = capture(torch, run, keep=True)
+    def call(self, l, stream=None):
+        self.pkv.decoder_layer_decode(self.cfg, self.layers[l], self.c, self.sn, self.pool, self.bts[l], self.pos,
+                                      self.hidden, self.ws, stream)
+
+    def run(self, stream):
+        for l in range(self.L):
+            self.call(l, stream)
+
+
+def qwen_layer_counters(torch, pkv, synth, passes=3):
+    """Launch sequence for the hardware-counter runs of the batch-1 Qwen
+    layer: `passes` eager passes over the 16-layer chain (single launch per
+    layer), then the counters' calibration copy."""
+    Q = QwenChain(torch, pkv, synth)
+    for _ in range(passes):
+        Q.run(None)
+    torch.cuda.synchronize()
+    assert pkv.device_error(Q.ws) == 0
+    n = calibration_copies(torch)
+    print("qwen-layer-counters: %d eager calls; copy calibration: 3 x %d bytes read + written"
+          % (passes * Q.L, n), flush=True)
+
+
+def _time_layer_qwen05_b1(torch, pkv, synth, reps, cold):
+    Q = QwenChain(torch, pkv, synth)
+    L = Q.L
+    graph = capture(torch, Q.run, keep=True)
     nodes = graph_nodes(graph)
     for _ in range(20):
         graph.replay()
     ms = timed_replays(torch, graph.replay, reps)
     cold_us = None
     if cold:
-        cold_us = cold_call_us(torch, lambda: pkv.decoder_layer_decode(cfg, layers[0], c, sn, pool, bts[0], pos,
-                                                                        hidden, ws))
-    assert pkv.device_error(ws) == 0
-    return [m / L for m in ms], layer_bytes(shape, 127), cold_us, (None if nodes is None else nodes / L)
+        cold_us = cold_call_us(torch, lambda: Q.call(0))
+    assert pkv.device_error(Q.ws) == 0
+    return [m / L for m in ms], layer_bytes(Q.shape, 127), cold_us, (None if nodes is None else nodes / L)
 
 
 def time_step_cfg(torch, pkv, synth, wl, shape, model, max_pos, reps=10):
@@ -839,6 +871,18 @@ def cpu_baseline(host, single_seqs, synth_mod):
     return (d1, single), (dn, n, allt), per_config
 
 
+def calibration_copies(torch):
+    """Three device copies of COPY_BYTES (the hardware counters' scale:
+    what FETCH_SIZE and WRITE_SIZE read for a known number of bytes)."""
+    n = COPY_BYTES
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return n
+
+
 def attention_only(torch, pkv, synth, rounds):
     """Launch sequence for the hardware-counter runs: the attention calls
     over the 16 layers' tables, one by one, then a device copy of known
@@ -851,12 +895,7 @@ def attention_only(torch, pkv, synth, rounds):
             A.launch(l, stream)
     torch.cuda.synchronize()
     assert pkv.device_error(A.ws) == 0
-    n = COPY_BYTES
-    a = torch.ones(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
+    n = calibration_copies(torch)
     abytes = attention_bytes(S.wl.lens, S.shape.heads, S.shape.kv_heads, 2)
     print("attention-only: %d calls, %d algorithmic bytes per call; copy calibration: 3 x %d bytes "
           "read + written" % (rounds * A.layers, abytes, n), flush=True)
@@ -871,12 +910,7 @@ def step_counters(torch, pkv, synth, steps=3):
         S.step(pkv)
     torch.cuda.synchronize()
     assert pkv.device_error(S.ws) == 0
-    n = COPY_BYTES
-    a = torch.ones(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
+    n = calibration_copies(torch)
     print("step-counters: %d eager steps; copy calibration: 3 x %d bytes read + written" % (steps, n),
           flush=True)
 
@@ -998,6 +1032,8 @@ def main():
                     help="time the page-geometry variants and the head-width-128 layer alone")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time the prefill alone (the step's model, no decode workload)")
+    ap.add_argument("--qwen-layer-counters", action="store_true",
+                    help="3 eager passes of the batch-1 Qwen layer chain and the calibration copy (counter runs)")
     ap.add_argument("--qwen-layer-only", action="store_true",
                     help="time the qwen2.5-0.5b-shape batch-1 layer chain alone (for profiling)")
     ap.add_argument("--decode-only", action="store_true",
@@ -1019,7 +1055,7 @@ def main():
     import synth
 
     if (args.attention_only or args.prefill_only or args.large_batch_only or args.variants_only
-            or args.step_counters or args.qwen_layer_only or args.decode_only):
+            or args.step_counters or args.qwen_layer_only or args.decode_only or args.qwen_layer_counters):
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(2)
@@ -1028,6 +1064,8 @@ def main():
             attention_only(torch, pkv, synth, args.attn_rounds)
         elif args.step_counters:
             step_counters(torch, pkv, synth)
+        elif args.qwen_layer_counters:
+            qwen_layer_counters(torch, pkv, synth)
         elif args.prefill_only:
             prefill_only(torch, pkv, synth, args.prefill_tokens)
         elif args.decode_only:
@@ -1041,6 +1079,8 @@ def main():
                               "multi_launch_us": round(float(np.median(lm_ms)) * 1e3, 3),
                               "multi_launch_launches_per_layer": lm_n}),
                   flush=True)
+            n = calibration_copies(torch)
+            print("copy calibration: 3 x %d bytes read + written" % n, flush=True)
         elif args.variants_only:
             print(json.dumps({"page_geometry": page_geometries(torch, pkv, synth),
                               "layer_llama8b": time_layer_llama8b(torch, pkv, synth)}))

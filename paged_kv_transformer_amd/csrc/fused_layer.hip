@@ -11,30 +11,45 @@
 // the latency of its first bytes, cost several times the data.
 //
 // Here the whole layer is one launch of one workgroup per compute unit,
-// all resident at once:
+// all resident at once (the LDS each workgroup holds allows one per unit):
 //   * Every projection is cut into units (a 16-row group of its packed
-//     weights, or, for the down projection, a part of one) dealt round-robin
-//     over the workgroups.  At kernel start the kFusedWaves compute waves of
-//     a workgroup issue every weight block of all of its units, of all
-//     phases, as direct global -> LDS copies (1 KiB per instruction), so the
-//     layer's weights stream from HBM at once, while the phases that need
-//     them are still waiting for their inputs.
-//   * The phases (QKV, attention, O, gate/up, down) hand each other only
-//     small vectors (q and the new K/V row, attention records, h1, the
-//     SwiGLU activations), as 8-byte words holding a value and the launch's
-//     epoch, stored and loaded at device scope.  A consumer polls the words
-//     it needs until each carries the current epoch: the data are their own
-//     flag, so no barrier, fence or counter is needed between phases, and
-//     no word can be mistaken for an older launch's.  One wave per
-//     workgroup (the communication wave) does these polls, so that the
-//     compute waves' counter of outstanding loads holds only weight blocks.
-//   * Each workgroup keeps its own launch counter (epoch); all workgroups
-//     run every launch, so the counters stay equal.  Every wait is bounded
-//     in time: a poll that outlives its deadline sets PKV_DEVERR_SYNC and
-//     lets the workgroup run on, so every wave always exits.
-//   * Products are FP32 FMAs of the BF16 weights with the FP32 input vector
-//     (at batch 1 the matrix cores would waste 15 of 16 columns); the
-//     attention is the paged attention kernel's own matrix-core tile code.
+//     weights; for gate/up, 8 interleaved gate and up rows together with
+//     the down projection's 8 matching columns) dealt round-robin over the
+//     workgroups, each phase from its own first workgroup so that the
+//     phases' units spread over the chip.
+//   * A workgroup has kFusedWaves worker waves and as many loader waves.
+//     At kernel start each loader wave issues every weight block of its
+//     worker's share of all the workgroup's units, of all phases, as direct
+//     global -> LDS copies (1 KiB per instruction, non-temporal), a few in
+//     flight at a time, and publishes in LDS how many have landed; the
+//     layer's weights thus stream from HBM at once while the phases that
+//     need them still wait for their inputs.  The workers wait only for
+//     the count of the blocks they are about to use and meet at a barrier
+//     of their own (an LDS arrival counter), never at one that includes the
+//     loaders.
+//   * The phases (QKV with the norm, RoPE and the append; attention; O with
+//     the residual; gate/up with SwiGLU and the down-projection partials;
+//     the reduction of those partials with the residual) hand each other
+//     only small vectors (q and the new K/V row, the attention records, h1,
+//     the per-workgroup partials of the layer output), as 8-byte words
+//     holding a value and the launch's epoch, stored and loaded at device
+//     scope.  A consumer polls the words it needs until each carries the
+//     current epoch: the data are their own flag, so no barrier, fence or
+//     counter is needed between phases, and no word can be mistaken for an
+//     older launch's or for another call's (the epoch is a tagged pattern no
+//     other stored value has).
+//   * Each workgroup keeps its own launch counter in the workspace's
+//     header; all workgroups run every launch, so the counters stay equal.
+//     Every wait is bounded in time: a poll that outlives its deadline sets
+//     PKV_DEVERR_SYNC and lets the workgroup run on, so every wave exits.
+//   * Products run on the matrix cores with the input vector as BF16 hi and
+//     lo halves (FP32-like precision, as the multi-launch path); the
+//     attention is the paged attention kernel's tile code on K/V tiles
+//     that the loader waves copy into LDS first.  The down projection is
+//     folded into the gate/up units: each multiplies its 8 SwiGLU outputs
+//     by its 8 columns of the down weights into a partial of the whole
+//     output row, and the reduction phase adds the partials of every
+//     workgroup in a fixed order.
 // Results are deterministic: every sum runs in a fixed order.
 #include <type_traits>
 
