@@ -273,10 +273,10 @@ int paged_gqa_decode_noalloc(const pkv_pool *pool, const uint16_t *q,
  * at once, the layer's weights streamed into LDS at kernel start and the
  * phases passing their small vectors through the workspace; nothing else may
  * occupy the GPU's compute units meanwhile, or a phase can wait past its
- * bounded deadline (PKV_DEVERR_SYNC, outputs unspecified).  Its sums run in
- * another order than the multi-launch path's (FP32 products of the FP32
- * activations with the BF16 weights), so the two agree to rounding, not bit
- * for bit.
+ * bounded deadline (PKV_DEVERR_SYNC, outputs unspecified).  Its products are
+ * the multi-launch path's (matrix-core products of the BF16 weights with the
+ * activations as BF16 hi and lo halves) summed in another order, so the two
+ * agree to rounding, not bit for bit.
  */
 int decoder_layer_decode(const pkv_config *cfg, const pkv_layer_weights *w,
 			 const float *rope_cos, const float *rope_sin,
@@ -481,10 +481,11 @@ int pkv_set_fused_layer(int32_t enable);
 /*
  * pkv_fused_layer_plan — 1 if decoder_layer_decode / decode_step calls with
  * this configuration, batch and block-table size run each layer as one
- * launch on a GPU of `compute_units` compute units (batch 1, the layer's
- * weights fit 32 KiB of LDS per compute wave of one workgroup per compute
- * unit, at most one 128-token attention unit per workgroup, the phase
- * vectors fit the kernel's 24 KiB buffer), 0 if they take the multi-launch
+ * launch on a GPU of `compute_units` compute units (batch 1, hidden size at
+ * most 2048, each worker wave's share of its workgroup's weights fits its
+ * 33 KiB of LDS slots with one workgroup per compute unit, at most one
+ * 128-token attention unit per workgroup, the phase vectors fit the
+ * kernel's 22 KiB staging buffer), 0 if they take the multi-launch
  * path; -EINVAL / -ENOTSUP on bad arguments.  Host only.  The Qwen2.5-0.5B
  * shape fits at 128-token tables on 256 compute units; the Llama-3.2-1B
  * shape does not (123 MB of layer weights).
