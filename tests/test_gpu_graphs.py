@@ -31,19 +31,23 @@ def capture(fn):
     return g
 
 
-@pytest.mark.parametrize("batch", [5, 64])
+@pytest.mark.parametrize("batch", [1, 5, 64])
 def test_decode_step_replays_match_eager(batch):
-    """Four replays, each one position further with new tokens; batch 64
-    takes the tiled projections."""
+    """Four replays, each one position further with new tokens; batch 1
+    takes the single-launch layers (whose exchange words carry a new epoch
+    on every replay), batch 64 the tiled projections."""
     shape = synth.tiny_shape(hidden=128, layers=3, heads=4, kv_heads=2, inter=256, vocab=1000)
     seed = 1100 + batch
     p0 = synth.rng(seed, "lens").integers(0, 200, size=batch).astype(np.int32)
-    p0[:3] = [0, 14, 15]
+    p0[:3] = [0, 14, 15][:batch]
     R = 4
     wl = synth.decode_workload("graph", shape, seed, p0 + R - 1)  # tables hold every replay's token
     weights = synth.model_weights(shape, seed, sigma=0.05, norm_sigma=0.3)
     mp = int(p0.max()) + R
     cfg = pkv.make_config(shape, max_pos=mp)
+    if batch == 1:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        assert pkv.fused_layer_plan(cfg, 1, wl.max_pages, 16, cus) == 1
     model = pkv.upload_model(weights, shape.theta, mp)
     bts = dev(wl.block_tables)
     pools, P = [], []
