@@ -132,21 +132,24 @@ def test_qwen_layer_positions(p):
     _check(shape, lw, hidden, wl, "qwen p=%d" % p)
 
 
-@pytest.mark.parametrize("page_tokens,split", [(256, False), (16, True), (256, True)])
-def test_page_geometries(page_tokens, split):
+@pytest.mark.parametrize("page_tokens,split,p", [(256, False, 200), (16, True, 200), (256, True, 200),
+                                                 (256, False, 511), (256, True, 300)])
+def test_page_geometries(page_tokens, split, p):
     """256-token pages (16 tiles under one table entry) and separate K and V
     pools: the attention units' tile copies and the append go through the
-    same pool view as every other kernel."""
+    same pool view as every other kernel; at positions 300 and 511 the two
+    256-token pages hold 3 and 4 attention units per kv head, whose records
+    the O phase merges."""
     shape = synth.QWEN05
-    seed = 2150 + page_tokens + int(split)
-    wl = synth.decode_workload("qwen-fused-geometry", shape, seed, [200], layers=1, page_tokens=page_tokens)
+    seed = 2150 + page_tokens + int(split) + p
+    wl = synth.decode_workload("qwen-fused-geometry", shape, seed, [p], layers=1, page_tokens=page_tokens)
     lw = synth.layer_weights(shape, seed, 0)
     hidden = synth.rng(seed, "hidden").standard_normal((1, shape.hidden)).astype(np.float32)
     pool = wl.pool
     if split:
         geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim, page_tokens)
         pool = oracle.split_pools(wl.pool, geo)
-    _check(shape, lw, hidden, wl, "qwen %d-token pages%s" % (page_tokens, ", K/V pools" if split else ""),
+    _check(shape, lw, hidden, wl, "qwen %d-token pages%s, p=%d" % (page_tokens, ", K/V pools" if split else "", p),
            pool=pool, page_tokens=page_tokens)
 
 
