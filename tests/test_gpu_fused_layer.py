@@ -323,3 +323,34 @@ def test_one_workspace_across_shapes_and_entry_points():
             assert pkv.device_error(fresh) == 0
             assert np.array_equal(got, want), "%s on the shared workspace differs" % label
     assert pkv.device_error(shared) == 0
+
+
+def test_step_qwen_batch1_single_launch_256_token_pages():
+    """decode_step at batch 1 with single-launch layers over 256-token pages
+    in separate K and V pools: a 2-layer model of the Qwen2.5-0.5B shape at
+    position 300 (two pages per layer, three live attention units per kv
+    head whose records the O phase merges); logits within 4e-4 of the
+    oracle's (the whole pool's), the argmax rule, the appended K/V."""
+    shape = dataclasses.replace(synth.QWEN05, layers=2)
+    seed = 2321
+    PT = 256
+    wl = synth.decode_workload("qwen-fused-step-256", shape, seed, [300], layers=2, page_tokens=PT)
+    weights = synth.model_weights(shape, seed, layers=2)
+    tokens = synth.rng(seed, "tokens").integers(0, shape.vocab, size=1).astype(np.int32)
+    cfg = pkv.make_config(shape, max_pos=301)
+    assert pkv.fused_layer_plan(cfg, 1, wl.max_pages, PT, _cus()) == 1
+    geo = oracle.PoolGeometry(shape.kv_heads, shape.head_dim, PT)
+    pools = oracle.split_pools(wl.pool, geo)
+    with FusedSetting(True):
+        logits, nxt, pool_after, err = step_gpu(shape, weights, pools, wl.block_tables, wl.positions, tokens,
+                                                page_tokens=PT)
+    assert err == 0
+    ref_logits, ref_tok, k_all, v_all = oracle.decode_step_paged(shape, weights, wl.pool, geo, wl.block_tables,
+                                                                 wl.positions, tokens)
+    assert_logits(logits, ref_logits, "qwen 2-layer step, 256-token pages, K/V pools", full_size=True)
+    check_argmax_rule(ref_logits, nxt)
+    want = wl.pool
+    for l in range(shape.layers):
+        want = expected_pool_after(want, geo, wl.block_tables[l], wl.positions, k_all[l], v_all[l])
+    kv_diff, kv_rms = check_pool_after(pool_after, want, wl.pool)
+    say("  appended K/V of both layers: max-abs %.3g (RMS %.3g)" % (kv_diff, kv_rms))
