@@ -265,7 +265,8 @@ def test_one_workspace_across_shapes_and_entry_points():
     """One workspace, sized for the largest call, serves in turn the
     single-launch layer at batch 1, the multi-launch layer at batch 4 over
     tables of up to 4 attention splits, attention alone at batch 6 with
-    another head grouping, then the first two calls again: each output is
+    another head grouping, sampling over 4 rows, then the first two calls
+    again: each output is
     bitwise that of the same call on a freshly initialised workspace.  The
     exchange words and launch counters one call leaves behind never pass for
     another's, whatever shape reuses their bytes."""
@@ -294,8 +295,17 @@ def test_one_workspace_across_shapes_and_entry_points():
     bta = dev(np.ascontiguousarray(wla.block_tables[0]))
     qa = synth.rng(seed, "q", 6).standard_normal((Ba, Hq_a, D)).astype(np.float32)
     qa_d = torch.from_numpy(qa).to(torch.bfloat16).view(torch.int16).cuda()
+    # sampling over 4 rows of 5000 logits (its histograms and candidate
+    # lists land where the layers keep other data)
+    Bs, Vs = 4, 5000
+    lg = torch.from_numpy(synth.rng(seed, "logits").standard_normal((Bs, Vs)).astype(np.float32) * 3).cuda()
+    temp = torch.tensor([1.0, 0.7, 1.3, 0.0], dtype=torch.float32, device="cuda")
+    topp = torch.tensor([0.9, 0.5, 1.0, 0.9], dtype=torch.float32, device="cuda")
+    topk = torch.tensor([0, 50, 7, 0], dtype=torch.int32, device="cuda")
+    uu = torch.from_numpy(synth.rng(seed, "sample").random(Bs).astype(np.float32)).cuda()
     need = max(pkv.workspace_bytes(cfg, 1, bt1.shape[1]), pkv.workspace_bytes(cfg, 4, bt4.shape[1]),
-               pkv.attention_workspace_bytes(Hq_a, Hkv, Ba, bta.shape[1], head_dim=D))
+               pkv.attention_workspace_bytes(Hq_a, Hkv, Ba, bta.shape[1], head_dim=D),
+               pkv.sample_workspace_bytes(Bs, Vs))
     shared = pkv.alloc_workspace(need)
 
     def layer_call(bt, pos, pool, h, ws):
@@ -308,9 +318,15 @@ def test_one_workspace_across_shapes_and_entry_points():
         pkv.paged_gqa_decode(pool4, qa_d, bta, lens_a, 0.125, out, ws)
         return out.cpu().numpy()
 
+    def sample_call(ws):
+        tok = torch.full((Bs,), -1, dtype=torch.int32, device="cuda")
+        pkv.sample_tokens(lg, temp, topp, topk, uu, tok, ws)
+        return tok.cpu().numpy()
+
     calls = [("layer b1 (single launch)", lambda ws: layer_call(bt1, pos1, pool1, h1, ws)),
              ("layer b4", lambda ws: layer_call(bt4, pos4, pool4, h4, ws)),
              ("attention b6 G4", attn_call),
+             ("sampling b4", sample_call),
              ("layer b1 again", lambda ws: layer_call(bt1, pos1, pool1, h1, ws)),
              ("layer b4 again", lambda ws: layer_call(bt4, pos4, pool4, h4, ws))]
     with FusedSetting(True):
